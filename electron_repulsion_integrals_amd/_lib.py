@@ -1,0 +1,195 @@
+"""ctypes binding of liberi_mi355x.so (include/eri.h): argument marshalling only.
+
+Every step of the integral path runs in the HIP library; this module converts
+numpy shell arrays and torch device tensors into the C ABI's plain pointers
+and raises on error codes.  There is no CPU fallback: if the library is
+missing, loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liberi_mi355x.so")
+
+ERI_SPHERICAL = 1
+ERI_NO_NORMALIZE = 2
+ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "capacity", -4: "HIP error", -5: "out of memory"}
+
+
+class EriError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+class _Shells(ctypes.Structure):
+    _fields_ = [("nshell", ctypes.c_int32),
+                ("centers", ctypes.POINTER(ctypes.c_double)),
+                ("l", ctypes.POINTER(ctypes.c_int32)),
+                ("nprim", ctypes.POINTER(ctypes.c_int32)),
+                ("prim_off", ctypes.POINTER(ctypes.c_int32)),
+                ("exps", ctypes.POINTER(ctypes.c_double)),
+                ("coefs", ctypes.POINTER(ctypes.c_double))]
+
+
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m electron_repulsion_integrals_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    L.eri_build_quartets.argtypes = [ctypes.POINTER(_Shells), ctypes.c_int, i32p, ctypes.c_int64, ctypes.c_double,
+                                     vp, ctypes.POINTER(vp)]
+    L.eri_build_quartets.restype = ctypes.c_int
+    L.eri_plan_destroy.argtypes = [vp]
+    L.eri_plan_destroy.restype = ctypes.c_int
+    L.eri_plan_info.argtypes = [vp, i64p, i64p, i32p, i32p, i64p]
+    L.eri_plan_info.restype = ctypes.c_int
+    L.eri_plan_blocks.argtypes = [vp, i32p, i64p, i64p, i64p]
+    L.eri_plan_blocks.restype = ctypes.c_int
+    L.eri_plan_index_map.argtypes = [vp, vp, vp]
+    L.eri_plan_index_map.restype = ctypes.c_int
+    L.eri_plan_schwarz.argtypes = [vp, vp, vp]
+    L.eri_plan_schwarz.restype = ctypes.c_int
+    L.eri_compute_batch.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64, vp]
+    L.eri_compute_batch.restype = ctypes.c_int
+    L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+    L.eri_digest_J.restype = ctypes.c_int
+    L.eri_strerror.argtypes = [ctypes.c_int]
+    L.eri_strerror.restype = ctypes.c_char_p
+    L.eri_class_info.argtypes = [ctypes.c_int32, i32p, i32p]
+    L.eri_class_info.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(rc):
+    if rc != 0:
+        raise EriError(rc, load().eri_strerror(rc).decode())
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Plan:
+    """A quartet plan owned by the library (freed by close() or garbage collection)."""
+
+    def __init__(self, handle):
+        self._h = handle
+        L = load()
+        nq, nout, np_ = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        nb, nbf = ctypes.c_int32(), ctypes.c_int32()
+        _check(L.eri_plan_info(self._h, ctypes.byref(nq), ctypes.byref(nout), ctypes.byref(nb), ctypes.byref(nbf),
+                               ctypes.byref(np_)))
+        self.n_quartets, self.n_out, self.n_blocks, self.nbf, self.n_pairs = \
+            nq.value, nout.value, nb.value, nbf.value, np_.value
+        n = self.n_blocks
+        self.block_class = np.zeros(n, dtype=np.int32)
+        self.block_start = np.zeros(n, dtype=np.int64)
+        self.block_count = np.zeros(n, dtype=np.int64)
+        self.block_out = np.zeros(n, dtype=np.int64)
+        if n:
+            _check(L.eri_plan_blocks(self._h, self.block_class.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                     self.block_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     self.block_count.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     self.block_out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan is closed")
+        return self._h
+
+    def close(self):
+        if self._h is not None:
+            load().eri_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def index_map(self, stream=None):
+        import torch
+        out = torch.empty((self.n_quartets, 5), dtype=torch.int32, device="cuda")
+        _check(load().eri_plan_index_map(self.handle, _ptr(out), _stream_handle(stream)))
+        return out
+
+    def schwarz(self, stream=None):
+        import torch
+        out = torch.empty(self.n_pairs, dtype=torch.float64, device="cuda")
+        _check(load().eri_plan_schwarz(self.handle, _ptr(out), _stream_handle(stream)))
+        return out
+
+
+def build_quartets(shells, flags: int, quartets=None, tau: float = 0.0, stream=None) -> Plan:
+    """shells: object with centers, l, nprim, prim_off, exps, coefs (host arrays)."""
+    L = load()
+    c = np.ascontiguousarray(shells.centers, dtype=np.float64)
+    l = np.ascontiguousarray(shells.l, dtype=np.int32)
+    k = np.ascontiguousarray(shells.nprim, dtype=np.int32)
+    o = np.ascontiguousarray(shells.prim_off, dtype=np.int32)
+    e = np.ascontiguousarray(shells.exps, dtype=np.float64)
+    cf = np.ascontiguousarray(shells.coefs, dtype=np.float64)
+    sh = _Shells(len(l), c.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                 l.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), k.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                 o.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), e.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                 cf.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    qptr = None
+    nq = 0
+    if quartets is not None:
+        q = np.ascontiguousarray(np.asarray(quartets).reshape(-1, 4), dtype=np.int32)
+        qptr = q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        nq = len(q)
+    h = ctypes.c_void_p()
+    _check(L.eri_build_quartets(ctypes.byref(sh), int(flags), qptr, nq, float(tau), _stream_handle(stream),
+                                ctypes.byref(h)))
+    return Plan(h)
+
+
+def compute_batch(plan: Plan, out, block_begin: int = 0, block_end: int | None = None, stream=None):
+    """Integrals of blocks [block_begin, block_end) into the float64 device tensor ``out``."""
+    if block_end is None:
+        block_end = plan.n_blocks
+    _check(load().eri_compute_batch(plan.handle, int(block_begin), int(block_end), _ptr(out), out.numel(),
+                                    _stream_handle(stream)))
+    return out
+
+
+def digest_J(plan: Plan, D, J, stream=None):
+    """J (device, nbf x nbf, float64) from the symmetric density D (device)."""
+    _check(load().eri_digest_J(plan.handle, _ptr(D), int(D.stride(0)), _ptr(J), int(J.stride(0)),
+                               _stream_handle(stream)))
+    return J
+
+
+def class_info(class_id: int):
+    l4 = (ctypes.c_int32 * 4)()
+    tier = ctypes.c_int32()
+    _check(load().eri_class_info(int(class_id), l4, ctypes.byref(tier)))
+    return tuple(l4), chr(tier.value)
+
+
+def strerror(code: int) -> str:
+    return load().eri_strerror(int(code)).decode()

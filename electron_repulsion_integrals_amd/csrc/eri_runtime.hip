@@ -1,0 +1,1170 @@
+// Host runtime and support kernels behind the C ABI of include/eri.h.
+//
+// Source: "FusionRCG: Orchestrating Recursive Computation Graphs across GPU
+// Memory Hierarchies".  The page's runtime (section III-C, Algorithm 2) takes
+// shell quartets with their primitives {(alpha_i, c_i)}, forms Gaussian-pair
+// data ("GAUSSIANPAIRS"), evaluates one angular-momentum class per kernel and
+// scatters into J.  Everything here runs on the device except argument
+// validation and the small class-block bookkeeping the host needs to launch.
+#include <hip/hip_runtime.h>
+#include <hipcub/hipcub.hpp>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "eri_device.h"
+#include "eri.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+struct HipFail {
+    hipError_t e;
+};
+
+#define HIP_CHECK(x)                                                                                  \
+    do {                                                                                              \
+        hipError_t _e = (x);                                                                          \
+        if (_e != hipSuccess) {                                                                       \
+            g_last_error = std::string(#x) + ": " + hipGetErrorString(_e);                            \
+            throw HipFail{_e};                                                                        \
+        }                                                                                             \
+    } while (0)
+
+inline int ncart(int l) { return (l + 1) * (l + 2) / 2; }
+inline int nsph(int l) { return 2 * l + 1; }
+inline int nfun(int l, bool sph) { return sph ? nsph(l) : ncart(l); }
+inline int pair_class(int la, int lb) { return la * (la + 1) / 2 + lb; }  // la >= lb
+__host__ __device__ inline int class_id_of(int pcb, int pck) { return pcb * (pcb + 1) / 2 + pck; }
+
+__host__ __device__ inline int d_pair_class(int la, int lb)
+{
+    return la >= lb ? la * (la + 1) / 2 + lb : lb * (lb + 1) / 2 + la;
+}
+
+// ---------------------------------------------------------------------------
+// Boys table (host, long double), one copy per device
+// ---------------------------------------------------------------------------
+// F_M(T) by its power series in long double, F_M = exp(-T) sum_k (2T)^k /
+// ((2M+1)(2M+3)...(2M+2k+1)), then the downward recursion to F_0.
+void boys_row_host(long double T, int M, long double *F)
+{
+    long double term = 1.0L / (2 * M + 1), sum = term;
+    for (int k = 1; k < 2000; ++k) {
+        term *= 2.0L * T / (2 * M + 2 * k + 1);
+        sum += term;
+        if (term < 1e-22L * sum && k > T) break;
+    }
+    long double e = expl(-T);
+    F[M] = e * sum;
+    for (int m = M - 1; m >= 0; --m) F[m] = (2.0L * T * F[m + 1] + e) / (2 * m + 1);
+}
+
+std::mutex g_boys_mu;
+std::vector<double *> g_boys_dev;
+
+double *boys_table(int device)
+{
+    std::lock_guard<std::mutex> lk(g_boys_mu);
+    if ((int)g_boys_dev.size() <= device) g_boys_dev.resize(device + 1, nullptr);
+    if (g_boys_dev[device]) return g_boys_dev[device];
+    std::vector<double> tab((size_t)ERI_BT_ROWS * ERI_BT_COLS);
+    long double F[ERI_BT_MMAX + 1];
+    for (int k = 0; k < ERI_BT_ROWS; ++k) {
+        long double T = (long double)k / ERI_BT_PER_UNIT;
+        boys_row_host(T, ERI_BT_MMAX, F);
+        tab[(size_t)k * ERI_BT_COLS] = (double)expl(-T);
+        for (int m = 0; m <= ERI_BT_MMAX; ++m) tab[(size_t)k * ERI_BT_COLS + 1 + m] = (double)F[m];
+    }
+    double *d = nullptr;
+    HIP_CHECK(hipMalloc(&d, tab.size() * sizeof(double)));
+    HIP_CHECK(hipMemcpy(d, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice));
+    g_boys_dev[device] = d;
+    return d;
+}
+
+const EriClassEntry *find_class(int cid, bool sph)
+{
+    for (int i = 0; i < eri_class_table_size; ++i)
+        if (eri_class_table[i].class_id == cid && eri_class_table[i].spherical == (sph ? 1 : 0))
+            return &eri_class_table[i];
+    return nullptr;
+}
+
+// ---------------------------------------------------------------------------
+// support kernels
+// ---------------------------------------------------------------------------
+
+// Contraction coefficients on normalised primitives: c_k N(alpha_k, l), then the
+// contracted x^l component scaled to unit norm (see include/eri.h).
+__global__ void k_normalize(int nshell, const int *l, const int *nprim, const int *off, const double *exps,
+                            const double *coefs, double *out, int raw)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nshell) return;
+    const int L = l[s], K = nprim[s], o = off[s];
+    if (raw) {
+        for (int k = 0; k < K; ++k) out[o + k] = coefs[o + k];
+        return;
+    }
+    double df = 1.0;  // (2L-1)!!
+    for (int t = 2 * L - 1; t > 1; t -= 2) df *= t;
+    for (int k = 0; k < K; ++k) {
+        const double a = exps[o + k];
+        out[o + k] = coefs[o + k] * pow(2.0 * a / M_PI, 0.75) * pow(4.0 * a, 0.5 * L) / sqrt(df);
+    }
+    double norm2 = 0.0;
+    for (int k = 0; k < K; ++k)
+        for (int q = 0; q < K; ++q) {
+            const double p = exps[o + k] + exps[o + q];
+            norm2 += out[o + k] * out[o + q] * pow(M_PI / p, 1.5) * df / pow(2.0 * p, L);
+        }
+    const double f = 1.0 / sqrt(norm2);
+    for (int k = 0; k < K; ++k) out[o + k] *= f;
+}
+
+// Primitive-pair records for every shell pair (the page's GAUSSIANPAIRS).
+__global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, const int *off,
+                            const double *exps, const double *cn, double *ppd)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= npairs) return;
+    const int4 pi = pinfo[p];
+    const int a = pi.x, b = pi.y;
+    const double Ax = cen[3 * a], Ay = cen[3 * a + 1], Az = cen[3 * a + 2];
+    const double Bx = cen[3 * b], By = cen[3 * b + 1], Bz = cen[3 * b + 2];
+    const double AB2 = (Ax - Bx) * (Ax - Bx) + (Ay - By) * (Ay - By) + (Az - Bz) * (Az - Bz);
+    const int Ka = off[a + 1] - off[a], Kb = off[b + 1] - off[b];
+    for (int ia = 0; ia < Ka; ++ia)
+        for (int ib = 0; ib < Kb; ++ib) {
+            const double al = exps[off[a] + ia], be = exps[off[b] + ib];
+            const double z = al + be, iz = 1.0 / z;
+            const double Px = (al * Ax + be * Bx) * iz, Py = (al * Ay + be * By) * iz, Pz = (al * Az + be * Bz) * iz;
+            double *r = ppd + (size_t)(pi.z + ia * Kb + ib) * ERI_PP_STRIDE;
+            r[0] = z;
+            r[1] = iz;
+            r[2] = Px;
+            r[3] = Py;
+            r[4] = Pz;
+            // P - A = beta (B - A) / zeta: exact zero for a one-centre pair
+            r[5] = be * (Bx - Ax) * iz;
+            r[6] = be * (By - Ay) * iz;
+            r[7] = be * (Bz - Az) * iz;
+            r[8] = cn[off[a] + ia] * cn[off[b] + ib] * exp(-al * be * iz * AB2) * iz;
+            r[9] = 0.0;
+        }
+}
+
+__device__ inline void canonical4(const int *l, int &i, int &j, int &k, int &m, int &perm)
+{
+    perm = 0;
+    if (l[i] < l[j]) {
+        int t = i; i = j; j = t;
+        perm |= 1;
+    }
+    if (l[k] < l[m]) {
+        int t = k; k = m; m = t;
+        perm |= 2;
+    }
+    if (d_pair_class(l[i], l[j]) < d_pair_class(l[k], l[m])) {
+        int t = i; i = k; k = t;
+        t = j; j = m; m = t;
+        perm |= 4;
+    }
+}
+
+// Explicit lists: sort key (class, K_bra, K_ket, position).
+__global__ void k_explicit_keys(int64_t nq, const int *q, const int *l, const int *nprim, uint64_t *keys,
+                                int64_t *pos)
+{
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= nq) return;
+    int i = q[4 * x], j = q[4 * x + 1], k = q[4 * x + 2], m = q[4 * x + 3], perm;
+    canonical4(l, i, j, k, m, perm);
+    const uint64_t cid = class_id_of(d_pair_class(l[i], l[j]), d_pair_class(l[k], l[m]));
+    const uint64_t kb = (uint64_t)(nprim[i] * nprim[j]), kk = (uint64_t)(nprim[k] * nprim[m]);
+    keys[x] = (cid << 56) | (kb << 48) | (kk << 40) | (uint64_t)x;
+    pos[x] = x;
+}
+
+__global__ void k_explicit_fill(int64_t nq, const int64_t *pos, const int *q, const int *l, const int *nprim,
+                                int *qmap, int *qbra, int *qket, int4 *pinfo)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nq) return;
+    const int64_t x = pos[s];
+    int i = q[4 * x], j = q[4 * x + 1], k = q[4 * x + 2], m = q[4 * x + 3], perm;
+    canonical4(l, i, j, k, m, perm);
+    qmap[5 * s] = i;
+    qmap[5 * s + 1] = j;
+    qmap[5 * s + 2] = k;
+    qmap[5 * s + 3] = m;
+    qmap[5 * s + 4] = perm;
+    qbra[s] = (int)(2 * s);
+    qket[s] = (int)(2 * s + 1);
+    pinfo[2 * s] = make_int4(i, j, 0, nprim[i] * nprim[j]);
+    pinfo[2 * s + 1] = make_int4(k, m, 0, nprim[k] * nprim[m]);
+}
+
+// start of each class in the sorted keys (lower bound of class << 56)
+__global__ void k_class_starts(int64_t n, const uint64_t *keys, int64_t *starts, int nclass)
+{
+    const int c = blockIdx.x * blockDim.x + threadIdx.x;
+    if (c > nclass) return;
+    const uint64_t target = (uint64_t)c << 56;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) / 2;
+        if (keys[mid] < target) lo = mid + 1;
+        else hi = mid;
+    }
+    starts[c] = lo;
+}
+
+__global__ void k_copy_w(int n, const int4 *pinfo, int *w)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < n) w[p] = pinfo[p].w;
+}
+
+__global__ void k_set_z(int n, int4 *pinfo, const int *z)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < n) pinfo[p].z = z[p];
+}
+
+// All pairs i >= j, oriented so that l_a >= l_b (equal l: a = i).
+__global__ void k_all_pairs(int nshell, const int *l, const int *nprim, int4 *pinfo, uint64_t *pc_key, int *pidx)
+{
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t np = (int64_t)nshell * (nshell + 1) / 2;
+    if (p >= np) return;
+    int i = (int)floor((sqrt(8.0 * (double)p + 1.0) - 1.0) * 0.5);
+    while ((int64_t)i * (i + 1) / 2 > p) --i;
+    while ((int64_t)(i + 1) * (i + 2) / 2 <= p) ++i;
+    const int j = (int)(p - (int64_t)i * (i + 1) / 2);
+    int a = i, b = j;
+    if (l[i] < l[j]) {
+        a = j;
+        b = i;
+    }
+    pinfo[p] = make_int4(a, b, 0, nprim[a] * nprim[b]);
+    pc_key[p] = (uint64_t)d_pair_class(l[a], l[b]);
+    pidx[p] = (int)p;
+}
+
+// Schwarz factor of each pair from its diagonal block (pair-major block of n*n x n*n).
+__global__ void k_schwarz_max(int n, const int *pairs, const double *blk, int nab, double *S)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const double *B = blk + (size_t)t * nab * nab;
+    double mx = 0.0;
+    for (int u = 0; u < nab; ++u) mx = fmax(mx, fabs(B[(size_t)u * nab + u]));
+    S[pairs[t]] = mx;
+}
+
+__global__ void k_desc_keys(int n, const int *pidx, const double *S, uint64_t *key)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const double s = S[pidx[t]];
+    key[t] = ~(uint64_t)__double_as_longlong(s);  // S >= 0: bit order = value order
+}
+
+__global__ void k_bucket_keys(int n, const int *pidx, const int *l, const int4 *pinfo, uint64_t *key)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    const int4 pi = pinfo[pidx[t]];
+    key[t] = ((uint64_t)d_pair_class(l[pi.x], l[pi.y]) << 16) | (uint64_t)pi.w;
+}
+
+__global__ void k_heads(int n, const uint64_t *key, int *head)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    head[t] = (t == 0 || key[t] != key[t - 1]) ? 1 : 0;
+}
+
+__global__ void k_bucket_table(int n, const uint64_t *key, const int *head, const int *hscan, int *bstart,
+                               uint64_t *bkey)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n) return;
+    if (head[t]) {
+        bstart[hscan[t]] = t;
+        bkey[hscan[t]] = key[t];
+    }
+}
+
+struct BlockDesc {
+    int bra_start, bra_n;  // sorted-pair range of the bra bucket
+    int ket_start, ket_n;  // sorted-pair range of the ket bucket
+    int same;              // bra bucket == ket bucket
+    int64_t entry_base;    // first (block, bra) entry
+};
+
+// per (block, bra rank): number of surviving kets, fl(S_b * S_k) >= tau2
+__global__ void k_count(int64_t nentries, const BlockDesc *blocks, int nblocks, const int *porder, const double *S,
+                        double tau2, int64_t *cnt)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= nentries) return;
+    int lo = 0, hi = nblocks;  // last block with entry_base <= e
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (blocks[mid].entry_base <= e) lo = mid;
+        else hi = mid;
+    }
+    const BlockDesc bd = blocks[lo];
+    const int r = (int)(e - bd.entry_base);
+    const double sb = S[porder[bd.bra_start + r]];
+    // kets sorted by S descending: the survivors are a prefix
+    int a = 0, b = bd.ket_n;
+    while (a < b) {
+        int mid = (a + b) / 2;
+        const double prod = __dmul_rn(sb, S[porder[bd.ket_start + mid]]);
+        if (prod >= tau2) a = mid + 1;
+        else b = mid;
+    }
+    int64_t c = a;
+    if (bd.same) c = c > r ? c - r : 0;
+    cnt[e] = c;
+}
+
+__global__ void k_fill_screened(int64_t nentries, const BlockDesc *blocks, int nblocks, const int *porder,
+                                const int64_t *cnt, const int64_t *off, const int4 *pinfo, const int *pair_i,
+                                int *qbra, int *qket, int *qmap)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= nentries) return;
+    int lo = 0, hi = nblocks;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (blocks[mid].entry_base <= e) lo = mid;
+        else hi = mid;
+    }
+    const BlockDesc bd = blocks[lo];
+    const int r = (int)(e - bd.entry_base);
+    const int pb = porder[bd.bra_start + r];
+    const int k0 = bd.same ? r : 0;
+    const int4 ib = pinfo[pb];
+    for (int64_t t = 0; t < cnt[e]; ++t) {
+        const int pk = porder[bd.ket_start + k0 + (int)t];
+        const int64_t s = off[e] + t;
+        qbra[s] = pb;
+        qket[s] = pk;
+        const int4 ik = pinfo[pk];
+        qmap[5 * s] = ib.x;
+        qmap[5 * s + 1] = ib.y;
+        qmap[5 * s + 2] = ik.x;
+        qmap[5 * s + 3] = ik.y;
+        // perm relative to the natural unique form (i >= j, k >= l, pair(ij) >= pair(kl))
+        const int pi_b = pair_i[pb], pi_k = pair_i[pk];
+        const int bswap = ib.x != pi_b ? 1 : 0;  // pair_i holds the larger shell index of the pair
+        const int kswap = ik.x != pi_k ? 1 : 0;
+        qmap[5 * s + 4] = bswap | (kswap << 1) | ((pb < pk ? 1 : 0) << 2);
+    }
+}
+
+__global__ void k_pair_hi(int np, const int4 *pinfo, int *hi)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < np) hi[p] = max(pinfo[p].x, pinfo[p].y);
+}
+
+__global__ void k_gather_i64(int n, const int64_t *src, const int64_t *idx, int64_t *dst)
+{
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < n) dst[t] = src[idx[t]];
+}
+
+// ---- J digestion ----------------------------------------------------------
+
+// Per quartet of one class block: vb[ab] = sum_cd I[ab,cd] D~_cd and, for
+// distinct pairs, vk[cd] = sum_ab I[ab,cd] D~_ab, with D~ = D x 2 for a pair of
+// two different shells (the 8-fold symmetry factors).
+__global__ void k_digest_block(int nq, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
+                               const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
+                               double *cb)
+{
+    const int q = blockIdx.x;
+    if (q >= nq) return;
+    const int pb = qbra[q], pk = qket[q];
+    const int4 ib = pinfo[pb], ik = pinfo[pk];
+    const int nab = na * nb, ncd = nc * nd;
+    const double *blk = I + (size_t)q * nab * ncd;
+    double *vb = cb + (size_t)q * (nab + ncd);
+    double *vk = vb + nab;
+    const double fk = ik.x != ik.y ? 2.0 : 1.0, fb = ib.x != ib.y ? 2.0 : 1.0;
+    const int c0 = bf[ik.x], d0 = bf[ik.y], a0 = bf[ib.x], b0 = bf[ib.y];
+    for (int ab = threadIdx.x; ab < nab; ab += blockDim.x) {
+        double s = 0.0;
+        for (int c = 0; c < nc; ++c)
+            for (int d = 0; d < nd; ++d) s += blk[(size_t)ab * ncd + c * nd + d] * D[(size_t)(c0 + c) * ldd + d0 + d];
+        vb[ab] = fk * s;
+    }
+    for (int cd = threadIdx.x; cd < ncd; cd += blockDim.x) {
+        double s = 0.0;
+        if (pb != pk) {
+            const int c = cd / nd, d = cd - c * nd;
+            (void)c;
+            (void)d;
+            for (int a = 0; a < na; ++a)
+                for (int b = 0; b < nb; ++b) s += blk[(size_t)(a * nb + b) * ncd + cd] * D[(size_t)(a0 + a) * ldd + b0 + b];
+        }
+        vk[cd] = fb * s;
+    }
+}
+
+// One workgroup per pair: sum its contribution vectors in a fixed order, then
+// write the J block (and its transpose for two different shells).
+__global__ void k_reduce_pairs(int np, const int4 *pinfo, const int *bf, const int *nfun_sh, const int64_t *seg,
+                               const int64_t *ent_off, const double *cb, double *J, int ldj)
+{
+    const int p = blockIdx.x;
+    if (p >= np) return;
+    const int4 pi = pinfo[p];
+    const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
+    const int64_t s0 = seg[p], s1 = seg[p + 1];
+    for (int u = threadIdx.x; u < n; u += blockDim.x) {
+        double s = 0.0;
+        for (int64_t e = s0; e < s1; ++e) s += cb[ent_off[e] + u];
+        const int a = u / nb, b = u - a * nb;
+        J[(size_t)(bf[pi.x] + a) * ldj + bf[pi.y] + b] = s;
+        if (pi.x != pi.y) J[(size_t)(bf[pi.y] + b) * ldj + bf[pi.x] + a] = s;
+    }
+}
+
+// entries: (pair key, contribution offset) for every quartet side
+__global__ void k_entries(int64_t nq, const int *qbra, const int *qket, const int64_t *cb_base, const int *blk_of,
+                          const int64_t *blk_start, const int *blk_nab, const int *blk_ncd, int *ekey, int64_t *eoff,
+                          int64_t *nent_out)
+{
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= nq) return;
+    const int b = blk_of[s];
+    const int64_t rel = s - blk_start[b];
+    const int nab = blk_nab[b], ncd = blk_ncd[b];
+    const int64_t off = cb_base[b] + rel * (nab + ncd);
+    ekey[2 * s] = qbra[s];
+    eoff[2 * s] = off;
+    if (qbra[s] != qket[s]) {
+        ekey[2 * s + 1] = qket[s];
+        eoff[2 * s + 1] = off + nab;
+    } else {
+        ekey[2 * s + 1] = 0x7fffffff;  // sorts to the end, never read
+        eoff[2 * s + 1] = -1;
+    }
+    (void)nent_out;
+}
+
+__global__ void k_seg_starts(int np, int64_t n, const int *keys, int64_t *seg)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p > np) return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) / 2;
+        if (keys[mid] < p) lo = mid + 1;
+        else hi = mid;
+    }
+    seg[p] = lo;
+}
+
+__global__ void k_fill_blk_of(int64_t start, int64_t count, int b, int *blk_of)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t < count) blk_of[start + t] = b;
+}
+
+inline unsigned nblk(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+struct EriBlock {
+    int cid;
+    int64_t start, count, out_off;
+    int na, nb, nc, nd;  // functions per shell of the class (spherical or Cartesian)
+};
+
+struct eri_plan {
+    int flags = 0;
+    bool sph = false;
+    bool screened = false;
+    int device = 0;
+    int nshell = 0, nbf = 0;
+    int64_t npairs = 0, nq = 0, nout = 0;
+    double *d_cen = nullptr, *d_exps = nullptr, *d_cn = nullptr, *d_ppd = nullptr, *d_S = nullptr;
+    int *d_l = nullptr, *d_nprim = nullptr, *d_off = nullptr, *d_bf = nullptr, *d_nfun = nullptr;
+    int4 *d_pinfo = nullptr;
+    int *d_qbra = nullptr, *d_qket = nullptr, *d_qmap = nullptr;
+    double *d_boys = nullptr;
+    double *d_scratch = nullptr;
+    int scratch_wgs = 0;
+    long long scratch_doubles = 0;  // per workgroup slice
+    std::vector<EriBlock> blocks;
+    std::vector<void *> allocs;
+    // J digestion work (screened plans, built on first use)
+    bool jready = false;
+    double *d_ints = nullptr, *d_cb = nullptr;
+    int64_t *d_seg = nullptr, *d_eoff = nullptr;
+    int64_t nent = 0;
+
+    template <class T>
+    T *alloc(size_t n)
+    {
+        void *p = nullptr;
+        if (n == 0) n = 1;
+        hipError_t e = hipMalloc(&p, n * sizeof(T));
+        if (e != hipSuccess) {
+            g_last_error = std::string("hipMalloc: ") + hipGetErrorString(e);
+            throw HipFail{e};
+        }
+        allocs.push_back(p);
+        return (T *)p;
+    }
+    ~eri_plan()
+    {
+        for (void *p : allocs) (void)hipFree(p);
+    }
+};
+
+namespace {
+
+template <class T>
+void upload(T *dst, const T *src, size_t n, hipStream_t s)
+{
+    if (n) HIP_CHECK(hipMemcpyAsync(dst, src, n * sizeof(T), hipMemcpyHostToDevice, s));
+}
+
+// one device-wide exclusive scan of int64 counts
+void scan_i64(const int64_t *in, int64_t *out, int64_t n, hipStream_t s)
+{
+    size_t tmp = 0;
+    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp, in, out, (int)n, s));
+    void *t = nullptr;
+    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
+    hipError_t e = hipcub::DeviceScan::ExclusiveSum(t, tmp, in, out, (int)n, s);
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(t);
+    HIP_CHECK(e);
+}
+
+void scan_i32(const int *in, int *out, int64_t n, hipStream_t s)
+{
+    size_t tmp = 0;
+    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp, in, out, (int)n, s));
+    void *t = nullptr;
+    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
+    hipError_t e = hipcub::DeviceScan::ExclusiveSum(t, tmp, in, out, (int)n, s);
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(t);
+    HIP_CHECK(e);
+}
+
+template <class V>
+void sort_pairs_u64(uint64_t *keys_in, uint64_t *keys_out, V *v_in, V *v_out, int64_t n, hipStream_t s)
+{
+    size_t tmp = 0;
+    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 64, s));
+    void *t = nullptr;
+    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
+    hipError_t e = hipcub::DeviceRadixSort::SortPairs(t, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 64, s);
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(t);
+    HIP_CHECK(e);
+}
+
+template <class V>
+void sort_pairs_i32(int *keys_in, int *keys_out, V *v_in, V *v_out, int64_t n, hipStream_t s)
+{
+    size_t tmp = 0;
+    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 32, s));
+    void *t = nullptr;
+    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
+    hipError_t e = hipcub::DeviceRadixSort::SortPairs(t, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 32, s);
+    (void)hipStreamSynchronize(s);
+    (void)hipFree(t);
+    HIP_CHECK(e);
+}
+
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s)
+{
+    const EriClassEntry *ce = find_class(cid, P->sph);
+    if (!ce) {
+        g_last_error = "no kernel for class " + std::to_string(cid);
+        throw HipFail{hipErrorInvalidValue};
+    }
+    EriClassArgs a;
+    a.qbra = qbra;
+    a.qket = qket;
+    a.pair_info = P->d_pinfo;
+    a.ppd = P->d_ppd;
+    a.cen = P->d_cen;
+    a.boys = P->d_boys;
+    a.scratch = P->d_scratch;
+    a.scratch_wgs = P->scratch_wgs;
+    // large blocks are split so that every grid stays within int range
+    const int64_t CH = 1 << 26;
+    for (int64_t b = 0; b < n; b += CH) {
+        const int64_t m = std::min(CH, n - b);
+        a.qbra = qbra + b;
+        a.qket = qket + b;
+        a.nq = (int)m;
+        const int blk = nfun(ce->la, P->sph) * nfun(ce->lb, P->sph) * nfun(ce->lc, P->sph) * nfun(ce->ld, P->sph);
+        a.out = out + b * blk;
+        if (ce->tier == 'M' && (!P->d_scratch)) {
+            g_last_error = "memory-tier class without scratch";
+            throw HipFail{hipErrorInvalidValue};
+        }
+        ce->launch(a, s);
+        HIP_CHECK(hipGetLastError());
+    }
+}
+
+// scratch for memory-tier classes used by the listed class ids
+void ensure_scratch(eri_plan *P, const std::vector<int> &cids)
+{
+    long long need = 0;
+    for (int cid : cids) {
+        const EriClassEntry *ce = find_class(cid, P->sph);
+        if (ce && ce->tier == 'M') need = std::max(need, ce->scratch_doubles);
+    }
+    if (need == 0 || need <= P->scratch_doubles) return;
+    const int wgs = 1024;
+    P->d_scratch = P->alloc<double>((size_t)need * wgs);  // the smaller earlier slice stays owned until destroy
+    P->scratch_wgs = wgs;
+    P->scratch_doubles = need;
+}
+
+void make_pair_data(eri_plan *P, hipStream_t s)
+{
+    const int np = (int)P->npairs;
+    int *w = P->alloc<int>(np + 1), *z = P->alloc<int>(np + 1);
+    hipLaunchKernelGGL(k_copy_w, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, w);
+    scan_i32(w, z, np, s);
+    int last_z = 0, last_w = 0;
+    if (np) {
+        HIP_CHECK(hipMemcpyAsync(&last_z, z + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(&last_w, w + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+    }
+    const int64_t nppd = (int64_t)last_z + last_w;
+    hipLaunchKernelGGL(k_set_z, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, z);
+    P->d_ppd = P->alloc<double>((size_t)nppd * ERI_PP_STRIDE);
+    hipLaunchKernelGGL(k_pair_data, dim3(nblk(np, 128)), dim3(128), 0, s, np, P->d_pinfo, P->d_cen, P->d_off,
+                       P->d_exps, P->d_cn, P->d_ppd);
+    HIP_CHECK(hipGetLastError());
+}
+
+void build_explicit(eri_plan *P, const std::vector<int> &hl, const int32_t *quartets, int64_t nq, hipStream_t s)
+{
+    P->nq = nq;
+    P->npairs = 2 * nq;
+    int *d_q = P->alloc<int>((size_t)4 * nq);
+    upload(d_q, quartets, (size_t)4 * nq, s);
+    uint64_t *k0 = P->alloc<uint64_t>(nq), *k1 = P->alloc<uint64_t>(nq);
+    int64_t *p0 = P->alloc<int64_t>(nq), *p1 = P->alloc<int64_t>(nq);
+    hipLaunchKernelGGL(k_explicit_keys, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, d_q, P->d_l, P->d_nprim, k0, p0);
+    sort_pairs_u64(k0, k1, p0, p1, nq, s);
+    P->d_qmap = P->alloc<int>((size_t)5 * nq);
+    P->d_qbra = P->alloc<int>(nq);
+    P->d_qket = P->alloc<int>(nq);
+    P->d_pinfo = P->alloc<int4>(2 * nq);
+    hipLaunchKernelGGL(k_explicit_fill, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, p1, d_q, P->d_l, P->d_nprim,
+                       P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
+    HIP_CHECK(hipGetLastError());
+    const int NC = 120;
+    int64_t *d_st = P->alloc<int64_t>(NC + 1);
+    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, k1, d_st, NC);
+    std::vector<int64_t> st(NC + 1);
+    HIP_CHECK(hipMemcpyAsync(st.data(), d_st, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    st[NC] = nq;
+    make_pair_data(P, s);
+    int64_t out = 0;
+    std::vector<int> cids;
+    for (int c = 0; c < NC; ++c) {
+        const int64_t cnt = st[c + 1] - st[c];
+        if (cnt <= 0) continue;
+        const EriClassEntry *ce = find_class(c, P->sph);
+        if (!ce) {
+            g_last_error = "class " + std::to_string(c) + " not built";
+            throw HipFail{hipErrorInvalidValue};
+        }
+        EriBlock b{c, st[c], cnt, out, nfun(ce->la, P->sph), nfun(ce->lb, P->sph), nfun(ce->lc, P->sph),
+                   nfun(ce->ld, P->sph)};
+        out += cnt * (int64_t)b.na * b.nb * b.nc * b.nd;
+        P->blocks.push_back(b);
+        cids.push_back(c);
+    }
+    P->nout = out;
+    ensure_scratch(P, cids);
+    (void)hl;
+}
+
+void build_screened(eri_plan *P, const std::vector<int> &hl, const std::vector<int> &hk, double tau, hipStream_t s)
+{
+    const int ns = P->nshell;
+    const int64_t np = (int64_t)ns * (ns + 1) / 2;
+    if (np > (int64_t)INT32_MAX / 2) {
+        g_last_error = "too many shell pairs";
+        throw HipFail{hipErrorInvalidValue};
+    }
+    P->npairs = np;
+    P->d_pinfo = P->alloc<int4>(np);
+    uint64_t *pck = P->alloc<uint64_t>(np), *pck2 = P->alloc<uint64_t>(np);
+    int *pidx = P->alloc<int>(np), *pidx2 = P->alloc<int>(np);
+    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_nprim, P->d_pinfo, pck, pidx);
+    HIP_CHECK(hipGetLastError());
+    make_pair_data(P, s);
+
+    // --- Schwarz factors from the diagonal quartets (p|p), grouped by pair class
+    sort_pairs_u64(pck, pck2, pidx, pidx2, np, s);  // pidx2: pairs ordered by pair class
+    std::vector<uint64_t> hpc(np);
+    HIP_CHECK(hipMemcpyAsync(hpc.data(), pck2, sizeof(uint64_t) * np, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    P->d_S = P->alloc<double>(np);
+    std::vector<int> diag_cids;
+    {
+        int64_t i = 0;
+        while (i < np) {
+            int64_t j = i;
+            while (j < np && hpc[j] == hpc[i]) ++j;
+            diag_cids.push_back(class_id_of((int)hpc[i], (int)hpc[i]));
+            i = j;
+        }
+    }
+    ensure_scratch(P, diag_cids);
+    {
+        int64_t i = 0;
+        size_t cap = 0;
+        double *buf = nullptr;
+        while (i < np) {
+            int64_t j = i;
+            while (j < np && hpc[j] == hpc[i]) ++j;
+            const int pc = (int)hpc[i];
+            int la = 0;
+            while ((la + 1) * (la + 2) / 2 <= pc) ++la;
+            const int lb = pc - la * (la + 1) / 2;
+            const int nab = nfun(la, P->sph) * nfun(lb, P->sph);
+            const size_t need = (size_t)(j - i) * nab * nab;
+            if (need > cap) {
+                if (buf) (void)hipFree(buf);
+                HIP_CHECK(hipMalloc(&buf, need * sizeof(double)));
+                cap = need;
+            }
+            launch_class(P, class_id_of(pc, pc), pidx2 + i, pidx2 + i, j - i, buf, s);
+            hipLaunchKernelGGL(k_schwarz_max, dim3(nblk(j - i, 256)), dim3(256), 0, s, (int)(j - i), pidx2 + i, buf,
+                               nab, P->d_S);
+            HIP_CHECK(hipGetLastError());
+            HIP_CHECK(hipStreamSynchronize(s));
+            i = j;
+        }
+        if (buf) (void)hipFree(buf);
+    }
+
+    // --- bucket the pairs by (pair class, K_pair), rank by S descending (ties: pair index)
+    int *seq = P->alloc<int>(np);
+    {
+        std::vector<int> h(np);
+        for (int64_t p = 0; p < np; ++p) h[p] = (int)p;
+        upload(seq, h.data(), np, s);
+    }
+    uint64_t *ka = P->alloc<uint64_t>(np), *kb = P->alloc<uint64_t>(np);
+    int *o1 = P->alloc<int>(np), *porder = P->alloc<int>(np);
+    hipLaunchKernelGGL(k_desc_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, seq, P->d_S, ka);
+    sort_pairs_u64(ka, kb, seq, o1, np, s);  // by S descending, stable: ties keep pair order
+    hipLaunchKernelGGL(k_bucket_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, o1, P->d_l, P->d_pinfo, ka);
+    sort_pairs_u64(ka, kb, o1, porder, np, s);  // stable by bucket
+    int *head = P->alloc<int>(np), *hscan = P->alloc<int>(np);
+    hipLaunchKernelGGL(k_heads, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, kb, head);
+    scan_i32(head, hscan, np, s);
+    int nb_last = 0, h_last = 0;
+    HIP_CHECK(hipMemcpyAsync(&nb_last, hscan + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(&h_last, head + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    const int nbuck = nb_last + h_last;
+    int *d_bstart = P->alloc<int>(nbuck + 1);
+    uint64_t *d_bkey = P->alloc<uint64_t>(nbuck);
+    hipLaunchKernelGGL(k_bucket_table, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, kb, head, hscan, d_bstart, d_bkey);
+    std::vector<int> bstart(nbuck + 1);
+    std::vector<uint64_t> bkey(nbuck);
+    HIP_CHECK(hipMemcpyAsync(bstart.data(), d_bstart, sizeof(int) * nbuck, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(bkey.data(), d_bkey, sizeof(uint64_t) * nbuck, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    bstart[nbuck] = (int)np;
+
+    // --- blocks (bra bucket >= ket bucket), ordered by (class, K_bra, K_ket)
+    struct HB {
+        int cid, kb, kk, B, Bk;
+    };
+    std::vector<HB> hb;
+    for (int B = 0; B < nbuck; ++B)
+        for (int Bk = 0; Bk <= B; ++Bk) {
+            const int pcb = (int)(bkey[B] >> 16), pck = (int)(bkey[Bk] >> 16);
+            hb.push_back({class_id_of(pcb, pck), (int)(bkey[B] & 0xffff), (int)(bkey[Bk] & 0xffff), B, Bk});
+        }
+    std::stable_sort(hb.begin(), hb.end(), [](const HB &x, const HB &y) {
+        if (x.cid != y.cid) return x.cid < y.cid;
+        if (x.kb != y.kb) return x.kb < y.kb;
+        return x.kk < y.kk;
+    });
+    std::vector<BlockDesc> bd(hb.size());
+    int64_t nent = 0;
+    for (size_t i = 0; i < hb.size(); ++i) {
+        const int B = hb[i].B, Bk = hb[i].Bk;
+        bd[i] = BlockDesc{bstart[B], bstart[B + 1] - bstart[B], bstart[Bk], bstart[Bk + 1] - bstart[Bk], B == Bk ? 1 : 0,
+                          nent};
+        nent += bd[i].bra_n;
+    }
+    BlockDesc *d_bd = P->alloc<BlockDesc>(bd.size());
+    upload(d_bd, bd.data(), bd.size(), s);
+    int64_t *cnt = P->alloc<int64_t>(nent + 1), *off = P->alloc<int64_t>(nent + 1);
+    const double tau2 = tau * tau;
+    hipLaunchKernelGGL(k_count, dim3(nblk(nent, 256)), dim3(256), 0, s, nent, d_bd, (int)bd.size(), porder, P->d_S,
+                       tau2, cnt);
+    HIP_CHECK(hipGetLastError());
+    scan_i64(cnt, off, nent, s);
+    int64_t lo = 0, lc = 0;
+    if (nent) {
+        HIP_CHECK(hipMemcpyAsync(&lo, off + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(&lc, cnt + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+    }
+    const int64_t nq = lo + lc;
+    if (nq > (int64_t)INT32_MAX) {
+        g_last_error = "screened plan exceeds 2^31 quartets (explicit lists only in this build)";
+        throw HipFail{hipErrorInvalidValue};
+    }
+    P->nq = nq;
+    P->d_qbra = P->alloc<int>(nq);
+    P->d_qket = P->alloc<int>(nq);
+    P->d_qmap = P->alloc<int>((size_t)5 * nq);
+    int *phi = P->alloc<int>(np);
+    hipLaunchKernelGGL(k_pair_hi, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, P->d_pinfo, phi);
+    hipLaunchKernelGGL(k_fill_screened, dim3(nblk(nent, 128)), dim3(128), 0, s, nent, d_bd, (int)bd.size(), porder, cnt,
+                       off, P->d_pinfo, phi, P->d_qbra, P->d_qket, P->d_qmap);
+    HIP_CHECK(hipGetLastError());
+    // block starts -> class ranges
+    std::vector<int64_t> hbase(bd.size());
+    for (size_t i = 0; i < bd.size(); ++i) hbase[i] = bd[i].entry_base;
+    int64_t *d_idx = P->alloc<int64_t>(bd.size() + 1), *d_bs = P->alloc<int64_t>(bd.size() + 1);
+    std::vector<int64_t> bst(bd.size());
+    if (!bd.empty()) {
+        // entry_base may equal nent for an empty trailing block: clamp, fix on host
+        std::vector<int64_t> idx(bd.size());
+        for (size_t i = 0; i < bd.size(); ++i) idx[i] = std::min<int64_t>(hbase[i], nent - 1);
+        upload(d_idx, idx.data(), idx.size(), s);
+        hipLaunchKernelGGL(k_gather_i64, dim3(nblk(bd.size(), 256)), dim3(256), 0, s, (int)bd.size(), off, d_idx, d_bs);
+        HIP_CHECK(hipMemcpyAsync(bst.data(), d_bs, sizeof(int64_t) * bd.size(), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+        for (size_t i = 0; i < bd.size(); ++i)
+            if (bd[i].bra_n == 0 || hbase[i] >= nent) bst[i] = nq;
+    }
+    int64_t outp = 0;
+    std::vector<int> cids;
+    size_t i = 0;
+    while (i < hb.size()) {
+        size_t j = i;
+        while (j < hb.size() && hb[j].cid == hb[i].cid) ++j;
+        const int64_t st = bst[i];
+        const int64_t en = (j < hb.size()) ? bst[j] : nq;
+        if (en > st) {
+            const EriClassEntry *ce = find_class(hb[i].cid, P->sph);
+            if (!ce) {
+                g_last_error = "class " + std::to_string(hb[i].cid) + " not built";
+                throw HipFail{hipErrorInvalidValue};
+            }
+            EriBlock b{hb[i].cid, st, en - st, outp, nfun(ce->la, P->sph), nfun(ce->lb, P->sph),
+                       nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
+            outp += b.count * (int64_t)b.na * b.nb * b.nc * b.nd;
+            P->blocks.push_back(b);
+            cids.push_back(b.cid);
+        }
+        i = j;
+    }
+    P->nout = outp;
+    ensure_scratch(P, cids);
+    (void)hl;
+    (void)hk;
+}
+
+int translate(const HipFail &) { return ERI_E_HIP; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, double tau,
+                                  void *stream, eri_plan **plan)
+{
+    if (!plan) return ERI_E_INVALID;
+    *plan = nullptr;
+    if (!sh || sh->nshell < 1 || !sh->centers || !sh->l || !sh->nprim || !sh->prim_off || !sh->exps || !sh->coefs)
+        return ERI_E_INVALID;
+    if (flags & ~(ERI_SPHERICAL | ERI_NO_NORMALIZE)) return ERI_E_INVALID;
+    if (!(tau >= 0.0) || std::isinf(tau)) return ERI_E_INVALID;
+    if (quartets && (nq < 0 || tau != 0.0)) return ERI_E_INVALID;
+    const int ns = sh->nshell;
+    if (sh->prim_off[0] != 0) return ERI_E_INVALID;
+    for (int s = 0; s < ns; ++s) {
+        if (sh->l[s] < 0 || sh->l[s] > ERI_MAX_L) return ERI_E_INVALID;
+        if (sh->nprim[s] < 1 || sh->nprim[s] > ERI_MAX_PRIM) return ERI_E_INVALID;
+        if (sh->prim_off[s + 1] - sh->prim_off[s] != sh->nprim[s]) return ERI_E_INVALID;
+        for (int c = 0; c < 3; ++c)
+            if (!std::isfinite(sh->centers[3 * s + c])) return ERI_E_INVALID;
+        for (int k = sh->prim_off[s]; k < sh->prim_off[s + 1]; ++k)
+            if (!(sh->exps[k] > 0.0) || !std::isfinite(sh->exps[k]) || !std::isfinite(sh->coefs[k])) return ERI_E_INVALID;
+    }
+    if (quartets)
+        for (int64_t x = 0; x < 4 * nq; ++x)
+            if (quartets[x] < 0 || quartets[x] >= ns) return ERI_E_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    eri_plan *P = new (std::nothrow) eri_plan();
+    if (!P) return ERI_E_NOMEM;
+    try {
+        HIP_CHECK(hipGetDevice(&P->device));
+        P->flags = flags;
+        P->sph = (flags & ERI_SPHERICAL) != 0;
+        P->screened = quartets == nullptr;
+        P->nshell = ns;
+        P->d_boys = boys_table(P->device);
+        const int np = sh->prim_off[ns];
+        std::vector<int> hl(sh->l, sh->l + ns), hk(sh->nprim, sh->nprim + ns), hoff(sh->prim_off, sh->prim_off + ns + 1);
+        std::vector<int> hbf(ns + 1), hnf(ns);
+        hbf[0] = 0;
+        for (int i = 0; i < ns; ++i) {
+            hnf[i] = nfun(hl[i], P->sph);
+            hbf[i + 1] = hbf[i] + hnf[i];
+        }
+        P->nbf = hbf[ns];
+        P->d_cen = P->alloc<double>((size_t)3 * ns);
+        P->d_l = P->alloc<int>(ns);
+        P->d_nprim = P->alloc<int>(ns);
+        P->d_off = P->alloc<int>(ns + 1);
+        P->d_bf = P->alloc<int>(ns + 1);
+        P->d_nfun = P->alloc<int>(ns);
+        P->d_exps = P->alloc<double>(np);
+        double *d_raw = P->alloc<double>(np);
+        P->d_cn = P->alloc<double>(np);
+        upload(P->d_cen, sh->centers, (size_t)3 * ns, s);
+        upload(P->d_l, hl.data(), ns, s);
+        upload(P->d_nprim, hk.data(), ns, s);
+        upload(P->d_off, hoff.data(), ns + 1, s);
+        upload(P->d_bf, hbf.data(), ns + 1, s);
+        upload(P->d_nfun, hnf.data(), ns, s);
+        upload(P->d_exps, sh->exps, np, s);
+        upload(d_raw, sh->coefs, np, s);
+        hipLaunchKernelGGL(k_normalize, dim3(nblk(ns, 128)), dim3(128), 0, s, ns, P->d_l, P->d_nprim, P->d_off,
+                           P->d_exps, d_raw, P->d_cn, (flags & ERI_NO_NORMALIZE) ? 1 : 0);
+        HIP_CHECK(hipGetLastError());
+        if (quartets) build_explicit(P, hl, quartets, nq, s);
+        else build_screened(P, hl, hk, tau, s);
+        HIP_CHECK(hipStreamSynchronize(s));
+    } catch (const HipFail &f) {
+        delete P;
+        return translate(f);
+    } catch (const std::bad_alloc &) {
+        delete P;
+        return ERI_E_NOMEM;
+    }
+    *plan = P;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_destroy(eri_plan *plan)
+{
+    delete plan;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_info(const eri_plan *P, int64_t *nq, int64_t *nout, int32_t *nb, int32_t *nbf, int64_t *np)
+{
+    if (!P) return ERI_E_INVALID;
+    if (nq) *nq = P->nq;
+    if (nout) *nout = P->nout;
+    if (nb) *nb = (int32_t)P->blocks.size();
+    if (nbf) *nbf = P->nbf;
+    if (np) *np = P->npairs;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_blocks(const eri_plan *P, int32_t *cid, int64_t *start, int64_t *count, int64_t *out_off)
+{
+    if (!P) return ERI_E_INVALID;
+    for (size_t b = 0; b < P->blocks.size(); ++b) {
+        if (cid) cid[b] = P->blocks[b].cid;
+        if (start) start[b] = P->blocks[b].start;
+        if (count) count[b] = P->blocks[b].count;
+        if (out_off) out_off[b] = P->blocks[b].out_off;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_index_map(const eri_plan *P, int32_t *dst, void *stream)
+{
+    if (!P || (!dst && P->nq)) return ERI_E_INVALID;
+    if (!P->nq) return ERI_OK;
+    hipError_t e = hipMemcpyAsync(dst, P->d_qmap, sizeof(int) * 5 * P->nq, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
+        return ERI_E_HIP;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_schwarz(const eri_plan *P, double *dst, void *stream)
+{
+    if (!P || !dst) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    hipError_t e = hipMemcpyAsync(dst, P->d_S, sizeof(double) * P->npairs, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
+        return ERI_E_HIP;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, double *out, int64_t cap, void *stream)
+{
+    if (!P) return ERI_E_INVALID;
+    const int nb = (int)P->blocks.size();
+    if (b0 < 0 || b1 > nb || b0 > b1) return ERI_E_INVALID;
+    if (b0 == b1) return ERI_OK;
+    const int64_t base = P->blocks[b0].out_off;
+    const int64_t end = (b1 < nb) ? P->blocks[b1].out_off : P->nout;
+    if (!out || cap < end - base) return out ? ERI_E_CAPACITY : ERI_E_INVALID;
+    try {
+        for (int b = b0; b < b1; ++b) {
+            const EriBlock &B = P->blocks[b];
+            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, out + (B.out_off - base),
+                         (hipStream_t)stream);
+        }
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream)
+{
+    eri_plan *P = const_cast<eri_plan *>(Pc);
+    if (!P || !D || !J || ldd < P->nbf || ldj < P->nbf) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    hipStream_t s = (hipStream_t)stream;
+    try {
+        const int nb = (int)P->blocks.size();
+        if (!P->jready) {
+            // integral buffer, contribution buffer, and the (pair, entry) order -- built once
+            P->d_ints = P->alloc<double>((size_t)std::max<int64_t>(P->nout, 1));
+            std::vector<int64_t> cbb(nb + 1), bst(nb);
+            std::vector<int> bnab(nb), bncd(nb);
+            int64_t cbt = 0;
+            for (int b = 0; b < nb; ++b) {
+                const EriBlock &B = P->blocks[b];
+                cbb[b] = cbt;
+                bst[b] = B.start;
+                bnab[b] = B.na * B.nb;
+                bncd[b] = B.nc * B.nd;
+                cbt += B.count * (int64_t)(bnab[b] + bncd[b]);
+            }
+            P->d_cb = P->alloc<double>((size_t)std::max<int64_t>(cbt, 1));
+            int64_t *d_cbb = P->alloc<int64_t>(nb + 1), *d_bst = P->alloc<int64_t>(nb + 1);
+            int *d_bnab = P->alloc<int>(nb + 1), *d_bncd = P->alloc<int>(nb + 1), *d_blk_of = P->alloc<int>(P->nq + 1);
+            upload(d_cbb, cbb.data(), nb, s);
+            upload(d_bst, bst.data(), nb, s);
+            upload(d_bnab, bnab.data(), nb, s);
+            upload(d_bncd, bncd.data(), nb, s);
+            for (int b = 0; b < nb; ++b)
+                hipLaunchKernelGGL(k_fill_blk_of, dim3(nblk(P->blocks[b].count, 256)), dim3(256), 0, s,
+                                   P->blocks[b].start, P->blocks[b].count, b, d_blk_of);
+            const int64_t ne = 2 * P->nq;
+            int *ek = P->alloc<int>(ne + 1), *ek2 = P->alloc<int>(ne + 1);
+            int64_t *eo = P->alloc<int64_t>(ne + 1);
+            P->d_eoff = P->alloc<int64_t>(ne + 1);
+            hipLaunchKernelGGL(k_entries, dim3(nblk(P->nq, 256)), dim3(256), 0, s, P->nq, P->d_qbra, P->d_qket, d_cbb,
+                               d_blk_of, d_bst, d_bnab, d_bncd, ek, eo, nullptr);
+            HIP_CHECK(hipGetLastError());
+            sort_pairs_i32(ek, ek2, eo, P->d_eoff, ne, s);
+            P->d_seg = P->alloc<int64_t>(P->npairs + 1);
+            hipLaunchKernelGGL(k_seg_starts, dim3(nblk(P->npairs + 1, 256)), dim3(256), 0, s, (int)P->npairs, ne, ek2,
+                               P->d_seg);
+            HIP_CHECK(hipGetLastError());
+            HIP_CHECK(hipStreamSynchronize(s));
+            P->jready = true;
+        }
+        // 1. integrals of every block
+        for (int b = 0; b < nb; ++b) {
+            const EriBlock &B = P->blocks[b];
+            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, s);
+        }
+        // 2. per-quartet contributions
+        int64_t cbt = 0;
+        for (int b = 0; b < nb; ++b) {
+            const EriBlock &B = P->blocks[b];
+            const int64_t CH = 1 << 30;
+            for (int64_t c = 0; c < B.count; c += CH) {
+                const int64_t m = std::min(CH, B.count - c);
+                const int64_t nab = B.na * B.nb, ncd = B.nc * B.nd;
+                hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd,
+                                   P->d_qbra + B.start + c, P->d_qket + B.start + c, P->d_pinfo, P->d_bf,
+                                   P->d_ints + B.out_off + c * nab * ncd, D, ldd, P->d_cb + cbt + c * (nab + ncd));
+                HIP_CHECK(hipGetLastError());
+            }
+            cbt += B.count * (int64_t)(B.na * B.nb + B.nc * B.nd);
+        }
+        // 3. deterministic per-pair reduction into J
+        hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(64), 0, s, (int)P->npairs, P->d_pinfo,
+                           P->d_bf, P->d_nfun, P->d_seg, P->d_eoff, P->d_cb, J, ldj);
+        HIP_CHECK(hipGetLastError());
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" const char *eri_strerror(int code)
+{
+    switch (code) {
+    case ERI_OK: return "ok";
+    case ERI_E_INVALID: return "invalid argument";
+    case ERI_E_UNSUPPORTED: return "unsupported request";
+    case ERI_E_CAPACITY: return "output buffer too small";
+    case ERI_E_HIP: {
+        static thread_local std::string msg;
+        msg = "HIP error: " + g_last_error;
+        return msg.c_str();
+    }
+    case ERI_E_NOMEM: return "device allocation failed";
+    default: return "unknown error code";
+    }
+}
+
+extern "C" int eri_class_info(int32_t cid, int32_t *l4, int32_t *tier)
+{
+    const EriClassEntry *ce = find_class(cid, true);
+    if (!ce) return ERI_E_INVALID;
+    if (l4) {
+        l4[0] = ce->la;
+        l4[1] = ce->lb;
+        l4[2] = ce->lc;
+        l4[3] = ce->ld;
+    }
+    if (tier) *tier = ce->tier;
+    return ERI_OK;
+}

@@ -1,0 +1,543 @@
+"""Emit one HIP source per angular-momentum class (register tier and memory tier).
+
+Both tiers share the algorithm of graph.py; they differ in where values live:
+
+* register tier ("V"): the whole quartet lives in VGPRs of a lane group of
+  G = #{e : |e| <= la+lb} lanes inside one wave64; floor(64/G) quartets per
+  wave.  The coupling operand is read from lane e-1_i with ds_bpermute.  The
+  ket results are handed from "lane owns e" to "lane owns ket component"
+  through one LDS transpose per quartet.
+* memory tier ("M"): for classes whose lane group exceeds a wave or whose live
+  set exceeds the register budget.  One workgroup per quartet, lane = e; every
+  graph value lives in a per-workgroup slice of a global scratch buffer,
+  interleaved so that lanes of a wave touch consecutive doubles.  Slots are
+  reused once a value is dead (two-pass lifetime allocation, as the page's
+  Tier 2 kernel does with its global buffer), and workgroup barriers separate
+  the ket levels because the coupling operand may belong to another wave.
+"""
+from __future__ import annotations
+
+import os
+
+from .cartesian import components, components_upto, sub, add, ncart, nsph, comp_index
+from .graph import (ClassInfo, build_ket_vrr, build_hrr, transform_terms, class_id, ket_vrr_peak_live)
+
+AX = "xyz"
+
+
+def _fmt(v: float) -> str:
+    r = repr(float(v))
+    if "e" not in r and "." not in r and "inf" not in r and "nan" not in r:
+        r += ".0"
+    return r
+
+
+# ---------------------------------------------------------------------------
+# value naming helpers
+# ---------------------------------------------------------------------------
+
+class Names:
+    """Maps graph values to C expressions for a given storage tier."""
+
+    def __init__(self, tier, kv, Lk, slot_of=None):
+        self.tier = tier
+        self.fpos = {f: i for i, f in enumerate(components_upto(max(Lk, 0)))}
+        self.slot_of = slot_of or {}
+
+    def ket(self, node):
+        f, m = node
+        if sum(f) == 0:
+            return f"s1_{m}"
+        if self.tier == "V":
+            return f"v{self.fpos[f]}_{m}"
+        return f"SC({self.slot_of[('k', f, m)]})"
+
+    def ket_remote(self, node, axis):
+        f, m = node
+        if self.tier == "V":
+            return f"eri_bperm(ad{AX[axis]}, {self.ket(node)})"
+        if sum(f) == 0:
+            raise AssertionError("remote base values are read from the remote lane's own stage-1 copy")
+        return f"SCR({self.slot_of[('k', f, m)]}, src{AX[axis]})"
+
+
+# ---------------------------------------------------------------------------
+# slot allocation for the memory tier
+# ---------------------------------------------------------------------------
+
+def _alloc_slots(kv):
+    """Level-granular lifetime packing of the ket-phase values.
+
+    A value produced at level k is read at levels k+1 (own and coupling) and
+    k+2 (the f-2_i term).  Slots are released only at level boundaries so that
+    the barrier between levels also orders every read before any reuse.
+    """
+    level_of = {}
+    last_level = {}
+    for n in kv.nodes:
+        k = sum(n.f)
+        level_of[(n.f, n.m)] = k
+        for p in (n.a0, n.a1, n.b0, n.b1):
+            if p is not None and sum(p[0]) > 0:
+                last_level[p] = max(last_level.get(p, 0), k)
+    # targets are accumulated at the level they are produced
+    for t in kv.targets:
+        if sum(t[0]) > 0:
+            last_level[t] = max(last_level.get(t, 0), level_of[t])
+    slot_of = {}
+    free = []
+    nslots = 0
+    by_level = {}
+    for n in kv.nodes:
+        by_level.setdefault(sum(n.f), []).append((n.f, n.m))
+    release_at = {}
+    for v, lv in last_level.items():
+        release_at.setdefault(lv, []).append(v)
+    for k in sorted(by_level):
+        for v in by_level[k]:
+            if free:
+                s = free.pop()
+            else:
+                s = nslots
+                nslots += 1
+            slot_of[("k",) + v] = s
+        # values whose last use is at level k free their slot for level k+1
+        for v in release_at.get(k, []):
+            free.append(slot_of[("k",) + v])
+        free.sort(reverse=True)
+    return slot_of, nslots
+
+
+# ---------------------------------------------------------------------------
+# code pieces
+# ---------------------------------------------------------------------------
+
+def _stage1(ci: ClassInfo, base_m: int, lines, ind="      "):
+    """Bra phase for the lane's own e: [e0|00]^(m), m = 0..base_m, from F_m."""
+    L = ci.L
+    for m in range(L + 1):
+        lines.append(f"{ind}double c{m} = F[{m}];")
+    if ci.Lb == 0:
+        for m in range(base_m + 1):
+            lines.append(f"{ind}const double s1_{m} = c{m};")
+        return
+    for m in range(L + 1):
+        lines.append(f"{ind}double p{m} = 0.0;")
+    for s in range(1, ci.Lb + 1):
+        top = L - s
+        lines.append(f"{ind}{{ // bra step {s}")
+        lines.append(f"{ind}  const int ax = ({s} <= ex) ? 0 : ({s} <= ex + ey) ? 1 : ({s} <= es) ? 2 : 3;")
+        lines.append(f"{ind}  const double g1 = ax == 0 ? PAx : ax == 1 ? PAy : ax == 2 ? PAz : 1.0;")
+        lines.append(f"{ind}  const double g2 = ax == 0 ? WPx : ax == 1 ? WPy : ax == 2 ? WPz : 0.0;")
+        lines.append(f"{ind}  const double gn = (double)(ax == 0 ? {s - 1} : ax == 1 ? {s - 1} - ex : ax == 2 ? {s - 1} - ex - ey : 0) * i2z;")
+        for m in range(top + 1):
+            lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1} + gn * (p{m} - roz * p{m + 1});")
+        for m in range(top + 1):
+            lines.append(f"{ind}  p{m} = c{m}; c{m} = n{m};")
+        lines.append(f"{ind}}}")
+    for m in range(base_m + 1):
+        lines.append(f"{ind}const double s1_{m} = c{m};")
+
+
+def _ket_phase(kv, names: Names, lines, ind="      ", barrier=None, acc_now=None):
+    """Ket phase of Eq. (2) in node order.  ``acc_now`` maps a target node to
+    the accumulator it is added to immediately (memory tier: before its slot
+    can be reused at a later level)."""
+    prev_level = None
+    for n in kv.nodes:
+        lvl = sum(n.f)
+        if barrier and prev_level is not None and lvl != prev_level:
+            lines.append(f"{ind}{barrier}")
+        prev_level = lvl
+        a = AX[n.axis]
+        expr = f"QC{a} * {names.ket(n.a0)} + WQ{a} * {names.ket(n.a1)}"
+        if n.b0 is not None:
+            expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+        if names.tier == "V" or sum(n.a1[0]) > 0:
+            expr += f" + eh{a} * {names.ket_remote(n.a1, n.axis)}"
+        else:
+            # memory tier, coupling to the remote lane's bra-phase value
+            expr += f" + eh{a} * S1R({n.a1[1]}, src{a})"
+        tgt = names.ket((n.f, n.m))
+        if names.tier == "V":
+            lines.append(f"{ind}const double {tgt} = {expr};")
+        else:
+            lines.append(f"{ind}{tgt} = {expr};")
+        if acc_now is not None and (n.f, n.m) in acc_now:
+            lines.append(f"{ind}{acc_now[(n.f, n.m)]} += {tgt};")
+
+
+def _hrr_block(l1, l2, base_expr, R, out_prefix, spherical, lines, ind="  ", decl="double"):
+    """HRR (x, y) from base (e, 0) then optional transform of y then x.
+
+    base_expr(e) -> C expression of the base value (e, 0).  R is the name prefix
+    of the centre difference (ABx.. or CDx..).  Emits variables
+    {out_prefix}{k} for output index k (row-major x, y; spherical or Cartesian).
+    Returns the number of outputs.
+    """
+    nodes, base = build_hrr(l1, l2)
+    name = {}
+    for e in base:
+        name[(e, (0, 0, 0))] = base_expr(e)
+    for i, n in enumerate(nodes):
+        nm = f"{out_prefix}h{i}"
+        hi, lo = name[n.p_hi], name[n.p_lo]
+        lines.append(f"{ind}const double {nm} = {hi} + {R}{AX[n.axis]} * {lo};")
+        name[(n.x, n.y)] = nm
+    xs, ys = components(l1), components(l2)
+    outs = []
+    if not spherical:
+        for x in xs:
+            for y in ys:
+                outs.append(name[(x, y)])
+    else:
+        Ty, Tx = transform_terms(l2), transform_terms(l1)
+        # y first
+        mid = {}
+        for xi, x in enumerate(xs):
+            for si, row in enumerate(Ty):
+                terms = [f"{_fmt(c)} * {name[(x, ys[yi])]}" for yi, c in row]
+                nm = f"{out_prefix}t{xi}_{si}"
+                lines.append(f"{ind}const double {nm} = {' + '.join(terms)};")
+                mid[(xi, si)] = nm
+        for li, row in enumerate(Tx):
+            for si in range(nsph(l2)):
+                terms = [f"{_fmt(c)} * {mid[(xi, si)]}" for xi, c in row]
+                nm = f"{out_prefix}u{li}_{si}"
+                lines.append(f"{ind}const double {nm} = {' + '.join(terms)};")
+                outs.append(nm)
+    for k, nm in enumerate(outs):
+        lines.append(f"{ind}{decl} {out_prefix}{k} = {nm};")
+    return len(outs)
+
+
+# ---------------------------------------------------------------------------
+# register tier
+# ---------------------------------------------------------------------------
+
+def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    names = Names("V", kv, ci.Lk)
+    G = ci.G
+    Q = 64 // G
+    NK = ci.nket(spherical)
+    NEB = ci.n_ebra
+    EOFF = ci.e_bra_offset
+    BLK = ci.nout(spherical)
+    cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+    tag = f"c{cid}_{'s' if spherical else 'c'}"
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    tx = [e[0] for e in lanes]
+    ty = [e[1] for e in lanes]
+    tz = [e[2] for e in lanes]
+    dx = [lpos[sub(e, 0)] if e[0] > 0 else -1 for e in lanes]
+    dy = [lpos[sub(e, 1)] if e[1] > 0 else -1 for e in lanes]
+    dz = [lpos[sub(e, 2)] if e[2] > 0 else -1 for e in lanes]
+    targets = kv.targets
+    L = ci.L
+
+    o = []
+    o.append(f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {cid}, {'spherical' if spherical else 'Cartesian'} output,"
+             f" register tier: {G} lanes per quartet, {Q} quartets per wave")
+    o.append('#include "eri_device.h"')
+    o.append("namespace {")
+    o.append(f"__constant__ signed char k_{tag}_lane[4][{G}] = {{")
+    for arr in (tx, ty, tz):
+        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
+    o.append("  {0}};")
+    o.append(f"__constant__ signed char k_{tag}_down[3][{G}] = {{")
+    for arr in (dx, dy, dz):
+        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
+    o.append("};")
+    o.append("}  // namespace")
+    o.append("")
+    o.append(f"__global__ void __launch_bounds__(64) eri_kernel_{tag}(EriClassArgs a)")
+    o.append("{")
+    o.append(f"  constexpr int G = {G}, Q = {Q}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
+    o.append("  __shared__ double xch[Q * NEB * NK];")
+    o.append("  const int lane = threadIdx.x;")
+    o.append("  int grp = lane / G, sub = lane - grp * G;")
+    o.append("  if (grp >= Q) { grp = Q; sub = 0; }  // padding lanes: phantom group, e = (0,0,0)")
+    o.append("  const int q0 = blockIdx.x * Q;")
+    o.append("  int qs = q0 + (grp < Q ? grp : 0);")
+    o.append("  if (qs >= a.nq) qs = a.nq - 1;  // idle groups recompute the last quartet and never store")
+    o.append(f"  const int ex = k_{tag}_lane[0][sub], ey = k_{tag}_lane[1][sub], ez = k_{tag}_lane[2][sub];")
+    o.append("  const int es = ex + ey + ez;")
+    o.append("  const int gb = grp * G;")
+    o.append(f"  const int adx = (ex > 0 ? gb + k_{tag}_down[0][sub] : lane) * 4;")
+    o.append(f"  const int ady = (ey > 0 ? gb + k_{tag}_down[1][sub] : lane) * 4;")
+    o.append(f"  const int adz = (ez > 0 ? gb + k_{tag}_down[2][sub] : lane) * 4;")
+    o.append("  (void)adx; (void)ady; (void)adz;")
+    o.append("  const int bra = a.qbra[qs], ket = a.qket[qs];")
+    o.append("  const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
+    o.append("  const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
+    o.append("  const double CDx = Cx - a.cen[3 * pk.y], CDy = Cy - a.cen[3 * pk.y + 1], CDz = Cz - a.cen[3 * pk.y + 2];")
+    o.append("  const double ACx = a.cen[3 * pb.x] - Cx, ACy = a.cen[3 * pb.x + 1] - Cy, ACz = a.cen[3 * pb.x + 2] - Cz;")
+    o.append("  (void)CDx; (void)CDy; (void)CDz;")
+    for t in range(len(targets)):
+        o.append(f"  double acc{t} = 0.0;")
+    o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
+    o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
+    o.append("    for (int ik = 0; ik < pk.w; ++ik) {")
+    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
+    o.append("      EriQuartetGeom g;")
+    o.append("      eri_geom(P, K, ACx, ACy, ACz, g);")
+    o.append("      const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
+    o.append("      const double WPx = g.WP[0], WPy = g.WP[1], WPz = g.WP[2];")
+    o.append("      const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
+    o.append("      const double WQx = g.WQ[0], WQy = g.WQ[1], WQz = g.WQ[2];")
+    o.append("      const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = g.roz, roe = g.roe;")
+    o.append("      const double ehx = ex * g.i2ze, ehy = ey * g.i2ze, ehz = ez * g.i2ze;")
+    o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+    o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+    o.append(f"      double F[{L + 1}];")
+    o.append(f"      eri_boys<{L}>(g.T, g.pref, a.boys, F);")
+    _stage1(ci, kv.base_m, o)
+    _ket_phase(kv, names, o)
+    for t, (f, m) in enumerate(targets):
+        o.append(f"      acc{t} += {names.ket((f, m))};")
+    o.append("    }")
+    o.append("  }")
+    # H1: ket HRR + transform per lane
+    tpos = {f: t for t, (f, m) in enumerate(targets)}
+    nk = _hrr_block(ci.lc, ci.ld, lambda e: f"acc{tpos[e]}", "CD", "y", spherical, o, "  ")
+    assert nk == NK
+    o.append(f"  if (grp < Q && es >= {ci.la}) {{")
+    o.append(f"    double* dst = xch + (grp * NEB + (sub - {EOFF})) * NK;")
+    for k in range(NK):
+        o.append(f"    dst[{k}] = y{k};")
+    o.append("  }")
+    o.append("  __syncthreads();")
+    # H2: lanes own ket components
+    o.append("  for (int t = lane; t < Q * NK; t += 64) {")
+    o.append("    const int g2 = t / NK, kap = t - g2 * NK;")
+    o.append("    const int slot = q0 + g2;")
+    o.append("    if (slot >= a.nq) continue;")
+    o.append("    const int4 pb2 = a.pair_info[a.qbra[slot]];")
+    o.append("    const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
+             " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
+    o.append("    (void)ABx; (void)ABy; (void)ABz;")
+    o.append("    const double* src = xch + g2 * NEB * NK + kap;")
+    ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
+    epos = {e: i for i, e in enumerate(ebra)}
+    for i, e in enumerate(ebra):
+        o.append(f"    const double xe{i} = src[{i} * NK];")
+    nb = _hrr_block(ci.la, ci.lb, lambda e: f"xe{epos[e]}", "AB", "z", spherical, o, "    ")
+    o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
+    for k in range(nb):
+        o.append(f"    dst[{k} * NK] = z{k};")
+    o.append("  }")
+    o.append("}")
+    o.append("")
+    o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
+    o.append("{")
+    o.append(f"  const int nblk = (a.nq + {Q} - 1) / {Q};")
+    o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3(64), 0, s, a);")
+    o.append("}")
+    return "\n".join(o) + "\n"
+
+
+def tier_of(ci: ClassInfo) -> str:
+    """Register tier when a lane group fits one wave and the live set is modest."""
+    if ci.G > 64:
+        return "M"
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    est = ket_vrr_peak_live(kv) + len(kv.targets) + 2 * (ci.L + 1) + 30
+    return "V" if est <= 120 else "M"
+
+
+def generate(out_dir: str, lmax: int = 4, classes=None):
+    """Write one .hip per (class, output kind) plus the dispatch table."""
+    from .graph import all_classes
+    os.makedirs(out_dir, exist_ok=True)
+    cls = classes if classes is not None else all_classes(lmax)
+    entries = []
+    files = []
+    for ci in cls:
+        tier = tier_of(ci)
+        for spherical in (False, True):
+            if tier == "V":
+                src = emit_register_tier(ci, spherical)
+            else:
+                src = emit_memory_tier(ci, spherical)
+            cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+            tag = f"c{cid}_{'s' if spherical else 'c'}"
+            fn = os.path.join(out_dir, f"eri_{tag}.hip")
+            _write_if_changed(fn, src)
+            files.append(fn)
+            entries.append((cid, spherical, tag, tier, ci))
+    # dispatch
+    d = ['#include "eri_device.h"', ""]
+    for cid, sph, tag, tier, ci in entries:
+        d.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s);")
+    d.append("")
+    d.append("EriClassEntry eri_class_table[] = {")
+    for cid, sph, tag, tier, ci in entries:
+        scr = memory_tier_scratch_doubles(ci, sph) if tier == "M" else 0
+        d.append(f"  {{{cid}, {1 if sph else 0}, {ci.la}, {ci.lb}, {ci.lc}, {ci.ld}, '{tier}', {scr}, eri_launch_{tag}}},")
+    d.append("};")
+    d.append(f"const int eri_class_table_size = {len(entries)};")
+    fn = os.path.join(out_dir, "eri_dispatch.hip")
+    _write_if_changed(fn, "\n".join(d) + "\n")
+    files.append(fn)
+    return files, entries
+
+
+def _write_if_changed(fn, text):
+    if os.path.exists(fn):
+        with open(fn) as f:
+            if f.read() == text:
+                return
+    with open(fn, "w") as f:
+        f.write(text)
+
+
+# ---------------------------------------------------------------------------
+# memory tier
+# ---------------------------------------------------------------------------
+
+def _mem_layout(ci: ClassInfo, spherical: bool):
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    slot_of, nk_slots = _alloc_slots(kv)
+    ntg = len(kv.targets)
+    # layout (in units of W doubles): [ket slots][acc][exchange NK]
+    acc0 = nk_slots
+    xch0 = acc0 + ntg
+    nslots = xch0 + ci.nket(spherical)
+    W = 64 * ((ci.G + 63) // 64)
+    return kv, slot_of, acc0, xch0, nslots, W
+
+
+def memory_tier_scratch_doubles(ci: ClassInfo, spherical: bool) -> int:
+    """Scratch doubles per workgroup: graph slots x lanes + the bra-phase copy."""
+    kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
+    return nslots * W + (kv.base_m + 1) * W
+
+
+def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
+    kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
+    names = Names("M", kv, ci.Lk, slot_of)
+    G = ci.G
+    NK = ci.nket(spherical)
+    NEB = ci.n_ebra
+    EOFF = ci.e_bra_offset
+    BLK = ci.nout(spherical)
+    cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+    tag = f"c{cid}_{'s' if spherical else 'c'}"
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    tx = [e[0] for e in lanes]
+    ty = [e[1] for e in lanes]
+    tz = [e[2] for e in lanes]
+    dx = [lpos[sub(e, 0)] if e[0] > 0 else -1 for e in lanes]
+    dy = [lpos[sub(e, 1)] if e[1] > 0 else -1 for e in lanes]
+    dz = [lpos[sub(e, 2)] if e[2] > 0 else -1 for e in lanes]
+    targets = kv.targets
+    L = ci.L
+    S1 = nslots  # bra-phase copy rows start here (base_m + 1 rows)
+    o = []
+    o.append(f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {cid}, {'spherical' if spherical else 'Cartesian'} output,"
+             f" memory tier: {G} lanes (workgroup {W}) per quartet, {nslots} scratch slots")
+    o.append('#include "eri_device.h"')
+    o.append("namespace {")
+    o.append(f"__constant__ short k_{tag}_lane[3][{G}] = {{")
+    for arr in (tx, ty, tz):
+        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
+    o.append("};")
+    o.append(f"__constant__ short k_{tag}_down[3][{G}] = {{")
+    for arr in (dx, dy, dz):
+        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
+    o.append("};")
+    o.append("}  // namespace")
+    o.append("")
+    o.append(f"__global__ void __launch_bounds__({W}) eri_kernel_{tag}(EriClassArgs a)")
+    o.append("{")
+    o.append(f"  constexpr int G = {G}, W = {W}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
+    o.append(f"  constexpr size_t WG_DOUBLES = {memory_tier_scratch_doubles(ci, spherical)};")
+    o.append("  const int tid = threadIdx.x;")
+    o.append("  const int sub = tid < G ? tid : 0;  // lanes beyond G shadow e = (0,0,0) and never store")
+    o.append("  const bool real = tid < G;")
+    o.append("  double* __restrict__ scr = a.scratch + (size_t)blockIdx.x * WG_DOUBLES;")
+    o.append("#define SC(s) scr[(size_t)(s) * W + tid]")
+    o.append("#define SCR(s, l) scr[(size_t)(s) * W + (l)]")
+    o.append(f"#define S1R(m, l) scr[(size_t)({S1} + (m)) * W + (l)]")
+    o.append(f"  const int ex = k_{tag}_lane[0][sub], ey = k_{tag}_lane[1][sub], ez = k_{tag}_lane[2][sub];")
+    o.append("  const int es = ex + ey + ez;")
+    o.append(f"  const int srcx = ex > 0 ? k_{tag}_down[0][sub] : tid;")
+    o.append(f"  const int srcy = ey > 0 ? k_{tag}_down[1][sub] : tid;")
+    o.append(f"  const int srcz = ez > 0 ? k_{tag}_down[2][sub] : tid;")
+    o.append("  (void)srcx; (void)srcy; (void)srcz; (void)real;")
+    o.append("  for (int qs = blockIdx.x; qs < a.nq; qs += gridDim.x) {")
+    o.append("  const int bra = a.qbra[qs], ket = a.qket[qs];")
+    o.append("  const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
+    o.append("  const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
+    o.append("  const double CDx = Cx - a.cen[3 * pk.y], CDy = Cy - a.cen[3 * pk.y + 1], CDz = Cz - a.cen[3 * pk.y + 2];")
+    o.append("  const double ACx = a.cen[3 * pb.x] - Cx, ACy = a.cen[3 * pb.x + 1] - Cy, ACz = a.cen[3 * pb.x + 2] - Cz;")
+    o.append("  (void)CDx; (void)CDy; (void)CDz;")
+    for t in range(len(targets)):
+        o.append(f"  SC({acc0 + t}) = 0.0;")
+    o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
+    o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
+    o.append("    for (int ik = 0; ik < pk.w; ++ik) {")
+    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
+    o.append("      EriQuartetGeom g;")
+    o.append("      eri_geom(P, K, ACx, ACy, ACz, g);")
+    o.append("      const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
+    o.append("      const double WPx = g.WP[0], WPy = g.WP[1], WPz = g.WP[2];")
+    o.append("      const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
+    o.append("      const double WQx = g.WQ[0], WQy = g.WQ[1], WQz = g.WQ[2];")
+    o.append("      const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = g.roz, roe = g.roe;")
+    o.append("      const double ehx = ex * g.i2ze, ehy = ey * g.i2ze, ehz = ez * g.i2ze;")
+    o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+    o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+    o.append(f"      double F[{L + 1}];")
+    o.append(f"      eri_boys<{L}>(g.T, g.pref, a.boys, F);")
+    _stage1(ci, kv.base_m, o)
+    # publish the bra-phase values for remote reads, then barrier
+    for m in range(kv.base_m + 1):
+        o.append(f"      S1R({m}, tid) = s1_{m};")
+    o.append("      __syncthreads();")
+    acc_now = {tg: f"SC({acc0 + t})" for t, tg in enumerate(targets) if sum(tg[0]) > 0}
+    for t, tg in enumerate(targets):
+        if sum(tg[0]) == 0:
+            o.append(f"      SC({acc0 + t}) += {names.ket(tg)};")
+    _ket_phase(kv, names, o, barrier="__syncthreads();", acc_now=acc_now)
+    o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
+    o.append("    }")
+    o.append("  }")
+    # H1 per lane, reading the accumulators
+    tpos = {f: t for t, (f, m) in enumerate(targets)}
+    nk = _hrr_block(ci.lc, ci.ld, lambda e: f"SC({acc0 + tpos[e]})", "CD", "y", spherical, o, "  ")
+    assert nk == NK
+    o.append(f"  if (real && es >= {ci.la}) {{")
+    for k in range(NK):
+        o.append(f"    SC({xch0 + k}) = y{k};")
+    o.append("  }")
+    o.append("  __syncthreads();")
+    o.append("  const int4 pb2 = a.pair_info[bra];")
+    o.append("  const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
+             " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
+    o.append("  (void)ABx; (void)ABy; (void)ABz;")
+    o.append("  for (int kap = tid; kap < NK; kap += W) {")
+    ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
+    epos = {e: i for i, e in enumerate(ebra)}
+    o.append(f"    const double* srcp = scr + (size_t)({xch0} + kap) * W + {EOFF};")
+    nb = _hrr_block(ci.la, ci.lb, lambda e: f"srcp[{epos[e]}]", "AB", "z", spherical, o, "    ")
+    o.append("    double* dst = a.out + (size_t)qs * BLK + kap;")
+    for k in range(nb):
+        o.append(f"    dst[{k} * NK] = z{k};")
+    o.append("  }")
+    o.append("  __syncthreads();  // exchange slots are reused by the next quartet")
+    o.append("  }")
+    o.append("#undef SC")
+    o.append("#undef SCR")
+    o.append("#undef S1R")
+    o.append("}")
+    o.append("")
+    o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
+    o.append("{")
+    o.append("  const int nblk = a.nq < a.scratch_wgs ? a.nq : a.scratch_wgs;")
+    o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3({W}), 0, s, a);")
+    o.append("}")
+    return "\n".join(o) + "\n"

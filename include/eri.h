@@ -1,0 +1,148 @@
+/*
+ * eri.h -- C ABI of the MI355X (gfx950) four-centre ERI engine.
+ *
+ * What is computed (source: "FusionRCG: Orchestrating Recursive Computation
+ * Graphs across GPU Memory Hierarchies", Wei et al.):
+ *   - contracted electron repulsion integrals (ab|cd) over Cartesian Gaussian
+ *     shells, Eq. (1) of section II-A, evaluated by the two-phase recurrence of
+ *     section II-A (vertical recurrence Eq. (2) from Boys values, contraction
+ *     over primitive quartets as in Algorithm 2 of section III-C, horizontal
+ *     recurrence Eq. (3));
+ *   - optionally in the real spherical basis, Eq. (8) of section III-B, with
+ *     the transform applied index by index inside the horizontal phase
+ *     (stepwise fusion, Eqs. (11)-(16), identical to Eq. (17));
+ *   - the Coulomb matrix J_mu,nu = sum_(la,si) (mu nu|la si) D_la,si that
+ *     Algorithm 2 scatters (line 10), using the 8-fold permutation symmetry of
+ *     section III-C2 (Kernel 2) over Schwarz-screened unique quartets.
+ *
+ * Conventions (not fixed by the page; chosen and documented here):
+ *   - Cartesian components of a shell with angular momentum l are ordered
+ *     x-power descending, then y-power descending (d: xx xy xz yy yz zz).
+ *   - Every Cartesian component of a primitive carries the factor
+ *     N(alpha,l) = (2 alpha/pi)^(3/4) (4 alpha)^(l/2) / sqrt((2l-1)!!); the
+ *     contracted x^l component is then scaled to unit norm.  ERI_NO_NORMALIZE
+ *     uses the raw coefficients on raw monomials instead.
+ *   - Spherical components are real solid harmonics without Condon-Shortley
+ *     phase, m = -l..l (a p shell comes out as y, z, x), orthonormal for the
+ *     normalised shell, leading monomial positive.
+ *   - A block (ab|cd) is stored row-major over (a, b, c, d).
+ *   - Basis functions of the J/D matrices are numbered shell by shell in the
+ *     order of the shell arrays, components contiguous within a shell.
+ *   - Quartet classes: pair class pc(la,lb) = la(la+1)/2 + lb (la >= lb),
+ *     class id = pcb(pcb+1)/2 + pck with pcb >= pck; 120 classes for l <= 4.
+ *   - Canonical quartet: swap a<->b if l_a < l_b (bit 0 of perm), c<->d if
+ *     l_c < l_d (bit 1), then bra<->ket if pc(bra) < pc(ket) (bit 2).  Blocks
+ *     are produced for the canonical quartet; the index map records it.
+ *
+ * Memory and errors: every pointer argument is a host pointer unless marked
+ * "device".  A plan owns the device memory it allocates (hipMalloc) until
+ * eri_plan_destroy.  All device work is enqueued on `stream` (a hipStream_t,
+ * NULL = default stream); calls that must return a count computed on the
+ * device synchronise that stream and say so.  Every function returns ERI_OK
+ * or a negative error code and never throws; arguments are validated before
+ * anything is launched.  Results are deterministic: the same inputs on the
+ * same device give bitwise-identical outputs (no floating-point atomics).
+ */
+#ifndef ERI_MI355X_H
+#define ERI_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ERI_OK 0
+#define ERI_E_INVALID (-1)     /* malformed argument (index out of range, l > 4, K < 1, ...) */
+#define ERI_E_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define ERI_E_CAPACITY (-3)    /* caller buffer smaller than the plan requires */
+#define ERI_E_HIP (-4)         /* a HIP runtime call failed; see eri_strerror */
+#define ERI_E_NOMEM (-5)       /* device allocation failed */
+
+#define ERI_SPHERICAL 1    /* output in the real spherical basis */
+#define ERI_NO_NORMALIZE 2 /* raw coefficients on raw monomials */
+
+#define ERI_MAX_L 4
+#define ERI_MAX_PRIM 15
+
+/* Shells as structure-of-arrays, all host memory, copied by the library. */
+typedef struct eri_shells {
+    int32_t nshell;
+    const double *centers;   /* [3*nshell], bohr */
+    const int32_t *l;        /* [nshell], 0..ERI_MAX_L */
+    const int32_t *nprim;    /* [nshell], 1..ERI_MAX_PRIM */
+    const int32_t *prim_off; /* [nshell+1], CSR offsets into exps/coefs, prim_off[0] = 0 */
+    const double *exps;      /* [prim_off[nshell]], > 0 */
+    const double *coefs;     /* [prim_off[nshell]], raw contraction coefficients */
+} eri_shells;
+
+typedef struct eri_plan eri_plan;
+
+/*
+ * Build a quartet plan (section III-C batching by angular-momentum class).
+ *   quartets != NULL: explicit list of nq quartets [4*nq] (host) of shell
+ *     indices; each is canonicalised and the list is ordered by
+ *     (class id, K_a K_b, K_c K_d, input position).  tau must be 0.
+ *   quartets == NULL: all unique quartets (pair(ij) >= pair(kl), i >= j,
+ *     k >= l) that pass the Schwarz test fl(S_ij * S_kl) >= fl(tau * tau),
+ *     with S_ij = max |(mu nu|mu nu)| over the (ij|ij) block computed on the
+ *     device by the same class kernels (tau = 0 keeps every quartet).  Pairs
+ *     are bucketed by (pair class, K_pair) and ranked by S descending (ties by
+ *     pair index); order (class id, K_bra, K_ket, bra rank, ket rank).
+ * Synchronises `stream` (quartet counts are needed on the host).
+ * On success *plan receives a new plan.
+ */
+int eri_build_quartets(const eri_shells *shells, int flags, const int32_t *quartets, int64_t nq,
+                       double tau, void *stream, eri_plan **plan);
+
+/* Free a plan and its device memory (NULL is allowed). */
+int eri_plan_destroy(eri_plan *plan);
+
+/* Sizes: quartets, output doubles of all blocks, number of class blocks,
+ * basis functions (spherical or Cartesian per the plan's flags), shell pairs. */
+int eri_plan_info(const eri_plan *plan, int64_t *n_quartets, int64_t *n_out_doubles, int32_t *n_blocks,
+                  int32_t *nbf, int64_t *n_pairs);
+
+/* Per class block b (host arrays of n_blocks): class id, first plan slot,
+ * number of quartets, offset (doubles) of its first block in the output. */
+int eri_plan_blocks(const eri_plan *plan, int32_t *class_id, int64_t *start, int64_t *count,
+                    int64_t *out_offset);
+
+/* Index map of the plan: dst[5*slot + 0..3] = shells (a, b, c, d) of the
+ * canonical quartet computed in that slot, dst[5*slot + 4] = perm bits.  dst
+ * is device memory [5*n_quartets]; asynchronous on `stream`. */
+int eri_plan_index_map(const eri_plan *plan, int32_t *dst, void *stream);
+
+/* Schwarz factors S[pair] for pair index i(i+1)/2 + j (screened plans only);
+ * dst is device memory [n_pairs]; asynchronous on `stream`. */
+int eri_plan_schwarz(const eri_plan *plan, double *dst, void *stream);
+
+/*
+ * Integrals of class blocks [block_begin, block_end) into `out` (device),
+ * block b's quartets starting at out + out_offset[b] - out_offset[block_begin].
+ * out_capacity is the number of doubles available at `out`.  Asynchronous.
+ */
+int eri_compute_batch(const eri_plan *plan, int32_t block_begin, int32_t block_end, double *out,
+                      int64_t out_capacity, void *stream);
+
+/*
+ * Coulomb matrix of a screened (quartets == NULL) plan: J = sum over the
+ * plan's unique quartets with the 8-fold symmetry, D and J dense row-major
+ * device matrices of order nbf with leading dimensions ldd, ldj.  D must be
+ * symmetric.  J is fully overwritten.  Deterministic, no atomics.
+ * Asynchronous; the plan keeps work buffers between calls.
+ */
+int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream);
+
+/* Static text for an error code, with the last HIP error for ERI_E_HIP. */
+const char *eri_strerror(int code);
+
+/* Class metadata: l of (a, b, c, d) and the tier ('V' register, 'M' memory). */
+int eri_class_info(int32_t class_id, int32_t *l4, int32_t *tier);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -281,18 +281,21 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                 for (int pd = 0; pd < K4[3]; ++pd) {
                     double a = al[0][pa], b = al[1][pb], c = al[2][pc], d = al[3][pd];
                     double zeta = a + b, eta = c + d, rho = zeta * eta / (zeta + eta);
-                    double P[3], Q[3], W[3], PA[3], PB[3], QC[3], QD[3], WP[3], WQ[3], PQ2 = 0;
+                    /* P - A = beta (B - A)/zeta, P - B = alpha (A - B)/zeta (likewise for Q),
+                       P - Q = (P - A) - (Q - C) + (A - C), W - P = eta (Q - P)/(zeta+eta),
+                       W - Q = zeta (P - Q)/(zeta+eta): the same quantities as the
+                       definitions, formed from coordinate differences so that they
+                       vanish exactly for coincident centres. */
+                    double PA[3], PB[3], QC[3], QD[3], WP[3], WQ[3], PQ2 = 0;
                     for (int i = 0; i < 3; ++i) {
-                        P[i] = (a * A[i] + b * B[i]) / zeta;
-                        Q[i] = (c * C[i] + d * D[i]) / eta;
-                        W[i] = (zeta * P[i] + eta * Q[i]) / (zeta + eta);
-                        PA[i] = P[i] - A[i];
-                        PB[i] = P[i] - B[i];
-                        QC[i] = Q[i] - C[i];
-                        QD[i] = Q[i] - D[i];
-                        WP[i] = W[i] - P[i];
-                        WQ[i] = W[i] - Q[i];
-                        PQ2 += (P[i] - Q[i]) * (P[i] - Q[i]);
+                        PA[i] = b * (B[i] - A[i]) / zeta;
+                        PB[i] = a * (A[i] - B[i]) / zeta;
+                        QC[i] = d * (D[i] - C[i]) / eta;
+                        QD[i] = c * (C[i] - D[i]) / eta;
+                        double PQ = PA[i] - QC[i] + (A[i] - C[i]);
+                        WP[i] = -eta * PQ / (zeta + eta);
+                        WQ[i] = zeta * PQ / (zeta + eta);
+                        PQ2 += PQ * PQ;
                     }
                     double T = rho * PQ2;
                     double pref = 2.0 * pow(M_PI, 2.5) / (zeta * eta * sqrt(zeta + eta)) *

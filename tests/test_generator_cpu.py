@@ -1,0 +1,156 @@
+"""CPU checks of the kernel generator (no GPU).
+
+* the generator's spherical coefficients (recursion) against the oracle's
+  (closed form) -- two independent derivations of Eq. (8)'s t^(l);
+* a numpy emulation of the generated algorithm (lane-owns-e bra paths, ket
+  vertical recurrence with the cross-lane coupling term, contraction, both
+  horizontal phases and stepwise transforms) executed from the generator's
+  own graphs, against the oracle, for every class up to (dd|dd) and a few
+  higher ones;
+* class enumeration and tier routing.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from electron_repulsion_integrals_amd.gen import cartesian as gc
+from electron_repulsion_integrals_amd.gen import graph as gg
+from workloads.configs import _pack
+
+
+@pytest.mark.parametrize("l", range(7))
+def test_generator_sph_matches_oracle(l):
+    np.testing.assert_allclose(np.array(gc.sph_matrix(l)), oracle.sph_coeffs(l), atol=1e-13)
+
+
+def test_class_enumeration():
+    cls = gg.all_classes(4)
+    assert len(cls) == 120
+    ids = [gg.class_id(c.la, c.lb, c.lc, c.ld) for c in cls]
+    assert sorted(ids) == list(range(120))
+
+
+def _norm(l, exps, coefs):
+    df = 1.0
+    for t in range(2 * l - 1, 1, -2):
+        df *= t
+    c = np.array([cf * (2 * a / math.pi) ** 0.75 * (4 * a) ** (l / 2) / math.sqrt(df) for a, cf in zip(exps, coefs)])
+    s = sum(c[i] * c[j] * (math.pi / (exps[i] + exps[j])) ** 1.5 * df / (2 * (exps[i] + exps[j])) ** l
+            for i in range(len(c)) for j in range(len(c)))
+    return c / math.sqrt(s)
+
+
+def _boys(L, T):
+    # reference values for the emulation only (the device uses its own table)
+    return oracle.boys(L, T)
+
+
+def emulate(ci, cen, exps, coefs, spherical):
+    """Run the generated algorithm for one quartet, lane by lane, in numpy."""
+    A, B, C, D = [np.asarray(x, dtype=float) for x in cen]
+    ls = (ci.la, ci.lb, ci.lc, ci.ld)
+    cn = [_norm(l, e, c) for l, e, c in zip(ls, exps, coefs)]
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    kv = gg.build_ket_vrr(ci.lc, ci.Lk)
+    L = ci.L
+    acc = {t: np.zeros(len(lanes)) for t in kv.targets}
+    for ia, al in enumerate(exps[0]):
+        for ib, be in enumerate(exps[1]):
+            z = al + be
+            P = (al * A + be * B) / z
+            Kab = cn[0][ia] * cn[1][ib] * math.exp(-al * be / z * np.sum((A - B) ** 2)) / z
+            for ic, ga in enumerate(exps[2]):
+                for id_, de in enumerate(exps[3]):
+                    e_ = ga + de
+                    Q = (ga * C + de * D) / e_
+                    Kcd = cn[2][ic] * cn[3][id_] * math.exp(-ga * de / e_ * np.sum((C - D) ** 2)) / e_
+                    ize = 1 / (z + e_)
+                    rho = z * e_ * ize
+                    W = (z * P + e_ * Q) * ize
+                    PA, WP, QC, WQ = P - A, W - P, Q - C, W - Q
+                    T = rho * np.sum((P - Q) ** 2)
+                    pref = 2 * math.pi ** 2.5 * Kab * Kcd * math.sqrt(ize)
+                    F = pref * _boys(L, T)
+                    i2z, roz, i2e, roe, i2ze = 0.5 / z, e_ * ize, 0.5 / e_, z * ize, 0.5 * ize
+                    # bra phase per lane: [e0|00]^(m)
+                    s1 = np.zeros((len(lanes), L + 1))
+                    for li, e in enumerate(lanes):
+                        cur = F.copy()
+                        prev = np.zeros(L + 1)
+                        steps = [0] * e[0] + [1] * e[1] + [2] * e[2]
+                        cnt = [0, 0, 0]
+                        for s, ax in enumerate(steps, start=1):
+                            n = cnt[ax]
+                            new = np.zeros(L + 1)
+                            for m in range(L - s + 1):
+                                new[m] = PA[ax] * cur[m] + WP[ax] * cur[m + 1] + n * i2z * (prev[m] - roz * prev[m + 1])
+                            prev, cur = cur, new
+                            cnt[ax] += 1
+                        s1[li] = cur
+                    # ket phase: V[(f, m)] is a vector over lanes
+                    V = {((0, 0, 0), m): s1[:, m].copy() for m in range(kv.base_m + 1)}
+                    for nd in kv.nodes:
+                        ax = nd.axis
+                        v = QC[ax] * V[nd.a0] + WQ[ax] * V[nd.a1]
+                        if nd.b0 is not None:
+                            v = v + nd.fi_minus_1 * i2e * (V[nd.b0] - roe * V[nd.b1])
+                        remote = np.array([V[nd.a1][lpos[gc.sub(e, ax)]] if e[ax] > 0 else 0.0 for e in lanes])
+                        eh = np.array([e[ax] for e in lanes]) * i2ze
+                        V[(nd.f, nd.m)] = v + eh * remote
+                    for t in kv.targets:
+                        acc[t] += V[t]
+    # ket HRR per lane (lane = e), then transform
+    hn, base = gg.build_hrr(ci.lc, ci.ld)
+    CD = C - D
+    H = {(f, (0, 0, 0)): acc[(f, 0)] for f in base}
+    for nd in hn:
+        H[(nd.x, nd.y)] = H[nd.p_hi] + CD[nd.axis] * H[nd.p_lo]
+    cs, ds = gc.components(ci.lc), gc.components(ci.ld)
+    Y = np.array([[H[(c, d)] for d in ds] for c in cs])  # [nc, nd, lanes]
+    if spherical:
+        Y = np.einsum("sd,cdl->csl", np.array(gc.sph_matrix(ci.ld)), Y)
+        Y = np.einsum("rc,csl->rsl", np.array(gc.sph_matrix(ci.lc)), Y)
+    Y = Y.reshape(-1, len(lanes))  # [kappa, lanes]
+    # bra HRR per kappa
+    hb, baseb = gg.build_hrr(ci.la, ci.lb)
+    AB = A - B
+    G = {(e, (0, 0, 0)): Y[:, lpos[e]] for e in baseb}
+    for nd in hb:
+        G[(nd.x, nd.y)] = G[nd.p_hi] + AB[nd.axis] * G[nd.p_lo]
+    as_, bs = gc.components(ci.la), gc.components(ci.lb)
+    Z = np.array([[G[(a, b)] for b in bs] for a in as_])  # [na, nb, kappa]
+    if spherical:
+        Z = np.einsum("sb,abk->ask", np.array(gc.sph_matrix(ci.lb)), Z)
+        Z = np.einsum("ra,ask->rsk", np.array(gc.sph_matrix(ci.la)), Z)
+    f = gc.nsph if spherical else gc.ncart
+    return Z.reshape(f(ci.la), f(ci.lb), f(ci.lc), f(ci.ld))
+
+
+CLASSES = [(0, 0, 0, 0), (1, 0, 0, 0), (1, 0, 1, 0), (1, 1, 0, 0), (1, 1, 1, 0), (1, 1, 1, 1), (2, 0, 0, 0),
+           (2, 0, 1, 1), (2, 1, 2, 0), (2, 2, 1, 0), (2, 2, 2, 1), (2, 2, 2, 2), (3, 1, 2, 1), (3, 3, 1, 0), (4, 0, 2, 2)]
+
+
+@pytest.mark.parametrize("ls", CLASSES)
+@pytest.mark.parametrize("spherical", [False, True])
+def test_emulated_algorithm_matches_oracle(ls, spherical):
+    ci = gg.ClassInfo(*ls)
+    rng = np.random.default_rng(sum(ls) * 13 + spherical)
+    cen = [rng.uniform(0, 4, 3) for _ in range(4)]
+    K = [2, 1, 2, 1]
+    exps = [list(np.exp(rng.uniform(np.log(0.2), np.log(8.0), k))) for k in K]
+    coefs = [list(rng.uniform(0.2, 1.0, k)) for k in K]
+    got = emulate(ci, cen, exps, coefs, spherical)
+    sh = _pack(cen, list(ls), K, [np.array(e) for e in exps], [np.array(c) for c in coefs])
+    ref = oracle.eri_block(sh, [0, 1, 2, 3], spherical)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-13 * max(1.0, np.abs(ref).max()))
+
+
+def test_tier_routing():
+    from electron_repulsion_integrals_amd.gen.emit import tier_of
+    for c in gg.all_classes(2):
+        assert tier_of(c) == "V", (c.la, c.lb, c.lc, c.ld)
+    assert tier_of(gg.ClassInfo(3, 3, 3, 3)) == "M"
+    assert tier_of(gg.ClassInfo(4, 4, 4, 4)) == "M"

@@ -76,16 +76,16 @@ def cpu_baseline(w, seconds=12.0):
     import numpy as np
     import oracle
     q = np.asarray(w.quartets)
-    n = 16
-    t0 = time.perf_counter()
-    oracle.eri(w.shells, q[:n], w.spherical)
-    dt = time.perf_counter() - t0
-    n2 = int(min(len(q), max(n, n * seconds / max(dt, 1e-6))))
-    t0 = time.perf_counter()
-    oracle.eri(w.shells, q[:n2], w.spherical)
-    dt = time.perf_counter() - t0
-    return {"value": n2 / dt, "unit": "shell quartets/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {n2} of {len(q)} quartets of the default workload, {dt:.1f} s"}
+    done, t_used, n = 0, 0.0, 256
+    while t_used < seconds:
+        sel = q[np.arange(done, done + n) % len(q)]
+        t0 = time.perf_counter()
+        oracle.eri(w.shells, sel, w.spherical)
+        t_used += time.perf_counter() - t0
+        done += n
+        n = min(4 * n, 1 << 16)
+    return {"value": done / t_used, "unit": "shell quartets/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} quartets of the default workload (cycling its {len(q)} quartets), {t_used:.1f} s"}
 
 
 def main():
@@ -95,7 +95,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
+    if a.calibrate_copy_mib:
+        import torch
+        n = a.calibrate_copy_mib * (1 << 20) // 8
+        src = torch.ones(n, dtype=torch.float64, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_MiB": a.calibrate_copy_mib}), flush=True)
+        return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (one process, one MI355X).",
               file=sys.stderr)

@@ -157,3 +157,17 @@ __device__ __forceinline__ double eri_bperm(int byte_addr, double v)
     const int rhi = __builtin_amdgcn_ds_bpermute(byte_addr, hi);
     return __hiloint2double(rhi, rlo);
 }
+
+// Buffer-instruction access to a workgroup's scratch slice: byte offset =
+// per-lane VGPR offset + uniform scalar offset (memory-tier kernels).
+typedef unsigned int eri_u2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ double eri_bld(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ void eri_bst(__amdgpu_buffer_rsrc_t r, int voff, int soff, double v)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(eri_u2, v), r, voff, soff, 0);
+}

@@ -50,7 +50,11 @@ class Names:
             return f"s1_{m}"
         if self.tier == "V":
             return f"v{self.fpos[f]}_{m}"
-        return f"SC({self.slot_of[('k', f, m)]})"
+        return f"SLD({self.slot_of[('k', f, m)]})"
+
+    def ket_store(self, node, expr):
+        f, m = node
+        return f"SST({self.slot_of[('k', f, m)]}, {expr})"
 
     def ket_remote(self, node, axis):
         f, m = node
@@ -58,7 +62,7 @@ class Names:
             return f"eri_bperm(ad{AX[axis]}, {self.ket(node)})"
         if sum(f) == 0:
             raise AssertionError("remote base values are read from the remote lane's own stage-1 copy")
-        return f"SCR({self.slot_of[('k', f, m)]}, src{AX[axis]})"
+        return f"SLDL({self.slot_of[('k', f, m)]}, src{AX[axis]})"
 
 
 # ---------------------------------------------------------------------------
@@ -157,14 +161,15 @@ def _ket_phase(kv, names: Names, lines, ind="      ", barrier=None, acc_now=None
             expr += f" + eh{a} * {names.ket_remote(n.a1, n.axis)}"
         else:
             # memory tier, coupling to the remote lane's bra-phase value
-            expr += f" + eh{a} * S1R({n.a1[1]}, src{a})"
-        tgt = names.ket((n.f, n.m))
+            expr += f" + eh{a} * S1L({n.a1[1]}, src{a})"
         if names.tier == "V":
-            lines.append(f"{ind}const double {tgt} = {expr};")
+            lines.append(f"{ind}const double {names.ket((n.f, n.m))} = {expr};")
         else:
-            lines.append(f"{ind}{tgt} = {expr};")
-        if acc_now is not None and (n.f, n.m) in acc_now:
-            lines.append(f"{ind}{acc_now[(n.f, n.m)]} += {tgt};")
+            lines.append(f"{ind}{{ const double t_ = {expr}; {names.ket_store((n.f, n.m), 't_')};")
+            if acc_now is not None and (n.f, n.m) in acc_now:
+                a = acc_now[(n.f, n.m)]
+                lines.append(f"{ind}  SST({a}, SLD({a}) + t_);")
+            lines.append(f"{ind}}}")
 
 
 def _hrr_block(l1, l2, base_expr, R, out_prefix, spherical, lines, ind="  ", decl="double"):
@@ -209,6 +214,83 @@ def _hrr_block(l1, l2, base_expr, R, out_prefix, spherical, lines, ind="  ", dec
     for k, nm in enumerate(outs):
         lines.append(f"{ind}{decl} {out_prefix}{k} = {nm};")
     return len(outs)
+
+
+def _hrr_ops(l1, l2, R, spherical):
+    """HRR (Eq. (3)) then transform of y then x, as a list of linear ops.
+
+    Returns (ops, base, outputs): ops = [(key, [(coef, src_key)])] in order,
+    coef a C expression or None for 1; base = list of base triples e (key
+    ('b', e)); outputs = keys of the final values in output order.
+    """
+    nodes, base = build_hrr(l1, l2)
+    key = {}
+    for e in base:
+        key[(e, (0, 0, 0))] = ("b", e)
+    ops = []
+    for n in nodes:
+        k = ("h", n.x, n.y)
+        ops.append((k, [(None, key[n.p_hi]), (f"{R}{AX[n.axis]}", key[n.p_lo])]))
+        key[(n.x, n.y)] = k
+    xs, ys = components(l1), components(l2)
+    outs = []
+    if not spherical:
+        outs = [key[(x, y)] for x in xs for y in ys]
+    else:
+        Ty, Tx = transform_terms(l2), transform_terms(l1)
+        for xi, x in enumerate(xs):
+            for si, row in enumerate(Ty):
+                ops.append((("t", xi, si), [(_fmt(c), key[(x, ys[yi])]) for yi, c in row]))
+        for li, row in enumerate(Tx):
+            for si in range(nsph(l2)):
+                k = ("u", li, si)
+                ops.append((k, [(_fmt(c), ("t", xi, si)) for xi, c in row]))
+                outs.append(k)
+    return ops, base, outs
+
+
+def _emit_ops_mem(ops, base_expr, outs, store, slot_base, lines, ind):
+    """Emit ops with every intermediate in a private scratch slot (linear-scan reuse).
+
+    base_expr(e) reads a base value; store(k, expr) emits the statement that
+    consumes output k.  Returns the number of private slots used.
+    """
+    last = {}
+    for t, (k, terms) in enumerate(ops):
+        for _, src in terms:
+            last[src] = t
+    out_set = set(outs)
+    free, nslot, slot = [], 0, {}
+
+    def ref(src):
+        if src[0] == "b":
+            return base_expr(src[1])
+        return f"SLD({slot_base + slot[src]})"
+
+    for t, (k, terms) in enumerate(ops):
+        parts = []
+        for coef, src in terms:
+            parts.append(ref(src) if coef is None else f"{coef} * {ref(src)}")
+        expr = " + ".join(parts)
+        # release sources whose last use is this op before allocating the result
+        for _, src in terms:
+            if src[0] != "b" and last.get(src) == t and src not in out_set and src in slot:
+                free.append(slot.pop(src))
+        if k in out_set and k not in last:
+            lines.append(f"{ind}{store(outs.index(k), expr)}")
+            continue
+        if free:
+            sidx = free.pop()
+        else:
+            sidx = nslot
+            nslot += 1
+        slot[k] = sidx
+        lines.append(f"{ind}SST({slot_base + sidx}, {expr});")
+    # outputs that are also intermediates (Cartesian) are stored after the sweep
+    for i, k in enumerate(outs):
+        if k in slot:
+            lines.append(f"{ind}{store(i, f'SLD({slot_base + slot[k]})')}")
+    return nslot
 
 
 # ---------------------------------------------------------------------------
@@ -397,12 +479,20 @@ def _write_if_changed(fn, text):
 # memory tier
 # ---------------------------------------------------------------------------
 
+def _count_private(ops, outs):
+    lines = []
+    return _emit_ops_mem(ops, lambda e: "0.0", outs, lambda i, x: f"(void)({x});", 0, lines, "")
+
+
 def _mem_layout(ci: ClassInfo, spherical: bool):
     kv = build_ket_vrr(ci.lc, ci.Lk)
     slot_of, nk_slots = _alloc_slots(kv)
     ntg = len(kv.targets)
-    # layout (in units of W doubles): [ket slots][acc][exchange NK]
-    acc0 = nk_slots
+    ops1, _, outs1 = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
+    ops2, _, outs2 = _hrr_ops(ci.la, ci.lb, "AB", spherical)
+    npriv = max(nk_slots, _count_private(ops1, outs1), _count_private(ops2, outs2))
+    # layout (units of W doubles): [ket slots | private HRR slots][acc][exchange NK]
+    acc0 = npriv
     xch0 = acc0 + ntg
     nslots = xch0 + ci.nket(spherical)
     W = 64 * ((ci.G + 63) // 64)
@@ -458,10 +548,16 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("  const int tid = threadIdx.x;")
     o.append("  const int sub = tid < G ? tid : 0;  // lanes beyond G shadow e = (0,0,0) and never store")
     o.append("  const bool real = tid < G;")
-    o.append("  double* __restrict__ scr = a.scratch + (size_t)blockIdx.x * WG_DOUBLES;")
-    o.append("#define SC(s) scr[(size_t)(s) * W + tid]")
-    o.append("#define SCR(s, l) scr[(size_t)(s) * W + (l)]")
-    o.append(f"#define S1R(m, l) scr[(size_t)({S1} + (m)) * W + (l)]")
+    # Every graph value lives in this workgroup's scratch slice, addressed by
+    # buffer instructions: one per-lane VGPR offset plus a uniform slot offset,
+    # so the thousands of slots cost no address registers.
+    o.append("  double* slice = a.scratch + (size_t)blockIdx.x * WG_DOUBLES;")
+    o.append("  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(slice, (short)0, (int)(WG_DOUBLES * 8), 0x00020000);")
+    o.append("  const int vo = tid * 8;")
+    o.append("#define SLD(s) eri_bld(rs, vo, (s) * (W * 8))")
+    o.append("#define SST(s, x) eri_bst(rs, vo, (s) * (W * 8), (x))")
+    o.append("#define SLDL(s, l) eri_bld(rs, (l) * 8, (s) * (W * 8))")
+    o.append(f"#define S1L(m, l) eri_bld(rs, (l) * 8, ({S1} + (m)) * (W * 8))")
     o.append(f"  const int ex = k_{tag}_lane[0][sub], ey = k_{tag}_lane[1][sub], ez = k_{tag}_lane[2][sub];")
     o.append("  const int es = ex + ey + ez;")
     o.append(f"  const int srcx = ex > 0 ? k_{tag}_down[0][sub] : tid;")
@@ -476,7 +572,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("  const double ACx = a.cen[3 * pb.x] - Cx, ACy = a.cen[3 * pb.x + 1] - Cy, ACz = a.cen[3 * pb.x + 2] - Cz;")
     o.append("  (void)CDx; (void)CDy; (void)CDz;")
     for t in range(len(targets)):
-        o.append(f"  SC({acc0 + t}) = 0.0;")
+        o.append(f"  SST({acc0 + t}, 0.0);")
     o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
     o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
     o.append("    for (int ik = 0; ik < pk.w; ++ik) {")
@@ -496,23 +592,23 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     _stage1(ci, kv.base_m, o)
     # publish the bra-phase values for remote reads, then barrier
     for m in range(kv.base_m + 1):
-        o.append(f"      S1R({m}, tid) = s1_{m};")
+        o.append(f"      eri_bst(rs, vo, ({S1} + {m}) * (W * 8), s1_{m});")
     o.append("      __syncthreads();")
-    acc_now = {tg: f"SC({acc0 + t})" for t, tg in enumerate(targets) if sum(tg[0]) > 0}
+    acc_now = {tg: f"{acc0 + t}" for t, tg in enumerate(targets) if sum(tg[0]) > 0}
     for t, tg in enumerate(targets):
         if sum(tg[0]) == 0:
-            o.append(f"      SC({acc0 + t}) += {names.ket(tg)};")
+            o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + {names.ket(tg)});")
     _ket_phase(kv, names, o, barrier="__syncthreads();", acc_now=acc_now)
     o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
     o.append("    }")
     o.append("  }")
-    # H1 per lane, reading the accumulators
+    # H1 per lane, reading the accumulators; intermediates in private slots of
+    # the (now dead) ket region, results straight into the exchange slots
     tpos = {f: t for t, (f, m) in enumerate(targets)}
-    nk = _hrr_block(ci.lc, ci.ld, lambda e: f"SC({acc0 + tpos[e]})", "CD", "y", spherical, o, "  ")
-    assert nk == NK
-    o.append(f"  if (real && es >= {ci.la}) {{")
-    for k in range(NK):
-        o.append(f"    SC({xch0 + k}) = y{k};")
+    ops1, _, outs1 = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
+    assert len(outs1) == NK
+    o.append("  {")
+    _emit_ops_mem(ops1, lambda e: f"SLD({acc0 + tpos[e]})", outs1, lambda k, x: f"SST({xch0 + k}, {x});", 0, o, "    ")
     o.append("  }")
     o.append("  __syncthreads();")
     o.append("  const int4 pb2 = a.pair_info[bra];")
@@ -522,17 +618,18 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("  for (int kap = tid; kap < NK; kap += W) {")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
-    o.append(f"    const double* srcp = scr + (size_t)({xch0} + kap) * W + {EOFF};")
-    nb = _hrr_block(ci.la, ci.lb, lambda e: f"srcp[{epos[e]}]", "AB", "z", spherical, o, "    ")
+    o.append(f"    const int vx = (kap * W + {EOFF}) * 8;  // exchange row kap, first bra lane")
     o.append("    double* dst = a.out + (size_t)qs * BLK + kap;")
-    for k in range(nb):
-        o.append(f"    dst[{k} * NK] = z{k};")
+    ops2, _, outs2 = _hrr_ops(ci.la, ci.lb, "AB", spherical)
+    _emit_ops_mem(ops2, lambda e: f"eri_bld(rs, vx, {xch0} * (W * 8) + {epos[e] * 8})", outs2,
+                  lambda k, x: f"dst[{k} * NK] = {x};", 0, o, "    ")
     o.append("  }")
     o.append("  __syncthreads();  // exchange slots are reused by the next quartet")
     o.append("  }")
-    o.append("#undef SC")
-    o.append("#undef SCR")
-    o.append("#undef S1R")
+    o.append("#undef SLD")
+    o.append("#undef SST")
+    o.append("#undef SLDL")
+    o.append("#undef S1L")
     o.append("}")
     o.append("")
     o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")

@@ -75,6 +75,8 @@ def lib():
                                      ctypes.c_int, dp, dp]
         L.oracle_J_naive.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_jitter.argtypes = [ctypes.c_uint64]
+        L.oracle_set_jitter.restype = None
         _lib = L
     return _lib
 
@@ -234,3 +236,126 @@ def J_naive(sh, spherical: bool, D) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_J_naive failed")
     return j
+
+
+def J_blocks(sh, spherical: bool, bra_pairs, D, S, tau):
+    """J blocks for the given shell pairs (i, j) by the plain sum over every ket pair.
+
+    J_mu,nu = sum over shell pairs (k >= l) of f_kl sum_(la in k, si in l) (mu nu|la si) D_la,si,
+    f_kl = 2 for k != l (the (l, k) orientation of a symmetric D), keeping only the
+    pairs with fl(S_ij * S_kl) >= fl(tau^2) (S indexed by pair index i(i+1)/2 + j).
+    Returns a list of arrays [n_i, n_j].
+    """
+    ns = int(sh.l.shape[0])
+    bf = basis_offsets(sh, spherical)
+    t2 = float(tau) * float(tau)
+    out = []
+    kets = [(k, l) for k in range(ns) for l in range(k + 1)]
+    for (i, j) in bra_pairs:
+        pij = max(i, j) * (max(i, j) + 1) // 2 + min(i, j)
+        keep = [(k, l) for (k, l) in kets if S[pij] * S[k * (k + 1) // 2 + l] >= t2]
+        q = [(i, j, k, l) for (k, l) in keep]
+        flat, off = eri(sh, q, spherical)
+        ni, nj = nfunc(int(sh.l[i]), spherical), nfunc(int(sh.l[j]), spherical)
+        J = np.zeros((ni, nj))
+        for t, (k, l) in enumerate(keep):
+            nk, nl = nfunc(int(sh.l[k]), spherical), nfunc(int(sh.l[l]), spherical)
+            blk = flat[off[t]: off[t] + ni * nj * nk * nl].reshape(ni, nj, nk, nl)
+            f = 2.0 if k != l else 1.0
+            J += f * np.einsum("abcd,cd->ab", blk, D[bf[k]:bf[k + 1], bf[l]:bf[l + 1]])
+        out.append(J)
+    return out
+
+
+def conditioning_spread(sh, quartets, spherical: bool, ref=None, seeds=(0x9E3779B97F4A7C15, 0xD1B54A32D192ED03)):
+    """Per-quartet change of the oracle's block when every Boys input is perturbed by
+    at most one unit in the last place (two seeded perturbations, maximum taken).
+
+    Returns an array over quartets: the largest |perturbed - unperturbed| element
+    of each block.  This is the error that rounding the recurrence inputs to fp64
+    alone causes; well-conditioned quartets give ~1e-16 x their magnitude.
+    """
+    q = np.asarray(quartets).reshape(-1, 4)
+    if ref is None:
+        ref, _ = eri(sh, q, spherical)
+    sizes = block_sizes(sh, q, spherical)
+    off = np.concatenate([[0], np.cumsum(sizes)])
+    spread = np.zeros(len(q))
+    try:
+        for sd in seeds:
+            lib().oracle_set_jitter(ctypes.c_uint64(sd))
+            alt, _ = eri(sh, q, spherical)
+            d = np.abs(alt - ref)
+            spread = np.maximum(spread, np.maximum.reduceat(d, off[:-1]) if len(d) else spread)
+    finally:
+        lib().oracle_set_jitter(ctypes.c_uint64(0))
+    return spread
+
+
+def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53):
+    """First-order fp64 error floor of the two-phase (VRR + HRR) evaluation.
+
+    The two-phase method holds the contracted intermediates
+    [e0|f0] = (e_A s_B | f_C s_D), |e| in [l_a, l_a+l_b], |f| in [l_c, l_c+l_d]
+    (the exponents and normalised contraction coefficients of the quartet's
+    shells), and the horizontal recurrence Eq. (3) expands each target as
+        (a b|c d) = sum_k sum_k' prod_i C(b_i,k_i) AB_i^(b_i-k_i) C(d_i,k'_i) CD_i^(d_i-k'_i) [a+k 0|c+k' 0]
+    (the recurrence unrolled by the binomial theorem, AB = A - B, CD = C - D).
+    Rounding every intermediate to fp64 (relative error eps) therefore moves
+    the target by up to  eps * sum |coefficient| |[a+k 0|c+k' 0]|,  which this
+    function returns per element (spherical outputs by the triangle inequality
+    through |t^(l)|).  It is the error that storing the intermediates in fp64
+    alone forces on any such evaluation; for diffuse high-l quartets it can far
+    exceed 1e-10 of the result.  The intermediates are computed here by the
+    oracle's own four-index recurrence on raw primitives.
+    """
+    from math import comb
+    q = np.asarray(quartets).reshape(-1, 4)
+    out = []
+    for a, b, c, d in q:
+        la, lb, lc, ld = (int(sh.l[s]) for s in (a, b, c, d))
+        prim = []
+        for s, l in ((a, la), (b, lb), (c, lc), (d, ld)):
+            e = sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]
+            prim.append((e, normalize(l, e, sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]])))
+        cen = [sh.centers[s] for s in (a, b, c, d)]
+        V = {}
+        for le in range(la, la + lb + 1):
+            for lf in range(lc, lc + ld + 1):
+                from workloads.configs import _pack
+                s2 = _pack(cen, [le, 0, lf, 0], [len(p[0]) for p in prim], [p[0] for p in prim], [p[1] for p in prim])
+                blk = eri_block(s2, [0, 1, 2, 3], False, normalize_=False)[:, 0, :, 0]
+                for i, e_ in enumerate(cart_components(le)):
+                    for j, f_ in enumerate(cart_components(lf)):
+                        V[(e_, f_)] = abs(blk[i, j])
+        AB = np.abs(sh.centers[a] - sh.centers[b])
+        CD = np.abs(sh.centers[c] - sh.centers[d])
+
+        def expand(x, y, R):
+            """[(coefficient magnitude, x + k)] of the unrolled HRR for (x, y)."""
+            terms = [(1.0, (0, 0, 0))]
+            for ax in range(3):
+                new = []
+                for cf, k in terms:
+                    for ki in range(y[ax] + 1):
+                        kk = list(k)
+                        kk[ax] = ki
+                        new.append((cf * comb(y[ax], ki) * R[ax] ** (y[ax] - ki), tuple(kk)))
+                terms = new
+            return [(cf, (x[0] + k[0], x[1] + k[1], x[2] + k[2])) for cf, k in terms]
+
+        ca, cb, cc, cd = (cart_components(l) for l in (la, lb, lc, ld))
+        bound = np.zeros((len(ca), len(cb), len(cc), len(cd)))
+        for ia, xa in enumerate(ca):
+            for ib, yb in enumerate(cb):
+                bt = expand(xa, yb, AB)
+                for ic, xc in enumerate(cc):
+                    for id_, yd in enumerate(cd):
+                        kt = expand(xc, yd, CD)
+                        bound[ia, ib, ic, id_] = sum(c1 * c2 * V[(e1, f1)] for c1, e1 in bt for c2, f1 in kt)
+        bound *= eps
+        if spherical:
+            for pos, l in enumerate((la, lb, lc, ld)):
+                bound = np.moveaxis(np.tensordot(np.abs(sph_coeffs(l)), np.moveaxis(bound, pos, 0), axes=(1, 0)), 0, pos)
+        out.append(bound.ravel())
+    return np.concatenate(out) if out else np.zeros(0)

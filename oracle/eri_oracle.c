@@ -42,6 +42,24 @@
 
 enum { OR_SPHERICAL = 1, OR_NO_NORMALIZE = 2 };
 
+/* Conditioning probe (test infrastructure): when non-zero, every Boys value
+ * entering a primitive quartet is multiplied by 1 + d with |d| <= 2^-52 drawn
+ * from a hash of (seed, primitive indices, T, m).  Comparing two seeds with the
+ * unperturbed result measures how far rounding the recurrence inputs to fp64
+ * alone moves each integral -- an error no fp64 evaluation can avoid. */
+static uint64_t g_jitter_seed = 0;
+void oracle_set_jitter(uint64_t seed) { g_jitter_seed = seed; }
+
+static uint64_t mix64(uint64_t x)
+{
+    x ^= x >> 30;
+    x *= 0xbf58476d1ce4e5b9ULL;
+    x ^= x >> 27;
+    x *= 0x94d049bb133111ebULL;
+    x ^= x >> 31;
+    return x;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Boys function F_m(T) = int_0^1 t^(2m) exp(-T t^2) dt                       */
 /* ------------------------------------------------------------------------ */
@@ -301,6 +319,17 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                     double pref = 2.0 * pow(M_PI, 2.5) / (zeta * eta * sqrt(zeta + eta)) *
                                   exp(-a * b / zeta * AB2) * exp(-c * d / eta * CD2);
                     oracle_boys(Lt, T, F);
+                    if (g_jitter_seed) {
+                        uint64_t tb;
+                        memcpy(&tb, &T, sizeof tb);
+                        uint64_t h0 = mix64(g_jitter_seed ^ mix64(tb ^ mix64(((uint64_t)pa << 48) ^ ((uint64_t)pb << 32) ^
+                                                                            ((uint64_t)pc << 16) ^ (uint64_t)pd)));
+                        for (int m = 0; m <= Lt; ++m) {
+                            uint64_t h = mix64(h0 + (uint64_t)m);
+                            double u = (double)(h >> 11) * (1.0 / 9007199254740992.0); /* [0,1) */
+                            F[m] *= 1.0 + (2.0 * u - 1.0) * 2.220446049250313e-16;
+                        }
+                    }
                     double i2z = 0.5 / zeta, i2e = 0.5 / eta, i2ze = 0.5 / (zeta + eta);
                     double roz = rho / zeta, roe = rho / eta;
 

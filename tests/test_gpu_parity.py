@@ -1,8 +1,14 @@
 """GPU parity: the HIP library through its C ABI against the CPU oracle.
 
-Bar (fp64): |gpu - oracle| <= max(1e-10 |oracle|, 1e-13) element by element;
-plans (index maps) bit-exact against the oracle's plan twin fed the GPU's
-Schwarz factors; Schwarz factors themselves to the same 1e-10 bar.
+Bar (fp64), element by element:
+    |gpu - oracle| <= max(1e-10 |oracle|, 1e-13, 16 * B)
+where B is the oracle's first-order fp64 error floor of the two-phase method
+(oracle.hgp_rounding_bound: rounding the contracted [e0|f0] intermediates to
+fp64, propagated through the unrolled horizontal recurrence).  B only matters
+for diffuse high-l quartets far apart, where that floor exceeds 1e-10 of the
+result; it is computed only for quartets that miss the first two terms, and
+every test reports how many elements needed it.  Plans (index maps) are
+bit-exact against the oracle's plan twin fed the GPU's Schwarz factors.
 """
 import sys
 
@@ -33,17 +39,37 @@ def eri():
     return E
 
 
-def assert_parity(got, ref, what=""):
-    got = np.asarray(got)
-    ref = np.asarray(ref)
+HGP_FLOOR_FACTOR = 16.0
+
+
+def assert_parity(got, ref, what="", sh=None, quartets=None, spherical=None):
+    """Element-wise bar; with (sh, quartets, spherical) the blocks of ``ref`` are the
+    quartets' blocks in order and the two-phase fp64 floor may be applied."""
+    got = np.asarray(got, dtype=float).ravel()
+    ref = np.asarray(ref, dtype=float).ravel()
     assert got.shape == ref.shape, (got.shape, ref.shape)
     err = np.abs(got - ref)
-    bound = np.maximum(RTOL * np.abs(ref), ATOL)
-    bad = err > bound
+    tol = np.maximum(RTOL * np.abs(ref), ATOL)
+    bad = err > tol
+    n_floor = 0
+    if bad.any() and sh is not None:
+        q = np.asarray(quartets).reshape(-1, 4)
+        sizes = oracle.block_sizes(sh, q, spherical)
+        offs = np.concatenate([[0], np.cumsum(sizes)])
+        qbad = np.unique(np.searchsorted(offs, np.nonzero(bad)[0], side="right") - 1)
+        for x in qbad:
+            B = oracle.hgp_rounding_bound(sh, q[x:x + 1], spherical)
+            sl = slice(offs[x], offs[x + 1])
+            newtol = np.maximum(tol[sl], HGP_FLOOR_FACTOR * B)
+            n_floor += int(np.sum((err[sl] > tol[sl]) & (err[sl] <= newtol)))
+            tol[sl] = newtol
+        bad = err > tol
+    if n_floor:
+        _log(f"  {what}: {n_floor} of {got.size} elements within the two-phase fp64 floor only")
     if bad.any():
-        i = int(np.argmax(err / bound))
+        i = int(np.argmax(err / tol))
         raise AssertionError(f"{what}: {int(bad.sum())} of {got.size} elements outside tolerance; worst at {i}: "
-                             f"gpu={got.flat[i]!r} oracle={ref.flat[i]!r} err={err.flat[i]:.3e}")
+                             f"gpu={got[i]!r} oracle={ref[i]!r} err={err[i]:.3e} tol={tol[i]:.3e}")
 
 
 def run_plan(E, sh, flags, quartets=None, tau=0.0):
@@ -54,6 +80,29 @@ def run_plan(E, sh, flags, quartets=None, tau=0.0):
     torch.cuda.synchronize()
     imap = plan.index_map().cpu().numpy() if plan.n_quartets else np.zeros((0, 5), np.int32)
     return plan, out[: plan.n_out].cpu().numpy(), imap
+
+
+def assert_schwarz(S_gpu, sh, spherical, what="Schwarz factors"):
+    """S_p = max |(mu nu|mu nu)|: compared with the oracle's, the per-pair floor taken
+    from the diagonal elements of the (ij|ij) block."""
+    S_ref = oracle.schwarz(sh, spherical)
+    err = np.abs(S_gpu - S_ref)
+    tol = np.maximum(RTOL * np.abs(S_ref), ATOL)
+    bad = np.nonzero(err > tol)[0]
+    for p in bad:
+        i = int((np.sqrt(8 * p + 1) - 1) // 2)
+        while i * (i + 1) // 2 > p:
+            i -= 1
+        while (i + 1) * (i + 2) // 2 <= p:
+            i += 1
+        j = p - i * (i + 1) // 2
+        B = oracle.hgp_rounding_bound(sh, [[i, j, i, j]], spherical)
+        n = int(round(np.sqrt(B.size)))
+        tol[p] = max(tol[p], HGP_FLOOR_FACTOR * float(np.max(np.diag(B.reshape(n, n)))))
+    if len(bad):
+        _log(f"  {what}: {len(bad)} of {len(S_ref)} factors checked against the two-phase fp64 floor")
+    worst = np.argmax(err / tol)
+    assert np.all(err <= tol), f"{what}: worst pair {worst}: gpu={S_gpu[worst]!r} oracle={S_ref[worst]!r}"
 
 
 def oracle_flat(sh, imap, spherical):
@@ -70,11 +119,11 @@ def test_c1_all_unique_cartesian(eri):
     plan, got, imap = run_plan(eri, sh, 0)
     assert plan.n_quartets == 666
     S_gpu = plan.schwarz().cpu().numpy()
-    assert_parity(S_gpu, oracle.schwarz(sh, False), "Schwarz factors")
+    assert_schwarz(S_gpu, sh, False)
     twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, 0.0)
     np.testing.assert_array_equal(imap, twin["index_map"])
     assert [b[0] for b in twin["blocks"]] == list(plan.block_class)
-    assert_parity(got, oracle_flat(sh, imap, False), "C1 integrals")
+    assert_parity(got, oracle_flat(sh, imap, False), "C1 integrals", sh, imap[:, :4], False)
 
 
 def _mixed_batch(seed, nshell, nq, lmax, kmax):
@@ -97,7 +146,7 @@ def test_explicit_mixed_classes_l2(eri, spherical):
     twin = oplan.explicit_plan(sh.l, sh.nprim, q)
     np.testing.assert_array_equal(imap, twin["index_map"])
     assert len(set(plan.block_class)) == 21
-    assert_parity(got, oracle_flat(sh, imap, spherical), "mixed integrals")
+    assert_parity(got, oracle_flat(sh, imap, spherical), "mixed integrals", sh, imap[:, :4], spherical)
 
 
 def test_c2_dddd_reduced_full_compare(eri):
@@ -105,7 +154,7 @@ def test_c2_dddd_reduced_full_compare(eri):
     w = make_config(2, scale={"nquartets": 333})
     plan, got, imap = run_plan(eri, w.shells, 1, w.quartets)
     assert plan.n_quartets == 333 and plan.n_blocks == 1
-    assert_parity(got, oracle_flat(w.shells, imap, True), "dddd integrals")
+    assert_parity(got, oracle_flat(w.shells, imap, True), "dddd integrals", w.shells, imap[:, :4], True)
 
 
 def test_c2_full_size_sampled(eri):
@@ -117,7 +166,7 @@ def test_c2_full_size_sampled(eri):
     rng = np.random.default_rng(2)
     idx = np.unique(np.concatenate([[0, 1, 19998, 19999], rng.choice(20000, 300, replace=False)]))
     ref = oracle_flat(w.shells, imap[idx], True).reshape(len(idx), 625)
-    assert_parity(got.reshape(20000, 625)[idx], ref, "dddd sampled")
+    assert_parity(got.reshape(20000, 625)[idx], ref, "dddd sampled", w.shells, imap[idx, :4], True)
     assert np.isfinite(got).all()
 
 
@@ -130,7 +179,7 @@ def test_single_quartet_and_long_contractions(eri):
     for spherical in (False, True):
         plan, got, imap = run_plan(eri, sh, 1 if spherical else 0, [[0, 1, 2, 3]])
         assert plan.n_quartets == 1
-        assert_parity(got, oracle_flat(sh, imap, spherical), "single quartet")
+        assert_parity(got, oracle_flat(sh, imap, spherical), "single quartet", sh, imap[:, :4], spherical)
 
 
 def test_unnormalised_flag(eri):
@@ -149,11 +198,11 @@ def test_c3_reduced_plan_and_J(eri):
     sh = w.shells
     plan, got, imap = run_plan(eri, sh, 1, None, w.tau)
     S_gpu = plan.schwarz().cpu().numpy()
-    assert_parity(S_gpu, oracle.schwarz(sh, True), "Schwarz factors")
+    assert_schwarz(S_gpu, sh, True)
     twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau)
     np.testing.assert_array_equal(imap, twin["index_map"])
     flat = oracle_flat(sh, imap, True)
-    assert_parity(got, flat, "C3 integrals")
+    assert_parity(got, flat, "C3 integrals", sh, imap[:, :4], True)
     D = torch.tensor(w.density, device="cuda")
     J = torch.empty_like(D)
     eri.digest_J(plan, D, J)
@@ -165,3 +214,79 @@ def test_c3_reduced_plan_and_J(eri):
     _, off = oracle.eri(sh, imap[:, :4], True)
     Jref = oracle.J_from_quartets(sh, True, imap[:, :4], flat, off, w.density)
     assert_parity(Jg, Jref, "J")
+
+
+def test_all_120_classes_explicit(eri):
+    """Every class up to (gg|gg), both output kinds, random shells with K <= 2."""
+    _log("case: explicit mixed batch over all 120 classes")
+    sh, q = _mixed_batch(21, 60, 4000, 4, 2)
+    for spherical in (True, False):
+        plan, got, imap = run_plan(eri, sh, 1 if spherical else 0, q)
+        twin = oplan.explicit_plan(sh.l, sh.nprim, q)
+        np.testing.assert_array_equal(imap, twin["index_map"])
+        assert len(set(plan.block_class)) == 120
+        assert_parity(got, oracle_flat(sh, imap, spherical), f"all classes sph={spherical}", sh, imap[:, :4], spherical)
+
+
+def test_c4_reduced_full_compare(eri):
+    _log("case: (ff|ff) x 64 + (gg|gg) x 16, K=2, spherical, full compare")
+    w = make_config(4, scale={"nquartets_f": 64, "nquartets_g": 16})
+    plan, got, imap = run_plan(eri, w.shells, 1, w.quartets)
+    assert list(plan.block_count) == [64, 16]
+    assert_parity(got, oracle_flat(w.shells, imap, True), "ff/gg integrals", w.shells, imap[:, :4], True)
+
+
+def test_c4_full_size_sampled(eri):
+    _log("case: (ff|ff) x 4000 + (gg|gg) x 1000 spherical, sampled compare")
+    w = make_config(4)
+    plan, got, imap = run_plan(eri, w.shells, 1, w.quartets)
+    assert list(plan.block_count) == [4000, 1000]
+    rng = np.random.default_rng(4)
+    fsel = np.unique(np.concatenate([[0, 3999], rng.choice(4000, 30, replace=False)]))
+    gsel = np.unique(np.concatenate([[4000, 4999], 4000 + rng.choice(1000, 6, replace=False)]))
+    ff = got[: 4000 * 2401].reshape(4000, 2401)
+    gg = got[4000 * 2401:].reshape(1000, 6561)
+    assert_parity(ff[fsel], oracle_flat(w.shells, imap[fsel], True), "ffff sampled", w.shells, imap[fsel, :4], True)
+    assert_parity(gg[gsel - 4000], oracle_flat(w.shells, imap[gsel], True), "gggg sampled", w.shells, imap[gsel, :4], True)
+    assert np.isfinite(got).all()
+
+
+def test_c3_full_size_plan_and_sampled_J(eri):
+    """30-atom SVP-like cluster, tau = 1e-12: bit-exact plan, sampled integrals, sampled J blocks."""
+    import torch
+    _log("case: C3 full 30-atom cluster, plan + J")
+    w = make_config(3)
+    sh = w.shells
+    plan = eri.build_quartets(sh, 1, None, w.tau)
+    S_gpu = plan.schwarz().cpu().numpy()
+    rng = np.random.default_rng(3)
+    pairs_all = [(i, j) for i in range(sh.nshell) for j in range(i + 1)]
+    psel = rng.choice(len(pairs_all), 60, replace=False)
+    assert_schwarz(S_gpu, sh, True)
+    imap = plan.index_map().cpu().numpy()
+    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau)
+    np.testing.assert_array_equal(imap, twin["index_map"])
+    _log(f"  plan: {plan.n_quartets} quartets in {plan.n_blocks} class blocks")
+    out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
+    eri.compute_batch(plan, out)
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.empty_like(D)
+    eri.digest_J(plan, D, J)
+    torch.cuda.synchronize()
+    # sampled integrals: 1500 quartets spread over every class block
+    sizes = oracle.block_sizes(sh, imap[:, :4], True)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    qs = np.unique(np.concatenate([plan.block_start, plan.block_start + plan.block_count - 1,
+                                   rng.choice(plan.n_quartets, 1500, replace=False)]))
+    got = out.cpu().numpy()
+    ref, roff = oracle.eri(sh, imap[qs, :4], True)
+    g = np.concatenate([got[offs[x]: offs[x + 1]] for x in qs])
+    assert_parity(g, ref, "C3 sampled integrals", sh, imap[qs, :4], True)
+    # sampled J blocks by the plain sum over all ket pairs
+    Jg = J.cpu().numpy()
+    bf = oracle.basis_offsets(sh, True)
+    bras = [pairs_all[x] for x in psel[:6]]
+    refs = oracle.J_blocks(sh, True, bras, w.density, S_gpu, w.tau)
+    for (i, j), Jb in zip(bras, refs):
+        assert_parity(Jg[bf[i]:bf[i + 1], bf[j]:bf[j + 1]], Jb, f"J block ({i},{j})")
+        assert_parity(Jg[bf[j]:bf[j + 1], bf[i]:bf[i + 1]], Jb.T, f"J block ({j},{i})")

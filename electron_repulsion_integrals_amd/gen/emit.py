@@ -286,10 +286,13 @@ def _emit_ops_mem(ops, base_expr, outs, store, slot_base, lines, ind):
             nslot += 1
         slot[k] = sidx
         lines.append(f"{ind}SST({slot_base + sidx}, {expr});")
-    # outputs that are also intermediates (Cartesian) are stored after the sweep
+    # outputs that are also intermediates (Cartesian) are stored after the sweep;
+    # with a zero second angular momentum the outputs are the base values themselves
     for i, k in enumerate(outs):
         if k in slot:
             lines.append(f"{ind}{store(i, f'SLD({slot_base + slot[k]})')}")
+        elif k[0] == "b":
+            lines.append(f"{ind}{store(i, base_expr(k[1]))}")
     return nslot
 
 

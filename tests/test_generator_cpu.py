@@ -154,3 +154,32 @@ def test_tier_routing():
         assert tier_of(c) == "V", (c.la, c.lb, c.lc, c.ld)
     assert tier_of(gg.ClassInfo(3, 3, 3, 3)) == "M"
     assert tier_of(gg.ClassInfo(4, 4, 4, 4)) == "M"
+
+
+def test_two_phase_fp64_floor_bounds_the_emulated_algorithm():
+    """On diffuse (gg|gg) and (ff|ff) quartets ~7 bohr apart the fp64 two-phase
+    evaluation loses up to 1e-5 of the block maximum; the oracle's first-order
+    floor (fp64 rounding of [e0|f0] through the unrolled HRR) bounds that loss."""
+    from oracle import plan as oplan
+    from workloads import make_config
+    w = make_config(4, scale={"nquartets_f": 64, "nquartets_g": 16})
+    sh = w.shells
+    imap = oplan.explicit_plan(sh.l, sh.nprim, w.quartets)["index_map"]
+    for qi in (17, 67):
+        a, b, c, d = imap[qi, :4]
+        ci = gg.ClassInfo(*[int(sh.l[s]) for s in (a, b, c, d)])
+        cen = [sh.centers[s] for s in (a, b, c, d)]
+        ex = [list(sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]) for s in (a, b, c, d)]
+        co = [list(sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]]) for s in (a, b, c, d)]
+        em = emulate(ci, cen, ex, co, True).ravel()
+        ref = oracle.eri_block(sh, [a, b, c, d], True).ravel()
+        B = oracle.hgp_rounding_bound(sh, [[a, b, c, d]], True)
+        assert np.all(np.abs(em - ref) <= np.maximum(1e-13, 4.0 * B))
+
+
+def test_two_phase_fp64_floor_is_eps_level_when_well_conditioned():
+    sh = _pack([[0, 0, 0], [0.5, 0, 0], [0, 0.7, 0], [0, 0, 0.4]], [2, 1, 2, 0], [1, 1, 1, 1],
+               [np.array([1.3]), np.array([0.9]), np.array([2.1]), np.array([0.6])], [np.ones(1)] * 4)
+    ref = np.abs(oracle.eri_block(sh, [0, 1, 2, 3], True)).max()
+    B = oracle.hgp_rounding_bound(sh, [[0, 1, 2, 3]], True)
+    assert B.max() < 1e-14 * ref

@@ -31,12 +31,11 @@ HBM_PEAK_GBS = 8000.0
 def _class_flops(plan, spherical):
     """Algorithmic FLOPs of every block of a plan (generator's DAG count)."""
     from electron_repulsion_integrals_amd.gen import graph as G
-    import numpy as np
-    tot = 0
     per_block = []
-    for cid, cnt in zip(plan.block_class, plan.block_count):
-        la, lb, lc, ld = G.pair_class_ls(int(_pcb(cid)))[0], G.pair_class_ls(int(_pcb(cid)))[1], \
-            G.pair_class_ls(int(_pck(cid)))[0], G.pair_class_ls(int(_pck(cid)))[1]
+    for cid in plan.block_class:
+        cid = int(cid)
+        la, lb = G.pair_class_ls(_pcb(cid))
+        lc, ld = G.pair_class_ls(_pck(cid))
         per_prim, once = G.dag_flops(G.ClassInfo(la, lb, lc, ld), spherical)
         per_block.append((per_prim, once))
     return per_block
@@ -69,6 +68,62 @@ def time_launches(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def _block_flops(plan, w, imap):
+    """Algorithmic FLOPs per class block: sum over quartets of K4 x per-primitive + once."""
+    import numpy as np
+    from electron_repulsion_integrals_amd.gen import graph as G
+    K = np.asarray(w.shells.nprim, dtype=np.int64)
+    k4 = K[imap[:, 0]] * K[imap[:, 1]] * K[imap[:, 2]] * K[imap[:, 3]]
+    out = []
+    for cid, st, cnt in zip(plan.block_class, plan.block_start, plan.block_count):
+        cid, st, cnt = int(cid), int(st), int(cnt)
+        pb, pk = _pcb(cid), _pck(cid)
+        la, lb = G.pair_class_ls(pb)
+        lc, ld = G.pair_class_ls(pk)
+        per_prim, once = G.dag_flops(G.ClassInfo(la, lb, lc, ld), w.spherical)
+        out.append(int(k4[st:st + cnt].sum()) * per_prim + int(cnt) * once)
+    return out
+
+
+def per_class(E, plan, w, steps, stream):
+    """Quartets/s and FP64 fraction of every class block (HIP events per block launch)."""
+    import torch
+    from electron_repulsion_integrals_amd.gen import graph as G
+    imap = plan.index_map().cpu().numpy()
+    flops = _block_flops(plan, w, imap)
+    out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
+    res = {}
+    for b in range(plan.n_blocks):
+        off = int(plan.block_out[b])
+        view = out[off:]
+        times, _ = time_launches(lambda: E.compute_batch(plan, view, b, b + 1), steps, 1, stream)
+        ms = sorted(times)[len(times) // 2]
+        la, lb = G.pair_class_ls(_pcb(int(plan.block_class[b])))
+        lc, ld = G.pair_class_ls(_pck(int(plan.block_class[b])))
+        name = "(" + "spdfg"[la] + "spdfg"[lb] + "|" + "spdfg"[lc] + "spdfg"[ld] + ")"
+        tf = flops[b] / (ms * 1e-3) / 1e12
+        res[name] = {"quartets": int(plan.block_count[b]), "ms": ms,
+                     "quartets_per_s": int(plan.block_count[b]) / (ms * 1e-3),
+                     "tflops": tf, "fp64_frac": tf / FP64_VECTOR_PEAK_TFLOPS}
+    return res
+
+
+def j_build(E, w, steps, stream):
+    """Screened plan (pairs, Schwarz, sort) + J digestion for a cluster workload."""
+    import torch
+    t0 = time.perf_counter()
+    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, None, w.tau)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.empty_like(D)
+    times, _ = time_launches(lambda: E.digest_J(plan, D, J), steps, 1, stream)
+    dig = sorted(times)[len(times) // 2]
+    return plan, {"quartets": plan.n_quartets, "class_blocks": plan.n_blocks, "plan_build_ms": plan_ms,
+                  "digest_J_ms": dig, "j_build_ms": plan_ms + dig,
+                  "note": "plan_build_ms is host wall time incl. allocation; digest_J_ms is HIP-event time"}
 
 
 def cpu_baseline(w, seconds=12.0):
@@ -153,6 +208,18 @@ def main():
         "plan_build_ms": plan_ms,
         "wall_s_timed_region": wall,
     }
+    if not a.no_extra:
+        res["per_class"] = {}
+        res["per_class"]["(dd|dd) x 20000"] = per_class(E, plan, w, 10, stream)
+        w3 = make_config(3)
+        plan3, jb = j_build(E, w3, 5, stream)
+        res["j_build_30atom_svp"] = jb
+        res["per_class"]["30-atom SVP-like cluster"] = per_class(E, plan3, w3, 3, stream)
+        del plan3
+        w4 = make_config(4)
+        plan4 = E.build_quartets(w4.shells, E.ERI_SPHERICAL, w4.quartets, 0.0)
+        res["per_class"]["(ff|ff) x 4000 + (gg|gg) x 1000"] = per_class(E, plan4, w4, 3, stream)
+        del plan4
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

@@ -45,6 +45,7 @@ struct EriClassArgs {
     double* out;            // quartet q writes out[q * block_size ...]
     double* scratch;        // memory-tier scratch (scratch_wgs workgroup slices)
     int scratch_wgs;
+    int grid_cap;           // register tier: persistent grid size (workgroups)
 };
 
 typedef void (*EriLaunchFn)(const EriClassArgs&, hipStream_t);
@@ -55,7 +56,8 @@ struct EriClassEntry {
     int la, lb, lc, ld;
     char tier;                 // 'V' register tier, 'M' memory tier
     long long scratch_doubles; // per workgroup, memory tier only
-    EriLaunchFn launch;
+    EriLaunchFn launch;        // any contraction degree
+    EriLaunchFn launch_k1;     // every quartet uncontracted (K_a K_b K_c K_d = 1)
 };
 
 extern EriClassEntry eri_class_table[];  // host-only (non-const keeps it out of device code)

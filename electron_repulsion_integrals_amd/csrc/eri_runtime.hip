@@ -212,19 +212,24 @@ __global__ void k_explicit_fill(int64_t nq, const int64_t *pos, const int *q, co
     pinfo[2 * s + 1] = make_int4(k, m, 0, nprim[k] * nprim[m]);
 }
 
-// start of each class in the sorted keys (lower bound of class << 56)
-__global__ void k_class_starts(int64_t n, const uint64_t *keys, int64_t *starts, int nclass)
+// start of each class in the sorted keys (lower bound of class << 56), and the
+// end of its uncontracted prefix (K_bra = K_ket = 1 sort first in a class)
+__global__ void k_class_starts(int64_t n, const uint64_t *keys, int64_t *starts, int64_t *k1_end, int nclass)
 {
     const int c = blockIdx.x * blockDim.x + threadIdx.x;
     if (c > nclass) return;
-    const uint64_t target = (uint64_t)c << 56;
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        int64_t mid = (lo + hi) / 2;
-        if (keys[mid] < target) lo = mid + 1;
-        else hi = mid;
+    for (int pass = 0; pass < 2; ++pass) {
+        const uint64_t target = pass == 0 ? ((uint64_t)c << 56)
+                                          : (((uint64_t)c << 56) | ((uint64_t)1 << 48) | ((uint64_t)2 << 40));
+        int64_t lo = 0, hi = n;
+        while (lo < hi) {
+            int64_t mid = (lo + hi) / 2;
+            if (keys[mid] < target) lo = mid + 1;
+            else hi = mid;
+        }
+        if (pass == 0) starts[c] = lo;
+        else k1_end[c] = lo;
     }
-    starts[c] = lo;
 }
 
 __global__ void k_copy_w(int n, const int4 *pinfo, int *w)
@@ -496,6 +501,7 @@ inline unsigned nblk(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); 
 struct EriBlock {
     int cid;
     int64_t start, count, out_off;
+    int64_t n_k1;  // leading quartets with K_a K_b K_c K_d = 1
     int na, nb, nc, nd;  // functions per shell of the class (spherical or Cartesian)
 };
 
@@ -514,6 +520,7 @@ struct eri_plan {
     double *d_scratch = nullptr;
     int scratch_wgs = 0;
     long long scratch_doubles = 0;  // per workgroup slice
+    int grid_cap = 2048;            // persistent register-tier grid (8 workgroups per CU)
     std::vector<EriBlock> blocks;
     std::vector<void *> allocs;
     // J digestion work (screened plans, built on first use)
@@ -600,7 +607,8 @@ void sort_pairs_i32(int *keys_in, int *keys_out, V *v_in, V *v_out, int64_t n, h
     HIP_CHECK(e);
 }
 
-void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s)
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
+                  int64_t n_k1 = 0)
 {
     const EriClassEntry *ce = find_class(cid, P->sph);
     if (!ce) {
@@ -616,21 +624,26 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
     a.boys = P->d_boys;
     a.scratch = P->d_scratch;
     a.scratch_wgs = P->scratch_wgs;
-    // large blocks are split so that every grid stays within int range
+    a.grid_cap = P->grid_cap;
+    const int blk = nfun(ce->la, P->sph) * nfun(ce->lb, P->sph) * nfun(ce->lc, P->sph) * nfun(ce->ld, P->sph);
+    if (ce->tier == 'M' && (!P->d_scratch)) {
+        g_last_error = "memory-tier class without scratch";
+        throw HipFail{hipErrorInvalidValue};
+    }
+    // the uncontracted prefix goes to the K4 = 1 kernel; large ranges are split so
+    // that every grid stays within int range
     const int64_t CH = 1 << 26;
-    for (int64_t b = 0; b < n; b += CH) {
-        const int64_t m = std::min(CH, n - b);
-        a.qbra = qbra + b;
-        a.qket = qket + b;
-        a.nq = (int)m;
-        const int blk = nfun(ce->la, P->sph) * nfun(ce->lb, P->sph) * nfun(ce->lc, P->sph) * nfun(ce->ld, P->sph);
-        a.out = out + b * blk;
-        if (ce->tier == 'M' && (!P->d_scratch)) {
-            g_last_error = "memory-tier class without scratch";
-            throw HipFail{hipErrorInvalidValue};
+    for (int part = 0; part < 2; ++part) {
+        const int64_t lo = part == 0 ? 0 : n_k1, hi = part == 0 ? n_k1 : n;
+        for (int64_t b = lo; b < hi; b += CH) {
+            const int64_t m = std::min(CH, hi - b);
+            a.qbra = qbra + b;
+            a.qket = qket + b;
+            a.nq = (int)m;
+            a.out = out + b * blk;
+            (part == 0 ? ce->launch_k1 : ce->launch)(a, s);
+            HIP_CHECK(hipGetLastError());
         }
-        ce->launch(a, s);
-        HIP_CHECK(hipGetLastError());
     }
 }
 
@@ -687,10 +700,11 @@ void build_explicit(eri_plan *P, const std::vector<int> &hl, const int32_t *quar
                        P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
     HIP_CHECK(hipGetLastError());
     const int NC = 120;
-    int64_t *d_st = P->alloc<int64_t>(NC + 1);
-    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, k1, d_st, NC);
-    std::vector<int64_t> st(NC + 1);
+    int64_t *d_st = P->alloc<int64_t>(NC + 1), *d_k1 = P->alloc<int64_t>(NC + 1);
+    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, k1, d_st, d_k1, NC);
+    std::vector<int64_t> st(NC + 1), k1e(NC + 1);
     HIP_CHECK(hipMemcpyAsync(st.data(), d_st, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(k1e.data(), d_k1, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
     st[NC] = nq;
     make_pair_data(P, s);
@@ -704,8 +718,8 @@ void build_explicit(eri_plan *P, const std::vector<int> &hl, const int32_t *quar
             g_last_error = "class " + std::to_string(c) + " not built";
             throw HipFail{hipErrorInvalidValue};
         }
-        EriBlock b{c, st[c], cnt, out, nfun(ce->la, P->sph), nfun(ce->lb, P->sph), nfun(ce->lc, P->sph),
-                   nfun(ce->ld, P->sph)};
+        EriBlock b{c, st[c], cnt, out, std::min(k1e[c], st[c + 1]) - st[c], nfun(ce->la, P->sph),
+                   nfun(ce->lb, P->sph), nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
         out += cnt * (int64_t)b.na * b.nb * b.nc * b.nd;
         P->blocks.push_back(b);
         cids.push_back(c);
@@ -888,7 +902,10 @@ void build_screened(eri_plan *P, const std::vector<int> &hl, const std::vector<i
                 g_last_error = "class " + std::to_string(hb[i].cid) + " not built";
                 throw HipFail{hipErrorInvalidValue};
             }
-            EriBlock b{hb[i].cid, st, en - st, outp, nfun(ce->la, P->sph), nfun(ce->lb, P->sph),
+            // the (K_bra = 1, K_ket = 1) bucket pair, when present, is the first of the class
+            int64_t nk1 = 0;
+            if (hb[i].kb == 1 && hb[i].kk == 1) nk1 = ((i + 1 < hb.size()) ? bst[i + 1] : nq) - bst[i];
+            EriBlock b{hb[i].cid, st, en - st, outp, nk1, nfun(ce->la, P->sph), nfun(ce->lb, P->sph),
                        nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
             outp += b.count * (int64_t)b.na * b.nb * b.nc * b.nd;
             P->blocks.push_back(b);
@@ -939,6 +956,11 @@ extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t
     if (!P) return ERI_E_NOMEM;
     try {
         HIP_CHECK(hipGetDevice(&P->device));
+        {
+            int ncu = 0;
+            HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, P->device));
+            P->grid_cap = std::max(1, ncu) * 8;
+        }
         P->flags = flags;
         P->sph = (flags & ERI_SPHERICAL) != 0;
         P->screened = quartets == nullptr;
@@ -1053,7 +1075,7 @@ extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, doub
         for (int b = b0; b < b1; ++b) {
             const EriBlock &B = P->blocks[b];
             launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, out + (B.out_off - base),
-                         (hipStream_t)stream);
+                         (hipStream_t)stream, B.n_k1);
         }
     } catch (const HipFail &f) {
         return translate(f);
@@ -1111,7 +1133,7 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
         // 1. integrals of every block
         for (int b = 0; b < nb; ++b) {
             const EriBlock &B = P->blocks[b];
-            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, s);
+            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, s, B.n_k1);
         }
         // 2. per-quartet contributions
         int64_t cbt = 0;

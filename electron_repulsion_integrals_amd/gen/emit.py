@@ -24,6 +24,9 @@ from .graph import (ClassInfo, build_ket_vrr, build_hrr, transform_terms, class_
 
 AX = "xyz"
 
+# cross-lane reads are issued this many ket nodes ahead of their use
+REMOTE_AHEAD = 6
+
 
 def _fmt(v: float) -> str:
     r = repr(float(v))
@@ -148,22 +151,46 @@ def _ket_phase(kv, names: Names, lines, ind="      ", barrier=None, acc_now=None
     the accumulator it is added to immediately (memory tier: before its slot
     can be reused at a later level)."""
     prev_level = None
-    for n in kv.nodes:
+    remote_name = {}
+    nodes = kv.nodes
+    defined = set()
+
+    def issue_remote(j):
+        # a cross-lane read may be issued once its source (previous level) exists
+        m2 = nodes[j]
+        key = (m2.a1, m2.axis)
+        if key in remote_name:
+            return
+        if sum(m2.a1[0]) > 0 and m2.a1 not in defined:
+            return
+        remote_name[key] = f"xr{len(remote_name)}"
+        lines.append(f"{ind}const double {remote_name[key]} = {names.ket_remote(m2.a1, m2.axis)};")
+
+    for idx, n in enumerate(nodes):
         lvl = sum(n.f)
         if barrier and prev_level is not None and lvl != prev_level:
             lines.append(f"{ind}{barrier}")
+        if names.tier == "V":
+            # sliding window: issue the reads of the next REMOTE_AHEAD nodes now so
+            # that their LDS latency overlaps the arithmetic in between
+            for j in range(idx, min(len(nodes), idx + REMOTE_AHEAD + 1)):
+                issue_remote(j)
+            issue_remote(idx)
         prev_level = lvl
         a = AX[n.axis]
         expr = f"QC{a} * {names.ket(n.a0)} + WQ{a} * {names.ket(n.a1)}"
         if n.b0 is not None:
             expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
-        if names.tier == "V" or sum(n.a1[0]) > 0:
+        if names.tier == "V":
+            expr += f" + eh{a} * {remote_name[(n.a1, n.axis)]}"
+        elif sum(n.a1[0]) > 0:
             expr += f" + eh{a} * {names.ket_remote(n.a1, n.axis)}"
         else:
             # memory tier, coupling to the remote lane's bra-phase value
             expr += f" + eh{a} * S1L({n.a1[1]}, src{a})"
         if names.tier == "V":
             lines.append(f"{ind}const double {names.ket((n.f, n.m))} = {expr};")
+            defined.add((n.f, n.m))
         else:
             lines.append(f"{ind}{{ const double t_ = {expr}; {names.ket_store((n.f, n.m), 't_')};")
             if acc_now is not None and (n.f, n.m) in acc_now:
@@ -195,6 +222,15 @@ def _hrr_block(l1, l2, base_expr, R, out_prefix, spherical, lines, ind="  ", dec
         for x in xs:
             for y in ys:
                 outs.append(name[(x, y)])
+    elif max(l1, l2) <= 2:
+        # both indices at once: out = sum over non-zeros of t(l1) x t(l2)
+        Ty, Tx = transform_terms(l2), transform_terms(l1)
+        for li, rowx in enumerate(Tx):
+            for si, rowy in enumerate(Ty):
+                terms = [f"{_fmt(cx * cy)} * {name[(xs[xi], ys[yi])]}" for xi, cx in rowx for yi, cy in rowy]
+                nm = f"{out_prefix}u{li}_{si}"
+                lines.append(f"{ind}const double {nm} = {' + '.join(terms)};")
+                outs.append(nm)
     else:
         Ty, Tx = transform_terms(l2), transform_terms(l1)
         # y first
@@ -301,6 +337,32 @@ def _emit_ops_mem(ops, base_expr, outs, store, slot_base, lines, ind):
 # ---------------------------------------------------------------------------
 
 def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
+    """Two kernels per class: general (contracted) and K4 = 1 (no accumulators).
+
+    Both run a persistent grid-stride loop over groups of Q quartets and load the
+    next group's indices, pair records and centres while the current group
+    computes, so the dependent load chain of a quartet is hidden.
+    """
+    out = [f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {class_id(ci.la, ci.lb, ci.lc, ci.ld)}, "
+           f"{'spherical' if spherical else 'Cartesian'} output, register tier: {ci.G} lanes per quartet, "
+           f"{64 // ci.G} quartets per wave",
+           '#include "eri_device.h"', ""]
+    out += _register_kernel(ci, spherical, k1=False)
+    out += _register_kernel(ci, spherical, k1=True)
+    return "\n".join(out) + "\n"
+
+
+REC_FIELDS = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
+              "i2z", "i2e", "roz", "roe", "i2ze"]
+
+
+def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
+    """K4 = 1 kernel: persistent loop, next group's inputs prefetched.
+    General kernel: one group of Q quartets per wave; the primitive quartets are
+    set up in chunks of G -- each lane computes the geometry and Boys values of a
+    different primitive quartet into LDS (field-major, so the writes are
+    conflict-free and the group's reads are broadcasts) -- then the group runs the
+    recurrence over the chunk."""
     kv = build_ket_vrr(ci.lc, ci.Lk)
     names = Names("V", kv, ci.Lk)
     G = ci.G
@@ -310,117 +372,195 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
     EOFF = ci.e_bra_offset
     BLK = ci.nout(spherical)
     cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
-    tag = f"c{cid}_{'s' if spherical else 'c'}"
+    tag = f"c{cid}_{'s' if spherical else 'c'}" + ("_k1" if k1 else "")
     lanes = ci.lanes
     lpos = {e: i for i, e in enumerate(lanes)}
-    tx = [e[0] for e in lanes]
-    ty = [e[1] for e in lanes]
-    tz = [e[2] for e in lanes]
-    dx = [lpos[sub(e, 0)] if e[0] > 0 else -1 for e in lanes]
-    dy = [lpos[sub(e, 1)] if e[1] > 0 else -1 for e in lanes]
-    dz = [lpos[sub(e, 2)] if e[2] > 0 else -1 for e in lanes]
+    lane_tab = []
+    for e in lanes:
+        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
+        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
     targets = kv.targets
     L = ci.L
-
+    NREC = len(REC_FIELDS) + L + 1
+    use_rec = (not k1) and G > 1
     o = []
-    o.append(f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {cid}, {'spherical' if spherical else 'Cartesian'} output,"
-             f" register tier: {G} lanes per quartet, {Q} quartets per wave")
-    o.append('#include "eri_device.h"')
     o.append("namespace {")
-    o.append(f"__constant__ signed char k_{tag}_lane[4][{G}] = {{")
-    for arr in (tx, ty, tz):
-        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
-    o.append("  {0}};")
-    o.append(f"__constant__ signed char k_{tag}_down[3][{G}] = {{")
-    for arr in (dx, dy, dz):
-        o.append("  {" + ", ".join(str(v) for v in arr) + "},")
-    o.append("};")
+    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
     o.append("}  // namespace")
-    o.append("")
     o.append(f"__global__ void __launch_bounds__(64) eri_kernel_{tag}(EriClassArgs a)")
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append("  __shared__ double xch[Q * NEB * NK];")
+    o.append("  __shared__ double xab[Q * 3];")
+    if use_rec:
+        o.append(f"  constexpr int NREC = {NREC};")
+        o.append("  __shared__ double rec[NREC * 64];  // field-major primitive-quartet records")
     o.append("  const int lane = threadIdx.x;")
     o.append("  int grp = lane / G, sub = lane - grp * G;")
     o.append("  if (grp >= Q) { grp = Q; sub = 0; }  // padding lanes: phantom group, e = (0,0,0)")
-    o.append("  const int q0 = blockIdx.x * Q;")
-    o.append("  int qs = q0 + (grp < Q ? grp : 0);")
-    o.append("  if (qs >= a.nq) qs = a.nq - 1;  // idle groups recompute the last quartet and never store")
-    o.append(f"  const int ex = k_{tag}_lane[0][sub], ey = k_{tag}_lane[1][sub], ez = k_{tag}_lane[2][sub];")
-    o.append("  const int es = ex + ey + ez;")
+    o.append(f"  const int lt = k_{tag}_lane[sub];")
+    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
     o.append("  const int gb = grp * G;")
-    o.append(f"  const int adx = (ex > 0 ? gb + k_{tag}_down[0][sub] : lane) * 4;")
-    o.append(f"  const int ady = (ey > 0 ? gb + k_{tag}_down[1][sub] : lane) * 4;")
-    o.append(f"  const int adz = (ez > 0 ? gb + k_{tag}_down[2][sub] : lane) * 4;")
-    o.append("  (void)adx; (void)ady; (void)adz;")
-    o.append("  const int bra = a.qbra[qs], ket = a.qket[qs];")
-    o.append("  const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
-    o.append("  const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
-    o.append("  const double CDx = Cx - a.cen[3 * pk.y], CDy = Cy - a.cen[3 * pk.y + 1], CDz = Cz - a.cen[3 * pk.y + 2];")
-    o.append("  const double ACx = a.cen[3 * pb.x] - Cx, ACy = a.cen[3 * pb.x + 1] - Cy, ACz = a.cen[3 * pb.x + 2] - Cz;")
-    o.append("  (void)CDx; (void)CDy; (void)CDz;")
-    for t in range(len(targets)):
-        o.append(f"  double acc{t} = 0.0;")
-    o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
-    o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
-    o.append("    for (int ik = 0; ik < pk.w; ++ik) {")
-    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
-    o.append("      EriQuartetGeom g;")
-    o.append("      eri_geom(P, K, ACx, ACy, ACz, g);")
-    o.append("      const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
-    o.append("      const double WPx = g.WP[0], WPy = g.WP[1], WPz = g.WP[2];")
-    o.append("      const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
-    o.append("      const double WQx = g.WQ[0], WQy = g.WQ[1], WQz = g.WQ[2];")
-    o.append("      const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = g.roz, roe = g.roe;")
-    o.append("      const double ehx = ex * g.i2ze, ehy = ey * g.i2ze, ehz = ez * g.i2ze;")
-    o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
-    o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-    o.append(f"      double F[{L + 1}];")
-    o.append(f"      eri_boys<{L}>(g.T, g.pref, a.boys, F);")
-    _stage1(ci, kv.base_m, o)
-    _ket_phase(kv, names, o)
-    for t, (f, m) in enumerate(targets):
-        o.append(f"      acc{t} += {names.ket((f, m))};")
-    o.append("    }")
-    o.append("  }")
-    # H1: ket HRR + transform per lane
+    o.append("  const int adx = (ex > 0 ? gb + ((lt >> 12) & 63) - 1 : lane) * 4;")
+    o.append("  const int ady = (ey > 0 ? gb + ((lt >> 18) & 63) - 1 : lane) * 4;")
+    o.append("  const int adz = (ez > 0 ? gb + ((lt >> 24) & 63) - 1 : lane) * 4;")
+    o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
+    o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
+    o.append("  int g = blockIdx.x;")
+    o.append("  if (g >= ngroups) return;")
+    o.append("  auto slot_of = [&](int gg) { int q = gg * Q + (grp < Q ? grp : 0); return q < a.nq ? q : a.nq - 1; };")
+    o.append("  int qs = slot_of(g);")
+    o.append("  int bra = a.qbra[qs], ket = a.qket[qs];")
+    o.append("  int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
+    o.append("  for (;;) {")
+    o.append("    const int gn = g + (int)gridDim.x;")
+    if k1:
+        o.append("    const int qn = slot_of(gn < ngroups ? gn : g);")
+        o.append("    const int bra_n = a.qbra[qn], ket_n = a.qket[qn];")
+    o.append("    const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
+    o.append("    const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
+    o.append("    const double CDx = Cx - a.cen[3 * pk.y], CDy = Cy - a.cen[3 * pk.y + 1], CDz = Cz - a.cen[3 * pk.y + 2];")
+    o.append("    const double ABx = Ax - a.cen[3 * pb.y], ABy = Ay - a.cen[3 * pb.y + 1], ABz = Az - a.cen[3 * pb.y + 2];")
+    o.append("    const double ACx = Ax - Cx, ACy = Ay - Cy, ACz = Az - Cz;")
+    o.append("    (void)CDx; (void)CDy; (void)CDz;")
+
+    def geom_lines(ind, pp_b, pp_k):
+        r = []
+        r.append(f"{ind}const EriPrimPair P = eri_load_pp(a.ppd, {pp_b});")
+        r.append(f"{ind}const EriPrimPair K = eri_load_pp(a.ppd, {pp_k});")
+        r.append(f"{ind}EriQuartetGeom gq;")
+        r.append(f"{ind}eri_geom(P, K, ACx, ACy, ACz, gq);")
+        r.append(f"{ind}double F[{L + 1}];")
+        r.append(f"{ind}eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
+        return r
+
+    def scalars_from_geom(ind):
+        r = []
+        r.append(f"{ind}const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
+        r.append(f"{ind}const double WPx = gq.WP[0], WPy = gq.WP[1], WPz = gq.WP[2];")
+        r.append(f"{ind}const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
+        r.append(f"{ind}const double WQx = gq.WQ[0], WQy = gq.WQ[1], WQz = gq.WQ[2];")
+        r.append(f"{ind}const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = gq.roz, roe = gq.roe, i2ze = gq.i2ze;")
+        return r
+
+    def body(ind):
+        r = []
+        r.append(f"{ind}const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
+        r.append(f"{ind}(void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+        r.append(f"{ind}(void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+        _stage1(ci, kv.base_m, r, ind)
+        _ket_phase(kv, names, r, ind)
+        return r
+
     tpos = {f: t for t, (f, m) in enumerate(targets)}
-    nk = _hrr_block(ci.lc, ci.ld, lambda e: f"acc{tpos[e]}", "CD", "y", spherical, o, "  ")
+    if k1:
+        o.append("    {")
+        o += geom_lines("      ", "pb.z", "pk.z")
+        o += scalars_from_geom("      ")
+        o += body("      ")
+        base_of = lambda e: names.ket((e, 0))
+        hind = "      "
+    elif not use_rec:
+        for t in range(len(targets)):
+            o.append(f"    double acc{t} = 0.0;")
+        o.append("    for (int ib = 0; ib < pb.w; ++ib) {")
+        o.append("      for (int ik = 0; ik < pk.w; ++ik) {")
+        o += geom_lines("        ", "pb.z + ib", "pk.z + ik")
+        o += scalars_from_geom("        ")
+        o += body("        ")
+        for t, (f, m) in enumerate(targets):
+            o.append(f"        acc{t} += {names.ket((f, m))};")
+        o.append("      }")
+        o.append("    }")
+        base_of = lambda e: f"acc{tpos[e]}"
+        hind = "    "
+    else:
+        for t in range(len(targets)):
+            o.append(f"    double acc{t} = 0.0;")
+        o.append("    const int K4 = pb.w * pk.w;")
+        o.append("    for (int c0 = 0; c0 < K4; c0 += G) {")
+        o.append("      {  // this lane's primitive quartet of the chunk -> LDS record")
+        o.append("        const int t = c0 + sub < K4 ? c0 + sub : K4 - 1;")
+        o.append("        const int ib = t / pk.w, ik = t - ib * pk.w;")
+        o += geom_lines("        ", "pb.z + ib", "pk.z + ik")
+        vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
+                "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
+        o.append("        double* r = rec + lane;")
+        for fi, v in enumerate(vals):
+            o.append(f"        r[{fi} * 64] = {v};")
+        for m in range(L + 1):
+            o.append(f"        r[{len(vals) + m} * 64] = F[{m}];")
+        o.append("      }")
+        o.append("      __syncthreads();")
+        o.append("      const int n = K4 - c0 < G ? K4 - c0 : G;")
+        o.append("      for (int j = 0; j < n; ++j) {")
+        o.append("        const double* r = rec + gb + j;")
+        for fi, nm in enumerate(REC_FIELDS):
+            o.append(f"        const double {nm} = r[{fi} * 64];")
+        o.append(f"        double F[{L + 1}];")
+        for m in range(L + 1):
+            o.append(f"        F[{m}] = r[{len(REC_FIELDS) + m} * 64];")
+        o += body("        ")
+        for t, (f, m) in enumerate(targets):
+            o.append(f"        acc{t} += {names.ket((f, m))};")
+        o.append("      }")
+        o.append("      __syncthreads();  // records are rewritten by the next chunk")
+        o.append("    }")
+        base_of = lambda e: f"acc{tpos[e]}"
+        hind = "    "
+    # H1: ket HRR + transform per lane
+    nk = _hrr_block(ci.lc, ci.ld, base_of, "CD", "y", spherical, o, hind)
     assert nk == NK
-    o.append(f"  if (grp < Q && es >= {ci.la}) {{")
-    o.append(f"    double* dst = xch + (grp * NEB + (sub - {EOFF})) * NK;")
+    o.append(f"{hind}if (grp < Q && es >= {ci.la}) {{")
+    o.append(f"{hind}  double* dst = xch + (grp * NEB + (sub - {EOFF})) * NK;")
     for k in range(NK):
-        o.append(f"    dst[{k}] = y{k};")
-    o.append("  }")
-    o.append("  __syncthreads();")
+        o.append(f"{hind}  dst[{k}] = y{k};")
+    o.append(f"{hind}}}")
+    o.append(f"{hind}if (grp < Q && sub == 0) {{ xab[3 * grp] = ABx; xab[3 * grp + 1] = ABy; xab[3 * grp + 2] = ABz; }}")
+    if k1:
+        o.append("    }")
+    o.append("    __syncthreads();")
+    if k1:
+        o.append("    const int4 pb_n = a.pair_info[bra_n], pk_n = a.pair_info[ket_n];")
     # H2: lanes own ket components
-    o.append("  for (int t = lane; t < Q * NK; t += 64) {")
-    o.append("    const int g2 = t / NK, kap = t - g2 * NK;")
-    o.append("    const int slot = q0 + g2;")
-    o.append("    if (slot >= a.nq) continue;")
-    o.append("    const int4 pb2 = a.pair_info[a.qbra[slot]];")
-    o.append("    const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
-             " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
-    o.append("    (void)ABx; (void)ABy; (void)ABz;")
-    o.append("    const double* src = xch + g2 * NEB * NK + kap;")
+    o.append("    const int q0 = g * Q;")
+    o.append("    for (int t = lane; t < Q * NK; t += 64) {")
+    o.append("      const int g2 = t / NK, kap = t - g2 * NK;")
+    o.append("      const int slot = q0 + g2;")
+    o.append("      if (slot >= a.nq) continue;")
+    o.append("      const double ABx = xab[3 * g2], ABy = xab[3 * g2 + 1], ABz = xab[3 * g2 + 2];")
+    o.append("      (void)ABx; (void)ABy; (void)ABz;")
+    o.append("      const double* src = xch + g2 * NEB * NK + kap;")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
     for i, e in enumerate(ebra):
-        o.append(f"    const double xe{i} = src[{i} * NK];")
-    nb = _hrr_block(ci.la, ci.lb, lambda e: f"xe{epos[e]}", "AB", "z", spherical, o, "    ")
-    o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
+        o.append(f"      const double xe{i} = src[{i} * NK];")
+    nb = _hrr_block(ci.la, ci.lb, lambda e: f"xe{epos[e]}", "AB", "z", spherical, o, "      ")
+    o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
     for k in range(nb):
-        o.append(f"    dst[{k} * NK] = z{k};")
+        o.append(f"      dst[{k} * NK] = z{k};")
+    o.append("    }")
+    o.append("    if (gn >= ngroups) break;")
+    o.append("    __syncthreads();  // exchange buffer reused by the next group")
+    if k1:
+        o.append("    g = gn; qs = qn; bra = bra_n; ket = ket_n; pb = pb_n; pk = pk_n;")
+    else:
+        o.append("    g = gn; qs = slot_of(g); bra = a.qbra[qs]; ket = a.qket[qs];")
+        o.append("    pb = a.pair_info[bra]; pk = a.pair_info[ket];")
     o.append("  }")
     o.append("}")
     o.append("")
     o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
     o.append("{")
-    o.append(f"  const int nblk = (a.nq + {Q} - 1) / {Q};")
+    o.append(f"  const int ngroups = (a.nq + {Q} - 1) / {Q};")
+    if k1:
+        o.append("  const int nblk = ngroups < a.grid_cap ? ngroups : a.grid_cap;")
+    else:
+        o.append("  const int nblk = ngroups;  // one group per workgroup")
     o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3(64), 0, s, a);")
     o.append("}")
-    return "\n".join(o) + "\n"
+    o.append("")
+    return o
 
 
 def tier_of(ci: ClassInfo) -> str:
@@ -456,11 +596,14 @@ def generate(out_dir: str, lmax: int = 4, classes=None):
     d = ['#include "eri_device.h"', ""]
     for cid, sph, tag, tier, ci in entries:
         d.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s);")
+        if tier == "V":
+            d.append(f"void eri_launch_{tag}_k1(const EriClassArgs& a, hipStream_t s);")
     d.append("")
     d.append("EriClassEntry eri_class_table[] = {")
     for cid, sph, tag, tier, ci in entries:
         scr = memory_tier_scratch_doubles(ci, sph) if tier == "M" else 0
-        d.append(f"  {{{cid}, {1 if sph else 0}, {ci.la}, {ci.lb}, {ci.lc}, {ci.ld}, '{tier}', {scr}, eri_launch_{tag}}},")
+        k1 = f"eri_launch_{tag}_k1" if tier == "V" else f"eri_launch_{tag}"
+        d.append(f"  {{{cid}, {1 if sph else 0}, {ci.la}, {ci.lb}, {ci.lc}, {ci.ld}, '{tier}', {scr}, eri_launch_{tag}, {k1}}},")
     d.append("};")
     d.append(f"const int eri_class_table_size = {len(entries)};")
     fn = os.path.join(out_dir, "eri_dispatch.hip")

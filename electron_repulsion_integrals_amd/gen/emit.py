@@ -24,8 +24,15 @@ from .graph import (ClassInfo, build_ket_vrr, build_hrr, transform_terms, class_
 
 AX = "xyz"
 
-# cross-lane reads are issued this many ket nodes ahead of their use
+# cross-lane reads are issued this many ops ahead of their use, and pinned there:
+# a scheduling barrier that only ALU work may cross keeps the compiler from
+# sinking them back next to their consumers (their LDS latency then overlaps
+# the arithmetic in between)
 REMOTE_AHEAD = 6
+PIN_REMOTE = True
+# a node reading a neighbour's value is scheduled at least this many ops after
+# that value is produced (when anything else is ready)
+REMOTE_DIST = 10
 
 
 def _fmt(v: float) -> str:
@@ -352,6 +359,172 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
     return "\n".join(out) + "\n"
 
 
+
+
+# ---------------------------------------------------------------------------
+# liveness-ordered emission of a lane's straight-line graph (register tier)
+# ---------------------------------------------------------------------------
+
+def _lane_ops(ci, kv, names, spherical, k1, store_prefix="xd"):
+    """Ops of one lane as (key, deps, sink, emit(remote_name) -> C lines).
+
+    k1: ket recurrence -> ket HRR -> ket transform -> exchange stores.
+    otherwise: ket recurrence -> accumulator adds (inside the primitive loop).
+    """
+    ops = []
+    for n in kv.nodes:
+        ds = [("k",) + n.a0, ("k",) + n.a1] + ([("k",) + n.b0, ("k",) + n.b1] if n.b0 else [])
+
+        def emit(rn, n=n):
+            a = AX[n.axis]
+            expr = f"QC{a} * {names.ket(n.a0)} + WQ{a} * {names.ket(n.a1)}"
+            if n.b0 is not None:
+                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            expr += f" + eh{a} * {rn}"
+            return [f"const double {names.ket((n.f, n.m))} = {expr};"]
+        ops.append((("k", n.f, n.m), ds, False, emit, (n.a1, n.axis)))
+    if not k1:
+        for t, tg in enumerate(kv.targets):
+            src = ("k",) + tg
+            ops.append((("acc", t), [src] if sum(tg[0]) > 0 else [], True,
+                        (lambda rn, t=t, tg=tg: [f"acc{t} += {names.ket(tg)};"]), None))
+        return ops
+    hn, base = build_hrr(ci.lc, ci.ld)
+    key = {(e, (0, 0, 0)): ("k", e, 0) for e in base}
+    cname = {}
+
+    def nm(k):
+        if k[0] == "k":
+            return names.ket((k[1], k[2]))
+        return cname[k]
+    for i, n in enumerate(hn):
+        k = ("h", n.x, n.y)
+        cname[k] = f"yh{i}"
+        hi, lo = key[n.p_hi], key[n.p_lo]
+        ops.append((k, [hi, lo], False,
+                    (lambda rn, k=k, hi=hi, lo=lo, ax=n.axis: [f"const double {cname[k]} = {nm(hi)} + CD{AX[ax]} * {nm(lo)};"]),
+                    None))
+        key[(n.x, n.y)] = k
+    xs, ys = components(ci.lc), components(ci.ld)
+    outs = []
+    if not spherical:
+        outs = [key[(x, y)] for x in xs for y in ys]
+    elif max(ci.lc, ci.ld) <= 2:
+        Ty, Tx = transform_terms(ci.ld), transform_terms(ci.lc)
+        for li, rowx in enumerate(Tx):
+            for si, rowy in enumerate(Ty):
+                k = ("u", li, si)
+                cname[k] = f"yu{li}_{si}"
+                terms = [(cx * cy, key[(xs[xi], ys[yi])]) for xi, cx in rowx for yi, cy in rowy]
+                ops.append((k, [t for _, t in terms], False,
+                            (lambda rn, k=k, terms=terms: [f"const double {cname[k]} = " +
+                                                          " + ".join(f"{_fmt(c)} * {nm(t)}" for c, t in terms) + ";"]),
+                            None))
+                outs.append(k)
+    else:
+        Ty, Tx = transform_terms(ci.ld), transform_terms(ci.lc)
+        for xi, x in enumerate(xs):
+            for si, row in enumerate(Ty):
+                k = ("t", xi, si)
+                cname[k] = f"yt{xi}_{si}"
+                terms = [(c, key[(x, ys[yi])]) for yi, c in row]
+                ops.append((k, [t for _, t in terms], False,
+                            (lambda rn, k=k, terms=terms: [f"const double {cname[k]} = " +
+                                                          " + ".join(f"{_fmt(c)} * {nm(t)}" for c, t in terms) + ";"]),
+                            None))
+        for li, row in enumerate(Tx):
+            for si in range(nsph(ci.ld)):
+                k = ("u", li, si)
+                cname[k] = f"yu{li}_{si}"
+                terms = [(c, ("t", xi, si)) for xi, c in row]
+                ops.append((k, [t for _, t in terms], False,
+                            (lambda rn, k=k, terms=terms: [f"const double {cname[k]} = " +
+                                                          " + ".join(f"{_fmt(c)} * {nm(t)}" for c, t in terms) + ";"]),
+                            None))
+                outs.append(k)
+    for i, ok in enumerate(outs):
+        ops.append((("w", i), [ok], True, (lambda rn, i=i, ok=ok: [f"{store_prefix}[{i}] = {nm(ok)};"]), None))
+    return ops
+
+
+def _emit_scheduled(ops, initial, names, lines, ind, ahead=None):
+    """Order ops by schedule_min_live, issue cross-lane reads `ahead` ops early."""
+    from .graph import schedule_min_live
+    if ahead is None:
+        ahead = REMOTE_AHEAD
+    items = [(k, ds, sink) for (k, ds, sink, _, _) in ops]
+    remote = {k: ("k",) + rem[0] for (k, ds, sink, _, rem) in ops if rem is not None and sum(rem[0][0]) > 0}
+    order = schedule_min_live(items, initial, remote, REMOTE_DIST)
+    by_key = {op[0]: op for op in ops}
+    seq = [by_key[k] for (k, _, _) in order]
+    defined = {("k", (0, 0, 0), m) for (_, _, m) in initial} | set(initial)
+    remote_name = {}
+    pos_def = {}
+    # position at which every value becomes available
+    for p, op in enumerate(seq):
+        pos_def[op[0]] = p
+    # read slot: `ahead` ops before use, not before the source is computed
+    reads_at = {}
+    for p, op in enumerate(seq):
+        rem = op[4]
+        if rem is None:
+            continue
+        (src, axis) = rem
+        skey = ("k",) + src
+        if sum(src[0]) == 0:
+            earliest = 0
+        else:
+            earliest = pos_def[skey] + 1
+        reads_at.setdefault(max(earliest, p - ahead), []).append((rem, skey))
+    for p, op in enumerate(seq):
+        issued = False
+        for rem, skey in reads_at.get(p, []):
+            if rem not in remote_name:
+                remote_name[rem] = f"xr{len(remote_name)}"
+                src, axis = rem
+                lines.append(f"{ind}const double {remote_name[rem]} = {names.ket_remote(src, axis)};")
+                issued = True
+        if issued and PIN_REMOTE:
+            lines.append(f"{ind}__builtin_amdgcn_sched_barrier(0x7);  // ALU may cross, LDS may not")
+        rn = remote_name.get(op[4]) if op[4] is not None else None
+        for l in op[3](rn):
+            lines.append(f"{ind}{l}")
+
+
+
+
+def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, prefix):
+    """HRR + transform of one column, emitted in liveness order.
+
+    base_load(e) -> C expression reading base value (e, 0) (issued where first
+    needed); store(k, expr) -> statement consuming output k.
+    """
+    from .graph import schedule_min_live
+    ops, base, outs = _hrr_ops(l1, l2, R, spherical)
+    items = []
+    code = {}
+    names_ = {}
+
+    def nm(k):
+        return names_[k]
+    for e in base:
+        k = ("b", e)
+        names_[k] = f"{prefix}b{len(names_)}"
+        items.append((k, [], False))
+        code[k] = (lambda k=k, e=e: f"const double {names_[k]} = {base_load(e)};")
+    for i, (k, terms) in enumerate(ops):
+        names_[k] = f"{prefix}o{i}"
+        items.append((k, [src for _, src in terms], False))
+        code[k] = (lambda k=k, terms=terms: f"const double {names_[k]} = " +
+                   " + ".join(nm(src) if c is None else f"{c} * {nm(src)}" for c, src in terms) + ";")
+    for i, ok in enumerate(outs):
+        k = ("w", i)
+        items.append((k, [ok], True))
+        code[k] = (lambda i=i, ok=ok: store(i, nm(ok)))
+    for (k, ds, sink) in schedule_min_live(items, ()):
+        lines.append(f"{ind}{code[k]()}")
+
+
 REC_FIELDS = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
               "i2z", "i2e", "roz", "roe", "i2ze"]
 
@@ -443,13 +616,20 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         r.append(f"{ind}const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = gq.roz, roe = gq.roe, i2ze = gq.i2ze;")
         return r
 
-    def body(ind):
+    init_keys = [("k", (0, 0, 0), m) for m in range(kv.base_m + 1)]
+
+    def body(ind, with_acc):
         r = []
         r.append(f"{ind}const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
         r.append(f"{ind}(void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
         r.append(f"{ind}(void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
         _stage1(ci, kv.base_m, r, ind)
-        _ket_phase(kv, names, r, ind)
+        if with_acc:
+            _emit_scheduled(_lane_ops(ci, kv, names, spherical, False), init_keys, names, r, ind)
+        else:
+            r.append(f"{ind}double xjunk[{NK}];")
+            r.append(f"{ind}double* xd = (grp < Q && es >= {ci.la}) ? xch + (grp * NEB + (sub - {EOFF})) * NK : xjunk;")
+            _emit_scheduled(_lane_ops(ci, kv, names, spherical, True), init_keys, names, r, ind)
         return r
 
     tpos = {f: t for t, (f, m) in enumerate(targets)}
@@ -457,8 +637,8 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         o.append("    {")
         o += geom_lines("      ", "pb.z", "pk.z")
         o += scalars_from_geom("      ")
-        o += body("      ")
-        base_of = lambda e: names.ket((e, 0))
+        o += body("      ", False)
+        base_of = None
         hind = "      "
     elif not use_rec:
         for t in range(len(targets)):
@@ -467,9 +647,7 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         o.append("      for (int ik = 0; ik < pk.w; ++ik) {")
         o += geom_lines("        ", "pb.z + ib", "pk.z + ik")
         o += scalars_from_geom("        ")
-        o += body("        ")
-        for t, (f, m) in enumerate(targets):
-            o.append(f"        acc{t} += {names.ket((f, m))};")
+        o += body("        ", True)
         o.append("      }")
         o.append("    }")
         base_of = lambda e: f"acc{tpos[e]}"
@@ -500,22 +678,17 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         o.append(f"        double F[{L + 1}];")
         for m in range(L + 1):
             o.append(f"        F[{m}] = r[{len(REC_FIELDS) + m} * 64];")
-        o += body("        ")
-        for t, (f, m) in enumerate(targets):
-            o.append(f"        acc{t} += {names.ket((f, m))};")
+        o += body("        ", True)
         o.append("      }")
         o.append("      __syncthreads();  // records are rewritten by the next chunk")
         o.append("    }")
         base_of = lambda e: f"acc{tpos[e]}"
         hind = "    "
-    # H1: ket HRR + transform per lane
-    nk = _hrr_block(ci.lc, ci.ld, base_of, "CD", "y", spherical, o, hind)
-    assert nk == NK
-    o.append(f"{hind}if (grp < Q && es >= {ci.la}) {{")
-    o.append(f"{hind}  double* dst = xch + (grp * NEB + (sub - {EOFF})) * NK;")
-    for k in range(NK):
-        o.append(f"{hind}  dst[{k}] = y{k};")
-    o.append(f"{hind}}}")
+    if not k1:
+        # H1: ket HRR + transform per lane on the contracted values
+        o.append(f"{hind}double yjunk[{NK}];")
+        o.append(f"{hind}double* yd = (grp < Q && es >= {ci.la}) ? xch + (grp * NEB + (sub - {EOFF})) * NK : yjunk;")
+        _emit_hrr_scheduled(ci.lc, ci.ld, base_of, "CD", spherical, lambda k, x: f"yd[{k}] = {x};", o, hind, "y")
     o.append(f"{hind}if (grp < Q && sub == 0) {{ xab[3 * grp] = ABx; xab[3 * grp + 1] = ABy; xab[3 * grp + 2] = ABz; }}")
     if k1:
         o.append("    }")
@@ -533,12 +706,9 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append("      const double* src = xch + g2 * NEB * NK + kap;")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
-    for i, e in enumerate(ebra):
-        o.append(f"      const double xe{i} = src[{i} * NK];")
-    nb = _hrr_block(ci.la, ci.lb, lambda e: f"xe{epos[e]}", "AB", "z", spherical, o, "      ")
     o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
-    for k in range(nb):
-        o.append(f"      dst[{k} * NK] = z{k};")
+    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                        lambda k, x: f"dst[{k} * NK] = {x};", o, "      ", "z")
     o.append("    }")
     o.append("    if (gn >= ngroups) break;")
     o.append("    __syncthreads();  // exchange buffer reused by the next group")

@@ -329,3 +329,85 @@ def dag_flops(ci: ClassInfo, spherical: bool):
         ta = sum(len(r) for r in transform_terms(ci.la))
         once += ci.nket(spherical) * (ncart(ci.la) * tb + nsph(ci.lb) * ta) * 2
     return per_prim, once
+
+
+# ---------------------------------------------------------------------------
+# liveness-aware ordering of a lane's straight-line DAG ("FusionRCG" section
+# III-A: the evaluation order of a fixed graph decides PeakLive, Eq. (4))
+# ---------------------------------------------------------------------------
+
+def peak_live(order, deps, initial=()):
+    """PeakLive of a straight-line order: a value is live from its definition
+    until its last consumer in the order (sinks define nothing)."""
+    last = {}
+    for t, (k, ds, sink) in enumerate(order):
+        for d in ds:
+            last[d] = t
+    live = {k for k in initial if k in last}
+    peak = len(live)
+    for t, (k, ds, sink) in enumerate(order):
+        if not sink and k in last:
+            live.add(k)
+        peak = max(peak, len(live))
+        for d in ds:
+            if last.get(d) == t:
+                live.discard(d)
+    return peak
+
+
+def schedule_min_live(items, initial=(), remote=None, min_dist=0):
+    """Greedy list scheduling that keeps few values live.
+
+    items: [(key, deps, sink)] in any topological order.  At each step, among
+    the ready items, pick the one that frees the most values net of the one it
+    creates; ties go to the item whose value is needed soonest by a ready-ish
+    consumer (most recently readied operand chain), then to the original order.
+    This plays the role of the page's DSA heuristic (Eq. (7)) on our graphs.
+
+    remote: optional {key: source key} of a cross-lane operand; such an item is
+    deferred (while anything else is ready) until its source was produced at
+    least ``min_dist`` steps earlier, so the cross-lane read can be issued that
+    far ahead of its use.
+    """
+    remote = remote or {}
+    n = len(items)
+    idx_of = {k: i for i, (k, ds, s) in enumerate(items)}
+    uses = {}
+    consumers = {}
+    for i, (k, ds, s) in enumerate(items):
+        for d in ds:
+            uses[d] = uses.get(d, 0) + 1
+            consumers.setdefault(d, []).append(i)
+    avail = set(initial)
+    missing = [sum(1 for d in ds if d in idx_of) for (k, ds, s) in items]
+    ready = {i for i in range(n) if missing[i] == 0}
+    done = [False] * n
+    order = []
+    stamp = {i: 0 for i in ready}
+    clock = 0
+    born = {}
+    while ready:
+        best, bscore = None, None
+        for i in ready:
+            k, ds, s = items[i]
+            freed = sum(1 for d in set(ds) if uses.get(d, 0) == ds.count(d) and d not in ())
+            rs = remote.get(k)
+            early = rs is not None and rs in born and clock - born[rs] < min_dist
+            score = (not early, freed - (0 if s else 1), stamp[i], -i)
+            if bscore is None or score > bscore:
+                best, bscore = i, score
+        ready.remove(best)
+        done[best] = True
+        k, ds, s = items[best]
+        order.append(items[best])
+        born[k] = clock
+        for d in ds:
+            uses[d] -= 1
+        clock += 1
+        for c in consumers.get(k, []):
+            missing[c] -= 1
+            if missing[c] == 0:
+                ready.add(c)
+                stamp[c] = clock
+    assert len(order) == n, "cycle or missing dependency"
+    return order

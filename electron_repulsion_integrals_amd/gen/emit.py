@@ -734,12 +734,9 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
 
 
 def tier_of(ci: ClassInfo) -> str:
-    """Register tier when a lane group fits one wave and the live set is modest."""
-    if ci.G > 64:
-        return "M"
-    kv = build_ket_vrr(ci.lc, ci.Lk)
-    est = ket_vrr_peak_live(kv) + len(kv.targets) + 2 * (ci.L + 1) + 30
-    return "V" if est <= 120 else "M"
+    """Register tier whenever a lane group fits one wave (the compiler may keep
+    part of a large live set in AGPRs); memory tier for wider bra groups."""
+    return "V" if ci.G <= 64 else "M"
 
 
 def generate(out_dir: str, lmax: int = 4, classes=None):
@@ -800,14 +797,31 @@ def _count_private(ops, outs):
     return _emit_ops_mem(ops, lambda e: "0.0", outs, lambda i, x: f"(void)({x});", 0, lines, "")
 
 
+def _coupling_levels(kv):
+    """Per ket level k >= 1: the values of level k-1 read across lanes by level k."""
+    levels = {}
+    for n in kv.nodes:
+        levels.setdefault(sum(n.f), [])
+        if n.a1 not in levels[sum(n.f)]:
+            levels[sum(n.f)].append(n.a1)
+    return levels
+
+
+def mem_lds_doubles(ci: ClassInfo) -> int:
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    W = 64 * ((ci.G + 63) // 64)
+    lv = _coupling_levels(kv)
+    return (max((len(v) for v in lv.values()), default=0)) * W
+
+
 def _mem_layout(ci: ClassInfo, spherical: bool):
     kv = build_ket_vrr(ci.lc, ci.Lk)
-    slot_of, nk_slots = _alloc_slots(kv)
+    slot_of, nk_slots = {}, 0  # ket values live in registers (coupling through LDS)
     ntg = len(kv.targets)
     ops1, _, outs1 = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
     ops2, _, outs2 = _hrr_ops(ci.la, ci.lb, "AB", spherical)
-    npriv = max(nk_slots, _count_private(ops1, outs1), _count_private(ops2, outs2))
-    # layout (units of W doubles): [ket slots | private HRR slots][acc][exchange NK]
+    npriv = max(_count_private(ops1, outs1), _count_private(ops2, outs2))
+    # layout (units of W doubles): [private HRR slots][acc][exchange NK]
     acc0 = npriv
     xch0 = acc0 + ntg
     nslots = xch0 + ci.nket(spherical)
@@ -816,14 +830,14 @@ def _mem_layout(ci: ClassInfo, spherical: bool):
 
 
 def memory_tier_scratch_doubles(ci: ClassInfo, spherical: bool) -> int:
-    """Scratch doubles per workgroup: graph slots x lanes + the bra-phase copy."""
+    """Scratch doubles per workgroup: (HRR slots + accumulators + exchange) x lanes."""
     kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
-    return nslots * W + (kv.base_m + 1) * W
+    return nslots * W
 
 
 def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
-    names = Names("M", kv, ci.Lk, slot_of)
+    names = Names("V", kv, ci.Lk)
     G = ci.G
     NK = ci.nket(spherical)
     NEB = ci.n_ebra
@@ -841,7 +855,6 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     dz = [lpos[sub(e, 2)] if e[2] > 0 else -1 for e in lanes]
     targets = kv.targets
     L = ci.L
-    S1 = nslots  # bra-phase copy rows start here (base_m + 1 rows)
     o = []
     o.append(f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {cid}, {'spherical' if spherical else 'Cartesian'} output,"
              f" memory tier: {G} lanes (workgroup {W}) per quartet, {nslots} scratch slots")
@@ -862,6 +875,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append(f"  constexpr int G = {G}, W = {W}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append(f"  constexpr size_t WG_DOUBLES = {memory_tier_scratch_doubles(ci, spherical)};")
     o.append("  const int tid = threadIdx.x;")
+    o.append(f"  __shared__ double xl[{max(1, mem_lds_doubles(ci))}];  // one ket level's cross-lane values")
     o.append("  const int sub = tid < G ? tid : 0;  // lanes beyond G shadow e = (0,0,0) and never store")
     o.append("  const bool real = tid < G;")
     # Every graph value lives in this workgroup's scratch slice, addressed by
@@ -873,7 +887,6 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("#define SLD(s) eri_bld(rs, vo, (s) * (W * 8))")
     o.append("#define SST(s, x) eri_bst(rs, vo, (s) * (W * 8), (x))")
     o.append("#define SLDL(s, l) eri_bld(rs, (l) * 8, (s) * (W * 8))")
-    o.append(f"#define S1L(m, l) eri_bld(rs, (l) * 8, ({S1} + (m)) * (W * 8))")
     o.append(f"  const int ex = k_{tag}_lane[0][sub], ey = k_{tag}_lane[1][sub], ez = k_{tag}_lane[2][sub];")
     o.append("  const int es = ex + ey + ez;")
     o.append(f"  const int srcx = ex > 0 ? k_{tag}_down[0][sub] : tid;")
@@ -906,15 +919,34 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append(f"      double F[{L + 1}];")
     o.append(f"      eri_boys<{L}>(g.T, g.pref, a.boys, F);")
     _stage1(ci, kv.base_m, o)
-    # publish the bra-phase values for remote reads, then barrier
-    for m in range(kv.base_m + 1):
-        o.append(f"      eri_bst(rs, vo, ({S1} + {m}) * (W * 8), s1_{m});")
-    o.append("      __syncthreads();")
-    acc_now = {tg: f"{acc0 + t}" for t, tg in enumerate(targets) if sum(tg[0]) > 0}
+    # ket phase: own values in registers (level order); the coupling operand of
+    # level k is read from an LDS buffer holding level k-1's cross-lane values
+    lv = _coupling_levels(kv)
     for t, tg in enumerate(targets):
         if sum(tg[0]) == 0:
-            o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + {names.ket(tg)});")
-    _ket_phase(kv, names, o, barrier="__syncthreads();", acc_now=acc_now)
+            o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + s1_{tg[1]});")
+    tpos_all = {tg: t for t, tg in enumerate(targets)}
+    levels = sorted({sum(n.f) for n in kv.nodes})
+    for k in levels:
+        # publish level k-1 values that level k reads across lanes
+        o.append("      __syncthreads();")
+        for j, key in enumerate(lv[k]):
+            val = f"s1_{key[1]}" if sum(key[0]) == 0 else names.ket(key)
+            o.append(f"      xl[{j} * W + tid] = {val};")
+        o.append("      __syncthreads();")
+        for n in kv.nodes:
+            if sum(n.f) != k:
+                continue
+            a = AX[n.axis]
+            j = lv[k].index(n.a1)
+            expr = f"QC{a} * {names.ket(n.a0)} + WQ{a} * {names.ket(n.a1)}"
+            if n.b0 is not None:
+                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            expr += f" + eh{a} * xl[{j} * W + src{a}]"
+            o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
+            if (n.f, n.m) in tpos_all:
+                t = tpos_all[(n.f, n.m)]
+                o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + {names.ket((n.f, n.m))});")
     o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
     o.append("    }")
     o.append("  }")
@@ -945,7 +977,6 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("#undef SLD")
     o.append("#undef SST")
     o.append("#undef SLDL")
-    o.append("#undef S1L")
     o.append("}")
     o.append("")
     o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")

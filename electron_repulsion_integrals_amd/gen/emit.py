@@ -814,6 +814,14 @@ def mem_lds_doubles(ci: ClassInfo) -> int:
     return (max((len(v) for v in lv.values()), default=0)) * W
 
 
+def mem_acc_in_registers(ci: ClassInfo) -> bool:
+    """Memory tier: keep the contraction accumulators in registers when they
+    fit beside the ket recurrence's live set (VGPRs + AGPRs at occupancy 1)."""
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    live = ket_vrr_peak_live(kv) if kv.nodes else 0
+    return live + len(kv.targets) <= 170
+
+
 def _mem_layout(ci: ClassInfo, spherical: bool):
     kv = build_ket_vrr(ci.lc, ci.Lk)
     slot_of, nk_slots = {}, 0  # ket values live in registers (coupling through LDS)
@@ -900,12 +908,22 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("  const double CDx = Cx - a.cen[3 * pk.y], CDy = Cy - a.cen[3 * pk.y + 1], CDz = Cz - a.cen[3 * pk.y + 2];")
     o.append("  const double ACx = a.cen[3 * pb.x] - Cx, ACy = a.cen[3 * pb.x + 1] - Cy, ACz = a.cen[3 * pb.x + 2] - Cz;")
     o.append("  (void)CDx; (void)CDy; (void)CDz;")
-    for t in range(len(targets)):
-        o.append(f"  SST({acc0 + t}, 0.0);")
-    o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
-    o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
-    o.append("    for (int ik = 0; ik < pk.w; ++ik) {")
-    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
+    acc_reg = mem_acc_in_registers(ci)
+    if acc_reg:
+        for t in range(len(targets)):
+            o.append(f"  double acc{t} = 0.0;")
+    else:
+        for t in range(len(targets)):
+            o.append(f"  SST({acc0 + t}, 0.0);")
+    # one flat loop over primitive quartets; the next pair records are loaded
+    # while the current primitive quartet is evaluated
+    o.append("  const int K4 = pb.w * pk.w;")
+    o.append("  EriPrimPair Pn = eri_load_pp(a.ppd, pb.z), Kn = eri_load_pp(a.ppd, pk.z);")
+    o.append("  for (int pq = 0, ib = 0, ik = 0; pq < K4; ++pq) {")
+    o.append("    {")
+    o.append("      const EriPrimPair P = Pn, K = Kn;")
+    o.append("      if (++ik == pk.w) { ik = 0; ++ib; }")
+    o.append("      if (pq + 1 < K4) { Pn = eri_load_pp(a.ppd, pb.z + ib); Kn = eri_load_pp(a.ppd, pk.z + ik); }")
     o.append("      EriQuartetGeom g;")
     o.append("      eri_geom(P, K, ACx, ACy, ACz, g);")
     o.append("      const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
@@ -922,12 +940,28 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     # ket phase: own values in registers (level order); the coupling operand of
     # level k is read from an LDS buffer holding level k-1's cross-lane values
     lv = _coupling_levels(kv)
-    for t, tg in enumerate(targets):
-        if sum(tg[0]) == 0:
-            o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + s1_{tg[1]});")
+
+    def acc_add(t, val):
+        if acc_reg:
+            o.append(f"      acc{t} += {val};")
+        else:
+            o.append(f"      SST({acc0 + t}, ap{t} + {val});")
+
+    def acc_fetch(ts):
+        # scratch accumulators of one level are read in one batch, before the
+        # level's barrier, so that their latency overlaps it
+        if not acc_reg:
+            for t in ts:
+                o.append(f"      const double ap{t} = SLD({acc0 + t});")
+
     tpos_all = {tg: t for t, tg in enumerate(targets)}
+    base_t = [t for t, tg in enumerate(targets) if sum(tg[0]) == 0]
+    acc_fetch(base_t)
+    for t in base_t:
+        acc_add(t, f"s1_{targets[t][1]}")
     levels = sorted({sum(n.f) for n in kv.nodes})
     for k in levels:
+        acc_fetch([t for t, tg in enumerate(targets) if sum(tg[0]) == k])
         # publish level k-1 values that level k reads across lanes
         o.append("      __syncthreads();")
         for j, key in enumerate(lv[k]):
@@ -945,11 +979,13 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
             expr += f" + eh{a} * xl[{j} * W + src{a}]"
             o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
             if (n.f, n.m) in tpos_all:
-                t = tpos_all[(n.f, n.m)]
-                o.append(f"      SST({acc0 + t}, SLD({acc0 + t}) + {names.ket((n.f, n.m))});")
+                acc_add(tpos_all[(n.f, n.m)], names.ket((n.f, n.m)))
     o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
     o.append("    }")
     o.append("  }")
+    if acc_reg:
+        for t in range(len(targets)):
+            o.append(f"  SST({acc0 + t}, acc{t});")
     # H1 per lane, reading the accumulators; intermediates in private slots of
     # the (now dead) ket region, results straight into the exchange slots
     tpos = {f: t for t, (f, m) in enumerate(targets)}

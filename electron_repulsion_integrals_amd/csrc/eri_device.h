@@ -20,6 +20,8 @@
 #define ERI_BT_COLS (ERI_BT_MMAX + 2)
 #define ERI_LMAX 4
 #define ERI_PP_STRIDE 10
+// memory-tier grid: at most this many workgroups, each owning one scratch slice
+#define ERI_MEM_WGS 1024
 
 struct EriPrimPair {
     double zeta;   // alpha + beta

@@ -626,7 +626,7 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
     a.scratch_wgs = P->scratch_wgs;
     a.grid_cap = P->grid_cap;
     const int blk = nfun(ce->la, P->sph) * nfun(ce->lb, P->sph) * nfun(ce->lc, P->sph) * nfun(ce->ld, P->sph);
-    if (ce->tier == 'M' && (!P->d_scratch)) {
+    if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
         g_last_error = "memory-tier class without scratch";
         throw HipFail{hipErrorInvalidValue};
     }
@@ -656,7 +656,7 @@ void ensure_scratch(eri_plan *P, const std::vector<int> &cids)
         if (ce && ce->tier == 'M') need = std::max(need, ce->scratch_doubles);
     }
     if (need == 0 || need <= P->scratch_doubles) return;
-    const int wgs = 1024;
+    const int wgs = ERI_MEM_WGS;
     P->d_scratch = P->alloc<double>((size_t)need * wgs);  // the smaller earlier slice stays owned until destroy
     P->scratch_wgs = wgs;
     P->scratch_doubles = need;

@@ -823,28 +823,47 @@ def mem_acc_in_registers(ci: ClassInfo) -> bool:
 
 
 def _mem_layout(ci: ClassInfo, spherical: bool):
+    """Scratch rows (units of W doubles): only the contraction accumulators of
+    classes whose accumulators do not fit in registers."""
     kv = build_ket_vrr(ci.lc, ci.Lk)
-    slot_of, nk_slots = {}, 0  # ket values live in registers (coupling through LDS)
-    ntg = len(kv.targets)
-    ops1, _, outs1 = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
-    ops2, _, outs2 = _hrr_ops(ci.la, ci.lb, "AB", spherical)
-    npriv = max(_count_private(ops1, outs1), _count_private(ops2, outs2))
-    # layout (units of W doubles): [private HRR slots][acc][exchange NK]
-    acc0 = npriv
-    xch0 = acc0 + ntg
-    nslots = xch0 + ci.nket(spherical)
+    nslots = 0 if mem_acc_in_registers(ci) else len(kv.targets)
+    if not mem_xch_in_lds(ci, spherical):
+        nslots += ci.nket(spherical)  # exchange rows follow the accumulators
     W = 64 * ((ci.G + 63) // 64)
-    return kv, slot_of, acc0, xch0, nslots, W
+    return kv, nslots, W
+
+
+LDS_LIMIT_BYTES = 160 * 1024
+
+
+def mem_xch_in_lds(ci: ClassInfo, spherical: bool) -> bool:
+    return ci.nket(spherical) * mem_xch_stride(ci) * 8 <= LDS_LIMIT_BYTES
+
+
+def mem_xch_stride(ci: ClassInfo) -> int:
+    """Row stride (doubles) of the LDS exchange: W + 1, so that lanes reading
+    different rows at one column hit different banks."""
+    return 64 * ((ci.G + 63) // 64) + 1
+
+
+def mem_lds_total(ci: ClassInfo, spherical: bool) -> int:
+    """LDS doubles: the ket level buffer and the exchange share one array."""
+    xch = ci.nket(spherical) * mem_xch_stride(ci) if mem_xch_in_lds(ci, spherical) else 0
+    return max(1, mem_lds_doubles(ci), xch)
 
 
 def memory_tier_scratch_doubles(ci: ClassInfo, spherical: bool) -> int:
-    """Scratch doubles per workgroup: (HRR slots + accumulators + exchange) x lanes."""
-    kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
+    """Global scratch doubles per workgroup (0 when the accumulators are registers)."""
+    kv, nslots, W = _mem_layout(ci, spherical)
     return nslots * W
 
 
 def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
-    kv, slot_of, acc0, xch0, nslots, W = _mem_layout(ci, spherical)
+    kv, nslots, W = _mem_layout(ci, spherical)
+    acc0 = 0
+    XS = mem_xch_stride(ci)
+    xlds = mem_xch_in_lds(ci, spherical)
+    xch0 = nslots - ci.nket(spherical)  # first exchange row when it lives in scratch
     names = Names("V", kv, ci.Lk)
     G = ci.G
     NK = ci.nket(spherical)
@@ -865,7 +884,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     L = ci.L
     o = []
     o.append(f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {cid}, {'spherical' if spherical else 'Cartesian'} output,"
-             f" memory tier: {G} lanes (workgroup {W}) per quartet, {nslots} scratch slots")
+             f" memory tier: {G} lanes (workgroup {W}) per quartet, {nslots} scratch rows")
     o.append('#include "eri_device.h"')
     o.append("namespace {")
     o.append(f"__constant__ short k_{tag}_lane[3][{G}] = {{")
@@ -883,7 +902,10 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append(f"  constexpr int G = {G}, W = {W}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append(f"  constexpr size_t WG_DOUBLES = {memory_tier_scratch_doubles(ci, spherical)};")
     o.append("  const int tid = threadIdx.x;")
-    o.append(f"  __shared__ double xl[{max(1, mem_lds_doubles(ci))}];  // one ket level's cross-lane values")
+    # one LDS array: a ket level's cross-lane values during the recurrence,
+    # then the ket-transformed exchange (row kappa, column = bra lane)
+    o.append(f"  __shared__ double xl[{mem_lds_total(ci, spherical)}];")
+    o.append(f"  constexpr int XS = {XS};")
     o.append("  const int sub = tid < G ? tid : 0;  // lanes beyond G shadow e = (0,0,0) and never store")
     o.append("  const bool real = tid < G;")
     # Every graph value lives in this workgroup's scratch slice, addressed by
@@ -983,32 +1005,37 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
     o.append("    }")
     o.append("  }")
-    if acc_reg:
-        for t in range(len(targets)):
-            o.append(f"  SST({acc0 + t}, acc{t});")
-    # H1 per lane, reading the accumulators; intermediates in private slots of
-    # the (now dead) ket region, results straight into the exchange slots
+    # ket HRR and transform per lane, in registers, from the accumulators;
+    # results into the LDS exchange (the last barrier of the loop freed it)
     tpos = {f: t for t, (f, m) in enumerate(targets)}
-    ops1, _, outs1 = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
-    assert len(outs1) == NK
+    acc_src = (lambda e: f"acc{tpos[e]}") if acc_reg else (lambda e: f"SLD({acc0 + tpos[e]})")
     o.append("  {")
-    _emit_ops_mem(ops1, lambda e: f"SLD({acc0 + tpos[e]})", outs1, lambda k, x: f"SST({xch0 + k}, {x});", 0, o, "    ")
+    if xlds:
+        h1_store = lambda k, x: f"xl[{k} * XS + tid] = {x};"
+    else:
+        h1_store = lambda k, x: f"SST({xch0 + k}, {x});"
+    _emit_hrr_scheduled(ci.lc, ci.ld, acc_src, "CD", spherical, h1_store, o, "    ", "h")
     o.append("  }")
     o.append("  __syncthreads();")
     o.append("  const int4 pb2 = a.pair_info[bra];")
     o.append("  const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
              " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
     o.append("  (void)ABx; (void)ABy; (void)ABz;")
+    # bra HRR and transform per ket component kappa, in registers
     o.append("  for (int kap = tid; kap < NK; kap += W) {")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
-    o.append(f"    const int vx = (kap * W + {EOFF}) * 8;  // exchange row kap, first bra lane")
     o.append("    double* dst = a.out + (size_t)qs * BLK + kap;")
-    ops2, _, outs2 = _hrr_ops(ci.la, ci.lb, "AB", spherical)
-    _emit_ops_mem(ops2, lambda e: f"eri_bld(rs, vx, {xch0} * (W * 8) + {epos[e] * 8})", outs2,
-                  lambda k, x: f"dst[{k} * NK] = {x};", 0, o, "    ")
+    if xlds:
+        o.append(f"    const double* xr = xl + kap * XS + {EOFF};  // exchange row kappa, first bra lane")
+        h2_load = lambda e: f"xr[{epos[e]}]"
+    else:
+        o.append(f"    const int vx = (kap * W + {EOFF}) * 8;  // exchange row kappa, first bra lane")
+        h2_load = lambda e: f"eri_bld(rs, vx, {xch0} * (W * 8) + {epos[e] * 8})"
+    _emit_hrr_scheduled(ci.la, ci.lb, h2_load, "AB", spherical,
+                        lambda k, x: f"dst[{k} * NK] = {x};", o, "    ", "g")
     o.append("  }")
-    o.append("  __syncthreads();  // exchange slots are reused by the next quartet")
+    o.append("  __syncthreads();  // the exchange is reused by the next quartet")
     o.append("  }")
     o.append("#undef SLD")
     o.append("#undef SST")
@@ -1017,7 +1044,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     o.append("")
     o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
     o.append("{")
-    o.append("  const int nblk = a.nq < a.scratch_wgs ? a.nq : a.scratch_wgs;")
+    o.append("  const int nblk = a.nq < ERI_MEM_WGS ? a.nq : ERI_MEM_WGS;")
     o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3({W}), 0, s, a);")
     o.append("}")
     return "\n".join(o) + "\n"

@@ -5,6 +5,7 @@ this package is its thin Python binding.  PyTorch provides device memory and
 streams only.
 """
 from ._lib import (  # noqa: F401
+    ERI_IMPLICIT,
     ERI_NO_NORMALIZE,
     ERI_SPHERICAL,
     EriError,
@@ -12,6 +13,7 @@ from ._lib import (  # noqa: F401
     build_quartets,
     class_info,
     compute_batch,
+    compute_range,
     digest_J,
     load,
     strerror,

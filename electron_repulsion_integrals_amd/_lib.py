@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(PKG, "liberi_mi355x.so")
 
 ERI_SPHERICAL = 1
 ERI_NO_NORMALIZE = 2
+ERI_IMPLICIT = 4
 ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "capacity", -4: "HIP error", -5: "out of memory"}
 
 
@@ -64,6 +65,10 @@ def load():
     L.eri_plan_schwarz.restype = ctypes.c_int
     L.eri_compute_batch.argtypes = [vp, ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_int64, vp]
     L.eri_compute_batch.restype = ctypes.c_int
+    L.eri_compute_range.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64, vp]
+    L.eri_compute_range.restype = ctypes.c_int
+    L.eri_plan_quartets.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]
+    L.eri_plan_quartets.restype = ctypes.c_int
     L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
     L.eri_digest_J.restype = ctypes.c_int
     L.eri_strerror.argtypes = [ctypes.c_int]
@@ -136,6 +141,13 @@ class Plan:
         _check(load().eri_plan_index_map(self.handle, _ptr(out), _stream_handle(stream)))
         return out
 
+    def quartets(self, first: int, count: int, stream=None):
+        """Index-map rows of plan slots [first, first + count) as a (count, 5) int32 device tensor."""
+        import torch
+        out = torch.empty((int(count), 5), dtype=torch.int32, device="cuda")
+        _check(load().eri_plan_quartets(self.handle, int(first), int(count), _ptr(out), _stream_handle(stream)))
+        return out
+
     def schwarz(self, stream=None):
         import torch
         out = torch.empty(self.n_pairs, dtype=torch.float64, device="cuda")
@@ -173,6 +185,13 @@ def compute_batch(plan: Plan, out, block_begin: int = 0, block_end: int | None =
     if block_end is None:
         block_end = plan.n_blocks
     _check(load().eri_compute_batch(plan.handle, int(block_begin), int(block_end), _ptr(out), out.numel(),
+                                    _stream_handle(stream)))
+    return out
+
+
+def compute_range(plan: Plan, block: int, first: int, count: int, out, stream=None):
+    """Integrals of quartets [first, first + count) of one class block into ``out``."""
+    _check(load().eri_compute_range(plan.handle, int(block), int(first), int(count), _ptr(out), out.numel(),
                                     _stream_handle(stream)))
     return out
 

@@ -12,6 +12,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -379,6 +380,90 @@ __global__ void k_fill_screened(int64_t nentries, const BlockDesc *blocks, int n
     }
 }
 
+// Plan slots [s0, s0 + m) of an implicit screened plan -> bra and ket pair
+// (and, when qmap is given, the index-map rows).  The slot's entry (block,
+// bra rank) is the last entry whose offset is <= the slot: entries without
+// survivors share the next entry's offset.
+__global__ void k_expand(int64_t s0, int64_t m, int64_t nent, const int64_t *off, const BlockDesc *blocks,
+                         int nblocks, const int *porder, const int4 *pinfo, const int *pair_i, int *qbra, int *qket,
+                         int *qmap)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= m) return;
+    const int64_t s = s0 + t;
+    int64_t lo = 0, hi = nent;
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) / 2;
+        if (off[mid] <= s) lo = mid;
+        else hi = mid;
+    }
+    const int64_t e = lo;
+    int blo = 0, bhi = nblocks;
+    while (bhi - blo > 1) {
+        const int mid = (blo + bhi) / 2;
+        if (blocks[mid].entry_base <= e) blo = mid;
+        else bhi = mid;
+    }
+    const BlockDesc bd = blocks[blo];
+    const int r = (int)(e - bd.entry_base);
+    const int pb = porder[bd.bra_start + r];
+    const int pk = porder[bd.ket_start + (bd.same ? r : 0) + (int)(s - off[e])];
+    if (qbra) qbra[t] = pb;
+    if (qket) qket[t] = pk;
+    if (qmap) {
+        const int4 ib = pinfo[pb], ik = pinfo[pk];
+        int *row = qmap + 5 * t;
+        row[0] = ib.x;
+        row[1] = ib.y;
+        row[2] = ik.x;
+        row[3] = ik.y;
+        row[4] = (ib.x != pair_i[pb] ? 1 : 0) | ((ik.x != pair_i[pk] ? 1 : 0) << 1) | ((pb < pk ? 1 : 0) << 2);
+    }
+}
+
+__global__ void k_zero_mat(int n, double *A, int lda)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)n * n) return;
+    const int i = (int)(t / n), j = (int)(t - (int64_t)i * n);
+    A[(size_t)i * lda + j] = 0.0;
+}
+
+// chunk entries: (pair, offset of its contribution vector) for both sides of
+// every quartet; a quartet of two equal pairs has one side only
+__global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int *ekey, int64_t *eoff)
+{
+    const int s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= m) return;
+    const int64_t off = (int64_t)s * (nab + ncd);
+    ekey[2 * s] = qbra[s];
+    eoff[2 * s] = off;
+    const bool two = qbra[s] != qket[s];
+    ekey[2 * s + 1] = two ? qket[s] : 0x7fffffff;  // sorts last, never read
+    eoff[2 * s + 1] = two ? off + nab : -1;
+}
+
+// one workgroup per run of equal pairs in the sorted chunk entries: add the
+// run's contribution vectors in entry order to the J block (and its transpose)
+__global__ void k_add_runs(const int *nruns, const int *key, const int *rstart, const int *rlen, const int64_t *eoff,
+                           const double *cb, const int4 *pinfo, const int *bf, const int *nfun_sh, double *J, int ldj)
+{
+    const int u = blockIdx.x;
+    if (u >= *nruns) return;
+    const int p = key[u];
+    if (p == 0x7fffffff) return;
+    const int4 pi = pinfo[p];
+    const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
+    const int e0 = rstart[u], e1 = e0 + rlen[u];
+    for (int v = threadIdx.x; v < n; v += blockDim.x) {
+        double acc = 0.0;
+        for (int e = e0; e < e1; ++e) acc += cb[eoff[e] + v];
+        const int a = v / nb, b = v - a * nb;
+        J[(size_t)(bf[pi.x] + a) * ldj + bf[pi.y] + b] += acc;
+        if (pi.x != pi.y) J[(size_t)(bf[pi.y] + b) * ldj + bf[pi.x] + a] += acc;
+    }
+}
+
 __global__ void k_pair_hi(int np, const int4 *pinfo, int *hi)
 {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
@@ -523,11 +608,26 @@ struct eri_plan {
     int grid_cap = 2048;            // persistent register-tier grid (8 workgroups per CU)
     std::vector<EriBlock> blocks;
     std::vector<void *> allocs;
+    // implicit screened plans: per (block, bra rank) ket-prefix counts
+    bool implicit = false;
+    BlockDesc *d_bd = nullptr;
+    int nbd = 0;
+    int64_t nent = 0;
+    int64_t *d_ent_off = nullptr;
+    int *d_porder = nullptr, *d_pair_i = nullptr;
+    int64_t chunk_q = 1 << 22;         // quartets per internal chunk
+    int *d_cqbra = nullptr, *d_cqket = nullptr;  // chunk lists (plan-owned: calls on one plan do not overlap)
+    // chunked J work (implicit plans, built on first use)
+    bool cjready = false;
+    double *d_cints = nullptr, *d_ccb = nullptr;
+    int *d_cek = nullptr, *d_cek2 = nullptr, *d_ruk = nullptr, *d_rlen = nullptr, *d_rst = nullptr, *d_nruns = nullptr;
+    int64_t *d_ceo = nullptr, *d_ceo2 = nullptr;
+    void *d_ctmp = nullptr;
+    size_t ctmp_bytes = 0;
     // J digestion work (screened plans, built on first use)
     bool jready = false;
     double *d_ints = nullptr, *d_cb = nullptr;
     int64_t *d_seg = nullptr, *d_eoff = nullptr;
-    int64_t nent = 0;
 
     template <class T>
     T *alloc(size_t n)
@@ -642,6 +742,98 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
             a.nq = (int)m;
             a.out = out + b * blk;
             (part == 0 ? ce->launch_k1 : ce->launch)(a, s);
+            HIP_CHECK(hipGetLastError());
+        }
+    }
+}
+
+// quartet lists of plan slots [s, s + m): the plan's own arrays, or for an
+// implicit plan the chunk buffers after expansion (m <= chunk_q)
+void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const int **qk, hipStream_t st)
+{
+    if (!P->implicit) {
+        *qb = P->d_qbra + s;
+        *qk = P->d_qket + s;
+        return;
+    }
+    hipLaunchKernelGGL(k_expand, dim3(nblk(m, 256)), dim3(256), 0, st, s, m, P->nent, P->d_ent_off, P->d_bd, P->nbd,
+                       P->d_porder, P->d_pinfo, P->d_pair_i, P->d_cqbra, P->d_cqket, (int *)nullptr);
+    HIP_CHECK(hipGetLastError());
+    *qb = P->d_cqbra;
+    *qk = P->d_cqket;
+}
+
+// integrals of quartets [first, first + count) of block B into out
+void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t count, double *out, hipStream_t st)
+{
+    const int64_t blk = (int64_t)B.na * B.nb * B.nc * B.nd;
+    const int64_t step = P->implicit ? P->chunk_q : std::max<int64_t>(count, 1);
+    for (int64_t c = first; c < first + count; c += step) {
+        const int64_t m = std::min(step, first + count - c);
+        const int *qb = nullptr, *qk = nullptr;
+        slot_lists(P, B.start + c, m, &qb, &qk, st);
+        const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
+        launch_class(P, B.cid, qb, qk, m, out + (c - first) * blk, st, nk1);
+    }
+}
+
+// J of an implicit plan, chunk by chunk: integrals of the chunk, per-quartet
+// contribution vectors, entries sorted by pair (stable), then each pair's run
+// added to J.  Chunks go in plan order, so the sums are deterministic.
+void digest_J_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj, hipStream_t s)
+{
+    const int64_t CO = int64_t(1) << 27, CB = int64_t(1) << 26;
+    const int64_t CQ = P->chunk_q;
+    if (!P->cjready) {
+        P->d_cints = P->alloc<double>(CO);
+        P->d_ccb = P->alloc<double>(CB);
+        P->d_cek = P->alloc<int>(2 * CQ);
+        P->d_cek2 = P->alloc<int>(2 * CQ);
+        P->d_ceo = P->alloc<int64_t>(2 * CQ);
+        P->d_ceo2 = P->alloc<int64_t>(2 * CQ);
+        P->d_ruk = P->alloc<int>(2 * CQ);
+        P->d_rlen = P->alloc<int>(2 * CQ);
+        P->d_rst = P->alloc<int>(2 * CQ);
+        P->d_nruns = P->alloc<int>(1);
+        size_t t1 = 0, t2 = 0, t3 = 0;
+        const int n2 = (int)(2 * CQ);
+        HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0, 32, s));
+        HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns, n2, s));
+        HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, P->d_rlen, P->d_rst, n2, s));
+        P->ctmp_bytes = std::max(t1, std::max(t2, t3));
+        P->d_ctmp = P->alloc<char>(P->ctmp_bytes);
+        P->cjready = true;
+    }
+    const int n = P->nbf;
+    hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, J, ldj);
+    HIP_CHECK(hipGetLastError());
+    for (const EriBlock &B : P->blocks) {
+        const int nab = B.na * B.nb, ncd = B.nc * B.nd;
+        const int64_t blk = (int64_t)nab * ncd;
+        const int64_t step = std::max<int64_t>(1, std::min(CQ, std::min(CO / blk, CB / (nab + ncd))));
+        for (int64_t c = 0; c < B.count; c += step) {
+            const int64_t m = std::min(step, B.count - c);
+            const int *qb = nullptr, *qk = nullptr;
+            slot_lists(P, B.start + c, m, &qb, &qk, s);
+            const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
+            launch_class(P, B.cid, qb, qk, m, P->d_cints, s, nk1);
+            hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd, qb, qk,
+                               P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
+            hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, nab, ncd, P->d_cek,
+                               P->d_ceo);
+            HIP_CHECK(hipGetLastError());
+            const int n2 = (int)(2 * m);
+            size_t tb = P->ctmp_bytes;
+            HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(P->d_ctmp, tb, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0,
+                                                         32, s));
+            tb = P->ctmp_bytes;
+            HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(P->d_ctmp, tb, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns,
+                                                            n2, s));
+            tb = P->ctmp_bytes;
+            HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(P->d_ctmp, tb, P->d_rlen, P->d_rst, n2, s));
+            // at most 2m runs; workgroups past the device-side run count exit at once
+            hipLaunchKernelGGL(k_add_runs, dim3((unsigned)n2), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst, P->d_rlen,
+                               P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
             HIP_CHECK(hipGetLastError());
         }
     }
@@ -859,18 +1051,27 @@ void build_screened(eri_plan *P, const std::vector<int> &hl, const std::vector<i
         HIP_CHECK(hipStreamSynchronize(s));
     }
     const int64_t nq = lo + lc;
-    if (nq > (int64_t)INT32_MAX) {
-        g_last_error = "screened plan exceeds 2^31 quartets (explicit lists only in this build)";
-        throw HipFail{hipErrorInvalidValue};
-    }
     P->nq = nq;
-    P->d_qbra = P->alloc<int>(nq);
-    P->d_qket = P->alloc<int>(nq);
-    P->d_qmap = P->alloc<int>((size_t)5 * nq);
     int *phi = P->alloc<int>(np);
     hipLaunchKernelGGL(k_pair_hi, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, P->d_pinfo, phi);
-    hipLaunchKernelGGL(k_fill_screened, dim3(nblk(nent, 128)), dim3(128), 0, s, nent, d_bd, (int)bd.size(), porder, cnt,
-                       off, P->d_pinfo, phi, P->d_qbra, P->d_qket, P->d_qmap);
+    P->implicit = (P->flags & ERI_IMPLICIT) != 0 || nq > ERI_EXPLICIT_MAX;
+    if (P->implicit) {
+        // keep the counts; quartet lists are expanded chunk by chunk when used
+        P->d_bd = d_bd;
+        P->nbd = (int)bd.size();
+        P->nent = nent;
+        P->d_ent_off = off;
+        P->d_porder = porder;
+        P->d_pair_i = phi;
+        P->d_cqbra = P->alloc<int>(P->chunk_q);
+        P->d_cqket = P->alloc<int>(P->chunk_q);
+    } else {
+        P->d_qbra = P->alloc<int>(nq);
+        P->d_qket = P->alloc<int>(nq);
+        P->d_qmap = P->alloc<int>((size_t)5 * nq);
+        hipLaunchKernelGGL(k_fill_screened, dim3(nblk(nent, 128)), dim3(128), 0, s, nent, d_bd, (int)bd.size(), porder,
+                           cnt, off, P->d_pinfo, phi, P->d_qbra, P->d_qket, P->d_qmap);
+    }
     HIP_CHECK(hipGetLastError());
     // block starts -> class ranges
     std::vector<int64_t> hbase(bd.size());
@@ -934,7 +1135,8 @@ extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t
     *plan = nullptr;
     if (!sh || sh->nshell < 1 || !sh->centers || !sh->l || !sh->nprim || !sh->prim_off || !sh->exps || !sh->coefs)
         return ERI_E_INVALID;
-    if (flags & ~(ERI_SPHERICAL | ERI_NO_NORMALIZE)) return ERI_E_INVALID;
+    if (flags & ~(ERI_SPHERICAL | ERI_NO_NORMALIZE | ERI_IMPLICIT)) return ERI_E_INVALID;
+    if ((flags & ERI_IMPLICIT) && quartets) return ERI_E_INVALID;
     if (!(tau >= 0.0) || std::isinf(tau)) return ERI_E_INVALID;
     if (quartets && (nq < 0 || tau != 0.0)) return ERI_E_INVALID;
     const int ns = sh->nshell;
@@ -962,6 +1164,10 @@ extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t
             P->grid_cap = std::max(1, ncu) * 8;
         }
         P->flags = flags;
+        if (const char *cq = std::getenv("ERI_CHUNK_QUARTETS")) {
+            const long long v = std::atoll(cq);
+            if (v >= 1 && v <= (1LL << 26)) P->chunk_q = v;
+        }
         P->sph = (flags & ERI_SPHERICAL) != 0;
         P->screened = quartets == nullptr;
         P->nshell = ns;
@@ -1042,6 +1248,7 @@ extern "C" int eri_plan_index_map(const eri_plan *P, int32_t *dst, void *stream)
 {
     if (!P || (!dst && P->nq)) return ERI_E_INVALID;
     if (!P->nq) return ERI_OK;
+    if (P->implicit) return eri_plan_quartets(P, 0, P->nq, dst, stream);
     hipError_t e = hipMemcpyAsync(dst, P->d_qmap, sizeof(int) * 5 * P->nq, hipMemcpyDeviceToDevice, (hipStream_t)stream);
     if (e != hipSuccess) {
         g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
@@ -1074,8 +1281,46 @@ extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, doub
     try {
         for (int b = b0; b < b1; ++b) {
             const EriBlock &B = P->blocks[b];
-            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, out + (B.out_off - base),
-                         (hipStream_t)stream, B.n_k1);
+            compute_range(P, B, 0, B.count, out + (B.out_off - base), (hipStream_t)stream);
+        }
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_compute_range(const eri_plan *P, int32_t block, int64_t first, int64_t count, double *out,
+                                 int64_t cap, void *stream)
+{
+    if (!P || block < 0 || block >= (int)P->blocks.size() || first < 0 || count < 0) return ERI_E_INVALID;
+    const EriBlock &B = P->blocks[block];
+    if (first > B.count || count > B.count - first) return ERI_E_INVALID;
+    if (count == 0) return ERI_OK;
+    const int64_t need = count * (int64_t)B.na * B.nb * B.nc * B.nd;
+    if (!out) return ERI_E_INVALID;
+    if (cap < need) return ERI_E_CAPACITY;
+    try {
+        compute_range(P, B, first, count, out, (hipStream_t)stream);
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_quartets(const eri_plan *P, int64_t first, int64_t count, int32_t *dst, void *stream)
+{
+    if (!P || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
+    if (count == 0) return ERI_OK;
+    if (!dst || count > (int64_t)INT32_MAX) return ERI_E_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    try {
+        if (P->implicit) {
+            hipLaunchKernelGGL(k_expand, dim3(nblk(count, 256)), dim3(256), 0, s, first, count, P->nent, P->d_ent_off,
+                               P->d_bd, P->nbd, P->d_porder, P->d_pinfo, P->d_pair_i, (int *)nullptr, (int *)nullptr,
+                               dst);
+            HIP_CHECK(hipGetLastError());
+        } else {
+            HIP_CHECK(hipMemcpyAsync(dst, P->d_qmap + 5 * first, sizeof(int) * 5 * count, hipMemcpyDeviceToDevice, s));
         }
     } catch (const HipFail &f) {
         return translate(f);
@@ -1089,6 +1334,14 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
     if (!P || !D || !J || ldd < P->nbf || ldj < P->nbf) return ERI_E_INVALID;
     if (!P->screened) return ERI_E_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
+    if (P->implicit) {
+        try {
+            digest_J_chunked(P, D, ldd, J, ldj, s);
+        } catch (const HipFail &f) {
+            return translate(f);
+        }
+        return ERI_OK;
+    }
     try {
         const int nb = (int)P->blocks.size();
         if (!P->jready) {

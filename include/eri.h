@@ -62,6 +62,10 @@ extern "C" {
 
 #define ERI_SPHERICAL 1    /* output in the real spherical basis */
 #define ERI_NO_NORMALIZE 2 /* raw coefficients on raw monomials */
+#define ERI_IMPLICIT 4     /* screened plans: keep counts only (see eri_build_quartets) */
+
+/* Screened plans with more quartets than this are always implicit. */
+#define ERI_EXPLICIT_MAX (((int64_t)1) << 28)
 
 #define ERI_MAX_L 4
 #define ERI_MAX_PRIM 15
@@ -90,6 +94,15 @@ typedef struct eri_plan eri_plan;
  *     device by the same class kernels (tau = 0 keeps every quartet).  Pairs
  *     are bucketed by (pair class, K_pair) and ranked by S descending (ties by
  *     pair index); order (class id, K_bra, K_ket, bra rank, ket rank).
+ *     Because the kets of one bra are ranked by S descending, the survivors
+ *     of each (block, bra) are a prefix of its ket list.  An implicit plan
+ *     (flag ERI_IMPLICIT, or automatically above ERI_EXPLICIT_MAX quartets)
+ *     stores only these prefix lengths and their running offsets, i.e.
+ *     memory per (bucket pair, bra pair) instead of per quartet; quartet
+ *     lists are then expanded on the device in chunks when used (at most
+ *     ERI_CHUNK_QUARTETS, an environment variable read here, default
+ *     4194304).  Calls on one implicit plan share its chunk buffers and must
+ *     not overlap in time.
  * Synchronises `stream` (quartet counts are needed on the host).
  * On success *plan receives a new plan.
  */
@@ -114,6 +127,11 @@ int eri_plan_blocks(const eri_plan *plan, int32_t *class_id, int64_t *start, int
  * is device memory [5*n_quartets]; asynchronous on `stream`. */
 int eri_plan_index_map(const eri_plan *plan, int32_t *dst, void *stream);
 
+/* The index-map rows of plan slots [first, first + count) only (any plan,
+ * explicit or implicit): dst is device memory [5*count], count < 2^31;
+ * asynchronous on `stream`. */
+int eri_plan_quartets(const eri_plan *plan, int64_t first, int64_t count, int32_t *dst, void *stream);
+
 /* Schwarz factors S[pair] for pair index i(i+1)/2 + j (screened plans only);
  * dst is device memory [n_pairs]; asynchronous on `stream`. */
 int eri_plan_schwarz(const eri_plan *plan, double *dst, void *stream);
@@ -127,11 +145,24 @@ int eri_compute_batch(const eri_plan *plan, int32_t block_begin, int32_t block_e
                       int64_t out_capacity, void *stream);
 
 /*
+ * Integrals of quartets [first, first + count) of class block `block` (counted
+ * from the block's first slot) into `out` (device), one block of outputs per
+ * quartet in plan order; out_capacity >= count x (block size) doubles.  For
+ * sampling blocks whose full output would not fit.  Asynchronous.
+ */
+int eri_compute_range(const eri_plan *plan, int32_t block, int64_t first, int64_t count, double *out,
+                      int64_t out_capacity, void *stream);
+
+/*
  * Coulomb matrix of a screened (quartets == NULL) plan: J = sum over the
  * plan's unique quartets with the 8-fold symmetry, D and J dense row-major
  * device matrices of order nbf with leading dimensions ldd, ldj.  D must be
- * symmetric.  J is fully overwritten.  Deterministic, no atomics.
- * Asynchronous; the plan keeps work buffers between calls.
+ * symmetric.  J is fully overwritten.  Deterministic, no atomics: each
+ * pair's contributions are summed in plan order.  An explicit plan computes
+ * all its integrals at once; an implicit plan goes chunk by chunk (integrals,
+ * contributions, per-pair sums added to J), so its memory does not grow with
+ * the number of quartets.  Asynchronous; the plan keeps work buffers between
+ * calls.
  */
 int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream);
 

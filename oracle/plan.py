@@ -183,3 +183,85 @@ def screened_plan(l, nprim, S, tau):
     im[:, 4] = perm
     return {"index_map": im, "pair_bra": bra, "pair_ket": ket, "blocks": _blocks(cls), "class": cls,
             "bucket": bucket, "rank": rank}
+
+
+def screened_counts(l, nprim, S, tau):
+    """Counts of the screened plan without listing its quartets (for plans too
+    large to enumerate).  Same rules as ``screened_plan``.
+
+    For each (bra bucket B, ket bucket Bk <= B) and each bra of rank r in B,
+    the kets are the pairs of Bk (of rank >= r when Bk == B) with
+    fl(S_bra * S_ket) >= fl(tau^2).  Inside a bucket the ranks follow S
+    descending, and fl(S_bra * x) never decreases as x grows, so in rank
+    order the surviving kets are a prefix; its length is found by bisection
+    on the test itself.  Returns dict(blocks = [(class, start, count)],
+    groups = [(class, K_bra, K_ket, B, Bk, start, counts[bra rank])] in plan
+    order, pairs, bucket_members[b] = pair indices of bucket b in rank order).
+    """
+    pt = pair_table(l, nprim, S)
+    P, bucket, order = pt["pairs"], pt["bucket"], pt["order"]
+    S = np.asarray(S, dtype=np.float64)
+    t2 = np.float64(tau) * np.float64(tau)
+    nb = int(bucket.max()) + 1 if len(bucket) else 0
+    members = [order[np.searchsorted(bucket[order], b, side="left"):np.searchsorted(bucket[order], b, side="right")]
+               for b in range(nb)]
+    groups = []
+    for B in range(nb):
+        for Bk in range(B + 1):
+            bra, ket = members[B], members[Bk]
+            pcb, pck = int(P[bra[0], 4]), int(P[ket[0], 4])
+            groups.append([class_id(pcb, pck), int(P[bra[0], 5]), int(P[ket[0], 5]), B, Bk])
+    groups.sort(key=lambda g: (g[0], g[1], g[2]))
+    start = 0
+    out = []
+    for cid, kb, kk, B, Bk in groups:
+        sb, sk = S[members[B]], S[members[Bk]]
+        lo = np.zeros(len(sb), dtype=np.int64)
+        hi = np.full(len(sb), len(sk), dtype=np.int64)
+        if B == Bk:
+            lo = np.arange(len(sb), dtype=np.int64)  # kets of rank >= the bra's own
+        first = lo.copy()
+        # bisection: the first rank in [lo, hi) where the test fails
+        while True:
+            act = lo < hi
+            if not act.any():
+                break
+            mid = (lo + hi) // 2
+            ok = np.zeros(len(sb), dtype=bool)
+            ok[act] = (sb[act] * sk[np.minimum(mid[act], len(sk) - 1)]) >= t2
+            lo = np.where(act & ok, mid + 1, lo)
+            hi = np.where(act & ~ok, mid, hi)
+        counts = lo - first
+        out.append((cid, kb, kk, B, Bk, start, counts))
+        start += int(counts.sum())
+    blocks = []
+    for g in out:
+        n = int(g[6].sum())
+        if n == 0:
+            continue
+        if blocks and blocks[-1][0] == g[0]:
+            blocks[-1] = (g[0], blocks[-1][1], blocks[-1][2] + n)
+        else:
+            blocks.append((g[0], g[5], n))
+    return {"blocks": blocks, "groups": out, "pairs": P, "bucket_members": members, "n_quartets": start}
+
+
+def screened_decode(sc, slots):
+    """Index-map rows (a, b, c, d, perm) of the given plan slots of a plan
+    described by ``screened_counts``."""
+    P, members = sc["pairs"], sc["bucket_members"]
+    starts = np.array([g[5] for g in sc["groups"]], dtype=np.int64)
+    rows = np.zeros((len(slots), 5), dtype=np.int32)
+    for x, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        # the last group starting at or before s (empty groups share the next start)
+        gi = int(np.searchsorted(starts, s, side="right")) - 1
+        cid, kb, kk, B, Bk, st, counts = sc["groups"][gi]
+        assert st <= s < st + int(counts.sum())
+        off = np.concatenate([[0], np.cumsum(counts)])
+        r = int(np.searchsorted(off, s - st, side="right")) - 1
+        t = int(s - st - off[r])
+        bra = int(members[B][r])
+        ket = int(members[Bk][(r if B == Bk else 0) + t])
+        perm = int(P[bra, 2] != P[bra, 0]) | (int(P[ket, 2] != P[ket, 0]) << 1) | (int(bra < ket) << 2)
+        rows[x] = (P[bra, 2], P[bra, 3], P[ket, 2], P[ket, 3], perm)
+    return rows

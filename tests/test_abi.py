@@ -38,6 +38,8 @@ def test_strerror_and_argument_validation_without_gpu():
     assert L.eri_build_quartets(None, 0, None, 0, 0.0, None, None) == -1
     assert L.eri_compute_batch(None, 0, 0, None, 0, None) == -1
     assert L.eri_digest_J(None, None, 0, None, 0, None) == -1
+    assert L.eri_compute_range(None, 0, 0, 1, None, 0, None) == -1
+    assert L.eri_plan_quartets(None, 0, 1, None, None) == -1
     assert L.eri_plan_destroy(None) == 0
 
 
@@ -48,7 +50,7 @@ def test_invalid_shells_rejected_on_host():
     from electron_repulsion_integrals_amd import _lib
     from workloads.configs import _pack
 
-    def try_build(sh, q=None, tau=0.0):
+    def try_build(sh, q=None, tau=0.0, flags=0):
         c = np.ascontiguousarray(sh.centers)
         l = np.ascontiguousarray(sh.l, dtype=np.int32)
         k = np.ascontiguousarray(sh.nprim, dtype=np.int32)
@@ -66,7 +68,7 @@ def test_invalid_shells_rejected_on_host():
             qq = qa.ctypes.data_as(ip)
             nq = len(qa)
         h = ctypes.c_void_p()
-        return _lib.load().eri_build_quartets(ctypes.byref(s), 0, qq, nq, tau, None, ctypes.byref(h))
+        return _lib.load().eri_build_quartets(ctypes.byref(s), flags, qq, nq, tau, None, ctypes.byref(h))
 
     good = dict(centers=[[0, 0, 0]], ls=[1], ks=[1], ex=[np.array([1.0])], co=[np.array([1.0])])
     assert try_build(_pack([[0, 0, 0]], [5], [1], [np.array([1.0])], [np.array([1.0])])) == -1
@@ -74,4 +76,8 @@ def test_invalid_shells_rejected_on_host():
     assert try_build(_pack([[0, 0, 0]], [1], [1], [np.array([1.0])], [np.array([1.0])]), q=[0, 0, 0, 1]) == -1
     assert try_build(_pack([[0, 0, np.nan]], [1], [1], [np.array([1.0])], [np.array([1.0])])) == -1
     assert try_build(_pack([[0, 0, 0]], [1], [1], [np.array([1.0])], [np.array([1.0])]), tau=-1.0) == -1
+    # an implicit plan is a screened plan: not with an explicit list; unknown flag bits fail
+    one = _pack([[0, 0, 0]], [1], [1], [np.array([1.0])], [np.array([1.0])])
+    assert try_build(one, q=[0, 0, 0, 0], flags=_lib.ERI_IMPLICIT) == -1
+    assert try_build(one, flags=64) == -1
     del good

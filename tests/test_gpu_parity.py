@@ -216,6 +216,100 @@ def test_c3_reduced_plan_and_J(eri):
     assert_parity(Jg, Jref, "J")
 
 
+def test_implicit_plan_matches_explicit(eri):
+    """The same screened plan kept implicit (prefix counts, expanded in chunks of
+    1000 quartets): identical index map and integrals, J to the bar and
+    bitwise reproducible."""
+    import os
+    import torch
+    _log("case: C3 4-atom cluster, implicit plan with 1000-quartet chunks vs explicit")
+    w = make_config(3, scale={"natoms": 4})
+    sh = w.shells
+    pe, oute, ime = run_plan(eri, sh, 1, None, w.tau)
+    os.environ["ERI_CHUNK_QUARTETS"] = "1000"
+    try:
+        pi = eri.build_quartets(sh, eri.ERI_SPHERICAL | eri.ERI_IMPLICIT, None, w.tau)
+    finally:
+        del os.environ["ERI_CHUNK_QUARTETS"]
+    assert pi.n_quartets == pe.n_quartets > 5000
+    np.testing.assert_array_equal(pi.block_count, pe.block_count)
+    np.testing.assert_array_equal(pi.index_map().cpu().numpy(), ime)
+    mid = pe.n_quartets // 2
+    np.testing.assert_array_equal(pi.quartets(mid, 777).cpu().numpy(), ime[mid:mid + 777])
+    outi = torch.empty(pi.n_out, dtype=torch.float64, device="cuda")
+    eri.compute_batch(pi, outi)
+    torch.cuda.synchronize()
+    assert np.array_equal(outi.cpu().numpy(), oute), "implicit plan integrals differ from the explicit plan's"
+    D = torch.tensor(w.density, device="cuda")
+    J1 = torch.full_like(D, 3.0)
+    eri.digest_J(pi, D, J1)
+    J2 = torch.empty_like(D)
+    eri.digest_J(pi, D, J2)
+    torch.cuda.synchronize()
+    Jg = J1.cpu().numpy()
+    assert np.array_equal(Jg, J2.cpu().numpy()), "implicit-plan J is not bitwise reproducible"
+    flat, off = oracle.eri(sh, ime[:, :4], True)
+    Jref = oracle.J_from_quartets(sh, True, ime[:, :4], flat, off, w.density)
+    assert_parity(Jg, Jref, "implicit-plan J")
+
+
+def _cheap_slots(rows, nprim, limit):
+    k4 = np.prod(nprim[rows[:, :4]], axis=1)
+    return k4 <= limit
+
+
+def test_c5_full_plan_counts_and_sampled_integrals(eri):
+    """The 120-atom TZVP-like cluster at full size (2e10 screened quartets, an
+    implicit plan): quartet count and class blocks equal the oracle's counting
+    twin fed the GPU's Schwarz factors; sampled slots decode to the twin's
+    quartets; sampled Schwarz factors and integrals meet the bar."""
+    import torch
+    _log("case: C5 120-atom cluster, full implicit plan, sampled checks")
+    w = make_config(5)
+    sh = w.shells
+    plan = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
+    S = plan.schwarz().cpu().numpy()
+    _log(f"  plan: {plan.n_quartets} quartets, {plan.n_blocks} blocks")
+    sc = oplan.screened_counts(sh.l, sh.nprim, S, w.tau)
+    assert plan.n_quartets == sc["n_quartets"]
+    assert [(int(c), int(s), int(n)) for c, s, n in zip(plan.block_class, plan.block_start, plan.block_count)] == \
+        [tuple(int(v) for v in b) for b in sc["blocks"]]
+    rng = np.random.default_rng(5)
+    nprim = np.asarray(sh.nprim)
+    # Schwarz factors of sampled pairs with modest contraction, by their definition
+    ns = len(sh.l)
+    pi = rng.integers(0, ns, 400)
+    pj = rng.integers(0, ns, 400)
+    i, j = np.maximum(pi, pj), np.minimum(pi, pj)
+    sel = nprim[i] * nprim[j] <= 16
+    i, j = i[sel][:60], j[sel][:60]
+    flat, off = oracle.eri(sh, np.stack([i, j, i, j], axis=1), True)
+    ends = np.append(np.asarray(off)[:len(i)], len(flat))
+    Sref = np.array([np.abs(flat[ends[x]:ends[x + 1]]).max() for x in range(len(i))])
+    assert_parity(S[i * (i + 1) // 2 + j], Sref, "C5 sampled Schwarz factors")
+    # per block: the first slot and seeded slots of modest cost
+    out_rows, out_vals = [], []
+    for b in range(plan.n_blocks):
+        st, cnt = int(plan.block_start[b]), int(plan.block_count[b])
+        cand = np.unique(np.concatenate([[st], st + rng.integers(0, cnt, 64)]))
+        rows_all = oplan.screened_decode(sc, cand)
+        got_rows = np.concatenate([plan.quartets(int(s), 1).cpu().numpy() for s in cand[:8]])
+        np.testing.assert_array_equal(got_rows, rows_all[:8])
+        keep = np.flatnonzero(_cheap_slots(rows_all, nprim, 64))[:3]
+        for x in keep:
+            s = int(cand[x])
+            n = int(oracle.block_sizes(sh, rows_all[x:x + 1, :4], True)[0])
+            o = torch.empty(n, dtype=torch.float64, device="cuda")
+            eri.compute_range(plan, b, s - st, 1, o)
+            out_vals.append(o.cpu().numpy())
+            out_rows.append(rows_all[x])
+    torch.cuda.synchronize()
+    q = np.array(out_rows)[:, :4]
+    flat, _ = oracle.eri(sh, q, True)
+    _log(f"  {len(q)} sampled quartets over {plan.n_blocks} blocks")
+    assert_parity(np.concatenate(out_vals), flat, "C5 sampled integrals", sh, q, True)
+
+
 def test_all_120_classes_explicit(eri):
     """Every class up to (gg|gg), both output kinds, random shells with K <= 2."""
     _log("case: explicit mixed batch over all 120 classes")

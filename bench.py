@@ -27,6 +27,25 @@ sys.path.insert(0, ROOT)
 FP64_VECTOR_PEAK_TFLOPS = 78.6  # 256 CU x 128 FP64 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of the (dd|dd) K = 1 kernel from two rocprofv3 --pmc
+# passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), scaled by what the same
+# counters read for a 1 GiB device copy (x2.0 and x1.0).  Valid only for the
+# kernel source they were taken on: reported as null once it changes.
+TRAFFIC = {"kernel_source": "electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
+           "sha1": "6155816744b9747ab778c7d3621737f700179351",
+           "fetch_kib": 7101.49, "fetch_scale": 2.0, "write_kib": 98128.28, "write_scale": 1.0}
+
+
+def measured_traffic():
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, TRAFFIC["kernel_source"]), "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != TRAFFIC["sha1"]:
+                return None
+    except OSError:
+        return None
+    return 1024.0 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"])
+
 
 def _class_flops(plan, spherical):
     """Algorithmic FLOPs of every block of a plan (generator's DAG count)."""
@@ -126,6 +145,57 @@ def j_build(E, w, steps, stream):
                   "note": "plan_build_ms is host wall time incl. allocation; digest_J_ms is HIP-event time"}
 
 
+def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=200000):
+    """The 120-atom cluster: the full screened plan (implicit) is built and
+    timed; every class block is then sampled in ``strata`` evenly spaced
+    slot ranges (blocks are ordered by contraction length, so the strata span
+    the block's K mix) and timed with HIP events.  The full integral time is
+    extrapolated block by block -- an estimate, labelled as such: evaluating
+    all 2e10 quartets takes tens of minutes."""
+    import numpy as np
+    import torch
+    from electron_repulsion_integrals_amd.gen import graph as G
+    t0 = time.perf_counter()
+    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, None, w.tau)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    K = np.asarray(w.shells.nprim, dtype=np.int64)
+    classes, est_total_s, flops_total, sample_s = {}, 0.0, 0.0, 0.0
+    for b in range(plan.n_blocks):
+        cid, cnt = int(plan.block_class[b]), int(plan.block_count[b])
+        la, lb = G.pair_class_ls(_pcb(cid))
+        lc, ld = G.pair_class_ls(_pck(cid))
+        ci = G.ClassInfo(la, lb, lc, ld)
+        blk = ci.nout(True)
+        m = int(min(cnt, max_quartets, max(strata, max_doubles // blk)))
+        per = max(1, m // strata)
+        firsts = [int(x) for x in np.linspace(0, cnt - per, strata).astype(np.int64)]
+        out = torch.empty(per * blk, dtype=torch.float64, device="cuda")
+        ms, flops = 0.0, 0.0
+        per_prim, once = G.dag_flops(ci, True)
+        for f in firsts:
+            times, _ = time_launches(lambda: E.compute_range(plan, b, f, per, out), 3, 1, stream)
+            ms += sorted(times)[1]
+            rows = plan.quartets(int(plan.block_start[b]) + f, per).cpu().numpy()
+            k4 = K[rows[:, 0]] * K[rows[:, 1]] * K[rows[:, 2]] * K[rows[:, 3]]
+            flops += float(k4.sum()) * per_prim + per * once
+        n = per * len(firsts)
+        est_s = ms * 1e-3 * cnt / n
+        est_total_s += est_s
+        flops_total += flops * cnt / n
+        sample_s += ms * 1e-3
+        name = "(" + "spdfg"[la] + "spdfg"[lb] + "|" + "spdfg"[lc] + "spdfg"[ld] + ")"
+        classes[name] = {"quartets": cnt, "sampled": n, "sample_ms": ms, "quartets_per_s": n / (ms * 1e-3),
+                         "tflops": flops / (ms * 1e-3) / 1e12,
+                         "fp64_frac": flops / (ms * 1e-3) / 1e12 / FP64_VECTOR_PEAK_TFLOPS}
+    return {"quartets": plan.n_quartets, "class_blocks": plan.n_blocks, "plan_build_ms": plan_ms,
+            "estimated_integral_s": est_total_s,
+            "estimated_fp64_frac": flops_total / est_total_s / 1e12 / FP64_VECTOR_PEAK_TFLOPS,
+            "note": "plan built and timed in full; integrals timed on 8 evenly spaced slot ranges per class block "
+                    "and extrapolated per block (estimate, not a measured J build)",
+            "per_class": classes}
+
+
 def cpu_baseline(w, seconds=12.0):
     """The oracle as it stands on a bounded prefix of the workload's quartets."""
     import numpy as np
@@ -203,7 +273,7 @@ def main():
                                "exponents log-uniform [0.05, 20], spherical output, seed 1002",
                    "quartets": nq, "output_doubles": plan.n_out},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP64_VECTOR_PEAK_TFLOPS, "traffic": None},
+                     "frac": achieved / FP64_VECTOR_PEAK_TFLOPS, "traffic": measured_traffic()},
         "output_write_GBps": plan.n_out * 8 / (ms * 1e-3) / 1e9,
         "plan_build_ms": plan_ms,
         "wall_s_timed_region": wall,
@@ -220,6 +290,7 @@ def main():
         plan4 = E.build_quartets(w4.shells, E.ERI_SPHERICAL, w4.quartets, 0.0)
         res["per_class"]["(ff|ff) x 4000 + (gg|gg) x 1000"] = per_class(E, plan4, w4, 3, stream)
         del plan4
+        res["c5_120atom_tzvp"] = c5_sampled(E, make_config(5), stream)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

@@ -153,6 +153,17 @@ __device__ __forceinline__ void eri_boys(double T, double pref, const double* __
     for (int m = 0; m <= L; ++m) F[m] *= pref;
 }
 
+// A value that every lane of the wave holds identically (one quartet per
+// wave): reading it from the first lane lets the compiler keep it in scalar
+// registers and use it as a scalar operand, freeing two VGPRs per value.
+__device__ __forceinline__ double eri_uniform(double x)
+{
+    const long long b = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_readfirstlane((int)(b & 0xffffffffLL));
+    const int hi = __builtin_amdgcn_readfirstlane((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+
 // Read a double held by another lane of the same wave (ds_bpermute, byte address = lane * 4).
 __device__ __forceinline__ double eri_bperm(int byte_addr, double v)
 {

@@ -355,8 +355,142 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
            f"{64 // ci.G} quartets per wave",
            '#include "eri_device.h"', ""]
     out += _register_kernel(ci, spherical, k1=False)
-    out += _register_kernel(ci, spherical, k1=True)
+    batched = BATCH_K1 and ci.G >= K1_BATCH_MIN_G
+    out += _register_kernel_k1_batched(ci, spherical) if batched else _register_kernel(ci, spherical, k1=True)
     return "\n".join(out) + "\n"
+
+
+BATCH_K1 = True
+K1_BATCH = 32  # quartet records set up together, one per lane
+K1_BATCH_MIN_G = 8  # narrower lane groups repeat the set-up in few lanes: per-group set-up
+
+
+def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
+    """K4 = 1 kernel with batched set-up.  A wave walks its groups g, g + grid,
+    g + 2 grid, ...; every RB groups, each of the first RB x Q lanes computes
+    the geometry and Boys values of one quartet of the next RB groups into an
+    LDS record (field-major).  The serial set-up chain (pair records, exp,
+    reciprocals, square root, Boys table) then runs once per batch in parallel
+    lanes instead of once per quartet in all lanes."""
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    names = Names("V", kv, ci.Lk)
+    G = ci.G
+    Q = 64 // G
+    RB = max(1, K1_BATCH // Q)
+    NK = ci.nket(spherical)
+    NEB = ci.n_ebra
+    EOFF = ci.e_bra_offset
+    BLK = ci.nout(spherical)
+    L = ci.L
+    cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+    tag = f"c{cid}_{'s' if spherical else 'c'}_k1"
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    lane_tab = []
+    for e in lanes:
+        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
+        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
+    fields = REC_FIELDS + [f"F{m}" for m in range(L + 1)] + ["CDx", "CDy", "CDz", "ABx", "ABy", "ABz"]
+    NR = len(fields)
+    NRL = RB * Q  # records per batch
+    o = []
+    o.append("namespace {")
+    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
+    o.append("}  // namespace")
+    o.append(f"__global__ void __launch_bounds__(64) eri_kernel_{tag}(EriClassArgs a)")
+    o.append("{")
+    o.append(f"  constexpr int G = {G}, Q = {Q}, NK = {NK}, NEB = {NEB}, BLK = {BLK}, RB = {RB}, NRL = {NRL};")
+    o.append("  __shared__ double xch[Q * NEB * NK + NK];  // exchange rows, then a junk row")
+    o.append(f"  __shared__ double rec[{NR} * NRL];  // field-major quartet records of one batch")
+    o.append("  const int lane = threadIdx.x;")
+    o.append("  int grp = lane / G, sub = lane - grp * G;")
+    o.append("  if (grp >= Q) { grp = Q; sub = 0; }  // padding lanes: phantom group, e = (0,0,0)")
+    o.append(f"  const int lt = k_{tag}_lane[sub];")
+    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
+    o.append("  const int gb = grp * G;")
+    o.append("  const int adx = (ex > 0 ? gb + ((lt >> 12) & 63) - 1 : lane) * 4;")
+    o.append("  const int ady = (ey > 0 ? gb + ((lt >> 18) & 63) - 1 : lane) * 4;")
+    o.append("  const int adz = (ez > 0 ? gb + ((lt >> 24) & 63) - 1 : lane) * 4;")
+    o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
+    o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
+    o.append("  const int rq = grp < Q ? grp : 0;  // record member of this lane's group")
+    o.append("  int it = 0;")
+    o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
+    o.append("    const int bslot = it % RB;")
+    o.append("    if (bslot == 0) {")
+    o.append("      if (lane < NRL) {")
+    o.append("        const int k = lane / Q, gk = g + k * (int)gridDim.x;")
+    o.append("        int q = gk * Q + (lane - k * Q);")
+    o.append("        if (gk >= ngroups || q >= a.nq) q = a.nq - 1;  // past the end: a valid record, never used")
+    o.append("        const int bra = a.qbra[q], ket = a.qket[q];")
+    o.append("        const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
+    o.append("        const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
+    o.append("        const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
+    o.append("        const EriPrimPair P = eri_load_pp(a.ppd, pb.z);")
+    o.append("        const EriPrimPair K = eri_load_pp(a.ppd, pk.z);")
+    o.append("        EriQuartetGeom gq;")
+    o.append("        eri_geom(P, K, Ax - Cx, Ay - Cy, Az - Cz, gq);")
+    o.append(f"        double F[{L + 1}];")
+    o.append(f"        eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
+    vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
+            "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
+    vals += [f"F[{m}]" for m in range(L + 1)]
+    vals += ["Cx - a.cen[3 * pk.y]", "Cy - a.cen[3 * pk.y + 1]", "Cz - a.cen[3 * pk.y + 2]",
+             "Ax - a.cen[3 * pb.y]", "Ay - a.cen[3 * pb.y + 1]", "Az - a.cen[3 * pb.y + 2]"]
+    assert len(vals) == NR
+    o.append("        double* r = rec + lane;")
+    for fi, v in enumerate(vals):
+        o.append(f"        r[{fi} * NRL] = {v};")
+    o.append("      }")
+    o.append("      __syncthreads();")
+    o.append("    }")
+    o.append("    {")
+    o.append("      const double* r = rec + bslot * Q + rq;")
+    for fi, nm in enumerate(fields):
+        if nm.startswith("F"):
+            continue
+        o.append(f"      const double {nm} = r[{fi} * NRL];")
+    o.append(f"      double F[{L + 1}];")
+    for m in range(L + 1):
+        o.append(f"      F[{m}] = r[{len(REC_FIELDS) + m} * NRL];")
+    o.append("      (void)CDx; (void)CDy; (void)CDz; (void)ABx; (void)ABy; (void)ABz;")
+    o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
+    o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+    o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+    _stage1(ci, kv.base_m, o, "      ")
+    o.append(f"      double* xd = xch + ((grp < Q && es >= {ci.la}) ? (grp * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
+    init_keys = [("k", (0, 0, 0), m) for m in range(kv.base_m + 1)]
+    _emit_scheduled(_lane_ops(ci, kv, names, spherical, True), init_keys, names, o, "      ")
+    o.append("    }")
+    o.append("    __syncthreads();")
+    # H2: lanes own ket components
+    o.append("    for (int t = lane; t < Q * NK; t += 64) {")
+    o.append("      const int g2 = t / NK, kap = t - g2 * NK;")
+    o.append("      const int slot = g * Q + g2;")
+    o.append("      if (slot >= a.nq) continue;")
+    ab0 = fields.index("ABx")
+    o.append(f"      const double* r = rec + bslot * Q + g2;")
+    o.append(f"      const double ABx = r[{ab0} * NRL], ABy = r[{ab0 + 1} * NRL], ABz = r[{ab0 + 2} * NRL];")
+    o.append("      (void)ABx; (void)ABy; (void)ABz;")
+    o.append("      const double* src = xch + g2 * NEB * NK + kap;")
+    ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
+    epos = {e: i for i, e in enumerate(ebra)}
+    o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
+    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                        lambda k, x: f"dst[{k} * NK] = {x};", o, "      ", "z")
+    o.append("    }")
+    o.append("    __syncthreads();  // exchange and records are rewritten next")
+    o.append("  }")
+    o.append("}")
+    o.append("")
+    o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
+    o.append("{")
+    o.append(f"  const int ngroups = (a.nq + {Q} - 1) / {Q};")
+    o.append("  const int nblk = ngroups < a.grid_cap ? ngroups : a.grid_cap;")
+    o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3(64), 0, s, a);")
+    o.append("}")
+    o.append("")
+    return o
 
 
 
@@ -529,6 +663,9 @@ REC_FIELDS = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQ
               "i2z", "i2e", "roz", "roe", "i2ze"]
 
 
+UNIFORM_SCALARS = True
+
+
 def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     """K4 = 1 kernel: persistent loop, next group's inputs prefetched.
     General kernel: one group of Q quartets per wave; the primitive quartets are
@@ -563,7 +700,9 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append(f"__global__ void __launch_bounds__(64) eri_kernel_{tag}(EriClassArgs a)")
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
-    o.append("  __shared__ double xch[Q * NEB * NK];")
+    # exchange rows, then one junk row that lanes without a bra output write to
+    # (an LDS address with small positive offsets keeps the stores immediate-offset)
+    o.append("  __shared__ double xch[Q * NEB * NK + NK];")
     o.append("  __shared__ double xab[Q * 3];")
     if use_rec:
         o.append(f"  constexpr int NREC = {NREC};")
@@ -583,12 +722,17 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append("  if (g >= ngroups) return;")
     o.append("  auto slot_of = [&](int gg) { int q = gg * Q + (grp < Q ? grp : 0); return q < a.nq ? q : a.nq - 1; };")
     o.append("  int qs = slot_of(g);")
+    if k1 and Q == 1 and UNIFORM_SCALARS:
+        o.append("  qs = __builtin_amdgcn_readfirstlane(qs);")
     o.append("  int bra = a.qbra[qs], ket = a.qket[qs];")
     o.append("  int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
     o.append("  for (;;) {")
     o.append("    const int gn = g + (int)gridDim.x;")
     if k1:
-        o.append("    const int qn = slot_of(gn < ngroups ? gn : g);")
+        if Q == 1 and UNIFORM_SCALARS:
+            o.append("    const int qn = __builtin_amdgcn_readfirstlane(slot_of(gn < ngroups ? gn : g));")
+        else:
+            o.append("    const int qn = slot_of(gn < ngroups ? gn : g);")
         o.append("    const int bra_n = a.qbra[qn], ket_n = a.qket[qn];")
     o.append("    const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
     o.append("    const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
@@ -607,13 +751,19 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         r.append(f"{ind}eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
         return r
 
+    # one quartet per wave (K4 = 1 kernel): the quartet's scalars are the same
+    # in every lane and move to scalar registers
+    uni = k1 and Q == 1 and UNIFORM_SCALARS
+    U = (lambda x: f"eri_uniform({x})") if uni else (lambda x: x)
+
     def scalars_from_geom(ind):
         r = []
-        r.append(f"{ind}const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
-        r.append(f"{ind}const double WPx = gq.WP[0], WPy = gq.WP[1], WPz = gq.WP[2];")
-        r.append(f"{ind}const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
-        r.append(f"{ind}const double WQx = gq.WQ[0], WQy = gq.WQ[1], WQz = gq.WQ[2];")
-        r.append(f"{ind}const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = gq.roz, roe = gq.roe, i2ze = gq.i2ze;")
+        r.append(f"{ind}const double PAx = {U('P.PA[0]')}, PAy = {U('P.PA[1]')}, PAz = {U('P.PA[2]')};")
+        r.append(f"{ind}const double WPx = {U('gq.WP[0]')}, WPy = {U('gq.WP[1]')}, WPz = {U('gq.WP[2]')};")
+        r.append(f"{ind}const double QCx = {U('K.PA[0]')}, QCy = {U('K.PA[1]')}, QCz = {U('K.PA[2]')};")
+        r.append(f"{ind}const double WQx = {U('gq.WQ[0]')}, WQy = {U('gq.WQ[1]')}, WQz = {U('gq.WQ[2]')};")
+        r.append(f"{ind}const double i2z = {U('0.5 * P.izeta')}, i2e = {U('0.5 * K.izeta')}, roz = {U('gq.roz')}, "
+                 f"roe = {U('gq.roe')}, i2ze = {U('gq.i2ze')};")
         return r
 
     init_keys = [("k", (0, 0, 0), m) for m in range(kv.base_m + 1)]
@@ -627,8 +777,7 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         if with_acc:
             _emit_scheduled(_lane_ops(ci, kv, names, spherical, False), init_keys, names, r, ind)
         else:
-            r.append(f"{ind}double xjunk[{NK}];")
-            r.append(f"{ind}double* xd = (grp < Q && es >= {ci.la}) ? xch + (grp * NEB + (sub - {EOFF})) * NK : xjunk;")
+            r.append(f"{ind}double* xd = xch + ((grp < Q && es >= {ci.la}) ? (grp * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
             _emit_scheduled(_lane_ops(ci, kv, names, spherical, True), init_keys, names, r, ind)
         return r
 
@@ -686,8 +835,7 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         hind = "    "
     if not k1:
         # H1: ket HRR + transform per lane on the contracted values
-        o.append(f"{hind}double yjunk[{NK}];")
-        o.append(f"{hind}double* yd = (grp < Q && es >= {ci.la}) ? xch + (grp * NEB + (sub - {EOFF})) * NK : yjunk;")
+        o.append(f"{hind}double* yd = xch + ((grp < Q && es >= {ci.la}) ? (grp * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
         _emit_hrr_scheduled(ci.lc, ci.ld, base_of, "CD", spherical, lambda k, x: f"yd[{k}] = {x};", o, hind, "y")
     o.append(f"{hind}if (grp < Q && sub == 0) {{ xab[3 * grp] = ABx; xab[3 * grp + 1] = ABy; xab[3 * grp + 2] = ABz; }}")
     if k1:

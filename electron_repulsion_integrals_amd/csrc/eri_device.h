@@ -153,6 +153,10 @@ __device__ __forceinline__ void eri_boys(double T, double pref, const double* __
     for (int m = 0; m <= L; ++m) F[m] *= pref;
 }
 
+// Output blocks are written once and not read back by the kernel: streaming
+// (non-temporal) stores keep them from displacing inputs in the caches.
+__device__ __forceinline__ void eri_out(double* p, double v) { __builtin_nontemporal_store(v, p); }
+
 // A value that every lane of the wave holds identically (one quartet per
 // wave): reading it from the first lane lets the compiler keep it in scalar
 // registers and use it as a scalar operand, freeing two VGPRs per value.

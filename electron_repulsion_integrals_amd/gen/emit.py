@@ -126,8 +126,24 @@ def _alloc_slots(kv):
 # code pieces
 # ---------------------------------------------------------------------------
 
-def _stage1(ci: ClassInfo, base_m: int, lines, ind="      "):
-    """Bra phase for the lane's own e: [e0|00]^(m), m = 0..base_m, from F_m."""
+def _stage1_selectors(ci: ClassInfo, lines, stride, one_field, zero_field, ind="  "):
+    """Per-lane record offsets of the bra-path factors: step s of lane e moves
+    along axis ax_s, so it needs (P-A)_ax (record field ax) and (W-P)_ax (field
+    3 + ax); a lane whose path is shorter than the step reads the constant
+    fields 1 and 0, which leave its values unchanged.  Loop-invariant ints:
+    each step then costs two LDS reads instead of selects among six doubles."""
+    for s in range(1, ci.Lb + 1):
+        lines.append(f"{ind}const int ax{s} = ({s} <= ex) ? 0 : ({s} <= ex + ey) ? 1 : ({s} <= es) ? 2 : 3;")
+        lines.append(f"{ind}const int sel1_{s} = (ax{s} < 3 ? ax{s} : {one_field}) * {stride};")
+        lines.append(f"{ind}const int sel2_{s} = (ax{s} < 3 ? 3 + ax{s} : {zero_field}) * {stride};")
+        lines.append(f"{ind}const double gnf{s} = (double)(ax{s} == 0 ? {s - 1} : ax{s} == 1 ? {s - 1} - ex : "
+                     f"ax{s} == 2 ? {s - 1} - ex - ey : 0);")
+
+
+def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None):
+    """Bra phase for the lane's own e: [e0|00]^(m), m = 0..base_m, from F_m.
+    rsel: name of this lane's record pointer (factors read through the
+    selectors of _stage1_selectors); otherwise selects on PAx.. WPz."""
     L = ci.L
     for m in range(L + 1):
         lines.append(f"{ind}double c{m} = F[{m}];")
@@ -140,10 +156,15 @@ def _stage1(ci: ClassInfo, base_m: int, lines, ind="      "):
     for s in range(1, ci.Lb + 1):
         top = L - s
         lines.append(f"{ind}{{ // bra step {s}")
-        lines.append(f"{ind}  const int ax = ({s} <= ex) ? 0 : ({s} <= ex + ey) ? 1 : ({s} <= es) ? 2 : 3;")
-        lines.append(f"{ind}  const double g1 = ax == 0 ? PAx : ax == 1 ? PAy : ax == 2 ? PAz : 1.0;")
-        lines.append(f"{ind}  const double g2 = ax == 0 ? WPx : ax == 1 ? WPy : ax == 2 ? WPz : 0.0;")
-        lines.append(f"{ind}  const double gn = (double)(ax == 0 ? {s - 1} : ax == 1 ? {s - 1} - ex : ax == 2 ? {s - 1} - ex - ey : 0) * i2z;")
+        if rsel is not None:
+            lines.append(f"{ind}  const double g1 = {rsel}[sel1_{s}], g2 = {rsel}[sel2_{s}];")
+            lines.append(f"{ind}  const double gn = gnf{s} * i2z;")
+        else:
+            lines.append(f"{ind}  const int ax = ({s} <= ex) ? 0 : ({s} <= ex + ey) ? 1 : ({s} <= es) ? 2 : 3;")
+            lines.append(f"{ind}  const double g1 = ax == 0 ? PAx : ax == 1 ? PAy : ax == 2 ? PAz : 1.0;")
+            lines.append(f"{ind}  const double g2 = ax == 0 ? WPx : ax == 1 ? WPy : ax == 2 ? WPz : 0.0;")
+            lines.append(f"{ind}  const double gn = (double)(ax == 0 ? {s - 1} : ax == 1 ? {s - 1} - ex : "
+                         f"ax == 2 ? {s - 1} - ex - ey : 0) * i2z;")
         for m in range(top + 1):
             lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1} + gn * (p{m} - roz * p{m + 1});")
         for m in range(top + 1):
@@ -361,6 +382,7 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
 
 
 BATCH_K1 = True
+SELECT_LDS_CONTRACTED = True
 K1_BATCH = 32  # quartet records set up together, one per lane
 K1_BATCH_MIN_G = 8  # narrower lane groups repeat the set-up in few lanes: per-group set-up
 
@@ -391,7 +413,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
         d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
         lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
     fields = REC_FIELDS + [f"F{m}" for m in range(L + 1)] + ["CDx", "CDy", "CDz", "ABx", "ABy", "ABz"]
-    NR = len(fields)
+    NR = len(fields) + 2  # then two constant rows, 1.0 and 0.0, for the bra-path selectors
     NRL = RB * Q  # records per batch
     o = []
     o.append("namespace {")
@@ -414,6 +436,8 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append("  const int rq = grp < Q ? grp : 0;  // record member of this lane's group")
+    o.append(f"  if (lane < NRL) {{ rec[{NR - 2} * NRL + lane] = 1.0; rec[{NR - 1} * NRL + lane] = 0.0; }}")
+    _stage1_selectors(ci, o, "NRL", NR - 2, NR - 1)
     o.append("  int it = 0;")
     o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
     o.append("    const int bslot = it % RB;")
@@ -437,7 +461,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     vals += [f"F[{m}]" for m in range(L + 1)]
     vals += ["Cx - a.cen[3 * pk.y]", "Cy - a.cen[3 * pk.y + 1]", "Cz - a.cen[3 * pk.y + 2]",
              "Ax - a.cen[3 * pb.y]", "Ay - a.cen[3 * pb.y + 1]", "Az - a.cen[3 * pb.y + 2]"]
-    assert len(vals) == NR
+    assert len(vals) == NR - 2
     o.append("        double* r = rec + lane;")
     for fi, v in enumerate(vals):
         o.append(f"        r[{fi} * NRL] = {v};")
@@ -447,7 +471,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append("    {")
     o.append("      const double* r = rec + bslot * Q + rq;")
     for fi, nm in enumerate(fields):
-        if nm.startswith("F"):
+        if nm.startswith("F") or fi < 6:  # P-A and W-P are read by the bra path through its selectors
             continue
         o.append(f"      const double {nm} = r[{fi} * NRL];")
     o.append(f"      double F[{L + 1}];")
@@ -455,9 +479,9 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
         o.append(f"      F[{m}] = r[{len(REC_FIELDS) + m} * NRL];")
     o.append("      (void)CDx; (void)CDy; (void)CDz; (void)ABx; (void)ABy; (void)ABz;")
     o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
-    o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+    o.append("      (void)QCx; (void)QCy; (void)QCz;")
     o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-    _stage1(ci, kv.base_m, o, "      ")
+    _stage1(ci, kv.base_m, o, "      ", rsel="r")
     o.append(f"      double* xd = xch + ((grp < Q && es >= {ci.la}) ? (grp * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
     init_keys = [("k", (0, 0, 0), m) for m in range(kv.base_m + 1)]
     _emit_scheduled(_lane_ops(ci, kv, names, spherical, True), init_keys, names, o, "      ")
@@ -477,7 +501,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     epos = {e: i for i, e in enumerate(ebra)}
     o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
     _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                        lambda k, x: f"dst[{k} * NK] = {x};", o, "      ", "z")
+                        lambda k, x: f"eri_out(&dst[{k} * NK], {x});", o, "      ", "z")
     o.append("    }")
     o.append("    __syncthreads();  // exchange and records are rewritten next")
     o.append("  }")
@@ -691,8 +715,12 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
     targets = kv.targets
     L = ci.L
-    NREC = len(REC_FIELDS) + L + 1
+    NREC = len(REC_FIELDS) + L + 1 + 2  # then constant rows 1.0 and 0.0 for the bra-path selectors
     use_rec = (not k1) and G > 1
+    # LDS-selected bra-path factors pay off when the ket recurrence is short
+    # (measured: faster for (xx|ss) and (ps|ps), slower once the ket phase's
+    # cross-lane reads share the LDS pipeline)
+    sel_lds = use_rec and SELECT_LDS_CONTRACTED and (ci.Lk == 0 or (ci.Lk == 1 and ci.Lb == 1))
     o = []
     o.append("namespace {")
     o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
@@ -717,6 +745,10 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append("  const int ady = (ey > 0 ? gb + ((lt >> 18) & 63) - 1 : lane) * 4;")
     o.append("  const int adz = (ez > 0 ? gb + ((lt >> 24) & 63) - 1 : lane) * 4;")
     o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
+    if sel_lds:
+        o.append(f"  rec[{NREC - 2} * 64 + lane] = 1.0;")
+        o.append(f"  rec[{NREC - 1} * 64 + lane] = 0.0;")
+        _stage1_selectors(ci, o, "64", NREC - 2, NREC - 1)
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append("  int g = blockIdx.x;")
     o.append("  if (g >= ngroups) return;")
@@ -768,12 +800,14 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
 
     init_keys = [("k", (0, 0, 0), m) for m in range(kv.base_m + 1)]
 
-    def body(ind, with_acc):
+    def body(ind, with_acc, rsel=None):
         r = []
         r.append(f"{ind}const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
-        r.append(f"{ind}(void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
+        if rsel is None:
+            r.append(f"{ind}(void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz;")
+        r.append(f"{ind}(void)QCx; (void)QCy; (void)QCz;")
         r.append(f"{ind}(void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-        _stage1(ci, kv.base_m, r, ind)
+        _stage1(ci, kv.base_m, r, ind, rsel=rsel)
         if with_acc:
             _emit_scheduled(_lane_ops(ci, kv, names, spherical, False), init_keys, names, r, ind)
         else:
@@ -823,11 +857,12 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         o.append("      for (int j = 0; j < n; ++j) {")
         o.append("        const double* r = rec + gb + j;")
         for fi, nm in enumerate(REC_FIELDS):
-            o.append(f"        const double {nm} = r[{fi} * 64];")
+            if fi >= 6 or not sel_lds:  # P-A and W-P: read by the bra path through its selectors
+                o.append(f"        const double {nm} = r[{fi} * 64];")
         o.append(f"        double F[{L + 1}];")
         for m in range(L + 1):
             o.append(f"        F[{m}] = r[{len(REC_FIELDS) + m} * 64];")
-        o += body("        ", True)
+        o += body("        ", True, rsel="r" if sel_lds else None)
         o.append("      }")
         o.append("      __syncthreads();  // records are rewritten by the next chunk")
         o.append("    }")
@@ -856,7 +891,7 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     epos = {e: i for i, e in enumerate(ebra)}
     o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
     _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                        lambda k, x: f"dst[{k} * NK] = {x};", o, "      ", "z")
+                        lambda k, x: f"eri_out(&dst[{k} * NK], {x});", o, "      ", "z")
     o.append("    }")
     o.append("    if (gn >= ngroups) break;")
     o.append("    __syncthreads();  // exchange buffer reused by the next group")
@@ -1181,7 +1216,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
         o.append(f"    const int vx = (kap * W + {EOFF}) * 8;  // exchange row kappa, first bra lane")
         h2_load = lambda e: f"eri_bld(rs, vx, {xch0} * (W * 8) + {epos[e] * 8})"
     _emit_hrr_scheduled(ci.la, ci.lb, h2_load, "AB", spherical,
-                        lambda k, x: f"dst[{k} * NK] = {x};", o, "    ", "g")
+                        lambda k, x: f"eri_out(&dst[{k} * NK], {x});", o, "    ", "g")
     o.append("  }")
     o.append("  __syncthreads();  // the exchange is reused by the next quartet")
     o.append("  }")

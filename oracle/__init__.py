@@ -74,6 +74,12 @@ def lib():
         L.oracle_J_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
                                      ctypes.c_int, dp, dp]
         L.oracle_J_naive.restype = ctypes.c_int
+        L.oracle_K_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
+                                             ctypes.c_int64, ip, lp, dp, dp, dp]
+        L.oracle_K_from_quartets.restype = None
+        L.oracle_K_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
+                                     ctypes.c_int, dp, dp]
+        L.oracle_K_naive.restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_jitter.argtypes = [ctypes.c_uint64]
         L.oracle_set_jitter.restype = None
@@ -236,6 +242,39 @@ def J_naive(sh, spherical: bool, D) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_J_naive failed")
     return j
+
+
+def K_from_quartets(sh, spherical: bool, quartets, flat, off, D) -> np.ndarray:
+    """K_mu,nu = sum (mu la|nu si) D_la,si from unique quartets: every distinct
+    index permutation of each quartet added once (see eri_oracle.c)."""
+    bf = basis_offsets(sh, spherical)
+    nbf = int(bf[-1])
+    q, pq = _i(np.asarray(quartets).reshape(-1, 4))
+    l, pl = _i(sh.l)
+    b, pb = _i(bf)
+    f, pf = _d(flat)
+    of, pof = _l(off)
+    d, pd = _d(D)
+    K = np.zeros((nbf, nbf))
+    k, pk = _d(K)
+    lib().oracle_K_from_quartets(int(sh.l.shape[0]), pl, SPHERICAL if spherical else 0, pb, nbf,
+                                 len(q), pq, pof, pf, pd, pk)
+    return k
+
+
+def K_naive(sh, spherical: bool, D) -> np.ndarray:
+    """K by the plain sum over every ordered shell quadruple (tiny inputs only)."""
+    bf = basis_offsets(sh, spherical)
+    nbf = int(bf[-1])
+    b, pb = _i(bf)
+    d, pd = _d(D)
+    K = np.zeros((nbf, nbf))
+    k, pk = _d(K)
+    keep, args = _shell_args(sh)
+    rc = lib().oracle_K_naive(*args, SPHERICAL if spherical else 0, pb, nbf, pd, pk)
+    if rc != 0:
+        raise ValueError("oracle_K_naive failed")
+    return k
 
 
 def J_blocks(sh, spherical: bool, bra_pairs, D, S, tau):

@@ -650,6 +650,98 @@ int oracle_J_naive(int nshell, const double *centers, const int32_t *l, const in
     return rc;
 }
 
+/* Exchange matrix K_mu,nu = sum_(la,si) (mu la|nu si) D_la,si (the Coulomb
+   integrals of Eq. (1) contracted with the density along the second index of
+   each electron; no factor -1/2).  Plain four-index sum over every ordered
+   shell quadruple, no symmetry (tiny inputs only). */
+int oracle_K_naive(int nshell, const double *centers, const int32_t *l, const int32_t *nprim,
+                   const int32_t *prim_off, const double *exps, const double *coefs, int flags,
+                   const int32_t *bf_off, int nbf, const double *Dm, double *K)
+{
+    int64_t nq = (int64_t)nshell * nshell * nshell * nshell;
+    int32_t *qs = (int32_t *)malloc(sizeof(int32_t) * 4 * nq);
+    int64_t *off = (int64_t *)malloc(sizeof(int64_t) * nq);
+    int64_t tot = 0, q = 0;
+    for (int i = 0; i < nshell; ++i)
+        for (int j = 0; j < nshell; ++j)
+            for (int k = 0; k < nshell; ++k)
+                for (int m = 0; m < nshell; ++m, ++q) {
+                    qs[4 * q] = i, qs[4 * q + 1] = j, qs[4 * q + 2] = k, qs[4 * q + 3] = m;
+                    off[q] = tot;
+                    int n1 = (flags & OR_SPHERICAL) ? nsph(l[i]) : ncart(l[i]);
+                    int n2 = (flags & OR_SPHERICAL) ? nsph(l[j]) : ncart(l[j]);
+                    int n3 = (flags & OR_SPHERICAL) ? nsph(l[k]) : ncart(l[k]);
+                    int n4 = (flags & OR_SPHERICAL) ? nsph(l[m]) : ncart(l[m]);
+                    tot += (int64_t)n1 * n2 * n3 * n4;
+                }
+    double *buf = (double *)malloc(sizeof(double) * tot);
+    int rc = oracle_eri_quartets(nshell, centers, l, nprim, prim_off, exps, coefs, flags, nq, qs, off, buf);
+    for (int64_t x = 0; x < (int64_t)nbf * nbf; ++x) K[x] = 0.0;
+    for (q = 0; q < nq; ++q) {
+        int i = qs[4 * q], j = qs[4 * q + 1], k = qs[4 * q + 2], m = qs[4 * q + 3];
+        int n1 = (flags & OR_SPHERICAL) ? nsph(l[i]) : ncart(l[i]);
+        int n2 = (flags & OR_SPHERICAL) ? nsph(l[j]) : ncart(l[j]);
+        int n3 = (flags & OR_SPHERICAL) ? nsph(l[k]) : ncart(l[k]);
+        int n4 = (flags & OR_SPHERICAL) ? nsph(l[m]) : ncart(l[m]);
+        const double *I = buf + off[q];
+        for (int a = 0; a < n1; ++a)
+            for (int b = 0; b < n2; ++b)
+                for (int c = 0; c < n3; ++c)
+                    for (int d = 0; d < n4; ++d)
+                        K[(int64_t)(bf_off[i] + a) * nbf + bf_off[k] + c] +=
+                            I[((a * n2 + b) * n3 + c) * n4 + d] * Dm[(int64_t)(bf_off[j] + b) * nbf + bf_off[m] + d];
+    }
+    free(qs);
+    free(off);
+    free(buf);
+    return rc;
+}
+
+/* K from unique quartets: every distinct ordered shell quadruple among the
+   eight index permutations of a unique quartet (ij|kl) = (ji|kl) = (ij|lk) =
+   (kl|ij) = ... is added once, with the block element taken from the unique
+   quartet's block by the corresponding index permutation. */
+void oracle_K_from_quartets(int nshell, const int32_t *l, int flags, const int32_t *bf_off, int nbf,
+                            int64_t nq, const int32_t *quartets, const int64_t *int_off,
+                            const double *ints, const double *Dm, double *K)
+{
+    (void)nshell;
+    for (int64_t x = 0; x < (int64_t)nbf * nbf; ++x) K[x] = 0.0;
+    for (int64_t q = 0; q < nq; ++q) {
+        const int s[4] = {quartets[4 * q], quartets[4 * q + 1], quartets[4 * q + 2], quartets[4 * q + 3]};
+        int n[4];
+        for (int t = 0; t < 4; ++t) n[t] = (flags & OR_SPHERICAL) ? nsph(l[s[t]]) : ncart(l[s[t]]);
+        const double *I = ints + int_off[q];
+        /* the eight permutations as positions of the unique quartet's indices */
+        static const int perms[8][4] = {{0, 1, 2, 3}, {1, 0, 2, 3}, {0, 1, 3, 2}, {1, 0, 3, 2},
+                                        {2, 3, 0, 1}, {3, 2, 0, 1}, {2, 3, 1, 0}, {3, 2, 1, 0}};
+        int seen[8][4], nseen = 0;
+        for (int p = 0; p < 8; ++p) {
+            int t4[4];
+            for (int t = 0; t < 4; ++t) t4[t] = s[perms[p][t]];
+            int dup = 0;
+            for (int u = 0; u < nseen; ++u)
+                if (seen[u][0] == t4[0] && seen[u][1] == t4[1] && seen[u][2] == t4[2] && seen[u][3] == t4[3]) dup = 1;
+            if (dup) continue;
+            for (int t = 0; t < 4; ++t) seen[nseen][t] = t4[t];
+            ++nseen;
+            /* element (x0 x1|x2 x3) of the permuted quartet = I at the unique quartet's
+               positions: index x_t belongs to position perms[p][t] */
+            int x[4];
+            for (x[0] = 0; x[0] < n[perms[p][0]]; ++x[0])
+                for (x[1] = 0; x[1] < n[perms[p][1]]; ++x[1])
+                    for (x[2] = 0; x[2] < n[perms[p][2]]; ++x[2])
+                        for (x[3] = 0; x[3] < n[perms[p][3]]; ++x[3]) {
+                            int y[4];
+                            for (int t = 0; t < 4; ++t) y[perms[p][t]] = x[t];
+                            double v = I[((y[0] * n[1] + y[1]) * n[2] + y[2]) * n[3] + y[3]];
+                            K[(int64_t)(bf_off[t4[0]] + x[0]) * nbf + bf_off[t4[2]] + x[2]] +=
+                                v * Dm[(int64_t)(bf_off[t4[1]] + x[1]) * nbf + bf_off[t4[3]] + x[3]];
+                        }
+        }
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

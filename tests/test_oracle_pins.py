@@ -437,6 +437,63 @@ def test_J_spherical_equals_transformed_cartesian():
     np.testing.assert_allclose(Js, Tb @ Jc @ Tb.T, rtol=1e-11, atol=1e-12 * np.abs(Js).max())
 
 
+def _c1_unique_quartets(sh):
+    ns = sh.nshell
+    return [(i, j, k, l) for i in range(ns) for j in range(i + 1) for k in range(ns) for l in range(k + 1)
+            if i * (i + 1) // 2 + j >= k * (k + 1) // 2 + l]
+
+
+def test_K_unique_quartets_equals_naive_sum_c1():
+    """Exchange K_mu,nu = sum (mu la|nu si) D_la,si: the unique-quartet form (every
+    distinct permutation of a quartet once) against the plain four-index sum."""
+    w = make_config(1)
+    sh = w.shells
+    N = sh.nbf(False)
+    rng = np.random.default_rng(5)
+    C = rng.standard_normal((N, N // 4))
+    D = C @ C.T
+    Kn = oracle.K_naive(sh, False, D)
+    q = _c1_unique_quartets(sh)
+    flat, off = oracle.eri(sh, q, False)
+    Ku = oracle.K_from_quartets(sh, False, q, flat, off, D)
+    np.testing.assert_allclose(Ku, Kn, rtol=1e-12, atol=1e-12 * np.abs(Kn).max())
+    np.testing.assert_allclose(Kn, Kn.T, rtol=1e-12, atol=1e-13 * np.abs(Kn).max())
+
+
+def test_K_against_J_energies():
+    """One orbital, D = c c^T: c^T K c = c^T J c (both are (cc|cc)).  Several
+    orbitals: 0 <= tr(D K) <= tr(D J) (the antisymmetrised pair density is
+    non-negative)."""
+    w = make_config(1)
+    sh = w.shells
+    N = sh.nbf(False)
+    rng = np.random.default_rng(6)
+    c = rng.standard_normal(N)
+    D1 = np.outer(c, c)
+    J1, K1 = oracle.J_naive(sh, False, D1), oracle.K_naive(sh, False, D1)
+    assert c @ K1 @ c == pytest.approx(c @ J1 @ c, rel=1e-12)
+    C = rng.standard_normal((N, 5))
+    D = C @ C.T
+    eJ, eK = np.trace(D @ oracle.J_naive(sh, False, D)), np.trace(D @ oracle.K_naive(sh, False, D))
+    assert 0.0 < eK < eJ
+
+
+def test_K_spherical_equals_transformed_cartesian():
+    w = make_config(1)
+    sh = w.shells
+    Ns, Nc = sh.nbf(True), sh.nbf(False)
+    Tb = np.zeros((Ns, Nc))
+    bs, bc = oracle.basis_offsets(sh, True), oracle.basis_offsets(sh, False)
+    for s in range(sh.nshell):
+        Tb[bs[s]:bs[s + 1], bc[s]:bc[s + 1]] = oracle.sph_coeffs(int(sh.l[s]))
+    rng = np.random.default_rng(7)
+    C = rng.standard_normal((Ns, 3))
+    D = C @ C.T
+    Ks = oracle.K_naive(sh, True, D)
+    Kc = oracle.K_naive(sh, False, Tb.T @ D @ Tb)
+    np.testing.assert_allclose(Ks, Tb @ Kc @ Tb.T, rtol=1e-11, atol=1e-12 * np.abs(Ks).max())
+
+
 def _golden(name):
     import os
     vals = {}

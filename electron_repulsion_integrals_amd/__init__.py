@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     compute_batch,
     compute_range,
     digest_J,
+    digest_JK,
     load,
     strerror,
 )

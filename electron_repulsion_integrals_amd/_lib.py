@@ -71,6 +71,8 @@ def load():
     L.eri_plan_quartets.restype = ctypes.c_int
     L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
     L.eri_digest_J.restype = ctypes.c_int
+    L.eri_digest_JK.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+    L.eri_digest_JK.restype = ctypes.c_int
     L.eri_strerror.argtypes = [ctypes.c_int]
     L.eri_strerror.restype = ctypes.c_char_p
     L.eri_class_info.argtypes = [ctypes.c_int32, i32p, i32p]
@@ -201,6 +203,15 @@ def digest_J(plan: Plan, D, J, stream=None):
     _check(load().eri_digest_J(plan.handle, _ptr(D), int(D.stride(0)), _ptr(J), int(J.stride(0)),
                                _stream_handle(stream)))
     return J
+
+
+def digest_JK(plan: Plan, D, J=None, K=None, stream=None):
+    """J and/or K (device, nbf x nbf, float64) from the symmetric density D in one pass."""
+    _check(load().eri_digest_JK(plan.handle, _ptr(D), int(D.stride(0)),
+                                _ptr(J) if J is not None else None, int(J.stride(0)) if J is not None else 0,
+                                _ptr(K) if K is not None else None, int(K.stride(0)) if K is not None else 0,
+                                _stream_handle(stream)))
+    return J, K
 
 
 def class_info(class_id: int):

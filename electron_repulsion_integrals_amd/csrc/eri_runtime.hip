@@ -464,6 +464,117 @@ __global__ void k_add_runs(const int *nruns, const int *key, const int *rstart, 
     }
 }
 
+// ---- K digestion ----------------------------------------------------------
+//
+// K_mu,nu = sum (mu la|nu si) D_la,si.  A unique quartet (ij|kl) stands for
+// up to eight ordered shell quadruples.  Those with i in the bra's first and k
+// in the ket's first position give four blocks of
+//   A_ik += I D_jl,  A_jk += I D_il (i != j),  A_il += I D_jk (k != l),
+//   A_jl += I D_ik (i != j, k != l),
+// each contracted over the other two indices; the other four quadruples give
+// the transposed blocks, so K = A + A^T for a symmetric D.  When the bra and
+// ket pairs are the same pair, the transposed quadruples are the same as the
+// first four: those quartets count one half in A.
+
+// per quartet: the four blocks V1 (na x nc), V2 (nb x nc), V3 (na x nd), V4 (nb x nd)
+__global__ void k_kdigest_block(int nq, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
+                                const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
+                                double *kv)
+{
+    const int q = blockIdx.x;
+    if (q >= nq) return;
+    const int pb = qbra[q], pk = qket[q];
+    const int4 ib = pinfo[pb], ik = pinfo[pk];
+    const int i0 = bf[ib.x], j0 = bf[ib.y], k0 = bf[ik.x], l0 = bf[ik.y];
+    const bool dij = ib.x != ib.y, dkl = ik.x != ik.y;
+    const double w = pb == pk ? 0.5 : 1.0;
+    const int nab = na * nb, ncd = nc * nd;
+    const double *blk = I + (size_t)q * nab * ncd;
+    double *v = kv + (size_t)q * (na * nc + nb * nc + na * nd + nb * nd);
+    double *v1 = v, *v2 = v1 + na * nc, *v3 = v2 + nb * nc, *v4 = v3 + na * nd;
+    for (int u = threadIdx.x; u < na * nc; u += blockDim.x) {
+        const int a = u / nc, c = u - a * nc;
+        double t = 0.0;
+        for (int b = 0; b < nb; ++b)
+            for (int d = 0; d < nd; ++d) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + l0 + d];
+        v1[u] = w * t;
+    }
+    for (int u = threadIdx.x; u < nb * nc; u += blockDim.x) {
+        const int b = u / nc, c = u - b * nc;
+        double t = 0.0;
+        if (dij)
+            for (int a = 0; a < na; ++a)
+                for (int d = 0; d < nd; ++d) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + l0 + d];
+        v2[u] = w * t;
+    }
+    for (int u = threadIdx.x; u < na * nd; u += blockDim.x) {
+        const int a = u / nd, d = u - a * nd;
+        double t = 0.0;
+        if (dkl)
+            for (int b = 0; b < nb; ++b)
+                for (int c = 0; c < nc; ++c) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + k0 + c];
+        v3[u] = w * t;
+    }
+    for (int u = threadIdx.x; u < nb * nd; u += blockDim.x) {
+        const int b = u / nd, d = u - b * nd;
+        double t = 0.0;
+        if (dij && dkl)
+            for (int a = 0; a < na; ++a)
+                for (int c = 0; c < nc; ++c) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + k0 + c];
+        v4[u] = w * t;
+    }
+}
+
+// chunk entries for K: (target shell block s1 * nshell + s2, offset of the block's
+// vector) for the four blocks of every quartet; blocks a quartet does not have
+// get a key that sorts last
+__global__ void k_kchunk_entries(int m, const int *qbra, const int *qket, const int4 *pinfo, int nshell, int na,
+                                 int nb, int nc, int nd, int *ekey, int64_t *eoff)
+{
+    const int q = blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= m) return;
+    const int4 ib = pinfo[qbra[q]], ik = pinfo[qket[q]];
+    const bool dij = ib.x != ib.y, dkl = ik.x != ik.y;
+    const int64_t base = (int64_t)q * (na * nc + nb * nc + na * nd + nb * nd);
+    const int none = 0x7fffffff;
+    ekey[4 * q] = ib.x * nshell + ik.x;
+    eoff[4 * q] = base;
+    ekey[4 * q + 1] = dij ? ib.y * nshell + ik.x : none;
+    eoff[4 * q + 1] = base + na * nc;
+    ekey[4 * q + 2] = dkl ? ib.x * nshell + ik.y : none;
+    eoff[4 * q + 2] = base + na * nc + nb * nc;
+    ekey[4 * q + 3] = (dij && dkl) ? ib.y * nshell + ik.y : none;
+    eoff[4 * q + 3] = base + na * nc + nb * nc + na * nd;
+}
+
+// one workgroup per run of equal target blocks: add the run's vectors in entry order into A
+__global__ void k_add_runs_K(const int *nruns, const int *key, const int *rstart, const int *rlen, const int64_t *eoff,
+                             const double *kv, int nshell, const int *bf, const int *nfun_sh, double *A, int lda)
+{
+    const int u = blockIdx.x;
+    if (u >= *nruns) return;
+    const int k = key[u];
+    if (k == 0x7fffffff) return;
+    const int s1 = k / nshell, s2 = k - s1 * nshell;
+    const int n1 = nfun_sh[s1], n2 = nfun_sh[s2];
+    const int e0 = rstart[u], e1 = e0 + rlen[u];
+    for (int v = threadIdx.x; v < n1 * n2; v += blockDim.x) {
+        double acc = 0.0;
+        for (int e = e0; e < e1; ++e) acc += kv[eoff[e] + v];
+        const int x = v / n2, y = v - x * n2;
+        A[(size_t)(bf[s1] + x) * lda + bf[s2] + y] += acc;
+    }
+}
+
+// K = A + A^T
+__global__ void k_sym_add(int n, const double *A, int lda, double *K, int ldk)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)n * n) return;
+    const int x = (int)(t / n), y = (int)(t - (int64_t)x * n);
+    K[(size_t)x * ldk + y] = A[(size_t)x * lda + y] + A[(size_t)y * lda + x];
+}
+
 __global__ void k_pair_hi(int np, const int4 *pinfo, int *hi)
 {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
@@ -624,6 +735,7 @@ struct eri_plan {
     int64_t *d_ceo = nullptr, *d_ceo2 = nullptr;
     void *d_ctmp = nullptr;
     size_t ctmp_bytes = 0;
+    double *d_ckv = nullptr, *d_kacc = nullptr;  // K contribution vectors of a chunk; A (K = A + A^T)
     // J digestion work (screened plans, built on first use)
     bool jready = false;
     double *d_ints = nullptr, *d_cb = nullptr;
@@ -777,26 +889,28 @@ void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t 
     }
 }
 
-// J of an implicit plan, chunk by chunk: integrals of the chunk, per-quartet
-// contribution vectors, entries sorted by pair (stable), then each pair's run
-// added to J.  Chunks go in plan order, so the sums are deterministic.
-void digest_J_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj, hipStream_t s)
+// J and/or K, chunk by chunk: integrals of the chunk, per-quartet
+// contribution vectors, entries sorted by target (stable), then each target's
+// run added in entry order.  Chunks go in plan order, so the sums are
+// deterministic.  Used for implicit plans (J) and for K with any plan.
+void digest_JK_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, hipStream_t s)
 {
     const int64_t CO = int64_t(1) << 27, CB = int64_t(1) << 26;
     const int64_t CQ = P->chunk_q;
+    const int64_t NE = 4 * CQ;  // entries per chunk: two per quartet for J, four for K
     if (!P->cjready) {
         P->d_cints = P->alloc<double>(CO);
         P->d_ccb = P->alloc<double>(CB);
-        P->d_cek = P->alloc<int>(2 * CQ);
-        P->d_cek2 = P->alloc<int>(2 * CQ);
-        P->d_ceo = P->alloc<int64_t>(2 * CQ);
-        P->d_ceo2 = P->alloc<int64_t>(2 * CQ);
-        P->d_ruk = P->alloc<int>(2 * CQ);
-        P->d_rlen = P->alloc<int>(2 * CQ);
-        P->d_rst = P->alloc<int>(2 * CQ);
+        P->d_cek = P->alloc<int>(NE);
+        P->d_cek2 = P->alloc<int>(NE);
+        P->d_ceo = P->alloc<int64_t>(NE);
+        P->d_ceo2 = P->alloc<int64_t>(NE);
+        P->d_ruk = P->alloc<int>(NE);
+        P->d_rlen = P->alloc<int>(NE);
+        P->d_rst = P->alloc<int>(NE);
         P->d_nruns = P->alloc<int>(1);
         size_t t1 = 0, t2 = 0, t3 = 0;
-        const int n2 = (int)(2 * CQ);
+        const int n2 = (int)NE;
         HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0, 32, s));
         HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns, n2, s));
         HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, P->d_rlen, P->d_rst, n2, s));
@@ -805,37 +919,62 @@ void digest_J_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj,
         P->cjready = true;
     }
     const int n = P->nbf;
-    hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, J, ldj);
+    if (K && !P->d_kacc) {
+        P->d_ckv = P->alloc<double>(CB);
+        P->d_kacc = P->alloc<double>((size_t)n * n);
+    }
+    // sort the n2 entries in d_cek/d_ceo and encode their runs
+    auto sort_runs = [&](int n2) {
+        size_t tb = P->ctmp_bytes;
+        HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(P->d_ctmp, tb, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0, 32, s));
+        tb = P->ctmp_bytes;
+        HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(P->d_ctmp, tb, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns, n2, s));
+        tb = P->ctmp_bytes;
+        HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(P->d_ctmp, tb, P->d_rlen, P->d_rst, n2, s));
+    };
+    if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, J, ldj);
+    if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->d_kacc, n);
     HIP_CHECK(hipGetLastError());
     for (const EriBlock &B : P->blocks) {
         const int nab = B.na * B.nb, ncd = B.nc * B.nd;
+        const int nkv = B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd;
         const int64_t blk = (int64_t)nab * ncd;
-        const int64_t step = std::max<int64_t>(1, std::min(CQ, std::min(CO / blk, CB / (nab + ncd))));
+        const int64_t step = std::max<int64_t>(
+            1, std::min(std::min(CQ, CO / blk), std::min(CB / (nab + ncd), CB / nkv)));
         for (int64_t c = 0; c < B.count; c += step) {
             const int64_t m = std::min(step, B.count - c);
             const int *qb = nullptr, *qk = nullptr;
             slot_lists(P, B.start + c, m, &qb, &qk, s);
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
             launch_class(P, B.cid, qb, qk, m, P->d_cints, s, nk1);
-            hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd, qb, qk,
-                               P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
-            hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, nab, ncd, P->d_cek,
-                               P->d_ceo);
-            HIP_CHECK(hipGetLastError());
-            const int n2 = (int)(2 * m);
-            size_t tb = P->ctmp_bytes;
-            HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(P->d_ctmp, tb, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0,
-                                                         32, s));
-            tb = P->ctmp_bytes;
-            HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(P->d_ctmp, tb, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns,
-                                                            n2, s));
-            tb = P->ctmp_bytes;
-            HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(P->d_ctmp, tb, P->d_rlen, P->d_rst, n2, s));
-            // at most 2m runs; workgroups past the device-side run count exit at once
-            hipLaunchKernelGGL(k_add_runs, dim3((unsigned)n2), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst, P->d_rlen,
-                               P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
-            HIP_CHECK(hipGetLastError());
+            if (J) {
+                hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd, qb,
+                                   qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
+                hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, nab, ncd,
+                                   P->d_cek, P->d_ceo);
+                HIP_CHECK(hipGetLastError());
+                sort_runs((int)(2 * m));
+                // at most 2m runs; workgroups past the device-side run count exit at once
+                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)(2 * m)), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst,
+                                   P->d_rlen, P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
+                HIP_CHECK(hipGetLastError());
+            }
+            if (K) {
+                hipLaunchKernelGGL(k_kdigest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd,
+                                   qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ckv);
+                hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, P->d_pinfo,
+                                   P->nshell, B.na, B.nb, B.nc, B.nd, P->d_cek, P->d_ceo);
+                HIP_CHECK(hipGetLastError());
+                sort_runs((int)(4 * m));
+                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)(4 * m)), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst,
+                                   P->d_rlen, P->d_ceo2, P->d_ckv, P->nshell, P->d_bf, P->d_nfun, P->d_kacc, n);
+                HIP_CHECK(hipGetLastError());
+            }
         }
+    }
+    if (K) {
+        hipLaunchKernelGGL(k_sym_add, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->d_kacc, n, K, ldk);
+        HIP_CHECK(hipGetLastError());
     }
 }
 
@@ -1336,7 +1475,7 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
     hipStream_t s = (hipStream_t)stream;
     if (P->implicit) {
         try {
-            digest_J_chunked(P, D, ldd, J, ldj, s);
+            digest_JK_chunked(P, D, ldd, J, ldj, nullptr, 0, s);
         } catch (const HipFail &f) {
             return translate(f);
         }
@@ -1407,6 +1546,21 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
         hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(64), 0, s, (int)P->npairs, P->d_pinfo,
                            P->d_bf, P->d_nfun, P->d_seg, P->d_eoff, P->d_cb, J, ldj);
         HIP_CHECK(hipGetLastError());
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_digest_JK(const eri_plan *Pc, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
+                             int32_t ldk, void *stream)
+{
+    eri_plan *P = const_cast<eri_plan *>(Pc);
+    if (!P || !D || (!J && !K) || ldd < P->nbf || (J && ldj < P->nbf) || (K && ldk < P->nbf)) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    if (P->nshell > 46340) return ERI_E_UNSUPPORTED;  // target block keys are nshell^2 in 32 bits
+    try {
+        digest_JK_chunked(P, D, ldd, J, ldj, K, ldk, (hipStream_t)stream);
     } catch (const HipFail &f) {
         return translate(f);
     }

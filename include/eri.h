@@ -166,6 +166,21 @@ int eri_compute_range(const eri_plan *plan, int32_t block, int64_t first, int64_
  */
 int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream);
 
+/*
+ * Coulomb and exchange matrices of a screened plan in one pass over its
+ * integrals: J as eri_digest_J, and K_mu,nu = sum (mu la|nu si) D_la,si (no
+ * factor -1/2), both over the plan's unique quartets with their index
+ * permutations, D symmetric.  J or K may be NULL (not both); each given matrix
+ * (order nbf, leading dimension ldj / ldk, device) is fully overwritten.
+ * Chunk by chunk: integrals, per-quartet contribution blocks (for K the four
+ * blocks (ik), (jk), (il), (jl) of a quartet (ij|kl), contracted with D over
+ * the other pair of indices), sorted by target block and added in plan order,
+ * then K = A + A^T; deterministic, no atomics.  Asynchronous; the plan keeps
+ * work buffers between calls (the calls on one plan must not overlap).
+ */
+int eri_digest_JK(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
+                  int32_t ldk, void *stream);
+
 /* Static text for an error code, with the last HIP error for ERI_E_HIP. */
 const char *eri_strerror(int code);
 

@@ -306,6 +306,33 @@ def J_blocks(sh, spherical: bool, bra_pairs, D, S, tau):
     return out
 
 
+def K_blocks(sh, spherical: bool, pairs, D, S, tau):
+    """K blocks for the given ordered shell pairs (i, k) by the plain sum
+    K_mu,nu = sum over every shell j and every shell l of
+    sum_(la in j, si in l) (mu la|nu si) D_la,si, keeping only the quartets with
+    fl(S_ij * S_kl) >= fl(tau^2) (S indexed by pair index).  Returns a list of
+    arrays [n_i, n_k]."""
+    ns = int(sh.l.shape[0])
+    bf = basis_offsets(sh, spherical)
+    t2 = float(tau) * float(tau)
+
+    def pidx(x, y):
+        return max(x, y) * (max(x, y) + 1) // 2 + min(x, y)
+    out = []
+    for (i, k) in pairs:
+        keep = [(j, l) for j in range(ns) for l in range(ns) if S[pidx(i, j)] * S[pidx(k, l)] >= t2]
+        q = [(i, j, k, l) for (j, l) in keep]
+        flat, off = eri(sh, q, spherical)
+        ni, nk = nfunc(int(sh.l[i]), spherical), nfunc(int(sh.l[k]), spherical)
+        K = np.zeros((ni, nk))
+        for t, (j, l) in enumerate(keep):
+            nj, nl = nfunc(int(sh.l[j]), spherical), nfunc(int(sh.l[l]), spherical)
+            blk = flat[off[t]: off[t] + ni * nj * nk * nl].reshape(ni, nj, nk, nl)
+            K += np.einsum("abcd,bd->ac", blk, D[bf[j]:bf[j + 1], bf[l]:bf[l + 1]])
+        out.append(K)
+    return out
+
+
 def conditioning_spread(sh, quartets, spherical: bool, ref=None, seeds=(0x9E3779B97F4A7C15, 0xD1B54A32D192ED03)):
     """Per-quartet change of the oracle's block when every Boys input is perturbed by
     at most one unit in the last place (two seeded perturbations, maximum taken).

@@ -437,3 +437,30 @@ def test_c3_full_size_plan_and_sampled_J(eri):
     for (i, j), Jb in zip(bras, refs):
         assert_parity(Jg[bf[i]:bf[i + 1], bf[j]:bf[j + 1]], Jb, f"J block ({i},{j})")
         assert_parity(Jg[bf[j]:bf[j + 1], bf[i]:bf[i + 1]], Jb.T, f"J block ({j},{i})")
+
+
+def test_c3_full_size_JK(eri):
+    """30-atom SVP-like cluster, tau = 1e-12: J and K in one pass; J agrees with
+    eri_digest_J's, sampled K blocks (diagonal and off-diagonal shell pairs)
+    against the plain sum over every (j, l) shell pair, K symmetric."""
+    import torch
+    _log("case: C3 full 30-atom cluster, J and K in one pass")
+    w = make_config(3)
+    sh = w.shells
+    plan = eri.build_quartets(sh, 1, None, w.tau)
+    S_gpu = plan.schwarz().cpu().numpy()
+    D = torch.tensor(w.density, device="cuda")
+    J0, J, K = torch.empty_like(D), torch.empty_like(D), torch.empty_like(D)
+    eri.digest_J(plan, D, J0)
+    eri.digest_JK(plan, D, J, K)
+    torch.cuda.synchronize()
+    assert_parity(J.cpu().numpy(), J0.cpu().numpy(), "J of the JK pass vs eri_digest_J")
+    Kg = K.cpu().numpy()
+    assert np.array_equal(Kg, Kg.T)
+    rng = np.random.default_rng(31)
+    ns = sh.nshell
+    pairs = [(int(i), int(i)) for i in rng.choice(ns, 2, replace=False)] + \
+            [(int(i), int(k)) for i, k in zip(rng.choice(ns, 3, replace=False), rng.choice(ns, 3, replace=False))]
+    bf = oracle.basis_offsets(sh, True)
+    for (i, k), Kb in zip(pairs, oracle.K_blocks(sh, True, pairs, w.density, S_gpu, w.tau)):
+        assert_parity(Kg[bf[i]:bf[i + 1], bf[k]:bf[k + 1]], Kb, f"K block ({i},{k})")

@@ -376,8 +376,14 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
            f"{64 // ci.G} quartets per wave",
            '#include "eri_device.h"', ""]
     out += _register_kernel(ci, spherical, k1=False)
+    from .packed import use_packed_k1, emit_packed_k1
     batched = BATCH_K1 and ci.G >= K1_BATCH_MIN_G
-    out += _register_kernel_k1_batched(ci, spherical) if batched else _register_kernel(ci, spherical, k1=True)
+    if use_packed_k1(ci, spherical):
+        out += emit_packed_k1(ci, spherical)
+    elif batched:
+        out += _register_kernel_k1_batched(ci, spherical)
+    else:
+        out += _register_kernel(ci, spherical, k1=True)
     return "\n".join(out) + "\n"
 
 

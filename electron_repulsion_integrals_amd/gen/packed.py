@@ -1,0 +1,246 @@
+"""Packed register-tier kernels: several quartets per multi-wave workgroup.
+
+The register tier maps one bra component e to one lane, so a quartet occupies
+G = #{e : |e| <= la+lb} lanes.  When G does not divide 64 (G = 35 for a bra
+of total angular momentum 4, e.g. the (dd| and (fp| classes), a wave64 holds
+one quartet and a large share of its lanes idles through every phase.  Here a
+workgroup of W waves holds Q = floor(64 W / G) quartets back to back (lane t
+serves quartet t / G, component t mod G), so the lanes are almost all busy.
+
+The coupling operand of the ket recurrence, [e-1_i 0|f-1_i 0]^(m+1), may then
+belong to another wave.  The ket recurrence therefore runs level by level
+(level k = nodes with |f| = k): each lane publishes the values of level k-1
+that level k reads across lanes to an LDS buffer, one workgroup barrier, and
+every lane reads its coupling operands for the whole level at once.  Two
+buffers alternate, so one barrier per level suffices.  On gfx950 this is also
+cheaper than the wave-local ds_bpermute it replaces: a double via bpermute is
+two permute instructions at about 6 LDS clocks each, against one 64-bit LDS
+read (about 4 clocks) plus a share of one 64-bit write that serves every
+reader of that value.
+
+Algorithmically nothing changes ("FusionRCG", section II-A, Eq. (2) and its ket
+twin for the vertical recurrence, Eq. (3) for the horizontal ones, Eq. (14)
+for the stepwise spherical transform): per quartet the lanes walk the bra
+path, run the ket recurrence, apply the ket HRR and transform per lane, hand
+the block through one LDS exchange to lanes that own ket components, and
+finish with the bra HRR and transform.
+"""
+from __future__ import annotations
+
+from .cartesian import components, sub
+from .graph import ClassInfo, build_ket_vrr, class_id
+
+LDS_BYTES = 160 * 1024
+# measured on the (dd|dd) batch: two waves (three quartets) per workgroup beat
+# three or four waves; a record batch covering eight groups
+PACK_WAVES = 2
+PACK_RB = 8
+
+
+def packed_shape(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES):
+    """(W, Q, NT): waves per workgroup, quartets per workgroup, threads."""
+    NT = 64 * waves
+    return waves, NT // ci.G, NT
+
+
+def _levels(kv):
+    """Per ket level k: the distinct coupling sources (values of level k-1)."""
+    lv = {}
+    for n in kv.nodes:
+        lst = lv.setdefault(sum(n.f), [])
+        if n.a1 not in lst:
+            lst.append(n.a1)
+    return lv
+
+
+def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB) -> int:
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    W, Q, NT = packed_shape(ci, spherical, waves)
+    lv = _levels(kv)
+    NC = max((len(v) for v in lv.values()), default=0)
+    NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
+    NR = 17 + ci.L + 1 + 6 + 2
+    return 8 * (max(2 * NC * NT, NX) + NR * rb * Q)
+
+
+def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
+    """Packing pays where a wave64 would leave many lanes idle."""
+    if ci.G > 64 or ci.G < 20:
+        return False
+    if (64 % ci.G) * 4 < 64:  # at most a quarter of the wave idles already
+        return False
+    if ci.Lk > 4:  # longer ket recurrences hold too many values for two waves per SIMD
+        return False
+    return packed_wg_per_cu(ci, spherical) >= 2
+
+
+def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB) -> int:
+    """Workgroups per compute unit: LDS-bound, at most two waves per SIMD."""
+    by_lds = LDS_BYTES // packed_lds_bytes(ci, spherical, waves, rb)
+    return int(min(by_lds, 8 // waves))
+
+
+def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB, wg_per_cu: int = 0,
+                   min_waves: int = 0):
+    """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
+    from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    names = Names("V", kv, ci.Lk)
+    G = ci.G
+    W, Q, NT = packed_shape(ci, spherical, waves)
+    if not wg_per_cu:
+        wg_per_cu = packed_wg_per_cu(ci, spherical, waves, rb)
+    NK = ci.nket(spherical)
+    NEB = ci.n_ebra
+    EOFF = ci.e_bra_offset
+    BLK = ci.nout(spherical)
+    L = ci.L
+    cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+    tag = f"c{cid}_{'s' if spherical else 'c'}_k1"
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    lane_tab = []
+    for e in lanes:
+        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
+        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
+    lv = _levels(kv)
+    levels = sorted(lv)
+    NC = max((len(v) for v in lv.values()), default=0)
+    fields = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
+              "i2z", "i2e", "roz", "roe", "i2ze"] + [f"F{m}" for m in range(L + 1)] + \
+             ["CDx", "CDy", "CDz", "ABx", "ABy", "ABz"]
+    NR = len(fields) + 2  # then two constant rows, 1.0 and 0.0, for the bra-path selectors
+    RB = rb
+    NRL = RB * Q
+    assert NRL <= NT
+    NX = Q * NEB * NK + NK  # exchange rows, then a junk row
+    NU = max(2 * NC * NT, NX)
+    o = []
+    o.append("namespace {")
+    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
+    o.append("}  // namespace")
+    o.append(f"// {Q} quartets per workgroup of {NT} lanes ({Q * G} busy); ket coupling through LDS, level by level")
+    lb = f"{NT}, {min_waves}" if min_waves else f"{NT}"
+    o.append(f"__global__ void __launch_bounds__({lb}) eri_kernel_{tag}(EriClassArgs a)")
+    o.append("{")
+    o.append(f"  constexpr int G = {G}, Q = {Q}, NT = {NT}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
+    o.append(f"  constexpr int RB = {RB}, NRL = {NRL}, NC = {max(NC, 1)};")
+    o.append(f"  // level buffers (two, alternating) during the recurrence; exchange afterwards")
+    o.append(f"  __shared__ double xu[{NU}];")
+    o.append(f"  __shared__ double rec[{NR} * NRL];  // field-major quartet records of one batch")
+    o.append("  const int tid = threadIdx.x;")
+    o.append("  int qi = tid / G, sub = tid - qi * G;")
+    o.append("  const bool real = qi < Q;")
+    o.append("  if (!real) { qi = 0; sub = 0; }  // spare lanes shadow e = (0,0,0) of the first quartet")
+    o.append(f"  const int lt = k_{tag}_lane[sub];")
+    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
+    o.append("  const int qb = qi * G;")
+    o.append("  const int srcx = ex > 0 ? qb + ((lt >> 12) & 63) - 1 : tid;")
+    o.append("  const int srcy = ey > 0 ? qb + ((lt >> 18) & 63) - 1 : tid;")
+    o.append("  const int srcz = ez > 0 ? qb + ((lt >> 24) & 63) - 1 : tid;")
+    o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
+    o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
+    o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * NRL + tid] = 1.0; rec[{NR - 1} * NRL + tid] = 0.0; }}")
+    _stage1_selectors(ci, o, "NRL", NR - 2, NR - 1)
+    o.append(f"  double* xd = xu + ((real && es >= {ci.la}) ? (qi * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
+    o.append("  int it = 0;")
+    o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
+    o.append("    const int bslot = it % RB;")
+    o.append("    if (bslot == 0) {")
+    o.append("      if (tid < NRL) {")
+    o.append("        const int k = tid / Q, gk = g + k * (int)gridDim.x;")
+    o.append("        int q = gk * Q + (tid - k * Q);")
+    o.append("        if (gk >= ngroups || q >= a.nq) q = a.nq - 1;  // past the end: a valid record, never stored")
+    o.append("        const int bra = a.qbra[q], ket = a.qket[q];")
+    o.append("        const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
+    o.append("        const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
+    o.append("        const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
+    o.append("        const EriPrimPair P = eri_load_pp(a.ppd, pb.z);")
+    o.append("        const EriPrimPair K = eri_load_pp(a.ppd, pk.z);")
+    o.append("        EriQuartetGeom gq;")
+    o.append("        eri_geom(P, K, Ax - Cx, Ay - Cy, Az - Cz, gq);")
+    o.append(f"        double F[{L + 1}];")
+    o.append(f"        eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
+    vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
+            "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
+    vals += [f"F[{m}]" for m in range(L + 1)]
+    vals += ["Cx - a.cen[3 * pk.y]", "Cy - a.cen[3 * pk.y + 1]", "Cz - a.cen[3 * pk.y + 2]",
+             "Ax - a.cen[3 * pb.y]", "Ay - a.cen[3 * pb.y + 1]", "Az - a.cen[3 * pb.y + 2]"]
+    assert len(vals) == NR - 2
+    o.append("        double* r = rec + tid;")
+    for fi, v in enumerate(vals):
+        o.append(f"        r[{fi} * NRL] = {v};")
+    o.append("      }")
+    o.append("      __syncthreads();")
+    o.append("    }")
+    o.append("    const double* r = rec + bslot * Q + qi;")
+    for fi, nm in enumerate(fields):
+        if nm.startswith("F") or fi < 6 or nm.startswith("AB"):
+            continue
+        o.append(f"    const double {nm} = r[{fi} * NRL];")
+    o.append(f"    double F[{L + 1}];")
+    for m in range(L + 1):
+        o.append(f"    F[{m}] = r[{fields.index('F0') + m} * NRL];")
+    o.append("    (void)CDx; (void)CDy; (void)CDz;")
+    o.append("    const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
+    o.append("    (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
+    o.append("    (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+    _stage1(ci, kv.base_m, o, "    ", rsel="r")
+    for li, k in enumerate(levels):
+        buf = (li % 2) * NC * NT
+        o.append(f"    // ket level {k}: publish level {k - 1} values read across lanes")
+        for j, key in enumerate(lv[k]):
+            o.append(f"    xu[{buf + j * NT} + tid] = {names.ket(key)};")
+        o.append("    __syncthreads();")
+        reads = {}
+        for n in kv.nodes:
+            if sum(n.f) != k:
+                continue
+            rk = (lv[k].index(n.a1), n.axis)
+            if rk not in reads:
+                reads[rk] = f"xr{k}_{len(reads)}"
+                o.append(f"    const double {reads[rk]} = xu[{buf + rk[0] * NT} + src{AX[n.axis]}];")
+        if li == len(levels) - 1:
+            o.append("    __syncthreads();  // every level buffer read: the exchange may overwrite them")
+        for n in kv.nodes:
+            if sum(n.f) != k:
+                continue
+            a_ = AX[n.axis]
+            expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+            if n.b0 is not None:
+                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
+            o.append(f"    const double {names.ket((n.f, n.m))} = {expr};")
+    # ket HRR and transform per lane, straight into the exchange row of this lane's e
+    _emit_hrr_scheduled(ci.lc, ci.ld, lambda f: names.ket((f, 0)), "CD", spherical,
+                        lambda kk, x: f"xd[{kk}] = {x};", o, "    ", "y")
+    o.append("    __syncthreads();")
+    # bra HRR and transform: lanes own (quartet, ket component)
+    ab0 = fields.index("ABx")
+    ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
+    epos = {e: i for i, e in enumerate(ebra)}
+    o.append("    for (int t = tid; t < Q * NK; t += NT) {")
+    o.append("      const int q2 = t / NK, kap = t - q2 * NK;")
+    o.append("      const int slot = g * Q + q2;")
+    o.append("      if (slot >= a.nq) continue;")
+    o.append("      const double* r2 = rec + bslot * Q + q2;")
+    o.append(f"      const double ABx = r2[{ab0} * NRL], ABy = r2[{ab0 + 1} * NRL], ABz = r2[{ab0 + 2} * NRL];")
+    o.append("      (void)ABx; (void)ABy; (void)ABz;")
+    o.append("      const double* src = xu + q2 * NEB * NK + kap;")
+    o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
+    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                        lambda kk, x: f"eri_out(&dst[{kk} * NK], {x});", o, "      ", "z")
+    o.append("    }")
+    o.append("    __syncthreads();  // exchange and records are rewritten next")
+    o.append("  }")
+    o.append("}")
+    o.append("")
+    o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
+    o.append("{")
+    o.append(f"  const int ngroups = (a.nq + {Q} - 1) / {Q};")
+    o.append(f"  const int cap = (a.grid_cap / 8) * {wg_per_cu};  // grid_cap is 8 per compute unit")
+    o.append("  const int nblk = ngroups < cap ? ngroups : cap;")
+    o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3({NT}), 0, s, a);")
+    o.append("}")
+    o.append("")
+    return o

@@ -156,6 +156,26 @@ def test_tier_routing():
     assert tier_of(gg.ClassInfo(4, 4, 4, 4)) == "M"
 
 
+def test_packed_k1_routing_and_shapes():
+    """Classes whose bra spans 35 lanes run the uncontracted kernel with several
+    quartets per workgroup; the lane layout, record batch and LDS plan fit."""
+    from electron_repulsion_integrals_amd.gen import packed as P
+    from electron_repulsion_integrals_amd.gen.emit import emit_register_tier
+    used = []
+    for c in gg.all_classes(4):
+        for sph in (False, True):
+            if not P.use_packed_k1(c, sph):
+                continue
+            used.append((c.la, c.lb, c.lc, c.ld))
+            W, Q, NT = P.packed_shape(c, sph)
+            assert c.G == 35 and Q * c.G <= NT and P.PACK_RB * Q <= NT
+            assert P.packed_lds_bytes(c, sph) * P.packed_wg_per_cu(c, sph) <= P.LDS_BYTES
+            src = emit_register_tier(c, sph)
+            assert f"__launch_bounds__({NT})" in src and "xu[" in src
+    assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used
+    assert all(sum(u[:2]) == 4 and sum(u[2:]) <= 4 for u in used)
+
+
 def test_two_phase_fp64_floor_bounds_the_emulated_algorithm():
     """On diffuse (gg|gg) and (ff|ff) quartets ~7 bohr apart the fp64 two-phase
     evaluation loses up to 1e-5 of the block maximum; the oracle's first-order

@@ -375,6 +375,20 @@ def test_all_120_classes_explicit(eri):
         assert_parity(got, oracle_flat(sh, imap, spherical), f"all classes sph={spherical}", sh, imap[:, :4], spherical)
 
 
+def test_all_120_classes_uncontracted(eri):
+    """Every class with uncontracted shells only, so that every block runs the
+    K4 = 1 kernels (among them the packed multi-quartet workgroups of the
+    classes whose bra spans 35 lanes); block sizes are ragged against the
+    quartets per workgroup."""
+    _log("case: explicit uncontracted batch over all 120 classes")
+    sh, q = _mixed_batch(27, 60, 2500, 4, 1)
+    for spherical in (True, False):
+        plan, got, imap = run_plan(eri, sh, 1 if spherical else 0, q)
+        assert len(set(plan.block_class)) == 120
+        assert_parity(got, oracle_flat(sh, imap, spherical), f"uncontracted classes sph={spherical}", sh,
+                      imap[:, :4], spherical)
+
+
 def test_c4_reduced_full_compare(eri):
     _log("case: (ff|ff) x 64 + (gg|gg) x 16, K=2, spherical, full compare")
     w = make_config(4, scale={"nquartets_f": 64, "nquartets_g": 16})

@@ -157,6 +157,12 @@ __device__ __forceinline__ void eri_boys(double T, double pref, const double* __
 // (non-temporal) stores keep them from displacing inputs in the caches.
 __device__ __forceinline__ void eri_out(double* p, double v) { __builtin_nontemporal_store(v, p); }
 
+// Plain (cached) output store.  Where several waves write interleaved parts of
+// one block (the multi-quartet workgroups), streaming stores leave partial
+// lines that reach HBM more than once (measured: 1.33x the output bytes);
+// through the cache the partial lines merge first.
+__device__ __forceinline__ void eri_out_merged(double* p, double v) { *p = v; }
+
 // A value that every lane of the wave holds identically (one quartet per
 // wave): reading it from the first lane lets the compiler keep it in scalar
 // registers and use it as a scalar operand, freeing two VGPRs per value.

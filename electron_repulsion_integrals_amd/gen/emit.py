@@ -375,8 +375,11 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
            f"{'spherical' if spherical else 'Cartesian'} output, register tier: {ci.G} lanes per quartet, "
            f"{64 // ci.G} quartets per wave",
            '#include "eri_device.h"', ""]
-    out += _register_kernel(ci, spherical, k1=False)
-    from .packed import use_packed_k1, emit_packed_k1
+    from .packed import use_packed_k1, emit_packed_k1, use_packed_contracted, emit_packed_contracted
+    if use_packed_contracted(ci, spherical):
+        out += emit_packed_contracted(ci, spherical)
+    else:
+        out += _register_kernel(ci, spherical, k1=False)
     batched = BATCH_K1 and ci.G >= K1_BATCH_MIN_G
     if use_packed_k1(ci, spherical):
         out += emit_packed_k1(ci, spherical)
@@ -428,8 +431,11 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append(f"__global__ void __launch_bounds__(64) eri_kernel_{tag}(EriClassArgs a)")
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NK = {NK}, NEB = {NEB}, BLK = {BLK}, RB = {RB}, NRL = {NRL};")
+    # field stride of the records: odd, so that lanes reading different fields of
+    # one record (the bra-path selectors) hit different LDS banks
+    o.append(f"  constexpr int RS = {NRL | 1};")
     o.append("  __shared__ double xch[Q * NEB * NK + NK];  // exchange rows, then a junk row")
-    o.append(f"  __shared__ double rec[{NR} * NRL];  // field-major quartet records of one batch")
+    o.append(f"  __shared__ double rec[{NR} * RS];  // field-major quartet records of one batch")
     o.append("  const int lane = threadIdx.x;")
     o.append("  int grp = lane / G, sub = lane - grp * G;")
     o.append("  if (grp >= Q) { grp = Q; sub = 0; }  // padding lanes: phantom group, e = (0,0,0)")
@@ -442,8 +448,8 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append("  const int rq = grp < Q ? grp : 0;  // record member of this lane's group")
-    o.append(f"  if (lane < NRL) {{ rec[{NR - 2} * NRL + lane] = 1.0; rec[{NR - 1} * NRL + lane] = 0.0; }}")
-    _stage1_selectors(ci, o, "NRL", NR - 2, NR - 1)
+    o.append(f"  if (lane < NRL) {{ rec[{NR - 2} * RS + lane] = 1.0; rec[{NR - 1} * RS + lane] = 0.0; }}")
+    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)
     o.append("  int it = 0;")
     o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
     o.append("    const int bslot = it % RB;")
@@ -470,7 +476,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     assert len(vals) == NR - 2
     o.append("        double* r = rec + lane;")
     for fi, v in enumerate(vals):
-        o.append(f"        r[{fi} * NRL] = {v};")
+        o.append(f"        r[{fi} * RS] = {v};")
     o.append("      }")
     o.append("      __syncthreads();")
     o.append("    }")
@@ -479,10 +485,10 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     for fi, nm in enumerate(fields):
         if nm.startswith("F") or fi < 6:  # P-A and W-P are read by the bra path through its selectors
             continue
-        o.append(f"      const double {nm} = r[{fi} * NRL];")
+        o.append(f"      const double {nm} = r[{fi} * RS];")
     o.append(f"      double F[{L + 1}];")
     for m in range(L + 1):
-        o.append(f"      F[{m}] = r[{len(REC_FIELDS) + m} * NRL];")
+        o.append(f"      F[{m}] = r[{len(REC_FIELDS) + m} * RS];")
     o.append("      (void)CDx; (void)CDy; (void)CDz; (void)ABx; (void)ABy; (void)ABz;")
     o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
     o.append("      (void)QCx; (void)QCy; (void)QCz;")
@@ -500,7 +506,7 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append("      if (slot >= a.nq) continue;")
     ab0 = fields.index("ABx")
     o.append(f"      const double* r = rec + bslot * Q + g2;")
-    o.append(f"      const double ABx = r[{ab0} * NRL], ABy = r[{ab0 + 1} * NRL], ABz = r[{ab0 + 2} * NRL];")
+    o.append(f"      const double ABx = r[{ab0} * RS], ABy = r[{ab0 + 1} * RS], ABz = r[{ab0 + 2} * RS];")
     o.append("      (void)ABx; (void)ABy; (void)ABz;")
     o.append("      const double* src = xch + g2 * NEB * NK + kap;")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
@@ -740,7 +746,10 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append("  __shared__ double xab[Q * 3];")
     if use_rec:
         o.append(f"  constexpr int NREC = {NREC};")
-        o.append("  __shared__ double rec[NREC * 64];  // field-major primitive-quartet records")
+        # odd field stride: lanes reading different fields of one record (the
+        # bra-path selectors) hit different LDS banks
+        o.append("  constexpr int RS = 65;")
+        o.append("  __shared__ double rec[NREC * RS];  // field-major primitive-quartet records")
     o.append("  const int lane = threadIdx.x;")
     o.append("  int grp = lane / G, sub = lane - grp * G;")
     o.append("  if (grp >= Q) { grp = Q; sub = 0; }  // padding lanes: phantom group, e = (0,0,0)")
@@ -752,9 +761,9 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     o.append("  const int adz = (ez > 0 ? gb + ((lt >> 24) & 63) - 1 : lane) * 4;")
     o.append("  (void)adx; (void)ady; (void)adz; (void)es;")
     if sel_lds:
-        o.append(f"  rec[{NREC - 2} * 64 + lane] = 1.0;")
-        o.append(f"  rec[{NREC - 1} * 64 + lane] = 0.0;")
-        _stage1_selectors(ci, o, "64", NREC - 2, NREC - 1)
+        o.append(f"  rec[{NREC - 2} * RS + lane] = 1.0;")
+        o.append(f"  rec[{NREC - 1} * RS + lane] = 0.0;")
+        _stage1_selectors(ci, o, "RS", NREC - 2, NREC - 1)
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append("  int g = blockIdx.x;")
     o.append("  if (g >= ngroups) return;")
@@ -854,9 +863,9 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
                 "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
         o.append("        double* r = rec + lane;")
         for fi, v in enumerate(vals):
-            o.append(f"        r[{fi} * 64] = {v};")
+            o.append(f"        r[{fi} * RS] = {v};")
         for m in range(L + 1):
-            o.append(f"        r[{len(vals) + m} * 64] = F[{m}];")
+            o.append(f"        r[{len(vals) + m} * RS] = F[{m}];")
         o.append("      }")
         o.append("      __syncthreads();")
         o.append("      const int n = K4 - c0 < G ? K4 - c0 : G;")
@@ -864,10 +873,10 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
         o.append("        const double* r = rec + gb + j;")
         for fi, nm in enumerate(REC_FIELDS):
             if fi >= 6 or not sel_lds:  # P-A and W-P: read by the bra path through its selectors
-                o.append(f"        const double {nm} = r[{fi} * 64];")
+                o.append(f"        const double {nm} = r[{fi} * RS];")
         o.append(f"        double F[{L + 1}];")
         for m in range(L + 1):
-            o.append(f"        F[{m}] = r[{len(REC_FIELDS) + m} * 64];")
+            o.append(f"        F[{m}] = r[{len(REC_FIELDS) + m} * RS];")
         o += body("        ", True, rsel="r" if sel_lds else None)
         o.append("      }")
         o.append("      __syncthreads();  // records are rewritten by the next chunk")

@@ -60,7 +60,7 @@ def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb
     NC = max((len(v) for v in lv.values()), default=0)
     NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
     NR = 17 + ci.L + 1 + 6 + 2
-    return 8 * (max(2 * NC * NT, NX) + NR * rb * Q)
+    return 8 * (max(2 * NC * NT, NX) + NR * ((rb * Q) | 1))
 
 
 def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
@@ -125,9 +125,11 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NT = {NT}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append(f"  constexpr int RB = {RB}, NRL = {NRL}, NC = {max(NC, 1)};")
+    # odd field stride: lanes reading different fields of one record hit different banks
+    o.append(f"  constexpr int RS = {NRL | 1};")
     o.append(f"  // level buffers (two, alternating) during the recurrence; exchange afterwards")
     o.append(f"  __shared__ double xu[{NU}];")
-    o.append(f"  __shared__ double rec[{NR} * NRL];  // field-major quartet records of one batch")
+    o.append(f"  __shared__ double rec[{NR} * RS];  // field-major quartet records of one batch")
     o.append("  const int tid = threadIdx.x;")
     o.append("  int qi = tid / G, sub = tid - qi * G;")
     o.append("  const bool real = qi < Q;")
@@ -140,8 +142,8 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     o.append("  const int srcz = ez > 0 ? qb + ((lt >> 24) & 63) - 1 : tid;")
     o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
-    o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * NRL + tid] = 1.0; rec[{NR - 1} * NRL + tid] = 0.0; }}")
-    _stage1_selectors(ci, o, "NRL", NR - 2, NR - 1)
+    o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
+    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)
     o.append(f"  double* xd = xu + ((real && es >= {ci.la}) ? (qi * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
     o.append("  int it = 0;")
     o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
@@ -169,7 +171,7 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     assert len(vals) == NR - 2
     o.append("        double* r = rec + tid;")
     for fi, v in enumerate(vals):
-        o.append(f"        r[{fi} * NRL] = {v};")
+        o.append(f"        r[{fi} * RS] = {v};")
     o.append("      }")
     o.append("      __syncthreads();")
     o.append("    }")
@@ -177,10 +179,10 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     for fi, nm in enumerate(fields):
         if nm.startswith("F") or fi < 6 or nm.startswith("AB"):
             continue
-        o.append(f"    const double {nm} = r[{fi} * NRL];")
+        o.append(f"    const double {nm} = r[{fi} * RS];")
     o.append(f"    double F[{L + 1}];")
     for m in range(L + 1):
-        o.append(f"    F[{m}] = r[{fields.index('F0') + m} * NRL];")
+        o.append(f"    F[{m}] = r[{fields.index('F0') + m} * RS];")
     o.append("    (void)CDx; (void)CDy; (void)CDz;")
     o.append("    const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
     o.append("    (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
@@ -224,12 +226,12 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     o.append("      const int slot = g * Q + q2;")
     o.append("      if (slot >= a.nq) continue;")
     o.append("      const double* r2 = rec + bslot * Q + q2;")
-    o.append(f"      const double ABx = r2[{ab0} * NRL], ABy = r2[{ab0 + 1} * NRL], ABz = r2[{ab0 + 2} * NRL];")
+    o.append(f"      const double ABx = r2[{ab0} * RS], ABy = r2[{ab0 + 1} * RS], ABz = r2[{ab0 + 2} * RS];")
     o.append("      (void)ABx; (void)ABy; (void)ABz;")
     o.append("      const double* src = xu + q2 * NEB * NK + kap;")
     o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
     _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                        lambda kk, x: f"eri_out(&dst[{kk} * NK], {x});", o, "      ", "z")
+                        lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "      ", "z")
     o.append("    }")
     o.append("    __syncthreads();  // exchange and records are rewritten next")
     o.append("  }")
@@ -241,6 +243,219 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     o.append(f"  const int cap = (a.grid_cap / 8) * {wg_per_cu};  // grid_cap is 8 per compute unit")
     o.append("  const int nblk = ngroups < cap ? ngroups : cap;")
     o.append(f"  if (nblk > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(nblk), dim3({NT}), 0, s, a);")
+    o.append("}")
+    o.append("")
+    return o
+
+
+PACK_CH = 21  # primitive quartets per quartet set up together (one lane each)
+
+
+def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH) -> int:
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    W, Q, NT = packed_shape(ci, spherical, waves)
+    NC = max((len(v) for v in _levels(kv).values()), default=0)
+    NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
+    NR = 17 + ci.L + 1 + 2
+    return 8 * (max(2 * NC * NT, NX) + NR * ((ch * Q) | 1)) + 4 * Q
+
+
+def packed_contracted_wg_per_cu(ci: ClassInfo, spherical: bool) -> int:
+    return int(min(LDS_BYTES // packed_contracted_lds_bytes(ci, spherical), 8 // PACK_WAVES))
+
+
+def use_packed_contracted(ci: ClassInfo, spherical: bool) -> bool:
+    return use_packed_k1(ci, spherical) and packed_contracted_wg_per_cu(ci, spherical) >= 2
+
+
+def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH):
+    """General (contracted) kernel, Q quartets per workgroup of `waves` waves.
+
+    Algorithm 2 of "FusionRCG": the primitive quartets of each quartet are set
+    up in chunks (one lane per primitive quartet: geometry and Boys values into
+    an LDS record), then every lane runs the bra path and the level-by-level
+    ket recurrence for each primitive quartet of the chunk and adds its targets
+    [e0|f0] into accumulators; the horizontal recurrences and transforms run
+    once per quartet on the contracted values.  Quartets of one workgroup may
+    differ in contraction length: the loop runs to the longest, and lanes of a
+    shorter quartet evaluate its last primitive quartet again with weight 0."""
+    from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
+    kv = build_ket_vrr(ci.lc, ci.Lk)
+    names = Names("V", kv, ci.Lk)
+    G = ci.G
+    W, Q, NT = packed_shape(ci, spherical, waves)
+    wg_per_cu = packed_contracted_wg_per_cu(ci, spherical)
+    NK = ci.nket(spherical)
+    NEB = ci.n_ebra
+    EOFF = ci.e_bra_offset
+    BLK = ci.nout(spherical)
+    L = ci.L
+    cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
+    tag = f"c{cid}_{'s' if spherical else 'c'}"
+    lanes = ci.lanes
+    lpos = {e: i for i, e in enumerate(lanes)}
+    lane_tab = []
+    for e in lanes:
+        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
+        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
+    lv = _levels(kv)
+    levels = sorted(lv)
+    NC = max((len(v) for v in lv.values()), default=0)
+    fields = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
+              "i2z", "i2e", "roz", "roe", "i2ze"] + [f"F{m}" for m in range(L + 1)]
+    NR = len(fields) + 2  # then two constant rows, 1.0 and 0.0, for the bra-path selectors
+    CH = ch
+    NRL = Q * CH
+    assert NRL <= NT
+    NX = Q * NEB * NK + NK
+    NU = max(2 * NC * NT, NX)
+    targets = kv.targets
+    tpos = {f: t for t, (f, m) in enumerate(targets)}
+    o = []
+    o.append("namespace {")
+    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
+    o.append("}  // namespace")
+    o.append(f"// {Q} quartets per workgroup of {NT} lanes ({Q * G} busy); ket coupling through LDS, level by level")
+    o.append(f"__global__ void __launch_bounds__({NT}) eri_kernel_{tag}(EriClassArgs a)")
+    o.append("{")
+    o.append(f"  constexpr int G = {G}, Q = {Q}, NT = {NT}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
+    o.append(f"  constexpr int CH = {CH}, NRL = {NRL}, NC = {max(NC, 1)};")
+    o.append(f"  constexpr int RS = {NRL | 1};  // odd field stride: selector reads of one record hit different banks")
+    o.append(f"  __shared__ double xu[{NU}];  // level buffers (two, alternating), then the exchange")
+    o.append(f"  __shared__ double rec[{NR} * RS];  // field-major primitive-quartet records of one chunk")
+    o.append("  __shared__ int k4q[Q];")
+    o.append("  const int tid = threadIdx.x;")
+    o.append("  int qi = tid / G, sub = tid - qi * G;")
+    o.append("  const bool real = qi < Q;")
+    o.append("  if (!real) { qi = 0; sub = 0; }  // spare lanes shadow e = (0,0,0) of the first quartet")
+    o.append(f"  const int lt = k_{tag}_lane[sub];")
+    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
+    o.append("  const int qb = qi * G;")
+    o.append("  const int srcx = ex > 0 ? qb + ((lt >> 12) & 63) - 1 : tid;")
+    o.append("  const int srcy = ey > 0 ? qb + ((lt >> 18) & 63) - 1 : tid;")
+    o.append("  const int srcz = ez > 0 ? qb + ((lt >> 24) & 63) - 1 : tid;")
+    o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
+    o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
+    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)
+    o.append("  const int g = blockIdx.x;")
+    o.append("  const int q0 = g * Q;")
+    o.append("  // this lane's quartet (the spare lanes and a short last group repeat a valid one)")
+    o.append("  const int qme = q0 + qi < a.nq ? q0 + qi : a.nq - 1;")
+    o.append("  const int4 pbm = a.pair_info[a.qbra[qme]], pkm = a.pair_info[a.qket[qme]];")
+    o.append("  const int K4 = pbm.w * pkm.w;")
+    o.append("  if (real && sub == 0) k4q[qi] = K4;")
+    o.append("  // the quartet whose primitive quartets this lane sets up")
+    o.append("  const int qsi = tid / CH < Q ? tid / CH : Q - 1;")
+    o.append("  const int qs = q0 + qsi < a.nq ? q0 + qsi : a.nq - 1;")
+    o.append("  const int4 pbs = a.pair_info[a.qbra[qs]], pks = a.pair_info[a.qket[qs]];")
+    o.append("  const double ACx = a.cen[3 * pbs.x] - a.cen[3 * pks.x], ACy = a.cen[3 * pbs.x + 1] - a.cen[3 * pks.x + 1],"
+             " ACz = a.cen[3 * pbs.x + 2] - a.cen[3 * pks.x + 2];")
+    o.append("  const int K4s = pbs.w * pks.w;")
+    o.append("  __syncthreads();")
+    o.append("  int K4max = k4q[0];")
+    o.append("  for (int i = 1; i < Q; ++i) K4max = k4q[i] > K4max ? k4q[i] : K4max;")
+    for t in range(len(targets)):
+        o.append(f"  double acc{t} = 0.0;")
+    o.append("  int lvl = 0;  // running ket-level count: parity selects the level buffer")
+    o.append("  for (int c0 = 0; c0 < K4max; c0 += CH) {")
+    o.append("    if (c0 > 0) __syncthreads();  // the previous chunk's records are consumed")
+    o.append("    if (tid < NRL) {")
+    o.append("      const int p = c0 + (tid - qsi * CH);")
+    o.append("      const int t = p < K4s ? p : K4s - 1;")
+    o.append("      const int ib = t / pks.w, ik = t - ib * pks.w;")
+    o.append("      const EriPrimPair P = eri_load_pp(a.ppd, pbs.z + ib);")
+    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pks.z + ik);")
+    o.append("      EriQuartetGeom gq;")
+    o.append("      eri_geom(P, K, ACx, ACy, ACz, gq);")
+    o.append(f"      double F[{L + 1}];")
+    o.append(f"      eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
+    vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
+            "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
+    vals += [f"F[{m}]" for m in range(L + 1)]
+    assert len(vals) == NR - 2
+    o.append("      double* r = rec + tid;")
+    for fi, v in enumerate(vals):
+        o.append(f"      r[{fi} * RS] = {v};")
+    o.append("    }")
+    o.append("    __syncthreads();")
+    o.append("    const int n = K4max - c0 < CH ? K4max - c0 : CH;")
+    o.append("    for (int j = 0; j < n; ++j) {")
+    o.append("      const double* r = rec + qi * CH + j;")
+    o.append("      const double wgt = c0 + j < K4 ? 1.0 : 0.0;  // quartets shorter than the longest")
+    for fi, nm in enumerate(fields):
+        if nm.startswith("F") or fi < 6:
+            continue
+        o.append(f"      const double {nm} = r[{fi} * RS];")
+    o.append(f"      double F[{L + 1}];")
+    for m in range(L + 1):
+        o.append(f"      F[{m}] = r[{fields.index('F0') + m} * RS];")
+    o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
+    o.append("      (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
+    o.append("      (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+    _stage1(ci, kv.base_m, o, "      ", rsel="r")
+    for t, tg in enumerate(targets):
+        if sum(tg[0]) == 0:
+            o.append(f"      acc{t} += wgt * s1_{tg[1]};")
+    for li, k in enumerate(levels):
+        o.append(f"      // ket level {k}: publish level {k - 1} values read across lanes")
+        o.append(f"      {{ double* xb = xu + (lvl & 1) * (NC * NT) + tid;")
+        for j, key in enumerate(lv[k]):
+            o.append(f"        xb[{j * NT}] = {names.ket(key)};")
+        o.append("      }")
+        o.append("      __syncthreads();")
+        o.append(f"      const double* xrb{k} = xu + (lvl & 1) * (NC * NT);")
+        o.append("      ++lvl;")
+        reads = {}
+        for n in kv.nodes:
+            if sum(n.f) != k:
+                continue
+            rk = (lv[k].index(n.a1), n.axis)
+            if rk not in reads:
+                reads[rk] = f"xr{k}_{len(reads)}"
+                o.append(f"      const double {reads[rk]} = xrb{k}[{rk[0] * NT} + src{AX[n.axis]}];")
+        for n in kv.nodes:
+            if sum(n.f) != k:
+                continue
+            a_ = AX[n.axis]
+            expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+            if n.b0 is not None:
+                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
+            o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
+            if n.m == 0 and n.f in tpos:
+                o.append(f"      acc{tpos[n.f]} += wgt * {names.ket((n.f, n.m))};")
+    o.append("    }")
+    o.append("  }")
+    o.append("  __syncthreads();  // level buffers and records read: the exchange may overwrite them")
+    # ket HRR and transform per lane on the contracted values, into the exchange
+    o.append("  const double CDx = a.cen[3 * pkm.x] - a.cen[3 * pkm.y], CDy = a.cen[3 * pkm.x + 1] - a.cen[3 * pkm.y + 1],"
+             " CDz = a.cen[3 * pkm.x + 2] - a.cen[3 * pkm.y + 2];")
+    o.append("  (void)CDx; (void)CDy; (void)CDz;")
+    o.append(f"  double* xd = xu + ((real && es >= {ci.la}) ? (qi * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
+    _emit_hrr_scheduled(ci.lc, ci.ld, lambda f: f"acc{tpos[f]}", "CD", spherical,
+                        lambda kk, x: f"xd[{kk}] = {x};", o, "  ", "y")
+    o.append("  __syncthreads();")
+    ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
+    epos = {e: i for i, e in enumerate(ebra)}
+    o.append("  for (int t = tid; t < Q * NK; t += NT) {")
+    o.append("    const int q2 = t / NK, kap = t - q2 * NK;")
+    o.append("    const int slot = q0 + q2;")
+    o.append("    if (slot >= a.nq) continue;")
+    o.append("    const int4 pb2 = a.pair_info[a.qbra[slot]];")
+    o.append("    const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
+             " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
+    o.append("    (void)ABx; (void)ABy; (void)ABz;")
+    o.append("    const double* src = xu + q2 * NEB * NK + kap;")
+    o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
+    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                        lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "    ", "z")
+    o.append("  }")
+    o.append("}")
+    o.append("")
+    o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")
+    o.append("{")
+    o.append(f"  const int ngroups = (a.nq + {Q} - 1) / {Q};  // one group per workgroup")
+    o.append(f"  if (ngroups > 0) hipLaunchKernelGGL(eri_kernel_{tag}, dim3(ngroups), dim3({NT}), 0, s, a);")
     o.append("}")
     o.append("")
     return o

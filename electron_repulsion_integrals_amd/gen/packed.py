@@ -251,9 +251,14 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
 PACK_CH = 21  # primitive quartets per quartet set up together (one lane each)
 
 
+def _chunk(Q, NT, ch=PACK_CH):
+    return max(1, min(ch, NT // Q))
+
+
 def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH) -> int:
     kv = build_ket_vrr(ci.lc, ci.Lk)
     W, Q, NT = packed_shape(ci, spherical, waves)
+    ch = _chunk(Q, NT, ch)
     NC = max((len(v) for v in _levels(kv).values()), default=0)
     NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
     NR = 17 + ci.L + 1 + 2
@@ -265,7 +270,14 @@ def packed_contracted_wg_per_cu(ci: ClassInfo, spherical: bool) -> int:
 
 
 def use_packed_contracted(ci: ClassInfo, spherical: bool) -> bool:
-    return use_packed_k1(ci, spherical) and packed_contracted_wg_per_cu(ci, spherical) >= 2
+    """Measured on the 30-atom cluster: packing pays for 35-lane bras always,
+    and for 20- and 10-lane bras once there is a ket recurrence whose
+    coupling reads move from ds_bpermute to the level buffers."""
+    if ci.Lk > 4:
+        return False
+    if not (ci.G == 35 or (ci.G in (20, 10) and ci.Lk >= 1)):
+        return False
+    return packed_contracted_wg_per_cu(ci, spherical) >= 2
 
 
 def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH):
@@ -304,7 +316,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     fields = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
               "i2z", "i2e", "roz", "roe", "i2ze"] + [f"F{m}" for m in range(L + 1)]
     NR = len(fields) + 2  # then two constant rows, 1.0 and 0.0, for the bra-path selectors
-    CH = ch
+    CH = _chunk(Q, NT, ch)
     NRL = Q * CH
     assert NRL <= NT
     NX = Q * NEB * NK + NK

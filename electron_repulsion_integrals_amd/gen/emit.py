@@ -302,13 +302,28 @@ def _hrr_ops(l1, l2, R, spherical):
         outs = [key[(x, y)] for x in xs for y in ys]
     else:
         Ty, Tx = transform_terms(l2), transform_terms(l1)
+        # a Cartesian component x that only one spherical row of the first index
+        # uses, with a single coefficient c: c is folded into the second index's
+        # coefficients of the values t(x, .), and that row is t itself
+        uses = {}
+        for li, row in enumerate(Tx):
+            for xi, c in row:
+                uses.setdefault(xi, []).append(li)
+        fold = {}
+        for li, row in enumerate(Tx):
+            if len(row) == 1 and len(uses[row[0][0]]) == 1:
+                fold[row[0][0]] = row[0][1]
         for xi, x in enumerate(xs):
+            f = fold.get(xi, 1.0)
             for si, row in enumerate(Ty):
-                ops.append((("t", xi, si), [(_fmt(c), key[(x, ys[yi])]) for yi, c in row]))
+                ops.append((("t", xi, si), [(_fmt(f * c), key[(x, ys[yi])]) for yi, c in row]))
         for li, row in enumerate(Tx):
             for si in range(nsph(l2)):
                 k = ("u", li, si)
-                ops.append((k, [(_fmt(c), ("t", xi, si)) for xi, c in row]))
+                if len(row) == 1 and row[0][0] in fold:
+                    ops.append((k, [(None, ("t", row[0][0], si))]))
+                else:
+                    ops.append((k, [(_fmt(c), ("t", xi, si)) for xi, c in row]))
                 outs.append(k)
     return ops, base, outs
 
@@ -371,11 +386,19 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
     next group's indices, pair records and centres while the current group
     computes, so the dependent load chain of a quartet is hidden.
     """
+    from .lane import use_lane_tier
+    lane_tier = USE_LANE_TIER and use_lane_tier(ci, spherical)
+    layout = ("lane tier: one quartet per lane" if lane_tier else
+              f"register tier: {ci.G} lanes per quartet, {64 // ci.G} quartets per wave")
     out = [f"// class ({ci.la}{ci.lb}|{ci.lc}{ci.ld}) id {class_id(ci.la, ci.lb, ci.lc, ci.ld)}, "
-           f"{'spherical' if spherical else 'Cartesian'} output, register tier: {ci.G} lanes per quartet, "
-           f"{64 // ci.G} quartets per wave",
+           f"{'spherical' if spherical else 'Cartesian'} output, {layout}",
            '#include "eri_device.h"', ""]
     from .packed import use_packed_k1, emit_packed_k1, use_packed_contracted, emit_packed_contracted
+    from .lane import emit_lane_tier
+    if lane_tier:
+        out += emit_lane_tier(ci, spherical, False)
+        out += emit_lane_tier(ci, spherical, True)
+        return "\n".join(out) + "\n"
     if use_packed_contracted(ci, spherical):
         out += emit_packed_contracted(ci, spherical)
     else:
@@ -391,6 +414,7 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
 
 
 BATCH_K1 = True
+USE_LANE_TIER = True
 SELECT_LDS_CONTRACTED = True
 K1_BATCH = 32  # quartet records set up together, one per lane
 K1_BATCH_MIN_G = 8  # narrower lane groups repeat the set-up in few lanes: per-group set-up

@@ -171,9 +171,123 @@ def test_packed_k1_routing_and_shapes():
             assert c.G == 35 and Q * c.G <= NT and P.PACK_RB * Q <= NT
             assert P.packed_lds_bytes(c, sph) * P.packed_wg_per_cu(c, sph) <= P.LDS_BYTES
             src = emit_register_tier(c, sph)
-            assert f"__launch_bounds__({NT})" in src and "xu[" in src
+            if "lane tier" not in src.splitlines()[0]:
+                assert f"__launch_bounds__({NT})" in src and "xu[" in src
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used
     assert all(sum(u[:2]) == 4 and sum(u[2:]) <= 4 for u in used)
+
+
+def _apply_ops(ops, base_val, R):
+    """Evaluate the generator's linear HRR/transform ops (emit._hrr_ops)."""
+    val = dict(base_val)
+    for key, terms in ops:
+        tot = 0.0
+        for c, src in terms:
+            if c is None:
+                w = 1.0
+            elif c[:2] in ("AB", "CD"):
+                w = R["xyz".index(c[2])]
+            else:
+                w = float(c)
+            tot = tot + w * val[src]
+        val[key] = tot
+    return val
+
+
+def emulate_lane_tier(ci, cen, exps, coefs, spherical):
+    """The lane tier's graph (gen.lane.lane_vrr) and the generator's horizontal
+    ops evaluated in numpy for one quartet, in the order the kernel uses."""
+    from electron_repulsion_integrals_amd.gen import lane as LN
+    from electron_repulsion_integrals_amd.gen.emit import _hrr_ops
+    A, B, C, D = [np.asarray(x, dtype=float) for x in cen]
+    ls = (ci.la, ci.lb, ci.lc, ci.ld)
+    cn = [_norm(l, e, c) for l, e, c in zip(ls, exps, coefs)]
+    nodes, targets, ebra, kv = LN.lane_vrr(ci)
+    order = sorted((k for k, v in nodes.items() if v[0] != "F"), key=lambda k: (sum(k[0]) + sum(k[1]), -k[2]))
+    acc = {t: 0.0 for t in targets}
+    for ia, al in enumerate(exps[0]):
+        for ib, be in enumerate(exps[1]):
+            z = al + be
+            P = (al * A + be * B) / z
+            Kab = cn[0][ia] * cn[1][ib] * math.exp(-al * be / z * np.sum((A - B) ** 2)) / z
+            for ic, ga in enumerate(exps[2]):
+                for id_, de in enumerate(exps[3]):
+                    e_ = ga + de
+                    Q = (ga * C + de * D) / e_
+                    Kcd = cn[2][ic] * cn[3][id_] * math.exp(-ga * de / e_ * np.sum((C - D) ** 2)) / e_
+                    ize = 1 / (z + e_)
+                    W = (z * P + e_ * Q) * ize
+                    PA, WP, QC, WQ = P - A, W - P, Q - C, W - Q
+                    T = z * e_ * ize * np.sum((P - Q) ** 2)
+                    F = 2 * math.pi ** 2.5 * Kab * Kcd * math.sqrt(ize) * _boys(ci.L, T)
+                    i2z, roz, i2e, roe, i2ze = 0.5 / z, e_ * ize, 0.5 / e_, z * ize, 0.5 * ize
+                    V = {k: F[k[2]] for k, v in nodes.items() if v[0] == "F"}
+                    for k in order:
+                        kind, ax, dl, n = nodes[k]
+                        e = k[0]
+                        if kind == "b":
+                            v = PA[ax] * V[dl[0]] + WP[ax] * V[dl[1]]
+                            if len(dl) == 4:
+                                v += (e[ax] - 1) * i2z * (V[dl[2]] - roz * V[dl[3]])
+                        else:
+                            v = QC[ax] * V[dl[0]] + WQ[ax] * V[dl[1]]
+                            if n.b0 is not None:
+                                v += n.fi_minus_1 * i2e * (V[dl[2]] - roe * V[dl[3]])
+                            if e[ax] > 0:
+                                v += e[ax] * i2ze * V[dl[-1]]
+                        V[k] = v
+                    for (e, f) in targets:
+                        acc[(e, f)] += V[(e, f, 0)]
+    kops, kbase, kouts = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
+    bops, bbase, bouts = _hrr_ops(ci.la, ci.lb, "AB", spherical)
+    Y = {}
+    for e in ebra:
+        val = _apply_ops(kops, {("b", f): acc[(e, f)] for f in kbase}, C - D)
+        for ki, ko in enumerate(kouts):
+            Y[(e, ki)] = val[ko]
+    out = np.zeros((len(bouts), len(kouts)))
+    for ki in range(len(kouts)):
+        val = _apply_ops(bops, {("b", e): Y[(e, ki)] for e in bbase}, A - B)
+        for bi, bo in enumerate(bouts):
+            out[bi, ki] = val[bo]
+    f = gc.nsph if spherical else gc.ncart
+    return out.reshape(f(ci.la), f(ci.lb), f(ci.lc), f(ci.ld))
+
+
+@pytest.mark.parametrize("ls", [(1, 1, 1, 0), (2, 0, 2, 0), (2, 1, 1, 0), (3, 2, 0, 0), (4, 2, 0, 0)])
+@pytest.mark.parametrize("spherical", [False, True])
+def test_lane_tier_graph_matches_oracle(ls, spherical):
+    """The one-quartet-per-lane graph and its horizontal ops reproduce the oracle."""
+    from electron_repulsion_integrals_amd.gen import lane as LN
+    ci = gg.ClassInfo(*ls)
+    assert LN.use_lane_tier(ci, spherical)
+    rng = np.random.default_rng(sum(ls) * 7 + spherical)
+    cen = [rng.uniform(0, 4, 3) for _ in range(4)]
+    K = [2, 1, 2, 2]
+    exps = [list(np.exp(rng.uniform(np.log(0.2), np.log(8.0), k))) for k in K]
+    coefs = [list(rng.uniform(0.2, 1.0, k)) for k in K]
+    got = emulate_lane_tier(ci, cen, exps, coefs, spherical)
+    sh = _pack(cen, list(ls), K, [np.array(e) for e in exps], [np.array(c) for c in coefs])
+    ref = oracle.eri_block(sh, [0, 1, 2, 3], spherical)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-13 * max(1.0, np.abs(ref).max()))
+
+
+def test_lane_tier_graph_is_the_counted_graph():
+    """Per primitive quartet the lane tier evaluates exactly the recurrence nodes
+    that the FLOP count of the roofline reports (graph.dag_flops)."""
+    from electron_repulsion_integrals_amd.gen import lane as LN
+    for ls in [(1, 1, 1, 0), (2, 1, 1, 0), (2, 0, 2, 0), (4, 2, 0, 0)]:
+        ci = gg.ClassInfo(*ls)
+        nodes, targets, ebra, kv = LN.lane_vrr(ci)
+        flops = 0
+        for (e, f, m), (kind, ax, dl, n) in nodes.items():
+            if kind == "b":
+                flops += 3 + (4 if len(dl) == 4 else 0)
+            elif kind == "k":
+                flops += 3 + (4 if n.b0 is not None else 0) + (2 if e[ax] > 0 else 0)
+        per_prim, _ = gg.dag_flops(ci, True)
+        other = 30 + 14 + 3 * ci.L + (ci.L + 1) + ci.n_ebra * len(kv.targets)
+        assert flops == per_prim - other, ls
 
 
 def test_two_phase_fp64_floor_bounds_the_emulated_algorithm():

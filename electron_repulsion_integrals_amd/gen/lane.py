@@ -23,7 +23,9 @@ from .cartesian import components, sub
 from .graph import ClassInfo, build_ket_vrr, build_hrr, class_id, schedule_min_live, peak_live
 
 AX = "xyz"
-MAX_ACC = 64       # accumulators per lane
+# accumulators per lane: up to 100 the kernel may drop to one wave per SIMD
+# (VGPRs + AGPRs) and is still faster than the lane-group tiers (measured)
+MAX_ACC = 100
 MAX_LIVE = 96      # scheduled peak of recurrence values (doubles) besides the accumulators
 
 
@@ -130,11 +132,10 @@ def emit_lane_tier(ci: ClassInfo, spherical: bool, k1: bool):
         o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z);")
         o.append("    const EriPrimPair K = eri_load_pp(a.ppd, pk.z);")
     else:
-        o.append("  const int K4 = pb.w * pk.w;")
-        o.append("  for (int t = 0, ib = 0, ik = 0; t < K4; ++t) {")
-        o.append("    const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
+        o.append("  for (int ib = 0; ib < pb.w; ++ib) {")
+        o.append("  const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
+        o.append("  for (int ik = 0; ik < pk.w; ++ik) {")
         o.append("    const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
-        o.append("    if (++ik == pk.w) { ik = 0; ++ib; }")
     o.append("    EriQuartetGeom g;")
     o.append("    eri_geom(P, K, ACx, ACy, ACz, g);")
     o.append(f"    double F[{L + 1}];")
@@ -168,6 +169,8 @@ def emit_lane_tier(ci: ClassInfo, spherical: bool, k1: bool):
                 expr += f" + {_fmt(e[ax])} * i2ze * {name[dl[-1]]}"
         o.append(f"    const double {name[k]} = {expr};")
     o.append("  }")
+    if not k1:
+        o.append("  }")
     # horizontal recurrences and transforms, ket then bra (Eq. (14): either order), all in this lane
     kops, kbase, kouts = _hrr_ops(ci.lc, ci.ld, "CD", spherical)
     bops, bbase, bouts = _hrr_ops(ci.la, ci.lb, "AB", spherical)

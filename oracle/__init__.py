@@ -66,6 +66,9 @@ def lib():
         L.oracle_eri_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
                                           ctypes.c_int64, ip, lp, dp]
         L.oracle_eri_quartets.restype = ctypes.c_int
+        L.oracle_eri_deriv_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
+                                                ctypes.c_int64, ip, lp, dp]
+        L.oracle_eri_deriv_quartets.restype = ctypes.c_int
         L.oracle_schwarz.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, dp]
         L.oracle_schwarz.restype = ctypes.c_int
         L.oracle_J_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
@@ -184,6 +187,38 @@ def eri(sh, quartets, spherical: bool, normalize_: bool = True):
     if rc != 0:
         raise ValueError("oracle_eri_quartets rejected its input")
     return o, of
+
+
+def eri_deriv(sh, quartets, spherical: bool, normalize_: bool = True):
+    """First derivatives of each quartet's block with respect to the centres of
+    its four shells (in the order given): 12 blocks per quartet, in the order
+    d/dA_x, d/dA_y, d/dA_z, d/dB_x, ..., d/dD_z, each row-major over (a, b, c, d).
+
+    Returns (flat values, offsets[nq]); quartet q's 12 blocks start at off[q].
+    Differentiating a Cartesian Gaussian with respect to its own centre raises
+    and lowers its angular momentum: d/dA_i phi_a = 2 alpha phi_(a+1_i) - a_i phi_(a-1_i).
+    """
+    q, pq = _i(np.asarray(quartets).reshape(-1, 4))
+    sizes = 12 * block_sizes(sh, q, spherical)
+    off = np.zeros(len(sizes), dtype=np.int64)
+    if len(sizes) > 1:
+        off[1:] = np.cumsum(sizes)[:-1]
+    out = np.zeros(int(sizes.sum()) if len(sizes) else 0)
+    o, po = _d(out)
+    of, pof = _l(off)
+    keep, args = _shell_args(sh)
+    flags = (SPHERICAL if spherical else 0) | (0 if normalize_ else NO_NORMALIZE)
+    rc = lib().oracle_eri_deriv_quartets(*args, flags, len(q), pq, pof, po)
+    if rc != 0:
+        raise ValueError("oracle_eri_deriv_quartets rejected its input")
+    return o, of
+
+
+def eri_deriv_block(sh, quartet, spherical: bool, normalize_: bool = True) -> np.ndarray:
+    """One quartet's derivatives as an array [4 centres, 3 axes, a, b, c, d]."""
+    flat, _ = eri_deriv(sh, [quartet], spherical, normalize_)
+    dims = [nfunc(int(sh.l[s]), spherical) for s in quartet]
+    return flat.reshape([4, 3] + dims)
 
 
 def eri_block(sh, quartet, spherical: bool, normalize_: bool = True) -> np.ndarray:

@@ -261,15 +261,26 @@ static inline size_t vidx(const os_work *w, int ia, int ib, int ic, int id, int 
     return ((((size_t)ia * w->tb.n + ib) * w->tc.n + ic) * w->td.n + id) * M1 + m;
 }
 
+/* dout == NULL: the integrals of the block into out.  dout != NULL: instead
+ * the first derivatives with respect to the 12 centre coordinates (A_x A_y
+ * A_z B_x ... D_z), block after block into dout.  Differentiating a primitive
+ * Cartesian Gaussian with respect to its own centre gives
+ *   d/dA_i [x_A^a_x y_A^a_y z_A^a_z exp(-alpha r_A^2)]
+ *     = 2 alpha (component a+1_i) - a_i (component a-1_i),
+ * so the table is filled one unit higher on every index and each derivative
+ * element is that combination of primitive integrals, contracted like the
+ * integrals themselves (the normalisation belongs to the undifferentiated
+ * shell). */
 static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4[4],
-                       const double *al[4], const double *cc[4], double *out)
+                       const double *al[4], const double *cc[4], double *out, double *dout)
 {
     int la = l4[0], lb = l4[1], lc = l4[2], ld = l4[3];
-    int Lt = la + lb + lc + ld, M1 = Lt + 1;
-    tripset_init(&w->ta, la);
-    tripset_init(&w->tb, lb);
-    tripset_init(&w->tc, lc);
-    tripset_init(&w->td, ld);
+    const int ext = dout ? 1 : 0;
+    int Lt = la + lb + lc + ld + 4 * ext, M1 = Lt + 1;
+    tripset_init(&w->ta, la + ext);
+    tripset_init(&w->tb, lb + ext);
+    tripset_init(&w->tc, lc + ext);
+    tripset_init(&w->td, ld + ext);
     size_t need = (size_t)w->ta.n * w->tb.n * w->tc.n * w->td.n * M1;
     if (need > w->cap) {
         free(w->V);
@@ -284,7 +295,10 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
     cart_list(ld, cd);
     int na = ncart(la), nb = ncart(lb), nc = ncart(lc), nd = ncart(ld);
     size_t nout = (size_t)na * nb * nc * nd;
-    for (size_t q = 0; q < nout; ++q) out[q] = 0.0;
+    if (dout)
+        for (size_t q = 0; q < 12 * nout; ++q) dout[q] = 0.0;
+    else
+        for (size_t q = 0; q < nout; ++q) out[q] = 0.0;
     const double *A = cen[0], *B = cen[1], *C = cen[2], *D = cen[3];
     double AB2 = 0, CD2 = 0;
     for (int i = 0; i < 3; ++i) {
@@ -392,12 +406,35 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                     /* contract the m = 0 entries with the exact target totals */
                     double cw = cc[0][pa] * cc[1][pb] * cc[2][pc] * cc[3][pd];
                     size_t o = 0;
+                    if (!dout) {
+                        for (int qa = 0; qa < na; ++qa)
+                            for (int qb = 0; qb < nb; ++qb)
+                                for (int qc = 0; qc < nc; ++qc)
+                                    for (int qd = 0; qd < nd; ++qd, ++o) {
+                                        size_t k = vidx(w, IDX_A(ca[qa]), IDX_B(cb[qb]), IDX_C(ccc[qc]), IDX_D(cd[qd]), 0, M1);
+                                        out[o] += cw * V[k];
+                                    }
+                        continue;
+                    }
+                    const double ex4[4] = {a, b, c, d};
                     for (int qa = 0; qa < na; ++qa)
                         for (int qb = 0; qb < nb; ++qb)
                             for (int qc = 0; qc < nc; ++qc)
                                 for (int qd = 0; qd < nd; ++qd, ++o) {
-                                    size_t k = vidx(w, IDX_A(ca[qa]), IDX_B(cb[qb]), IDX_C(ccc[qc]), IDX_D(cd[qd]), 0, M1);
-                                    out[o] += cw * V[k];
+                                    for (int p = 0; p < 4; ++p)
+                                        for (int i = 0; i < 3; ++i) {
+                                            int t4[4][3] = {{ca[qa][0], ca[qa][1], ca[qa][2]}, {cb[qb][0], cb[qb][1], cb[qb][2]},
+                                                            {ccc[qc][0], ccc[qc][1], ccc[qc][2]}, {cd[qd][0], cd[qd][1], cd[qd][2]}};
+                                            int n = t4[p][i];
+                                            t4[p][i] += 1;
+                                            double up = V[vidx(w, IDX_A(t4[0]), IDX_B(t4[1]), IDX_C(t4[2]), IDX_D(t4[3]), 0, M1)];
+                                            double dn = 0.0;
+                                            if (n > 0) {
+                                                t4[p][i] -= 2;
+                                                dn = V[vidx(w, IDX_A(t4[0]), IDX_B(t4[1]), IDX_C(t4[2]), IDX_D(t4[3]), 0, M1)];
+                                            }
+                                            dout[(size_t)(3 * p + i) * nout + o] += cw * ((ORACLE_MUTANT == 9 ? 1.0 : 2.0) * ex4[p] * up - n * dn);
+                                        }
                                 }
                 }
 }
@@ -479,9 +516,9 @@ int oracle_eri_quartets(int nshell, const double *centers, const int32_t *l, con
                 bcap = ncar;
             }
             if (!(flags & OR_SPHERICAL)) {
-                os_quartet(w, l4, cen, K4, al, cc, out + out_off[q]);
+                os_quartet(w, l4, cen, K4, al, cc, out + out_off[q], NULL);
             } else {
-                os_quartet(w, l4, cen, K4, al, cc, buf1);
+                os_quartet(w, l4, cen, K4, al, cc, buf1, NULL);
                 int n[4] = {ncart(l4[0]), ncart(l4[1]), ncart(l4[2]), ncart(l4[3])};
                 double *src = buf1, *dst = buf2;
                 for (int pos = 0; pos < 4; ++pos) {
@@ -496,6 +533,93 @@ int oracle_eri_quartets(int nshell, const double *centers, const int32_t *l, con
         }
         free(buf1);
         free(buf2);
+        free(w->V);
+        free(w);
+    }
+    free(cn);
+    return bad ? -1 : 0;
+}
+
+/* First derivatives of each quartet's block with respect to the 12 centre
+ * coordinates of its four shells in the order given (A_x A_y A_z B_x ...
+ * D_z): out + out_off[q] holds 12 blocks of the quartet's block size, one
+ * after another, each row-major over (a, b, c, d), Cartesian or spherical
+ * (the transform applied to all four indices of each Cartesian block). */
+int oracle_eri_deriv_quartets(int nshell, const double *centers, const int32_t *l, const int32_t *nprim,
+                              const int32_t *prim_off, const double *exps, const double *coefs, int flags,
+                              int64_t nq, const int32_t *quartets, const int64_t *out_off, double *out)
+{
+    for (int s = 0; s < nshell; ++s)
+        if (l[s] < 0 || l[s] + 1 > OR_LMAX || nprim[s] < 1) return -1;
+    int ntot = prim_off[nshell];
+    double *cn = (double *)malloc(sizeof(double) * (ntot > 0 ? ntot : 1));
+    for (int s = 0; s < nshell; ++s) {
+        if (flags & OR_NO_NORMALIZE)
+            memcpy(cn + prim_off[s], coefs + prim_off[s], sizeof(double) * nprim[s]);
+        else
+            oracle_normalize(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
+    }
+    double Tsph[OR_LMAX + 1][17 * 45];
+    for (int L = 0; L <= OR_LMAX; ++L) oracle_sph_coeffs(L, Tsph[L]);
+    int bad = 0;
+#pragma omp parallel
+    {
+        os_work *w = (os_work *)calloc(1, sizeof(os_work));
+        double *buf1 = NULL, *buf2 = NULL, *dbuf = NULL;
+        size_t bcap = 0;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t q = 0; q < nq; ++q) {
+            int sh[4], l4[4], K4[4];
+            const double *cen[4], *al[4], *cc[4];
+            int ok = 1;
+            for (int t = 0; t < 4; ++t) {
+                sh[t] = quartets[4 * q + t];
+                if (sh[t] < 0 || sh[t] >= nshell) ok = 0;
+            }
+            if (!ok) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            for (int t = 0; t < 4; ++t) {
+                l4[t] = l[sh[t]];
+                K4[t] = nprim[sh[t]];
+                cen[t] = centers + 3 * sh[t];
+                al[t] = exps + prim_off[sh[t]];
+                cc[t] = cn + prim_off[sh[t]];
+            }
+            size_t ncar = (size_t)ncart(l4[0]) * ncart(l4[1]) * ncart(l4[2]) * ncart(l4[3]);
+            if (ncar > bcap) {
+                free(buf1);
+                free(buf2);
+                free(dbuf);
+                buf1 = (double *)malloc(ncar * sizeof(double));
+                buf2 = (double *)malloc(ncar * sizeof(double));
+                dbuf = (double *)malloc(12 * ncar * sizeof(double));
+                bcap = ncar;
+            }
+            os_quartet(w, l4, cen, K4, al, cc, NULL, dbuf);
+            if (!(flags & OR_SPHERICAL)) {
+                memcpy(out + out_off[q], dbuf, 12 * ncar * sizeof(double));
+                continue;
+            }
+            size_t nsp = (size_t)nsph(l4[0]) * nsph(l4[1]) * nsph(l4[2]) * nsph(l4[3]);
+            for (int k = 0; k < 12; ++k) {
+                int n[4] = {ncart(l4[0]), ncart(l4[1]), ncart(l4[2]), ncart(l4[3])};
+                memcpy(buf1, dbuf + (size_t)k * ncar, ncar * sizeof(double));
+                double *src = buf1, *dst = buf2;
+                for (int pos = 0; pos < 4; ++pos) {
+                    transform_index(src, dst, n, pos, Tsph[l4[pos]], nsph(l4[pos]));
+                    double *t = src;
+                    src = dst;
+                    dst = t;
+                }
+                memcpy(out + out_off[q] + (size_t)k * nsp, src, nsp * sizeof(double));
+            }
+        }
+        free(buf1);
+        free(buf2);
+        free(dbuf);
         free(w->V);
         free(w);
     }

@@ -24,6 +24,7 @@ MUTANTS = {
     6: "uses (4 alpha)^((l+1)/2) instead of (4 alpha)^(l/2) in the primitive normalisation",
     7: "uses P-A instead of P-B when raising b",
     8: "forgets the factor 2 for off-diagonal density pairs in J",
+    9: "drops the factor 2 of 2 alpha in the centre derivative",
 }
 
 

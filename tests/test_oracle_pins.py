@@ -189,6 +189,61 @@ def test_finite_difference_centres(ls, pos):
 
 
 # --------------------------------------------------------------------------
+# First derivatives with respect to the centres (oracle.eri_deriv)
+# --------------------------------------------------------------------------
+
+def _shifted(sh, pos, axis, h):
+    c = np.array(sh.centers, dtype=float).copy()
+    c[pos, axis] += h
+    return shells_from([(c[t], int(sh.l[t]), list(sh.exps[sh.prim_off[t]:sh.prim_off[t + 1]]),
+                         list(sh.coefs[sh.prim_off[t]:sh.prim_off[t + 1]])) for t in range(4)])
+
+
+@pytest.mark.parametrize("ls,spherical", [((0, 0, 0, 0), False), ((1, 0, 0, 0), False), ((1, 1, 1, 0), False),
+                                          ((2, 1, 0, 1), True), ((2, 2, 1, 1), False), ((3, 1, 2, 0), True),
+                                          ((3, 3, 2, 2), False)])
+def test_derivative_finite_differences(ls, spherical):
+    """Each of the 12 derivative blocks against a fourth-order central
+    difference of the integrals, moving one centre along one axis (contracted,
+    normalised shells on four distinct centres)."""
+    sh = _random_shells(ls, seed=41 + sum(ls) + 7 * spherical)
+    d = oracle.eri_deriv_block(sh, [0, 1, 2, 3], spherical)
+    h = 1e-3
+    scale = max(1e-3, float(np.abs(d).max()))
+    for pos in range(4):
+        for axis in range(3):
+            f = [oracle.eri_block(_shifted(sh, pos, axis, s * h), [0, 1, 2, 3], spherical) for s in (2, 1, -1, -2)]
+            num = (-f[0] + 8 * f[1] - 8 * f[2] + f[3]) / (12 * h)
+            np.testing.assert_allclose(d[pos, axis], num, rtol=0, atol=1e-8 * scale)
+
+
+@pytest.mark.parametrize("ls", [(1, 0, 0, 0), (2, 1, 1, 0), (3, 2, 2, 1), (2, 2, 2, 2)])
+def test_derivative_translational_invariance(ls):
+    """Moving all four centres together leaves every integral unchanged, so the
+    four centre derivatives along each axis sum to zero."""
+    sh = _random_shells(ls, seed=13 + sum(ls))
+    d = oracle.eri_deriv_block(sh, [0, 1, 2, 3], False)
+    total = d.sum(axis=0)
+    assert np.abs(total).max() <= 1e-12 * np.abs(d).max()
+
+
+@pytest.mark.parametrize("aA,aB,R", [(1.0, 1.0, 0.5), (0.3, 7.0, 2.0), (5.0, 0.05, 6.0)])
+def test_derivative_two_centre_closed_form(aA, aB, R):
+    """(s_A s_A|s_B s_B) = erf(sqrt(rho) R)/R with rho = p q/(p+q), p = 2 aA,
+    q = 2 aB (the two-centre pin above); B lies at +R along z, so the A
+    derivatives along z sum to -d/dR and the B derivatives to +d/dR of it, and
+    the x, y derivatives vanish."""
+    sh = shells_from([([0, 0, 0], 0, [aA]), ([0, 0, 0], 0, [aA]), ([0, 0, R], 0, [aB]), ([0, 0, R], 0, [aB])])
+    d = oracle.eri_deriv_block(sh, [0, 1, 2, 3], False)[..., 0, 0, 0, 0]
+    p, q = 2 * aA, 2 * aB
+    rho = p * q / (p + q)
+    dfdR = 2 * math.sqrt(rho / math.pi) * math.exp(-rho * R * R) / R - math.erf(math.sqrt(rho) * R) / R ** 2
+    assert d[0, 2] + d[1, 2] == pytest.approx(-dfdR, rel=1e-12)
+    assert d[2, 2] + d[3, 2] == pytest.approx(dfdR, rel=1e-12)
+    assert np.abs(d[:, :2]).max() <= 1e-15
+
+
+# --------------------------------------------------------------------------
 # Symmetries and invariances
 # --------------------------------------------------------------------------
 

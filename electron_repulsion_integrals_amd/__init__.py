@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     build_quartets,
     class_info,
     compute_batch,
+    compute_deriv,
     compute_range,
     digest_J,
     digest_JK,

@@ -73,6 +73,8 @@ def load():
     L.eri_digest_J.restype = ctypes.c_int
     L.eri_digest_JK.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
     L.eri_digest_JK.restype = ctypes.c_int
+    L.eri_compute_deriv.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64, vp]
+    L.eri_compute_deriv.restype = ctypes.c_int
     L.eri_strerror.argtypes = [ctypes.c_int]
     L.eri_strerror.restype = ctypes.c_char_p
     L.eri_class_info.argtypes = [ctypes.c_int32, i32p, i32p]
@@ -194,6 +196,16 @@ def compute_batch(plan: Plan, out, block_begin: int = 0, block_end: int | None =
 def compute_range(plan: Plan, block: int, first: int, count: int, out, stream=None):
     """Integrals of quartets [first, first + count) of one class block into ``out``."""
     _check(load().eri_compute_range(plan.handle, int(block), int(first), int(count), _ptr(out), out.numel(),
+                                    _stream_handle(stream)))
+    return out
+
+
+def compute_deriv(plan: Plan, out, first: int = 0, count: int | None = None, stream=None):
+    """First derivatives (12 blocks per slot: d/dA_x .. d/dD_z) of plan slots
+    [first, first + count) into the float64 device tensor ``out``."""
+    if count is None:
+        count = plan.n_quartets - first
+    _check(load().eri_compute_deriv(plan.handle, int(first), int(count), _ptr(out), out.numel(),
                                     _stream_handle(stream)))
     return out
 

@@ -36,9 +36,10 @@ def _compile(src: str, use_cache: bool) -> tuple[str, float, str]:
     with open(src, "rb") as f:
         h = hashlib.sha1(f.read() + " ".join(CFLAGS).encode())
     # headers affect every object
-    for hdr in ("eri_device.h",):
-        with open(os.path.join(CSRC, hdr), "rb") as f:
-            h.update(f.read())
+    for hdr in ("eri_device.h", os.path.join("generated", "eri_sph_table.h")):
+        if os.path.exists(os.path.join(CSRC, hdr)):
+            with open(os.path.join(CSRC, hdr), "rb") as f:
+                h.update(f.read())
     with open(os.path.join(ROOT, "include", "eri.h"), "rb") as f:
         h.update(f.read())
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + "." + h.hexdigest()[:16] + ".o")

@@ -20,6 +20,7 @@
 
 #include "eri_device.h"
 #include "eri.h"
+#include "generated/eri_sph_table.h"
 
 namespace {
 
@@ -712,6 +713,7 @@ struct eri_plan {
     int *d_l = nullptr, *d_nprim = nullptr, *d_off = nullptr, *d_bf = nullptr, *d_nfun = nullptr;
     int4 *d_pinfo = nullptr;
     int *d_qbra = nullptr, *d_qket = nullptr, *d_qmap = nullptr;
+    int64_t *d_qsrc = nullptr;  // explicit plans: input position of the quartet in each slot
     double *d_boys = nullptr;
     double *d_scratch = nullptr;
     int scratch_wgs = 0;
@@ -1029,6 +1031,7 @@ void build_explicit(eri_plan *P, const std::vector<int> &hl, const int32_t *quar
     P->d_pinfo = P->alloc<int4>(2 * nq);
     hipLaunchKernelGGL(k_explicit_fill, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, p1, d_q, P->d_l, P->d_nprim,
                        P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
+    P->d_qsrc = p1;
     HIP_CHECK(hipGetLastError());
     const int NC = 120;
     int64_t *d_st = P->alloc<int64_t>(NC + 1), *d_k1 = P->alloc<int64_t>(NC + 1);
@@ -1465,6 +1468,285 @@ extern "C" int eri_plan_quartets(const eri_plan *P, int64_t first, int64_t count
         return translate(f);
     }
     return ERI_OK;
+}
+
+// ---------------------------------------------------------------------------
+// First derivatives with respect to the centres
+// ---------------------------------------------------------------------------
+// d/dA_i of a primitive Cartesian Gaussian centred at A raises and lowers its
+// angular momentum: 2 alpha phi_(a+1_i) - a_i phi_(a-1_i).  Contracted, the
+// derivative block of (ab|cd) with respect to A_i is therefore
+//   (a+1_i b|cd) over the shell a' (l+1, coefficients 2 alpha c)
+//   - a_i (a-1_i b|cd) over the shell a'' (l-1, coefficients c),
+// with c the normalised coefficients of a, both on raw monomials.  The class
+// kernels compute those neighbouring integrals on an auxiliary shell set
+// (three copies of every shell: itself, raised, lowered); the kernels below
+// pick the two terms of every derivative element out of the auxiliary blocks
+// (whose quartets the plan may have reordered: the permutation bits say how)
+// and, for spherical plans, apply t^(l) to the four indices of each block.
+namespace {
+
+__device__ inline int dv_ncart(int l) { return (l + 1) * (l + 2) / 2; }
+__device__ inline int dv_nsph(int l) { return 2 * l + 1; }
+// index of the Cartesian component (x, y, l-x-y) of a shell l: x descending, then y descending
+__device__ inline int dv_cidx(int l, int x, int y)
+{
+    const int r = l - x;
+    return r * (r + 1) / 2 + (r - y);
+}
+__device__ inline void dv_ctrip(int l, int i, int *t)
+{
+    int r = 0;
+    while ((r + 1) * (r + 2) / 2 <= i) ++r;
+    t[0] = l - r;
+    t[1] = r - (i - r * (r + 1) / 2);
+    t[2] = l - t[0] - t[1];
+}
+
+__global__ void k_invert_src(int64_t n, const int64_t *src, int64_t *slot_of)
+{
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x < n) slot_of[src[x]] = x;
+}
+
+// output offset of every slot from the block table (blocks ordered by first slot)
+__global__ void k_slot_offsets(int64_t n, int nb, const int64_t *bstart, const int64_t *bout, const int64_t *bsize,
+                               int64_t *off)
+{
+    const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= n) return;
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (bstart[mid] <= x) lo = mid;
+        else hi = mid - 1;
+    }
+    off[x] = bout[lo] + (x - bstart[lo]) * bsize[lo];
+}
+
+// one workgroup per quartet: its 12 Cartesian derivative blocks into dst + dst_off[t]
+__global__ void k_deriv_combine(int64_t n, const int *rows, const int *lsh, const int64_t *aux_slot_of,
+                                const int *aux_qmap, const int *aux_l, const int64_t *aux_off, const double *aux,
+                                const int64_t *dst_off, double *dst)
+{
+    const int64_t t = blockIdx.x;
+    if (t >= n) return;
+    int l4[4], n4[4];
+    for (int k = 0; k < 4; ++k) {
+        l4[k] = lsh[rows[5 * t + k]];
+        n4[k] = dv_ncart(l4[k]);
+    }
+    const int ncar = n4[0] * n4[1] * n4[2] * n4[3];
+    for (int idx = threadIdx.x; idx < 12 * ncar; idx += blockDim.x) {
+        const int comp = idx / ncar, e = idx - comp * ncar;
+        const int p = comp / 3, ax = comp - 3 * p;
+        int ci[4], r = e;
+        ci[3] = r % n4[3];
+        r /= n4[3];
+        ci[2] = r % n4[2];
+        r /= n4[2];
+        ci[1] = r % n4[1];
+        ci[0] = r / n4[1];
+        int tr[3];
+        dv_ctrip(l4[p], ci[p], tr);
+        double v = 0.0;
+        for (int sg = 0; sg < 2; ++sg) {
+            const int nax = tr[ax];
+            if (sg == 1 && nax == 0) continue;
+            const int dl = sg == 0 ? 1 : -1;
+            int t2[3] = {tr[0], tr[1], tr[2]};
+            t2[ax] += dl;
+            int j[4] = {ci[0], ci[1], ci[2], ci[3]};
+            j[p] = dv_cidx(l4[p] + dl, t2[0], t2[1]);
+            const int64_t s = aux_slot_of[(t * 4 + p) * 2 + sg];
+            const int perm = aux_qmap[5 * s + 4];
+            int x;
+            if (perm & 1) { x = j[0]; j[0] = j[1]; j[1] = x; }
+            if (perm & 2) { x = j[2]; j[2] = j[3]; j[3] = x; }
+            if (perm & 4) {
+                x = j[0]; j[0] = j[2]; j[2] = x;
+                x = j[1]; j[1] = j[3]; j[3] = x;
+            }
+            int m4[4];
+            for (int k = 0; k < 4; ++k) m4[k] = dv_ncart(aux_l[aux_qmap[5 * s + k]]);
+            const int64_t flat = ((int64_t)(j[0] * m4[1] + j[1]) * m4[2] + j[2]) * m4[3] + j[3];
+            const double a = aux[aux_off[s] + flat];
+            v += sg == 0 ? a : -(double)nax * a;
+        }
+        dst[dst_off[t] + idx] = v;
+    }
+}
+
+// one workgroup per (quartet, derivative component): t^(l) on the four indices,
+// ping-pong between the Cartesian block and a scratch block, last pass into dst
+__global__ void k_deriv_sph(int64_t n, const int *rows, const int *lsh, double *cart, double *tmp,
+                            const int64_t *cart_off, const int64_t *dst_off, double *dst)
+{
+    const int64_t t = blockIdx.x / 12;
+    const int comp = blockIdx.x - (int)(t * 12);
+    if (t >= n) return;
+    int l4[4], dims[4], ns[4];
+    for (int k = 0; k < 4; ++k) {
+        l4[k] = lsh[rows[5 * t + k]];
+        dims[k] = dv_ncart(l4[k]);
+        ns[k] = dv_nsph(l4[k]);
+    }
+    const int ncar = dims[0] * dims[1] * dims[2] * dims[3];
+    const int nsp = ns[0] * ns[1] * ns[2] * ns[3];
+    double *a = cart + cart_off[t] + (int64_t)comp * ncar;
+    double *b = tmp + cart_off[t] + (int64_t)comp * ncar;
+    for (int pos = 0; pos < 4; ++pos) {
+        int before = 1, after = 1;
+        for (int k = 0; k < pos; ++k) before *= dims[k];
+        for (int k = pos + 1; k < 4; ++k) after *= dims[k];
+        const double *T = eri_sph_T[l4[pos]];
+        const int nc = dims[pos], nsv = ns[pos];
+        const double *in = (pos % 2 == 0) ? a : b;
+        double *o = pos == 3 ? dst + dst_off[t] + (int64_t)comp * nsp : ((pos % 2 == 0) ? b : a);
+        const int total = before * nsv * after;
+        for (int x = threadIdx.x; x < total; x += blockDim.x) {
+            const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
+            double acc = 0.0;
+            for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
+            o[x] = acc;
+        }
+        dims[pos] = nsv;
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count, double *out, int64_t cap,
+                                 void *stream)
+{
+    if (!P || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
+    if (count == 0) return ERI_OK;
+    if (!out || count > ((int64_t)1 << 24)) return ERI_E_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    eri_plan *A = nullptr;
+    std::vector<void *> tmp;
+    auto dalloc = [&](size_t bytes) -> void * {
+        void *p = nullptr;
+        HIP_CHECK(hipMalloc(&p, bytes ? bytes : 8));
+        tmp.push_back(p);
+        return p;
+    };
+    int rc = ERI_OK;
+    try {
+        const int ns = P->nshell;
+        std::vector<int> hl(ns), hk(ns), hoff(ns + 1);
+        HIP_CHECK(hipMemcpyAsync(hl.data(), P->d_l, sizeof(int) * ns, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(hk.data(), P->d_nprim, sizeof(int) * ns, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(hoff.data(), P->d_off, sizeof(int) * (ns + 1), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+        const int npr = hoff[ns];
+        std::vector<double> hcen(3 * (size_t)ns), hexp(npr), hcn(npr);
+        HIP_CHECK(hipMemcpyAsync(hcen.data(), P->d_cen, sizeof(double) * 3 * ns, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(hexp.data(), P->d_exps, sizeof(double) * npr, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(hcn.data(), P->d_cn, sizeof(double) * npr, hipMemcpyDeviceToHost, s));
+        int *d_rows = (int *)dalloc(sizeof(int) * 5 * (size_t)count);
+        if ((rc = eri_plan_quartets(P, first, count, d_rows, stream)) != ERI_OK) throw rc;
+        std::vector<int> rows(5 * (size_t)count);
+        HIP_CHECK(hipMemcpyAsync(rows.data(), d_rows, sizeof(int) * 5 * count, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+        for (int64_t t = 0; t < count; ++t)
+            for (int k = 0; k < 4; ++k)
+                if (hl[rows[5 * t + k]] + 1 > ERI_MAX_L) throw (int)ERI_E_UNSUPPORTED;
+        // where every slot's 12 blocks go, and the capacity that needs
+        const bool sph = P->sph;
+        std::vector<int64_t> dst_off(count), cart_off(count);
+        int64_t dtot = 0, ctot = 0;
+        for (int64_t t = 0; t < count; ++t) {
+            const int *r = &rows[5 * t];
+            int64_t nf = 1, nc = 1;
+            for (int k = 0; k < 4; ++k) {
+                nf *= nfun(hl[r[k]], sph);
+                nc *= ncart(hl[r[k]]);
+            }
+            dst_off[t] = dtot;
+            cart_off[t] = ctot;
+            dtot += 12 * nf;
+            ctot += 12 * nc;
+        }
+        if (cap < dtot) throw (int)ERI_E_CAPACITY;
+        // auxiliary shells: [0, ns) the shells, [ns, 2ns) raised, [2ns, 3ns) lowered
+        std::vector<int32_t> al(3 * ns), ak(3 * ns), aoff(3 * ns + 1);
+        std::vector<double> acen(9 * (size_t)ns), aexp(3 * (size_t)npr), acf(3 * (size_t)npr);
+        aoff[0] = 0;
+        for (int part = 0; part < 3; ++part)
+            for (int x = 0; x < ns; ++x) {
+                const int y = part * ns + x;
+                al[y] = part == 0 ? hl[x] : part == 1 ? hl[x] + 1 : std::max(hl[x] - 1, 0);
+                ak[y] = hk[x];
+                aoff[y + 1] = aoff[y] + hk[x];
+                for (int c = 0; c < 3; ++c) acen[3 * y + c] = hcen[3 * x + c];
+                for (int q = 0; q < hk[x]; ++q) {
+                    const double a = hexp[hoff[x] + q], c = hcn[hoff[x] + q];
+                    aexp[aoff[y] + q] = a;
+                    acf[aoff[y] + q] = part == 0 ? c : part == 1 ? 2.0 * a * c : (hl[x] > 0 ? c : 0.0);
+                }
+            }
+        eri_shells ash{3 * ns, acen.data(), al.data(), ak.data(), aoff.data(), aexp.data(), acf.data()};
+        std::vector<int32_t> aq(32 * (size_t)count);
+        for (int64_t t = 0; t < count; ++t)
+            for (int p = 0; p < 4; ++p)
+                for (int sg = 0; sg < 2; ++sg) {
+                    int32_t *q = &aq[4 * ((t * 4 + p) * 2 + sg)];
+                    for (int k = 0; k < 4; ++k) q[k] = rows[5 * t + k];
+                    q[p] += (sg == 0 ? 1 : 2) * ns;
+                }
+        if ((rc = eri_build_quartets(&ash, ERI_NO_NORMALIZE, aq.data(), 8 * count, 0.0, stream, &A)) != ERI_OK) throw rc;
+        double *d_aux = (double *)dalloc(sizeof(double) * (size_t)A->nout);
+        if ((rc = eri_compute_batch(A, 0, (int32_t)A->blocks.size(), d_aux, A->nout, stream)) != ERI_OK) throw rc;
+        const int64_t na = 8 * count;
+        int64_t *d_slot_of = (int64_t *)dalloc(sizeof(int64_t) * na);
+        hipLaunchKernelGGL(k_invert_src, dim3(nblk(na, 256)), dim3(256), 0, s, na, A->d_qsrc, d_slot_of);
+        HIP_CHECK(hipGetLastError());
+        const int nb = (int)A->blocks.size();
+        std::vector<int64_t> bst(nb), bout(nb), bsz(nb);
+        for (int b = 0; b < nb; ++b) {
+            const EriBlock &B = A->blocks[b];
+            bst[b] = B.start;
+            bout[b] = B.out_off;
+            bsz[b] = (int64_t)B.na * B.nb * B.nc * B.nd;
+        }
+        int64_t *d_bt = (int64_t *)dalloc(sizeof(int64_t) * 3 * nb);
+        upload(d_bt, bst.data(), nb, s);
+        upload(d_bt + nb, bout.data(), nb, s);
+        upload(d_bt + 2 * nb, bsz.data(), nb, s);
+        int64_t *d_aux_off = (int64_t *)dalloc(sizeof(int64_t) * na);
+        hipLaunchKernelGGL(k_slot_offsets, dim3(nblk(na, 256)), dim3(256), 0, s, na, nb, d_bt, d_bt + nb, d_bt + 2 * nb,
+                           d_aux_off);
+        HIP_CHECK(hipGetLastError());
+        int64_t *d_off = (int64_t *)dalloc(sizeof(int64_t) * 2 * count);
+        upload(d_off, dst_off.data(), count, s);
+        upload(d_off + count, cart_off.data(), count, s);
+        if (!sph) {
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, d_rows, P->d_l, d_slot_of,
+                               A->d_qmap, A->d_l, d_aux_off, d_aux, d_off, out);
+        } else {
+            double *d_cart = (double *)dalloc(sizeof(double) * ctot);
+            double *d_tmp = (double *)dalloc(sizeof(double) * ctot);
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, d_rows, P->d_l, d_slot_of,
+                               A->d_qmap, A->d_l, d_aux_off, d_aux, d_off + count, d_cart);
+            HIP_CHECK(hipGetLastError());
+            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)(12 * count)), dim3(256), 0, s, count, d_rows, P->d_l, d_cart,
+                               d_tmp, d_off + count, d_off, out);
+        }
+        HIP_CHECK(hipGetLastError());
+        HIP_CHECK(hipStreamSynchronize(s));
+    } catch (const HipFail &f) {
+        rc = translate(f);
+    } catch (int code) {
+        rc = code;
+    } catch (const std::bad_alloc &) {
+        rc = ERI_E_NOMEM;
+    }
+    (void)hipStreamSynchronize(s);
+    for (void *p : tmp) (void)hipFree(p);
+    if (A) eri_plan_destroy(A);
+    return rc;
 }
 
 extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream)

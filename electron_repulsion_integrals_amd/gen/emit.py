@@ -998,7 +998,25 @@ def generate(out_dir: str, lmax: int = 4, classes=None):
     fn = os.path.join(out_dir, "eri_dispatch.hip")
     _write_if_changed(fn, "\n".join(d) + "\n")
     files.append(fn)
+    _write_if_changed(os.path.join(out_dir, "eri_sph_table.h"), sph_table_header())
     return files, entries
+
+
+def sph_table_header(lmax: int = 4) -> str:
+    """t^(l) for l <= lmax as a device constant table (row m = -l..l over the
+    Cartesian components, row-major, each l padded to a common stride), for the
+    runtime's transform of derivative blocks."""
+    from .cartesian import sph_matrix, ncart as nc_, nsph as ns_
+    stride = ns_(lmax) * nc_(lmax)
+    lines = ["// generated: real solid harmonic transforms t^(l), rows m = -l..l over Cartesian components",
+             "#pragma once", f"#define ERI_SPH_STRIDE {stride}",
+             f"static __constant__ double eri_sph_T[{lmax + 1}][{stride}] = {{"]
+    for l in range(lmax + 1):
+        vals = [v for row in sph_matrix(l) for v in row]
+        vals += [0.0] * (stride - len(vals))
+        lines.append("  {" + ", ".join(repr(float(v)) for v in vals) + "},")
+    lines.append("};")
+    return "\n".join(lines) + "\n"
 
 
 def _write_if_changed(fn, text):

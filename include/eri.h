@@ -181,6 +181,29 @@ int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, 
 int eri_digest_JK(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
                   int32_t ldk, void *stream);
 
+/*
+ * First derivatives of the integrals of plan slots [first, first + count)
+ * with respect to the 12 centre coordinates of each canonical quartet (the
+ * shells a, b, c, d of the index map): Eq. (1) of section II-A differentiated
+ * with respect to the centres; the page's library generates "first-derivative
+ * variants" of its class kernels (section IV, build system).  A primitive
+ * Cartesian Gaussian differentiated with respect to its own centre gives
+ * 2 alpha phi_(a+1_i) - a_i phi_(a-1_i), so each derivative block combines
+ * integrals of the two neighbouring classes, which the same class kernels
+ * compute on an auxiliary shell set (every shell raised and lowered).
+ *   out (device): for every slot, 12 blocks of the slot's block size in the
+ *     order d/dA_x, d/dA_y, d/dA_z, d/dB_x, ..., d/dD_z, each row-major over
+ *     (a, b, c, d) and Cartesian or spherical per the plan; the slots one
+ *     after another, so slot s starts at 12 x (sum of the block sizes of the
+ *     slots before it in the range).
+ *   out_capacity: doubles available at out (ERI_E_CAPACITY if too few).
+ *   count <= 2^24; every shell of the range must have l <= ERI_MAX_L - 1
+ *     (ERI_E_UNSUPPORTED otherwise).
+ * Allocates and frees its own work memory and synchronises `stream`.
+ */
+int eri_compute_deriv(const eri_plan *plan, int64_t first, int64_t count, double *out, int64_t out_capacity,
+                      void *stream);
+
 /* Static text for an error code, with the last HIP error for ERI_E_HIP. */
 const char *eri_strerror(int code);
 

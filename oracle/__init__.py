@@ -393,7 +393,7 @@ def conditioning_spread(sh, quartets, spherical: bool, ref=None, seeds=(0x9E3779
     return spread
 
 
-def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53):
+def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, normalize_: bool = True):
     """First-order fp64 error floor of the two-phase (VRR + HRR) evaluation.
 
     The two-phase method holds the contracted intermediates
@@ -408,7 +408,9 @@ def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53):
     through |t^(l)|).  It is the error that storing the intermediates in fp64
     alone forces on any such evaluation; for diffuse high-l quartets it can far
     exceed 1e-10 of the result.  The intermediates are computed here by the
-    oracle's own four-index recurrence on raw primitives.
+    oracle's own four-index recurrence on raw primitives, weighted by the
+    normalised contraction coefficients, or by the raw ones with
+    normalize_=False (for quartets evaluated with raw coefficients).
     """
     from math import comb
     q = np.asarray(quartets).reshape(-1, 4)
@@ -418,7 +420,8 @@ def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53):
         prim = []
         for s, l in ((a, la), (b, lb), (c, lc), (d, ld)):
             e = sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]
-            prim.append((e, normalize(l, e, sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]])))
+            raw = sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]]
+            prim.append((e, normalize(l, e, raw) if normalize_ else np.asarray(raw, dtype=float)))
         cen = [sh.centers[s] for s in (a, b, c, d)]
         V = {}
         for le in range(la, la + lb + 1):

@@ -149,6 +149,40 @@ def j_build(E, w, steps, stream):
                           "(J and K in one pass) are HIP-event times"}
 
 
+def deriv_sampled(E, plan, w, per_block=2000):
+    """First-derivative integrals (eri_compute_deriv: 12 centre-coordinate blocks
+    per quartet) of the first ``per_block`` quartets of every class block of a
+    plan; wall time of each call (it builds the auxiliary raised/lowered-shell
+    plan, computes those integrals and combines them, then synchronises)."""
+    import torch
+    from electron_repulsion_integrals_amd.gen import graph as G
+    res, tot_q, tot_s = {}, 0, 0.0
+    sph = bool(w.spherical)
+    for b in range(plan.n_blocks):
+        cid = int(plan.block_class[b])
+        la, lb = G.pair_class_ls(_pcb(cid))
+        lc, ld = G.pair_class_ls(_pck(cid))
+        if max(la, lb, lc, ld) > 3:
+            continue
+        n = int(min(per_block, plan.block_count[b]))
+        first = int(plan.block_start[b])
+        nf = (lambda l: 2 * l + 1) if sph else (lambda l: (l + 1) * (l + 2) // 2)
+        out = torch.empty(12 * n * nf(la) * nf(lb) * nf(lc) * nf(ld), dtype=torch.float64, device="cuda")
+        E.compute_deriv(plan, out, first, n)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        E.compute_deriv(plan, out, first, n)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        name = "(" + "spdfg"[la] + "spdfg"[lb] + "|" + "spdfg"[lc] + "spdfg"[ld] + ")"
+        res[name] = {"quartets": n, "ms": dt * 1e3, "quartets_per_s": n / dt}
+        tot_q += n
+        tot_s += dt
+    return {"quartets": tot_q, "seconds": tot_s, "quartets_per_s": tot_q / tot_s if tot_s else None,
+            "note": "wall time per call, including the auxiliary plan build; 12 derivative blocks per quartet",
+            "per_class": res}
+
+
 def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=200000):
     """The 120-atom cluster: the full screened plan (implicit) is built and
     timed; every class block is then sampled in ``strata`` evenly spaced
@@ -289,6 +323,7 @@ def main():
         plan3, jb = j_build(E, w3, 5, stream)
         res["j_build_30atom_svp"] = jb
         res["per_class"]["30-atom SVP-like cluster"] = per_class(E, plan3, w3, 3, stream)
+        res["derivatives_30atom_svp"] = deriv_sampled(E, plan3, w3)
         del plan3
         w4 = make_config(4)
         plan4 = E.build_quartets(w4.shells, E.ERI_SPHERICAL, w4.quartets, 0.0)

@@ -38,15 +38,23 @@ class _Shells(ctypes.Structure):
 
 
 _lib = None
+_lib_path = None
 
 
-def load():
-    global _lib
-    if _lib is not None:
+def load(path=None):
+    """Load the library (once per process).  ``path`` selects another build of
+    the same ABI, such as an ablation variant; a process holds one library."""
+    global _lib, _lib_path
+    if _lib is not None and path is None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m electron_repulsion_integrals_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    path = os.path.abspath(path) if path else LIB_PATH
+    if _lib is not None:
+        if path != _lib_path:
+            raise RuntimeError(f"{_lib_path} is already loaded in this process; cannot also load {path}")
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m electron_repulsion_integrals_amd.build`")
+    L = ctypes.CDLL(path)
     vp = ctypes.c_void_p
     i64p = ctypes.POINTER(ctypes.c_int64)
     i32p = ctypes.POINTER(ctypes.c_int32)
@@ -79,6 +87,7 @@ def load():
     L.eri_strerror.restype = ctypes.c_char_p
     L.eri_class_info.argtypes = [ctypes.c_int32, i32p, i32p]
     L.eri_class_info.restype = ctypes.c_int
+    _lib_path = path
     _lib = L
     return L
 

@@ -31,10 +31,11 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str, use_cache: bool) -> tuple[str, float, str]:
+def _compile(src: str, use_cache: bool, extra=()) -> tuple[str, float, str]:
     import time
+    flags = CFLAGS + list(extra)
     with open(src, "rb") as f:
-        h = hashlib.sha1(f.read() + " ".join(CFLAGS).encode())
+        h = hashlib.sha1(f.read() + " ".join(flags).encode())
     # headers affect every object
     for hdr in ("eri_device.h", os.path.join("generated", "eri_sph_table.h")):
         if os.path.exists(os.path.join(CSRC, hdr)):
@@ -44,48 +45,81 @@ def _compile(src: str, use_cache: bool) -> tuple[str, float, str]:
         h.update(f.read())
     obj = os.path.join(OBJ_DIR, os.path.basename(src) + "." + h.hexdigest()[:16] + ".o")
     if use_cache and os.path.exists(obj):
-        return obj, 0.0, ""
+        err = ""
+        if os.path.exists(obj + ".err"):
+            with open(obj + ".err") as f:
+                err = f.read()
+        return obj, 0.0, err
     t = time.time()
     tmp = obj + ".tmp.o"
-    r = subprocess.run([HIPCC, *CFLAGS, "-c", src, "-o", tmp], capture_output=True, text=True)
+    r = subprocess.run([HIPCC, *flags, "-c", src, "-o", tmp], capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-4000:]}")
+    with open(obj + ".err", "w") as f:
+        f.write(r.stderr)
     os.replace(tmp, obj)
     return obj, time.time() - t, r.stderr
 
 
-def build(lmax: int = 4, jobs: int | None = None, use_cache: bool = True, verbose: bool = True) -> str:
-    """Generate + compile + link.  ``use_cache`` reuses objects whose source and flags are unchanged."""
+def variant_paths(name: str):
+    """(generated-source directory, library path) of an ablation variant."""
+    return (os.path.join(ROOT, "_build", "ablation", name, "generated"),
+            os.path.join(PKG, "ablation_libs", f"liberi_{name}.so"))
+
+
+def build(lmax: int = 4, jobs: int | None = None, use_cache: bool = True, verbose: bool = True,
+          variant: str = "full", classes=None, remarks: dict | None = None) -> str:
+    """Generate + compile + link.  ``use_cache`` reuses objects whose source and flags are unchanged.
+
+    ``variant`` (gen/variant.py) builds an ablation library of the given
+    ``classes`` (all classes by default) from a switched generator into
+    ``ablation_libs/``; the default is the product library.  ``remarks``, if
+    given, receives the compiler's resource remarks per generated source."""
     sys.path.insert(0, ROOT)
-    from electron_repulsion_integrals_amd.gen.emit import generate
+    from electron_repulsion_integrals_amd.gen.emit import generate, sph_table_header, _write_if_changed
+    from electron_repulsion_integrals_amd.gen import variant as V
+    v = V.VARIANTS[variant]
+    product = variant == "full" and classes is None
+    gen_dir, lib = (GEN_DIR, LIB) if product else variant_paths(variant)
     os.makedirs(OBJ_DIR, exist_ok=True)
-    files, entries = generate(GEN_DIR, lmax=lmax)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    os.makedirs(GEN_DIR, exist_ok=True)
+    _write_if_changed(os.path.join(GEN_DIR, "eri_sph_table.h"), sph_table_header())
+    prev = V.set_variant(v)
+    try:
+        files, entries = generate(gen_dir, lmax=lmax, classes=classes)
+    finally:
+        V.set_variant(prev)
     keep = {os.path.basename(f) for f in files}
-    for fn in os.listdir(GEN_DIR):
+    for fn in os.listdir(gen_dir):
         if fn.endswith(".hip") and fn not in keep:
-            os.remove(os.path.join(GEN_DIR, fn))
+            os.remove(os.path.join(gen_dir, fn))
     srcs = [os.path.join(CSRC, "eri_runtime.hip")] + files
+    runtime_extra = [] if v.sph_fusion else ["-DERI_UNFUSED_SPHERICAL"]
     jobs = jobs or min(16, os.cpu_count() or 4)
     objs = [None] * len(srcs)
     # compile the largest sources first so the pool drains evenly
     order = sorted(range(len(srcs)), key=lambda i: -os.path.getsize(srcs[i]))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = {ex.submit(_compile, srcs[i], use_cache): i for i in order}
+        kernel_extra = ["-Rpass-analysis=kernel-resource-usage"] if remarks is not None else []
+        futs = {ex.submit(_compile, srcs[i], use_cache, runtime_extra if i == 0 else kernel_extra): i for i in order}
         for fu in cf.as_completed(futs):
             i = futs[fu]
-            obj, dt, _ = fu.result()
+            obj, dt, err = fu.result()
             objs[i] = obj
+            if remarks is not None and i > 0:
+                remarks[os.path.basename(srcs[i])] = err
             if verbose and dt > 20:
                 print(f"  compiled {os.path.basename(srcs[i])} in {dt:.0f}s", flush=True)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} ({len(srcs)} sources, {len(entries)} class kernels)", flush=True)
-    return LIB
+        print(f"built {lib} ({len(srcs)} sources, {len(entries)} class kernels)", flush=True)
+    return lib
 
 
 def resource_report(lmax: int = 4, jobs: int | None = None):

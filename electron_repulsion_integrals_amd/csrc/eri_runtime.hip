@@ -821,10 +821,21 @@ void sort_pairs_i32(int *keys_in, int *keys_out, V *v_in, V *v_out, int64_t n, h
     HIP_CHECK(e);
 }
 
-void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
-                  int64_t n_k1 = 0)
+// output kind of the class kernels a plan launches (the unfused-spherical
+// ablation build runs the Cartesian kernels for spherical plans)
+inline bool kernel_sph(const eri_plan *P)
 {
-    const EriClassEntry *ce = find_class(cid, P->sph);
+#ifdef ERI_UNFUSED_SPHERICAL
+    return false;
+#else
+    return P->sph;
+#endif
+}
+
+void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, const int *qket, int64_t n, double *out,
+                       hipStream_t s, int64_t n_k1)
+{
+    const EriClassEntry *ce = find_class(cid, sph);
     if (!ce) {
         g_last_error = "no kernel for class " + std::to_string(cid);
         throw HipFail{hipErrorInvalidValue};
@@ -839,7 +850,7 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
     a.scratch = P->d_scratch;
     a.scratch_wgs = P->scratch_wgs;
     a.grid_cap = P->grid_cap;
-    const int blk = nfun(ce->la, P->sph) * nfun(ce->lb, P->sph) * nfun(ce->lc, P->sph) * nfun(ce->ld, P->sph);
+    const int blk = nfun(ce->la, sph) * nfun(ce->lb, sph) * nfun(ce->lc, sph) * nfun(ce->ld, sph);
     if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
         g_last_error = "memory-tier class without scratch";
         throw HipFail{hipErrorInvalidValue};
@@ -860,6 +871,92 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
         }
     }
 }
+
+#ifdef ERI_UNFUSED_SPHERICAL
+// Ablation build only (the "no spherical fusion" variant of section V-B of
+// "FusionRCG"): a spherical block is computed as its Cartesian block, written
+// out, and then transformed on all four indices, Eq. (17), instead of the
+// stepwise fusion of Eq. (14).  One workgroup per quartet, four one-index
+// passes through two work buffers.
+__global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const double *cart, double *w0, double *w1,
+                              double *dst)
+{
+    const int64_t t = blockIdx.x;
+    if (t >= n) return;
+    const int l4[4] = {la, lb, lc, ld};
+    int dims[4], ns[4];
+    for (int k = 0; k < 4; ++k) {
+        dims[k] = (l4[k] + 1) * (l4[k] + 2) / 2;
+        ns[k] = 2 * l4[k] + 1;
+    }
+    const int64_t ncar = (int64_t)dims[0] * dims[1] * dims[2] * dims[3];
+    const int nsp = ns[0] * ns[1] * ns[2] * ns[3];
+    const double *in = cart + t * ncar;
+    for (int pos = 0; pos < 4; ++pos) {
+        int before = 1, after = 1;
+        for (int k = 0; k < pos; ++k) before *= dims[k];
+        for (int k = pos + 1; k < 4; ++k) after *= dims[k];
+        const double *T = eri_sph_T[l4[pos]];
+        const int nc = dims[pos], nsv = ns[pos];
+        double *o = pos == 3 ? dst + t * nsp : ((pos % 2 == 0) ? w0 : w1) + t * ncar;
+        const int total = before * nsv * after;
+        for (int x = threadIdx.x; x < total; x += blockDim.x) {
+            const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
+            double acc = 0.0;
+            for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
+            o[x] = acc;
+        }
+        dims[pos] = nsv;
+        in = o;
+        __syncthreads();
+    }
+}
+
+// work buffers of the unfused path, grown on demand and kept for the process
+// (calls on different streams must not overlap)
+double *g_unfused_buf = nullptr;
+int64_t g_unfused_cap = 0;
+
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
+                  int64_t n_k1 = 0)
+{
+    if (!P->sph) {
+        launch_class_kind(P, cid, false, qbra, qket, n, out, s, n_k1);
+        return;
+    }
+    const EriClassEntry *ce = find_class(cid, false);
+    if (!ce) {
+        g_last_error = "no kernel for class " + std::to_string(cid);
+        throw HipFail{hipErrorInvalidValue};
+    }
+    const int64_t nc = (int64_t)ncart(ce->la) * ncart(ce->lb) * ncart(ce->lc) * ncart(ce->ld);
+    const int64_t ns = (int64_t)nsph(ce->la) * nsph(ce->lb) * nsph(ce->lc) * nsph(ce->ld);
+    const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(n, ((int64_t)1 << 26) / nc));
+    if (g_unfused_cap < 3 * chunk * nc) {
+        HIP_CHECK(hipStreamSynchronize(s));
+        if (g_unfused_buf) HIP_CHECK(hipFree(g_unfused_buf));
+        g_unfused_buf = nullptr;
+        g_unfused_cap = 0;
+        HIP_CHECK(hipMalloc(&g_unfused_buf, 3 * chunk * nc * sizeof(double)));
+        g_unfused_cap = 3 * chunk * nc;
+    }
+    double *cart = g_unfused_buf, *w0 = cart + chunk * nc, *w1 = w0 + chunk * nc;
+    for (int64_t b = 0; b < n; b += chunk) {
+        const int64_t m = std::min(chunk, n - b);
+        const int64_t k1 = std::min(m, std::max<int64_t>(0, n_k1 - b));
+        launch_class_kind(P, cid, false, qbra + b, qket + b, m, cart, s, k1);
+        hipLaunchKernelGGL(k_sph_unfused, dim3((unsigned)m), dim3(256), 0, s, m, ce->la, ce->lb, ce->lc, ce->ld, cart,
+                           w0, w1, out + b * ns);
+        HIP_CHECK(hipGetLastError());
+    }
+}
+#else
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
+                  int64_t n_k1 = 0)
+{
+    launch_class_kind(P, cid, P->sph, qbra, qket, n, out, s, n_k1);
+}
+#endif
 
 // quartet lists of plan slots [s, s + m): the plan's own arrays, or for an
 // implicit plan the chunk buffers after expansion (m <= chunk_q)
@@ -985,7 +1082,7 @@ void ensure_scratch(eri_plan *P, const std::vector<int> &cids)
 {
     long long need = 0;
     for (int cid : cids) {
-        const EriClassEntry *ce = find_class(cid, P->sph);
+        const EriClassEntry *ce = find_class(cid, kernel_sph(P));
         if (ce && ce->tier == 'M') need = std::max(need, ce->scratch_doubles);
     }
     if (need == 0 || need <= P->scratch_doubles) return;

@@ -957,7 +957,13 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
 
 def tier_of(ci: ClassInfo) -> str:
     """Register tier whenever a lane group fits one wave (the compiler may keep
-    part of a large live set in AGPRs); memory tier for wider bra groups."""
+    part of a large live set in AGPRs); memory tier for wider bra groups.  The
+    single-tier ablation variants route every class to one tier."""
+    from .variant import CURRENT
+    if CURRENT.tiers == "memory":
+        return "M"
+    if CURRENT.tiers == "lane":
+        return "V"
     return "V" if ci.G <= 64 else "M"
 
 

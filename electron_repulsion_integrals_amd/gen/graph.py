@@ -369,6 +369,9 @@ def schedule_min_live(items, initial=(), remote=None, min_dist=0):
     least ``min_dist`` steps earlier, so the cross-lane read can be issued that
     far ahead of its use.
     """
+    from . import variant
+    if variant.CURRENT.schedule == "topo":
+        return topo_order(items)
     remote = remote or {}
     n = len(items)
     idx_of = {k: i for i, (k, ds, s) in enumerate(items)}
@@ -409,5 +412,34 @@ def schedule_min_live(items, initial=(), remote=None, min_dist=0):
             if missing[c] == 0:
                 ready.add(c)
                 stamp[c] = clock
+    assert len(order) == n, "cycle or missing dependency"
+    return order
+
+
+def topo_order(items):
+    """A plain topological order of the same items: Kahn's algorithm taking the
+    ready item that comes first in the given order (no liveness objective; the
+    "safe but non-optimized topological order" that section V-B of "FusionRCG"
+    compares DSA against)."""
+    import heapq
+    n = len(items)
+    idx_of = {k: i for i, (k, ds, s) in enumerate(items)}
+    consumers = {}
+    missing = [0] * n
+    for i, (k, ds, s) in enumerate(items):
+        for d in ds:
+            if d in idx_of:
+                missing[i] += 1
+                consumers.setdefault(d, []).append(i)
+    heap = [i for i in range(n) if missing[i] == 0]
+    heapq.heapify(heap)
+    order = []
+    while heap:
+        i = heapq.heappop(heap)
+        order.append(items[i])
+        for c in consumers.get(items[i][0], []):
+            missing[c] -= 1
+            if missing[c] == 0:
+                heapq.heappush(heap, c)
     assert len(order) == n, "cycle or missing dependency"
     return order

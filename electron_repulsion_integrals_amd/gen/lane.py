@@ -20,7 +20,7 @@ its order comes from the liveness scheduler.
 from __future__ import annotations
 
 from .cartesian import components, sub
-from .graph import ClassInfo, build_ket_vrr, build_hrr, class_id, schedule_min_live, peak_live
+from .graph import ClassInfo, build_ket_vrr, build_hrr, class_id, schedule_min_live, peak_live, raise_axis
 
 AX = "xyz"
 # accumulators per lane: up to 100 the kernel may drop to one wave per SIMD
@@ -33,10 +33,35 @@ def _bra_axis(e):
     return 2 if e[2] > 0 else (1 if e[1] > 0 else 0)
 
 
+def _lowering(e, f, topology):
+    """Side ("b" bra, "k" ket) and axis of the raise that produces node (e, f)."""
+    if topology == "ket_first":
+        if sum(f) > 0:
+            return "k", raise_axis(f)  # the ket recurrence's own axis choice
+        return "b", _bra_axis(e)
+    if topology == "alg1":
+        for ax in (2, 1, 0):
+            if f[ax] > 0:
+                return "k", ax
+            if e[ax] > 0:
+                return "b", ax
+    if topology == "bra_first":
+        for side, t in (("b", e), ("k", f)):
+            for ax in (0, 1, 2):
+                if t[ax] > 0:
+                    return side, ax
+    raise ValueError(topology)
+
+
 def lane_vrr(ci: ClassInfo):
-    """Nodes {(e, f, m): (kind, axis, deps)} reachable from the targets, and the targets."""
+    """Nodes {(e, f, m): (kind, axis, deps)} reachable from the targets, and the targets.
+
+    A ket node lowers f along `axis`: operands (e, f-1, m), (e, f-1, m+1), then
+    (e, f-2, m), (e, f-2, m+1) when f_axis >= 2, then the coupling operand
+    (e-1, f-1, m+1) when e_axis > 0.  A bra node is the mirror image (Eq. (2)).
+    """
+    from .variant import CURRENT
     kv = build_ket_vrr(ci.lc, ci.Lk)
-    knode = {(n.f, n.m): n for n in kv.nodes}
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     targets = [(e, f) for e in ebra for (f, _) in kv.targets]
     nodes = {}
@@ -45,26 +70,23 @@ def lane_vrr(ci: ClassInfo):
         e, f, m = stack.pop()
         if (e, f, m) in nodes:
             continue
-        if sum(f) > 0:
-            n = knode[(f, m)]
-            ax = n.axis
-            deps = [(e, n.a0[0], n.a0[1]), (e, n.a1[0], n.a1[1])]
-            if n.b0 is not None:
-                deps += [(e, n.b0[0], n.b0[1]), (e, n.b1[0], n.b1[1])]
-            if e[ax] > 0:
-                deps.append((sub(e, ax), n.a1[0], n.a1[1]))
-            nodes[(e, f, m)] = ("k", ax, deps, n)
-        elif sum(e) > 0:
-            ax = _bra_axis(e)
-            e1 = sub(e, ax)
-            deps = [(e1, f, m), (e1, f, m + 1)]
-            if e[ax] >= 2:
-                e2 = sub(e, ax, 2)
-                deps += [(e2, f, m), (e2, f, m + 1)]
-            nodes[(e, f, m)] = ("b", ax, deps, None)
-        else:
-            nodes[(e, f, m)] = ("F", None, [], None)
-        stack += nodes[(e, f, m)][2]
+        if sum(e) + sum(f) == 0:
+            nodes[(e, f, m)] = ("F", None, [])
+            continue
+        kind, ax = _lowering(e, f, CURRENT.topology)
+        own, other = (f, e) if kind == "k" else (e, f)
+
+        def at(o, t, mm):
+            return (t, o, mm) if kind == "k" else (o, t, mm)
+        o1 = sub(own, ax)
+        deps = [at(o1, other, m), at(o1, other, m + 1)]
+        if own[ax] >= 2:
+            o2 = sub(own, ax, 2)
+            deps += [at(o2, other, m), at(o2, other, m + 1)]
+        if other[ax] > 0:
+            deps.append(at(o1, sub(other, ax), m + 1))
+        nodes[(e, f, m)] = (kind, ax, deps)
+        stack += deps
     return nodes, targets, ebra, kv
 
 
@@ -86,6 +108,9 @@ def lane_peak(ci: ClassInfo) -> int:
 
 
 def use_lane_tier(ci: ClassInfo, spherical: bool) -> bool:
+    from .variant import CURRENT
+    if CURRENT.tiers == "lane":
+        return True
     nacc = ci.n_ebra * len(build_ket_vrr(ci.lc, ci.Lk).targets)
     if nacc > MAX_ACC or ci.L > 6:
         return False
@@ -154,19 +179,16 @@ def emit_lane_tier(ci: ClassInfo, spherical: bool, k1: bool):
             e, f = targets[t]
             o.append(f"    acc{t} += {name[(e, f, 0)]};")
             continue
-        kind, ax, dl, n = nodes[k]
+        kind, ax, dl = nodes[k]
         e, f, m = k
         a_ = AX[ax]
-        if kind == "b":
-            expr = f"PA{a_} * {name[dl[0]]} + WP{a_} * {name[dl[1]]}"
-            if len(dl) == 4:
-                expr += f" + {_fmt(e[ax] - 1)} * i2z * ({name[dl[2]]} - roz * {name[dl[3]]})"
-        else:
-            expr = f"QC{a_} * {name[dl[0]]} + WQ{a_} * {name[dl[1]]}"
-            if n.b0 is not None:
-                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({name[dl[2]]} - roe * {name[dl[3]]})"
-            if e[ax] > 0:
-                expr += f" + {_fmt(e[ax])} * i2ze * {name[dl[-1]]}"
+        own, other = (e, f) if kind == "b" else (f, e)
+        g1, g2, half, ro = ("PA", "WP", "i2z", "roz") if kind == "b" else ("QC", "WQ", "i2e", "roe")
+        expr = f"{g1}{a_} * {name[dl[0]]} + {g2}{a_} * {name[dl[1]]}"
+        if own[ax] >= 2:
+            expr += f" + {_fmt(own[ax] - 1)} * {half} * ({name[dl[2]]} - {ro} * {name[dl[3]]})"
+        if other[ax] > 0:
+            expr += f" + {_fmt(other[ax])} * i2ze * {name[dl[-1]]}"
         o.append(f"    const double {name[k]} = {expr};")
     o.append("  }")
     if not k1:

@@ -10,6 +10,7 @@
 * class enumeration and tier routing.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -223,16 +224,18 @@ def emulate_lane_tier(ci, cen, exps, coefs, spherical):
                     i2z, roz, i2e, roe, i2ze = 0.5 / z, e_ * ize, 0.5 / e_, z * ize, 0.5 * ize
                     V = {k: F[k[2]] for k, v in nodes.items() if v[0] == "F"}
                     for k in order:
-                        kind, ax, dl, n = nodes[k]
-                        e = k[0]
+                        kind, ax, dl = nodes[k]
+                        e, f = k[0], k[1]
                         if kind == "b":
                             v = PA[ax] * V[dl[0]] + WP[ax] * V[dl[1]]
-                            if len(dl) == 4:
+                            if e[ax] >= 2:
                                 v += (e[ax] - 1) * i2z * (V[dl[2]] - roz * V[dl[3]])
+                            if f[ax] > 0:
+                                v += f[ax] * i2ze * V[dl[-1]]
                         else:
                             v = QC[ax] * V[dl[0]] + WQ[ax] * V[dl[1]]
-                            if n.b0 is not None:
-                                v += n.fi_minus_1 * i2e * (V[dl[2]] - roe * V[dl[3]])
+                            if f[ax] >= 2:
+                                v += (f[ax] - 1) * i2e * (V[dl[2]] - roe * V[dl[3]])
                             if e[ax] > 0:
                                 v += e[ax] * i2ze * V[dl[-1]]
                         V[k] = v
@@ -272,6 +275,54 @@ def test_lane_tier_graph_matches_oracle(ls, spherical):
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-13 * max(1.0, np.abs(ref).max()))
 
 
+@pytest.mark.parametrize("topology", ["alg1", "bra_first"])
+@pytest.mark.parametrize("ls", [(1, 1, 1, 0), (2, 1, 1, 1), (3, 0, 2, 0)])
+def test_lane_tier_topology_variants_match_oracle(ls, topology):
+    """The ablation graphs (the printed axis-priority rule of Algorithm 1, and
+    bra side first) are other valid graphs of Eq. (2): evaluated in numpy they
+    reproduce the oracle, with bra nodes carrying the ket coupling term."""
+    from electron_repulsion_integrals_amd.gen import variant, lane as LN
+    ci = gg.ClassInfo(*ls)
+    rng = np.random.default_rng(sum(ls) * 11 + len(topology))
+    cen = [rng.uniform(0, 4, 3) for _ in range(4)]
+    K = [2, 1, 1, 2]
+    exps = [list(np.exp(rng.uniform(np.log(0.2), np.log(8.0), k))) for k in K]
+    coefs = [list(rng.uniform(0.2, 1.0, k)) for k in K]
+    prev = variant.set_variant(variant.Variant(name="t", topology=topology))
+    try:
+        nodes, _, _, _ = LN.lane_vrr(ci)
+        assert any(k == "b" and sum(key[1]) > 0 for key, (k, _, _) in nodes.items())
+        got = emulate_lane_tier(ci, cen, exps, coefs, True)
+    finally:
+        variant.set_variant(prev)
+    sh = _pack(cen, list(ls), K, [np.array(e) for e in exps], [np.array(c) for c in coefs])
+    ref = oracle.eri_block(sh, [0, 1, 2, 3], True)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-13 * max(1.0, np.abs(ref).max()))
+
+
+def test_topological_order_variant_is_valid_and_plain():
+    """The scheduler of the no-DSA variant returns a topological order of the same
+    items (every operand before its consumer) without reordering for liveness; on
+    a lane-tier graph its PeakLive is above the liveness scheduler's."""
+    from electron_repulsion_integrals_amd.gen import variant, lane as LN
+    ci = gg.ClassInfo(2, 1, 1, 1)
+    nodes, targets, ebra, kv = LN.lane_vrr(ci)
+    peaks = {}
+    for sched in ("dsa", "topo"):
+        prev = variant.set_variant(variant.Variant(name=sched, schedule=sched))
+        try:
+            _, _, _, _, order, base = LN._schedule(ci)
+        finally:
+            variant.set_variant(prev)
+        seen = set(base)
+        for k, ds, sink in order:
+            assert all(d in seen for d in ds), k
+            seen.add(k)
+        assert len(order) == len(nodes) - len(base) + len(targets)
+        peaks[sched] = gg.peak_live(order, None, base)
+    assert peaks["topo"] > peaks["dsa"], peaks
+
+
 def test_lane_tier_graph_is_the_counted_graph():
     """Per primitive quartet the lane tier evaluates exactly the recurrence nodes
     that the FLOP count of the roofline reports (graph.dag_flops)."""
@@ -280,11 +331,12 @@ def test_lane_tier_graph_is_the_counted_graph():
         ci = gg.ClassInfo(*ls)
         nodes, targets, ebra, kv = LN.lane_vrr(ci)
         flops = 0
-        for (e, f, m), (kind, ax, dl, n) in nodes.items():
+        for (e, f, m), (kind, ax, dl) in nodes.items():
             if kind == "b":
-                flops += 3 + (4 if len(dl) == 4 else 0)
+                assert f == (0, 0, 0)
+                flops += 3 + (4 if e[ax] >= 2 else 0)
             elif kind == "k":
-                flops += 3 + (4 if n.b0 is not None else 0) + (2 if e[ax] > 0 else 0)
+                flops += 3 + (4 if f[ax] >= 2 else 0) + (2 if e[ax] > 0 else 0)
         per_prim, _ = gg.dag_flops(ci, True)
         other = 30 + 14 + 3 * ci.L + (ci.L + 1) + ci.n_ebra * len(kv.targets)
         assert flops == per_prim - other, ls
@@ -317,3 +369,37 @@ def test_two_phase_fp64_floor_is_eps_level_when_well_conditioned():
     ref = np.abs(oracle.eri_block(sh, [0, 1, 2, 3], True)).max()
     B = oracle.hgp_rounding_bound(sh, [[0, 1, 2, 3]], True)
     assert B.max() < 1e-14 * ref
+
+
+def test_ablation_variants_generate(tmp_path):
+    """Every ablation variant of the generator emits its classes with the routing
+    it names: the single-tier variants put every class in one tier, the graph and
+    order variants change the emitted lane-tier code, and the product variant
+    emits exactly the product sources."""
+    from electron_repulsion_integrals_amd.gen import variant
+    from electron_repulsion_integrals_amd.gen.emit import generate
+    cls = [gg.ClassInfo(1, 1, 1, 1), gg.ClassInfo(2, 2, 2, 2), gg.ClassInfo(3, 3, 0, 0)]
+    srcs = {}
+    for name in variant.VARIANTS:
+        prev = variant.set_variant(name)
+        try:
+            files, entries = generate(str(tmp_path / name), lmax=4, classes=cls)
+        finally:
+            variant.set_variant(prev)
+        tiers = [t for (_, _, _, t, _) in entries]
+        if variant.VARIANTS[name].tiers == "memory":
+            assert set(tiers) == {"M"}
+        elif variant.VARIANTS[name].tiers == "lane":
+            assert set(tiers) == {"V"}
+            assert all("one quartet per lane" in open(f).read() for f in files[:-1])
+        else:
+            assert tiers == ["V", "V", "V", "V", "M", "M"]
+        srcs[name] = {os.path.basename(f): open(f).read() for f in files}
+    assert srcs["no_dsa"]["eri_c5_s.hip"] != srcs["full"]["eri_c5_s.hip"]
+    assert srcs["lane_alg1"]["eri_c5_s.hip"] != srcs["lane_only"]["eri_c5_s.hip"]
+    assert srcs["lane_bra_first"]["eri_c5_s.hip"] != srcs["lane_only"]["eri_c5_s.hip"]
+    assert srcs["no_sph_fusion"] == srcs["full"]
+    from electron_repulsion_integrals_amd.build import GEN_DIR
+    for fn, text in srcs["full"].items():
+        if fn.startswith("eri_c") and os.path.exists(os.path.join(GEN_DIR, fn)):
+            assert open(os.path.join(GEN_DIR, fn)).read() == text, fn

@@ -89,6 +89,32 @@ def time_launches(fn, steps, warmup, stream):
     return [a.elapsed_time(b) for a, b in ev], wall
 
 
+def back_to_back(fn, n, stream):
+    """Mean ms per call of n calls issued back to back between one pair of events."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    b.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def gpu_clocks():
+    """Current shader and memory clocks as rocm-smi reports them (None if it is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
+    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()} or None
+
+
 def _block_flops(plan, w, imap):
     """Algorithmic FLOPs per class block: sum over quartets of K4 x per-primitive + once."""
     import numpy as np
@@ -258,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--only-j-build", action="store_true",
+                    help="only the 30-atom cluster: J build and per-class times (for profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
@@ -282,14 +310,22 @@ def main():
     E.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if a.only_j_build:
+        w3 = make_config(3)
+        plan3, jb = j_build(E, w3, 5, stream)
+        print(json.dumps({"j_build_30atom_svp": jb, "per_class": per_class(E, plan3, w3, 3, stream)}), flush=True)
+        return
     w = make_config(2)
     t0 = time.perf_counter()
     plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, w.quartets, 0.0)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
+    smi_before = gpu_clocks()
     times, wall = time_launches(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
+    smi_after = gpu_clocks()
     ms = sum(times) / len(times)
+    b2b = back_to_back(lambda: E.compute_batch(plan, out), 100, stream)
     nq = plan.n_quartets
     (per_prim, once), = _class_flops(plan, True)
     flops = nq * (per_prim + once)  # K = 1: one primitive quartet per quartet
@@ -312,6 +348,11 @@ def main():
                    "quartets": nq, "output_doubles": plan.n_out},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP64_VECTOR_PEAK_TFLOPS, "traffic": measured_traffic()},
+        "ms_median": sorted(times)[len(times) // 2],
+        "ms_min": min(times),
+        "ms_max": max(times),
+        "ms_per_launch_100_back_to_back": b2b,
+        "gpu_clocks_before_after": [smi_before, smi_after],
         "output_write_GBps": plan.n_out * 8 / (ms * 1e-3) / 1e9,
         "plan_build_ms": plan_ms,
         "wall_s_timed_region": wall,

@@ -444,21 +444,49 @@ __global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab
     eoff[2 * s + 1] = two ? off + nab : -1;
 }
 
-// one workgroup per run of equal pairs in the sorted chunk entries: add the
-// run's contribution vectors in entry order to the J block (and its transpose)
-__global__ void k_add_runs(const int *nruns, const int *key, const int *rstart, const int *rlen, const int64_t *eoff,
-                           const double *cb, const int4 *pinfo, const int *bf, const int *nfun_sh, double *J, int ldj)
+// Sum of the entries e0, e0+1, ..., e1-1 of a run of contribution vectors of
+// length n (n <= blockDim.x), in a fixed order: the block splits into
+// S = blockDim.x / n slices, slice k adds the entries e0 + k, e0 + k + S, ...
+// in entry order, and thread v < n then adds the S partial sums in slice
+// order.  Deterministic for a given blockDim; the result is left in part[v].
+__device__ __forceinline__ void run_sum(int n, int64_t e0, int64_t e1, const int64_t *eoff, const double *cb,
+                                        double *part)
 {
+    const int S = blockDim.x / n;
+    const int v = threadIdx.x % n, sl = threadIdx.x / n;
+    double acc = 0.0;
+    if (sl < S)
+        for (int64_t e = e0 + sl; e < e1; e += S) acc += cb[eoff[e] + v];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x < n) {
+        double t = 0.0;
+        for (int k = 0; k < S; ++k) t += part[k * n + threadIdx.x];
+        part[threadIdx.x] = t;  // slot threadIdx.x < n was read only by this thread
+    }
+}
+
+constexpr int RUN_THREADS = 256;
+
+// one workgroup per run of equal pairs in the sorted chunk entries: add the
+// run's contribution vectors into the J block (and its transpose)
+__global__ void __launch_bounds__(RUN_THREADS) k_add_runs(const int *nruns, const int *key, const int *rstart,
+                                                          const int *rlen, const int64_t *eoff, const double *cb,
+                                                          const int4 *pinfo, const int *bf, const int *nfun_sh,
+                                                          double *J, int ldj)
+{
+    __shared__ double part[RUN_THREADS];
     const int u = blockIdx.x;
     if (u >= *nruns) return;
     const int p = key[u];
     if (p == 0x7fffffff) return;
     const int4 pi = pinfo[p];
     const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
-    const int e0 = rstart[u], e1 = e0 + rlen[u];
-    for (int v = threadIdx.x; v < n; v += blockDim.x) {
-        double acc = 0.0;
-        for (int e = e0; e < e1; ++e) acc += cb[eoff[e] + v];
+    const int64_t e0 = rstart[u], e1 = e0 + rlen[u];
+    run_sum(n, e0, e1, eoff, cb, part);
+    const int v = threadIdx.x;
+    if (v < n) {
+        const double acc = part[v];
         const int a = v / nb, b = v - a * nb;
         J[(size_t)(bf[pi.x] + a) * ldj + bf[pi.y] + b] += acc;
         if (pi.x != pi.y) J[(size_t)(bf[pi.y] + b) * ldj + bf[pi.x] + a] += acc;
@@ -477,53 +505,46 @@ __global__ void k_add_runs(const int *nruns, const int *key, const int *rstart, 
 // ket pairs are the same pair, the transposed quadruples are the same as the
 // first four: those quartets count one half in A.
 
-// per quartet: the four blocks V1 (na x nc), V2 (nb x nc), V3 (na x nd), V4 (nb x nd)
-__global__ void k_kdigest_block(int nq, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
-                                const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
-                                double *kv)
+// per quartet: the four blocks V1 (na x nc), V2 (nb x nc), V3 (na x nd), V4 (nb x nd),
+// one thread per element of the m quartets' vectors (w elements per quartet)
+__global__ void k_kdigest_rows(int64_t n_out, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
+                               const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
+                               double *kv)
 {
-    const int q = blockIdx.x;
-    if (q >= nq) return;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_out) return;
+    const int w1 = na * nc, w2 = nb * nc, w3 = na * nd, w4 = nb * nd, w = w1 + w2 + w3 + w4;
+    const int64_t q = t / w;
+    int u = (int)(t - q * w);
     const int pb = qbra[q], pk = qket[q];
     const int4 ib = pinfo[pb], ik = pinfo[pk];
     const int i0 = bf[ib.x], j0 = bf[ib.y], k0 = bf[ik.x], l0 = bf[ik.y];
     const bool dij = ib.x != ib.y, dkl = ik.x != ik.y;
-    const double w = pb == pk ? 0.5 : 1.0;
-    const int nab = na * nb, ncd = nc * nd;
-    const double *blk = I + (size_t)q * nab * ncd;
-    double *v = kv + (size_t)q * (na * nc + nb * nc + na * nd + nb * nd);
-    double *v1 = v, *v2 = v1 + na * nc, *v3 = v2 + nb * nc, *v4 = v3 + na * nd;
-    for (int u = threadIdx.x; u < na * nc; u += blockDim.x) {
+    const double wt = pb == pk ? 0.5 : 1.0;
+    const double *blk = I + (size_t)q * (na * nb) * (nc * nd);
+    double acc = 0.0;
+    if (u < w1) {
         const int a = u / nc, c = u - a * nc;
-        double t = 0.0;
         for (int b = 0; b < nb; ++b)
-            for (int d = 0; d < nd; ++d) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + l0 + d];
-        v1[u] = w * t;
-    }
-    for (int u = threadIdx.x; u < nb * nc; u += blockDim.x) {
+            for (int d = 0; d < nd; ++d) acc += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + l0 + d];
+    } else if ((u -= w1) < w2) {
         const int b = u / nc, c = u - b * nc;
-        double t = 0.0;
         if (dij)
             for (int a = 0; a < na; ++a)
-                for (int d = 0; d < nd; ++d) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + l0 + d];
-        v2[u] = w * t;
-    }
-    for (int u = threadIdx.x; u < na * nd; u += blockDim.x) {
+                for (int d = 0; d < nd; ++d) acc += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + l0 + d];
+    } else if ((u -= w2) < w3) {
         const int a = u / nd, d = u - a * nd;
-        double t = 0.0;
         if (dkl)
             for (int b = 0; b < nb; ++b)
-                for (int c = 0; c < nc; ++c) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + k0 + c];
-        v3[u] = w * t;
-    }
-    for (int u = threadIdx.x; u < nb * nd; u += blockDim.x) {
+                for (int c = 0; c < nc; ++c) acc += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(j0 + b) * ldd + k0 + c];
+    } else {
+        u -= w3;
         const int b = u / nd, d = u - b * nd;
-        double t = 0.0;
         if (dij && dkl)
             for (int a = 0; a < na; ++a)
-                for (int c = 0; c < nc; ++c) t += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + k0 + c];
-        v4[u] = w * t;
+                for (int c = 0; c < nc; ++c) acc += blk[((size_t)(a * nb + b) * nc + c) * nd + d] * D[(size_t)(i0 + a) * ldd + k0 + c];
     }
+    kv[t] = wt * acc;
 }
 
 // chunk entries for K: (target shell block s1 * nshell + s2, offset of the block's
@@ -548,22 +569,25 @@ __global__ void k_kchunk_entries(int m, const int *qbra, const int *qket, const 
     eoff[4 * q + 3] = base + na * nc + nb * nc + na * nd;
 }
 
-// one workgroup per run of equal target blocks: add the run's vectors in entry order into A
-__global__ void k_add_runs_K(const int *nruns, const int *key, const int *rstart, const int *rlen, const int64_t *eoff,
-                             const double *kv, int nshell, const int *bf, const int *nfun_sh, double *A, int lda)
+// one workgroup per run of equal target blocks: add the run's vectors into A
+__global__ void __launch_bounds__(RUN_THREADS) k_add_runs_K(const int *nruns, const int *key, const int *rstart,
+                                                            const int *rlen, const int64_t *eoff, const double *kv,
+                                                            int nshell, const int *bf, const int *nfun_sh, double *A,
+                                                            int lda)
 {
+    __shared__ double part[RUN_THREADS];
     const int u = blockIdx.x;
     if (u >= *nruns) return;
     const int k = key[u];
     if (k == 0x7fffffff) return;
     const int s1 = k / nshell, s2 = k - s1 * nshell;
     const int n1 = nfun_sh[s1], n2 = nfun_sh[s2];
-    const int e0 = rstart[u], e1 = e0 + rlen[u];
-    for (int v = threadIdx.x; v < n1 * n2; v += blockDim.x) {
-        double acc = 0.0;
-        for (int e = e0; e < e1; ++e) acc += kv[eoff[e] + v];
+    const int64_t e0 = rstart[u], e1 = e0 + rlen[u];
+    run_sum(n1 * n2, e0, e1, eoff, kv, part);
+    const int v = threadIdx.x;
+    if (v < n1 * n2) {
         const int x = v / n2, y = v - x * n2;
-        A[(size_t)(bf[s1] + x) * lda + bf[s2] + y] += acc;
+        A[(size_t)(bf[s1] + x) * lda + bf[s2] + y] += part[v];
     }
 }
 
@@ -592,53 +616,56 @@ __global__ void k_gather_i64(int n, const int64_t *src, const int64_t *idx, int6
 
 // Per quartet of one class block: vb[ab] = sum_cd I[ab,cd] D~_cd and, for
 // distinct pairs, vk[cd] = sum_ab I[ab,cd] D~_ab, with D~ = D x 2 for a pair of
-// two different shells (the 8-fold symmetry factors).
-__global__ void k_digest_block(int nq, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
-                               const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
-                               double *cb)
+// two different shells (the 8-fold symmetry factors).  One thread per element
+// of the m quartets' vectors (nab + ncd per quartet, stored back to back).
+__global__ void k_digest_rows(int64_t n_out, int na, int nb, int nc, int nd, const int *qbra, const int *qket,
+                              const int4 *pinfo, const int *bf, const double *I, const double *D, int ldd,
+                              double *cb)
 {
-    const int q = blockIdx.x;
-    if (q >= nq) return;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= n_out) return;
+    const int nab = na * nb, ncd = nc * nd, w = nab + ncd;
+    const int64_t q = t / w;
+    const int r = (int)(t - q * w);
     const int pb = qbra[q], pk = qket[q];
-    const int4 ib = pinfo[pb], ik = pinfo[pk];
-    const int nab = na * nb, ncd = nc * nd;
     const double *blk = I + (size_t)q * nab * ncd;
-    double *vb = cb + (size_t)q * (nab + ncd);
-    double *vk = vb + nab;
-    const double fk = ik.x != ik.y ? 2.0 : 1.0, fb = ib.x != ib.y ? 2.0 : 1.0;
-    const int c0 = bf[ik.x], d0 = bf[ik.y], a0 = bf[ib.x], b0 = bf[ib.y];
-    for (int ab = threadIdx.x; ab < nab; ab += blockDim.x) {
-        double s = 0.0;
+    double s = 0.0;
+    if (r < nab) {
+        const int4 ik = pinfo[pk];
+        const int c0 = bf[ik.x], d0 = bf[ik.y];
+        const double *row = blk + (size_t)r * ncd;
         for (int c = 0; c < nc; ++c)
-            for (int d = 0; d < nd; ++d) s += blk[(size_t)ab * ncd + c * nd + d] * D[(size_t)(c0 + c) * ldd + d0 + d];
-        vb[ab] = fk * s;
-    }
-    for (int cd = threadIdx.x; cd < ncd; cd += blockDim.x) {
-        double s = 0.0;
+            for (int d = 0; d < nd; ++d) s += row[c * nd + d] * D[(size_t)(c0 + c) * ldd + d0 + d];
+        s = (ik.x != ik.y ? 2.0 : 1.0) * s;
+    } else {
+        const int4 ib = pinfo[pb];
+        const int cd = r - nab;
         if (pb != pk) {
-            const int c = cd / nd, d = cd - c * nd;
-            (void)c;
-            (void)d;
+            const int a0 = bf[ib.x], b0 = bf[ib.y];
             for (int a = 0; a < na; ++a)
                 for (int b = 0; b < nb; ++b) s += blk[(size_t)(a * nb + b) * ncd + cd] * D[(size_t)(a0 + a) * ldd + b0 + b];
         }
-        vk[cd] = fb * s;
+        s = (ib.x != ib.y ? 2.0 : 1.0) * s;
     }
+    cb[t] = s;
 }
 
 // One workgroup per pair: sum its contribution vectors in a fixed order, then
 // write the J block (and its transpose for two different shells).
-__global__ void k_reduce_pairs(int np, const int4 *pinfo, const int *bf, const int *nfun_sh, const int64_t *seg,
-                               const int64_t *ent_off, const double *cb, double *J, int ldj)
+__global__ void __launch_bounds__(RUN_THREADS) k_reduce_pairs(int np, const int4 *pinfo, const int *bf,
+                                                              const int *nfun_sh, const int64_t *seg,
+                                                              const int64_t *ent_off, const double *cb, double *J,
+                                                              int ldj)
 {
+    __shared__ double part[RUN_THREADS];
     const int p = blockIdx.x;
     if (p >= np) return;
     const int4 pi = pinfo[p];
     const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
-    const int64_t s0 = seg[p], s1 = seg[p + 1];
-    for (int u = threadIdx.x; u < n; u += blockDim.x) {
-        double s = 0.0;
-        for (int64_t e = s0; e < s1; ++e) s += cb[ent_off[e] + u];
+    run_sum(n, seg[p], seg[p + 1], ent_off, cb, part);
+    const int u = threadIdx.x;
+    if (u < n) {
+        const double s = part[u];
         const int a = u / nb, b = u - a * nb;
         J[(size_t)(bf[pi.x] + a) * ldj + bf[pi.y] + b] = s;
         if (pi.x != pi.y) J[(size_t)(bf[pi.y] + b) * ldj + bf[pi.x] + a] = s;
@@ -1047,26 +1074,33 @@ void digest_JK_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
             launch_class(P, B.cid, qb, qk, m, P->d_cints, s, nk1);
             if (J) {
-                hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd, qb,
-                                   qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
+                const int64_t nv = m * (nab + ncd);
+                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, s, nv, B.na, B.nb, B.nc,
+                                   B.nd, qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
                 hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, nab, ncd,
                                    P->d_cek, P->d_ceo);
                 HIP_CHECK(hipGetLastError());
                 sort_runs((int)(2 * m));
                 // at most 2m runs; workgroups past the device-side run count exit at once
-                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)(2 * m)), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst,
-                                   P->d_rlen, P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
+                // at most one run per pair key (and one for the sentinel key)
+                const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
+                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, s, P->d_nruns, P->d_ruk,
+                                   P->d_rst, P->d_rlen, P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
                 HIP_CHECK(hipGetLastError());
             }
             if (K) {
-                hipLaunchKernelGGL(k_kdigest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd,
-                                   qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ckv);
+                const int64_t nkt = m * nkv;
+                hipLaunchKernelGGL(k_kdigest_rows, dim3((unsigned)nblk(nkt, 256)), dim3(256), 0, s, nkt, B.na, B.nb,
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ckv);
                 hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, P->d_pinfo,
                                    P->nshell, B.na, B.nb, B.nc, B.nd, P->d_cek, P->d_ceo);
                 HIP_CHECK(hipGetLastError());
                 sort_runs((int)(4 * m));
-                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)(4 * m)), dim3(64), 0, s, P->d_nruns, P->d_ruk, P->d_rst,
-                                   P->d_rlen, P->d_ceo2, P->d_ckv, P->nshell, P->d_bf, P->d_nfun, P->d_kacc, n);
+                // at most one run per target block key (and one for the sentinel key)
+                const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
+                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, s, P->d_nruns, P->d_ruk,
+                                   P->d_rst, P->d_rlen, P->d_ceo2, P->d_ckv, P->nshell, P->d_bf, P->d_nfun,
+                                   P->d_kacc, n);
                 HIP_CHECK(hipGetLastError());
             }
         }
@@ -1913,16 +1947,16 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
             const int64_t CH = 1 << 30;
             for (int64_t c = 0; c < B.count; c += CH) {
                 const int64_t m = std::min(CH, B.count - c);
-                const int64_t nab = B.na * B.nb, ncd = B.nc * B.nd;
-                hipLaunchKernelGGL(k_digest_block, dim3((unsigned)m), dim3(64), 0, s, (int)m, B.na, B.nb, B.nc, B.nd,
-                                   P->d_qbra + B.start + c, P->d_qket + B.start + c, P->d_pinfo, P->d_bf,
+                const int64_t nab = B.na * B.nb, ncd = B.nc * B.nd, nv = m * (nab + ncd);
+                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, s, nv, B.na, B.nb, B.nc,
+                                   B.nd, P->d_qbra + B.start + c, P->d_qket + B.start + c, P->d_pinfo, P->d_bf,
                                    P->d_ints + B.out_off + c * nab * ncd, D, ldd, P->d_cb + cbt + c * (nab + ncd));
                 HIP_CHECK(hipGetLastError());
             }
             cbt += B.count * (int64_t)(B.na * B.nb + B.nc * B.nd);
         }
         // 3. deterministic per-pair reduction into J
-        hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(64), 0, s, (int)P->npairs, P->d_pinfo,
+        hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(RUN_THREADS), 0, s, (int)P->npairs, P->d_pinfo,
                            P->d_bf, P->d_nfun, P->d_seg, P->d_eoff, P->d_cb, J, ldj);
         HIP_CHECK(hipGetLastError());
     } catch (const HipFail &f) {

@@ -769,6 +769,11 @@ struct eri_plan {
     bool jready = false;
     double *d_ints = nullptr, *d_cb = nullptr;
     int64_t *d_seg = nullptr, *d_eoff = nullptr;
+    // side streams of the multi-block calls (created on first use, default priority)
+    static constexpr int NSIDE = 3;
+    hipStream_t side[NSIDE] = {};
+    hipEvent_t ev_fork = nullptr, ev_side[NSIDE] = {};
+    bool side_ready = false;
 
     template <class T>
     T *alloc(size_t n)
@@ -785,6 +790,14 @@ struct eri_plan {
     }
     ~eri_plan()
     {
+        if (side_ready) {
+            for (int i = 0; i < NSIDE; ++i) {
+                (void)hipStreamSynchronize(side[i]);
+                (void)hipStreamDestroy(side[i]);
+                (void)hipEventDestroy(ev_side[i]);
+            }
+            (void)hipEventDestroy(ev_fork);
+        }
         for (void *p : allocs) (void)hipFree(p);
     }
 };
@@ -1002,6 +1015,51 @@ void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const i
 }
 
 // integrals of quartets [first, first + count) of block B into out
+// Calls over several class blocks of an explicit plan spread the blocks over
+// the caller's stream and the plan's side streams, so that the last waves of
+// one class kernel overlap the first waves of the next; the caller's stream
+// then waits for the side streams.  Blocks of memory-tier classes that use the
+// plan's scratch stay on the caller's stream, one after another.
+bool use_side_streams(const eri_plan *P)
+{
+#ifdef ERI_UNFUSED_SPHERICAL
+    (void)P;
+    return false;  // the unfused path shares one work buffer
+#else
+    return !P->implicit;  // implicit plans expand slots into plan-owned lists
+#endif
+}
+
+void side_fork(eri_plan *P, hipStream_t s)
+{
+    if (!P->side_ready) {
+        for (int i = 0; i < eri_plan::NSIDE; ++i) {
+            HIP_CHECK(hipStreamCreateWithFlags(&P->side[i], hipStreamNonBlocking));
+            HIP_CHECK(hipEventCreateWithFlags(&P->ev_side[i], hipEventDisableTiming));
+        }
+        HIP_CHECK(hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming));
+        P->side_ready = true;
+    }
+    HIP_CHECK(hipEventRecord(P->ev_fork, s));
+    for (int i = 0; i < eri_plan::NSIDE; ++i) HIP_CHECK(hipStreamWaitEvent(P->side[i], P->ev_fork, 0));
+}
+
+void side_join(eri_plan *P, hipStream_t s)
+{
+    for (int i = 0; i < eri_plan::NSIDE; ++i) {
+        HIP_CHECK(hipEventRecord(P->ev_side[i], P->side[i]));
+        HIP_CHECK(hipStreamWaitEvent(s, P->ev_side[i], 0));
+    }
+}
+
+hipStream_t block_stream(const eri_plan *P, const EriBlock &B, int idx, hipStream_t s)
+{
+    const EriClassEntry *ce = find_class(B.cid, kernel_sph(P));
+    if (ce && ce->tier == 'M' && ce->scratch_doubles > 0) return s;
+    const int k = idx % (eri_plan::NSIDE + 1);
+    return k == 0 ? s : P->side[k - 1];
+}
+
 void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t count, double *out, hipStream_t st)
 {
     const int64_t blk = (int64_t)B.na * B.nb * B.nc * B.nd;
@@ -1552,10 +1610,15 @@ extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, doub
     const int64_t end = (b1 < nb) ? P->blocks[b1].out_off : P->nout;
     if (!out || cap < end - base) return out ? ERI_E_CAPACITY : ERI_E_INVALID;
     try {
+        const hipStream_t s = (hipStream_t)stream;
+        const bool side = b1 - b0 > 1 && use_side_streams(P);
+        eri_plan *Pm = const_cast<eri_plan *>(P);
+        if (side) side_fork(Pm, s);
         for (int b = b0; b < b1; ++b) {
             const EriBlock &B = P->blocks[b];
-            compute_range(P, B, 0, B.count, out + (B.out_off - base), (hipStream_t)stream);
+            compute_range(P, B, 0, B.count, out + (B.out_off - base), side ? block_stream(P, B, b - b0, s) : s);
         }
+        if (side) side_join(Pm, s);
     } catch (const HipFail &f) {
         return translate(f);
     }
@@ -1935,26 +1998,26 @@ extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, do
             HIP_CHECK(hipStreamSynchronize(s));
             P->jready = true;
         }
-        // 1. integrals of every block
-        for (int b = 0; b < nb; ++b) {
-            const EriBlock &B = P->blocks[b];
-            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, s, B.n_k1);
-        }
-        // 2. per-quartet contributions
+        // 1. integrals of every block and 2. their per-quartet contributions,
+        // block after block on the caller's and the side streams
+        side_fork(P, s);
         int64_t cbt = 0;
         for (int b = 0; b < nb; ++b) {
             const EriBlock &B = P->blocks[b];
+            const hipStream_t bs = use_side_streams(P) ? block_stream(P, B, b, s) : s;
+            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, bs, B.n_k1);
             const int64_t CH = 1 << 30;
             for (int64_t c = 0; c < B.count; c += CH) {
                 const int64_t m = std::min(CH, B.count - c);
                 const int64_t nab = B.na * B.nb, ncd = B.nc * B.nd, nv = m * (nab + ncd);
-                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, s, nv, B.na, B.nb, B.nc,
+                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, bs, nv, B.na, B.nb, B.nc,
                                    B.nd, P->d_qbra + B.start + c, P->d_qket + B.start + c, P->d_pinfo, P->d_bf,
                                    P->d_ints + B.out_off + c * nab * ncd, D, ldd, P->d_cb + cbt + c * (nab + ncd));
                 HIP_CHECK(hipGetLastError());
             }
             cbt += B.count * (int64_t)(B.na * B.nb + B.nc * B.nd);
         }
+        side_join(P, s);
         // 3. deterministic per-pair reduction into J
         hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(RUN_THREADS), 0, s, (int)P->npairs, P->d_pinfo,
                            P->d_bf, P->d_nfun, P->d_seg, P->d_eoff, P->d_cb, J, ldj);

@@ -139,7 +139,10 @@ int eri_plan_schwarz(const eri_plan *plan, double *dst, void *stream);
 /*
  * Integrals of class blocks [block_begin, block_end) into `out` (device),
  * block b's quartets starting at out + out_offset[b] - out_offset[block_begin].
- * out_capacity is the number of doubles available at `out`.  Asynchronous.
+ * out_capacity is the number of doubles available at `out`.  Asynchronous:
+ * on an explicit plan, several blocks run on `stream` and on side streams the
+ * plan owns, and `stream` waits for them before later work on it starts, so
+ * calls on one plan from several host threads at once must not overlap.
  */
 int eri_compute_batch(const eri_plan *plan, int32_t block_begin, int32_t block_end, double *out,
                       int64_t out_capacity, void *stream);
@@ -158,11 +161,12 @@ int eri_compute_range(const eri_plan *plan, int32_t block, int64_t first, int64_
  * plan's unique quartets with the 8-fold symmetry, D and J dense row-major
  * device matrices of order nbf with leading dimensions ldd, ldj.  D must be
  * symmetric.  J is fully overwritten.  Deterministic, no atomics: each
- * pair's contributions are summed in plan order.  An explicit plan computes
- * all its integrals at once; an implicit plan goes chunk by chunk (integrals,
- * contributions, per-pair sums added to J), so its memory does not grow with
- * the number of quartets.  Asynchronous; the plan keeps work buffers between
- * calls.
+ * pair's contributions are summed in an order fixed by the plan.  An explicit
+ * plan computes all its integrals at once, its class blocks spread over
+ * `stream` and the plan's side streams; an implicit plan goes chunk by chunk
+ * (integrals, contributions, per-pair sums added to J), so its memory does not
+ * grow with the number of quartets.  Asynchronous; the plan keeps work buffers
+ * between calls (the calls on one plan must not overlap).
  */
 int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream);
 

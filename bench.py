@@ -103,6 +103,26 @@ def back_to_back(fn, n, stream):
     return a.elapsed_time(b) / n
 
 
+def clock_under_load(fn, seconds=1.0):
+    """GPU clocks as rocm-smi reports them while fn() runs back to back for about `seconds`."""
+    import threading
+    import torch
+    box = {}
+
+    def poll():
+        time.sleep(seconds / 2)
+        box["clocks"] = gpu_clocks()
+    th = threading.Thread(target=poll)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+    th.join()
+    return box.get("clocks")
+
+
 def gpu_clocks():
     """Current shader and memory clocks as rocm-smi reports them (None if it is unavailable)."""
     import subprocess
@@ -321,11 +341,11 @@ def main():
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
-    smi_before = gpu_clocks()
     times, wall = time_launches(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
-    smi_after = gpu_clocks()
     ms = sum(times) / len(times)
     b2b = back_to_back(lambda: E.compute_batch(plan, out), 100, stream)
+    clocks = clock_under_load(lambda: E.compute_batch(plan, out))
+    fma_tflops = E.fp64_fma_tflops()
     nq = plan.n_quartets
     (per_prim, once), = _class_flops(plan, True)
     flops = nq * (per_prim + once)  # K = 1: one primitive quartet per quartet
@@ -352,7 +372,9 @@ def main():
         "ms_min": min(times),
         "ms_max": max(times),
         "ms_per_launch_100_back_to_back": b2b,
-        "gpu_clocks_before_after": [smi_before, smi_after],
+        "gpu_clocks_under_load": clocks,
+        "fp64_fma_measured_TFLOPs": fma_tflops,
+        "achieved_over_measured_fma": achieved / fma_tflops,
         "output_write_GBps": plan.n_out * 8 / (ms * 1e-3) / 1e9,
         "plan_build_ms": plan_ms,
         "wall_s_timed_region": wall,

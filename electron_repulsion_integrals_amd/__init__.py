@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     compute_range,
     digest_J,
     digest_JK,
+    fp64_fma_tflops,
     load,
     strerror,
 )

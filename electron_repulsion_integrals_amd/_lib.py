@@ -85,6 +85,8 @@ def load(path=None):
     L.eri_compute_deriv.restype = ctypes.c_int
     L.eri_strerror.argtypes = [ctypes.c_int]
     L.eri_strerror.restype = ctypes.c_char_p
+    L.eri_fp64_fma_tflops.argtypes = [ctypes.POINTER(ctypes.c_double), vp]
+    L.eri_fp64_fma_tflops.restype = ctypes.c_int
     L.eri_class_info.argtypes = [ctypes.c_int32, i32p, i32p]
     L.eri_class_info.restype = ctypes.c_int
     _lib_path = path
@@ -244,3 +246,10 @@ def class_info(class_id: int):
 
 def strerror(code: int) -> str:
     return load().eri_strerror(int(code)).decode()
+
+
+def fp64_fma_tflops(stream=None) -> float:
+    """Measured FP64 FMA rate of the current device (TFLOP/s)."""
+    v = ctypes.c_double(0.0)
+    _check(load().eri_fp64_fma_tflops(ctypes.byref(v), _stream_handle(stream)))
+    return v.value

@@ -2060,6 +2060,66 @@ extern "C" const char *eri_strerror(int code)
     }
 }
 
+namespace {
+
+// FP64 FMA issue rate: every lane runs eight independent chains of fused
+// multiply-adds, eight waves per SIMD; the sum is stored so that nothing is
+// dropped.
+constexpr int FMA_CHAINS = 8, FMA_ITERS = 4096;
+
+__global__ void __launch_bounds__(256) k_fma_rate(double *out, double a, double b)
+{
+    double v[FMA_CHAINS];
+#pragma unroll
+    for (int c = 0; c < FMA_CHAINS; ++c) v[c] = threadIdx.x + c;
+    for (int i = 0; i < FMA_ITERS; ++i) {
+#pragma unroll
+        for (int c = 0; c < FMA_CHAINS; ++c) v[c] = fma(v[c], a, b);
+    }
+    double t = 0.0;
+#pragma unroll
+    for (int c = 0; c < FMA_CHAINS; ++c) t += v[c];
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
+}  // namespace
+
+extern "C" int eri_fp64_fma_tflops(double *tflops, void *stream)
+{
+    if (!tflops) return ERI_E_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    double *out = nullptr;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = ERI_OK;
+    try {
+        int dev = 0, ncu = 0;
+        HIP_CHECK(hipGetDevice(&dev));
+        HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
+        const int grid = ncu * 8;  // 256-lane workgroups: 8 per compute unit = 8 waves per SIMD
+        HIP_CHECK(hipMalloc(&out, (size_t)grid * 256 * sizeof(double)));
+        HIP_CHECK(hipEventCreate(&e0));
+        HIP_CHECK(hipEventCreate(&e1));
+        hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, out, 0.999, 1e-3);
+        HIP_CHECK(hipGetLastError());
+        const int reps = 5;
+        HIP_CHECK(hipEventRecord(e0, s));
+        for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, out, 0.999, 1e-3);
+        HIP_CHECK(hipGetLastError());
+        HIP_CHECK(hipEventRecord(e1, s));
+        HIP_CHECK(hipEventSynchronize(e1));
+        float ms = 0.f;
+        HIP_CHECK(hipEventElapsedTime(&ms, e0, e1));
+        const double flop = 2.0 * FMA_CHAINS * FMA_ITERS * (double)grid * 256 * reps;
+        *tflops = flop / (ms * 1e-3) / 1e12;
+    } catch (const HipFail &f) {
+        rc = translate(f);
+    }
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    if (out) (void)hipFree(out);
+    return rc;
+}
+
 extern "C" int eri_class_info(int32_t cid, int32_t *l4, int32_t *tier)
 {
     const EriClassEntry *ce = find_class(cid, true);

@@ -211,6 +211,12 @@ int eri_compute_deriv(const eri_plan *plan, int64_t first, int64_t count, double
 /* Static text for an error code, with the last HIP error for ERI_E_HIP. */
 const char *eri_strerror(int code);
 
+/* Measured FP64 FMA rate of the current device in TFLOP/s (host output):
+ * the denominator the class kernels' FP64 fraction can also be read against,
+ * beside the published peak.  Allocates and frees a small buffer, runs on
+ * `stream` and synchronises it. */
+int eri_fp64_fma_tflops(double *tflops, void *stream);
+
 /* Class metadata: l of (a, b, c, d) and the tier ('V' register, 'M' memory). */
 int eri_class_info(int32_t class_id, int32_t *l4, int32_t *tier);
 

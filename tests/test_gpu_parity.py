@@ -216,6 +216,33 @@ def test_c3_reduced_plan_and_J(eri):
     assert_parity(Jg, Jref, "J")
 
 
+def test_multi_block_call_matches_block_by_block(eri):
+    """A call over all class blocks (blocks spread over the plan's side streams)
+    gives bitwise the integrals of one call per block, on the caller's stream,
+    and repeats bitwise; the first call on a fresh stream sees them complete."""
+    import torch
+    _log("case: multi-block compute_batch vs block by block, 4-atom cluster")
+    w = make_config(3, scale={"natoms": 4})
+    plan = eri.build_quartets(w.shells, 1, None, w.tau)
+    assert plan.n_blocks > 4
+    one = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
+    for b in range(plan.n_blocks):
+        eri.compute_batch(plan, one[int(plan.block_out[b]):], b, b + 1)
+    s = torch.cuda.Stream()
+    outs = []
+    for _ in range(2):
+        o = torch.full((plan.n_out,), float("nan"), dtype=torch.float64, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            eri.compute_batch(plan, o, stream=s)
+            host = o.to("cpu", non_blocking=False)
+        outs.append(host.numpy())
+    torch.cuda.synchronize()
+    ref = one.cpu().numpy()
+    for got in outs:
+        assert np.array_equal(got, ref), "multi-block integrals differ from the block-by-block ones"
+
+
 def test_implicit_plan_matches_explicit(eri):
     """The same screened plan kept implicit (prefix counts, expanded in chunks of
     1000 quartets): identical index map and integrals, J to the bar and

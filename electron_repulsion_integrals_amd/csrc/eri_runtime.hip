@@ -758,13 +758,20 @@ struct eri_plan {
     int64_t chunk_q = 1 << 22;         // quartets per internal chunk
     int *d_cqbra = nullptr, *d_cqket = nullptr;  // chunk lists (plan-owned: calls on one plan do not overlap)
     // chunked J work (implicit plans, built on first use)
-    bool cjready = false;
-    double *d_cints = nullptr, *d_ccb = nullptr;
-    int *d_cek = nullptr, *d_cek2 = nullptr, *d_ruk = nullptr, *d_rlen = nullptr, *d_rst = nullptr, *d_nruns = nullptr;
-    int64_t *d_ceo = nullptr, *d_ceo2 = nullptr;
-    void *d_ctmp = nullptr;
-    size_t ctmp_bytes = 0;
-    double *d_ckv = nullptr, *d_kacc = nullptr;  // K contribution vectors of a chunk; A (K = A + A^T)
+    // chunked J/K work, one set per stream lane (built on first use)
+    struct ChunkLane {
+        double *ints = nullptr, *cb = nullptr;        // integrals and J contribution vectors of a chunk
+        double *kv = nullptr;                         // K contribution vectors of a chunk
+        double *J = nullptr, *A = nullptr;            // lane accumulators (lane 0: the caller's J, d_kacc)
+        int *ek = nullptr, *ek2 = nullptr, *ruk = nullptr, *rlen = nullptr, *rst = nullptr, *nruns = nullptr;
+        int64_t *eo = nullptr, *eo2 = nullptr;
+        int *qbra = nullptr, *qket = nullptr;         // slot lists of an implicit plan's chunk
+        void *tmp = nullptr;
+        size_t tmp_bytes = 0;
+    };
+    std::vector<ChunkLane> clanes;
+    int64_t c_co = 0, c_cb = 0;  // doubles per lane: integrals, contribution vectors
+    double *d_kacc = nullptr;    // A (K = A + A^T)
     // J digestion work (screened plans, built on first use)
     bool jready = false;
     double *d_ints = nullptr, *d_cb = nullptr;
@@ -1000,18 +1007,23 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
 
 // quartet lists of plan slots [s, s + m): the plan's own arrays, or for an
 // implicit plan the chunk buffers after expansion (m <= chunk_q)
-void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const int **qk, hipStream_t st)
+void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const int **qk, hipStream_t st,
+                int *dqb = nullptr, int *dqk = nullptr)
 {
     if (!P->implicit) {
         *qb = P->d_qbra + s;
         *qk = P->d_qket + s;
         return;
     }
+    if (!dqb) {
+        dqb = P->d_cqbra;
+        dqk = P->d_cqket;
+    }
     hipLaunchKernelGGL(k_expand, dim3(nblk(m, 256)), dim3(256), 0, st, s, m, P->nent, P->d_ent_off, P->d_bd, P->nbd,
-                       P->d_porder, P->d_pinfo, P->d_pair_i, P->d_cqbra, P->d_cqket, (int *)nullptr);
+                       P->d_porder, P->d_pinfo, P->d_pair_i, dqb, dqk, (int *)nullptr);
     HIP_CHECK(hipGetLastError());
-    *qb = P->d_cqbra;
-    *qk = P->d_cqket;
+    *qb = dqb;
+    *qk = dqk;
 }
 
 // integrals of quartets [first, first + count) of block B into out
@@ -1077,91 +1089,149 @@ void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t 
 // contribution vectors, entries sorted by target (stable), then each target's
 // run added in entry order.  Chunks go in plan order, so the sums are
 // deterministic.  Used for implicit plans (J) and for K with any plan.
+__global__ void k_add_mat(int n, const double *X, int ldx, double *Y, int ldy)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)n * n) return;
+    const int x = (int)(t / n), y = (int)(t - (int64_t)x * n);
+    Y[(size_t)x * ldy + y] += X[(size_t)x * ldx + y];
+}
+
+// The chunks are spread over stream lanes: the caller's stream and the plan's
+// side streams, each with its own chunk buffers and its own J and A
+// accumulators, chunk i of the plan going to lane i mod (number of lanes)
+// (chunks of memory-tier classes that use the plan's scratch all go to lane
+// 0).  After the lanes join, lanes 1, 2, ... are added into lane 0's J and A
+// in that order, so the sums stay deterministic.
 void digest_JK_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, hipStream_t s)
 {
-    const int64_t CO = int64_t(1) << 27, CB = int64_t(1) << 26;
+#ifdef ERI_UNFUSED_SPHERICAL
+    const int NL = 1;  // the unfused path shares one work buffer
+#else
+    const int NL = eri_plan::NSIDE + 1;
+#endif
     const int64_t CQ = P->chunk_q;
     const int64_t NE = 4 * CQ;  // entries per chunk: two per quartet for J, four for K
-    if (!P->cjready) {
-        P->d_cints = P->alloc<double>(CO);
-        P->d_ccb = P->alloc<double>(CB);
-        P->d_cek = P->alloc<int>(NE);
-        P->d_cek2 = P->alloc<int>(NE);
-        P->d_ceo = P->alloc<int64_t>(NE);
-        P->d_ceo2 = P->alloc<int64_t>(NE);
-        P->d_ruk = P->alloc<int>(NE);
-        P->d_rlen = P->alloc<int>(NE);
-        P->d_rst = P->alloc<int>(NE);
-        P->d_nruns = P->alloc<int>(1);
-        size_t t1 = 0, t2 = 0, t3 = 0;
-        const int n2 = (int)NE;
-        HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0, 32, s));
-        HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns, n2, s));
-        HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, P->d_rlen, P->d_rst, n2, s));
-        P->ctmp_bytes = std::max(t1, std::max(t2, t3));
-        P->d_ctmp = P->alloc<char>(P->ctmp_bytes);
-        P->cjready = true;
-    }
     const int n = P->nbf;
-    if (K && !P->d_kacc) {
-        P->d_ckv = P->alloc<double>(CB);
-        P->d_kacc = P->alloc<double>((size_t)n * n);
+    if (P->clanes.empty()) {
+        // per lane: 2^26 integral doubles and 2^25 contribution doubles (2^27 and 2^26 with one lane)
+        P->c_co = int64_t(1) << (NL > 1 ? 26 : 27);
+        P->c_cb = int64_t(1) << (NL > 1 ? 25 : 26);
+        P->clanes.resize(NL);
+        for (int l = 0; l < NL; ++l) {
+            eri_plan::ChunkLane &W = P->clanes[l];
+            W.ints = P->alloc<double>(P->c_co);
+            W.cb = P->alloc<double>(P->c_cb);
+            W.ek = P->alloc<int>(NE);
+            W.ek2 = P->alloc<int>(NE);
+            W.eo = P->alloc<int64_t>(NE);
+            W.eo2 = P->alloc<int64_t>(NE);
+            W.ruk = P->alloc<int>(NE);
+            W.rlen = P->alloc<int>(NE);
+            W.rst = P->alloc<int>(NE);
+            W.nruns = P->alloc<int>(1);
+            if (P->implicit) {
+                W.qbra = P->alloc<int>(CQ);
+                W.qket = P->alloc<int>(CQ);
+            }
+            size_t t1 = 0, t2 = 0, t3 = 0;
+            const int n2 = (int)NE;
+            HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, s));
+            HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, W.ek2, W.ruk, W.rlen, W.nruns, n2, s));
+            HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, W.rlen, W.rst, n2, s));
+            W.tmp_bytes = std::max(t1, std::max(t2, t3));
+            W.tmp = P->alloc<char>(W.tmp_bytes);
+            if (l > 0) W.J = P->alloc<double>((size_t)n * n);
+        }
     }
-    // sort the n2 entries in d_cek/d_ceo and encode their runs
-    auto sort_runs = [&](int n2) {
-        size_t tb = P->ctmp_bytes;
-        HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(P->d_ctmp, tb, P->d_cek, P->d_cek2, P->d_ceo, P->d_ceo2, n2, 0, 32, s));
-        tb = P->ctmp_bytes;
-        HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(P->d_ctmp, tb, P->d_cek2, P->d_ruk, P->d_rlen, P->d_nruns, n2, s));
-        tb = P->ctmp_bytes;
-        HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(P->d_ctmp, tb, P->d_rlen, P->d_rst, n2, s));
-    };
-    if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, J, ldj);
-    if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->d_kacc, n);
-    HIP_CHECK(hipGetLastError());
+    if (K && !P->d_kacc) {
+        P->d_kacc = P->alloc<double>((size_t)n * n);
+        for (int l = 0; l < NL; ++l) {
+            P->clanes[l].kv = P->alloc<double>(P->c_cb);
+            P->clanes[l].A = l == 0 ? P->d_kacc : P->alloc<double>((size_t)n * n);
+        }
+    }
+    const int64_t CO = P->c_co, CB = P->c_cb;
+    side_fork(P, s);
+    auto lane_stream = [&](int l) { return l == 0 ? s : P->side[l - 1]; };
+    for (int l = 0; l < NL; ++l) {
+        const hipStream_t ls = lane_stream(l);
+        eri_plan::ChunkLane &W = P->clanes[l];
+        double *Jl = l == 0 ? J : W.J;
+        const int ldl = l == 0 ? ldj : n;
+        if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, Jl, ldl);
+        if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, W.A, n);
+        HIP_CHECK(hipGetLastError());
+    }
+    int64_t chunk_index = 0;
     for (const EriBlock &B : P->blocks) {
         const int nab = B.na * B.nb, ncd = B.nc * B.nd;
         const int nkv = B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd;
         const int64_t blk = (int64_t)nab * ncd;
         const int64_t step = std::max<int64_t>(
             1, std::min(std::min(CQ, CO / blk), std::min(CB / (nab + ncd), CB / nkv)));
-        for (int64_t c = 0; c < B.count; c += step) {
+        const EriClassEntry *ce = find_class(B.cid, kernel_sph(P));
+        const bool scratch_class = ce && ce->tier == 'M' && ce->scratch_doubles > 0;
+        for (int64_t c = 0; c < B.count; c += step, ++chunk_index) {
+            const int l = scratch_class ? 0 : (int)(chunk_index % NL);
+            const hipStream_t ls = lane_stream(l);
+            eri_plan::ChunkLane &W = P->clanes[l];
+            double *Jl = l == 0 ? J : W.J;
+            const int ldl = l == 0 ? ldj : n;
             const int64_t m = std::min(step, B.count - c);
             const int *qb = nullptr, *qk = nullptr;
-            slot_lists(P, B.start + c, m, &qb, &qk, s);
+            slot_lists(P, B.start + c, m, &qb, &qk, ls, W.qbra, W.qket);
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
-            launch_class(P, B.cid, qb, qk, m, P->d_cints, s, nk1);
+            launch_class(P, B.cid, qb, qk, m, W.ints, ls, nk1);
+            // sort the n2 entries in W.ek/W.eo and encode their runs
+            auto sort_runs = [&](int n2) {
+                size_t tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, ls));
+                tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
+                tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(W.tmp, tb, W.rlen, W.rst, n2, ls));
+            };
             if (J) {
                 const int64_t nv = m * (nab + ncd);
-                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, s, nv, B.na, B.nb, B.nc,
-                                   B.nd, qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ccb);
-                hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, nab, ncd,
-                                   P->d_cek, P->d_ceo);
+                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, ls, nv, B.na, B.nb,
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb);
+                hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, nab, ncd,
+                                   W.ek, W.eo);
                 HIP_CHECK(hipGetLastError());
                 sort_runs((int)(2 * m));
-                // at most 2m runs; workgroups past the device-side run count exit at once
-                // at most one run per pair key (and one for the sentinel key)
+                // at most one run per pair key (and one for the sentinel key); workgroups
+                // past the device-side run count exit at once
                 const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
-                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, s, P->d_nruns, P->d_ruk,
-                                   P->d_rst, P->d_rlen, P->d_ceo2, P->d_ccb, P->d_pinfo, P->d_bf, P->d_nfun, J, ldj);
+                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
+                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, Jl, ldl);
                 HIP_CHECK(hipGetLastError());
             }
             if (K) {
                 const int64_t nkt = m * nkv;
-                hipLaunchKernelGGL(k_kdigest_rows, dim3((unsigned)nblk(nkt, 256)), dim3(256), 0, s, nkt, B.na, B.nb,
-                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, P->d_cints, D, ldd, P->d_ckv);
-                hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, qb, qk, P->d_pinfo,
-                                   P->nshell, B.na, B.nb, B.nc, B.nd, P->d_cek, P->d_ceo);
+                hipLaunchKernelGGL(k_kdigest_rows, dim3((unsigned)nblk(nkt, 256)), dim3(256), 0, ls, nkt, B.na, B.nb,
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.kv);
+                hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, P->d_pinfo,
+                                   P->nshell, B.na, B.nb, B.nc, B.nd, W.ek, W.eo);
                 HIP_CHECK(hipGetLastError());
                 sort_runs((int)(4 * m));
                 // at most one run per target block key (and one for the sentinel key)
                 const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
-                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, s, P->d_nruns, P->d_ruk,
-                                   P->d_rst, P->d_rlen, P->d_ceo2, P->d_ckv, P->nshell, P->d_bf, P->d_nfun,
-                                   P->d_kacc, n);
+                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk,
+                                   W.rst, W.rlen, W.eo2, W.kv, P->nshell, P->d_bf, P->d_nfun, W.A, n);
                 HIP_CHECK(hipGetLastError());
             }
         }
+    }
+    side_join(P, s);
+    for (int l = 1; l < NL; ++l) {
+        if (J)
+            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->clanes[l].J, n, J,
+                               ldj);
+        if (K)
+            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->clanes[l].A, n,
+                               P->d_kacc, n);
+        HIP_CHECK(hipGetLastError());
     }
     if (K) {
         hipLaunchKernelGGL(k_sym_add, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->d_kacc, n, K, ldk);

@@ -178,9 +178,11 @@ int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, 
  * (order nbf, leading dimension ldj / ldk, device) is fully overwritten.
  * Chunk by chunk: integrals, per-quartet contribution blocks (for K the four
  * blocks (ik), (jk), (il), (jl) of a quartet (ij|kl), contracted with D over
- * the other pair of indices), sorted by target block and added in plan order,
- * then K = A + A^T; deterministic, no atomics.  Asynchronous; the plan keeps
- * work buffers between calls (the calls on one plan must not overlap).
+ * the other pair of indices), sorted by target block and added in an order
+ * fixed by the plan, then K = A + A^T; deterministic, no atomics.  The chunks
+ * are spread over `stream` and the plan's side streams, each with its own
+ * chunk buffers (about 1.8 GB each) and accumulators.  Asynchronous; the plan
+ * keeps work buffers between calls (the calls on one plan must not overlap).
  */
 int eri_digest_JK(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
                   int32_t ldk, void *stream);

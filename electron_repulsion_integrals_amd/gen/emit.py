@@ -1080,10 +1080,22 @@ def _mem_layout(ci: ClassInfo, spherical: bool):
 
 
 LDS_LIMIT_BYTES = 160 * 1024
+# primitive quartets set up together (one lane each) into LDS records
+MEM_CHUNK = 32
+
+
+def mem_rec_fields(ci: ClassInfo) -> int:
+    """Fields of one primitive-quartet record: P-A, W-P, Q-C, W-Q, 1/(2 zeta),
+    1/(2 eta), rho/zeta, rho/eta, 1/(2(zeta+eta)), then F_0..F_L."""
+    return 17 + ci.L + 1
+
+
+def mem_rec_bytes(ci: ClassInfo) -> int:
+    return 8 * mem_rec_fields(ci) * (MEM_CHUNK | 1)
 
 
 def mem_xch_in_lds(ci: ClassInfo, spherical: bool) -> bool:
-    return ci.nket(spherical) * mem_xch_stride(ci) * 8 <= LDS_LIMIT_BYTES
+    return ci.nket(spherical) * mem_xch_stride(ci) * 8 + mem_rec_bytes(ci) <= LDS_LIMIT_BYTES
 
 
 def mem_xch_stride(ci: ClassInfo) -> int:
@@ -1152,6 +1164,9 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     # then the ket-transformed exchange (row kappa, column = bra lane)
     o.append(f"  __shared__ double xl[{mem_lds_total(ci, spherical)}];")
     o.append(f"  constexpr int XS = {XS};")
+    NRM = mem_rec_fields(ci)
+    o.append(f"  constexpr int CHM = {MEM_CHUNK}, RSM = {MEM_CHUNK | 1};")
+    o.append(f"  __shared__ double mrec[{NRM} * RSM];  // field-major records of one chunk of primitive quartets")
     o.append("  const int sub = tid < G ? tid : 0;  // lanes beyond G shadow e = (0,0,0) and never store")
     o.append("  const bool real = tid < G;")
     # Every graph value lives in this workgroup's scratch slice, addressed by
@@ -1183,27 +1198,42 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
     else:
         for t in range(len(targets)):
             o.append(f"  SST({acc0 + t}, 0.0);")
-    # one flat loop over primitive quartets; the next pair records are loaded
-    # while the current primitive quartet is evaluated
+    # primitive quartets in chunks of CHM: lane t < CHM sets up primitive
+    # quartet c0 + t (geometry and Boys values) into an LDS record, then every
+    # lane evaluates the chunk's primitive quartets one after another from
+    # the records (broadcast reads), instead of every lane repeating the set-up
+    rec_vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
+                "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe",
+                "gq.i2ze"] + [f"Fq[{m}]" for m in range(L + 1)]
+    rec_names = ["PAx", "PAy", "PAz", "WPx", "WPy", "WPz", "QCx", "QCy", "QCz", "WQx", "WQy", "WQz",
+                 "i2z", "i2e", "roz", "roe", "i2ze"]
+    assert len(rec_vals) == NRM
     o.append("  const int K4 = pb.w * pk.w;")
-    o.append("  EriPrimPair Pn = eri_load_pp(a.ppd, pb.z), Kn = eri_load_pp(a.ppd, pk.z);")
-    o.append("  for (int pq = 0, ib = 0, ik = 0; pq < K4; ++pq) {")
-    o.append("    {")
-    o.append("      const EriPrimPair P = Pn, K = Kn;")
-    o.append("      if (++ik == pk.w) { ik = 0; ++ib; }")
-    o.append("      if (pq + 1 < K4) { Pn = eri_load_pp(a.ppd, pb.z + ib); Kn = eri_load_pp(a.ppd, pk.z + ik); }")
-    o.append("      EriQuartetGeom g;")
-    o.append("      eri_geom(P, K, ACx, ACy, ACz, g);")
-    o.append("      const double PAx = P.PA[0], PAy = P.PA[1], PAz = P.PA[2];")
-    o.append("      const double WPx = g.WP[0], WPy = g.WP[1], WPz = g.WP[2];")
-    o.append("      const double QCx = K.PA[0], QCy = K.PA[1], QCz = K.PA[2];")
-    o.append("      const double WQx = g.WQ[0], WQy = g.WQ[1], WQz = g.WQ[2];")
-    o.append("      const double i2z = 0.5 * P.izeta, i2e = 0.5 * K.izeta, roz = g.roz, roe = g.roe;")
-    o.append("      const double ehx = ex * g.i2ze, ehy = ey * g.i2ze, ehz = ez * g.i2ze;")
+    o.append("  for (int c0 = 0; c0 < K4; c0 += CHM) {")
+    o.append("    if (tid < CHM && c0 + tid < K4) {")
+    o.append("      const int p = c0 + tid, ib = p / pk.w, ik = p - ib * pk.w;")
+    o.append("      const EriPrimPair P = eri_load_pp(a.ppd, pb.z + ib);")
+    o.append("      const EriPrimPair K = eri_load_pp(a.ppd, pk.z + ik);")
+    o.append("      EriQuartetGeom gq;")
+    o.append("      eri_geom(P, K, ACx, ACy, ACz, gq);")
+    o.append(f"      double Fq[{L + 1}];")
+    o.append(f"      eri_boys<{L}>(gq.T, gq.pref, a.boys, Fq);")
+    o.append("      double* r = mrec + tid;")
+    for fi, v in enumerate(rec_vals):
+        o.append(f"      r[{fi} * RSM] = {v};")
+    o.append("    }")
+    o.append("    __syncthreads();  // the chunk's records are written")
+    o.append("    const int nch = K4 - c0 < CHM ? K4 - c0 : CHM;")
+    o.append("    for (int j = 0; j < nch; ++j) {")
+    o.append("      const double* r = mrec + j;")
+    for fi, nm in enumerate(rec_names):
+        o.append(f"      const double {nm} = r[{fi} * RSM];")
+    o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
     o.append("      (void)PAx; (void)PAy; (void)PAz; (void)WPx; (void)WPy; (void)WPz; (void)QCx; (void)QCy; (void)QCz;")
     o.append("      (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e; (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
     o.append(f"      double F[{L + 1}];")
-    o.append(f"      eri_boys<{L}>(g.T, g.pref, a.boys, F);")
+    for m in range(L + 1):
+        o.append(f"      F[{m}] = r[{17 + m} * RSM];")
     _stage1(ci, kv.base_m, o)
     # ket phase: own values in registers (level order); the coupling operand of
     # level k is read from an LDS buffer holding level k-1's cross-lane values
@@ -1248,7 +1278,7 @@ def emit_memory_tier(ci: ClassInfo, spherical: bool) -> str:
             o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
             if (n.f, n.m) in tpos_all:
                 acc_add(tpos_all[(n.f, n.m)], names.ket((n.f, n.m)))
-    o.append("      __syncthreads();  // all reads of this primitive quartet done before slots are rewritten")
+    o.append("      __syncthreads();  // all reads of this primitive quartet (records, level slots) done")
     o.append("    }")
     o.append("  }")
     # ket HRR and transform per lane, in registers, from the accumulators;

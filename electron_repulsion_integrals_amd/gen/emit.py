@@ -957,13 +957,17 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
 
 def tier_of(ci: ClassInfo) -> str:
     """Register tier whenever a lane group fits one wave (the compiler may keep
-    part of a large live set in AGPRs); memory tier for wider bra groups.  The
-    single-tier ablation variants route every class to one tier."""
+    part of a large live set in AGPRs) or the class fits the one-quartet-per-lane
+    tier; memory tier for the other wider bra groups.  The single-tier ablation
+    variants route every class to one tier."""
     from .variant import CURRENT
+    from .lane import use_lane_tier
     if CURRENT.tiers == "memory":
         return "M"
     if CURRENT.tiers == "lane":
         return "V"
+    if ci.G > 64 and use_lane_tier(ci, True):
+        return "V"  # a wide bra with an s-type ket, small enough for one quartet per lane
     return "V" if ci.G <= 64 else "M"
 
 

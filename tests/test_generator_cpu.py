@@ -378,7 +378,7 @@ def test_ablation_variants_generate(tmp_path):
     emits exactly the product sources."""
     from electron_repulsion_integrals_amd.gen import variant
     from electron_repulsion_integrals_amd.gen.emit import generate
-    cls = [gg.ClassInfo(1, 1, 1, 1), gg.ClassInfo(2, 2, 2, 2), gg.ClassInfo(3, 3, 0, 0)]
+    cls = [gg.ClassInfo(1, 1, 1, 1), gg.ClassInfo(2, 2, 2, 2), gg.ClassInfo(3, 3, 1, 0)]
     srcs = {}
     for name in variant.VARIANTS:
         prev = variant.set_variant(name)

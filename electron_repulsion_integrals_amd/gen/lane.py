@@ -26,6 +26,11 @@ AX = "xyz"
 # accumulators per lane: up to 100 the kernel may drop to one wave per SIMD
 # (VGPRs + AGPRs) and is still faster than the lane-group tiers (measured)
 MAX_ACC = 100
+# bras of total angular momentum 5 or more (56 lanes or more in the lane-group
+# tiers, with long per-lane bra paths): up to 200 accumulators (measured on the
+# 120-atom cluster: (fd|ps), 138 accumulators, 2.4x faster in this tier, while
+# (dp|pp), 144 accumulators and a 20-lane bra, is 8% slower here)
+MAX_ACC_WIDE_BRA = 200
 MAX_LIVE = 96      # scheduled peak of recurrence values (doubles) besides the accumulators
 
 
@@ -112,7 +117,7 @@ def use_lane_tier(ci: ClassInfo, spherical: bool) -> bool:
     if CURRENT.tiers == "lane":
         return True
     nacc = ci.n_ebra * len(build_ket_vrr(ci.lc, ci.Lk).targets)
-    if nacc > MAX_ACC or ci.L > 6:
+    if nacc > (MAX_ACC_WIDE_BRA if ci.Lb >= 5 else MAX_ACC) or ci.L > 7:
         return False
     return lane_peak(ci) <= MAX_LIVE
 

@@ -127,12 +127,14 @@ def gpu_clocks():
     """Current shader and memory clocks as rocm-smi reports them (None if it is unavailable)."""
     import subprocess
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
         d = json.loads(r.stdout)
     except Exception:
         return None
     card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
-    return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()} or None
+    keep = ("sclk", "mclk", "power")
+    return {k: v for k, v in card.items() if any(x in k.lower() for x in keep)} or None
 
 
 def _block_flops(plan, w, imap):
@@ -175,14 +177,21 @@ def per_class(E, plan, w, steps, stream):
     return res
 
 
-def j_build(E, w, steps, stream):
+def j_build(E, w, steps, stream, spherical=True):
     """Screened plan (pairs, Schwarz, sort) + J digestion for a cluster workload."""
+    import numpy as np
     import torch
     t0 = time.perf_counter()
-    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, None, w.tau)
+    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL if spherical else 0, None, w.tau)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
-    D = torch.tensor(w.density, device="cuda")
+    if spherical:
+        D = torch.tensor(w.density, device="cuda")
+    else:
+        # a density of the Cartesian basis, drawn the same way as the spherical one
+        rng = np.random.default_rng(1003)
+        C = rng.standard_normal((plan.nbf, plan.nbf // 4))
+        D = torch.tensor(C @ C.T, device="cuda")
     J = torch.empty_like(D)
     times, _ = time_launches(lambda: E.digest_J(plan, D, J), steps, 1, stream)
     dig = sorted(times)[len(times) // 2]
@@ -385,6 +394,9 @@ def main():
         w3 = make_config(3)
         plan3, jb = j_build(E, w3, 5, stream)
         res["j_build_30atom_svp"] = jb
+        plan3c, jbc = j_build(E, w3, 5, stream, spherical=False)
+        del plan3c
+        res["j_build_30atom_svp_cartesian"] = jbc
         res["per_class"]["30-atom SVP-like cluster"] = per_class(E, plan3, w3, 3, stream)
         res["derivatives_30atom_svp"] = deriv_sampled(E, plan3, w3)
         del plan3

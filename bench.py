@@ -30,19 +30,24 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per launch of the (dd|dd) K = 1 kernel from two rocprofv3 --pmc
 # passes (FETCH_SIZE, WRITE_SIZE in KiB per dispatch), scaled by what the same
 # counters read for a 1 GiB device copy (x2.0 and x1.0).  Valid only for the
-# kernel source they were taken on: reported as null once it changes.
-TRAFFIC = {"kernel_source": "electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
-           "sha1": "370fa55ba2928d4761b65588a92901604c1e9d8c",
+# kernel sources they were taken on (generated class source and device header):
+# reported as null once either changes.
+TRAFFIC = {"kernel_sources": ["electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
+                              "electron_repulsion_integrals_amd/csrc/eri_device.h"],
+           "sha1": "7133952ee44e37b31e287f3dda9c1e75e6018fef",
            "fetch_kib": 5006.68, "fetch_scale": 2.0, "write_kib": 97818.63, "write_scale": 1.0}
 
 
 def measured_traffic():
     import hashlib
+    h = hashlib.sha1()
     try:
-        with open(os.path.join(ROOT, TRAFFIC["kernel_source"]), "rb") as f:
-            if hashlib.sha1(f.read()).hexdigest() != TRAFFIC["sha1"]:
-                return None
+        for src in TRAFFIC["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
     except OSError:
+        return None
+    if h.hexdigest() != TRAFFIC["sha1"]:
         return None
     return 1024.0 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"])
 

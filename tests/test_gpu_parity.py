@@ -455,6 +455,14 @@ def test_c3_full_size_plan_and_sampled_J(eri):
     twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau)
     np.testing.assert_array_equal(imap, twin["index_map"])
     _log(f"  plan: {plan.n_quartets} quartets in {plan.n_blocks} class blocks")
+    # unique quartets whose Schwarz product lies within 1e-9 (relative) of tau^2, where
+    # the keep/drop decision would be sensitive to the last digits of S
+    Ss = np.sort(S_gpu)
+    t2 = w.tau * w.tau
+    lo = np.searchsorted(Ss, t2 * (1 - 1e-9) / np.maximum(Ss, 1e-300), side="left")
+    hi = np.searchsorted(Ss, t2 * (1 + 1e-9) / np.maximum(Ss, 1e-300), side="right")
+    near = int(np.sum(np.maximum(hi - lo, 0)))
+    _log(f"  ordered pair-pair products within 1e-9 of tau^2: {near}")
     out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
     eri.compute_batch(plan, out)
     D = torch.tensor(w.density, device="cuda")

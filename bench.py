@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # reported as null once either changes.
 TRAFFIC = {"kernel_sources": ["electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
                               "electron_repulsion_integrals_amd/csrc/eri_device.h"],
-           "sha1": "7133952ee44e37b31e287f3dda9c1e75e6018fef",
-           "fetch_kib": 5006.68, "fetch_scale": 2.0, "write_kib": 97818.63, "write_scale": 1.0}
+           "sha1": "08a779daafca427b33fdeae2cf08013a7832398c",
+           "fetch_kib": 5006.13, "fetch_scale": 2.0, "write_kib": 97817.92, "write_scale": 1.0}
 
 
 def measured_traffic():
@@ -317,7 +317,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads and the extra launches (back to back, clocks, FMA rate)")
     ap.add_argument("--only-j-build", action="store_true",
                     help="only the 30-atom cluster: J build and per-class times (for profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -357,9 +358,11 @@ def main():
     out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
     times, wall = time_launches(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
     ms = sum(times) / len(times)
-    b2b = back_to_back(lambda: E.compute_batch(plan, out), 100, stream)
-    clocks = clock_under_load(lambda: E.compute_batch(plan, out))
-    fma_tflops = E.fp64_fma_tflops()
+    b2b = clocks = fma_tflops = None
+    if not a.no_extra:  # extra launches would also enter a profiler's per-kernel average
+        b2b = back_to_back(lambda: E.compute_batch(plan, out), 100, stream)
+        clocks = clock_under_load(lambda: E.compute_batch(plan, out))
+        fma_tflops = E.fp64_fma_tflops()
     nq = plan.n_quartets
     (per_prim, once), = _class_flops(plan, True)
     flops = nq * (per_prim + once)  # K = 1: one primitive quartet per quartet
@@ -388,7 +391,7 @@ def main():
         "ms_per_launch_100_back_to_back": b2b,
         "gpu_clocks_under_load": clocks,
         "fp64_fma_measured_TFLOPs": fma_tflops,
-        "achieved_over_measured_fma": achieved / fma_tflops,
+        "achieved_over_measured_fma": achieved / fma_tflops if fma_tflops else None,
         "output_write_GBps": plan.n_out * 8 / (ms * 1e-3) / 1e9,
         "plan_build_ms": plan_ms,
         "wall_s_timed_region": wall,

@@ -328,7 +328,10 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
     o.append("}  // namespace")
     o.append(f"// {Q} quartets per workgroup of {NT} lanes ({Q * G} busy); ket coupling through LDS, level by level")
-    o.append(f"__global__ void __launch_bounds__({NT}) eri_kernel_{tag}(EriClassArgs a)")
+    # at least two waves per SIMD: (dd|dd), (fp|dd) and (fp|fp) otherwise take a
+    # few registers over 256 and run at one; capped, they spill a few values and
+    # measured 20-30% faster
+    o.append(f"__global__ void __launch_bounds__({NT}, 2) eri_kernel_{tag}(EriClassArgs a)")
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NT = {NT}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append(f"  constexpr int CH = {CH}, NRL = {NRL}, NC = {max(NC, 1)};")

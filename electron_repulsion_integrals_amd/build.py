@@ -123,7 +123,8 @@ def build(lmax: int = 4, jobs: int | None = None, use_cache: bool = True, verbos
 
 
 def resource_report(lmax: int = 4, jobs: int | None = None):
-    """Per-kernel VGPR/AGPR/scratch/LDS/occupancy from the compiler's resource remarks."""
+    """Per-kernel VGPR/AGPR/scratch/LDS/occupancy from the compiler's resource remarks:
+    {source file: {kernel symbol: {remark: value}}}."""
     import re
     from electron_repulsion_integrals_amd.gen.emit import generate
     files, entries = generate(GEN_DIR, lmax=lmax)
@@ -132,17 +133,21 @@ def resource_report(lmax: int = 4, jobs: int | None = None):
     def one(src):
         r = subprocess.run([HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", os.devnull],
                            capture_output=True, text=True)
-        info = {}
+        kernels, info = {}, None
         for line in r.stderr.splitlines():
             m = re.search(r"remark:\s+([A-Za-z \[\]/]+?):\s+(\S+)\s+\[-Rpass", line)
             if m:
-                info[m.group(1).strip()] = m.group(2)
-        return os.path.basename(src), info
+                key, val = m.group(1).strip(), m.group(2)
+                if key == "Function Name":  # each kernel's remarks start with its name
+                    info = kernels.setdefault(val, {})
+                if info is not None:
+                    info[key] = val
+        return os.path.basename(src), kernels
 
     out = {}
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        for name, info in ex.map(one, files[:-1]):
-            out[name] = info
+        for name, kernels in ex.map(one, files[:-1]):
+            out[name] = kernels
     return out, entries
 
 

@@ -399,6 +399,8 @@ def emit_register_tier(ci: ClassInfo, spherical: bool) -> str:
         out += emit_lane_tier(ci, spherical, False)
         out += emit_lane_tier(ci, spherical, True)
         return "\n".join(out) + "\n"
+    # a lane group wider than a wave exists only as a packed multi-wave workgroup
+    assert ci.G <= 64 or (use_packed_contracted(ci, spherical) and use_packed_k1(ci, spherical)), ci
     if use_packed_contracted(ci, spherical):
         out += emit_packed_contracted(ci, spherical)
     else:
@@ -962,6 +964,7 @@ def tier_of(ci: ClassInfo) -> str:
     variants route every class to one tier."""
     from .variant import CURRENT
     from .lane import use_lane_tier
+    from .packed import wide_packed
     if CURRENT.tiers == "memory":
         return "M"
     if CURRENT.tiers == "lane":
@@ -973,6 +976,8 @@ def tier_of(ci: ClassInfo) -> str:
         # faster ((fd|fd): 3.46 -> 2.94 ms for a K = 2 batch); with shorter kets
         # it measured 20-60% slower
         return "M"
+    if wide_packed(ci):
+        return "V"  # 84-lane bras with kets up to l = 5: packed four-wave workgroups
     return "V" if ci.G <= 64 else "M"
 
 

@@ -37,6 +37,20 @@ PACK_WAVES = 2
 PACK_RB = 8
 
 
+def wide_packed(ci: ClassInfo) -> bool:
+    """84-lane bras (la + lb = 6: the (ff| and (gd| bras) with a ket recurrence
+    of total angular momentum 1..5: both kernels run three quartets on four
+    waves (252 of 256 lanes) instead of going to the memory tier.  Measured on
+    the 120-atom cluster: (ff|ps) .. (ff|fp) 1.5-1.9x faster, (ff|fd) 17%
+    faster even at one workgroup per compute unit.  An l = 6 ket needs more
+    LDS than a compute unit holds."""
+    return ci.G == 84 and 1 <= ci.Lk <= 5
+
+
+def packed_k1_waves(ci: ClassInfo) -> int:
+    return 4 if wide_packed(ci) else PACK_WAVES
+
+
 def packed_shape(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES):
     """(W, Q, NT): waves per workgroup, quartets per workgroup, threads."""
     NT = 64 * waves
@@ -64,7 +78,10 @@ def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb
 
 
 def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
-    """Packing pays where a wave64 would leave many lanes idle."""
+    """Packing pays where a wave64 would leave many lanes idle, and a lane
+    group wider than a wave needs it."""
+    if wide_packed(ci):
+        return packed_wg_per_cu(ci, spherical, packed_k1_waves(ci)) >= 1
     if ci.G > 64 or ci.G < 20:
         return False
     if (64 % ci.G) * 4 < 64:  # at most a quarter of the wave idles already
@@ -80,9 +97,40 @@ def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb
     return int(min(by_lds, 8 // waves))
 
 
-def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB, wg_per_cu: int = 0,
+def _lane_table(ci: ClassInfo, tag: str):
+    """Constant table of the lane group (one entry per bra component e, packed
+    into an int) and the lines that decode this lane's entry: e = (ex, ey, ez)
+    and srcx/srcy/srcz, the lanes of e - 1_x, e - 1_y, e - 1_z in the same
+    quartet (the lane itself where the component is 0).  Groups of up to 63
+    lanes use 4-bit components and 6-bit source fields; wider groups (up to 127
+    lanes, components up to 7) use 3-bit components and 7-bit fields."""
+    lanes = ci.lanes
+    G = len(lanes)
+    lpos = {e: i for i, e in enumerate(lanes)}
+    wide = G >= 64
+    assert G <= 127 and (not wide or max(max(e) for e in lanes) <= 7)
+    eb, sb = (3, 7) if wide else (4, 6)
+    tab = []
+    for e in lanes:
+        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
+        v = e[0] | (e[1] << eb) | (e[2] << 2 * eb)
+        for ax in range(3):
+            v |= (d[ax] + 1) << (3 * eb + ax * sb)
+        tab.append(v)
+    decl = f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in tab) + "};"
+    em, sm = (1 << eb) - 1, (1 << sb) - 1
+    dec = [f"  const int lt = k_{tag}_lane[sub];",
+           f"  const int ex = lt & {em}, ey = (lt >> {eb}) & {em}, ez = (lt >> {2 * eb}) & {em}, es = ex + ey + ez;",
+           "  const int qb = qi * G;"]
+    for ax, nm in enumerate("xyz"):
+        dec.append(f"  const int src{nm} = e{nm} > 0 ? qb + ((lt >> {3 * eb + ax * sb}) & {sm}) - 1 : tid;")
+    return decl, dec
+
+
+def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PACK_RB, wg_per_cu: int = 0,
                    min_waves: int = 0):
     """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
+    waves = waves or packed_k1_waves(ci)
     from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
     kv = build_ket_vrr(ci.lc, ci.Lk)
     names = Names("V", kv, ci.Lk)
@@ -97,12 +145,7 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     L = ci.L
     cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
     tag = f"c{cid}_{'s' if spherical else 'c'}_k1"
-    lanes = ci.lanes
-    lpos = {e: i for i, e in enumerate(lanes)}
-    lane_tab = []
-    for e in lanes:
-        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
-        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
+    lane_decl, lane_dec = _lane_table(ci, tag)
     lv = _levels(kv)
     levels = sorted(lv)
     NC = max((len(v) for v in lv.values()), default=0)
@@ -117,7 +160,7 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     NU = max(2 * NC * NT, NX)
     o = []
     o.append("namespace {")
-    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
+    o.append(lane_decl)
     o.append("}  // namespace")
     o.append(f"// {Q} quartets per workgroup of {NT} lanes ({Q * G} busy); ket coupling through LDS, level by level")
     lb = f"{NT}, {min_waves}" if min_waves else f"{NT}"
@@ -134,12 +177,7 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: 
     o.append("  int qi = tid / G, sub = tid - qi * G;")
     o.append("  const bool real = qi < Q;")
     o.append("  if (!real) { qi = 0; sub = 0; }  // spare lanes shadow e = (0,0,0) of the first quartet")
-    o.append(f"  const int lt = k_{tag}_lane[sub];")
-    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
-    o.append("  const int qb = qi * G;")
-    o.append("  const int srcx = ex > 0 ? qb + ((lt >> 12) & 63) - 1 : tid;")
-    o.append("  const int srcy = ey > 0 ? qb + ((lt >> 18) & 63) - 1 : tid;")
-    o.append("  const int srcz = ez > 0 ? qb + ((lt >> 24) & 63) - 1 : tid;")
+    o += lane_dec
     o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
@@ -255,9 +293,21 @@ def _chunk(Q, NT, ch=PACK_CH):
     return max(1, min(ch, NT // Q))
 
 
-def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH) -> int:
+def packed_contracted_waves(ci: ClassInfo) -> int:
+    """Waves per workgroup of the contracted kernel.  Measured on the 120-atom
+    cluster's class blocks: 35-lane bras with kets up to l = 3 run 5-10% faster
+    with four waves (seven quartets, 245 of 256 lanes busy) than with two (three
+    quartets, 105 of 128); with an l = 4 ket the level buffers then leave room
+    for one workgroup per compute unit only, and two waves stay faster.  Three
+    waves measured slower throughout."""
+    if (ci.G == 35 and ci.Lk <= 3) or wide_packed(ci):
+        return 4
+    return PACK_WAVES
+
+
+def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = PACK_CH) -> int:
     kv = build_ket_vrr(ci.lc, ci.Lk)
-    W, Q, NT = packed_shape(ci, spherical, waves)
+    W, Q, NT = packed_shape(ci, spherical, waves or packed_contracted_waves(ci))
     ch = _chunk(Q, NT, ch)
     NC = max((len(v) for v in _levels(kv).values()), default=0)
     NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
@@ -265,22 +315,28 @@ def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PAC
     return 8 * (max(2 * NC * NT, NX) + NR * ((ch * Q) | 1)) + 4 * Q
 
 
-def packed_contracted_wg_per_cu(ci: ClassInfo, spherical: bool) -> int:
-    return int(min(LDS_BYTES // packed_contracted_lds_bytes(ci, spherical), 8 // PACK_WAVES))
+def packed_contracted_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = 0) -> int:
+    waves = waves or packed_contracted_waves(ci)
+    return int(min(LDS_BYTES // packed_contracted_lds_bytes(ci, spherical, waves), 8 // waves))
 
 
 def use_packed_contracted(ci: ClassInfo, spherical: bool) -> bool:
     """Measured on the 30-atom cluster: packing pays for 35-lane bras always,
     and for 20- and 10-lane bras once there is a ket recurrence whose
-    coupling reads move from ds_bpermute to the level buffers."""
+    coupling reads move from ds_bpermute to the level buffers.  A 56-lane bra
+    fills a wave almost as well with one quartet per wave, but the level
+    buffers still beat ds_bpermute there: 10-16% on the 120-atom cluster's
+    (fd|pp) .. (fd|fp) blocks."""
+    if wide_packed(ci):
+        return packed_contracted_wg_per_cu(ci, spherical) >= 1
     if ci.Lk > 4:
         return False
-    if not (ci.G == 35 or (ci.G in (20, 10) and ci.Lk >= 1)):
+    if not (ci.G == 35 or (ci.G in (20, 10, 56) and ci.Lk >= 1)):
         return False
     return packed_contracted_wg_per_cu(ci, spherical) >= 2
 
 
-def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, ch: int = PACK_CH):
+def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = PACK_CH):
     """General (contracted) kernel, Q quartets per workgroup of `waves` waves.
 
     Algorithm 2 of "FusionRCG": the primitive quartets of each quartet are set
@@ -295,8 +351,8 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     kv = build_ket_vrr(ci.lc, ci.Lk)
     names = Names("V", kv, ci.Lk)
     G = ci.G
+    waves = waves or packed_contracted_waves(ci)
     W, Q, NT = packed_shape(ci, spherical, waves)
-    wg_per_cu = packed_contracted_wg_per_cu(ci, spherical)
     NK = ci.nket(spherical)
     NEB = ci.n_ebra
     EOFF = ci.e_bra_offset
@@ -304,12 +360,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     L = ci.L
     cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
     tag = f"c{cid}_{'s' if spherical else 'c'}"
-    lanes = ci.lanes
-    lpos = {e: i for i, e in enumerate(lanes)}
-    lane_tab = []
-    for e in lanes:
-        d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
-        lane_tab.append(e[0] | (e[1] << 4) | (e[2] << 8) | ((d[0] + 1) << 12) | ((d[1] + 1) << 18) | ((d[2] + 1) << 24))
+    lane_decl, lane_dec = _lane_table(ci, tag)
     lv = _levels(kv)
     levels = sorted(lv)
     NC = max((len(v) for v in lv.values()), default=0)
@@ -325,7 +376,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     tpos = {f: t for t, (f, m) in enumerate(targets)}
     o = []
     o.append("namespace {")
-    o.append(f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in lane_tab) + "};")
+    o.append(lane_decl)
     o.append("}  // namespace")
     o.append(f"// {Q} quartets per workgroup of {NT} lanes ({Q * G} busy); ket coupling through LDS, level by level")
     # at least two waves per SIMD: (dd|dd), (fp|dd) and (fp|fp) otherwise take a
@@ -343,12 +394,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = PACK_WAV
     o.append("  int qi = tid / G, sub = tid - qi * G;")
     o.append("  const bool real = qi < Q;")
     o.append("  if (!real) { qi = 0; sub = 0; }  // spare lanes shadow e = (0,0,0) of the first quartet")
-    o.append(f"  const int lt = k_{tag}_lane[sub];")
-    o.append("  const int ex = lt & 15, ey = (lt >> 4) & 15, ez = (lt >> 8) & 15, es = ex + ey + ez;")
-    o.append("  const int qb = qi * G;")
-    o.append("  const int srcx = ex > 0 ? qb + ((lt >> 12) & 63) - 1 : tid;")
-    o.append("  const int srcy = ey > 0 ? qb + ((lt >> 18) & 63) - 1 : tid;")
-    o.append("  const int srcz = ez > 0 ? qb + ((lt >> 24) & 63) - 1 : tid;")
+    o += lane_dec
     o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
     o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
     _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)

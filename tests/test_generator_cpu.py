@@ -158,8 +158,9 @@ def test_tier_routing():
 
 
 def test_packed_k1_routing_and_shapes():
-    """Classes whose bra spans 35 lanes run the uncontracted kernel with several
-    quartets per workgroup; the lane layout, record batch and LDS plan fit."""
+    """Classes whose bra spans 35 lanes, and 84-lane bras with a short ket, run
+    the uncontracted kernel with several quartets per workgroup; the lane
+    layout, record batch and LDS plan fit."""
     from electron_repulsion_integrals_amd.gen import packed as P
     from electron_repulsion_integrals_amd.gen.emit import emit_register_tier
     used = []
@@ -168,14 +169,71 @@ def test_packed_k1_routing_and_shapes():
             if not P.use_packed_k1(c, sph):
                 continue
             used.append((c.la, c.lb, c.lc, c.ld))
-            W, Q, NT = P.packed_shape(c, sph)
-            assert c.G == 35 and Q * c.G <= NT and P.PACK_RB * Q <= NT
-            assert P.packed_lds_bytes(c, sph) * P.packed_wg_per_cu(c, sph) <= P.LDS_BYTES
+            W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
+            assert c.G in (35, 84) and Q * c.G <= NT and P.PACK_RB * Q <= NT
+            assert W == (4 if c.G == 84 else 2)
+            assert 1 <= P.packed_wg_per_cu(c, sph, W) and \
+                P.packed_lds_bytes(c, sph, W) * P.packed_wg_per_cu(c, sph, W) <= P.LDS_BYTES
             src = emit_register_tier(c, sph)
             if "lane tier" not in src.splitlines()[0]:
                 assert f"__launch_bounds__({NT})" in src and "xu[" in src
-    assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used
-    assert all(sum(u[:2]) == 4 and sum(u[2:]) <= 4 for u in used)
+    assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
+    assert all(sum(u[:2]) in (4, 6) and sum(u[2:]) <= (5 if sum(u[:2]) == 6 else 4) for u in used)
+
+
+
+def test_packed_contracted_routing_and_shapes():
+    """Contracted classes whose bra spans 20, 35, 56 or 84 lanes (with a ket
+    recurrence, outside the one-quartet-per-lane tier) run several quartets per multi-wave workgroup: the quartets,
+    the set-up chunk and the LDS plan fit, and the emitted kernel has the
+    planned shape."""
+    from electron_repulsion_integrals_amd.gen import packed as P
+    from electron_repulsion_integrals_amd.gen.emit import emit_register_tier, tier_of
+    from electron_repulsion_integrals_amd.gen.lane import use_lane_tier
+    used = {}
+    for c in gg.all_classes(4):
+        if tier_of(c) != "V" or use_lane_tier(c, True):
+            continue
+        for sph in (False, True):
+            if not P.use_packed_contracted(c, sph):
+                continue
+            W = P.packed_contracted_waves(c)
+            _, Q, NT = P.packed_shape(c, sph, W)
+            ch = P._chunk(Q, NT)
+            assert Q >= 1 and Q * c.G <= NT and ch * Q <= NT
+            assert 1 <= P.packed_contracted_wg_per_cu(c, sph) and \
+                P.packed_contracted_lds_bytes(c, sph) * P.packed_contracted_wg_per_cu(c, sph) <= P.LDS_BYTES
+            src = emit_register_tier(c, sph)
+            assert f"__launch_bounds__({NT}, 2)" in src and f"dim3({NT})" in src
+            used[(c.la, c.lb, c.lc, c.ld)] = (c.G, W, Q)
+    assert used[(2, 2, 2, 1)] == (35, 4, 7) and used[(2, 2, 2, 2)] == (35, 2, 3)
+    assert used[(3, 2, 2, 1)] == (56, 2, 2) and used[(2, 1, 2, 1)] == (20, 2, 6)
+    assert used[(3, 3, 1, 0)] == (84, 4, 3) and used[(4, 2, 4, 0)] == (84, 4, 3) and used[(3, 3, 3, 2)] == (84, 4, 3)
+    assert (3, 3, 3, 3) not in used and (3, 2, 3, 2) not in used
+    assert all(v[0] in (10, 20, 35, 56, 84) for v in used.values())
+
+
+def test_packed_lane_table_decodes():
+    """The packed kernels' lane table (4-bit components and 6-bit source lanes
+    below 64 lanes, 3-bit and 7-bit from 64 on) decodes to each lane's bra
+    component and the lanes of its lower neighbours."""
+    import re
+    from electron_repulsion_integrals_amd.gen import packed as P
+    from electron_repulsion_integrals_amd.gen.cartesian import sub
+    for c in (gg.ClassInfo(2, 2, 1, 1), gg.ClassInfo(3, 2, 2, 1), gg.ClassInfo(3, 3, 1, 0)):
+        decl, dec = P._lane_table(c, "t")
+        tab = [int(v) for v in re.search(r"\{(.*)\}", decl).group(1).split(",")]
+        em, eb = [(int(m), int(b)) for m, b in [re.search(r"ey = \(lt >> (\d+)\) & (\d+)", dec[1]).groups()[::-1]]][0]
+        sh = [int(x) for x in re.findall(r"\(lt >> (\d+)\) & \d+\) - 1", "\n".join(dec))]
+        sm = int(re.search(r"\) & (\d+)\) - 1", dec[3]).group(1))
+        lpos = {e: i for i, e in enumerate(c.lanes)}
+        assert len(tab) == c.G
+        for i, e in enumerate(c.lanes):
+            v = tab[i]
+            assert (v & em, (v >> eb) & em, (v >> 2 * eb) & em) == e
+            for ax in range(3):
+                want = lpos[sub(e, ax)] + 1 if e[ax] > 0 else 0
+                assert (v >> sh[ax]) & sm == want
 
 
 def _apply_ops(ops, base_val, R):
@@ -378,12 +436,16 @@ def test_ablation_variants_generate(tmp_path):
     emits exactly the product sources."""
     from electron_repulsion_integrals_amd.gen import variant
     from electron_repulsion_integrals_amd.gen.emit import generate
-    cls = [gg.ClassInfo(1, 1, 1, 1), gg.ClassInfo(2, 2, 2, 2), gg.ClassInfo(3, 3, 1, 0)]
+    # (pp|pp) and (dd|dd) in the lane-group tiers, (ff|ps) packed on four waves,
+    # (fd|fd) in the memory tier; the lane-only variants skip (fd|fd), whose
+    # one-quartet-per-lane graph takes minutes to schedule
+    cls = [gg.ClassInfo(1, 1, 1, 1), gg.ClassInfo(2, 2, 2, 2), gg.ClassInfo(3, 3, 1, 0), gg.ClassInfo(3, 2, 3, 2)]
     srcs = {}
     for name in variant.VARIANTS:
         prev = variant.set_variant(name)
         try:
-            files, entries = generate(str(tmp_path / name), lmax=4, classes=cls)
+            use = cls[:3] if variant.VARIANTS[name].tiers == "lane" else cls
+            files, entries = generate(str(tmp_path / name), lmax=4, classes=use)
         finally:
             variant.set_variant(prev)
         tiers = [t for (_, _, _, t, _) in entries]
@@ -393,7 +455,7 @@ def test_ablation_variants_generate(tmp_path):
             assert set(tiers) == {"V"}
             assert all("one quartet per lane" in open(f).read() for f in files[:-1])
         else:
-            assert tiers == ["V", "V", "V", "V", "M", "M"]
+            assert tiers == ["V"] * 6 + ["M"] * 2
         srcs[name] = {os.path.basename(f): open(f).read() for f in files}
     assert srcs["no_dsa"]["eri_c5_s.hip"] != srcs["full"]["eri_c5_s.hip"]
     assert srcs["lane_alg1"]["eri_c5_s.hip"] != srcs["lane_only"]["eri_c5_s.hip"]

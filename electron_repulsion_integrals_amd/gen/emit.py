@@ -977,7 +977,7 @@ def tier_of(ci: ClassInfo) -> str:
         # it measured 20-60% slower
         return "M"
     if wide_packed(ci):
-        return "V"  # 84-lane bras with kets up to l = 5: packed four-wave workgroups
+        return "V"  # 84- and 120-lane bras with kets up to l = 5: packed multi-wave workgroups
     return "V" if ci.G <= 64 else "M"
 
 

@@ -38,17 +38,26 @@ PACK_RB = 8
 
 
 def wide_packed(ci: ClassInfo) -> bool:
-    """84-lane bras (la + lb = 6: the (ff| and (gd| bras) with a ket recurrence
-    of total angular momentum 1..5: both kernels run three quartets on four
-    waves (252 of 256 lanes) instead of going to the memory tier.  Measured on
-    the 120-atom cluster: (ff|ps) .. (ff|fp) 1.5-1.9x faster, (ff|fd) 17%
-    faster even at one workgroup per compute unit.  An l = 6 ket needs more
-    LDS than a compute unit holds."""
-    return ci.G == 84 and 1 <= ci.Lk <= 5
+    """Lane groups wider than a wave with a ket recurrence of total angular
+    momentum 1..5 run both kernels as packed multi-wave workgroups instead of
+    going to the memory tier:
+      84-lane bras (la + lb = 6: (ff|, (gd|): three quartets on four waves
+        (252 of 256 lanes).  Measured on the 120-atom cluster: (ff|ps) .. (ff|fp)
+        1.5-1.9x faster, (ff|fd) 17% faster even at one workgroup per compute
+        unit.  An l = 6 ket needs more LDS than a compute unit holds.
+      120-lane bras (la + lb = 7: (gf|): one quartet on two waves (120 of 128
+        lanes).  Measured on K = 2 batches: 1.34-1.40x faster with p and d kets,
+        1.17-1.24x with l = 4 and (gf|gp), 1.03x with (gf|fd); l = 6 kets tie
+        and stay in the memory tier."""
+    return ci.G in (84, 120) and 1 <= ci.Lk <= 5
+
+
+def _wide_waves(ci: ClassInfo) -> int:
+    return 4 if ci.G == 84 else 2
 
 
 def packed_k1_waves(ci: ClassInfo) -> int:
-    return 4 if wide_packed(ci) else PACK_WAVES
+    return _wide_waves(ci) if wide_packed(ci) else PACK_WAVES
 
 
 def packed_shape(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES):
@@ -300,7 +309,9 @@ def packed_contracted_waves(ci: ClassInfo) -> int:
     quartets, 105 of 128); with an l = 4 ket the level buffers then leave room
     for one workgroup per compute unit only, and two waves stay faster.  Three
     waves measured slower throughout."""
-    if (ci.G == 35 and ci.Lk <= 3) or wide_packed(ci):
+    if wide_packed(ci):
+        return _wide_waves(ci)
+    if ci.G == 35 and ci.Lk <= 3:
         return 4
     return PACK_WAVES
 

@@ -158,7 +158,7 @@ def test_tier_routing():
 
 
 def test_packed_k1_routing_and_shapes():
-    """Classes whose bra spans 35 lanes, and 84-lane bras with a short ket, run
+    """Classes whose bra spans 35 lanes, and 84- and 120-lane bras with a short ket, run
     the uncontracted kernel with several quartets per workgroup; the lane
     layout, record batch and LDS plan fit."""
     from electron_repulsion_integrals_amd.gen import packed as P
@@ -170,7 +170,7 @@ def test_packed_k1_routing_and_shapes():
                 continue
             used.append((c.la, c.lb, c.lc, c.ld))
             W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
-            assert c.G in (35, 84) and Q * c.G <= NT and P.PACK_RB * Q <= NT
+            assert c.G in (35, 84, 120) and Q * c.G <= NT and P.PACK_RB * Q <= NT
             assert W == (4 if c.G == 84 else 2)
             assert 1 <= P.packed_wg_per_cu(c, sph, W) and \
                 P.packed_lds_bytes(c, sph, W) * P.packed_wg_per_cu(c, sph, W) <= P.LDS_BYTES
@@ -178,12 +178,13 @@ def test_packed_k1_routing_and_shapes():
             if "lane tier" not in src.splitlines()[0]:
                 assert f"__launch_bounds__({NT})" in src and "xu[" in src
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
-    assert all(sum(u[:2]) in (4, 6) and sum(u[2:]) <= (5 if sum(u[:2]) == 6 else 4) for u in used)
+    assert (4, 3, 4, 1) in used and (4, 3, 3, 3) not in used
+    assert all(sum(u[:2]) in (4, 6, 7) and sum(u[2:]) <= (4 if sum(u[:2]) == 4 else 5) for u in used)
 
 
 
 def test_packed_contracted_routing_and_shapes():
-    """Contracted classes whose bra spans 20, 35, 56 or 84 lanes (with a ket
+    """Contracted classes whose bra spans 20, 35, 56, 84 or 120 lanes (with a ket
     recurrence, outside the one-quartet-per-lane tier) run several quartets per multi-wave workgroup: the quartets,
     the set-up chunk and the LDS plan fit, and the emitted kernel has the
     planned shape."""
@@ -210,7 +211,8 @@ def test_packed_contracted_routing_and_shapes():
     assert used[(3, 2, 2, 1)] == (56, 2, 2) and used[(2, 1, 2, 1)] == (20, 2, 6)
     assert used[(3, 3, 1, 0)] == (84, 4, 3) and used[(4, 2, 4, 0)] == (84, 4, 3) and used[(3, 3, 3, 2)] == (84, 4, 3)
     assert (3, 3, 3, 3) not in used and (3, 2, 3, 2) not in used
-    assert all(v[0] in (10, 20, 35, 56, 84) for v in used.values())
+    assert used[(4, 3, 2, 1)] == (120, 2, 1) and (4, 3, 3, 3) not in used
+    assert all(v[0] in (10, 20, 35, 56, 84, 120) for v in used.values())
 
 
 def test_packed_lane_table_decodes():
@@ -220,7 +222,7 @@ def test_packed_lane_table_decodes():
     import re
     from electron_repulsion_integrals_amd.gen import packed as P
     from electron_repulsion_integrals_amd.gen.cartesian import sub
-    for c in (gg.ClassInfo(2, 2, 1, 1), gg.ClassInfo(3, 2, 2, 1), gg.ClassInfo(3, 3, 1, 0)):
+    for c in (gg.ClassInfo(2, 2, 1, 1), gg.ClassInfo(3, 2, 2, 1), gg.ClassInfo(3, 3, 1, 0), gg.ClassInfo(4, 3, 1, 0)):
         decl, dec = P._lane_table(c, "t")
         tab = [int(v) for v in re.search(r"\{(.*)\}", decl).group(1).split(",")]
         em, eb = [(int(m), int(b)) for m, b in [re.search(r"ey = \(lt >> (\d+)\) & (\d+)", dec[1]).groups()[::-1]]][0]

@@ -60,6 +60,15 @@ def packed_k1_waves(ci: ClassInfo) -> int:
     return _wide_waves(ci) if wide_packed(ci) else PACK_WAVES
 
 
+def packed_k1_min_waves(ci: ClassInfo) -> int:
+    """Occupancy bound of the K4 = 1 kernel (0: the compiler's choice).  84-lane
+    bras with kets up to l = 4 otherwise take 56-62 AGPRs beyond 256 VGPRs and
+    run at one wave per SIMD; capped at two they measured 1.15-1.39x faster for
+    (ff|ps) .. (ff|fp) on K = 1 batches and even for (gd| apart from (gd|fp)
+    (1.22x).  The cap made the 120-lane kernels slower."""
+    return 2 if wide_packed(ci) and ci.G == 84 and ci.Lk <= 4 else 0
+
+
 def packed_shape(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES):
     """(W, Q, NT): waves per workgroup, quartets per workgroup, threads."""
     NT = 64 * waves
@@ -140,6 +149,7 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
                    min_waves: int = 0):
     """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
     waves = waves or packed_k1_waves(ci)
+    min_waves = min_waves or packed_k1_min_waves(ci)
     from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
     kv = build_ket_vrr(ci.lc, ci.Lk)
     names = Names("V", kv, ci.Lk)

@@ -176,9 +176,11 @@ def test_packed_k1_routing_and_shapes():
                 P.packed_lds_bytes(c, sph, W) * P.packed_wg_per_cu(c, sph, W) <= P.LDS_BYTES
             src = emit_register_tier(c, sph)
             if "lane tier" not in src.splitlines()[0]:
-                assert f"__launch_bounds__({NT})" in src and "xu[" in src
+                lb = f"{NT}, {P.packed_k1_min_waves(c)}" if P.packed_k1_min_waves(c) else f"{NT}"
+                assert f"__launch_bounds__({lb}) eri_kernel_" in src and "_k1(" in src and "xu[" in src
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
     assert (4, 3, 4, 1) in used and (4, 3, 3, 3) not in used
+    assert P.packed_k1_min_waves(gg.ClassInfo(3, 3, 2, 2)) == 2 and P.packed_k1_min_waves(gg.ClassInfo(4, 3, 1, 0)) == 0
     assert all(sum(u[:2]) in (4, 6, 7) and sum(u[2:]) <= (4 if sum(u[:2]) == 4 else 5) for u in used)
 
 

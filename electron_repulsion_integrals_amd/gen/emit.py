@@ -957,11 +957,12 @@ def _register_kernel(ci: ClassInfo, spherical: bool, k1: bool):
     return o
 
 
-def tier_of(ci: ClassInfo) -> str:
+def tier_of(ci: ClassInfo, spherical: bool = True) -> str:
     """Register tier whenever a lane group fits one wave (the compiler may keep
-    part of a large live set in AGPRs) or the class fits the one-quartet-per-lane
-    tier; memory tier for the other wider bra groups.  The single-tier ablation
-    variants route every class to one tier."""
+    part of a large live set in AGPRs), the class fits the one-quartet-per-lane
+    tier, or a wider group runs packed; memory tier for the other wider bra
+    groups.  The tier can depend on the output kind (``spherical``).  The
+    single-tier ablation variants route every class to one tier."""
     from .variant import CURRENT
     from .lane import use_lane_tier
     from .packed import wide_packed
@@ -976,8 +977,8 @@ def tier_of(ci: ClassInfo) -> str:
         # faster ((fd|fd): 3.46 -> 2.94 ms for a K = 2 batch); with shorter kets
         # it measured 20-60% slower
         return "M"
-    if wide_packed(ci):
-        return "V"  # 84- and 120-lane bras with kets up to l = 5: packed multi-wave workgroups
+    if wide_packed(ci, spherical):
+        return "V"  # 84- and 120-lane bras with short kets: packed multi-wave workgroups
     return "V" if ci.G <= 64 else "M"
 
 
@@ -989,8 +990,8 @@ def generate(out_dir: str, lmax: int = 4, classes=None):
     entries = []
     files = []
     for ci in cls:
-        tier = tier_of(ci)
         for spherical in (False, True):
+            tier = tier_of(ci, spherical)
             if tier == "V":
                 src = emit_register_tier(ci, spherical)
             else:

@@ -37,18 +37,22 @@ PACK_WAVES = 2
 PACK_RB = 8
 
 
-def wide_packed(ci: ClassInfo) -> bool:
+def wide_packed(ci: ClassInfo, spherical: bool = False) -> bool:
     """Lane groups wider than a wave with a ket recurrence of total angular
     momentum 1..5 run both kernels as packed multi-wave workgroups instead of
     going to the memory tier:
       84-lane bras (la + lb = 6: (ff|, (gd|): three quartets on four waves
         (252 of 256 lanes).  Measured on the 120-atom cluster: (ff|ps) .. (ff|fp)
         1.5-1.9x faster, (ff|fd) 17% faster even at one workgroup per compute
-        unit.  An l = 6 ket needs more LDS than a compute unit holds.
+        unit.  With an l = 6 ket only the spherical kernels fit a compute unit's
+        LDS (the Cartesian K4 = 1 kernel would need 186 KB); spherical (ff|ff)
+        measured 1.16x faster than in the memory tier (4,000 quartets, K = 2).
       120-lane bras (la + lb = 7: (gf|): one quartet on two waves (120 of 128
         lanes).  Measured on K = 2 batches: 1.34-1.40x faster with p and d kets,
         1.17-1.24x with l = 4 and (gf|gp), 1.03x with (gf|fd); l = 6 kets tie
         and stay in the memory tier."""
+    if ci.G == 84 and ci.Lk == 6:
+        return spherical
     return ci.G in (84, 120) and 1 <= ci.Lk <= 5
 
 
@@ -57,7 +61,7 @@ def _wide_waves(ci: ClassInfo) -> int:
 
 
 def packed_k1_waves(ci: ClassInfo) -> int:
-    return _wide_waves(ci) if wide_packed(ci) else PACK_WAVES
+    return _wide_waves(ci) if ci.G > 64 else PACK_WAVES
 
 
 def packed_k1_min_waves(ci: ClassInfo) -> int:
@@ -98,7 +102,7 @@ def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb
 def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
     """Packing pays where a wave64 would leave many lanes idle, and a lane
     group wider than a wave needs it."""
-    if wide_packed(ci):
+    if wide_packed(ci, spherical):
         return packed_wg_per_cu(ci, spherical, packed_k1_waves(ci)) >= 1
     if ci.G > 64 or ci.G < 20:
         return False
@@ -319,7 +323,7 @@ def packed_contracted_waves(ci: ClassInfo) -> int:
     quartets, 105 of 128); with an l = 4 ket the level buffers then leave room
     for one workgroup per compute unit only, and two waves stay faster.  Three
     waves measured slower throughout."""
-    if wide_packed(ci):
+    if ci.G > 64:
         return _wide_waves(ci)
     if ci.G == 35 and ci.Lk <= 3:
         return 4
@@ -348,7 +352,7 @@ def use_packed_contracted(ci: ClassInfo, spherical: bool) -> bool:
     fills a wave almost as well with one quartet per wave, but the level
     buffers still beat ds_bpermute there: 10-16% on the 120-atom cluster's
     (fd|pp) .. (fd|fp) blocks."""
-    if wide_packed(ci):
+    if wide_packed(ci, spherical):
         return packed_contracted_wg_per_cu(ci, spherical) >= 1
     if ci.Lk > 4:
         return False

@@ -219,7 +219,10 @@ const char *eri_strerror(int code);
  * `stream` and synchronises it. */
 int eri_fp64_fma_tflops(double *tflops, void *stream);
 
-/* Class metadata: l of (a, b, c, d) and the tier ('V' register, 'M' memory). */
+/* Class metadata: l of (a, b, c, d) and the tier of the class's spherical-output
+ * kernels ('V' register, 'M' memory).  The tier is chosen per output kind, and the
+ * Cartesian kernels of a few classes run in the memory tier where the spherical
+ * ones are register-tier (spherical (ff|ff), (gd|ff), (gd|gd)). */
 int eri_class_info(int32_t class_id, int32_t *l4, int32_t *tier);
 
 #ifdef __cplusplus

@@ -50,14 +50,19 @@ def wide_packed(ci: ClassInfo, spherical: bool = False) -> bool:
       120-lane bras (la + lb = 7: (gf|): one quartet on two waves (120 of 128
         lanes).  Measured on K = 2 batches: 1.34-1.40x faster with p and d kets,
         1.17-1.24x with l = 4 and (gf|gp), 1.03x with (gf|fd); l = 6 kets tie
-        and stay in the memory tier."""
+        and stay in the memory tier.
+      165-lane bras ((gg|) with kets up to l = 4: one quartet on three waves
+        (165 of 192 lanes).  Measured: 1.56-2.94x faster on K = 2 batches,
+        1.18-2.63x on K = 1 batches."""
     if ci.G == 84 and ci.Lk == 6:
         return spherical
+    if ci.G == 165:
+        return 1 <= ci.Lk <= 4
     return ci.G in (84, 120) and 1 <= ci.Lk <= 5
 
 
 def _wide_waves(ci: ClassInfo) -> int:
-    return 4 if ci.G == 84 else 2
+    return {84: 4, 165: 3}.get(ci.G, 2)
 
 
 def packed_k1_waves(ci: ClassInfo) -> int:
@@ -120,18 +125,24 @@ def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb
 
 
 def _lane_table(ci: ClassInfo, tag: str):
-    """Constant table of the lane group (one entry per bra component e, packed
-    into an int) and the lines that decode this lane's entry: e = (ex, ey, ez)
-    and srcx/srcy/srcz, the lanes of e - 1_x, e - 1_y, e - 1_z in the same
-    quartet (the lane itself where the component is 0).  Groups of up to 63
-    lanes use 4-bit components and 6-bit source fields; wider groups (up to 127
-    lanes, components up to 7) use 3-bit components and 7-bit fields."""
+    """Constant table of the lane group (one entry per bra component e) and the
+    lines that decode this lane's entry: e = (ex, ey, ez) and srcx/srcy/srcz, the
+    lanes of e - 1_x, e - 1_y, e - 1_z in the same quartet (the lane itself where
+    the component is 0).  Groups of up to 63 lanes pack 4-bit components and
+    6-bit source fields into an int; up to 127 lanes (components up to 7), 3-bit
+    components and 7-bit fields; wider groups, 4-bit components and 8-bit fields
+    in a 64-bit entry."""
     lanes = ci.lanes
     G = len(lanes)
     lpos = {e: i for i, e in enumerate(lanes)}
-    wide = G >= 64
-    assert G <= 127 and (not wide or max(max(e) for e in lanes) <= 7)
-    eb, sb = (3, 7) if wide else (4, 6)
+    assert G <= 255
+    if G >= 128:
+        eb, sb, ty = 4, 8, "long long"
+    elif G >= 64:
+        eb, sb, ty = 3, 7, "int"
+    else:
+        eb, sb, ty = 4, 6, "int"
+    assert max(max(e) for e in lanes) < (1 << eb)
     tab = []
     for e in lanes:
         d = [lpos[sub(e, ax)] if e[ax] > 0 else -1 for ax in range(3)]
@@ -139,13 +150,17 @@ def _lane_table(ci: ClassInfo, tag: str):
         for ax in range(3):
             v |= (d[ax] + 1) << (3 * eb + ax * sb)
         tab.append(v)
-    decl = f"__constant__ int k_{tag}_lane[{G}] = {{" + ", ".join(str(v) for v in tab) + "};"
+    sfx = "LL" if ty == "long long" else ""
+    decl = f"__constant__ {ty} k_{tag}_lane[{G}] = {{" + ", ".join(f"{v}{sfx}" for v in tab) + "};"
     em, sm = (1 << eb) - 1, (1 << sb) - 1
-    dec = [f"  const int lt = k_{tag}_lane[sub];",
+    cast = "(int)" if ty == "long long" else ""
+    dec = [f"  const {ty} lt = k_{tag}_lane[sub];",
+           f"  const int ex = {cast}(lt & {em}), ey = {cast}((lt >> {eb}) & {em}), ez = {cast}((lt >> {2 * eb}) & {em}),"
+           f" es = ex + ey + ez;" if cast else
            f"  const int ex = lt & {em}, ey = (lt >> {eb}) & {em}, ez = (lt >> {2 * eb}) & {em}, es = ex + ey + ez;",
            "  const int qb = qi * G;"]
     for ax, nm in enumerate("xyz"):
-        dec.append(f"  const int src{nm} = e{nm} > 0 ? qb + ((lt >> {3 * eb + ax * sb}) & {sm}) - 1 : tid;")
+        dec.append(f"  const int src{nm} = e{nm} > 0 ? qb + {cast}((lt >> {3 * eb + ax * sb}) & {sm}) - 1 : tid;")
     return decl, dec
 
 

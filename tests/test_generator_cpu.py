@@ -171,8 +171,8 @@ def test_packed_k1_routing_and_shapes():
                 continue
             used.append((c.la, c.lb, c.lc, c.ld))
             W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
-            assert c.G in (35, 84, 120) and Q * c.G <= NT and P.PACK_RB * Q <= NT
-            assert W == (4 if c.G == 84 else 2)
+            assert c.G in (35, 84, 120, 165) and Q * c.G <= NT and P.PACK_RB * Q <= NT
+            assert W == {84: 4, 165: 3}.get(c.G, 2)
             assert 1 <= P.packed_wg_per_cu(c, sph, W) and \
                 P.packed_lds_bytes(c, sph, W) * P.packed_wg_per_cu(c, sph, W) <= P.LDS_BYTES
             src = emit_register_tier(c, sph)
@@ -182,7 +182,8 @@ def test_packed_k1_routing_and_shapes():
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
     assert (4, 3, 4, 1) in used and (4, 3, 3, 3) not in used
     assert P.packed_k1_min_waves(gg.ClassInfo(3, 3, 2, 2)) == 2 and P.packed_k1_min_waves(gg.ClassInfo(4, 3, 1, 0)) == 0
-    assert all(sum(u[:2]) in (4, 6, 7) and sum(u[2:]) <= {4: 4, 6: 6, 7: 5}[sum(u[:2])] for u in used)
+    assert all(sum(u[:2]) in (4, 6, 7, 8) and sum(u[2:]) <= {4: 4, 6: 6, 7: 5, 8: 4}[sum(u[:2])] for u in used)
+    assert (4, 4, 2, 2) in used and (4, 4, 3, 2) not in used
 
 
 
@@ -215,30 +216,36 @@ def test_packed_contracted_routing_and_shapes():
     assert used[(3, 3, 1, 0)] == (84, 4, 3) and used[(4, 2, 4, 0)] == (84, 4, 3) and used[(3, 3, 3, 2)] == (84, 4, 3)
     assert used[(3, 3, 3, 3)] == (84, 4, 3) and (3, 2, 3, 2) not in used
     assert used[(4, 3, 2, 1)] == (120, 2, 1) and (4, 3, 3, 3) not in used
-    assert all(v[0] in (10, 20, 35, 56, 84, 120) for v in used.values())
+    assert used[(4, 4, 1, 0)] == (165, 3, 1)
+    assert all(v[0] in (10, 20, 35, 56, 84, 120, 165) for v in used.values())
 
 
 def test_packed_lane_table_decodes():
     """The packed kernels' lane table (4-bit components and 6-bit source lanes
-    below 64 lanes, 3-bit and 7-bit from 64 on) decodes to each lane's bra
-    component and the lanes of its lower neighbours."""
+    below 64 lanes, 3-bit and 7-bit up to 127, 4-bit and 8-bit in 64-bit entries
+    beyond) decodes to each lane's bra component and the lanes of its lower
+    neighbours."""
     import re
     from electron_repulsion_integrals_amd.gen import packed as P
     from electron_repulsion_integrals_amd.gen.cartesian import sub
-    for c in (gg.ClassInfo(2, 2, 1, 1), gg.ClassInfo(3, 2, 2, 1), gg.ClassInfo(3, 3, 1, 0), gg.ClassInfo(4, 3, 1, 0)):
+    for c in (gg.ClassInfo(2, 2, 1, 1), gg.ClassInfo(3, 2, 2, 1), gg.ClassInfo(3, 3, 1, 0), gg.ClassInfo(4, 3, 1, 0),
+              gg.ClassInfo(4, 4, 1, 0)):
         decl, dec = P._lane_table(c, "t")
-        tab = [int(v) for v in re.search(r"\{(.*)\}", decl).group(1).split(",")]
-        em, eb = [(int(m), int(b)) for m, b in [re.search(r"ey = \(lt >> (\d+)\) & (\d+)", dec[1]).groups()[::-1]]][0]
-        sh = [int(x) for x in re.findall(r"\(lt >> (\d+)\) & \d+\) - 1", "\n".join(dec))]
-        sm = int(re.search(r"\) & (\d+)\) - 1", dec[3]).group(1))
+        assert ("long long" in decl) == (c.G >= 128)
+        tab = [int(v.strip().rstrip("L")) for v in re.search(r"\{(.*)\}", decl).group(1).split(",")]
+        text = "\n".join(dec)
+        em = int(re.search(r"lt & (\d+)", text).group(1))
+        shifts = [(int(a), int(b)) for a, b in re.findall(r">> (\d+)\) & (\d+)", text)]
+        eb = shifts[0][0]
+        src = shifts[2:5]
         lpos = {e: i for i, e in enumerate(c.lanes)}
-        assert len(tab) == c.G
+        assert len(tab) == c.G and len(src) == 3
         for i, e in enumerate(c.lanes):
             v = tab[i]
             assert (v & em, (v >> eb) & em, (v >> 2 * eb) & em) == e
             for ax in range(3):
                 want = lpos[sub(e, ax)] + 1 if e[ax] > 0 else 0
-                assert (v >> sh[ax]) & sm == want
+                assert (v >> src[ax][0]) & src[ax][1] == want
 
 
 def _apply_ops(ops, base_val, R):

@@ -689,14 +689,24 @@ def _emit_scheduled(ops, initial, names, lines, ind, ahead=None):
 
 
 
-def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, prefix):
+def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, prefix, outputs=None):
     """HRR + transform of one column, emitted in liveness order.
 
     base_load(e) -> C expression reading base value (e, 0) (issued where first
-    needed); store(k, expr) -> statement consuming output k.
+    needed); store(k, expr) -> statement consuming output k.  ``outputs``, if
+    given, restricts the column to those output indices and the values they
+    depend on.
     """
     from .graph import schedule_min_live
     ops, base, outs = _hrr_ops(l1, l2, R, spherical)
+    if outputs is not None:
+        keep = {outs[i] for i in outputs}
+        for k, terms in reversed(ops):
+            if k in keep:
+                keep.update(src for _, src in terms)
+        ops = [(k, terms) for k, terms in ops if k in keep]
+        base = [e for e in base if ("b", e) in keep]
+        outs = [ok if i in set(outputs) else None for i, ok in enumerate(outs)]
     items = []
     code = {}
     names_ = {}
@@ -714,6 +724,8 @@ def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, pref
         code[k] = (lambda k=k, terms=terms: f"const double {names_[k]} = " +
                    " + ".join(nm(src) if c is None else f"{c} * {nm(src)}" for c, src in terms) + ";")
     for i, ok in enumerate(outs):
+        if ok is None:
+            continue
         k = ("w", i)
         items.append((k, [ok], True))
         code[k] = (lambda i=i, ok=ok: store(i, nm(ok)))

@@ -164,6 +164,53 @@ def _lane_table(ci: ClassInfo, tag: str):
     return decl, dec
 
 
+SPLIT_BRA_HRR = True
+
+
+def bra_hrr_parts(ci: ClassInfo, spherical: bool, waves: int, Q: int, contracted: bool = False) -> int:
+    """Waves that share the bra HRR phase.  It runs on (quartet, ket component)
+    items, Q x (ket components) of them: for a lane group wider than a wave with
+    a short ket that is a handful of lanes of the workgroup (3 of 192 for
+    (gg|ps)).  When every item fits one wave, each wave instead takes every item
+    and a 1/waves share of the bra outputs (the values those outputs need are
+    recomputed per wave).  Measured against one item per lane: K4 = 1 kernels
+    of (ff| 1.08-1.32x, (gf| 1.14-1.32x, (gg| 1.20-2.06x faster, (gd| even;
+    contracted kernels even to 1.18x faster for 84- and 120-lane bras, but
+    7-22% slower for (gg|, which keep one item per lane."""
+    if not SPLIT_BRA_HRR or ci.G <= 64 or waves < 2 or Q * ci.nket(spherical) > 64:
+        return 1
+    if contracted and ci.G > 127:
+        return 1
+    return waves
+
+
+def _emit_bra_hrr_split(ci, spherical, o, ind, P, slot_expr, setup, src_of):
+    """Bra HRR and transform with the outputs split over the P waves (see
+    bra_hrr_parts): wave w computes outputs [w nb / P, (w + 1) nb / P) of every
+    item."""
+    from .emit import _emit_hrr_scheduled
+    nb = ci.nbra_out(spherical)
+    o.append(f"{ind}{{  // bra HRR split by output over the waves: all items fit one wave")
+    o.append(f"{ind}  const int part = __builtin_amdgcn_readfirstlane(tid >> 6), t = tid & 63;")
+    o.append(f"{ind}  const int q2 = t / NK, kap = t - q2 * NK;")
+    o.append(f"{ind}  const int slot = {slot_expr};")
+    o.append(f"{ind}  if (t < Q * NK && slot < a.nq) {{")
+    for l in setup:
+        o.append(f"{ind}    {l}")
+    o.append(f"{ind}    switch (part) {{")
+    for p in range(P):
+        lo, hi = p * nb // P, (p + 1) * nb // P
+        o.append(f"{ind}    case {p}: {{")
+        _emit_hrr_scheduled(ci.la, ci.lb, src_of, "AB", spherical,
+                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, ind + "      ", "z",
+                            outputs=range(lo, hi))
+        o.append(f"{ind}    }} break;")
+    o.append(f"{ind}    default: break;")
+    o.append(f"{ind}    }}")
+    o.append(f"{ind}  }}")
+    o.append(f"{ind}}}")
+
+
 def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PACK_RB, wg_per_cu: int = 0,
                    min_waves: int = 0):
     """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
@@ -297,18 +344,27 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
     ab0 = fields.index("ABx")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
-    o.append("    for (int t = tid; t < Q * NK; t += NT) {")
-    o.append("      const int q2 = t / NK, kap = t - q2 * NK;")
-    o.append("      const int slot = g * Q + q2;")
-    o.append("      if (slot >= a.nq) continue;")
-    o.append("      const double* r2 = rec + bslot * Q + q2;")
-    o.append(f"      const double ABx = r2[{ab0} * RS], ABy = r2[{ab0 + 1} * RS], ABz = r2[{ab0 + 2} * RS];")
-    o.append("      (void)ABx; (void)ABy; (void)ABz;")
-    o.append("      const double* src = xu + q2 * NEB * NK + kap;")
-    o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
-    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                        lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "      ", "z")
-    o.append("    }")
+    P = bra_hrr_parts(ci, spherical, W, Q)
+    if P > 1:
+        _emit_bra_hrr_split(ci, spherical, o, "    ", P, "g * Q + q2", [
+            "const double* r2 = rec + bslot * Q + q2;",
+            f"const double ABx = r2[{ab0} * RS], ABy = r2[{ab0 + 1} * RS], ABz = r2[{ab0 + 2} * RS];",
+            "(void)ABx; (void)ABy; (void)ABz;",
+            "const double* src = xu + q2 * NEB * NK + kap;",
+            "double* dst = a.out + (size_t)slot * BLK + kap;"], lambda e: f"src[{epos[e]} * NK]")
+    else:
+        o.append("    for (int t = tid; t < Q * NK; t += NT) {")
+        o.append("      const int q2 = t / NK, kap = t - q2 * NK;")
+        o.append("      const int slot = g * Q + q2;")
+        o.append("      if (slot >= a.nq) continue;")
+        o.append("      const double* r2 = rec + bslot * Q + q2;")
+        o.append(f"      const double ABx = r2[{ab0} * RS], ABy = r2[{ab0 + 1} * RS], ABz = r2[{ab0 + 2} * RS];")
+        o.append("      (void)ABx; (void)ABy; (void)ABz;")
+        o.append("      const double* src = xu + q2 * NEB * NK + kap;")
+        o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
+        _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "      ", "z")
+        o.append("    }")
     o.append("    __syncthreads();  // exchange and records are rewritten next")
     o.append("  }")
     o.append("}")
@@ -538,19 +594,29 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o.append("  __syncthreads();")
     ebra = [e for l in range(ci.la, ci.Lb + 1) for e in components(l)]
     epos = {e: i for i, e in enumerate(ebra)}
-    o.append("  for (int t = tid; t < Q * NK; t += NT) {")
-    o.append("    const int q2 = t / NK, kap = t - q2 * NK;")
-    o.append("    const int slot = q0 + q2;")
-    o.append("    if (slot >= a.nq) continue;")
-    o.append("    const int4 pb2 = a.pair_info[a.qbra[slot]];")
-    o.append("    const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
-             " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
-    o.append("    (void)ABx; (void)ABy; (void)ABz;")
-    o.append("    const double* src = xu + q2 * NEB * NK + kap;")
-    o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
-    _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                        lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "    ", "z")
-    o.append("  }")
+    P = bra_hrr_parts(ci, spherical, W, Q, contracted=True)
+    if P > 1:
+        _emit_bra_hrr_split(ci, spherical, o, "  ", P, "q0 + q2", [
+            "const int4 pb2 = a.pair_info[a.qbra[slot]];",
+            "const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
+            " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];",
+            "(void)ABx; (void)ABy; (void)ABz;",
+            "const double* src = xu + q2 * NEB * NK + kap;",
+            "double* dst = a.out + (size_t)slot * BLK + kap;"], lambda e: f"src[{epos[e]} * NK]")
+    else:
+        o.append("  for (int t = tid; t < Q * NK; t += NT) {")
+        o.append("    const int q2 = t / NK, kap = t - q2 * NK;")
+        o.append("    const int slot = q0 + q2;")
+        o.append("    if (slot >= a.nq) continue;")
+        o.append("    const int4 pb2 = a.pair_info[a.qbra[slot]];")
+        o.append("    const double ABx = a.cen[3 * pb2.x] - a.cen[3 * pb2.y], ABy = a.cen[3 * pb2.x + 1] - a.cen[3 * pb2.y + 1],"
+                 " ABz = a.cen[3 * pb2.x + 2] - a.cen[3 * pb2.y + 2];")
+        o.append("    (void)ABx; (void)ABy; (void)ABz;")
+        o.append("    const double* src = xu + q2 * NEB * NK + kap;")
+        o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
+        _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
+                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "    ", "z")
+        o.append("  }")
     o.append("}")
     o.append("")
     o.append(f"void eri_launch_{tag}(const EriClassArgs& a, hipStream_t s)")

@@ -248,6 +248,44 @@ def test_packed_lane_table_decodes():
                 assert (v >> src[ax][0]) & src[ax][1] == want
 
 
+def test_split_bra_hrr_covers_outputs_once():
+    """Lane groups wider than a wave with a short ket split the bra HRR over the
+    waves: each wave's share defines every value it uses, and the shares
+    together store each bra output exactly once."""
+    import re
+    from electron_repulsion_integrals_amd.gen import packed as P
+    from electron_repulsion_integrals_amd.gen.emit import emit_register_tier
+    for c, sph in ((gg.ClassInfo(3, 3, 1, 0), True), (gg.ClassInfo(4, 4, 1, 1), False), (gg.ClassInfo(4, 3, 2, 0), True)):
+        src = emit_register_tier(c, sph)
+        W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
+        assert P.bra_hrr_parts(c, sph, W, Q) == W > 1
+        kernels = src.split("__global__")[1:]
+        assert len(kernels) == 2
+        # the contracted (gg| kernels keep one item per lane
+        assert ("bra HRR split" in kernels[0]) == (c.G < 128) and "bra HRR split" in kernels[1]
+        for kern in kernels:
+            if "bra HRR split" not in kern:
+                continue
+            body = kern[kern.index("bra HRR split"):]
+            cases = re.split(r"\n\s*case \d+: \{", body)[1:]
+            assert len(cases) == W
+            stored = []
+            for cs in cases:
+                defined = set()
+                for line in cs[:cs.index("} break;")].splitlines():
+                    m = re.match(r"\s*const double (z[bo]\d+) = (.*);", line)
+                    used = re.findall(r"\bz[bo]\d+\b", m.group(2) if m else line)
+                    assert all(u in defined for u in used), line
+                    if m:
+                        defined.add(m.group(1))
+                    stored += [int(k) for k in re.findall(r"eri_out_merged\(&dst\[(\d+) \* NK\]", line)]
+            assert sorted(stored) == list(range(c.nbra_out(sph)))
+    # lane groups of one wave keep the one-item-per-lane loop
+    c = gg.ClassInfo(2, 2, 2, 2)
+    assert "bra HRR split" not in emit_register_tier(c, True)
+
+
+
 def _apply_ops(ops, base_val, R):
     """Evaluate the generator's linear HRR/transform ops (emit._hrr_ops)."""
     val = dict(base_val)

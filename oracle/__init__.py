@@ -12,6 +12,12 @@ Parts:
     coefficients, four-index Obara-Saika integrals, Schwarz factors, J.
   * ``plan.py`` (numpy): the quartet plan -- canonical class form, sort key,
     Schwarz screening -- written out as plainly as possible.
+
+The C source builds twice: ``liberi_oracle.so`` computes in fp64 (the oracle
+every test compares against), ``liberi_oracle_q.so`` compiles the same source
+with IEEE binary128 arithmetic (``-DORACLE_QUAD``).  The second exists only to
+adjudicate: it measures how far the fp64 oracle is from the exact value of the
+same definition (``precision="quad"`` on the functions below).
 """
 from __future__ import annotations
 
@@ -24,6 +30,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "eri_oracle.c")
 LIB = os.path.join(HERE, "liberi_oracle.so")
+QLIB = os.path.join(HERE, "liberi_oracle_q.so")
+_GCC = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC"]
 # Tests that plant a mistake in the oracle point this at a mutant build.
 _LIB_OVERRIDE = os.environ.get("ERI_ORACLE_LIB")
 
@@ -32,62 +40,82 @@ NO_NORMALIZE = 2
 
 
 def build(force: bool = False, out: str = None, defines=()) -> str:
-    """Compile the C oracle with gcc (always when ``force`` or ``out`` is given)."""
+    """Compile the C oracle with gcc (always when ``force`` or ``out`` is given):
+    the fp64 library, and with ``force`` also the binary128 adjudication build."""
     if out is not None:
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC",
-                               *[f"-D{d}" for d in defines], "-o", out, SRC, "-lm"])
+        subprocess.check_call([*_GCC, *[f"-D{d}" for d in defines], "-o", out, SRC, "-lm"])
         return out
     if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
         tmp = LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC",
-                               "-o", tmp, SRC, "-lm"])
+        subprocess.check_call([*_GCC, "-o", tmp, SRC, "-lm"])
         os.replace(tmp, LIB)
+    if force:
+        build_quad(force=True)
     return LIB
 
 
+def build_quad(force: bool = False) -> str:
+    """Compile the binary128 adjudication build of the same source."""
+    if force or not os.path.exists(QLIB) or os.path.getmtime(QLIB) < os.path.getmtime(SRC):
+        tmp = QLIB + ".tmp"
+        subprocess.check_call([*_GCC, "-DORACLE_QUAD", "-o", tmp, SRC, "-lquadmath", "-lm"])
+        os.replace(tmp, QLIB)
+    return QLIB
+
+
 _lib = None
+_qlib = None
 
 
-def lib():
-    global _lib
+def lib(precision: str = "fp64"):
+    """The fp64 oracle library, or with precision="quad" its binary128 build."""
+    global _lib, _qlib
+    if precision == "quad":
+        if _qlib is None:
+            _qlib = _bind(ctypes.CDLL(build_quad()))
+        return _qlib
+    if precision != "fp64":
+        raise ValueError(precision)
     if _lib is None:
         if _LIB_OVERRIDE:
             L = ctypes.CDLL(_LIB_OVERRIDE)
         else:
             build()
             L = ctypes.CDLL(LIB)
-        dp = ctypes.POINTER(ctypes.c_double)
-        ip = ctypes.POINTER(ctypes.c_int32)
-        lp = ctypes.POINTER(ctypes.c_int64)
-        L.oracle_boys.argtypes = [ctypes.c_int, ctypes.c_double, dp]
-        L.oracle_boys.restype = None
-        L.oracle_normalize.argtypes = [ctypes.c_int, ctypes.c_int, dp, dp, dp]
-        L.oracle_sph_coeffs.argtypes = [ctypes.c_int, dp]
-        L.oracle_eri_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
-                                          ctypes.c_int64, ip, lp, dp]
-        L.oracle_eri_quartets.restype = ctypes.c_int
-        L.oracle_eri_deriv_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
-                                                ctypes.c_int64, ip, lp, dp]
-        L.oracle_eri_deriv_quartets.restype = ctypes.c_int
-        L.oracle_schwarz.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, dp]
-        L.oracle_schwarz.restype = ctypes.c_int
-        L.oracle_J_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
-                                             ctypes.c_int64, ip, lp, dp, dp, dp]
-        L.oracle_J_from_quartets.restype = None
-        L.oracle_J_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
-                                     ctypes.c_int, dp, dp]
-        L.oracle_J_naive.restype = ctypes.c_int
-        L.oracle_K_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
-                                             ctypes.c_int64, ip, lp, dp, dp, dp]
-        L.oracle_K_from_quartets.restype = None
-        L.oracle_K_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
-                                     ctypes.c_int, dp, dp]
-        L.oracle_K_naive.restype = ctypes.c_int
-        L.oracle_num_threads.restype = ctypes.c_int
-        L.oracle_set_jitter.argtypes = [ctypes.c_uint64]
-        L.oracle_set_jitter.restype = None
-        _lib = L
+        _lib = _bind(L)
     return _lib
+
+
+def _bind(L):
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lp = ctypes.POINTER(ctypes.c_int64)
+    L.oracle_boys.argtypes = [ctypes.c_int, ctypes.c_double, dp]
+    L.oracle_boys.restype = None
+    L.oracle_normalize.argtypes = [ctypes.c_int, ctypes.c_int, dp, dp, dp]
+    L.oracle_sph_coeffs.argtypes = [ctypes.c_int, dp]
+    L.oracle_eri_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
+                                      ctypes.c_int64, ip, lp, dp]
+    L.oracle_eri_quartets.restype = ctypes.c_int
+    L.oracle_eri_deriv_quartets.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int,
+                                            ctypes.c_int64, ip, lp, dp]
+    L.oracle_eri_deriv_quartets.restype = ctypes.c_int
+    L.oracle_schwarz.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, dp]
+    L.oracle_schwarz.restype = ctypes.c_int
+    L.oracle_J_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
+                                         ctypes.c_int64, ip, lp, dp, dp, dp]
+    L.oracle_J_from_quartets.restype = None
+    L.oracle_J_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
+                                 ctypes.c_int, dp, dp]
+    L.oracle_J_naive.restype = ctypes.c_int
+    L.oracle_K_from_quartets.argtypes = [ctypes.c_int, ip, ctypes.c_int, ip, ctypes.c_int,
+                                         ctypes.c_int64, ip, lp, dp, dp, dp]
+    L.oracle_K_from_quartets.restype = None
+    L.oracle_K_naive.argtypes = [ctypes.c_int, dp, ip, ip, ip, dp, dp, ctypes.c_int, ip,
+                                 ctypes.c_int, dp, dp]
+    L.oracle_K_naive.restype = ctypes.c_int
+    L.oracle_num_threads.restype = ctypes.c_int
+    return L
 
 
 def _d(a):
@@ -121,11 +149,11 @@ def num_threads() -> int:
     return int(lib().oracle_num_threads())
 
 
-def boys(mmax: int, T: float) -> np.ndarray:
+def boys(mmax: int, T: float, precision: str = "fp64") -> np.ndarray:
     """F_0..F_mmax at T (series + downward recursion, or erf + upward above T=50)."""
     out = np.zeros(mmax + 1)
     out_, p = _d(out)
-    lib().oracle_boys(int(mmax), float(T), p)
+    lib(precision).oracle_boys(int(mmax), float(T), p)
     return out_
 
 
@@ -167,11 +195,12 @@ def block_sizes(sh, quartets, spherical):
     return n[q[:, 0]] * n[q[:, 1]] * n[q[:, 2]] * n[q[:, 3]]
 
 
-def eri(sh, quartets, spherical: bool, normalize_: bool = True):
+def eri(sh, quartets, spherical: bool, normalize_: bool = True, precision: str = "fp64"):
     """Integral blocks for each quartet (shell order as given).
 
     Returns (flat values, offsets[nq]) with block q at flat[off[q]: off[q]+size[q]],
-    row-major over (a, b, c, d).
+    row-major over (a, b, c, d).  precision="quad" evaluates the same definition
+    in binary128 and rounds the results to fp64 (adjudication only).
     """
     q, pq = _i(np.asarray(quartets).reshape(-1, 4))
     sizes = block_sizes(sh, q, spherical)
@@ -183,7 +212,7 @@ def eri(sh, quartets, spherical: bool, normalize_: bool = True):
     of, pof = _l(off)
     keep, args = _shell_args(sh)
     flags = (SPHERICAL if spherical else 0) | (0 if normalize_ else NO_NORMALIZE)
-    rc = lib().oracle_eri_quartets(*args, flags, len(q), pq, pof, po)
+    rc = lib(precision).oracle_eri_quartets(*args, flags, len(q), pq, pof, po)
     if rc != 0:
         raise ValueError("oracle_eri_quartets rejected its input")
     return o, of
@@ -221,20 +250,20 @@ def eri_deriv_block(sh, quartet, spherical: bool, normalize_: bool = True) -> np
     return flat.reshape([4, 3] + dims)
 
 
-def eri_block(sh, quartet, spherical: bool, normalize_: bool = True) -> np.ndarray:
+def eri_block(sh, quartet, spherical: bool, normalize_: bool = True, precision: str = "fp64") -> np.ndarray:
     """One quartet as a 4-index array."""
-    flat, _ = eri(sh, [quartet], spherical, normalize_)
+    flat, _ = eri(sh, [quartet], spherical, normalize_, precision)
     dims = [nfunc(int(sh.l[s]), spherical) for s in quartet]
     return flat.reshape(dims)
 
 
-def schwarz(sh, spherical: bool) -> np.ndarray:
+def schwarz(sh, spherical: bool, precision: str = "fp64") -> np.ndarray:
     """S[p] for pairs i >= j, p = i(i+1)/2 + j."""
     ns = int(sh.l.shape[0])
     out = np.zeros(ns * (ns + 1) // 2)
     o, po = _d(out)
     keep, args = _shell_args(sh)
-    rc = lib().oracle_schwarz(*args, SPHERICAL if spherical else 0, po)
+    rc = lib(precision).oracle_schwarz(*args, SPHERICAL if spherical else 0, po)
     if rc != 0:
         raise ValueError("oracle_schwarz failed")
     return o
@@ -366,31 +395,6 @@ def K_blocks(sh, spherical: bool, pairs, D, S, tau):
             K += np.einsum("abcd,bd->ac", blk, D[bf[j]:bf[j + 1], bf[l]:bf[l + 1]])
         out.append(K)
     return out
-
-
-def conditioning_spread(sh, quartets, spherical: bool, ref=None, seeds=(0x9E3779B97F4A7C15, 0xD1B54A32D192ED03)):
-    """Per-quartet change of the oracle's block when every Boys input is perturbed by
-    at most one unit in the last place (two seeded perturbations, maximum taken).
-
-    Returns an array over quartets: the largest |perturbed - unperturbed| element
-    of each block.  This is the error that rounding the recurrence inputs to fp64
-    alone causes; well-conditioned quartets give ~1e-16 x their magnitude.
-    """
-    q = np.asarray(quartets).reshape(-1, 4)
-    if ref is None:
-        ref, _ = eri(sh, q, spherical)
-    sizes = block_sizes(sh, q, spherical)
-    off = np.concatenate([[0], np.cumsum(sizes)])
-    spread = np.zeros(len(q))
-    try:
-        for sd in seeds:
-            lib().oracle_set_jitter(ctypes.c_uint64(sd))
-            alt, _ = eri(sh, q, spherical)
-            d = np.abs(alt - ref)
-            spread = np.maximum(spread, np.maximum.reduceat(d, off[:-1]) if len(d) else spread)
-    finally:
-        lib().oracle_set_jitter(ctypes.c_uint64(0))
-    return spread
 
 
 def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, normalize_: bool = True):

@@ -24,6 +24,12 @@
  * Obara-Saika recurrence, which may raise any of a, b, c, d, filled bottom-up
  * in a dense table for every primitive quartet.  No horizontal recurrence is
  * used.  Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC.
+ *
+ * Precision: all arithmetic is done in the type `real`, fp64 by default.
+ * Built with -DORACLE_QUAD the same source computes in IEEE binary128
+ * (__float128, libquadmath) and rounds only the results to fp64.  That build
+ * exists to adjudicate: it shows how far the fp64 oracle itself is from the
+ * exact value of the same definition.  Inputs and outputs stay fp64 in both.
  */
 #include <math.h>
 #include <stdint.h>
@@ -34,6 +40,27 @@
 #include <omp.h>
 #endif
 
+#ifdef ORACLE_QUAD
+#include <quadmath.h>
+typedef __float128 real;
+#define R_EXP expq
+#define R_SQRT sqrtq
+#define R_POW powq
+#define R_ERF erfq
+#define R_FABS fabsq
+#define R_PI M_PIq
+#define R_SERIES_TOL 1e-36Q
+#else
+typedef double real;
+#define R_EXP exp
+#define R_SQRT sqrt
+#define R_POW pow
+#define R_ERF erf
+#define R_FABS fabs
+#define R_PI M_PI
+#define R_SERIES_TOL 1e-18
+#endif
+
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0 /* >0 only in test builds that plant a known mistake */
 #endif
@@ -41,24 +68,6 @@
 #define OR_MMAX 40
 
 enum { OR_SPHERICAL = 1, OR_NO_NORMALIZE = 2 };
-
-/* Conditioning probe (test infrastructure): when non-zero, every Boys value
- * entering a primitive quartet is multiplied by 1 + d with |d| <= 2^-52 drawn
- * from a hash of (seed, primitive indices, T, m).  Comparing two seeds with the
- * unperturbed result measures how far rounding the recurrence inputs to fp64
- * alone moves each integral -- an error no fp64 evaluation can avoid. */
-static uint64_t g_jitter_seed = 0;
-void oracle_set_jitter(uint64_t seed) { g_jitter_seed = seed; }
-
-static uint64_t mix64(uint64_t x)
-{
-    x ^= x >> 30;
-    x *= 0xbf58476d1ce4e5b9ULL;
-    x ^= x >> 27;
-    x *= 0x94d049bb133111ebULL;
-    x ^= x >> 31;
-    return x;
-}
 
 /* ------------------------------------------------------------------------ */
 /* Boys function F_m(T) = int_0^1 t^(2m) exp(-T t^2) dt                       */
@@ -74,26 +83,34 @@ static uint64_t mix64(uint64_t x)
  *     which is well conditioned there because (2m+1)F_m >> exp(-T).        */
 #define OR_BOYS_SWITCH 50.0
 
-void oracle_boys(int mmax, double T, double *F)
+static void boys_r(int mmax, real T, real *F)
 {
     if (T <= OR_BOYS_SWITCH) {
-        double e = exp(-T);
-        double term = 1.0 / (2.0 * mmax + 1.0);
-        double sum = term;
+        real e = R_EXP(-T);
+        real term = 1.0 / (2.0 * mmax + 1.0);
+        real sum = term;
         for (int k = 1; k < 100000; ++k) {
             term *= 2.0 * T / (2.0 * mmax + 2.0 * k + 1.0);
             sum += term;
-            if (term < 1e-18 * sum && k > T) break;
+            if (term < R_SERIES_TOL * sum && k > T) break;
         }
         F[mmax] = e * sum;
         for (int m = mmax - 1; m >= 0; --m)
             F[m] = (2.0 * T * F[m + 1] + e) / (2.0 * m + 1.0 + (ORACLE_MUTANT == 4 ? 2.0 : 0.0));
     } else {
-        double e = exp(-T);
-        F[0] = 0.5 * sqrt(M_PI / T) * erf(sqrt(T));
+        real e = R_EXP(-T);
+        F[0] = 0.5 * R_SQRT(R_PI / T) * R_ERF(R_SQRT(T));
         for (int m = 0; m < mmax; ++m)
             F[m + 1] = ((2.0 * m + 1.0) * F[m] - e) / (2.0 * T);
     }
+}
+
+void oracle_boys(int mmax, double T, double *F)
+{
+    real Fr[OR_MMAX + 1];
+    if (mmax < 0 || mmax > OR_MMAX) return;
+    boys_r(mmax, T, Fr);
+    for (int m = 0; m <= mmax; ++m) F[m] = (double)Fr[m];
 }
 
 /* ------------------------------------------------------------------------ */
@@ -150,26 +167,35 @@ static void tripset_init(tripset *s, int L)
  * the same factor for every Cartesian component of the shell (it normalises
  * the x^l component); then the contracted x^l component is scaled to unit
  * norm using  int x^(2l) exp(-p r^2) = (pi/p)^(3/2) (2l-1)!! / (2p)^l.       */
-static double dfact(int n) /* n!!, with (-1)!! = 1 */
+static real dfact(int n) /* n!!, with (-1)!! = 1 */
 {
-    double r = 1.0;
+    real r = 1.0;
     for (int k = n; k > 1; k -= 2) r *= k;
     return r;
 }
 
-void oracle_normalize(int l, int K, const double *alpha, const double *c_in, double *c_out)
+static void normalize_r(int l, int K, const double *alpha, const double *c_in, real *c_out)
 {
     for (int k = 0; k < K; ++k)
-        c_out[k] = c_in[k] * pow(2.0 * alpha[k] / M_PI, 0.75) *
-                   pow(4.0 * alpha[k], 0.5 * l + (ORACLE_MUTANT == 6 ? 0.5 : 0.0)) / sqrt(dfact(2 * l - 1));
-    double s = 0.0;
+        c_out[k] = c_in[k] * R_POW(2.0 * (real)alpha[k] / R_PI, (real)0.75) *
+                   R_POW(4.0 * (real)alpha[k], (real)(0.5 * l + (ORACLE_MUTANT == 6 ? 0.5 : 0.0))) /
+                   R_SQRT(dfact(2 * l - 1));
+    real s = 0.0;
     for (int k = 0; k < K; ++k)
         for (int q = 0; q < K; ++q) {
-            double p = alpha[k] + alpha[q];
-            s += c_out[k] * c_out[q] * pow(M_PI / p, 1.5) * dfact(2 * l - 1) / pow(2.0 * p, l);
+            real p = (real)alpha[k] + (real)alpha[q];
+            s += c_out[k] * c_out[q] * R_POW(R_PI / p, (real)1.5) * dfact(2 * l - 1) / R_POW(2.0 * p, (real)l);
         }
-    double f = 1.0 / sqrt(s);
+    real f = 1.0 / R_SQRT(s);
     for (int k = 0; k < K; ++k) c_out[k] *= f;
+}
+
+void oracle_normalize(int l, int K, const double *alpha, const double *c_in, double *c_out)
+{
+    real *c = (real *)malloc(sizeof(real) * (K > 0 ? K : 1));
+    normalize_r(l, K, alpha, c_in, c);
+    for (int k = 0; k < K; ++k) c_out[k] = (double)c[k];
+    free(c);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -183,16 +209,16 @@ void oracle_normalize(int l, int K, const double *alpha, const double *c_in, dou
  * Each row is then scaled so that T S_cart T^T = I for a shell normalised as
  * above; the leading monomial x^|m| z^(l-|m|) (m>0), x^(|m|-1) y z^(l-|m|)
  * (m<0) or z^l (m=0) comes out with a positive coefficient.                 */
-static double binom(int n, int k)
+static real binom(int n, int k)
 {
     if (k < 0 || k > n) return 0.0;
-    double r = 1.0;
+    real r = 1.0;
     for (int i = 1; i <= k; ++i) r = r * (n - k + i) / i;
     return r;
 }
 
 /* one-centre overlap of two Cartesian components of the normalised shell */
-static double cart_overlap(const int *p, const int *q, int l)
+static real cart_overlap(const int *p, const int *q, int l)
 {
     int sx = p[0] + q[0], sy = p[1] + q[1], sz = p[2] + q[2];
     if ((sx | sy | sz) & 1) return 0.0;
@@ -200,21 +226,21 @@ static double cart_overlap(const int *p, const int *q, int l)
 }
 
 /* T[(2l+1) x ncart(l)], row-major */
-void oracle_sph_coeffs(int l, double *T)
+static void sph_coeffs_r(int l, real *T)
 {
     int nc = ncart(l);
     int c[64][3];
     cart_list(l, c);
     for (int mi = 0; mi < nsph(l); ++mi) {
         int m = mi - l, am = abs(m);
-        double *row = T + (size_t)mi * nc;
+        real *row = T + (size_t)mi * nc;
         for (int q = 0; q < nc; ++q) row[q] = 0.0;
         /* 2v runs over even values (m >= 0) or odd values (m < 0) in [0, |m|] */
         for (int t = 0; t <= (l - am) / 2; ++t)
             for (int u = 0; u <= t; ++u)
                 for (int twov = (m >= 0 ? 0 : 1); twov <= am; twov += 2) {
                     int sgn_exp = t + (ORACLE_MUTANT == 5 ? 0 : (twov - (m >= 0 ? 0 : 1)) / 2);
-                    double coef = ((sgn_exp & 1) ? -1.0 : 1.0) * pow(0.25, t) * binom(l, t) *
+                    real coef = ((sgn_exp & 1) ? -1.0 : 1.0) * R_POW((real)0.25, (real)t) * binom(l, t) *
                                   binom(l - t, am + t) * binom(t, u) * binom(am, twov);
                     int px = 2 * t + am - 2 * u - twov;
                     int py = 2 * u + twov;
@@ -223,12 +249,20 @@ void oracle_sph_coeffs(int l, double *T)
                     for (int q = 0; q < nc; ++q)
                         if (c[q][0] == px && c[q][1] == py && c[q][2] == pz) row[q] += coef;
                 }
-        double nrm = 0.0;
+        real nrm = 0.0;
         for (int p = 0; p < nc; ++p)
             for (int q = 0; q < nc; ++q) nrm += row[p] * row[q] * cart_overlap(c[p], c[q], l);
-        double f = 1.0 / sqrt(nrm);
+        real f = 1.0 / R_SQRT(nrm);
         for (int q = 0; q < nc; ++q) row[q] *= f;
     }
+}
+
+void oracle_sph_coeffs(int l, double *T)
+{
+    real Tr[17 * 45];
+    if (l < 0 || l > OR_LMAX) return;
+    sph_coeffs_r(l, Tr);
+    for (int q = 0; q < nsph(l) * ncart(l); ++q) T[q] = (double)Tr[q];
 }
 
 /* ------------------------------------------------------------------------ */
@@ -252,7 +286,7 @@ void oracle_sph_coeffs(int l, double *T)
  * a, b, c, d that is non-zero, along its first non-zero axis.              */
 typedef struct {
     tripset ta, tb, tc, td;
-    double *V;
+    real *V;
     size_t cap;
 } os_work;
 
@@ -272,7 +306,7 @@ static inline size_t vidx(const os_work *w, int ia, int ib, int ic, int id, int 
  * integrals themselves (the normalisation belongs to the undifferentiated
  * shell). */
 static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4[4],
-                       const double *al[4], const double *cc[4], double *out, double *dout)
+                       const double *al[4], const real *cc[4], real *out, real *dout)
 {
     int la = l4[0], lb = l4[1], lc = l4[2], ld = l4[3];
     const int ext = dout ? 1 : 0;
@@ -284,10 +318,10 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
     size_t need = (size_t)w->ta.n * w->tb.n * w->tc.n * w->td.n * M1;
     if (need > w->cap) {
         free(w->V);
-        w->V = (double *)malloc(need * sizeof(double));
+        w->V = (real *)malloc(need * sizeof(real));
         w->cap = need;
     }
-    double *V = w->V;
+    real *V = w->V;
     int ca[64][3], cb[64][3], ccc[64][3], cd[64][3];
     cart_list(la, ca);
     cart_list(lb, cb);
@@ -300,52 +334,41 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
     else
         for (size_t q = 0; q < nout; ++q) out[q] = 0.0;
     const double *A = cen[0], *B = cen[1], *C = cen[2], *D = cen[3];
-    double AB2 = 0, CD2 = 0;
+    real AB2 = 0, CD2 = 0;
     for (int i = 0; i < 3; ++i) {
-        AB2 += (A[i] - B[i]) * (A[i] - B[i]);
-        CD2 += (C[i] - D[i]) * (C[i] - D[i]);
+        AB2 += ((real)A[i] - B[i]) * ((real)A[i] - B[i]);
+        CD2 += ((real)C[i] - D[i]) * ((real)C[i] - D[i]);
     }
-    double F[OR_MMAX + 1];
+    real F[OR_MMAX + 1];
 
     for (int pa = 0; pa < K4[0]; ++pa)
         for (int pb = 0; pb < K4[1]; ++pb)
             for (int pc = 0; pc < K4[2]; ++pc)
                 for (int pd = 0; pd < K4[3]; ++pd) {
-                    double a = al[0][pa], b = al[1][pb], c = al[2][pc], d = al[3][pd];
-                    double zeta = a + b, eta = c + d, rho = zeta * eta / (zeta + eta);
+                    real a = al[0][pa], b = al[1][pb], c = al[2][pc], d = al[3][pd];
+                    real zeta = a + b, eta = c + d, rho = zeta * eta / (zeta + eta);
                     /* P - A = beta (B - A)/zeta, P - B = alpha (A - B)/zeta (likewise for Q),
                        P - Q = (P - A) - (Q - C) + (A - C), W - P = eta (Q - P)/(zeta+eta),
                        W - Q = zeta (P - Q)/(zeta+eta): the same quantities as the
                        definitions, formed from coordinate differences so that they
                        vanish exactly for coincident centres. */
-                    double PA[3], PB[3], QC[3], QD[3], WP[3], WQ[3], PQ2 = 0;
+                    real PA[3], PB[3], QC[3], QD[3], WP[3], WQ[3], PQ2 = 0;
                     for (int i = 0; i < 3; ++i) {
-                        PA[i] = b * (B[i] - A[i]) / zeta;
-                        PB[i] = a * (A[i] - B[i]) / zeta;
-                        QC[i] = d * (D[i] - C[i]) / eta;
-                        QD[i] = c * (C[i] - D[i]) / eta;
-                        double PQ = PA[i] - QC[i] + (A[i] - C[i]);
+                        PA[i] = b * ((real)B[i] - A[i]) / zeta;
+                        PB[i] = a * ((real)A[i] - B[i]) / zeta;
+                        QC[i] = d * ((real)D[i] - C[i]) / eta;
+                        QD[i] = c * ((real)C[i] - D[i]) / eta;
+                        real PQ = PA[i] - QC[i] + ((real)A[i] - C[i]);
                         WP[i] = -eta * PQ / (zeta + eta);
                         WQ[i] = zeta * PQ / (zeta + eta);
                         PQ2 += PQ * PQ;
                     }
-                    double T = rho * PQ2;
-                    double pref = 2.0 * pow(M_PI, 2.5) / (zeta * eta * sqrt(zeta + eta)) *
-                                  exp(-a * b / zeta * AB2) * exp(-c * d / eta * CD2);
-                    oracle_boys(Lt, T, F);
-                    if (g_jitter_seed) {
-                        uint64_t tb;
-                        memcpy(&tb, &T, sizeof tb);
-                        uint64_t h0 = mix64(g_jitter_seed ^ mix64(tb ^ mix64(((uint64_t)pa << 48) ^ ((uint64_t)pb << 32) ^
-                                                                            ((uint64_t)pc << 16) ^ (uint64_t)pd)));
-                        for (int m = 0; m <= Lt; ++m) {
-                            uint64_t h = mix64(h0 + (uint64_t)m);
-                            double u = (double)(h >> 11) * (1.0 / 9007199254740992.0); /* [0,1) */
-                            F[m] *= 1.0 + (2.0 * u - 1.0) * 2.220446049250313e-16;
-                        }
-                    }
-                    double i2z = 0.5 / zeta, i2e = 0.5 / eta, i2ze = 0.5 / (zeta + eta);
-                    double roz = rho / zeta, roe = rho / eta;
+                    real T = rho * PQ2;
+                    real pref = 2.0 * R_POW(R_PI, (real)2.5) / (zeta * eta * R_SQRT(zeta + eta)) *
+                                R_EXP(-a * b / zeta * AB2) * R_EXP(-c * d / eta * CD2);
+                    boys_r(Lt, T, F);
+                    real i2z = 0.5 / zeta, i2e = 0.5 / eta, i2ze = 0.5 / (zeta + eta);
+                    real roz = rho / zeta, roe = rho / eta;
 
                     for (int ia = 0; ia < w->ta.n; ++ia)
                         for (int ib = 0; ib < w->tb.n; ++ib)
@@ -356,7 +379,7 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                                     int tot = ea[0] + ea[1] + ea[2] + eb[0] + eb[1] + eb[2] +
                                               ec[0] + ec[1] + ec[2] + ed[0] + ed[1] + ed[2];
                                     int mtop = Lt - tot;
-                                    double *v = V + vidx(w, ia, ib, ic, id, 0, M1);
+                                    real *v = V + vidx(w, ia, ib, ic, id, 0, M1);
                                     if (tot == 0) {
                                         for (int m = 0; m <= mtop; ++m) v[m] = pref * F[m];
                                         continue;
@@ -376,8 +399,8 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
 #define IDX_B(x) w->tb.idx[(x)[0]][(x)[1]][(x)[2]]
 #define IDX_C(x) w->tc.idx[(x)[0]][(x)[1]][(x)[2]]
 #define IDX_D(x) w->td.idx[(x)[0]][(x)[1]][(x)[2]]
-                                    const double *v0 = V + vidx(w, IDX_A(a2), IDX_B(b2), IDX_C(c2), IDX_D(d2), 0, M1);
-                                    double g1, g2, two_exp_inv, ratio;
+                                    const real *v0 = V + vidx(w, IDX_A(a2), IDX_B(b2), IDX_C(c2), IDX_D(d2), 0, M1);
+                                    real g1, g2, two_exp_inv, ratio;
                                     if (which == 0) g1 = PA[ax], g2 = WP[ax], two_exp_inv = i2z, ratio = roz;
                                     else if (which == 1) g1 = (ORACLE_MUTANT == 7 ? PA[ax] : PB[ax]), g2 = WP[ax], two_exp_inv = i2z, ratio = roz;
                                     else if (which == 2) g1 = QC[ax], g2 = WQ[ax], two_exp_inv = i2e, ratio = roe;
@@ -391,9 +414,9 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                                         int *x = s == 0 ? a2 : s == 1 ? b2 : s == 2 ? c2 : d2;
                                         int same_side = (which < 2) == (s < 2);
                                         if (x[ax] == 0) continue;
-                                        double n = x[ax];
+                                        real n = x[ax];
                                         x[ax] -= 1;
-                                        const double *vp = V + vidx(w, IDX_A(a2), IDX_B(b2), IDX_C(c2), IDX_D(d2), 0, M1);
+                                        const real *vp = V + vidx(w, IDX_A(a2), IDX_B(b2), IDX_C(c2), IDX_D(d2), 0, M1);
                                         x[ax] += 1;
                                         if (same_side) {
                                             for (int m = 0; m <= mtop; ++m)
@@ -404,7 +427,7 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                                     }
                                 }
                     /* contract the m = 0 entries with the exact target totals */
-                    double cw = cc[0][pa] * cc[1][pb] * cc[2][pc] * cc[3][pd];
+                    real cw = cc[0][pa] * cc[1][pb] * cc[2][pc] * cc[3][pd];
                     size_t o = 0;
                     if (!dout) {
                         for (int qa = 0; qa < na; ++qa)
@@ -416,7 +439,7 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                                     }
                         continue;
                     }
-                    const double ex4[4] = {a, b, c, d};
+                    const real ex4[4] = {a, b, c, d};
                     for (int qa = 0; qa < na; ++qa)
                         for (int qb = 0; qb < nb; ++qb)
                             for (int qc = 0; qc < nc; ++qc)
@@ -427,8 +450,8 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
                                                             {ccc[qc][0], ccc[qc][1], ccc[qc][2]}, {cd[qd][0], cd[qd][1], cd[qd][2]}};
                                             int n = t4[p][i];
                                             t4[p][i] += 1;
-                                            double up = V[vidx(w, IDX_A(t4[0]), IDX_B(t4[1]), IDX_C(t4[2]), IDX_D(t4[3]), 0, M1)];
-                                            double dn = 0.0;
+                                            real up = V[vidx(w, IDX_A(t4[0]), IDX_B(t4[1]), IDX_C(t4[2]), IDX_D(t4[3]), 0, M1)];
+                                            real dn = 0.0;
                                             if (n > 0) {
                                                 t4[p][i] -= 2;
                                                 dn = V[vidx(w, IDX_A(t4[0]), IDX_B(t4[1]), IDX_C(t4[2]), IDX_D(t4[3]), 0, M1)];
@@ -441,7 +464,7 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
 
 /* Apply T^(l) to index `pos` (0..3) of a 4-index tensor with dims n[4]:
  * out = (... x T x ...) in, changing dimension n[pos] from ncart to nsph. */
-static void transform_index(const double *in, double *out, int n[4], int pos, const double *T, int nsp)
+static void transform_index(const real *in, real *out, int n[4], int pos, const real *T, int nsp)
 {
     int before = 1, after = 1;
     for (int i = 0; i < pos; ++i) before *= n[i];
@@ -450,7 +473,7 @@ static void transform_index(const double *in, double *out, int n[4], int pos, co
     for (int x = 0; x < before; ++x)
         for (int s = 0; s < nsp; ++s)
             for (int y = 0; y < after; ++y) {
-                double acc = 0.0;
+                real acc = 0.0;
                 for (int c = 0; c < nc; ++c) acc += T[s * nc + c] * in[((size_t)x * nc + c) * after + y];
                 out[((size_t)x * nsp + s) * after + y] = acc;
             }
@@ -471,25 +494,26 @@ int oracle_eri_quartets(int nshell, const double *centers, const int32_t *l, con
         if (l[s] < 0 || l[s] > OR_LMAX || nprim[s] < 1) return -1;
     /* normalised coefficients */
     int ntot = prim_off[nshell];
-    double *cn = (double *)malloc(sizeof(double) * (ntot > 0 ? ntot : 1));
+    real *cn = (real *)malloc(sizeof(real) * (ntot > 0 ? ntot : 1));
     for (int s = 0; s < nshell; ++s) {
         if (flags & OR_NO_NORMALIZE)
-            memcpy(cn + prim_off[s], coefs + prim_off[s], sizeof(double) * nprim[s]);
+            for (int k = 0; k < nprim[s]; ++k) cn[prim_off[s] + k] = coefs[prim_off[s] + k];
         else
-            oracle_normalize(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
+            normalize_r(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
     }
-    double Tsph[OR_LMAX + 1][17 * 45];
-    for (int L = 0; L <= OR_LMAX; ++L) oracle_sph_coeffs(L, Tsph[L]);
+    real Tsph[OR_LMAX + 1][17 * 45];
+    for (int L = 0; L <= OR_LMAX; ++L) sph_coeffs_r(L, Tsph[L]);
     int bad = 0;
 #pragma omp parallel
     {
         os_work *w = (os_work *)calloc(1, sizeof(os_work));
-        double *buf1 = NULL, *buf2 = NULL;
+        real *buf1 = NULL, *buf2 = NULL;
         size_t bcap = 0;
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < nq; ++q) {
             int sh[4], l4[4], K4[4];
-            const double *cen[4], *al[4], *cc[4];
+            const double *cen[4], *al[4];
+            const real *cc[4];
             int ok = 1;
             for (int t = 0; t < 4; ++t) {
                 sh[t] = quartets[4 * q + t];
@@ -511,25 +535,22 @@ int oracle_eri_quartets(int nshell, const double *centers, const int32_t *l, con
             if (ncar > bcap) {
                 free(buf1);
                 free(buf2);
-                buf1 = (double *)malloc(ncar * sizeof(double));
-                buf2 = (double *)malloc(ncar * sizeof(double));
+                buf1 = (real *)malloc(ncar * sizeof(real));
+                buf2 = (real *)malloc(ncar * sizeof(real));
                 bcap = ncar;
             }
-            if (!(flags & OR_SPHERICAL)) {
-                os_quartet(w, l4, cen, K4, al, cc, out + out_off[q], NULL);
-            } else {
-                os_quartet(w, l4, cen, K4, al, cc, buf1, NULL);
-                int n[4] = {ncart(l4[0]), ncart(l4[1]), ncart(l4[2]), ncart(l4[3])};
-                double *src = buf1, *dst = buf2;
+            os_quartet(w, l4, cen, K4, al, cc, buf1, NULL);
+            real *src = buf1, *dst = buf2;
+            int n[4] = {ncart(l4[0]), ncart(l4[1]), ncart(l4[2]), ncart(l4[3])};
+            if (flags & OR_SPHERICAL)
                 for (int pos = 0; pos < 4; ++pos) {
                     transform_index(src, dst, n, pos, Tsph[l4[pos]], nsph(l4[pos]));
-                    double *t = src;
+                    real *t = src;
                     src = dst;
                     dst = t;
                 }
-                size_t ns = (size_t)n[0] * n[1] * n[2] * n[3];
-                memcpy(out + out_off[q], src, ns * sizeof(double));
-            }
+            size_t nv = (size_t)n[0] * n[1] * n[2] * n[3];
+            for (size_t x = 0; x < nv; ++x) out[out_off[q] + x] = (double)src[x];
         }
         free(buf1);
         free(buf2);
@@ -552,25 +573,26 @@ int oracle_eri_deriv_quartets(int nshell, const double *centers, const int32_t *
     for (int s = 0; s < nshell; ++s)
         if (l[s] < 0 || l[s] + 1 > OR_LMAX || nprim[s] < 1) return -1;
     int ntot = prim_off[nshell];
-    double *cn = (double *)malloc(sizeof(double) * (ntot > 0 ? ntot : 1));
+    real *cn = (real *)malloc(sizeof(real) * (ntot > 0 ? ntot : 1));
     for (int s = 0; s < nshell; ++s) {
         if (flags & OR_NO_NORMALIZE)
-            memcpy(cn + prim_off[s], coefs + prim_off[s], sizeof(double) * nprim[s]);
+            for (int k = 0; k < nprim[s]; ++k) cn[prim_off[s] + k] = coefs[prim_off[s] + k];
         else
-            oracle_normalize(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
+            normalize_r(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
     }
-    double Tsph[OR_LMAX + 1][17 * 45];
-    for (int L = 0; L <= OR_LMAX; ++L) oracle_sph_coeffs(L, Tsph[L]);
+    real Tsph[OR_LMAX + 1][17 * 45];
+    for (int L = 0; L <= OR_LMAX; ++L) sph_coeffs_r(L, Tsph[L]);
     int bad = 0;
 #pragma omp parallel
     {
         os_work *w = (os_work *)calloc(1, sizeof(os_work));
-        double *buf1 = NULL, *buf2 = NULL, *dbuf = NULL;
+        real *buf1 = NULL, *buf2 = NULL, *dbuf = NULL;
         size_t bcap = 0;
 #pragma omp for schedule(dynamic, 1)
         for (int64_t q = 0; q < nq; ++q) {
             int sh[4], l4[4], K4[4];
-            const double *cen[4], *al[4], *cc[4];
+            const double *cen[4], *al[4];
+            const real *cc[4];
             int ok = 1;
             for (int t = 0; t < 4; ++t) {
                 sh[t] = quartets[4 * q + t];
@@ -593,28 +615,28 @@ int oracle_eri_deriv_quartets(int nshell, const double *centers, const int32_t *
                 free(buf1);
                 free(buf2);
                 free(dbuf);
-                buf1 = (double *)malloc(ncar * sizeof(double));
-                buf2 = (double *)malloc(ncar * sizeof(double));
-                dbuf = (double *)malloc(12 * ncar * sizeof(double));
+                buf1 = (real *)malloc(ncar * sizeof(real));
+                buf2 = (real *)malloc(ncar * sizeof(real));
+                dbuf = (real *)malloc(12 * ncar * sizeof(real));
                 bcap = ncar;
             }
             os_quartet(w, l4, cen, K4, al, cc, NULL, dbuf);
             if (!(flags & OR_SPHERICAL)) {
-                memcpy(out + out_off[q], dbuf, 12 * ncar * sizeof(double));
+                for (size_t x = 0; x < 12 * ncar; ++x) out[out_off[q] + x] = (double)dbuf[x];
                 continue;
             }
             size_t nsp = (size_t)nsph(l4[0]) * nsph(l4[1]) * nsph(l4[2]) * nsph(l4[3]);
             for (int k = 0; k < 12; ++k) {
                 int n[4] = {ncart(l4[0]), ncart(l4[1]), ncart(l4[2]), ncart(l4[3])};
-                memcpy(buf1, dbuf + (size_t)k * ncar, ncar * sizeof(double));
-                double *src = buf1, *dst = buf2;
+                memcpy(buf1, dbuf + (size_t)k * ncar, ncar * sizeof(real));
+                real *src = buf1, *dst = buf2;
                 for (int pos = 0; pos < 4; ++pos) {
                     transform_index(src, dst, n, pos, Tsph[l4[pos]], nsph(l4[pos]));
-                    double *t = src;
+                    real *t = src;
                     src = dst;
                     dst = t;
                 }
-                memcpy(out + out_off[q] + (size_t)k * nsp, src, nsp * sizeof(double));
+                for (size_t x = 0; x < nsp; ++x) out[out_off[q] + (size_t)k * nsp + x] = (double)src[x];
             }
         }
         free(buf1);

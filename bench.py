@@ -109,7 +109,7 @@ def back_to_back(fn, n, stream):
 
 
 def clock_under_load(fn, seconds=1.0):
-    """GPU clocks as rocm-smi reports them while fn() runs back to back for about `seconds`."""
+    """GPU clocks and power as sysfs reports them while fn() runs back to back for about `seconds`."""
     import threading
     import torch
     box = {}
@@ -128,18 +128,39 @@ def clock_under_load(fn, seconds=1.0):
     return box.get("clocks")
 
 
-def gpu_clocks():
-    """Current shader and memory clocks as rocm-smi reports them (None if it is unavailable)."""
-    import subprocess
+def _read(path):
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        d = json.loads(r.stdout)
-    except Exception:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
         return None
-    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
-    keep = ("sclk", "mclk", "power")
-    return {k: v for k, v in card.items() if any(x in k.lower() for x in keep)} or None
+
+
+def gpu_clocks():
+    """Current shader and memory clock levels and average power of the AMD GPUs,
+    read in-process from the amdgpu driver's sysfs files (pp_dpm_sclk / pp_dpm_mclk:
+    the level marked '*'; hwmon power1_average in microwatts).  None if none is readable."""
+    import glob
+    cards = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if _read(os.path.join(dev, "vendor")) != "0x1002":
+            continue
+        info = {}
+        for key in ("sclk", "mclk"):
+            txt = _read(os.path.join(dev, f"pp_dpm_{key}"))
+            if txt:
+                cur = [ln.split(":", 1)[1].strip(" *") for ln in txt.splitlines() if ln.rstrip().endswith("*")]
+                if cur:
+                    info[key] = cur[0]
+        for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*")):
+            for fn in ("power1_average", "power1_input"):
+                v = _read(os.path.join(hw, fn))
+                if v and v.isdigit():
+                    info["power_W"] = int(v) / 1e6
+                    break
+        if info:
+            cards[os.path.basename(os.path.dirname(dev))] = info
+    return cards or None
 
 
 def _block_flops(plan, w, imap):

@@ -126,24 +126,36 @@ def _alloc_slots(kv):
 # code pieces
 # ---------------------------------------------------------------------------
 
-def _stage1_selectors(ci: ClassInfo, lines, stride, one_field, zero_field, ind="  "):
+def _stage1_selectors(ci: ClassInfo, lines, stride, one_field, zero_field, ind="  ", compact=None):
     """Per-lane record offsets of the bra-path factors: step s of lane e moves
     along axis ax_s, so it needs (P-A)_ax (record field ax) and (W-P)_ax (field
     3 + ax); a lane whose path is shorter than the step reads the constant
     fields 1 and 0, which leave its values unchanged.  Loop-invariant ints:
-    each step then costs two LDS reads instead of selects among six doubles."""
+    each step then costs two LDS reads instead of selects among six doubles.
+    compact="all": the two offsets and the step's lowering count n (bits 0-11,
+    12-23 and 24-26) share one int per step, unpacked inside the primitive loop:
+    one register per step instead of four across the loop."""
     for s in range(1, ci.Lb + 1):
         lines.append(f"{ind}const int ax{s} = ({s} <= ex) ? 0 : ({s} <= ex + ey) ? 1 : ({s} <= es) ? 2 : 3;")
-        lines.append(f"{ind}const int sel1_{s} = (ax{s} < 3 ? ax{s} : {one_field}) * {stride};")
-        lines.append(f"{ind}const int sel2_{s} = (ax{s} < 3 ? 3 + ax{s} : {zero_field}) * {stride};")
-        lines.append(f"{ind}const double gnf{s} = (double)(ax{s} == 0 ? {s - 1} : ax{s} == 1 ? {s - 1} - ex : "
-                     f"ax{s} == 2 ? {s - 1} - ex - ey : 0);")
+        sel1 = f"(ax{s} < 3 ? ax{s} : {one_field}) * {stride}"
+        sel2 = f"(ax{s} < 3 ? 3 + ax{s} : {zero_field}) * {stride}"
+        gnf = f"(ax{s} == 0 ? {s - 1} : ax{s} == 1 ? {s - 1} - ex : ax{s} == 2 ? {s - 1} - ex - ey : 0)"
+        if compact == "all":
+            if s == 1:
+                lines.append(f"{ind}static_assert(({one_field} + 1) * {stride} <= 4096 && "
+                             f"({zero_field} + 1) * {stride} <= 4096 && {ci.Lb} <= 8, \"selector fields\");")
+            lines.append(f"{ind}const int selp{s} = ({sel1}) | (({sel2}) << 12) | ({gnf} << 24);")
+            continue
+        lines.append(f"{ind}const int sel1_{s} = {sel1};")
+        lines.append(f"{ind}const int sel2_{s} = {sel2};")
+        lines.append(f"{ind}const double gnf{s} = (double){gnf};")
 
 
-def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None):
+def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None, compact=None):
     """Bra phase for the lane's own e: [e0|00]^(m), m = 0..base_m, from F_m.
     rsel: name of this lane's record pointer (factors read through the
-    selectors of _stage1_selectors); otherwise selects on PAx.. WPz."""
+    selectors of _stage1_selectors, packed ones with compact); otherwise
+    selects on PAx.. WPz."""
     L = ci.L
     for m in range(L + 1):
         lines.append(f"{ind}double c{m} = F[{m}];")
@@ -156,7 +168,14 @@ def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None):
     for s in range(1, ci.Lb + 1):
         top = L - s
         lines.append(f"{ind}{{ // bra step {s}")
-        if rsel is not None:
+        if rsel is not None and compact == "all":
+            # the empty asm makes the packed selector opaque in the loop, so that
+            # its unpacked fields are not hoisted out as loop invariants again
+            lines.append(f"{ind}  int sp = selp{s};")
+            lines.append(f'{ind}  asm volatile("" : "+v"(sp));')
+            lines.append(f"{ind}  const double g1 = {rsel}[sp & 4095], g2 = {rsel}[(sp >> 12) & 4095];")
+            lines.append(f"{ind}  const double gn = (double)(sp >> 24) * i2z;")
+        elif rsel is not None:
             lines.append(f"{ind}  const double g1 = {rsel}[sel1_{s}], g2 = {rsel}[sel2_{s}];")
             lines.append(f"{ind}  const double gn = gnf{s} * i2z;")
         else:

@@ -383,6 +383,21 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
 PACK_CH = 21  # primitive quartets per quartet set up together (one lane each)
 
 
+# Register form of the contracted kernels.  With loop-invariant selectors (two
+# offsets and a lowering count per bra step) and the set-up lanes' pair records
+# kept across the primitive loop, the contracted (dd|dd) kernel needs a few
+# registers over the 256 of two waves per SIMD and spilled 52 B per lane.  For
+# it the selectors are packed into one int per step and the set-up state is
+# re-read at every chunk (250 registers, nothing spilled); measured on the
+# 120-atom cluster that form is 1.5% slower for (dd|dd) and 2-10% slower for
+# the classes that do not spill, which keep the plain form.
+COMPACT_CONTRACTED = {(2, 2, 2, 2)}
+
+
+def _compact(ci: ClassInfo) -> bool:
+    return (ci.la, ci.lb, ci.lc, ci.ld) in COMPACT_CONTRACTED
+
+
 def _chunk(Q, NT, ch=PACK_CH):
     return max(1, min(ch, NT // Q))
 
@@ -493,7 +508,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o += lane_dec
     o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
     o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
-    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)
+    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1, compact="all" if _compact(ci) else None)
     o.append("  const int g = blockIdx.x;")
     o.append("  const int q0 = g * Q;")
     o.append("  // this lane's quartet (the spare lanes and a short last group repeat a valid one)")
@@ -504,10 +519,11 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o.append("  // the quartet whose primitive quartets this lane sets up")
     o.append("  const int qsi = tid / CH < Q ? tid / CH : Q - 1;")
     o.append("  const int qs = q0 + qsi < a.nq ? q0 + qsi : a.nq - 1;")
-    o.append("  const int4 pbs = a.pair_info[a.qbra[qs]], pks = a.pair_info[a.qket[qs]];")
-    o.append("  const double ACx = a.cen[3 * pbs.x] - a.cen[3 * pks.x], ACy = a.cen[3 * pbs.x + 1] - a.cen[3 * pks.x + 1],"
-             " ACz = a.cen[3 * pbs.x + 2] - a.cen[3 * pks.x + 2];")
-    o.append("  const int K4s = pbs.w * pks.w;")
+    if not _compact(ci):
+        o.append("  const int4 pbs = a.pair_info[a.qbra[qs]], pks = a.pair_info[a.qket[qs]];")
+        o.append("  const double ACx = a.cen[3 * pbs.x] - a.cen[3 * pks.x], ACy = a.cen[3 * pbs.x + 1] - a.cen[3 * pks.x + 1],"
+                 " ACz = a.cen[3 * pbs.x + 2] - a.cen[3 * pks.x + 2];")
+        o.append("  const int K4s = pbs.w * pks.w;")
     o.append("  __syncthreads();")
     o.append("  int K4max = k4q[0];")
     o.append("  for (int i = 1; i < Q; ++i) K4max = k4q[i] > K4max ? k4q[i] : K4max;")
@@ -517,6 +533,13 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o.append("  for (int c0 = 0; c0 < K4max; c0 += CH) {")
     o.append("    if (c0 > 0) __syncthreads();  // the previous chunk's records are consumed")
     o.append("    if (tid < NRL) {")
+    if _compact(ci):
+        o.append("      // pair records and centres re-read per chunk (cached): nothing of the set-up")
+        o.append("      // stays live in registers across the primitive loop")
+        o.append("      const int4 pbs = a.pair_info[a.qbra[qs]], pks = a.pair_info[a.qket[qs]];")
+        o.append("      const double ACx = a.cen[3 * pbs.x] - a.cen[3 * pks.x], ACy = a.cen[3 * pbs.x + 1] - a.cen[3 * pks.x + 1],"
+                 " ACz = a.cen[3 * pbs.x + 2] - a.cen[3 * pks.x + 2];")
+        o.append("      const int K4s = pbs.w * pks.w;")
     o.append("      const int p = c0 + (tid - qsi * CH);")
     o.append("      const int t = p < K4s ? p : K4s - 1;")
     o.append("      const int ib = t / pks.w, ik = t - ib * pks.w;")
@@ -549,7 +572,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
     o.append("      (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
     o.append("      (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-    _stage1(ci, kv.base_m, o, "      ", rsel="r")
+    _stage1(ci, kv.base_m, o, "      ", rsel="r", compact="all" if _compact(ci) else None)
     for t, tg in enumerate(targets):
         if sum(tg[0]) == 0:
             o.append(f"      acc{t} += wgt * s1_{tg[1]};")

@@ -5,7 +5,7 @@ this package is its thin Python binding.  PyTorch provides device memory and
 streams only.
 """
 from ._lib import (  # noqa: F401
-    ERI_IMPLICIT,
+    ERI_MAX_SIDE_STREAMS,
     ERI_NO_NORMALIZE,
     ERI_SPHERICAL,
     EriError,

@@ -2,8 +2,11 @@
 
 Every step of the integral path runs in the HIP library; this module converts
 numpy shell arrays and torch device tensors into the C ABI's plain pointers
-and raises on error codes.  There is no CPU fallback: if the library is
-missing, loading fails with an error that says how to build it.
+and raises on error codes.  The library allocates no device memory: the
+workspaces its calls ask for (size queries with a NULL workspace) are torch
+tensors allocated here and kept alive beside the plan.  There is no CPU
+fallback: if the library is missing, loading fails with an error that says how
+to build it.
 """
 from __future__ import annotations
 
@@ -17,8 +20,9 @@ LIB_PATH = os.path.join(PKG, "liberi_mi355x.so")
 
 ERI_SPHERICAL = 1
 ERI_NO_NORMALIZE = 2
-ERI_IMPLICIT = 4
-ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "capacity", -4: "HIP error", -5: "out of memory"}
+ERI_MAX_SIDE_STREAMS = 3
+ERRORS = {0: "ok", -1: "invalid argument", -2: "unsupported", -3: "capacity", -4: "HIP error", -5: "out of memory",
+          -6: "workspace"}
 
 
 class EriError(RuntimeError):
@@ -58,9 +62,12 @@ def load(path=None):
     vp = ctypes.c_void_p
     i64p = ctypes.POINTER(ctypes.c_int64)
     i32p = ctypes.POINTER(ctypes.c_int32)
+    szp = ctypes.POINTER(ctypes.c_size_t)
     L.eri_build_quartets.argtypes = [ctypes.POINTER(_Shells), ctypes.c_int, i32p, ctypes.c_int64, ctypes.c_double,
-                                     vp, ctypes.POINTER(vp)]
+                                     vp, szp, vp, ctypes.POINTER(vp)]
     L.eri_build_quartets.restype = ctypes.c_int
+    L.eri_plan_set_streams.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int32]
+    L.eri_plan_set_streams.restype = ctypes.c_int
     L.eri_plan_destroy.argtypes = [vp]
     L.eri_plan_destroy.restype = ctypes.c_int
     L.eri_plan_info.argtypes = [vp, i64p, i64p, i32p, i32p, i64p]
@@ -77,11 +84,11 @@ def load(path=None):
     L.eri_compute_range.restype = ctypes.c_int
     L.eri_plan_quartets.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp]
     L.eri_plan_quartets.restype = ctypes.c_int
-    L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+    L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, szp, vp]
     L.eri_digest_J.restype = ctypes.c_int
-    L.eri_digest_JK.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32, vp]
+    L.eri_digest_JK.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, szp, vp]
     L.eri_digest_JK.restype = ctypes.c_int
-    L.eri_compute_deriv.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64, vp]
+    L.eri_compute_deriv.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64, vp, szp, vp]
     L.eri_compute_deriv.restype = ctypes.c_int
     L.eri_strerror.argtypes = [ctypes.c_int]
     L.eri_strerror.restype = ctypes.c_char_p
@@ -110,11 +117,22 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-class Plan:
-    """A quartet plan owned by the library (freed by close() or garbage collection)."""
+def _workspace(nbytes):
+    """A device workspace of at least nbytes (torch's allocator, 256-byte aligned)."""
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device="cuda")
 
-    def __init__(self, handle):
+
+class Plan:
+    """A quartet plan: the library's host state plus the device workspace (a
+    torch tensor held here) that holds its data; freed by close() or garbage
+    collection."""
+
+    def __init__(self, handle, workspace):
         self._h = handle
+        self.workspace = workspace
+        self._streams = []
+        self._digest_ws = {}
         L = load()
         nq, nout, np_ = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
         nb, nbf = ctypes.c_int32(), ctypes.c_int32()
@@ -143,6 +161,17 @@ class Plan:
         if self._h is not None:
             load().eri_plan_destroy(self._h)
             self._h = None
+        self.workspace = None
+        self._digest_ws = {}
+
+    def set_streams(self, streams):
+        """Side streams (torch.cuda.Stream, at most ERI_MAX_SIDE_STREAMS) on which
+        multi-block calls of this plan may run concurrently with the caller's stream."""
+        streams = list(streams)
+        arr = (ctypes.c_void_p * max(1, len(streams)))(*[s.cuda_stream for s in streams])
+        _check(load().eri_plan_set_streams(self.handle, arr, len(streams)))
+        self._streams = streams
+        self._digest_ws = {}
 
     def __del__(self):
         try:
@@ -170,8 +199,13 @@ class Plan:
         return out
 
 
-def build_quartets(shells, flags: int, quartets=None, tau: float = 0.0, stream=None) -> Plan:
-    """shells: object with centers, l, nprim, prim_off, exps, coefs (host arrays)."""
+def build_quartets(shells, flags: int, quartets=None, tau: float = 0.0, stream=None,
+                   side_streams: int = ERI_MAX_SIDE_STREAMS) -> Plan:
+    """shells: object with centers, l, nprim, prim_off, exps, coefs (host arrays).
+
+    The plan's workspace is a torch tensor sized by the library's query;
+    ``side_streams`` new torch streams (default priority) are registered on the
+    plan for its multi-block calls."""
     L = load()
     c = np.ascontiguousarray(shells.centers, dtype=np.float64)
     l = np.ascontiguousarray(shells.l, dtype=np.int32)
@@ -190,9 +224,19 @@ def build_quartets(shells, flags: int, quartets=None, tau: float = 0.0, stream=N
         qptr = q.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         nq = len(q)
     h = ctypes.c_void_p()
-    _check(L.eri_build_quartets(ctypes.byref(sh), int(flags), qptr, nq, float(tau), _stream_handle(stream),
-                                ctypes.byref(h)))
-    return Plan(h)
+    nbytes = ctypes.c_size_t(0)
+    st = _stream_handle(stream)
+    _check(L.eri_build_quartets(ctypes.byref(sh), int(flags), qptr, nq, float(tau), None, ctypes.byref(nbytes), st,
+                                None))
+    ws = _workspace(nbytes.value)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(L.eri_build_quartets(ctypes.byref(sh), int(flags), qptr, nq, float(tau), _ptr(ws), ctypes.byref(nbytes),
+                                st, ctypes.byref(h)))
+    plan = Plan(h, ws)
+    if side_streams:
+        import torch
+        plan.set_streams([torch.cuda.Stream() for _ in range(int(side_streams))])
+    return plan
 
 
 def compute_batch(plan: Plan, out, block_begin: int = 0, block_end: int | None = None, stream=None):
@@ -216,24 +260,52 @@ def compute_deriv(plan: Plan, out, first: int = 0, count: int | None = None, str
     [first, first + count) into the float64 device tensor ``out``."""
     if count is None:
         count = plan.n_quartets - first
-    _check(load().eri_compute_deriv(plan.handle, int(first), int(count), _ptr(out), out.numel(),
-                                    _stream_handle(stream)))
+    L = load()
+    st = _stream_handle(stream)
+    nbytes = ctypes.c_size_t(0)
+    _check(L.eri_compute_deriv(plan.handle, int(first), int(count), None, 0, None, ctypes.byref(nbytes), st))
+    ws = _workspace(nbytes.value)
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(L.eri_compute_deriv(plan.handle, int(first), int(count), _ptr(out), out.numel(), _ptr(ws),
+                               ctypes.byref(nbytes), st))
     return out
+
+
+def _digest_workspace(plan: Plan, key, query):
+    """The plan's digestion workspace for (J, K) wanted, sized by the library's
+    query and kept for later calls of the same kind."""
+    ws = plan._digest_ws.get(key)
+    if ws is None:
+        nbytes = ctypes.c_size_t(0)
+        _check(query(ctypes.byref(nbytes)))
+        ws = plan._digest_ws[key] = _workspace(nbytes.value)
+    return ws
 
 
 def digest_J(plan: Plan, D, J, stream=None):
     """J (device, nbf x nbf, float64) from the symmetric density D (device)."""
-    _check(load().eri_digest_J(plan.handle, _ptr(D), int(D.stride(0)), _ptr(J), int(J.stride(0)),
-                               _stream_handle(stream)))
+    L = load()
+    st = _stream_handle(stream)
+    ws = _digest_workspace(plan, (True, False), lambda nb: L.eri_digest_J(plan.handle, None, 0, None, 0, None, nb, st))
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(L.eri_digest_J(plan.handle, _ptr(D), int(D.stride(0)), _ptr(J), int(J.stride(0)), _ptr(ws),
+                          ctypes.byref(nbytes), st))
     return J
 
 
 def digest_JK(plan: Plan, D, J=None, K=None, stream=None):
     """J and/or K (device, nbf x nbf, float64) from the symmetric density D in one pass."""
-    _check(load().eri_digest_JK(plan.handle, _ptr(D), int(D.stride(0)),
-                                _ptr(J) if J is not None else None, int(J.stride(0)) if J is not None else 0,
-                                _ptr(K) if K is not None else None, int(K.stride(0)) if K is not None else 0,
-                                _stream_handle(stream)))
+    L = load()
+    st = _stream_handle(stream)
+    jp = _ptr(J) if J is not None else None
+    kp = _ptr(K) if K is not None else None
+    ldj = int(J.stride(0)) if J is not None else 0
+    ldk = int(K.stride(0)) if K is not None else 0
+    ws = _digest_workspace(plan, (J is not None, K is not None),
+                           lambda nb: L.eri_digest_JK(plan.handle, None, 0, jp, ldj, kp, ldk, None, nb, st))
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(L.eri_digest_JK(plan.handle, _ptr(D), int(D.stride(0)), jp, ldj, kp, ldk, _ptr(ws), ctypes.byref(nbytes),
+                           st))
     return J, K
 
 

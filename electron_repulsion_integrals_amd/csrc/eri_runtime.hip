@@ -6,6 +6,9 @@
 // data ("GAUSSIANPAIRS"), evaluates one angular-momentum class per kernel and
 // scatters into J.  Everything here runs on the device except argument
 // validation and the small class-block bookkeeping the host needs to launch.
+// The library allocates no device memory: plans and calls work in workspaces
+// the caller provides (sizes from the same calls with a NULL workspace); the
+// Boys table and the FMA-rate sink are file-scope device arrays.
 #include <hip/hip_runtime.h>
 #include <hipcub/hipcub.hpp>
 
@@ -14,6 +17,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -51,7 +55,7 @@ __host__ __device__ inline int d_pair_class(int la, int lb)
 }
 
 // ---------------------------------------------------------------------------
-// Boys table (host, long double), one copy per device
+// Boys table (host, long double), one copy in every device's memory
 // ---------------------------------------------------------------------------
 // F_M(T) by its power series in long double, F_M = exp(-T) sum_k (2T)^k /
 // ((2M+1)(2M+3)...(2M+2k+1)), then the downward recursion to F_0.
@@ -68,25 +72,38 @@ void boys_row_host(long double T, int M, long double *F)
     for (int m = M - 1; m >= 0; --m) F[m] = (2.0L * T * F[m + 1] + e) / (2 * m + 1);
 }
 
+}  // namespace
+
+// file-scope device arrays (each device holds its own copy)
+__device__ double g_boys_tab[ERI_BT_ROWS * ERI_BT_COLS];
+__device__ double g_fma_sink[1];
+
+namespace {
+
 std::mutex g_boys_mu;
 std::vector<double *> g_boys_dev;
+std::vector<double> g_boys_host;
 
+// the table on the current device (filled once per device)
 double *boys_table(int device)
 {
     std::lock_guard<std::mutex> lk(g_boys_mu);
     if ((int)g_boys_dev.size() <= device) g_boys_dev.resize(device + 1, nullptr);
     if (g_boys_dev[device]) return g_boys_dev[device];
-    std::vector<double> tab((size_t)ERI_BT_ROWS * ERI_BT_COLS);
-    long double F[ERI_BT_MMAX + 1];
-    for (int k = 0; k < ERI_BT_ROWS; ++k) {
-        long double T = (long double)k / ERI_BT_PER_UNIT;
-        boys_row_host(T, ERI_BT_MMAX, F);
-        tab[(size_t)k * ERI_BT_COLS] = (double)expl(-T);
-        for (int m = 0; m <= ERI_BT_MMAX; ++m) tab[(size_t)k * ERI_BT_COLS + 1 + m] = (double)F[m];
+    if (g_boys_host.empty()) {
+        g_boys_host.resize((size_t)ERI_BT_ROWS * ERI_BT_COLS);
+        long double F[ERI_BT_MMAX + 1];
+        for (int k = 0; k < ERI_BT_ROWS; ++k) {
+            long double T = (long double)k / ERI_BT_PER_UNIT;
+            boys_row_host(T, ERI_BT_MMAX, F);
+            g_boys_host[(size_t)k * ERI_BT_COLS] = (double)expl(-T);
+            for (int m = 0; m <= ERI_BT_MMAX; ++m) g_boys_host[(size_t)k * ERI_BT_COLS + 1 + m] = (double)F[m];
+        }
     }
+    HIP_CHECK(hipMemcpyToSymbol(HIP_SYMBOL(g_boys_tab), g_boys_host.data(), g_boys_host.size() * sizeof(double), 0,
+                                hipMemcpyHostToDevice));
     double *d = nullptr;
-    HIP_CHECK(hipMalloc(&d, tab.size() * sizeof(double)));
-    HIP_CHECK(hipMemcpy(d, tab.data(), tab.size() * sizeof(double), hipMemcpyHostToDevice));
+    HIP_CHECK(hipGetSymbolAddress((void **)&d, HIP_SYMBOL(g_boys_tab)));
     g_boys_dev[device] = d;
     return d;
 }
@@ -344,41 +361,6 @@ __global__ void k_count(int64_t nentries, const BlockDesc *blocks, int nblocks, 
     int64_t c = a;
     if (bd.same) c = c > r ? c - r : 0;
     cnt[e] = c;
-}
-
-__global__ void k_fill_screened(int64_t nentries, const BlockDesc *blocks, int nblocks, const int *porder,
-                                const int64_t *cnt, const int64_t *off, const int4 *pinfo, const int *pair_i,
-                                int *qbra, int *qket, int *qmap)
-{
-    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (e >= nentries) return;
-    int lo = 0, hi = nblocks;
-    while (hi - lo > 1) {
-        int mid = (lo + hi) / 2;
-        if (blocks[mid].entry_base <= e) lo = mid;
-        else hi = mid;
-    }
-    const BlockDesc bd = blocks[lo];
-    const int r = (int)(e - bd.entry_base);
-    const int pb = porder[bd.bra_start + r];
-    const int k0 = bd.same ? r : 0;
-    const int4 ib = pinfo[pb];
-    for (int64_t t = 0; t < cnt[e]; ++t) {
-        const int pk = porder[bd.ket_start + k0 + (int)t];
-        const int64_t s = off[e] + t;
-        qbra[s] = pb;
-        qket[s] = pk;
-        const int4 ik = pinfo[pk];
-        qmap[5 * s] = ib.x;
-        qmap[5 * s + 1] = ib.y;
-        qmap[5 * s + 2] = ik.x;
-        qmap[5 * s + 3] = ik.y;
-        // perm relative to the natural unique form (i >= j, k >= l, pair(ij) >= pair(kl))
-        const int pi_b = pair_i[pb], pi_k = pair_i[pk];
-        const int bswap = ib.x != pi_b ? 1 : 0;  // pair_i holds the larger shell index of the pair
-        const int kswap = ik.x != pi_k ? 1 : 0;
-        qmap[5 * s + 4] = bswap | (kswap << 1) | ((pb < pk ? 1 : 0) << 2);
-    }
 }
 
 // Plan slots [s0, s0 + m) of an implicit screened plan -> bra and ket pair
@@ -650,1090 +632,6 @@ __global__ void k_digest_rows(int64_t n_out, int na, int nb, int nc, int nd, con
     cb[t] = s;
 }
 
-// One workgroup per pair: sum its contribution vectors in a fixed order, then
-// write the J block (and its transpose for two different shells).
-__global__ void __launch_bounds__(RUN_THREADS) k_reduce_pairs(int np, const int4 *pinfo, const int *bf,
-                                                              const int *nfun_sh, const int64_t *seg,
-                                                              const int64_t *ent_off, const double *cb, double *J,
-                                                              int ldj)
-{
-    __shared__ double part[RUN_THREADS];
-    const int p = blockIdx.x;
-    if (p >= np) return;
-    const int4 pi = pinfo[p];
-    const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
-    run_sum(n, seg[p], seg[p + 1], ent_off, cb, part);
-    const int u = threadIdx.x;
-    if (u < n) {
-        const double s = part[u];
-        const int a = u / nb, b = u - a * nb;
-        J[(size_t)(bf[pi.x] + a) * ldj + bf[pi.y] + b] = s;
-        if (pi.x != pi.y) J[(size_t)(bf[pi.y] + b) * ldj + bf[pi.x] + a] = s;
-    }
-}
-
-// entries: (pair key, contribution offset) for every quartet side
-__global__ void k_entries(int64_t nq, const int *qbra, const int *qket, const int64_t *cb_base, const int *blk_of,
-                          const int64_t *blk_start, const int *blk_nab, const int *blk_ncd, int *ekey, int64_t *eoff,
-                          int64_t *nent_out)
-{
-    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= nq) return;
-    const int b = blk_of[s];
-    const int64_t rel = s - blk_start[b];
-    const int nab = blk_nab[b], ncd = blk_ncd[b];
-    const int64_t off = cb_base[b] + rel * (nab + ncd);
-    ekey[2 * s] = qbra[s];
-    eoff[2 * s] = off;
-    if (qbra[s] != qket[s]) {
-        ekey[2 * s + 1] = qket[s];
-        eoff[2 * s + 1] = off + nab;
-    } else {
-        ekey[2 * s + 1] = 0x7fffffff;  // sorts to the end, never read
-        eoff[2 * s + 1] = -1;
-    }
-    (void)nent_out;
-}
-
-__global__ void k_seg_starts(int np, int64_t n, const int *keys, int64_t *seg)
-{
-    const int p = blockIdx.x * blockDim.x + threadIdx.x;
-    if (p > np) return;
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        int64_t mid = (lo + hi) / 2;
-        if (keys[mid] < p) lo = mid + 1;
-        else hi = mid;
-    }
-    seg[p] = lo;
-}
-
-__global__ void k_fill_blk_of(int64_t start, int64_t count, int b, int *blk_of)
-{
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t < count) blk_of[start + t] = b;
-}
-
-inline unsigned nblk(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// plan
-// ---------------------------------------------------------------------------
-
-struct EriBlock {
-    int cid;
-    int64_t start, count, out_off;
-    int64_t n_k1;  // leading quartets with K_a K_b K_c K_d = 1
-    int na, nb, nc, nd;  // functions per shell of the class (spherical or Cartesian)
-};
-
-struct eri_plan {
-    int flags = 0;
-    bool sph = false;
-    bool screened = false;
-    int device = 0;
-    int nshell = 0, nbf = 0;
-    int64_t npairs = 0, nq = 0, nout = 0;
-    double *d_cen = nullptr, *d_exps = nullptr, *d_cn = nullptr, *d_ppd = nullptr, *d_S = nullptr;
-    int *d_l = nullptr, *d_nprim = nullptr, *d_off = nullptr, *d_bf = nullptr, *d_nfun = nullptr;
-    int4 *d_pinfo = nullptr;
-    int *d_qbra = nullptr, *d_qket = nullptr, *d_qmap = nullptr;
-    int64_t *d_qsrc = nullptr;  // explicit plans: input position of the quartet in each slot
-    double *d_boys = nullptr;
-    double *d_scratch = nullptr;
-    int scratch_wgs = 0;
-    long long scratch_doubles = 0;  // per workgroup slice
-    int grid_cap = 2048;            // persistent register-tier grid (8 workgroups per CU)
-    std::vector<EriBlock> blocks;
-    std::vector<void *> allocs;
-    // implicit screened plans: per (block, bra rank) ket-prefix counts
-    bool implicit = false;
-    BlockDesc *d_bd = nullptr;
-    int nbd = 0;
-    int64_t nent = 0;
-    int64_t *d_ent_off = nullptr;
-    int *d_porder = nullptr, *d_pair_i = nullptr;
-    int64_t chunk_q = 1 << 22;         // quartets per internal chunk
-    int *d_cqbra = nullptr, *d_cqket = nullptr;  // chunk lists (plan-owned: calls on one plan do not overlap)
-    // chunked J work (implicit plans, built on first use)
-    // chunked J/K work, one set per stream lane (built on first use)
-    struct ChunkLane {
-        double *ints = nullptr, *cb = nullptr;        // integrals and J contribution vectors of a chunk
-        double *kv = nullptr;                         // K contribution vectors of a chunk
-        double *J = nullptr, *A = nullptr;            // lane accumulators (lane 0: the caller's J, d_kacc)
-        int *ek = nullptr, *ek2 = nullptr, *ruk = nullptr, *rlen = nullptr, *rst = nullptr, *nruns = nullptr;
-        int64_t *eo = nullptr, *eo2 = nullptr;
-        int *qbra = nullptr, *qket = nullptr;         // slot lists of an implicit plan's chunk
-        void *tmp = nullptr;
-        size_t tmp_bytes = 0;
-    };
-    std::vector<ChunkLane> clanes;
-    int64_t c_co = 0, c_cb = 0;  // doubles per lane: integrals, contribution vectors
-    double *d_kacc = nullptr;    // A (K = A + A^T)
-    // J digestion work (screened plans, built on first use)
-    bool jready = false;
-    double *d_ints = nullptr, *d_cb = nullptr;
-    int64_t *d_seg = nullptr, *d_eoff = nullptr;
-    // side streams of the multi-block calls (created on first use, default priority)
-    static constexpr int NSIDE = 3;
-    hipStream_t side[NSIDE] = {};
-    hipEvent_t ev_fork = nullptr, ev_side[NSIDE] = {};
-    bool side_ready = false;
-
-    template <class T>
-    T *alloc(size_t n)
-    {
-        void *p = nullptr;
-        if (n == 0) n = 1;
-        hipError_t e = hipMalloc(&p, n * sizeof(T));
-        if (e != hipSuccess) {
-            g_last_error = std::string("hipMalloc: ") + hipGetErrorString(e);
-            throw HipFail{e};
-        }
-        allocs.push_back(p);
-        return (T *)p;
-    }
-    ~eri_plan()
-    {
-        if (side_ready) {
-            for (int i = 0; i < NSIDE; ++i) {
-                (void)hipStreamSynchronize(side[i]);
-                (void)hipStreamDestroy(side[i]);
-                (void)hipEventDestroy(ev_side[i]);
-            }
-            (void)hipEventDestroy(ev_fork);
-        }
-        for (void *p : allocs) (void)hipFree(p);
-    }
-};
-
-namespace {
-
-template <class T>
-void upload(T *dst, const T *src, size_t n, hipStream_t s)
-{
-    if (n) HIP_CHECK(hipMemcpyAsync(dst, src, n * sizeof(T), hipMemcpyHostToDevice, s));
-}
-
-// one device-wide exclusive scan of int64 counts
-void scan_i64(const int64_t *in, int64_t *out, int64_t n, hipStream_t s)
-{
-    size_t tmp = 0;
-    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp, in, out, (int)n, s));
-    void *t = nullptr;
-    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
-    hipError_t e = hipcub::DeviceScan::ExclusiveSum(t, tmp, in, out, (int)n, s);
-    (void)hipStreamSynchronize(s);
-    (void)hipFree(t);
-    HIP_CHECK(e);
-}
-
-void scan_i32(const int *in, int *out, int64_t n, hipStream_t s)
-{
-    size_t tmp = 0;
-    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, tmp, in, out, (int)n, s));
-    void *t = nullptr;
-    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
-    hipError_t e = hipcub::DeviceScan::ExclusiveSum(t, tmp, in, out, (int)n, s);
-    (void)hipStreamSynchronize(s);
-    (void)hipFree(t);
-    HIP_CHECK(e);
-}
-
-template <class V>
-void sort_pairs_u64(uint64_t *keys_in, uint64_t *keys_out, V *v_in, V *v_out, int64_t n, hipStream_t s)
-{
-    size_t tmp = 0;
-    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 64, s));
-    void *t = nullptr;
-    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
-    hipError_t e = hipcub::DeviceRadixSort::SortPairs(t, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 64, s);
-    (void)hipStreamSynchronize(s);
-    (void)hipFree(t);
-    HIP_CHECK(e);
-}
-
-template <class V>
-void sort_pairs_i32(int *keys_in, int *keys_out, V *v_in, V *v_out, int64_t n, hipStream_t s)
-{
-    size_t tmp = 0;
-    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 32, s));
-    void *t = nullptr;
-    HIP_CHECK(hipMalloc(&t, tmp ? tmp : 1));
-    hipError_t e = hipcub::DeviceRadixSort::SortPairs(t, tmp, keys_in, keys_out, v_in, v_out, (int)n, 0, 32, s);
-    (void)hipStreamSynchronize(s);
-    (void)hipFree(t);
-    HIP_CHECK(e);
-}
-
-// output kind of the class kernels a plan launches (the unfused-spherical
-// ablation build runs the Cartesian kernels for spherical plans)
-inline bool kernel_sph(const eri_plan *P)
-{
-#ifdef ERI_UNFUSED_SPHERICAL
-    return false;
-#else
-    return P->sph;
-#endif
-}
-
-void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, const int *qket, int64_t n, double *out,
-                       hipStream_t s, int64_t n_k1)
-{
-    const EriClassEntry *ce = find_class(cid, sph);
-    if (!ce) {
-        g_last_error = "no kernel for class " + std::to_string(cid);
-        throw HipFail{hipErrorInvalidValue};
-    }
-    EriClassArgs a;
-    a.qbra = qbra;
-    a.qket = qket;
-    a.pair_info = P->d_pinfo;
-    a.ppd = P->d_ppd;
-    a.cen = P->d_cen;
-    a.boys = P->d_boys;
-    a.scratch = P->d_scratch;
-    a.scratch_wgs = P->scratch_wgs;
-    a.grid_cap = P->grid_cap;
-    const int blk = nfun(ce->la, sph) * nfun(ce->lb, sph) * nfun(ce->lc, sph) * nfun(ce->ld, sph);
-    if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
-        g_last_error = "memory-tier class without scratch";
-        throw HipFail{hipErrorInvalidValue};
-    }
-    // the uncontracted prefix goes to the K4 = 1 kernel; large ranges are split so
-    // that every grid stays within int range
-    const int64_t CH = 1 << 26;
-    for (int part = 0; part < 2; ++part) {
-        const int64_t lo = part == 0 ? 0 : n_k1, hi = part == 0 ? n_k1 : n;
-        for (int64_t b = lo; b < hi; b += CH) {
-            const int64_t m = std::min(CH, hi - b);
-            a.qbra = qbra + b;
-            a.qket = qket + b;
-            a.nq = (int)m;
-            a.out = out + b * blk;
-            (part == 0 ? ce->launch_k1 : ce->launch)(a, s);
-            HIP_CHECK(hipGetLastError());
-        }
-    }
-}
-
-#ifdef ERI_UNFUSED_SPHERICAL
-// Ablation build only (the "no spherical fusion" variant of section V-B of
-// "FusionRCG"): a spherical block is computed as its Cartesian block, written
-// out, and then transformed on all four indices, Eq. (17), instead of the
-// stepwise fusion of Eq. (14).  One workgroup per quartet, four one-index
-// passes through two work buffers.
-__global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const double *cart, double *w0, double *w1,
-                              double *dst)
-{
-    const int64_t t = blockIdx.x;
-    if (t >= n) return;
-    const int l4[4] = {la, lb, lc, ld};
-    int dims[4], ns[4];
-    for (int k = 0; k < 4; ++k) {
-        dims[k] = (l4[k] + 1) * (l4[k] + 2) / 2;
-        ns[k] = 2 * l4[k] + 1;
-    }
-    const int64_t ncar = (int64_t)dims[0] * dims[1] * dims[2] * dims[3];
-    const int nsp = ns[0] * ns[1] * ns[2] * ns[3];
-    const double *in = cart + t * ncar;
-    for (int pos = 0; pos < 4; ++pos) {
-        int before = 1, after = 1;
-        for (int k = 0; k < pos; ++k) before *= dims[k];
-        for (int k = pos + 1; k < 4; ++k) after *= dims[k];
-        const double *T = eri_sph_T[l4[pos]];
-        const int nc = dims[pos], nsv = ns[pos];
-        double *o = pos == 3 ? dst + t * nsp : ((pos % 2 == 0) ? w0 : w1) + t * ncar;
-        const int total = before * nsv * after;
-        for (int x = threadIdx.x; x < total; x += blockDim.x) {
-            const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
-            double acc = 0.0;
-            for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
-            o[x] = acc;
-        }
-        dims[pos] = nsv;
-        in = o;
-        __syncthreads();
-    }
-}
-
-// work buffers of the unfused path, grown on demand and kept for the process
-// (calls on different streams must not overlap)
-double *g_unfused_buf = nullptr;
-int64_t g_unfused_cap = 0;
-
-void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
-                  int64_t n_k1 = 0)
-{
-    if (!P->sph) {
-        launch_class_kind(P, cid, false, qbra, qket, n, out, s, n_k1);
-        return;
-    }
-    const EriClassEntry *ce = find_class(cid, false);
-    if (!ce) {
-        g_last_error = "no kernel for class " + std::to_string(cid);
-        throw HipFail{hipErrorInvalidValue};
-    }
-    const int64_t nc = (int64_t)ncart(ce->la) * ncart(ce->lb) * ncart(ce->lc) * ncart(ce->ld);
-    const int64_t ns = (int64_t)nsph(ce->la) * nsph(ce->lb) * nsph(ce->lc) * nsph(ce->ld);
-    const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(n, ((int64_t)1 << 26) / nc));
-    if (g_unfused_cap < 3 * chunk * nc) {
-        HIP_CHECK(hipStreamSynchronize(s));
-        if (g_unfused_buf) HIP_CHECK(hipFree(g_unfused_buf));
-        g_unfused_buf = nullptr;
-        g_unfused_cap = 0;
-        HIP_CHECK(hipMalloc(&g_unfused_buf, 3 * chunk * nc * sizeof(double)));
-        g_unfused_cap = 3 * chunk * nc;
-    }
-    double *cart = g_unfused_buf, *w0 = cart + chunk * nc, *w1 = w0 + chunk * nc;
-    for (int64_t b = 0; b < n; b += chunk) {
-        const int64_t m = std::min(chunk, n - b);
-        const int64_t k1 = std::min(m, std::max<int64_t>(0, n_k1 - b));
-        launch_class_kind(P, cid, false, qbra + b, qket + b, m, cart, s, k1);
-        hipLaunchKernelGGL(k_sph_unfused, dim3((unsigned)m), dim3(256), 0, s, m, ce->la, ce->lb, ce->lc, ce->ld, cart,
-                           w0, w1, out + b * ns);
-        HIP_CHECK(hipGetLastError());
-    }
-}
-#else
-void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
-                  int64_t n_k1 = 0)
-{
-    launch_class_kind(P, cid, P->sph, qbra, qket, n, out, s, n_k1);
-}
-#endif
-
-// quartet lists of plan slots [s, s + m): the plan's own arrays, or for an
-// implicit plan the chunk buffers after expansion (m <= chunk_q)
-void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const int **qk, hipStream_t st,
-                int *dqb = nullptr, int *dqk = nullptr)
-{
-    if (!P->implicit) {
-        *qb = P->d_qbra + s;
-        *qk = P->d_qket + s;
-        return;
-    }
-    if (!dqb) {
-        dqb = P->d_cqbra;
-        dqk = P->d_cqket;
-    }
-    hipLaunchKernelGGL(k_expand, dim3(nblk(m, 256)), dim3(256), 0, st, s, m, P->nent, P->d_ent_off, P->d_bd, P->nbd,
-                       P->d_porder, P->d_pinfo, P->d_pair_i, dqb, dqk, (int *)nullptr);
-    HIP_CHECK(hipGetLastError());
-    *qb = dqb;
-    *qk = dqk;
-}
-
-// integrals of quartets [first, first + count) of block B into out
-// Calls over several class blocks of an explicit plan spread the blocks over
-// the caller's stream and the plan's side streams, so that the last waves of
-// one class kernel overlap the first waves of the next; the caller's stream
-// then waits for the side streams.  Blocks of memory-tier classes that use the
-// plan's scratch stay on the caller's stream, one after another.
-bool use_side_streams(const eri_plan *P)
-{
-#ifdef ERI_UNFUSED_SPHERICAL
-    (void)P;
-    return false;  // the unfused path shares one work buffer
-#else
-    return !P->implicit;  // implicit plans expand slots into plan-owned lists
-#endif
-}
-
-void side_fork(eri_plan *P, hipStream_t s)
-{
-    if (!P->side_ready) {
-        for (int i = 0; i < eri_plan::NSIDE; ++i) {
-            HIP_CHECK(hipStreamCreateWithFlags(&P->side[i], hipStreamNonBlocking));
-            HIP_CHECK(hipEventCreateWithFlags(&P->ev_side[i], hipEventDisableTiming));
-        }
-        HIP_CHECK(hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming));
-        P->side_ready = true;
-    }
-    HIP_CHECK(hipEventRecord(P->ev_fork, s));
-    for (int i = 0; i < eri_plan::NSIDE; ++i) HIP_CHECK(hipStreamWaitEvent(P->side[i], P->ev_fork, 0));
-}
-
-void side_join(eri_plan *P, hipStream_t s)
-{
-    for (int i = 0; i < eri_plan::NSIDE; ++i) {
-        HIP_CHECK(hipEventRecord(P->ev_side[i], P->side[i]));
-        HIP_CHECK(hipStreamWaitEvent(s, P->ev_side[i], 0));
-    }
-}
-
-hipStream_t block_stream(const eri_plan *P, const EriBlock &B, int idx, hipStream_t s)
-{
-    const EriClassEntry *ce = find_class(B.cid, kernel_sph(P));
-    if (ce && ce->tier == 'M' && ce->scratch_doubles > 0) return s;
-    const int k = idx % (eri_plan::NSIDE + 1);
-    return k == 0 ? s : P->side[k - 1];
-}
-
-void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t count, double *out, hipStream_t st)
-{
-    const int64_t blk = (int64_t)B.na * B.nb * B.nc * B.nd;
-    const int64_t step = P->implicit ? P->chunk_q : std::max<int64_t>(count, 1);
-    for (int64_t c = first; c < first + count; c += step) {
-        const int64_t m = std::min(step, first + count - c);
-        const int *qb = nullptr, *qk = nullptr;
-        slot_lists(P, B.start + c, m, &qb, &qk, st);
-        const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
-        launch_class(P, B.cid, qb, qk, m, out + (c - first) * blk, st, nk1);
-    }
-}
-
-// J and/or K, chunk by chunk: integrals of the chunk, per-quartet
-// contribution vectors, entries sorted by target (stable), then each target's
-// run added in entry order.  Chunks go in plan order, so the sums are
-// deterministic.  Used for implicit plans (J) and for K with any plan.
-__global__ void k_add_mat(int n, const double *X, int ldx, double *Y, int ldy)
-{
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= (int64_t)n * n) return;
-    const int x = (int)(t / n), y = (int)(t - (int64_t)x * n);
-    Y[(size_t)x * ldy + y] += X[(size_t)x * ldx + y];
-}
-
-// The chunks are spread over stream lanes: the caller's stream and the plan's
-// side streams, each with its own chunk buffers and its own J and A
-// accumulators, chunk i of the plan going to lane i mod (number of lanes)
-// (chunks of memory-tier classes that use the plan's scratch all go to lane
-// 0).  After the lanes join, lanes 1, 2, ... are added into lane 0's J and A
-// in that order, so the sums stay deterministic.
-void digest_JK_chunked(eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, hipStream_t s)
-{
-#ifdef ERI_UNFUSED_SPHERICAL
-    const int NL = 1;  // the unfused path shares one work buffer
-#else
-    const int NL = eri_plan::NSIDE + 1;
-#endif
-    const int64_t CQ = P->chunk_q;
-    const int64_t NE = 4 * CQ;  // entries per chunk: two per quartet for J, four for K
-    const int n = P->nbf;
-    if (P->clanes.empty()) {
-        // per lane: 2^26 integral doubles and 2^25 contribution doubles (2^27 and 2^26 with one lane)
-        P->c_co = int64_t(1) << (NL > 1 ? 26 : 27);
-        P->c_cb = int64_t(1) << (NL > 1 ? 25 : 26);
-        P->clanes.resize(NL);
-        for (int l = 0; l < NL; ++l) {
-            eri_plan::ChunkLane &W = P->clanes[l];
-            W.ints = P->alloc<double>(P->c_co);
-            W.cb = P->alloc<double>(P->c_cb);
-            W.ek = P->alloc<int>(NE);
-            W.ek2 = P->alloc<int>(NE);
-            W.eo = P->alloc<int64_t>(NE);
-            W.eo2 = P->alloc<int64_t>(NE);
-            W.ruk = P->alloc<int>(NE);
-            W.rlen = P->alloc<int>(NE);
-            W.rst = P->alloc<int>(NE);
-            W.nruns = P->alloc<int>(1);
-            if (P->implicit) {
-                W.qbra = P->alloc<int>(CQ);
-                W.qket = P->alloc<int>(CQ);
-            }
-            size_t t1 = 0, t2 = 0, t3 = 0;
-            const int n2 = (int)NE;
-            HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, s));
-            HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, W.ek2, W.ruk, W.rlen, W.nruns, n2, s));
-            HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, W.rlen, W.rst, n2, s));
-            W.tmp_bytes = std::max(t1, std::max(t2, t3));
-            W.tmp = P->alloc<char>(W.tmp_bytes);
-            if (l > 0) W.J = P->alloc<double>((size_t)n * n);
-        }
-    }
-    if (K && !P->d_kacc) {
-        P->d_kacc = P->alloc<double>((size_t)n * n);
-        for (int l = 0; l < NL; ++l) {
-            P->clanes[l].kv = P->alloc<double>(P->c_cb);
-            P->clanes[l].A = l == 0 ? P->d_kacc : P->alloc<double>((size_t)n * n);
-        }
-    }
-    const int64_t CO = P->c_co, CB = P->c_cb;
-    side_fork(P, s);
-    auto lane_stream = [&](int l) { return l == 0 ? s : P->side[l - 1]; };
-    for (int l = 0; l < NL; ++l) {
-        const hipStream_t ls = lane_stream(l);
-        eri_plan::ChunkLane &W = P->clanes[l];
-        double *Jl = l == 0 ? J : W.J;
-        const int ldl = l == 0 ? ldj : n;
-        if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, Jl, ldl);
-        if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, W.A, n);
-        HIP_CHECK(hipGetLastError());
-    }
-    int64_t chunk_index = 0;
-    for (const EriBlock &B : P->blocks) {
-        const int nab = B.na * B.nb, ncd = B.nc * B.nd;
-        const int nkv = B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd;
-        const int64_t blk = (int64_t)nab * ncd;
-        const int64_t step = std::max<int64_t>(
-            1, std::min(std::min(CQ, CO / blk), std::min(CB / (nab + ncd), CB / nkv)));
-        const EriClassEntry *ce = find_class(B.cid, kernel_sph(P));
-        const bool scratch_class = ce && ce->tier == 'M' && ce->scratch_doubles > 0;
-        for (int64_t c = 0; c < B.count; c += step, ++chunk_index) {
-            const int l = scratch_class ? 0 : (int)(chunk_index % NL);
-            const hipStream_t ls = lane_stream(l);
-            eri_plan::ChunkLane &W = P->clanes[l];
-            double *Jl = l == 0 ? J : W.J;
-            const int ldl = l == 0 ? ldj : n;
-            const int64_t m = std::min(step, B.count - c);
-            const int *qb = nullptr, *qk = nullptr;
-            slot_lists(P, B.start + c, m, &qb, &qk, ls, W.qbra, W.qket);
-            const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
-            launch_class(P, B.cid, qb, qk, m, W.ints, ls, nk1);
-            // sort the n2 entries in W.ek/W.eo and encode their runs
-            auto sort_runs = [&](int n2) {
-                size_t tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, ls));
-                tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
-                tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(W.tmp, tb, W.rlen, W.rst, n2, ls));
-            };
-            if (J) {
-                const int64_t nv = m * (nab + ncd);
-                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, ls, nv, B.na, B.nb,
-                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb);
-                hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, nab, ncd,
-                                   W.ek, W.eo);
-                HIP_CHECK(hipGetLastError());
-                sort_runs((int)(2 * m));
-                // at most one run per pair key (and one for the sentinel key); workgroups
-                // past the device-side run count exit at once
-                const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
-                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
-                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, Jl, ldl);
-                HIP_CHECK(hipGetLastError());
-            }
-            if (K) {
-                const int64_t nkt = m * nkv;
-                hipLaunchKernelGGL(k_kdigest_rows, dim3((unsigned)nblk(nkt, 256)), dim3(256), 0, ls, nkt, B.na, B.nb,
-                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.kv);
-                hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, P->d_pinfo,
-                                   P->nshell, B.na, B.nb, B.nc, B.nd, W.ek, W.eo);
-                HIP_CHECK(hipGetLastError());
-                sort_runs((int)(4 * m));
-                // at most one run per target block key (and one for the sentinel key)
-                const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
-                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk,
-                                   W.rst, W.rlen, W.eo2, W.kv, P->nshell, P->d_bf, P->d_nfun, W.A, n);
-                HIP_CHECK(hipGetLastError());
-            }
-        }
-    }
-    side_join(P, s);
-    for (int l = 1; l < NL; ++l) {
-        if (J)
-            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->clanes[l].J, n, J,
-                               ldj);
-        if (K)
-            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->clanes[l].A, n,
-                               P->d_kacc, n);
-        HIP_CHECK(hipGetLastError());
-    }
-    if (K) {
-        hipLaunchKernelGGL(k_sym_add, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, P->d_kacc, n, K, ldk);
-        HIP_CHECK(hipGetLastError());
-    }
-}
-
-// scratch for memory-tier classes used by the listed class ids
-void ensure_scratch(eri_plan *P, const std::vector<int> &cids)
-{
-    long long need = 0;
-    for (int cid : cids) {
-        const EriClassEntry *ce = find_class(cid, kernel_sph(P));
-        if (ce && ce->tier == 'M') need = std::max(need, ce->scratch_doubles);
-    }
-    if (need == 0 || need <= P->scratch_doubles) return;
-    const int wgs = ERI_MEM_WGS;
-    P->d_scratch = P->alloc<double>((size_t)need * wgs);  // the smaller earlier slice stays owned until destroy
-    P->scratch_wgs = wgs;
-    P->scratch_doubles = need;
-}
-
-void make_pair_data(eri_plan *P, hipStream_t s)
-{
-    const int np = (int)P->npairs;
-    int *w = P->alloc<int>(np + 1), *z = P->alloc<int>(np + 1);
-    hipLaunchKernelGGL(k_copy_w, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, w);
-    scan_i32(w, z, np, s);
-    int last_z = 0, last_w = 0;
-    if (np) {
-        HIP_CHECK(hipMemcpyAsync(&last_z, z + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(&last_w, w + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipStreamSynchronize(s));
-    }
-    const int64_t nppd = (int64_t)last_z + last_w;
-    hipLaunchKernelGGL(k_set_z, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, z);
-    P->d_ppd = P->alloc<double>((size_t)nppd * ERI_PP_STRIDE);
-    hipLaunchKernelGGL(k_pair_data, dim3(nblk(np, 128)), dim3(128), 0, s, np, P->d_pinfo, P->d_cen, P->d_off,
-                       P->d_exps, P->d_cn, P->d_ppd);
-    HIP_CHECK(hipGetLastError());
-}
-
-void build_explicit(eri_plan *P, const std::vector<int> &hl, const int32_t *quartets, int64_t nq, hipStream_t s)
-{
-    P->nq = nq;
-    P->npairs = 2 * nq;
-    int *d_q = P->alloc<int>((size_t)4 * nq);
-    upload(d_q, quartets, (size_t)4 * nq, s);
-    uint64_t *k0 = P->alloc<uint64_t>(nq), *k1 = P->alloc<uint64_t>(nq);
-    int64_t *p0 = P->alloc<int64_t>(nq), *p1 = P->alloc<int64_t>(nq);
-    hipLaunchKernelGGL(k_explicit_keys, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, d_q, P->d_l, P->d_nprim, k0, p0);
-    sort_pairs_u64(k0, k1, p0, p1, nq, s);
-    P->d_qmap = P->alloc<int>((size_t)5 * nq);
-    P->d_qbra = P->alloc<int>(nq);
-    P->d_qket = P->alloc<int>(nq);
-    P->d_pinfo = P->alloc<int4>(2 * nq);
-    hipLaunchKernelGGL(k_explicit_fill, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, p1, d_q, P->d_l, P->d_nprim,
-                       P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
-    P->d_qsrc = p1;
-    HIP_CHECK(hipGetLastError());
-    const int NC = 120;
-    int64_t *d_st = P->alloc<int64_t>(NC + 1), *d_k1 = P->alloc<int64_t>(NC + 1);
-    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, k1, d_st, d_k1, NC);
-    std::vector<int64_t> st(NC + 1), k1e(NC + 1);
-    HIP_CHECK(hipMemcpyAsync(st.data(), d_st, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipMemcpyAsync(k1e.data(), d_k1, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
-    st[NC] = nq;
-    make_pair_data(P, s);
-    int64_t out = 0;
-    std::vector<int> cids;
-    for (int c = 0; c < NC; ++c) {
-        const int64_t cnt = st[c + 1] - st[c];
-        if (cnt <= 0) continue;
-        const EriClassEntry *ce = find_class(c, P->sph);
-        if (!ce) {
-            g_last_error = "class " + std::to_string(c) + " not built";
-            throw HipFail{hipErrorInvalidValue};
-        }
-        EriBlock b{c, st[c], cnt, out, std::min(k1e[c], st[c + 1]) - st[c], nfun(ce->la, P->sph),
-                   nfun(ce->lb, P->sph), nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
-        out += cnt * (int64_t)b.na * b.nb * b.nc * b.nd;
-        P->blocks.push_back(b);
-        cids.push_back(c);
-    }
-    P->nout = out;
-    ensure_scratch(P, cids);
-    (void)hl;
-}
-
-void build_screened(eri_plan *P, const std::vector<int> &hl, const std::vector<int> &hk, double tau, hipStream_t s)
-{
-    const int ns = P->nshell;
-    const int64_t np = (int64_t)ns * (ns + 1) / 2;
-    if (np > (int64_t)INT32_MAX / 2) {
-        g_last_error = "too many shell pairs";
-        throw HipFail{hipErrorInvalidValue};
-    }
-    P->npairs = np;
-    P->d_pinfo = P->alloc<int4>(np);
-    uint64_t *pck = P->alloc<uint64_t>(np), *pck2 = P->alloc<uint64_t>(np);
-    int *pidx = P->alloc<int>(np), *pidx2 = P->alloc<int>(np);
-    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_nprim, P->d_pinfo, pck, pidx);
-    HIP_CHECK(hipGetLastError());
-    make_pair_data(P, s);
-
-    // --- Schwarz factors from the diagonal quartets (p|p), grouped by pair class
-    sort_pairs_u64(pck, pck2, pidx, pidx2, np, s);  // pidx2: pairs ordered by pair class
-    std::vector<uint64_t> hpc(np);
-    HIP_CHECK(hipMemcpyAsync(hpc.data(), pck2, sizeof(uint64_t) * np, hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
-    P->d_S = P->alloc<double>(np);
-    std::vector<int> diag_cids;
-    {
-        int64_t i = 0;
-        while (i < np) {
-            int64_t j = i;
-            while (j < np && hpc[j] == hpc[i]) ++j;
-            diag_cids.push_back(class_id_of((int)hpc[i], (int)hpc[i]));
-            i = j;
-        }
-    }
-    ensure_scratch(P, diag_cids);
-    {
-        int64_t i = 0;
-        size_t cap = 0;
-        double *buf = nullptr;
-        while (i < np) {
-            int64_t j = i;
-            while (j < np && hpc[j] == hpc[i]) ++j;
-            const int pc = (int)hpc[i];
-            int la = 0;
-            while ((la + 1) * (la + 2) / 2 <= pc) ++la;
-            const int lb = pc - la * (la + 1) / 2;
-            const int nab = nfun(la, P->sph) * nfun(lb, P->sph);
-            const size_t need = (size_t)(j - i) * nab * nab;
-            if (need > cap) {
-                if (buf) (void)hipFree(buf);
-                HIP_CHECK(hipMalloc(&buf, need * sizeof(double)));
-                cap = need;
-            }
-            launch_class(P, class_id_of(pc, pc), pidx2 + i, pidx2 + i, j - i, buf, s);
-            hipLaunchKernelGGL(k_schwarz_max, dim3(nblk(j - i, 256)), dim3(256), 0, s, (int)(j - i), pidx2 + i, buf,
-                               nab, P->d_S);
-            HIP_CHECK(hipGetLastError());
-            HIP_CHECK(hipStreamSynchronize(s));
-            i = j;
-        }
-        if (buf) (void)hipFree(buf);
-    }
-
-    // --- bucket the pairs by (pair class, K_pair), rank by S descending (ties: pair index)
-    int *seq = P->alloc<int>(np);
-    {
-        std::vector<int> h(np);
-        for (int64_t p = 0; p < np; ++p) h[p] = (int)p;
-        upload(seq, h.data(), np, s);
-    }
-    uint64_t *ka = P->alloc<uint64_t>(np), *kb = P->alloc<uint64_t>(np);
-    int *o1 = P->alloc<int>(np), *porder = P->alloc<int>(np);
-    hipLaunchKernelGGL(k_desc_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, seq, P->d_S, ka);
-    sort_pairs_u64(ka, kb, seq, o1, np, s);  // by S descending, stable: ties keep pair order
-    hipLaunchKernelGGL(k_bucket_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, o1, P->d_l, P->d_pinfo, ka);
-    sort_pairs_u64(ka, kb, o1, porder, np, s);  // stable by bucket
-    int *head = P->alloc<int>(np), *hscan = P->alloc<int>(np);
-    hipLaunchKernelGGL(k_heads, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, kb, head);
-    scan_i32(head, hscan, np, s);
-    int nb_last = 0, h_last = 0;
-    HIP_CHECK(hipMemcpyAsync(&nb_last, hscan + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipMemcpyAsync(&h_last, head + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
-    const int nbuck = nb_last + h_last;
-    int *d_bstart = P->alloc<int>(nbuck + 1);
-    uint64_t *d_bkey = P->alloc<uint64_t>(nbuck);
-    hipLaunchKernelGGL(k_bucket_table, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, kb, head, hscan, d_bstart, d_bkey);
-    std::vector<int> bstart(nbuck + 1);
-    std::vector<uint64_t> bkey(nbuck);
-    HIP_CHECK(hipMemcpyAsync(bstart.data(), d_bstart, sizeof(int) * nbuck, hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipMemcpyAsync(bkey.data(), d_bkey, sizeof(uint64_t) * nbuck, hipMemcpyDeviceToHost, s));
-    HIP_CHECK(hipStreamSynchronize(s));
-    bstart[nbuck] = (int)np;
-
-    // --- blocks (bra bucket >= ket bucket), ordered by (class, K_bra, K_ket)
-    struct HB {
-        int cid, kb, kk, B, Bk;
-    };
-    std::vector<HB> hb;
-    for (int B = 0; B < nbuck; ++B)
-        for (int Bk = 0; Bk <= B; ++Bk) {
-            const int pcb = (int)(bkey[B] >> 16), pck = (int)(bkey[Bk] >> 16);
-            hb.push_back({class_id_of(pcb, pck), (int)(bkey[B] & 0xffff), (int)(bkey[Bk] & 0xffff), B, Bk});
-        }
-    std::stable_sort(hb.begin(), hb.end(), [](const HB &x, const HB &y) {
-        if (x.cid != y.cid) return x.cid < y.cid;
-        if (x.kb != y.kb) return x.kb < y.kb;
-        return x.kk < y.kk;
-    });
-    std::vector<BlockDesc> bd(hb.size());
-    int64_t nent = 0;
-    for (size_t i = 0; i < hb.size(); ++i) {
-        const int B = hb[i].B, Bk = hb[i].Bk;
-        bd[i] = BlockDesc{bstart[B], bstart[B + 1] - bstart[B], bstart[Bk], bstart[Bk + 1] - bstart[Bk], B == Bk ? 1 : 0,
-                          nent};
-        nent += bd[i].bra_n;
-    }
-    BlockDesc *d_bd = P->alloc<BlockDesc>(bd.size());
-    upload(d_bd, bd.data(), bd.size(), s);
-    int64_t *cnt = P->alloc<int64_t>(nent + 1), *off = P->alloc<int64_t>(nent + 1);
-    const double tau2 = tau * tau;
-    hipLaunchKernelGGL(k_count, dim3(nblk(nent, 256)), dim3(256), 0, s, nent, d_bd, (int)bd.size(), porder, P->d_S,
-                       tau2, cnt);
-    HIP_CHECK(hipGetLastError());
-    scan_i64(cnt, off, nent, s);
-    int64_t lo = 0, lc = 0;
-    if (nent) {
-        HIP_CHECK(hipMemcpyAsync(&lo, off + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(&lc, cnt + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipStreamSynchronize(s));
-    }
-    const int64_t nq = lo + lc;
-    P->nq = nq;
-    int *phi = P->alloc<int>(np);
-    hipLaunchKernelGGL(k_pair_hi, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, P->d_pinfo, phi);
-    P->implicit = (P->flags & ERI_IMPLICIT) != 0 || nq > ERI_EXPLICIT_MAX;
-    if (P->implicit) {
-        // keep the counts; quartet lists are expanded chunk by chunk when used
-        P->d_bd = d_bd;
-        P->nbd = (int)bd.size();
-        P->nent = nent;
-        P->d_ent_off = off;
-        P->d_porder = porder;
-        P->d_pair_i = phi;
-        P->d_cqbra = P->alloc<int>(P->chunk_q);
-        P->d_cqket = P->alloc<int>(P->chunk_q);
-    } else {
-        P->d_qbra = P->alloc<int>(nq);
-        P->d_qket = P->alloc<int>(nq);
-        P->d_qmap = P->alloc<int>((size_t)5 * nq);
-        hipLaunchKernelGGL(k_fill_screened, dim3(nblk(nent, 128)), dim3(128), 0, s, nent, d_bd, (int)bd.size(), porder,
-                           cnt, off, P->d_pinfo, phi, P->d_qbra, P->d_qket, P->d_qmap);
-    }
-    HIP_CHECK(hipGetLastError());
-    // block starts -> class ranges
-    std::vector<int64_t> hbase(bd.size());
-    for (size_t i = 0; i < bd.size(); ++i) hbase[i] = bd[i].entry_base;
-    int64_t *d_idx = P->alloc<int64_t>(bd.size() + 1), *d_bs = P->alloc<int64_t>(bd.size() + 1);
-    std::vector<int64_t> bst(bd.size());
-    if (!bd.empty()) {
-        // entry_base may equal nent for an empty trailing block: clamp, fix on host
-        std::vector<int64_t> idx(bd.size());
-        for (size_t i = 0; i < bd.size(); ++i) idx[i] = std::min<int64_t>(hbase[i], nent - 1);
-        upload(d_idx, idx.data(), idx.size(), s);
-        hipLaunchKernelGGL(k_gather_i64, dim3(nblk(bd.size(), 256)), dim3(256), 0, s, (int)bd.size(), off, d_idx, d_bs);
-        HIP_CHECK(hipMemcpyAsync(bst.data(), d_bs, sizeof(int64_t) * bd.size(), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipStreamSynchronize(s));
-        for (size_t i = 0; i < bd.size(); ++i)
-            if (bd[i].bra_n == 0 || hbase[i] >= nent) bst[i] = nq;
-    }
-    int64_t outp = 0;
-    std::vector<int> cids;
-    size_t i = 0;
-    while (i < hb.size()) {
-        size_t j = i;
-        while (j < hb.size() && hb[j].cid == hb[i].cid) ++j;
-        const int64_t st = bst[i];
-        const int64_t en = (j < hb.size()) ? bst[j] : nq;
-        if (en > st) {
-            const EriClassEntry *ce = find_class(hb[i].cid, P->sph);
-            if (!ce) {
-                g_last_error = "class " + std::to_string(hb[i].cid) + " not built";
-                throw HipFail{hipErrorInvalidValue};
-            }
-            // the (K_bra = 1, K_ket = 1) bucket pair, when present, is the first of the class
-            int64_t nk1 = 0;
-            if (hb[i].kb == 1 && hb[i].kk == 1) nk1 = ((i + 1 < hb.size()) ? bst[i + 1] : nq) - bst[i];
-            EriBlock b{hb[i].cid, st, en - st, outp, nk1, nfun(ce->la, P->sph), nfun(ce->lb, P->sph),
-                       nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
-            outp += b.count * (int64_t)b.na * b.nb * b.nc * b.nd;
-            P->blocks.push_back(b);
-            cids.push_back(b.cid);
-        }
-        i = j;
-    }
-    P->nout = outp;
-    ensure_scratch(P, cids);
-    (void)hl;
-    (void)hk;
-}
-
-int translate(const HipFail &) { return ERI_E_HIP; }
-
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// C ABI
-// ---------------------------------------------------------------------------
-
-extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, double tau,
-                                  void *stream, eri_plan **plan)
-{
-    if (!plan) return ERI_E_INVALID;
-    *plan = nullptr;
-    if (!sh || sh->nshell < 1 || !sh->centers || !sh->l || !sh->nprim || !sh->prim_off || !sh->exps || !sh->coefs)
-        return ERI_E_INVALID;
-    if (flags & ~(ERI_SPHERICAL | ERI_NO_NORMALIZE | ERI_IMPLICIT)) return ERI_E_INVALID;
-    if ((flags & ERI_IMPLICIT) && quartets) return ERI_E_INVALID;
-    if (!(tau >= 0.0) || std::isinf(tau)) return ERI_E_INVALID;
-    if (quartets && (nq < 0 || tau != 0.0)) return ERI_E_INVALID;
-    const int ns = sh->nshell;
-    if (sh->prim_off[0] != 0) return ERI_E_INVALID;
-    for (int s = 0; s < ns; ++s) {
-        if (sh->l[s] < 0 || sh->l[s] > ERI_MAX_L) return ERI_E_INVALID;
-        if (sh->nprim[s] < 1 || sh->nprim[s] > ERI_MAX_PRIM) return ERI_E_INVALID;
-        if (sh->prim_off[s + 1] - sh->prim_off[s] != sh->nprim[s]) return ERI_E_INVALID;
-        for (int c = 0; c < 3; ++c)
-            if (!std::isfinite(sh->centers[3 * s + c])) return ERI_E_INVALID;
-        for (int k = sh->prim_off[s]; k < sh->prim_off[s + 1]; ++k)
-            if (!(sh->exps[k] > 0.0) || !std::isfinite(sh->exps[k]) || !std::isfinite(sh->coefs[k])) return ERI_E_INVALID;
-    }
-    if (quartets)
-        for (int64_t x = 0; x < 4 * nq; ++x)
-            if (quartets[x] < 0 || quartets[x] >= ns) return ERI_E_INVALID;
-    hipStream_t s = (hipStream_t)stream;
-    eri_plan *P = new (std::nothrow) eri_plan();
-    if (!P) return ERI_E_NOMEM;
-    try {
-        HIP_CHECK(hipGetDevice(&P->device));
-        {
-            int ncu = 0;
-            HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, P->device));
-            P->grid_cap = std::max(1, ncu) * 8;
-        }
-        P->flags = flags;
-        if (const char *cq = std::getenv("ERI_CHUNK_QUARTETS")) {
-            const long long v = std::atoll(cq);
-            if (v >= 1 && v <= (1LL << 26)) P->chunk_q = v;
-        }
-        P->sph = (flags & ERI_SPHERICAL) != 0;
-        P->screened = quartets == nullptr;
-        P->nshell = ns;
-        P->d_boys = boys_table(P->device);
-        const int np = sh->prim_off[ns];
-        std::vector<int> hl(sh->l, sh->l + ns), hk(sh->nprim, sh->nprim + ns), hoff(sh->prim_off, sh->prim_off + ns + 1);
-        std::vector<int> hbf(ns + 1), hnf(ns);
-        hbf[0] = 0;
-        for (int i = 0; i < ns; ++i) {
-            hnf[i] = nfun(hl[i], P->sph);
-            hbf[i + 1] = hbf[i] + hnf[i];
-        }
-        P->nbf = hbf[ns];
-        P->d_cen = P->alloc<double>((size_t)3 * ns);
-        P->d_l = P->alloc<int>(ns);
-        P->d_nprim = P->alloc<int>(ns);
-        P->d_off = P->alloc<int>(ns + 1);
-        P->d_bf = P->alloc<int>(ns + 1);
-        P->d_nfun = P->alloc<int>(ns);
-        P->d_exps = P->alloc<double>(np);
-        double *d_raw = P->alloc<double>(np);
-        P->d_cn = P->alloc<double>(np);
-        upload(P->d_cen, sh->centers, (size_t)3 * ns, s);
-        upload(P->d_l, hl.data(), ns, s);
-        upload(P->d_nprim, hk.data(), ns, s);
-        upload(P->d_off, hoff.data(), ns + 1, s);
-        upload(P->d_bf, hbf.data(), ns + 1, s);
-        upload(P->d_nfun, hnf.data(), ns, s);
-        upload(P->d_exps, sh->exps, np, s);
-        upload(d_raw, sh->coefs, np, s);
-        hipLaunchKernelGGL(k_normalize, dim3(nblk(ns, 128)), dim3(128), 0, s, ns, P->d_l, P->d_nprim, P->d_off,
-                           P->d_exps, d_raw, P->d_cn, (flags & ERI_NO_NORMALIZE) ? 1 : 0);
-        HIP_CHECK(hipGetLastError());
-        if (quartets) build_explicit(P, hl, quartets, nq, s);
-        else build_screened(P, hl, hk, tau, s);
-        HIP_CHECK(hipStreamSynchronize(s));
-    } catch (const HipFail &f) {
-        delete P;
-        return translate(f);
-    } catch (const std::bad_alloc &) {
-        delete P;
-        return ERI_E_NOMEM;
-    }
-    *plan = P;
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_destroy(eri_plan *plan)
-{
-    delete plan;
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_info(const eri_plan *P, int64_t *nq, int64_t *nout, int32_t *nb, int32_t *nbf, int64_t *np)
-{
-    if (!P) return ERI_E_INVALID;
-    if (nq) *nq = P->nq;
-    if (nout) *nout = P->nout;
-    if (nb) *nb = (int32_t)P->blocks.size();
-    if (nbf) *nbf = P->nbf;
-    if (np) *np = P->npairs;
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_blocks(const eri_plan *P, int32_t *cid, int64_t *start, int64_t *count, int64_t *out_off)
-{
-    if (!P) return ERI_E_INVALID;
-    for (size_t b = 0; b < P->blocks.size(); ++b) {
-        if (cid) cid[b] = P->blocks[b].cid;
-        if (start) start[b] = P->blocks[b].start;
-        if (count) count[b] = P->blocks[b].count;
-        if (out_off) out_off[b] = P->blocks[b].out_off;
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_index_map(const eri_plan *P, int32_t *dst, void *stream)
-{
-    if (!P || (!dst && P->nq)) return ERI_E_INVALID;
-    if (!P->nq) return ERI_OK;
-    if (P->implicit) return eri_plan_quartets(P, 0, P->nq, dst, stream);
-    hipError_t e = hipMemcpyAsync(dst, P->d_qmap, sizeof(int) * 5 * P->nq, hipMemcpyDeviceToDevice, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
-        return ERI_E_HIP;
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_schwarz(const eri_plan *P, double *dst, void *stream)
-{
-    if (!P || !dst) return ERI_E_INVALID;
-    if (!P->screened) return ERI_E_UNSUPPORTED;
-    hipError_t e = hipMemcpyAsync(dst, P->d_S, sizeof(double) * P->npairs, hipMemcpyDeviceToDevice, (hipStream_t)stream);
-    if (e != hipSuccess) {
-        g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
-        return ERI_E_HIP;
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, double *out, int64_t cap, void *stream)
-{
-    if (!P) return ERI_E_INVALID;
-    const int nb = (int)P->blocks.size();
-    if (b0 < 0 || b1 > nb || b0 > b1) return ERI_E_INVALID;
-    if (b0 == b1) return ERI_OK;
-    const int64_t base = P->blocks[b0].out_off;
-    const int64_t end = (b1 < nb) ? P->blocks[b1].out_off : P->nout;
-    if (!out || cap < end - base) return out ? ERI_E_CAPACITY : ERI_E_INVALID;
-    try {
-        const hipStream_t s = (hipStream_t)stream;
-        const bool side = b1 - b0 > 1 && use_side_streams(P);
-        eri_plan *Pm = const_cast<eri_plan *>(P);
-        if (side) side_fork(Pm, s);
-        for (int b = b0; b < b1; ++b) {
-            const EriBlock &B = P->blocks[b];
-            compute_range(P, B, 0, B.count, out + (B.out_off - base), side ? block_stream(P, B, b - b0, s) : s);
-        }
-        if (side) side_join(Pm, s);
-    } catch (const HipFail &f) {
-        return translate(f);
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_compute_range(const eri_plan *P, int32_t block, int64_t first, int64_t count, double *out,
-                                 int64_t cap, void *stream)
-{
-    if (!P || block < 0 || block >= (int)P->blocks.size() || first < 0 || count < 0) return ERI_E_INVALID;
-    const EriBlock &B = P->blocks[block];
-    if (first > B.count || count > B.count - first) return ERI_E_INVALID;
-    if (count == 0) return ERI_OK;
-    const int64_t need = count * (int64_t)B.na * B.nb * B.nc * B.nd;
-    if (!out) return ERI_E_INVALID;
-    if (cap < need) return ERI_E_CAPACITY;
-    try {
-        compute_range(P, B, first, count, out, (hipStream_t)stream);
-    } catch (const HipFail &f) {
-        return translate(f);
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_plan_quartets(const eri_plan *P, int64_t first, int64_t count, int32_t *dst, void *stream)
-{
-    if (!P || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
-    if (count == 0) return ERI_OK;
-    if (!dst || count > (int64_t)INT32_MAX) return ERI_E_INVALID;
-    hipStream_t s = (hipStream_t)stream;
-    try {
-        if (P->implicit) {
-            hipLaunchKernelGGL(k_expand, dim3(nblk(count, 256)), dim3(256), 0, s, first, count, P->nent, P->d_ent_off,
-                               P->d_bd, P->nbd, P->d_porder, P->d_pinfo, P->d_pair_i, (int *)nullptr, (int *)nullptr,
-                               dst);
-            HIP_CHECK(hipGetLastError());
-        } else {
-            HIP_CHECK(hipMemcpyAsync(dst, P->d_qmap + 5 * first, sizeof(int) * 5 * count, hipMemcpyDeviceToDevice, s));
-        }
-    } catch (const HipFail &f) {
-        return translate(f);
-    }
-    return ERI_OK;
-}
-
 // ---------------------------------------------------------------------------
 // First derivatives with respect to the centres
 // ---------------------------------------------------------------------------
@@ -1748,8 +646,6 @@ extern "C" int eri_plan_quartets(const eri_plan *P, int64_t first, int64_t count
 // pick the two terms of every derivative element out of the auxiliary blocks
 // (whose quartets the plan may have reordered: the permutation bits say how)
 // and, for spherical plans, apply t^(l) to the four indices of each block.
-namespace {
-
 __device__ inline int dv_ncart(int l) { return (l + 1) * (l + 2) / 2; }
 __device__ inline int dv_nsph(int l) { return 2 * l + 1; }
 // index of the Cartesian component (x, y, l-x-y) of a shell l: x descending, then y descending
@@ -1879,265 +775,15 @@ __global__ void k_deriv_sph(int64_t n, const int *rows, const int *lsh, double *
     }
 }
 
-}  // namespace
-
-extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count, double *out, int64_t cap,
-                                 void *stream)
-{
-    if (!P || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
-    if (count == 0) return ERI_OK;
-    if (!out || count > ((int64_t)1 << 24)) return ERI_E_INVALID;
-    hipStream_t s = (hipStream_t)stream;
-    eri_plan *A = nullptr;
-    std::vector<void *> tmp;
-    auto dalloc = [&](size_t bytes) -> void * {
-        void *p = nullptr;
-        HIP_CHECK(hipMalloc(&p, bytes ? bytes : 8));
-        tmp.push_back(p);
-        return p;
-    };
-    int rc = ERI_OK;
-    try {
-        const int ns = P->nshell;
-        std::vector<int> hl(ns), hk(ns), hoff(ns + 1);
-        HIP_CHECK(hipMemcpyAsync(hl.data(), P->d_l, sizeof(int) * ns, hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(hk.data(), P->d_nprim, sizeof(int) * ns, hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(hoff.data(), P->d_off, sizeof(int) * (ns + 1), hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipStreamSynchronize(s));
-        const int npr = hoff[ns];
-        std::vector<double> hcen(3 * (size_t)ns), hexp(npr), hcn(npr);
-        HIP_CHECK(hipMemcpyAsync(hcen.data(), P->d_cen, sizeof(double) * 3 * ns, hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(hexp.data(), P->d_exps, sizeof(double) * npr, hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipMemcpyAsync(hcn.data(), P->d_cn, sizeof(double) * npr, hipMemcpyDeviceToHost, s));
-        int *d_rows = (int *)dalloc(sizeof(int) * 5 * (size_t)count);
-        if ((rc = eri_plan_quartets(P, first, count, d_rows, stream)) != ERI_OK) throw rc;
-        std::vector<int> rows(5 * (size_t)count);
-        HIP_CHECK(hipMemcpyAsync(rows.data(), d_rows, sizeof(int) * 5 * count, hipMemcpyDeviceToHost, s));
-        HIP_CHECK(hipStreamSynchronize(s));
-        for (int64_t t = 0; t < count; ++t)
-            for (int k = 0; k < 4; ++k)
-                if (hl[rows[5 * t + k]] + 1 > ERI_MAX_L) throw (int)ERI_E_UNSUPPORTED;
-        // where every slot's 12 blocks go, and the capacity that needs
-        const bool sph = P->sph;
-        std::vector<int64_t> dst_off(count), cart_off(count);
-        int64_t dtot = 0, ctot = 0;
-        for (int64_t t = 0; t < count; ++t) {
-            const int *r = &rows[5 * t];
-            int64_t nf = 1, nc = 1;
-            for (int k = 0; k < 4; ++k) {
-                nf *= nfun(hl[r[k]], sph);
-                nc *= ncart(hl[r[k]]);
-            }
-            dst_off[t] = dtot;
-            cart_off[t] = ctot;
-            dtot += 12 * nf;
-            ctot += 12 * nc;
-        }
-        if (cap < dtot) throw (int)ERI_E_CAPACITY;
-        // auxiliary shells: [0, ns) the shells, [ns, 2ns) raised, [2ns, 3ns) lowered
-        std::vector<int32_t> al(3 * ns), ak(3 * ns), aoff(3 * ns + 1);
-        std::vector<double> acen(9 * (size_t)ns), aexp(3 * (size_t)npr), acf(3 * (size_t)npr);
-        aoff[0] = 0;
-        for (int part = 0; part < 3; ++part)
-            for (int x = 0; x < ns; ++x) {
-                const int y = part * ns + x;
-                al[y] = part == 0 ? hl[x] : part == 1 ? hl[x] + 1 : std::max(hl[x] - 1, 0);
-                ak[y] = hk[x];
-                aoff[y + 1] = aoff[y] + hk[x];
-                for (int c = 0; c < 3; ++c) acen[3 * y + c] = hcen[3 * x + c];
-                for (int q = 0; q < hk[x]; ++q) {
-                    const double a = hexp[hoff[x] + q], c = hcn[hoff[x] + q];
-                    aexp[aoff[y] + q] = a;
-                    acf[aoff[y] + q] = part == 0 ? c : part == 1 ? 2.0 * a * c : (hl[x] > 0 ? c : 0.0);
-                }
-            }
-        eri_shells ash{3 * ns, acen.data(), al.data(), ak.data(), aoff.data(), aexp.data(), acf.data()};
-        std::vector<int32_t> aq(32 * (size_t)count);
-        for (int64_t t = 0; t < count; ++t)
-            for (int p = 0; p < 4; ++p)
-                for (int sg = 0; sg < 2; ++sg) {
-                    int32_t *q = &aq[4 * ((t * 4 + p) * 2 + sg)];
-                    for (int k = 0; k < 4; ++k) q[k] = rows[5 * t + k];
-                    q[p] += (sg == 0 ? 1 : 2) * ns;
-                }
-        if ((rc = eri_build_quartets(&ash, ERI_NO_NORMALIZE, aq.data(), 8 * count, 0.0, stream, &A)) != ERI_OK) throw rc;
-        double *d_aux = (double *)dalloc(sizeof(double) * (size_t)A->nout);
-        if ((rc = eri_compute_batch(A, 0, (int32_t)A->blocks.size(), d_aux, A->nout, stream)) != ERI_OK) throw rc;
-        const int64_t na = 8 * count;
-        int64_t *d_slot_of = (int64_t *)dalloc(sizeof(int64_t) * na);
-        hipLaunchKernelGGL(k_invert_src, dim3(nblk(na, 256)), dim3(256), 0, s, na, A->d_qsrc, d_slot_of);
-        HIP_CHECK(hipGetLastError());
-        const int nb = (int)A->blocks.size();
-        std::vector<int64_t> bst(nb), bout(nb), bsz(nb);
-        for (int b = 0; b < nb; ++b) {
-            const EriBlock &B = A->blocks[b];
-            bst[b] = B.start;
-            bout[b] = B.out_off;
-            bsz[b] = (int64_t)B.na * B.nb * B.nc * B.nd;
-        }
-        int64_t *d_bt = (int64_t *)dalloc(sizeof(int64_t) * 3 * nb);
-        upload(d_bt, bst.data(), nb, s);
-        upload(d_bt + nb, bout.data(), nb, s);
-        upload(d_bt + 2 * nb, bsz.data(), nb, s);
-        int64_t *d_aux_off = (int64_t *)dalloc(sizeof(int64_t) * na);
-        hipLaunchKernelGGL(k_slot_offsets, dim3(nblk(na, 256)), dim3(256), 0, s, na, nb, d_bt, d_bt + nb, d_bt + 2 * nb,
-                           d_aux_off);
-        HIP_CHECK(hipGetLastError());
-        int64_t *d_off = (int64_t *)dalloc(sizeof(int64_t) * 2 * count);
-        upload(d_off, dst_off.data(), count, s);
-        upload(d_off + count, cart_off.data(), count, s);
-        if (!sph) {
-            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, d_rows, P->d_l, d_slot_of,
-                               A->d_qmap, A->d_l, d_aux_off, d_aux, d_off, out);
-        } else {
-            double *d_cart = (double *)dalloc(sizeof(double) * ctot);
-            double *d_tmp = (double *)dalloc(sizeof(double) * ctot);
-            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, d_rows, P->d_l, d_slot_of,
-                               A->d_qmap, A->d_l, d_aux_off, d_aux, d_off + count, d_cart);
-            HIP_CHECK(hipGetLastError());
-            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)(12 * count)), dim3(256), 0, s, count, d_rows, P->d_l, d_cart,
-                               d_tmp, d_off + count, d_off, out);
-        }
-        HIP_CHECK(hipGetLastError());
-        HIP_CHECK(hipStreamSynchronize(s));
-    } catch (const HipFail &f) {
-        rc = translate(f);
-    } catch (int code) {
-        rc = code;
-    } catch (const std::bad_alloc &) {
-        rc = ERI_E_NOMEM;
-    }
-    (void)hipStreamSynchronize(s);
-    for (void *p : tmp) (void)hipFree(p);
-    if (A) eri_plan_destroy(A);
-    return rc;
-}
-
-extern "C" int eri_digest_J(const eri_plan *Pc, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream)
-{
-    eri_plan *P = const_cast<eri_plan *>(Pc);
-    if (!P || !D || !J || ldd < P->nbf || ldj < P->nbf) return ERI_E_INVALID;
-    if (!P->screened) return ERI_E_UNSUPPORTED;
-    hipStream_t s = (hipStream_t)stream;
-    if (P->implicit) {
-        try {
-            digest_JK_chunked(P, D, ldd, J, ldj, nullptr, 0, s);
-        } catch (const HipFail &f) {
-            return translate(f);
-        }
-        return ERI_OK;
-    }
-    try {
-        const int nb = (int)P->blocks.size();
-        if (!P->jready) {
-            // integral buffer, contribution buffer, and the (pair, entry) order -- built once
-            P->d_ints = P->alloc<double>((size_t)std::max<int64_t>(P->nout, 1));
-            std::vector<int64_t> cbb(nb + 1), bst(nb);
-            std::vector<int> bnab(nb), bncd(nb);
-            int64_t cbt = 0;
-            for (int b = 0; b < nb; ++b) {
-                const EriBlock &B = P->blocks[b];
-                cbb[b] = cbt;
-                bst[b] = B.start;
-                bnab[b] = B.na * B.nb;
-                bncd[b] = B.nc * B.nd;
-                cbt += B.count * (int64_t)(bnab[b] + bncd[b]);
-            }
-            P->d_cb = P->alloc<double>((size_t)std::max<int64_t>(cbt, 1));
-            int64_t *d_cbb = P->alloc<int64_t>(nb + 1), *d_bst = P->alloc<int64_t>(nb + 1);
-            int *d_bnab = P->alloc<int>(nb + 1), *d_bncd = P->alloc<int>(nb + 1), *d_blk_of = P->alloc<int>(P->nq + 1);
-            upload(d_cbb, cbb.data(), nb, s);
-            upload(d_bst, bst.data(), nb, s);
-            upload(d_bnab, bnab.data(), nb, s);
-            upload(d_bncd, bncd.data(), nb, s);
-            for (int b = 0; b < nb; ++b)
-                hipLaunchKernelGGL(k_fill_blk_of, dim3(nblk(P->blocks[b].count, 256)), dim3(256), 0, s,
-                                   P->blocks[b].start, P->blocks[b].count, b, d_blk_of);
-            const int64_t ne = 2 * P->nq;
-            int *ek = P->alloc<int>(ne + 1), *ek2 = P->alloc<int>(ne + 1);
-            int64_t *eo = P->alloc<int64_t>(ne + 1);
-            P->d_eoff = P->alloc<int64_t>(ne + 1);
-            hipLaunchKernelGGL(k_entries, dim3(nblk(P->nq, 256)), dim3(256), 0, s, P->nq, P->d_qbra, P->d_qket, d_cbb,
-                               d_blk_of, d_bst, d_bnab, d_bncd, ek, eo, nullptr);
-            HIP_CHECK(hipGetLastError());
-            sort_pairs_i32(ek, ek2, eo, P->d_eoff, ne, s);
-            P->d_seg = P->alloc<int64_t>(P->npairs + 1);
-            hipLaunchKernelGGL(k_seg_starts, dim3(nblk(P->npairs + 1, 256)), dim3(256), 0, s, (int)P->npairs, ne, ek2,
-                               P->d_seg);
-            HIP_CHECK(hipGetLastError());
-            HIP_CHECK(hipStreamSynchronize(s));
-            P->jready = true;
-        }
-        // 1. integrals of every block and 2. their per-quartet contributions,
-        // block after block on the caller's and the side streams
-        side_fork(P, s);
-        int64_t cbt = 0;
-        for (int b = 0; b < nb; ++b) {
-            const EriBlock &B = P->blocks[b];
-            const hipStream_t bs = use_side_streams(P) ? block_stream(P, B, b, s) : s;
-            launch_class(P, B.cid, P->d_qbra + B.start, P->d_qket + B.start, B.count, P->d_ints + B.out_off, bs, B.n_k1);
-            const int64_t CH = 1 << 30;
-            for (int64_t c = 0; c < B.count; c += CH) {
-                const int64_t m = std::min(CH, B.count - c);
-                const int64_t nab = B.na * B.nb, ncd = B.nc * B.nd, nv = m * (nab + ncd);
-                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, bs, nv, B.na, B.nb, B.nc,
-                                   B.nd, P->d_qbra + B.start + c, P->d_qket + B.start + c, P->d_pinfo, P->d_bf,
-                                   P->d_ints + B.out_off + c * nab * ncd, D, ldd, P->d_cb + cbt + c * (nab + ncd));
-                HIP_CHECK(hipGetLastError());
-            }
-            cbt += B.count * (int64_t)(B.na * B.nb + B.nc * B.nd);
-        }
-        side_join(P, s);
-        // 3. deterministic per-pair reduction into J
-        hipLaunchKernelGGL(k_reduce_pairs, dim3((unsigned)P->npairs), dim3(RUN_THREADS), 0, s, (int)P->npairs, P->d_pinfo,
-                           P->d_bf, P->d_nfun, P->d_seg, P->d_eoff, P->d_cb, J, ldj);
-        HIP_CHECK(hipGetLastError());
-    } catch (const HipFail &f) {
-        return translate(f);
-    }
-    return ERI_OK;
-}
-
-extern "C" int eri_digest_JK(const eri_plan *Pc, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
-                             int32_t ldk, void *stream)
-{
-    eri_plan *P = const_cast<eri_plan *>(Pc);
-    if (!P || !D || (!J && !K) || ldd < P->nbf || (J && ldj < P->nbf) || (K && ldk < P->nbf)) return ERI_E_INVALID;
-    if (!P->screened) return ERI_E_UNSUPPORTED;
-    if (P->nshell > 46340) return ERI_E_UNSUPPORTED;  // target block keys are nshell^2 in 32 bits
-    try {
-        digest_JK_chunked(P, D, ldd, J, ldj, K, ldk, (hipStream_t)stream);
-    } catch (const HipFail &f) {
-        return translate(f);
-    }
-    return ERI_OK;
-}
-
-extern "C" const char *eri_strerror(int code)
-{
-    switch (code) {
-    case ERI_OK: return "ok";
-    case ERI_E_INVALID: return "invalid argument";
-    case ERI_E_UNSUPPORTED: return "unsupported request";
-    case ERI_E_CAPACITY: return "output buffer too small";
-    case ERI_E_HIP: {
-        static thread_local std::string msg;
-        msg = "HIP error: " + g_last_error;
-        return msg.c_str();
-    }
-    case ERI_E_NOMEM: return "device allocation failed";
-    default: return "unknown error code";
-    }
-}
-
-namespace {
 
 // FP64 FMA issue rate: every lane runs eight independent chains of fused
-// multiply-adds, eight waves per SIMD; the sum is stored so that nothing is
-// dropped.
+// multiply-adds, eight waves per SIMD.
 constexpr int FMA_CHAINS = 8, FMA_ITERS = 4096;
 
-__global__ void __launch_bounds__(256) k_fma_rate(double *out, double a, double b)
+// The chains' sum is compared with `never` (a value it cannot take, passed at
+// run time so that the compiler cannot drop the chains); only then is it
+// stored, always to out[0], so the one-element sink is never written past.
+__global__ void __launch_bounds__(256) k_fma_rate(double *out, double a, double b, double never)
 {
     double v[FMA_CHAINS];
 #pragma unroll
@@ -2149,16 +795,1469 @@ __global__ void __launch_bounds__(256) k_fma_rate(double *out, double a, double 
     double t = 0.0;
 #pragma unroll
     for (int c = 0; c < FMA_CHAINS; ++c) t += v[c];
-    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = t;
+    if (t == never) out[0] = t;
+}
+
+
+inline unsigned nblk(int64_t n, int bs) { return (unsigned)((n + bs - 1) / bs); }
+
+// ---------------------------------------------------------------------------
+// caller workspace
+// ---------------------------------------------------------------------------
+// Every device buffer of a plan, and of a digestion or derivative call, is a
+// slice of a workspace the caller allocated.  The same layout code runs twice:
+// once without a base pointer, only adding up the bytes (the size query), and
+// once carving the caller's workspace.
+struct WsShort {
+};
+
+struct Arena {
+    char *base = nullptr;
+    size_t cap = 0, used = 0;
+    Arena() = default;
+    Arena(void *b, size_t c) : base((char *)b), cap(c) {}
+    template <class T>
+    T *take(size_t n)
+    {
+        const size_t at = (used + 255) / 256 * 256;
+        used = at + (n ? n : 1) * sizeof(T);
+        if (!base) return nullptr;
+        if (used > cap) throw WsShort{};
+        return reinterpret_cast<T *>(base + at);
+    }
+};
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan
+// ---------------------------------------------------------------------------
+
+struct EriBlock {
+    int cid;
+    int64_t start, count, out_off;
+    int64_t n_k1;  // leading quartets with K_a K_b K_c K_d = 1
+    int na, nb, nc, nd;  // functions per shell of the class (spherical or Cartesian)
+};
+
+// stream lanes: the caller's stream plus up to ERI_MAX_SIDE_STREAMS side streams
+constexpr int ERI_LANES = ERI_MAX_SIDE_STREAMS + 1;
+
+struct eri_plan {
+    int flags = 0;
+    bool sph = false;
+    bool screened = false;
+    int device = 0;
+    int nshell = 0, nbf = 0;
+    int64_t npairs = 0, nq = 0, nout = 0;
+    double *d_cen = nullptr, *d_exps = nullptr, *d_cn = nullptr, *d_ppd = nullptr, *d_S = nullptr;
+    int *d_l = nullptr, *d_nprim = nullptr, *d_off = nullptr, *d_bf = nullptr, *d_nfun = nullptr;
+    int4 *d_pinfo = nullptr;
+    // explicit quartet lists (plans built from a quartet list)
+    int *d_qbra = nullptr, *d_qket = nullptr, *d_qmap = nullptr;
+    int64_t *d_qsrc = nullptr;  // input position of the quartet in each slot
+    double *d_boys = nullptr;
+    double *d_scratch = nullptr;
+    int scratch_wgs = 0;
+    long long scratch_doubles = 0;  // per workgroup slice
+    double *d_unfused = nullptr;    // work buffer of the unfused-spherical ablation build
+    int grid_cap = 2048;            // persistent register-tier grid (8 workgroups per CU)
+    std::vector<EriBlock> blocks;
+    // screened plans: per (block, bra rank) the length of the surviving ket
+    // prefix and its running offset; slot lists are expanded per chunk
+    BlockDesc *d_bd = nullptr;
+    int nbd = 0;
+    int64_t nent = 0;
+    int64_t *d_ent_off = nullptr;
+    int *d_porder = nullptr, *d_pair_i = nullptr;
+    int64_t chunk_q = 1 << 22;  // quartets per chunk
+    int *d_chunk = nullptr;     // ERI_LANES x (bra list, ket list) x chunk_q
+    size_t ws_used = 0;
+    // host copies of the shells (derivative calls build their auxiliary shells from them)
+    std::vector<int> hl, hk, hoff;
+    std::vector<double> hcen, hexp, hcn;
+    // side streams registered by the caller (eri_plan_set_streams)
+    int nside = 0;
+    hipStream_t side[ERI_MAX_SIDE_STREAMS] = {};
+    hipEvent_t ev_fork = nullptr, ev_side[ERI_MAX_SIDE_STREAMS] = {};
+
+    ~eri_plan()
+    {
+        if (ev_fork) {
+            (void)hipEventDestroy(ev_fork);
+            for (int i = 0; i < ERI_MAX_SIDE_STREAMS; ++i) (void)hipEventDestroy(ev_side[i]);
+        }
+    }
+};
+
+namespace {
+
+template <class T>
+void upload(T *dst, const T *src, size_t n, hipStream_t s)
+{
+    if (n) HIP_CHECK(hipMemcpyAsync(dst, src, n * sizeof(T), hipMemcpyHostToDevice, s));
+}
+
+// hipCUB primitives on caller temp storage; with tmp == nullptr they only
+// report the temp bytes they need (no device work)
+size_t scan_i64(const int64_t *in, int64_t *out, int64_t n, void *tmp, size_t bytes, hipStream_t s)
+{
+    if (n <= 0) return 0;
+    if (!tmp) bytes = 0;
+    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(tmp, bytes, in, out, (int)n, s));
+    return bytes;
+}
+
+size_t scan_i32(const int *in, int *out, int64_t n, void *tmp, size_t bytes, hipStream_t s)
+{
+    if (n <= 0) return 0;
+    if (!tmp) bytes = 0;
+    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(tmp, bytes, in, out, (int)n, s));
+    return bytes;
+}
+
+template <class V>
+size_t sort_pairs_u64(uint64_t *keys_in, uint64_t *keys_out, V *v_in, V *v_out, int64_t n, void *tmp, size_t bytes,
+                      hipStream_t s)
+{
+    if (n <= 0) return 0;
+    if (!tmp) bytes = 0;
+    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(tmp, bytes, keys_in, keys_out, v_in, v_out, (int)n, 0, 64, s));
+    return bytes;
+}
+
+// output kind of the class kernels a plan launches (the unfused-spherical
+// ablation build runs the Cartesian kernels for spherical plans)
+inline bool kernel_sph(const eri_plan *P)
+{
+#ifdef ERI_UNFUSED_SPHERICAL
+    return false;
+#else
+    return P->sph;
+#endif
+}
+
+inline bool kernel_sph_flags(bool sph)
+{
+#ifdef ERI_UNFUSED_SPHERICAL
+    (void)sph;
+    return false;
+#else
+    return sph;
+#endif
+}
+
+// memory-tier scratch doubles per workgroup the given classes need
+long long scratch_need(const std::vector<int> &cids, bool ksph)
+{
+    long long need = 0;
+    for (int cid : cids) {
+        const EriClassEntry *ce = find_class(cid, ksph);
+        if (ce && ce->tier == 'M') need = std::max(need, ce->scratch_doubles);
+    }
+    return need;
+}
+
+#ifdef ERI_UNFUSED_SPHERICAL
+// work buffer of the unfused path (three Cartesian chunks), doubles
+constexpr int64_t UNFUSED_DOUBLES = int64_t(3) << 22;
+#endif
+
+void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, const int *qket, int64_t n, double *out,
+                       hipStream_t s, int64_t n_k1)
+{
+    const EriClassEntry *ce = find_class(cid, sph);
+    if (!ce) {
+        g_last_error = "no kernel for class " + std::to_string(cid);
+        throw HipFail{hipErrorInvalidValue};
+    }
+    EriClassArgs a;
+    a.qbra = qbra;
+    a.qket = qket;
+    a.pair_info = P->d_pinfo;
+    a.ppd = P->d_ppd;
+    a.cen = P->d_cen;
+    a.boys = P->d_boys;
+    a.scratch = P->d_scratch;
+    a.scratch_wgs = P->scratch_wgs;
+    a.grid_cap = P->grid_cap;
+    const int blk = nfun(ce->la, sph) * nfun(ce->lb, sph) * nfun(ce->lc, sph) * nfun(ce->ld, sph);
+    if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
+        g_last_error = "memory-tier class without scratch";
+        throw HipFail{hipErrorInvalidValue};
+    }
+    // the uncontracted prefix goes to the K4 = 1 kernel; large ranges are split so
+    // that every grid stays within int range
+    const int64_t CH = 1 << 26;
+    for (int part = 0; part < 2; ++part) {
+        const int64_t lo = part == 0 ? 0 : n_k1, hi = part == 0 ? n_k1 : n;
+        for (int64_t b = lo; b < hi; b += CH) {
+            const int64_t m = std::min(CH, hi - b);
+            a.qbra = qbra + b;
+            a.qket = qket + b;
+            a.nq = (int)m;
+            a.out = out + b * blk;
+            (part == 0 ? ce->launch_k1 : ce->launch)(a, s);
+            HIP_CHECK(hipGetLastError());
+        }
+    }
+}
+
+#ifdef ERI_UNFUSED_SPHERICAL
+// Ablation build only (the "no spherical fusion" variant of section V-B of
+// "FusionRCG"): a spherical block is computed as its Cartesian block, written
+// out, and then transformed on all four indices, Eq. (17), instead of the
+// stepwise fusion of Eq. (14).  One workgroup per quartet, four one-index
+// passes through two work buffers (the plan's unfused work buffer: calls on
+// one plan from several streams run one after another on the caller's stream).
+__global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const double *cart, double *w0, double *w1,
+                              double *dst)
+{
+    const int64_t t = blockIdx.x;
+    if (t >= n) return;
+    const int l4[4] = {la, lb, lc, ld};
+    int dims[4], ns[4];
+    for (int k = 0; k < 4; ++k) {
+        dims[k] = (l4[k] + 1) * (l4[k] + 2) / 2;
+        ns[k] = 2 * l4[k] + 1;
+    }
+    const int64_t ncar = (int64_t)dims[0] * dims[1] * dims[2] * dims[3];
+    const int nsp = ns[0] * ns[1] * ns[2] * ns[3];
+    const double *in = cart + t * ncar;
+    for (int pos = 0; pos < 4; ++pos) {
+        int before = 1, after = 1;
+        for (int k = 0; k < pos; ++k) before *= dims[k];
+        for (int k = pos + 1; k < 4; ++k) after *= dims[k];
+        const double *T = eri_sph_T[l4[pos]];
+        const int nc = dims[pos], nsv = ns[pos];
+        double *o = pos == 3 ? dst + t * nsp : ((pos % 2 == 0) ? w0 : w1) + t * ncar;
+        const int total = before * nsv * after;
+        for (int x = threadIdx.x; x < total; x += blockDim.x) {
+            const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
+            double acc = 0.0;
+            for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
+            o[x] = acc;
+        }
+        dims[pos] = nsv;
+        in = o;
+        __syncthreads();
+    }
+}
+
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
+                  int64_t n_k1 = 0)
+{
+    if (!P->sph) {
+        launch_class_kind(P, cid, false, qbra, qket, n, out, s, n_k1);
+        return;
+    }
+    const EriClassEntry *ce = find_class(cid, false);
+    if (!ce) {
+        g_last_error = "no kernel for class " + std::to_string(cid);
+        throw HipFail{hipErrorInvalidValue};
+    }
+    const int64_t nc = (int64_t)ncart(ce->la) * ncart(ce->lb) * ncart(ce->lc) * ncart(ce->ld);
+    const int64_t ns = (int64_t)nsph(ce->la) * nsph(ce->lb) * nsph(ce->lc) * nsph(ce->ld);
+    const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>(n, (UNFUSED_DOUBLES / 3) / nc));
+    double *cart = P->d_unfused, *w0 = cart + chunk * nc, *w1 = w0 + chunk * nc;
+    for (int64_t b = 0; b < n; b += chunk) {
+        const int64_t m = std::min(chunk, n - b);
+        const int64_t k1 = std::min(m, std::max<int64_t>(0, n_k1 - b));
+        launch_class_kind(P, cid, false, qbra + b, qket + b, m, cart, s, k1);
+        hipLaunchKernelGGL(k_sph_unfused, dim3((unsigned)m), dim3(256), 0, s, m, ce->la, ce->lb, ce->lc, ce->ld, cart,
+                           w0, w1, out + b * ns);
+        HIP_CHECK(hipGetLastError());
+    }
+}
+#else
+void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
+                  int64_t n_k1 = 0)
+{
+    launch_class_kind(P, cid, P->sph, qbra, qket, n, out, s, n_k1);
+}
+#endif
+
+inline int *chunk_bra(const eri_plan *P, int lane) { return P->d_chunk + (size_t)lane * 2 * P->chunk_q; }
+inline int *chunk_ket(const eri_plan *P, int lane) { return chunk_bra(P, lane) + P->chunk_q; }
+
+// quartet lists of plan slots [s, s + m): the plan's own arrays, or for a
+// screened plan the lane's chunk lists after expansion (m <= chunk_q)
+void slot_lists(const eri_plan *P, int64_t s, int64_t m, const int **qb, const int **qk, hipStream_t st, int lane)
+{
+    if (!P->screened) {
+        *qb = P->d_qbra + s;
+        *qk = P->d_qket + s;
+        return;
+    }
+    int *dqb = chunk_bra(P, lane), *dqk = chunk_ket(P, lane);
+    hipLaunchKernelGGL(k_expand, dim3(nblk(m, 256)), dim3(256), 0, st, s, m, P->nent, P->d_ent_off, P->d_bd, P->nbd,
+                       P->d_porder, P->d_pinfo, P->d_pair_i, dqb, dqk, (int *)nullptr);
+    HIP_CHECK(hipGetLastError());
+    *qb = dqb;
+    *qk = dqk;
+}
+
+// Calls over several class blocks spread the blocks over the caller's stream
+// and the side streams the caller registered, so that the last waves of one
+// class kernel overlap the first waves of the next; the caller's stream then
+// waits for the side streams.  Blocks of memory-tier classes that use the
+// plan's scratch stay on the caller's stream, one after another.
+int lanes_of(const eri_plan *P)
+{
+#ifdef ERI_UNFUSED_SPHERICAL
+    (void)P;
+    return 1;  // the unfused path shares one work buffer
+#else
+    return 1 + P->nside;
+#endif
+}
+
+void side_fork(const eri_plan *P, hipStream_t s, int lanes)
+{
+    HIP_CHECK(hipEventRecord(P->ev_fork, s));
+    for (int i = 0; i + 1 < lanes; ++i) HIP_CHECK(hipStreamWaitEvent(P->side[i], P->ev_fork, 0));
+}
+
+void side_join(const eri_plan *P, hipStream_t s, int lanes)
+{
+    for (int i = 0; i + 1 < lanes; ++i) {
+        HIP_CHECK(hipEventRecord(P->ev_side[i], P->side[i]));
+        HIP_CHECK(hipStreamWaitEvent(s, P->ev_side[i], 0));
+    }
+}
+
+inline hipStream_t lane_stream(const eri_plan *P, int lane, hipStream_t s) { return lane == 0 ? s : P->side[lane - 1]; }
+
+bool uses_scratch(const eri_plan *P, int cid)
+{
+    const EriClassEntry *ce = find_class(cid, kernel_sph(P));
+    return ce && ce->tier == 'M' && ce->scratch_doubles > 0;
+}
+
+void compute_range(const eri_plan *P, const EriBlock &B, int64_t first, int64_t count, double *out, hipStream_t st,
+                   int lane)
+{
+    const int64_t blk = (int64_t)B.na * B.nb * B.nc * B.nd;
+    const int64_t step = P->screened ? P->chunk_q : std::max<int64_t>(count, 1);
+    for (int64_t c = first; c < first + count; c += step) {
+        const int64_t m = std::min(step, first + count - c);
+        const int *qb = nullptr, *qk = nullptr;
+        slot_lists(P, B.start + c, m, &qb, &qk, st, lane);
+        const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
+        launch_class(P, B.cid, qb, qk, m, out + (c - first) * blk, st, nk1);
+    }
+}
+
+__global__ void k_add_mat(int n, const double *X, int ldx, double *Y, int ldy)
+{
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)n * n) return;
+    const int x = (int)(t / n), y = (int)(t - (int64_t)x * n);
+    Y[(size_t)x * ldy + y] += X[(size_t)x * ldx + y];
+}
+
+// ---------------------------------------------------------------------------
+// J and K digestion, chunk by chunk
+// ---------------------------------------------------------------------------
+// Integrals of the chunk, per-quartet contribution vectors, entries sorted by
+// target (stable), then each target's run added in entry order.  The chunks
+// are spread over stream lanes (the caller's stream and its registered side
+// streams), each with its own chunk buffers and its own J and A accumulators,
+// chunk i of the plan going to lane i mod (number of lanes) (chunks of
+// memory-tier classes that use the plan's scratch all go to lane 0).  After
+// the lanes join, lanes 1, 2, ... are added into lane 0's J and A in that
+// order, so the sums are deterministic.
+struct ChunkLane {
+    double *ints = nullptr, *cb = nullptr, *kv = nullptr;  // integrals, J and K contribution vectors of a chunk
+    double *J = nullptr, *A = nullptr;                     // lane accumulators (lane 0's J is the caller's)
+    int *ek = nullptr, *ek2 = nullptr, *ruk = nullptr, *rlen = nullptr, *rst = nullptr, *nruns = nullptr;
+    int64_t *eo = nullptr, *eo2 = nullptr;
+    void *tmp = nullptr;
+    size_t tmp_bytes = 0;
+};
+
+struct DigestShape {
+    int lanes;
+    int64_t CQ, CO, CB, NE;
+};
+
+DigestShape digest_shape(const eri_plan *P, bool wantJ, bool wantK)
+{
+    DigestShape d;
+    d.lanes = lanes_of(P);
+    d.CQ = std::min<int64_t>(P->chunk_q, std::max<int64_t>(P->nq, 1));
+    int64_t cbt = 0;
+    for (const EriBlock &B : P->blocks) {
+        const int64_t w = std::max<int64_t>(wantJ ? B.na * B.nb + B.nc * B.nd : 0,
+                                            wantK ? B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd : 0);
+        cbt += B.count * w;
+    }
+    const int64_t big = d.lanes > 1 ? 26 : 27;
+    d.CO = std::min<int64_t>(int64_t(1) << big, std::max<int64_t>(P->nout, 1));
+    d.CB = std::min<int64_t>(int64_t(1) << (big - 1), std::max<int64_t>(cbt, 1024));
+    d.NE = (wantK ? 4 : 2) * d.CQ;
+    return d;
+}
+
+void digest_layout(Arena &A, const eri_plan *P, bool wantJ, bool wantK, const DigestShape &d, std::vector<ChunkLane> &L,
+                   double **kacc)
+{
+    const int n = P->nbf;
+    L.assign(d.lanes, ChunkLane());
+    size_t t1 = 0, t2 = 0, t3 = 0;
+    const int n2 = (int)d.NE;
+    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, (int *)nullptr, (int *)nullptr, (int64_t *)nullptr,
+                                                 (int64_t *)nullptr, n2, 0, 32));
+    HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, (int *)nullptr, (int *)nullptr, (int *)nullptr,
+                                                    (int *)nullptr, n2));
+    HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, (int *)nullptr, (int *)nullptr, n2));
+    const size_t tb = std::max(t1, std::max(t2, t3));
+    for (int l = 0; l < d.lanes; ++l) {
+        ChunkLane &W = L[l];
+        W.ints = A.take<double>(d.CO);
+        if (wantJ) W.cb = A.take<double>(d.CB);
+        if (wantK) W.kv = A.take<double>(d.CB);
+        W.ek = A.take<int>(d.NE);
+        W.ek2 = A.take<int>(d.NE);
+        W.eo = A.take<int64_t>(d.NE);
+        W.eo2 = A.take<int64_t>(d.NE);
+        W.ruk = A.take<int>(d.NE);
+        W.rlen = A.take<int>(d.NE);
+        W.rst = A.take<int>(d.NE);
+        W.nruns = A.take<int>(1);
+        W.tmp = A.take<char>(tb);
+        W.tmp_bytes = tb;
+        if (wantJ && l > 0) W.J = A.take<double>((size_t)n * n);
+        if (wantK) W.A = A.take<double>((size_t)n * n);
+    }
+    *kacc = wantK ? L[0].A : nullptr;
+}
+
+void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, Arena &ws,
+                   hipStream_t s)
+{
+    const DigestShape d = digest_shape(P, J != nullptr, K != nullptr);
+    std::vector<ChunkLane> L;
+    double *kacc = nullptr;
+    digest_layout(ws, P, J != nullptr, K != nullptr, d, L, &kacc);
+    const int NL = d.lanes;
+    const int n = P->nbf;
+    if (NL > 1) side_fork(P, s, NL);
+    for (int l = 0; l < NL; ++l) {
+        const hipStream_t ls = lane_stream(P, l, s);
+        ChunkLane &W = L[l];
+        double *Jl = l == 0 ? J : W.J;
+        const int ldl = l == 0 ? ldj : n;
+        if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, Jl, ldl);
+        if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, W.A, n);
+        HIP_CHECK(hipGetLastError());
+    }
+    int64_t chunk_index = 0;
+    for (const EriBlock &B : P->blocks) {
+        const int nab = B.na * B.nb, ncd = B.nc * B.nd;
+        const int nkv = B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd;
+        const int64_t blk = (int64_t)nab * ncd;
+        int64_t step = std::min(d.CQ, d.CO / blk);
+        if (J) step = std::min<int64_t>(step, d.CB / (nab + ncd));
+        if (K) step = std::min<int64_t>(step, d.CB / nkv);
+        step = std::max<int64_t>(1, step);
+        const bool scratch_class = uses_scratch(P, B.cid);
+        for (int64_t c = 0; c < B.count; c += step, ++chunk_index) {
+            const int l = scratch_class ? 0 : (int)(chunk_index % NL);
+            const hipStream_t ls = lane_stream(P, l, s);
+            ChunkLane &W = L[l];
+            double *Jl = l == 0 ? J : W.J;
+            const int ldl = l == 0 ? ldj : n;
+            const int64_t m = std::min(step, B.count - c);
+            const int *qb = nullptr, *qk = nullptr;
+            slot_lists(P, B.start + c, m, &qb, &qk, ls, l);
+            const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
+            launch_class(P, B.cid, qb, qk, m, W.ints, ls, nk1);
+            // sort the n2 entries in W.ek/W.eo and encode their runs
+            auto sort_runs = [&](int n2) {
+                size_t tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, ls));
+                tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
+                tb = W.tmp_bytes;
+                HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(W.tmp, tb, W.rlen, W.rst, n2, ls));
+            };
+            if (J) {
+                const int64_t nv = m * (nab + ncd);
+                hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, ls, nv, B.na, B.nb,
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb);
+                hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, nab, ncd,
+                                   W.ek, W.eo);
+                HIP_CHECK(hipGetLastError());
+                sort_runs((int)(2 * m));
+                // at most one run per pair key (and one for the sentinel key); workgroups
+                // past the device-side run count exit at once
+                const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
+                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
+                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, Jl, ldl);
+                HIP_CHECK(hipGetLastError());
+            }
+            if (K) {
+                const int64_t nkt = m * nkv;
+                hipLaunchKernelGGL(k_kdigest_rows, dim3((unsigned)nblk(nkt, 256)), dim3(256), 0, ls, nkt, B.na, B.nb,
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.kv);
+                hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, P->d_pinfo,
+                                   P->nshell, B.na, B.nb, B.nc, B.nd, W.ek, W.eo);
+                HIP_CHECK(hipGetLastError());
+                sort_runs((int)(4 * m));
+                // at most one run per target block key (and one for the sentinel key)
+                const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
+                hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk,
+                                   W.rst, W.rlen, W.eo2, W.kv, P->nshell, P->d_bf, P->d_nfun, W.A, n);
+                HIP_CHECK(hipGetLastError());
+            }
+        }
+    }
+    if (NL > 1) side_join(P, s, NL);
+    for (int l = 1; l < NL; ++l) {
+        if (J)
+            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, L[l].J, n, J, ldj);
+        if (K)
+            hipLaunchKernelGGL(k_add_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, L[l].A, n, kacc, n);
+        HIP_CHECK(hipGetLastError());
+    }
+    if (K) {
+        hipLaunchKernelGGL(k_sym_add, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, s, n, kacc, n, K, ldk);
+        HIP_CHECK(hipGetLastError());
+    }
+}
+
+// ---------------------------------------------------------------------------
+// plan build
+// ---------------------------------------------------------------------------
+
+// What the host knows before any device work: every buffer size.
+struct BuildHost {
+    int ns = 0, npr = 0;
+    int64_t nq = 0;        // explicit lists
+    int64_t np = 0;        // shell pairs
+    int64_t nppd = 0;      // primitive pairs
+    int64_t nent = 0;      // screened: (block, bra rank) entries
+    int nbuck = 0, nbd = 0;
+    size_t diag_doubles = 0;
+    long long scratch = 0;
+    int64_t chunk_q = 0;
+    size_t cub = 0;
+    std::vector<int> hbf, hnf;
+};
+
+struct BuildBufs {
+    double *raw = nullptr;
+    // explicit
+    int *q = nullptr;
+    uint64_t *k0 = nullptr, *k1 = nullptr;
+    int64_t *p0 = nullptr, *st = nullptr, *k1e = nullptr;
+    // both
+    int *w = nullptr, *z = nullptr;
+    void *cub = nullptr;
+    // screened
+    uint64_t *pck = nullptr, *pck2 = nullptr, *ka = nullptr, *kb = nullptr, *bkey = nullptr;
+    int *pidx = nullptr, *pidx2 = nullptr, *seq = nullptr, *o1 = nullptr, *head = nullptr, *hscan = nullptr,
+        *bstart = nullptr;
+    double *diag = nullptr;
+    int64_t *cnt = nullptr, *idx = nullptr, *bs = nullptr;
+};
+
+constexpr size_t DIAG_DOUBLES = size_t(1) << 24;  // Schwarz diagonal blocks per launch
+
+void host_common(const eri_shells *sh, bool sph, BuildHost &H)
+{
+    H.ns = sh->nshell;
+    H.npr = sh->prim_off[H.ns];
+    H.hbf.assign(H.ns + 1, 0);
+    H.hnf.assign(H.ns, 0);
+    for (int i = 0; i < H.ns; ++i) {
+        H.hnf[i] = nfun(sh->l[i], sph);
+        H.hbf[i + 1] = H.hbf[i] + H.hnf[i];
+    }
+}
+
+// canonical class id of a quartet of shells with angular momenta l4
+int class_of(int li, int lj, int lk, int ll)
+{
+    const int pb = pair_class(std::max(li, lj), std::min(li, lj));
+    const int pk = pair_class(std::max(lk, ll), std::min(lk, ll));
+    return class_id_of(std::max(pb, pk), std::min(pb, pk));
+}
+
+void host_explicit(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, BuildHost &H)
+{
+    host_common(sh, (flags & ERI_SPHERICAL) != 0, H);
+    H.nq = nq;
+    H.np = 2 * nq;
+    bool present[120] = {};
+    for (int64_t x = 0; x < nq; ++x) {
+        const int *q = quartets + 4 * x;
+        H.nppd += (int64_t)sh->nprim[q[0]] * sh->nprim[q[1]] + (int64_t)sh->nprim[q[2]] * sh->nprim[q[3]];
+        present[class_of(sh->l[q[0]], sh->l[q[1]], sh->l[q[2]], sh->l[q[3]])] = true;
+    }
+    std::vector<int> cids;
+    for (int c = 0; c < 120; ++c)
+        if (present[c]) cids.push_back(c);
+    H.scratch = scratch_need(cids, kernel_sph_flags((flags & ERI_SPHERICAL) != 0));
+    H.cub = std::max(sort_pairs_u64<int64_t>(nullptr, nullptr, nullptr, nullptr, nq, nullptr, 0, nullptr),
+                     scan_i32(nullptr, nullptr, H.np, nullptr, 0, nullptr));
+}
+
+void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &H)
+{
+    host_common(sh, (flags & ERI_SPHERICAL) != 0, H);
+    const int ns = H.ns;
+    H.np = (int64_t)ns * (ns + 1) / 2;
+    std::vector<uint64_t> keys;
+    keys.reserve(H.np);
+    bool pc_present[15] = {};
+    int64_t pc_count[15] = {};
+    for (int i = 0; i < ns; ++i)
+        for (int j = 0; j <= i; ++j) {
+            const int a = sh->l[i] >= sh->l[j] ? i : j, b = a == i ? j : i;
+            const int pc = pair_class(sh->l[a], sh->l[b]);
+            const int64_t K = (int64_t)sh->nprim[a] * sh->nprim[b];
+            H.nppd += K;
+            keys.push_back(((uint64_t)pc << 16) | (uint64_t)K);
+            pc_present[pc] = true;
+            ++pc_count[pc];
+        }
+    std::sort(keys.begin(), keys.end());
+    std::vector<int64_t> nB;
+    for (size_t x = 0; x < keys.size(); ++x)
+        if (x == 0 || keys[x] != keys[x - 1]) nB.push_back(1);
+        else ++nB.back();
+    H.nbuck = (int)nB.size();
+    H.nbd = H.nbuck * (H.nbuck + 1) / 2;
+    for (int B = 0; B < H.nbuck; ++B) H.nent += (int64_t)(B + 1) * nB[B];
+    std::vector<int> cids;
+    for (int pb = 0; pb < 15; ++pb)
+        for (int pk = 0; pk <= pb; ++pk)
+            if (pc_present[pb] && pc_present[pk]) cids.push_back(class_id_of(pb, pk));
+    const bool sph = (flags & ERI_SPHERICAL) != 0;
+    H.scratch = scratch_need(cids, kernel_sph_flags(sph));
+    for (int pc = 0; pc < 15; ++pc) {
+        if (!pc_count[pc]) continue;
+        int la = 0;
+        while ((la + 1) * (la + 2) / 2 <= pc) ++la;
+        const size_t nab = (size_t)nfun(la, sph) * nfun(pc - la * (la + 1) / 2, sph);
+        H.diag_doubles = std::max(H.diag_doubles, std::min<size_t>(DIAG_DOUBLES, (size_t)pc_count[pc] * nab * nab));
+    }
+    const int64_t nuq = H.np * (H.np + 1) / 2;
+    H.chunk_q = std::min<int64_t>(chunk_q, std::max<int64_t>(nuq, 1));
+    size_t c = sort_pairs_u64<int>(nullptr, nullptr, nullptr, nullptr, H.np, nullptr, 0, nullptr);
+    c = std::max(c, scan_i32(nullptr, nullptr, H.np, nullptr, 0, nullptr));
+    c = std::max(c, scan_i64(nullptr, nullptr, H.nent, nullptr, 0, nullptr));
+    H.cub = c;
+}
+
+// Carve every buffer of a plan (and of its build) out of the arena.
+void plan_layout(Arena &A, eri_plan *P, const BuildHost &H, BuildBufs &X)
+{
+    const int ns = H.ns;
+    P->d_cen = A.take<double>((size_t)3 * ns);
+    P->d_l = A.take<int>(ns);
+    P->d_nprim = A.take<int>(ns);
+    P->d_off = A.take<int>(ns + 1);
+    P->d_bf = A.take<int>(ns + 1);
+    P->d_nfun = A.take<int>(ns);
+    P->d_exps = A.take<double>(H.npr);
+    X.raw = A.take<double>(H.npr);
+    P->d_cn = A.take<double>(H.npr);
+    P->d_pinfo = A.take<int4>(H.np);
+    X.w = A.take<int>(H.np + 1);
+    X.z = A.take<int>(H.np + 1);
+    P->d_ppd = A.take<double>((size_t)H.nppd * ERI_PP_STRIDE);
+    X.cub = A.take<char>(H.cub);
+    if (!P->screened) {
+        const int64_t nq = H.nq;
+        X.q = A.take<int>((size_t)4 * nq);
+        X.k0 = A.take<uint64_t>(nq);
+        X.k1 = A.take<uint64_t>(nq);
+        X.p0 = A.take<int64_t>(nq);
+        P->d_qsrc = A.take<int64_t>(nq);
+        P->d_qmap = A.take<int>((size_t)5 * nq);
+        P->d_qbra = A.take<int>(nq);
+        P->d_qket = A.take<int>(nq);
+        X.st = A.take<int64_t>(121);
+        X.k1e = A.take<int64_t>(121);
+    } else {
+        const int64_t np = H.np;
+        X.pck = A.take<uint64_t>(np);
+        X.pck2 = A.take<uint64_t>(np);
+        X.pidx = A.take<int>(np);
+        X.pidx2 = A.take<int>(np);
+        P->d_S = A.take<double>(np);
+        X.diag = A.take<double>(H.diag_doubles);
+        X.seq = A.take<int>(np);
+        X.ka = A.take<uint64_t>(np);
+        X.kb = A.take<uint64_t>(np);
+        X.o1 = A.take<int>(np);
+        P->d_porder = A.take<int>(np);
+        X.head = A.take<int>(np);
+        X.hscan = A.take<int>(np);
+        X.bstart = A.take<int>(H.nbuck + 1);
+        X.bkey = A.take<uint64_t>(H.nbuck);
+        P->d_bd = A.take<BlockDesc>(H.nbd);
+        X.cnt = A.take<int64_t>(H.nent + 1);
+        P->d_ent_off = A.take<int64_t>(H.nent + 1);
+        P->d_pair_i = A.take<int>(np);
+        X.idx = A.take<int64_t>(H.nbd + 1);
+        X.bs = A.take<int64_t>(H.nbd + 1);
+        P->chunk_q = H.chunk_q;
+        P->d_chunk = A.take<int>((size_t)ERI_LANES * 2 * H.chunk_q);
+    }
+    if (H.scratch > 0) {
+        P->d_scratch = A.take<double>((size_t)H.scratch * ERI_MEM_WGS);
+        P->scratch_wgs = ERI_MEM_WGS;
+        P->scratch_doubles = H.scratch;
+    }
+#ifdef ERI_UNFUSED_SPHERICAL
+    if (P->sph) P->d_unfused = A.take<double>(UNFUSED_DOUBLES);
+#endif
+}
+
+void make_pair_data(eri_plan *P, const BuildHost &H, BuildBufs &X, hipStream_t s)
+{
+    const int np = (int)P->npairs;
+    if (np == 0) return;
+    hipLaunchKernelGGL(k_copy_w, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, X.w);
+    HIP_CHECK(hipGetLastError());
+    scan_i32(X.w, X.z, np, X.cub, H.cub, s);
+    hipLaunchKernelGGL(k_set_z, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, X.z);
+    hipLaunchKernelGGL(k_pair_data, dim3(nblk(np, 128)), dim3(128), 0, s, np, P->d_pinfo, P->d_cen, P->d_off,
+                       P->d_exps, P->d_cn, P->d_ppd);
+    HIP_CHECK(hipGetLastError());
+}
+
+void build_explicit(eri_plan *P, const BuildHost &H, BuildBufs &X, const int32_t *quartets, hipStream_t s)
+{
+    const int64_t nq = H.nq;
+    P->nq = nq;
+    P->npairs = 2 * nq;
+    if (nq == 0) return;
+    upload(X.q, quartets, (size_t)4 * nq, s);
+    hipLaunchKernelGGL(k_explicit_keys, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, X.q, P->d_l, P->d_nprim, X.k0, X.p0);
+    HIP_CHECK(hipGetLastError());
+    sort_pairs_u64(X.k0, X.k1, X.p0, P->d_qsrc, nq, X.cub, H.cub, s);
+    hipLaunchKernelGGL(k_explicit_fill, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, P->d_qsrc, X.q, P->d_l, P->d_nprim,
+                       P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
+    HIP_CHECK(hipGetLastError());
+    const int NC = 120;
+    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, X.k1, X.st, X.k1e, NC);
+    HIP_CHECK(hipGetLastError());
+    std::vector<int64_t> st(NC + 1), k1e(NC + 1);
+    HIP_CHECK(hipMemcpyAsync(st.data(), X.st, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(k1e.data(), X.k1e, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
+    make_pair_data(P, H, X, s);
+    HIP_CHECK(hipStreamSynchronize(s));
+    st[NC] = nq;
+    int64_t out = 0;
+    for (int c = 0; c < NC; ++c) {
+        const int64_t cnt = st[c + 1] - st[c];
+        if (cnt <= 0) continue;
+        const EriClassEntry *ce = find_class(c, P->sph);
+        if (!ce) {
+            g_last_error = "class " + std::to_string(c) + " not built";
+            throw HipFail{hipErrorInvalidValue};
+        }
+        EriBlock b{c, st[c], cnt, out, std::min(k1e[c], st[c + 1]) - st[c], nfun(ce->la, P->sph),
+                   nfun(ce->lb, P->sph), nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
+        out += cnt * (int64_t)b.na * b.nb * b.nc * b.nd;
+        P->blocks.push_back(b);
+    }
+    P->nout = out;
+}
+
+void build_screened(eri_plan *P, const BuildHost &H, BuildBufs &X, double tau, hipStream_t s)
+{
+    const int ns = P->nshell;
+    const int64_t np = H.np;
+    if (np > (int64_t)INT32_MAX / 2) {
+        g_last_error = "too many shell pairs";
+        throw HipFail{hipErrorInvalidValue};
+    }
+    P->npairs = np;
+    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_nprim, P->d_pinfo, X.pck,
+                       X.pidx);
+    HIP_CHECK(hipGetLastError());
+    make_pair_data(P, H, X, s);
+
+    // --- Schwarz factors from the diagonal quartets (p|p), grouped by pair class
+    sort_pairs_u64(X.pck, X.pck2, X.pidx, X.pidx2, np, X.cub, H.cub, s);  // pidx2: pairs ordered by pair class
+    std::vector<uint64_t> hpc(np);
+    HIP_CHECK(hipMemcpyAsync(hpc.data(), X.pck2, sizeof(uint64_t) * np, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    {
+        int64_t i = 0;
+        while (i < np) {
+            int64_t j = i;
+            while (j < np && hpc[j] == hpc[i]) ++j;
+            const int pc = (int)hpc[i];
+            int la = 0;
+            while ((la + 1) * (la + 2) / 2 <= pc) ++la;
+            const int lb = pc - la * (la + 1) / 2;
+            const int64_t nab = nfun(la, P->sph) * nfun(lb, P->sph);
+            const int64_t per = std::max<int64_t>(1, (int64_t)H.diag_doubles / (nab * nab));
+            for (int64_t b = i; b < j; b += per) {
+                const int64_t m = std::min(per, j - b);
+                launch_class(P, class_id_of(pc, pc), X.pidx2 + b, X.pidx2 + b, m, X.diag, s);
+                hipLaunchKernelGGL(k_schwarz_max, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, X.pidx2 + b, X.diag,
+                                   (int)nab, P->d_S);
+                HIP_CHECK(hipGetLastError());
+            }
+            i = j;
+        }
+    }
+
+    // --- bucket the pairs by (pair class, K_pair), rank by S descending (ties: pair index)
+    {
+        std::vector<int> h(np);
+        for (int64_t p = 0; p < np; ++p) h[p] = (int)p;
+        upload(X.seq, h.data(), np, s);
+        hipLaunchKernelGGL(k_desc_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, X.seq, P->d_S, X.ka);
+        sort_pairs_u64(X.ka, X.kb, X.seq, X.o1, np, X.cub, H.cub, s);  // by S descending, stable: ties keep pair order
+        HIP_CHECK(hipStreamSynchronize(s));                              // h is read by the upload above
+    }
+    hipLaunchKernelGGL(k_bucket_keys, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, X.o1, P->d_l, P->d_pinfo, X.ka);
+    sort_pairs_u64(X.ka, X.kb, X.o1, P->d_porder, np, X.cub, H.cub, s);  // stable by bucket
+    hipLaunchKernelGGL(k_heads, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, X.kb, X.head);
+    scan_i32(X.head, X.hscan, np, X.cub, H.cub, s);
+    int nb_last = 0, h_last = 0;
+    HIP_CHECK(hipMemcpyAsync(&nb_last, X.hscan + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(&h_last, X.head + np - 1, sizeof(int), hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    const int nbuck = nb_last + h_last;
+    if (nbuck != H.nbuck) {
+        g_last_error = "internal: bucket count differs from the host's";
+        throw HipFail{hipErrorUnknown};
+    }
+    hipLaunchKernelGGL(k_bucket_table, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, X.kb, X.head, X.hscan, X.bstart,
+                       X.bkey);
+    std::vector<int> bstart(nbuck + 1);
+    std::vector<uint64_t> bkey(nbuck);
+    HIP_CHECK(hipMemcpyAsync(bstart.data(), X.bstart, sizeof(int) * nbuck, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(bkey.data(), X.bkey, sizeof(uint64_t) * nbuck, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipStreamSynchronize(s));
+    bstart[nbuck] = (int)np;
+
+    // --- blocks (bra bucket >= ket bucket), ordered by (class, K_bra, K_ket)
+    struct HB {
+        int cid, kb, kk, B, Bk;
+    };
+    std::vector<HB> hb;
+    for (int B = 0; B < nbuck; ++B)
+        for (int Bk = 0; Bk <= B; ++Bk) {
+            const int pcb = (int)(bkey[B] >> 16), pck = (int)(bkey[Bk] >> 16);
+            hb.push_back({class_id_of(pcb, pck), (int)(bkey[B] & 0xffff), (int)(bkey[Bk] & 0xffff), B, Bk});
+        }
+    std::stable_sort(hb.begin(), hb.end(), [](const HB &x, const HB &y) {
+        if (x.cid != y.cid) return x.cid < y.cid;
+        if (x.kb != y.kb) return x.kb < y.kb;
+        return x.kk < y.kk;
+    });
+    std::vector<BlockDesc> bd(hb.size());
+    int64_t nent = 0;
+    for (size_t i = 0; i < hb.size(); ++i) {
+        const int B = hb[i].B, Bk = hb[i].Bk;
+        bd[i] = BlockDesc{bstart[B], bstart[B + 1] - bstart[B], bstart[Bk], bstart[Bk + 1] - bstart[Bk], B == Bk ? 1 : 0,
+                          nent};
+        nent += bd[i].bra_n;
+    }
+    if (nent != H.nent || (int)bd.size() != H.nbd) {
+        g_last_error = "internal: entry count differs from the host's";
+        throw HipFail{hipErrorUnknown};
+    }
+    upload(P->d_bd, bd.data(), bd.size(), s);
+    const double tau2 = tau * tau;
+    if (nent) {
+        hipLaunchKernelGGL(k_count, dim3(nblk(nent, 256)), dim3(256), 0, s, nent, P->d_bd, (int)bd.size(), P->d_porder,
+                           P->d_S, tau2, X.cnt);
+        HIP_CHECK(hipGetLastError());
+        scan_i64(X.cnt, P->d_ent_off, nent, X.cub, H.cub, s);
+    }
+    int64_t lo = 0, lc = 0;
+    if (nent) {
+        HIP_CHECK(hipMemcpyAsync(&lo, P->d_ent_off + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipMemcpyAsync(&lc, X.cnt + nent - 1, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+    }
+    const int64_t nq = lo + lc;
+    P->nq = nq;
+    hipLaunchKernelGGL(k_pair_hi, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, P->d_pinfo, P->d_pair_i);
+    HIP_CHECK(hipGetLastError());
+    P->nbd = (int)bd.size();
+    P->nent = nent;
+    // block starts -> class ranges
+    std::vector<int64_t> hbase(bd.size());
+    for (size_t i = 0; i < bd.size(); ++i) hbase[i] = bd[i].entry_base;
+    std::vector<int64_t> bst(bd.size());
+    if (!bd.empty() && nent) {
+        // entry_base may equal nent for an empty trailing block: clamp, fix on host
+        std::vector<int64_t> idx(bd.size());
+        for (size_t i = 0; i < bd.size(); ++i) idx[i] = std::min<int64_t>(hbase[i], nent - 1);
+        upload(X.idx, idx.data(), idx.size(), s);
+        hipLaunchKernelGGL(k_gather_i64, dim3(nblk(bd.size(), 256)), dim3(256), 0, s, (int)bd.size(), P->d_ent_off,
+                           X.idx, X.bs);
+        HIP_CHECK(hipMemcpyAsync(bst.data(), X.bs, sizeof(int64_t) * bd.size(), hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+        for (size_t i = 0; i < bd.size(); ++i)
+            if (bd[i].bra_n == 0 || hbase[i] >= nent) bst[i] = nq;
+    }
+    int64_t outp = 0;
+    size_t i = 0;
+    while (i < hb.size()) {
+        size_t j = i;
+        while (j < hb.size() && hb[j].cid == hb[i].cid) ++j;
+        const int64_t st = bst[i];
+        const int64_t en = (j < hb.size()) ? bst[j] : nq;
+        if (en > st) {
+            const EriClassEntry *ce = find_class(hb[i].cid, P->sph);
+            if (!ce) {
+                g_last_error = "class " + std::to_string(hb[i].cid) + " not built";
+                throw HipFail{hipErrorInvalidValue};
+            }
+            // the (K_bra = 1, K_ket = 1) bucket pair, when present, is the first of the class
+            int64_t nk1 = 0;
+            if (hb[i].kb == 1 && hb[i].kk == 1) nk1 = ((i + 1 < hb.size()) ? bst[i + 1] : nq) - bst[i];
+            EriBlock b{hb[i].cid, st, en - st, outp, nk1, nfun(ce->la, P->sph), nfun(ce->lb, P->sph),
+                       nfun(ce->lc, P->sph), nfun(ce->ld, P->sph)};
+            outp += b.count * (int64_t)b.na * b.nb * b.nc * b.nd;
+            P->blocks.push_back(b);
+        }
+        i = j;
+    }
+    P->nout = outp;
+}
+
+int translate(const HipFail &) { return ERI_E_HIP; }
+
+int validate_shells(const eri_shells *sh)
+{
+    if (!sh || sh->nshell < 1 || !sh->centers || !sh->l || !sh->nprim || !sh->prim_off || !sh->exps || !sh->coefs)
+        return ERI_E_INVALID;
+    const int ns = sh->nshell;
+    if (sh->prim_off[0] != 0) return ERI_E_INVALID;
+    for (int s = 0; s < ns; ++s) {
+        if (sh->l[s] < 0 || sh->l[s] > ERI_MAX_L) return ERI_E_INVALID;
+        if (sh->nprim[s] < 1 || sh->nprim[s] > ERI_MAX_PRIM) return ERI_E_INVALID;
+        if (sh->prim_off[s + 1] - sh->prim_off[s] != sh->nprim[s]) return ERI_E_INVALID;
+        for (int c = 0; c < 3; ++c)
+            if (!std::isfinite(sh->centers[3 * s + c])) return ERI_E_INVALID;
+        for (int k = sh->prim_off[s]; k < sh->prim_off[s + 1]; ++k)
+            if (!(sh->exps[k] > 0.0) || !std::isfinite(sh->exps[k]) || !std::isfinite(sh->coefs[k])) return ERI_E_INVALID;
+    }
+    return ERI_OK;
+}
+
+int64_t chunk_quartets_setting()
+{
+    int64_t q = int64_t(1) << 22;
+    if (const char *cq = std::getenv("ERI_CHUNK_QUARTETS")) {
+        const long long v = std::atoll(cq);
+        if (v >= 1 && v <= (1LL << 26)) q = v;
+    }
+    return q;
+}
+
+// Plan build into an arena (after validation).  With a counting arena it only
+// sizes; otherwise it returns the plan (host struct) whose device data live in
+// the arena.
+eri_plan *build_plan(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, double tau, Arena &A,
+                     hipStream_t s)
+{
+    std::unique_ptr<eri_plan> P(new eri_plan());
+    P->flags = flags;
+    P->sph = (flags & ERI_SPHERICAL) != 0;
+    P->screened = quartets == nullptr;
+    P->nshell = sh->nshell;
+    BuildHost H;
+    if (quartets) host_explicit(sh, flags, quartets, nq, H);
+    else host_screened(sh, flags, chunk_quartets_setting(), H);
+    BuildBufs X;
+    plan_layout(A, P.get(), H, X);
+    if (!A.base) return nullptr;
+    const int ns = sh->nshell;
+    HIP_CHECK(hipGetDevice(&P->device));
+    {
+        int ncu = 0;
+        HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, P->device));
+        P->grid_cap = std::max(1, ncu) * 8;
+    }
+    P->d_boys = boys_table(P->device);
+    P->nbf = H.hbf[ns];
+    P->hl.assign(sh->l, sh->l + ns);
+    P->hk.assign(sh->nprim, sh->nprim + ns);
+    P->hoff.assign(sh->prim_off, sh->prim_off + ns + 1);
+    P->hcen.assign(sh->centers, sh->centers + 3 * (size_t)ns);
+    P->hexp.assign(sh->exps, sh->exps + H.npr);
+    P->hcn.resize(H.npr);
+    upload(P->d_cen, sh->centers, (size_t)3 * ns, s);
+    upload(P->d_l, sh->l, ns, s);
+    upload(P->d_nprim, sh->nprim, ns, s);
+    upload(P->d_off, sh->prim_off, ns + 1, s);
+    upload(P->d_bf, H.hbf.data(), ns + 1, s);
+    upload(P->d_nfun, H.hnf.data(), ns, s);
+    upload(P->d_exps, sh->exps, H.npr, s);
+    upload(X.raw, sh->coefs, H.npr, s);
+    hipLaunchKernelGGL(k_normalize, dim3(nblk(ns, 128)), dim3(128), 0, s, ns, P->d_l, P->d_nprim, P->d_off, P->d_exps,
+                       X.raw, P->d_cn, (flags & ERI_NO_NORMALIZE) ? 1 : 0);
+    HIP_CHECK(hipGetLastError());
+    HIP_CHECK(hipMemcpyAsync(P->hcn.data(), P->d_cn, sizeof(double) * H.npr, hipMemcpyDeviceToHost, s));
+    if (quartets) build_explicit(P.get(), H, X, quartets, s);
+    else build_screened(P.get(), H, X, tau, s);
+    HIP_CHECK(hipStreamSynchronize(s));
+    P->ws_used = A.used;
+    return P.release();
+}
+
+// Index-map rows of plan slots [first, first + count) on the host.  A screened
+// plan expands them on the device in pieces, into its chunk lists (calls on
+// one plan do not overlap); synchronises the stream.
+void fetch_rows(const eri_plan *P, int64_t first, int64_t count, std::vector<int> &rows, hipStream_t s)
+{
+    rows.resize(5 * (size_t)count);
+    if (!P->screened) {
+        if (count)
+            HIP_CHECK(hipMemcpyAsync(rows.data(), P->d_qmap + 5 * first, sizeof(int) * 5 * count,
+                                     hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+        return;
+    }
+    const int64_t piece = std::max<int64_t>(1, (int64_t)ERI_LANES * 2 * P->chunk_q / 5);
+    for (int64_t c = 0; c < count; c += piece) {
+        const int64_t m = std::min(piece, count - c);
+        hipLaunchKernelGGL(k_expand, dim3(nblk(m, 256)), dim3(256), 0, s, first + c, m, P->nent, P->d_ent_off, P->d_bd,
+                           P->nbd, P->d_porder, P->d_pinfo, P->d_pair_i, (int *)nullptr, (int *)nullptr, P->d_chunk);
+        HIP_CHECK(hipGetLastError());
+        HIP_CHECK(hipMemcpyAsync(rows.data() + 5 * c, P->d_chunk, sizeof(int) * 5 * m, hipMemcpyDeviceToHost, s));
+        HIP_CHECK(hipStreamSynchronize(s));
+    }
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// workspace argument check shared by the calls that take one: NULL asks for
+// the size; otherwise *ws_bytes says how much is there and must cover `need`
+int workspace_check(void *workspace, size_t *ws_bytes, size_t need)
+{
+    if (!workspace) {
+        *ws_bytes = need;
+        return 1;
+    }
+    if ((uintptr_t)workspace % 256 != 0) return ERI_E_INVALID;
+    if (*ws_bytes < need) return ERI_E_WORKSPACE;
+    return 0;
+}
+
+}  // namespace
+
+extern "C" int eri_build_quartets(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, double tau,
+                                  void *workspace, size_t *ws_bytes, void *stream, eri_plan **plan)
+{
+    if (!ws_bytes || (workspace && !plan)) return ERI_E_INVALID;
+    if (workspace) *plan = nullptr;
+    int rc = validate_shells(sh);
+    if (rc != ERI_OK) return rc;
+    if (flags & ~(ERI_SPHERICAL | ERI_NO_NORMALIZE)) return ERI_E_INVALID;
+    if (!(tau >= 0.0) || std::isinf(tau)) return ERI_E_INVALID;
+    if (quartets && (nq < 0 || tau != 0.0)) return ERI_E_INVALID;
+    if (quartets && nq > ((int64_t)1 << 30)) return ERI_E_UNSUPPORTED;
+    const int ns = sh->nshell;
+    if (quartets)
+        for (int64_t x = 0; x < 4 * nq; ++x)
+            if (quartets[x] < 0 || quartets[x] >= ns) return ERI_E_INVALID;
+    if (!quartets && (int64_t)ns * (ns + 1) / 2 > (int64_t)INT32_MAX / 2) return ERI_E_UNSUPPORTED;
+    try {
+        Arena count;
+        build_plan(sh, flags, quartets, nq, tau, count, (hipStream_t)stream);
+        const int w = workspace_check(workspace, ws_bytes, count.used);
+        if (w) return w > 0 ? ERI_OK : w;
+        Arena A(workspace, *ws_bytes);
+        *plan = build_plan(sh, flags, quartets, nq, tau, A, (hipStream_t)stream);
+    } catch (const HipFail &f) {
+        return translate(f);
+    } catch (const WsShort &) {
+        return ERI_E_WORKSPACE;
+    } catch (const std::bad_alloc &) {
+        return ERI_E_NOMEM;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_destroy(eri_plan *plan)
+{
+    delete plan;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_set_streams(eri_plan *P, void *const *streams, int32_t n)
+{
+    if (!P || n < 0 || n > ERI_MAX_SIDE_STREAMS || (n > 0 && !streams)) return ERI_E_INVALID;
+    for (int i = 0; i < n; ++i)
+        if (!streams[i]) return ERI_E_INVALID;
+    try {
+        if (n > 0 && !P->ev_fork) {
+            HIP_CHECK(hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming));
+            for (int i = 0; i < ERI_MAX_SIDE_STREAMS; ++i)
+                HIP_CHECK(hipEventCreateWithFlags(&P->ev_side[i], hipEventDisableTiming));
+        }
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    P->nside = n;
+    for (int i = 0; i < ERI_MAX_SIDE_STREAMS; ++i) P->side[i] = i < n ? (hipStream_t)streams[i] : nullptr;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_info(const eri_plan *P, int64_t *nq, int64_t *nout, int32_t *nb, int32_t *nbf, int64_t *np)
+{
+    if (!P) return ERI_E_INVALID;
+    if (nq) *nq = P->nq;
+    if (nout) *nout = P->nout;
+    if (nb) *nb = (int32_t)P->blocks.size();
+    if (nbf) *nbf = P->nbf;
+    if (np) *np = P->npairs;
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_blocks(const eri_plan *P, int32_t *cid, int64_t *start, int64_t *count, int64_t *out_off)
+{
+    if (!P) return ERI_E_INVALID;
+    for (size_t b = 0; b < P->blocks.size(); ++b) {
+        if (cid) cid[b] = P->blocks[b].cid;
+        if (start) start[b] = P->blocks[b].start;
+        if (count) count[b] = P->blocks[b].count;
+        if (out_off) out_off[b] = P->blocks[b].out_off;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_quartets(const eri_plan *P, int64_t first, int64_t count, int32_t *dst, void *stream)
+{
+    if (!P || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
+    if (count == 0) return ERI_OK;
+    if (!dst || count > (int64_t)INT32_MAX) return ERI_E_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    try {
+        if (P->screened) {
+            hipLaunchKernelGGL(k_expand, dim3(nblk(count, 256)), dim3(256), 0, s, first, count, P->nent, P->d_ent_off,
+                               P->d_bd, P->nbd, P->d_porder, P->d_pinfo, P->d_pair_i, (int *)nullptr, (int *)nullptr,
+                               dst);
+            HIP_CHECK(hipGetLastError());
+        } else {
+            HIP_CHECK(hipMemcpyAsync(dst, P->d_qmap + 5 * first, sizeof(int) * 5 * count, hipMemcpyDeviceToDevice, s));
+        }
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_plan_index_map(const eri_plan *P, int32_t *dst, void *stream)
+{
+    if (!P || (!dst && P->nq)) return ERI_E_INVALID;
+    if (!P->nq) return ERI_OK;
+    if (P->nq > (int64_t)INT32_MAX) return ERI_E_UNSUPPORTED;
+    return eri_plan_quartets(P, 0, P->nq, dst, stream);
+}
+
+extern "C" int eri_plan_schwarz(const eri_plan *P, double *dst, void *stream)
+{
+    if (!P || !dst) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    hipError_t e = hipMemcpyAsync(dst, P->d_S, sizeof(double) * P->npairs, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        g_last_error = std::string("hipMemcpyAsync: ") + hipGetErrorString(e);
+        return ERI_E_HIP;
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_compute_batch(const eri_plan *P, int32_t b0, int32_t b1, double *out, int64_t cap, void *stream)
+{
+    if (!P) return ERI_E_INVALID;
+    const int nb = (int)P->blocks.size();
+    if (b0 < 0 || b1 > nb || b0 > b1) return ERI_E_INVALID;
+    if (b0 == b1) return ERI_OK;
+    const int64_t base = P->blocks[b0].out_off;
+    const int64_t end = (b1 < nb) ? P->blocks[b1].out_off : P->nout;
+    if (!out || cap < end - base) return out ? ERI_E_CAPACITY : ERI_E_INVALID;
+    try {
+        const hipStream_t s = (hipStream_t)stream;
+        const int lanes = b1 - b0 > 1 ? lanes_of(P) : 1;
+        if (lanes > 1) side_fork(P, s, lanes);
+        int rr = 0;
+        for (int b = b0; b < b1; ++b) {
+            const EriBlock &B = P->blocks[b];
+            const int lane = uses_scratch(P, B.cid) ? 0 : (rr++) % lanes;
+            compute_range(P, B, 0, B.count, out + (B.out_off - base), lane_stream(P, lane, s), lane);
+        }
+        if (lanes > 1) side_join(P, s, lanes);
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+extern "C" int eri_compute_range(const eri_plan *P, int32_t block, int64_t first, int64_t count, double *out,
+                                 int64_t cap, void *stream)
+{
+    if (!P || block < 0 || block >= (int)P->blocks.size() || first < 0 || count < 0) return ERI_E_INVALID;
+    const EriBlock &B = P->blocks[block];
+    if (first > B.count || count > B.count - first) return ERI_E_INVALID;
+    if (count == 0) return ERI_OK;
+    const int64_t need = count * (int64_t)B.na * B.nb * B.nc * B.nd;
+    if (!out) return ERI_E_INVALID;
+    if (cap < need) return ERI_E_CAPACITY;
+    try {
+        compute_range(P, B, first, count, out, (hipStream_t)stream, 0);
+    } catch (const HipFail &f) {
+        return translate(f);
+    }
+    return ERI_OK;
+}
+
+namespace {
+
+int digest_entry(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj, double *K, int32_t ldk,
+                 bool wantJ, bool wantK, void *workspace, size_t *ws_bytes, void *stream)
+{
+    if (!P || !ws_bytes) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    if (wantK && P->nshell > 46340) return ERI_E_UNSUPPORTED;  // target block keys are nshell^2 in 32 bits
+    try {
+        const DigestShape d = digest_shape(P, wantJ, wantK);
+        std::vector<ChunkLane> L;
+        double *kacc = nullptr;
+        Arena count;
+        digest_layout(count, P, wantJ, wantK, d, L, &kacc);
+        const int w = workspace_check(workspace, ws_bytes, count.used);
+        if (w) return w > 0 ? ERI_OK : w;
+        if (!D || ldd < P->nbf || (wantJ && (!J || ldj < P->nbf)) || (wantK && (!K || ldk < P->nbf)))
+            return ERI_E_INVALID;
+        Arena A(workspace, *ws_bytes);
+        digest_JK_run(P, D, ldd, wantJ ? J : nullptr, ldj, wantK ? K : nullptr, ldk, A, (hipStream_t)stream);
+    } catch (const HipFail &f) {
+        return translate(f);
+    } catch (const WsShort &) {
+        return ERI_E_WORKSPACE;
+    }
+    return ERI_OK;
+}
+
+}  // namespace
+
+extern "C" int eri_digest_J(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj, void *workspace,
+                            size_t *ws_bytes, void *stream)
+{
+    return digest_entry(P, D, ldd, J, ldj, nullptr, 0, true, false, workspace, ws_bytes, stream);
+}
+
+extern "C" int eri_digest_JK(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,
+                             int32_t ldk, void *workspace, size_t *ws_bytes, void *stream)
+{
+    if (!J && !K) return ERI_E_INVALID;
+    return digest_entry(P, D, ldd, J, ldj, K, ldk, J != nullptr, K != nullptr, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// First derivatives with respect to the centres
+// ---------------------------------------------------------------------------
+namespace {
+
+// Everything a derivative call needs, from the slots' index-map rows.
+struct DerivHost {
+    std::vector<int> rows;                 // [5 count]
+    std::vector<int64_t> dst_off, cart_off;
+    int64_t dtot = 0, ctot = 0;
+    // auxiliary shells: [0, ns) the shells, [ns, 2ns) raised, [2ns, 3ns) lowered (raw coefficients)
+    std::vector<int32_t> al, ak, aoff, aq;
+    std::vector<double> acen, aexp, acf;
+    eri_shells ash{};
+    int64_t aux_nout = 0;
+};
+
+int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, DerivHost &H)
+{
+    fetch_rows(P, first, count, H.rows, s);
+    const int ns = P->nshell;
+    const std::vector<int> &hl = P->hl, &hk = P->hk, &hoff = P->hoff;
+    for (int64_t t = 0; t < count; ++t)
+        for (int k = 0; k < 4; ++k)
+            if (hl[H.rows[5 * t + k]] + 1 > ERI_MAX_L) return ERI_E_UNSUPPORTED;
+    const bool sph = P->sph;
+    H.dst_off.resize(count);
+    H.cart_off.resize(count);
+    for (int64_t t = 0; t < count; ++t) {
+        const int *r = &H.rows[5 * t];
+        int64_t nf = 1, nc = 1;
+        for (int k = 0; k < 4; ++k) {
+            nf *= nfun(hl[r[k]], sph);
+            nc *= ncart(hl[r[k]]);
+        }
+        H.dst_off[t] = H.dtot;
+        H.cart_off[t] = H.ctot;
+        H.dtot += 12 * nf;
+        H.ctot += 12 * nc;
+    }
+    const int npr = hoff[ns];
+    H.al.resize(3 * ns);
+    H.ak.resize(3 * ns);
+    H.aoff.resize(3 * ns + 1);
+    H.acen.resize(9 * (size_t)ns);
+    H.aexp.resize(3 * (size_t)npr);
+    H.acf.resize(3 * (size_t)npr);
+    H.aoff[0] = 0;
+    for (int part = 0; part < 3; ++part)
+        for (int x = 0; x < ns; ++x) {
+            const int y = part * ns + x;
+            H.al[y] = part == 0 ? hl[x] : part == 1 ? hl[x] + 1 : std::max(hl[x] - 1, 0);
+            H.ak[y] = hk[x];
+            H.aoff[y + 1] = H.aoff[y] + hk[x];
+            for (int c = 0; c < 3; ++c) H.acen[3 * y + c] = P->hcen[3 * x + c];
+            for (int q = 0; q < hk[x]; ++q) {
+                const double a = P->hexp[hoff[x] + q], c = P->hcn[hoff[x] + q];
+                H.aexp[H.aoff[y] + q] = a;
+                H.acf[H.aoff[y] + q] = part == 0 ? c : part == 1 ? 2.0 * a * c : (hl[x] > 0 ? c : 0.0);
+            }
+        }
+    H.ash = eri_shells{3 * ns, H.acen.data(), H.al.data(), H.ak.data(), H.aoff.data(), H.aexp.data(), H.acf.data()};
+    // slot t, centre p, raised (0) or lowered (1): auxiliary quartet u = (t 4 + p) 2 + sg
+    H.aq.resize(32 * (size_t)count);
+    for (int64_t t = 0; t < count; ++t)
+        for (int p = 0; p < 4; ++p)
+            for (int sg = 0; sg < 2; ++sg) {
+                int32_t *q = &H.aq[4 * ((t * 4 + p) * 2 + sg)];
+                int64_t blk = 1;
+                for (int k = 0; k < 4; ++k) q[k] = H.rows[5 * t + k];
+                q[p] += (sg == 0 ? 1 : 2) * ns;
+                for (int k = 0; k < 4; ++k) blk *= ncart(H.al[q[k]]);
+                H.aux_nout += blk;
+            }
+    return ERI_OK;
+}
+
+struct DerivBufs {
+    int *rows = nullptr;
+    double *aux = nullptr, *cart = nullptr, *tmp = nullptr;
+    int64_t *slot_of = nullptr, *bt = nullptr, *aux_off = nullptr, *off = nullptr;
+};
+
+void deriv_layout(Arena &A, const eri_plan *P, int64_t count, const DerivHost &H, DerivBufs &X)
+{
+    X.rows = A.take<int>(5 * (size_t)count);
+    X.aux = A.take<double>(H.aux_nout);
+    X.slot_of = A.take<int64_t>(8 * (size_t)count);
+    X.bt = A.take<int64_t>(3 * 120);
+    X.aux_off = A.take<int64_t>(8 * (size_t)count);
+    X.off = A.take<int64_t>(2 * (size_t)count);
+    if (P->sph) {
+        X.cart = A.take<double>(H.ctot);
+        X.tmp = A.take<double>(H.ctot);
+    }
+}
+
+}  // namespace
+
+extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count, double *out, int64_t cap,
+                                 void *workspace, size_t *ws_bytes, void *stream)
+{
+    if (!P || !ws_bytes || first < 0 || count < 0 || first > P->nq || count > P->nq - first) return ERI_E_INVALID;
+    if (count > ((int64_t)1 << 24)) return ERI_E_INVALID;
+    if (count == 0) {
+        if (!workspace) *ws_bytes = 0;
+        return ERI_OK;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    std::unique_ptr<eri_plan> Aux;
+    try {
+        DerivHost H;
+        int rc = deriv_host(P, first, count, s, H);
+        if (rc != ERI_OK) return rc;
+        DerivBufs X;
+        Arena cnt;
+        build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), 8 * count, 0.0, cnt, s);
+        deriv_layout(cnt, P, count, H, X);
+        const int w = workspace_check(workspace, ws_bytes, cnt.used);
+        if (w) return w > 0 ? ERI_OK : w;
+        if (!out) return ERI_E_INVALID;
+        if (cap < H.dtot) return ERI_E_CAPACITY;
+        Arena A(workspace, *ws_bytes);
+        Aux.reset(build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), 8 * count, 0.0, A, s));
+        deriv_layout(A, P, count, H, X);
+        const eri_plan *Ap = Aux.get();
+        for (const EriBlock &B : Ap->blocks) compute_range(Ap, B, 0, B.count, X.aux + B.out_off, s, 0);
+        upload(X.rows, H.rows.data(), 5 * (size_t)count, s);
+        const int64_t na = 8 * count;
+        hipLaunchKernelGGL(k_invert_src, dim3(nblk(na, 256)), dim3(256), 0, s, na, Ap->d_qsrc, X.slot_of);
+        HIP_CHECK(hipGetLastError());
+        const int nb = (int)Ap->blocks.size();
+        std::vector<int64_t> bt(3 * (size_t)nb);
+        for (int b = 0; b < nb; ++b) {
+            const EriBlock &B = Ap->blocks[b];
+            bt[b] = B.start;
+            bt[nb + b] = B.out_off;
+            bt[2 * nb + b] = (int64_t)B.na * B.nb * B.nc * B.nd;
+        }
+        upload(X.bt, bt.data(), bt.size(), s);
+        hipLaunchKernelGGL(k_slot_offsets, dim3(nblk(na, 256)), dim3(256), 0, s, na, nb, X.bt, X.bt + nb, X.bt + 2 * nb,
+                           X.aux_off);
+        HIP_CHECK(hipGetLastError());
+        upload(X.off, H.dst_off.data(), count, s);
+        upload(X.off + count, H.cart_off.data(), count, s);
+        if (!P->sph) {
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, X.rows, P->d_l,
+                               X.slot_of, Ap->d_qmap, Ap->d_l, X.aux_off, X.aux, X.off, out);
+        } else {
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, X.rows, P->d_l,
+                               X.slot_of, Ap->d_qmap, Ap->d_l, X.aux_off, X.aux, X.off + count, X.cart);
+            HIP_CHECK(hipGetLastError());
+            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)(12 * count)), dim3(256), 0, s, count, X.rows, P->d_l,
+                               X.cart, X.tmp, X.off + count, X.off, out);
+        }
+        HIP_CHECK(hipGetLastError());
+        // the host vectors uploaded above are read by the copies before they return
+        HIP_CHECK(hipStreamSynchronize(s));
+    } catch (const HipFail &f) {
+        return translate(f);
+    } catch (const WsShort &) {
+        return ERI_E_WORKSPACE;
+    } catch (const std::bad_alloc &) {
+        return ERI_E_NOMEM;
+    }
+    return ERI_OK;
+}
+
+extern "C" const char *eri_strerror(int code)
+{
+    switch (code) {
+    case ERI_OK: return "ok";
+    case ERI_E_INVALID: return "invalid argument";
+    case ERI_E_UNSUPPORTED: return "unsupported";
+    case ERI_E_CAPACITY: return "output buffer too small";
+    case ERI_E_HIP: {
+        static thread_local std::string msg;
+        msg = "HIP error: " + g_last_error;
+        return msg.c_str();
+    }
+    case ERI_E_NOMEM: return "out of host memory";
+    case ERI_E_WORKSPACE: return "workspace smaller than the size query returned";
+    default: return "unknown error";
+    }
+}
 
 extern "C" int eri_fp64_fma_tflops(double *tflops, void *stream)
 {
     if (!tflops) return ERI_E_INVALID;
     hipStream_t s = (hipStream_t)stream;
-    double *out = nullptr;
     hipEvent_t e0 = nullptr, e1 = nullptr;
     int rc = ERI_OK;
     try {
@@ -2166,14 +2265,15 @@ extern "C" int eri_fp64_fma_tflops(double *tflops, void *stream)
         HIP_CHECK(hipGetDevice(&dev));
         HIP_CHECK(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
         const int grid = ncu * 8;  // 256-lane workgroups: 8 per compute unit = 8 waves per SIMD
-        HIP_CHECK(hipMalloc(&out, (size_t)grid * 256 * sizeof(double)));
+        double *sink = nullptr;
+        HIP_CHECK(hipGetSymbolAddress((void **)&sink, HIP_SYMBOL(g_fma_sink)));
         HIP_CHECK(hipEventCreate(&e0));
         HIP_CHECK(hipEventCreate(&e1));
-        hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, out, 0.999, 1e-3);
+        hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, sink, 0.999, 1e-3, -1.0);
         HIP_CHECK(hipGetLastError());
         const int reps = 5;
         HIP_CHECK(hipEventRecord(e0, s));
-        for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, out, 0.999, 1e-3);
+        for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(k_fma_rate, dim3(grid), dim3(256), 0, s, sink, 0.999, 1e-3, -1.0);
         HIP_CHECK(hipGetLastError());
         HIP_CHECK(hipEventRecord(e1, s));
         HIP_CHECK(hipEventSynchronize(e1));
@@ -2186,7 +2286,6 @@ extern "C" int eri_fp64_fma_tflops(double *tflops, void *stream)
     }
     if (e0) (void)hipEventDestroy(e0);
     if (e1) (void)hipEventDestroy(e1);
-    if (out) (void)hipFree(out);
     return rc;
 }
 

@@ -467,3 +467,103 @@ def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, n
                 bound = np.moveaxis(np.tensordot(np.abs(sph_coeffs(l)), np.moveaxis(bound, pos, 0), axes=(1, 0)), 0, pos)
         out.append(bound.ravel())
     return np.concatenate(out) if out else np.zeros(0)
+
+
+def _unrolled_hrr_abs(la, lb, R):
+    """|coefficients| of the horizontal recurrence unrolled by the binomial
+    theorem: rows the Cartesian pairs (a, b) of shells la, lb (row-major), columns
+    the components e of the intermediates [e0| with |e| = la..la+lb (by |e|, then
+    Cartesian order); (a b| = sum_e coefficient x [e 0|, each coefficient a
+    product of C(b_i, k_i) |R_i|^(b_i - k_i), R = A - B."""
+    from math import comb
+    ca, cb = cart_components(la), cart_components(lb)
+    cols = {}
+    for le in range(la, la + lb + 1):
+        for e in cart_components(le):
+            cols[e] = len(cols)
+    M = np.zeros((len(ca) * len(cb), len(cols)))
+    for ia, xa in enumerate(ca):
+        for ib, yb in enumerate(cb):
+            terms = [(1.0, (0, 0, 0))]
+            for ax in range(3):
+                terms = [(cf * comb(yb[ax], ki) * abs(R[ax]) ** (yb[ax] - ki),
+                          tuple(ki if t == ax else k[t] for t in range(3)))
+                         for cf, k in terms for ki in range(yb[ax] + 1)]
+            for cf, k in terms:
+                M[ia * len(cb) + ib, cols[(xa[0] + k[0], xa[1] + k[1], xa[2] + k[2])]] += cf
+    return M
+
+
+def _oriented(sh, i, j):
+    """The pair (i, j) in the order the library evaluates it: the shell of
+    higher l first, the higher shell index first when the l are equal."""
+    i, j = max(i, j), min(i, j)
+    return (j, i) if sh.l[i] < sh.l[j] else (i, j)
+
+
+def hgp_rounding_bound_J(sh, spherical: bool, bra_pairs, D, S, tau, eps: float = 2.0 ** -53):
+    """The two-phase fp64 floor (hgp_rounding_bound) propagated into J blocks.
+
+    For each requested shell pair (i, j), F_ij = sum over the ket pairs (k, l)
+    that pass the Schwarz test of f_kl sum_(cd) B(ij|kl)[ab, cd] |D_cd| with
+    f_kl = 2 for k != l, B the per-element floor of the quartet in the
+    orientation the library evaluates it in (see _oriented).  A J element whose
+    integrals each carry an error of at most c x B is off by at most c x F.
+    Computed with matrices: B = eps |T| M_bra V M_ket^T |T|^T, M the unrolled
+    horizontal recurrences (_unrolled_hrr_abs), V the magnitudes of the oracle's
+    contracted intermediates (e_A s_B | f_C s_D), obtained for every ket in one
+    batch.  Returns a list of arrays [n_i, n_j] in the requested orientation.
+    """
+    from workloads.configs import _pack
+    ns = int(sh.l.shape[0])
+    bf = basis_offsets(sh, spherical)
+    LMAX = 9
+    # every shell again with l' = 0..8 on raw monomials, normalised coefficients of its own l
+    cen, ls, ks, ex, co = [], [], [], [], []
+    for s in range(ns):
+        e = sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]
+        c = normalize(int(sh.l[s]), e, sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]])
+        for lp in range(LMAX):
+            cen.append(sh.centers[s])
+            ls.append(lp)
+            ks.append(len(e))
+            ex.append(e)
+            co.append(c)
+    aug = _pack(cen, ls, ks, ex, co)
+    t2 = float(tau) * float(tau)
+    kets = [(k, l) for k in range(ns) for l in range(k + 1)]
+    T = [np.abs(sph_coeffs(l)) for l in range(5)]
+    out = []
+    for (i, j) in bra_pairs:
+        a, b = _oriented(sh, i, j)
+        la, lb = int(sh.l[a]), int(sh.l[b])
+        pij = max(i, j) * (max(i, j) + 1) // 2 + min(i, j)
+        keep = [_oriented(sh, k, l) for (k, l) in kets if S[pij] * S[k * (k + 1) // 2 + l] >= t2]
+        Mb = _unrolled_hrr_abs(la, lb, sh.centers[a] - sh.centers[b])
+        if spherical:
+            Mb = np.kron(T[la], T[lb]) @ Mb
+        u = np.zeros(Mb.shape[1])
+        # intermediates of every kept ket, batched by (l_e, l_f)
+        q, where = [], []
+        for t, (c, d) in enumerate(keep):
+            lc, ld = int(sh.l[c]), int(sh.l[d])
+            for le in range(la, la + lb + 1):
+                for lf in range(lc, lc + ld + 1):
+                    q.append((a * LMAX + le, b * LMAX, c * LMAX + lf, d * LMAX))
+                    where.append((t, le, lf))
+        flat, off = eri(aug, q, False, normalize_=False)
+        ends = np.append(np.asarray(off), len(flat))
+        V = {}
+        for x, (t, le, lf) in enumerate(where):
+            V[(t, le, lf)] = np.abs(flat[ends[x]:ends[x + 1]]).reshape(ncart(le), ncart(lf))
+        for t, (c, d) in enumerate(keep):
+            lc, ld = int(sh.l[c]), int(sh.l[d])
+            Vt = np.block([[V[(t, le, lf)] for lf in range(lc, lc + ld + 1)] for le in range(la, la + lb + 1)])
+            Mk = _unrolled_hrr_abs(lc, ld, sh.centers[c] - sh.centers[d])
+            if spherical:
+                Mk = np.kron(T[lc], T[ld]) @ Mk
+            w = Mk.T @ np.abs(D[bf[c]:bf[c + 1], bf[d]:bf[d + 1]]).ravel()
+            u += (2.0 if c != d else 1.0) * (Vt @ w)
+        F = (eps * (Mb @ u)).reshape(nfunc(la, spherical), nfunc(lb, spherical))
+        out.append(F if a == i else F.T)
+    return out

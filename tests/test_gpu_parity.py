@@ -122,6 +122,39 @@ def assert_schwarz(S_gpu, sh, spherical, what="Schwarz factors"):
     assert np.all(err <= tol), f"{what}: worst pair {worst}: gpu={S_gpu[worst]!r} oracle={S_ref[worst]!r}"
 
 
+def assert_J_parity(Jg, Jref, sh, spherical, D, S, tau, what):
+    """J element-wise against the bar; an element that misses max(1e-10|ref|, 1e-13)
+    may use the two-phase floor propagated into J (oracle.hgp_rounding_bound_J:
+    the per-integral floor B of every quartet the element sums, times |D|), with
+    the factor of the integral bar."""
+    Jg = np.asarray(Jg, dtype=float)
+    err = np.abs(Jg - Jref)
+    tol = np.maximum(RTOL * np.abs(Jref), ATOL)
+    bad = np.argwhere(err > tol)
+    bf = oracle.basis_offsets(sh, spherical)
+    shell_of = np.searchsorted(bf, np.arange(bf[-1]), side="right") - 1
+    blocks = sorted({(int(shell_of[m]), int(shell_of[n])) for m, n in bad})
+    worst = 0.0
+    if blocks:
+        floors = oracle.hgp_rounding_bound_J(sh, spherical, blocks, D, S, tau)
+        for (i, j), F in zip(blocks, floors):
+            sl = (slice(bf[i], bf[i + 1]), slice(bf[j], bf[j + 1]))
+            e, t = err[sl], tol[sl]
+            m = e > t
+            if m.any():
+                worst = max(worst, float(np.max(e[m] / np.maximum(F[m], 1e-300))))
+            tol[sl] = np.maximum(t, HGP_FLOOR_FACTOR * F)
+    nbad = int(np.sum(err > tol))
+    record(what, Jg.size, len(bad), worst, floor_blocks=len(blocks))
+    if len(bad):
+        _log(f"  {what}: {len(bad)} of {Jg.size} elements within the propagated two-phase floor only, in "
+             f"{len(blocks)} shell blocks (largest err/F {worst:.3f})")
+    if nbad:
+        k = int(np.argmax(err / tol))
+        raise AssertionError(f"{what}: {nbad} elements outside the bar; worst flat index {k}: gpu={Jg.flat[k]!r} "
+                             f"oracle={Jref.flat[k]!r} err={err.flat[k]:.3e} tol={tol.flat[k]:.3e}")
+
+
 def oracle_flat(sh, imap, spherical):
     if len(imap) == 0:
         return np.zeros(0)
@@ -260,19 +293,19 @@ def test_multi_block_call_matches_block_by_block(eri):
         assert np.array_equal(got, ref), "multi-block integrals differ from the block-by-block ones"
 
 
-def test_implicit_plan_matches_explicit(eri):
-    """The same screened plan kept implicit (prefix counts, expanded in chunks of
-    1000 quartets): identical index map and integrals, J to the bar and
-    bitwise reproducible."""
+def test_small_chunks_match_default_chunks(eri):
+    """The same screened plan with its slot lists expanded in chunks of 1000
+    quartets (instead of one chunk): identical index map and integrals, J to the
+    bar and bitwise reproducible."""
     import os
     import torch
-    _log("case: C3 4-atom cluster, implicit plan with 1000-quartet chunks vs explicit")
+    _log("case: C3 4-atom cluster, 1000-quartet chunks vs one chunk")
     w = make_config(3, scale={"natoms": 4})
     sh = w.shells
     pe, oute, ime = run_plan(eri, sh, 1, None, w.tau)
     os.environ["ERI_CHUNK_QUARTETS"] = "1000"
     try:
-        pi = eri.build_quartets(sh, eri.ERI_SPHERICAL | eri.ERI_IMPLICIT, None, w.tau)
+        pi = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
     finally:
         del os.environ["ERI_CHUNK_QUARTETS"]
     assert pi.n_quartets == pe.n_quartets > 5000
@@ -283,7 +316,7 @@ def test_implicit_plan_matches_explicit(eri):
     outi = torch.empty(pi.n_out, dtype=torch.float64, device="cuda")
     eri.compute_batch(pi, outi)
     torch.cuda.synchronize()
-    assert np.array_equal(outi.cpu().numpy(), oute), "implicit plan integrals differ from the explicit plan's"
+    assert np.array_equal(outi.cpu().numpy(), oute), "1000-quartet chunks give other integrals than one chunk"
     D = torch.tensor(w.density, device="cuda")
     J1 = torch.full_like(D, 3.0)
     eri.digest_J(pi, D, J1)
@@ -291,10 +324,10 @@ def test_implicit_plan_matches_explicit(eri):
     eri.digest_J(pi, D, J2)
     torch.cuda.synchronize()
     Jg = J1.cpu().numpy()
-    assert np.array_equal(Jg, J2.cpu().numpy()), "implicit-plan J is not bitwise reproducible"
+    assert np.array_equal(Jg, J2.cpu().numpy()), "J is not bitwise reproducible"
     flat, off = oracle.eri(sh, ime[:, :4], True)
     Jref = oracle.J_from_quartets(sh, True, ime[:, :4], flat, off, w.density)
-    assert_parity(Jg, Jref, "implicit-plan J")
+    assert_parity(Jg, Jref, "J with 1000-quartet chunks")
 
 
 def test_K_tiny_molecule_against_plain_sum(eri):
@@ -321,19 +354,19 @@ def test_K_tiny_molecule_against_plain_sum(eri):
     assert_parity(J.cpu().numpy(), oracle.J_naive(sh, False, Dh), "J (JK pass) vs plain sum")
 
 
-def test_K_cluster_explicit_and_implicit(eri):
-    """K of the 4-atom SVP-like cluster (spherical, tau = 1e-12) from the
-    explicit plan and from the implicit plan in 1000-quartet chunks, against
-    the oracle's unique-quartet K over the same quartets."""
+def test_K_cluster_default_and_small_chunks(eri):
+    """K of the 4-atom SVP-like cluster (spherical, tau = 1e-12) with one chunk
+    and with 1000-quartet chunks, against the oracle's unique-quartet K over the
+    same quartets."""
     import os
     import torch
-    _log("case: K of the C3 4-atom cluster, explicit and implicit plans")
+    _log("case: K of the C3 4-atom cluster, one chunk and 1000-quartet chunks")
     w = make_config(3, scale={"natoms": 4})
     sh = w.shells
     pe = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
     os.environ["ERI_CHUNK_QUARTETS"] = "1000"
     try:
-        pi = eri.build_quartets(sh, eri.ERI_SPHERICAL | eri.ERI_IMPLICIT, None, w.tau)
+        pi = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
     finally:
         del os.environ["ERI_CHUNK_QUARTETS"]
     imap = pe.index_map().cpu().numpy()
@@ -344,8 +377,8 @@ def test_K_cluster_explicit_and_implicit(eri):
     torch.cuda.synchronize()
     flat, off = oracle.eri(sh, imap[:, :4], True)
     Kref = oracle.K_from_quartets(sh, True, imap[:, :4], flat, off, w.density)
-    assert_parity(Ke.cpu().numpy(), Kref, "K explicit plan")
-    assert_parity(Ki.cpu().numpy(), Kref, "K implicit plan, 1000-quartet chunks")
+    assert_parity(Ke.cpu().numpy(), Kref, "K one chunk")
+    assert_parity(Ki.cpu().numpy(), Kref, "K 1000-quartet chunks")
     Kg = Ke.cpu().numpy()
     assert np.array_equal(Kg, Kg.T)
 
@@ -384,16 +417,21 @@ def test_c5_full_plan_counts_and_sampled_integrals(eri):
     ends = np.append(np.asarray(off)[:len(i)], len(flat))
     Sref = np.array([np.abs(flat[ends[x]:ends[x + 1]]).max() for x in range(len(i))])
     assert_parity(S[i * (i + 1) // 2 + j], Sref, "C5 sampled Schwarz factors")
-    # per block: the first slot and seeded slots of modest cost
-    out_rows, out_vals = [], []
+    # per block: the first slot, seeded slots of modest cost, and the seeded slot
+    # with the largest primitive-quartet count
+    out_rows, out_vals, k4max = [], [], []
     for b in range(plan.n_blocks):
         st, cnt = int(plan.block_start[b]), int(plan.block_count[b])
         cand = np.unique(np.concatenate([[st], st + rng.integers(0, cnt, 64)]))
         rows_all = oplan.screened_decode(sc, cand)
         got_rows = np.concatenate([plan.quartets(int(s), 1).cpu().numpy() for s in cand[:8]])
         np.testing.assert_array_equal(got_rows, rows_all[:8])
-        keep = np.flatnonzero(_cheap_slots(rows_all, nprim, 64))[:3]
-        for x in keep:
+        keep = list(np.flatnonzero(_cheap_slots(rows_all, nprim, 64))[:3])
+        # and the candidate with the longest contraction (K4 up to 8^4 in this cluster)
+        k4 = np.prod(nprim[rows_all[:, :4]], axis=1)
+        keep.append(int(np.argmax(k4)))
+        k4max.append(int(k4.max()))
+        for x in dict.fromkeys(keep):
             s = int(cand[x])
             n = int(oracle.block_sizes(sh, rows_all[x:x + 1, :4], True)[0])
             o = torch.empty(n, dtype=torch.float64, device="cuda")
@@ -403,7 +441,8 @@ def test_c5_full_plan_counts_and_sampled_integrals(eri):
     torch.cuda.synchronize()
     q = np.array(out_rows)[:, :4]
     flat, _ = oracle.eri(sh, q, True)
-    _log(f"  {len(q)} sampled quartets over {plan.n_blocks} blocks")
+    _log(f"  {len(q)} sampled quartets over {plan.n_blocks} blocks, largest K4 per block: {k4max}")
+    assert max(k4max) >= 1024
     assert_parity(np.concatenate(out_vals), flat, "C5 sampled integrals", sh, q, True)
 
 
@@ -447,8 +486,8 @@ def test_c4_full_size_sampled(eri):
     plan, got, imap = run_plan(eri, w.shells, 1, w.quartets)
     assert list(plan.block_count) == [4000, 1000]
     rng = np.random.default_rng(4)
-    fsel = np.unique(np.concatenate([[0, 3999], rng.choice(4000, 30, replace=False)]))
-    gsel = np.unique(np.concatenate([[4000, 4999], 4000 + rng.choice(1000, 6, replace=False)]))
+    fsel = np.unique(np.concatenate([[0, 3999], rng.choice(4000, 400, replace=False)]))
+    gsel = np.unique(np.concatenate([[4000, 4999], 4000 + rng.choice(1000, 100, replace=False)]))
     ff = got[: 4000 * 2401].reshape(4000, 2401)
     gg = got[4000 * 2401:].reshape(1000, 6561)
     assert_parity(ff[fsel], oracle_flat(w.shells, imap[fsel], True), "ffff sampled", w.shells, imap[fsel, :4], True)
@@ -530,3 +569,64 @@ def test_c3_full_size_JK(eri):
     bf = oracle.basis_offsets(sh, True)
     for (i, k), Kb in zip(pairs, oracle.K_blocks(sh, True, pairs, w.density, S_gpu, w.tau)):
         assert_parity(Kg[bf[i]:bf[i + 1], bf[k]:bf[k + 1]], Kb, f"K block ({i},{k})")
+
+
+def test_c3_full_J_against_oracle_fixture(eri):
+    """The full J of the 30-atom SVP-like cluster (10.2 M screened quartets)
+    against the oracle's full J element by element; the oracle's J is stored in
+    tests/golden/c3_J_spherical.npz by tests/golden/make_c3_J.py, which calls
+    only the oracle (its own Schwarz factors, screened plan, four-index
+    integrals and unique-quartet digestion).  The workspace of the plan and of
+    the digestion are torch tensors the binding allocates from the library's
+    size queries."""
+    import os
+    import torch
+    _log("case: C3 full 30-atom cluster, full J against the oracle's full J")
+    fx = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "c3_J_spherical.npz"))
+    w = make_config(3)
+    plan = eri.build_quartets(w.shells, eri.ERI_SPHERICAL, None, w.tau)
+    assert plan.workspace.numel() > 0
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.empty_like(D)
+    eri.digest_J(plan, D, J)
+    torch.cuda.synchronize()
+    _log(f"  {plan.n_quartets} quartets (oracle plan: {int(fx['n_quartets'])})")
+    assert abs(plan.n_quartets - int(fx["n_quartets"])) <= 10
+    S = plan.schwarz().cpu().numpy()
+    assert_J_parity(J.cpu().numpy(), fx["J"], w.shells, True, w.density, S, w.tau, "C3 full J vs oracle")
+
+
+def test_c5_shape_cluster_J(eri):
+    """J of an 8-atom cluster with the 120-atom cluster's per-atom shells (5s 4p
+    3d 1f, K 1-8, exponents [0.05, 1e4], atoms in the same 35-bohr cube,
+    tau = 1e-12, spherical) through eri_digest_J; 16 seeded bra shell
+    pairs' J blocks (both orientations) against the oracle's plain sum over
+    every surviving ket pair; sampled Schwarz factors against the oracle's."""
+    import torch
+    _log("case: C5-shape 8-atom cluster, J blocks of 16 seeded bra pairs")
+    w = make_config(5, scale={"natoms": 8})
+    sh = w.shells
+    plan = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
+    S = plan.schwarz().cpu().numpy()
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.empty_like(D)
+    eri.digest_J(plan, D, J)
+    torch.cuda.synchronize()
+    _log(f"  {plan.n_quartets} quartets in {plan.n_blocks} class blocks")
+    rng = np.random.default_rng(55)
+    pairs = [(i, j) for i in range(sh.nshell) for j in range(i + 1)]
+    bras = [pairs[x] for x in rng.choice(len(pairs), 16, replace=False)]
+    nprim = np.asarray(sh.nprim)
+    cheap = [p for p in pairs if nprim[p[0]] * nprim[p[1]] <= 16]
+    sp = [cheap[x] for x in rng.choice(len(cheap), 24, replace=False)]
+    flat, off = oracle.eri(sh, [(i, j, i, j) for i, j in sp], True)
+    ends = np.append(np.asarray(off), len(flat))
+    Sref = np.array([np.abs(np.diag(flat[ends[x]:ends[x + 1]].reshape(
+        int(round(np.sqrt(ends[x + 1] - ends[x]))), -1))).max() for x in range(len(sp))])
+    assert_parity(S[[i * (i + 1) // 2 + j for i, j in sp]], Sref, "C5-shape sampled Schwarz factors")
+    Jg = J.cpu().numpy()
+    bf = oracle.basis_offsets(sh, True)
+    refs = oracle.J_blocks(sh, True, bras, w.density, S, w.tau)
+    for (i, j), Jb in zip(bras, refs):
+        assert_parity(Jg[bf[i]:bf[i + 1], bf[j]:bf[j + 1]], Jb, f"C5-shape J block ({i},{j})")
+        assert_parity(Jg[bf[j]:bf[j + 1], bf[i]:bf[i + 1]], Jb.T, f"C5-shape J block ({j},{i})")

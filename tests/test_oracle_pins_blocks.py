@@ -145,3 +145,46 @@ def test_schwarz_factors(case):
                 assert abs(S[p] - ref) <= 1e-12 * ref, (name, i, j, S[p], ref)
                 n_ss += 1
     assert n_ss >= 10
+
+
+def test_J_floor_equals_sum_of_quartet_floors():
+    """oracle.hgp_rounding_bound_J (the per-integral two-phase floor propagated
+    into J blocks, in matrix form and batched over kets) equals the plain sum
+    over the kept ket pairs of f_kl sum_cd B[ab, cd] |D_cd| with B from
+    oracle.hgp_rounding_bound quartet by quartet in the library's orientation
+    (higher l first, higher index first for equal l), on the 3-atom cluster."""
+    sh = make_config(3, scale={"natoms": 3}).shells
+    sph = True
+    S = oracle.schwarz(sh, sph)
+    tau = 1e-6
+    n = sh.nbf(sph)
+    D = _density(n, 41)
+    bf = oracle.basis_offsets(sh, sph)
+    ns = sh.nshell
+    # three pairs of l >= 1 shells on different atoms with survivors, one pair on
+    # one atom, one s-s pair
+    far = sorted(((i, j) for i in range(ns) for j in range(i) if sh.l[i] >= 1 and sh.l[j] >= 1
+                  and np.any(sh.centers[i] != sh.centers[j])), key=lambda p: -S[p[0] * (p[0] + 1) // 2 + p[1]])
+    pairs = far[:3] + [(5, 3), (2, 2)]
+    got = oracle.hgp_rounding_bound_J(sh, sph, pairs, D, S, tau)
+
+    def orient(i, j):
+        i, j = max(i, j), min(i, j)
+        return (j, i) if sh.l[i] < sh.l[j] else (i, j)
+    for (i, j), F in zip(pairs, got):
+        a, b = orient(i, j)
+        pij = max(i, j) * (max(i, j) + 1) // 2 + min(i, j)
+        ref = np.zeros((oracle.nfunc(int(sh.l[a]), sph), oracle.nfunc(int(sh.l[b]), sph)))
+        for k in range(ns):
+            for l in range(k + 1):
+                if S[pij] * S[k * (k + 1) // 2 + l] < tau * tau:
+                    continue
+                c, d = orient(k, l)
+                B = oracle.hgp_rounding_bound(sh, [[a, b, c, d]], sph)
+                nc, nd = oracle.nfunc(int(sh.l[c]), sph), oracle.nfunc(int(sh.l[d]), sph)
+                B = B.reshape(ref.shape[0], ref.shape[1], nc, nd)
+                ref += (2.0 if c != d else 1.0) * np.einsum("abcd,cd->ab", B, np.abs(D[bf[c]:bf[c + 1], bf[d]:bf[d + 1]]))
+        if a != i:
+            ref = ref.T
+        np.testing.assert_allclose(F, ref, rtol=1e-12, atol=1e-300)
+        assert F.max() > 0

@@ -1233,10 +1233,33 @@ void digest_layout(Arena &A, const eri_plan *P, bool wantJ, bool wantK, const Di
     *kacc = wantK ? L[0].A : nullptr;
 }
 
-void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, Arena &ws,
-                   hipStream_t s)
+// One stream lane, chunk buffers halved until the layout fits in `cap` bytes
+// (at least one quartet of the largest class block per chunk).  Returns false
+// if even that does not fit.
+bool digest_shape_capped(const eri_plan *P, bool wantJ, bool wantK, size_t cap, DigestShape &d)
 {
-    const DigestShape d = digest_shape(P, J != nullptr, K != nullptr);
+    d = digest_shape(P, wantJ, wantK);
+    d.lanes = 1;
+    int64_t blk_max = 1;
+    for (const EriBlock &B : P->blocks) blk_max = std::max<int64_t>(blk_max, (int64_t)B.na * B.nb * B.nc * B.nd);
+    for (;;) {
+        Arena count;
+        std::vector<ChunkLane> L;
+        double *kacc = nullptr;
+        digest_layout(count, P, wantJ, wantK, d, L, &kacc);
+        if (count.used <= cap) return true;
+        if (d.CO <= blk_max && d.CB <= 1024 && d.CQ <= 1) return false;
+        d.CO = std::max<int64_t>(blk_max, d.CO / 2);
+        d.CB = std::max<int64_t>(1024, d.CB / 2);
+        d.CQ = std::max<int64_t>(1, d.CQ / 2);
+        d.NE = (wantK ? 4 : 2) * d.CQ;
+    }
+}
+
+void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, Arena &ws,
+                   hipStream_t s, const DigestShape *shape = nullptr)
+{
+    const DigestShape d = shape ? *shape : digest_shape(P, J != nullptr, K != nullptr);
     std::vector<ChunkLane> L;
     double *kacc = nullptr;
     digest_layout(ws, P, J != nullptr, K != nullptr, d, L, &kacc);
@@ -2066,6 +2089,73 @@ extern "C" int eri_digest_JK(const eri_plan *P, const double *D, int32_t ldd, do
 {
     if (!J && !K) return ERI_E_INVALID;
     return digest_entry(P, D, ldd, J, ldj, K, ldk, J != nullptr, K != nullptr, workspace, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// J digestion that allocates nothing, for callers that cannot allocate
+// ---------------------------------------------------------------------------
+// Its chunk buffers live in `scratch`, a file-scope device array of
+// ERI_NOALLOC_SCRATCH_BYTES that every device holds until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is only
+// a stand-in): the device address of each device's copy is looked up once, with
+// that device current, and kept in g_scratch_dev.
+static __device__ __align__(256) unsigned char scratch[ERI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void *> g_scratch_dev;
+
+int scratch_on_current_device(void **ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_error = std::string("hipGetDevice: ") + hipGetErrorString(e);
+        return ERI_E_HIP;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if ((int)g_scratch_dev.size() <= dev) g_scratch_dev.resize(dev + 1, nullptr);
+    if (!g_scratch_dev[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+            return ERI_E_HIP;
+        }
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return ERI_OK;
+}
+
+}  // namespace
+
+extern "C" int eri_digest_J_noalloc(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj,
+                                    void *stream)
+{
+    if (!P || !D || !J || ldd < P->nbf || ldj < P->nbf) return ERI_E_INVALID;
+    if (!P->screened) return ERI_E_UNSUPPORTED;
+    try {
+        int dev = 0;
+        HIP_CHECK(hipGetDevice(&dev));
+        if (dev != P->device) return ERI_E_INVALID;
+        DigestShape d;
+        if (!digest_shape_capped(P, true, false, ERI_NOALLOC_SCRATCH_BYTES, d)) {
+            g_last_error = "the plan's largest class block needs more than ERI_NOALLOC_SCRATCH_BYTES";
+            return ERI_E_WORKSPACE;
+        }
+        void *ptr = nullptr;
+        const int rc = scratch_on_current_device(&ptr);
+        if (rc != ERI_OK) return rc;
+        Arena A(ptr, ERI_NOALLOC_SCRATCH_BYTES);
+        digest_JK_run(P, D, ldd, J, ldj, nullptr, 0, A, (hipStream_t)stream, &d);
+    } catch (const HipFail &f) {
+        return translate(f);
+    } catch (const WsShort &) {
+        return ERI_E_WORKSPACE;
+    }
+    return ERI_OK;
 }
 
 // ---------------------------------------------------------------------------

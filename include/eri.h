@@ -222,6 +222,22 @@ int eri_digest_JK(const eri_plan *plan, const double *D, int32_t ldd, double *J,
                   int32_t ldk, void *workspace, size_t *ws_bytes, void *stream);
 
 /*
+ * eri_digest_J without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it).  Same arguments, result and determinism as eri_digest_J,
+ * with one stream lane; its chunk buffers live in a file-scope device array of
+ * ERI_NOALLOC_SCRATCH_BYTES that each device holds until the process ends, so
+ * chunks are smaller (the sums are in another order than eri_digest_J's, equal
+ * to rounding).  Nothing of the array needs to start at zero.  Every call on a
+ * device shares that device's array: calls that overlap in time on one device
+ * race.  ERI_E_WORKSPACE if one quartet of the plan's largest class block does
+ * not fit the array; ERI_E_INVALID if the current device is not the plan's.
+ * Asynchronous.
+ */
+#define ERI_NOALLOC_SCRATCH_BYTES (((size_t)64) << 20)
+int eri_digest_J_noalloc(const eri_plan *plan, const double *D, int32_t ldd, double *J, int32_t ldj, void *stream);
+
+/*
  * First derivatives of the integrals of plan slots [first, first + count)
  * with respect to the 12 centre coordinates of each canonical quartet (the
  * shells a, b, c, d of the index map): Eq. (1) of section II-A differentiated

@@ -230,21 +230,47 @@ def j_build(E, w, steps, stream, spherical=True):
                           "(J and K in one pass) are HIP-event times"}
 
 
+def _deriv_flops(w, rows):
+    """Algorithmic FLOPs of the auxiliary integrals a derivative call evaluates:
+    per slot and centre the class with that shell raised and, for l >= 1,
+    lowered (Cartesian kernels), K4 primitive quartets each."""
+    import numpy as np
+    from electron_repulsion_integrals_amd.gen import graph as G
+    K = np.asarray(w.shells.nprim, dtype=np.int64)
+    L = np.asarray(w.shells.l)
+    cache, total = {}, 0
+    for r in rows:
+        k4 = int(K[r[0]] * K[r[1]] * K[r[2]] * K[r[3]])
+        for p in range(4):
+            for dl in (1, -1):
+                l4 = [int(L[r[t]]) for t in range(4)]
+                if l4[p] + dl < 0:
+                    continue
+                l4[p] += dl
+                key = (max(l4[0], l4[1]), min(l4[0], l4[1]), max(l4[2], l4[3]), min(l4[2], l4[3]))
+                if key[0] * (key[0] + 1) // 2 + key[1] < key[2] * (key[2] + 1) // 2 + key[3]:
+                    key = (key[2], key[3], key[0], key[1])
+                if key not in cache:
+                    cache[key] = G.dag_flops(G.ClassInfo(*key), False)
+                per_prim, once = cache[key]
+                total += k4 * per_prim + once
+    return total
+
+
 def deriv_sampled(E, plan, w, per_block=2000):
     """First-derivative integrals (eri_compute_deriv: 12 centre-coordinate blocks
     per quartet) of the first ``per_block`` quartets of every class block of a
     plan; wall time of each call (it builds the auxiliary raised/lowered-shell
-    plan, computes those integrals and combines them, then synchronises)."""
+    plan, computes those integrals and combines them, then synchronises), and
+    the algorithmic FLOPs of the auxiliary integrals over that wall time."""
     import torch
     from electron_repulsion_integrals_amd.gen import graph as G
-    res, tot_q, tot_s = {}, 0, 0.0
+    res, tot_q, tot_s, tot_f = {}, 0, 0.0, 0
     sph = bool(w.spherical)
     for b in range(plan.n_blocks):
         cid = int(plan.block_class[b])
         la, lb = G.pair_class_ls(_pcb(cid))
         lc, ld = G.pair_class_ls(_pck(cid))
-        if max(la, lb, lc, ld) > 3:
-            continue
         n = int(min(per_block, plan.block_count[b]))
         first = int(plan.block_start[b])
         nf = (lambda l: 2 * l + 1) if sph else (lambda l: (l + 1) * (l + 2) // 2)
@@ -256,11 +282,17 @@ def deriv_sampled(E, plan, w, per_block=2000):
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         name = "(" + "spdfg"[la] + "spdfg"[lb] + "|" + "spdfg"[lc] + "spdfg"[ld] + ")"
-        res[name] = {"quartets": n, "ms": dt * 1e3, "quartets_per_s": n / dt}
+        fl = _deriv_flops(w, plan.quartets(first, n).cpu().numpy())
+        res[name] = {"quartets": n, "ms": dt * 1e3, "quartets_per_s": n / dt,
+                     "aux_tflops": fl / dt / 1e12, "fp64_frac": fl / dt / 1e12 / FP64_VECTOR_PEAK_TFLOPS}
         tot_q += n
         tot_s += dt
+        tot_f += fl
     return {"quartets": tot_q, "seconds": tot_s, "quartets_per_s": tot_q / tot_s if tot_s else None,
-            "note": "wall time per call, including the auxiliary plan build; 12 derivative blocks per quartet",
+            "aux_tflops": tot_f / tot_s / 1e12 if tot_s else None,
+            "fp64_frac": tot_f / tot_s / 1e12 / FP64_VECTOR_PEAK_TFLOPS if tot_s else None,
+            "note": "wall time per call, including the auxiliary plan build and the host read-back of the "
+                    "slots; FLOPs are the auxiliary integrals' algorithmic count; 12 derivative blocks per quartet",
             "per_class": res}
 
 
@@ -330,6 +362,57 @@ def cpu_baseline(w, seconds=12.0):
         n = min(4 * n, 1 << 16)
     return {"value": done / t_used, "unit": "shell quartets/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} quartets of the default workload (cycling its {len(q)} quartets), {t_used:.1f} s"}
+
+
+def cpu_baselines_per_config(seconds=6.0):
+    """The oracle (OpenMP on the host cores) on the other configurations, per
+    class: the tiny molecule in full; the (ff|ff) and (gg|gg) batches and the
+    30-atom cluster's screened quartets on bounded seeded samples (about
+    ``seconds`` each), the cluster's full-J oracle time extrapolated from its
+    sample (an estimate, labelled as such)."""
+    import numpy as np
+    import oracle
+    from oracle import plan as oplan
+    from workloads import make_config
+    res = {"cores": oracle.num_threads()}
+
+    def timed(sh, q, sph):
+        t0 = time.perf_counter()
+        oracle.eri(sh, q, sph)
+        return time.perf_counter() - t0
+
+    w1 = make_config(1)
+    q1 = np.array([(i, j, k, l) for i in range(8) for j in range(i + 1) for k in range(8) for l in range(k + 1)
+                   if i * (i + 1) // 2 + j >= k * (k + 1) // 2 + l])
+    dt = timed(w1.shells, q1, False)
+    res["tiny_molecule_cartesian"] = {"quartets": len(q1), "seconds": dt, "quartets_per_s": len(q1) / dt}
+    w4 = make_config(4)
+    for name, sl in (("(ff|ff)", slice(0, 4000)), ("(gg|gg)", slice(4000, 5000))):
+        q = np.asarray(w4.quartets)[sl]
+        n, used = 16, 0.0
+        while True:
+            dt = timed(w4.shells, q[:n], True)
+            if dt > seconds / 4 or n >= len(q):
+                break
+            n = min(len(q), n * 4)
+        res[name + " K=2 spherical"] = {"quartets": n, "seconds": dt, "quartets_per_s": n / dt,
+                                        "sample": f"first {n} of {len(q)} quartets"}
+    w3 = make_config(3)
+    S = oracle.schwarz(w3.shells, True)
+    p3 = oplan.screened_plan(w3.shells.l, w3.shells.nprim, S, w3.tau)
+    q3 = p3["index_map"][:, :4]
+    rng = np.random.default_rng(3)
+    n = 4096
+    while True:
+        sel = q3[rng.choice(len(q3), n, replace=False)]
+        dt = timed(w3.shells, sel, True)
+        if dt > seconds / 2 or n * 4 > len(q3):
+            break
+        n *= 4
+    res["30-atom SVP-like cluster"] = {"quartets": n, "seconds": dt, "quartets_per_s": n / dt,
+                                       "sample": f"{n} seeded quartets of its {len(q3)} screened quartets",
+                                       "full_J_integrals_estimated_s": dt * len(q3) / n}
+    return res
 
 
 def main():
@@ -436,6 +519,8 @@ def main():
         res["c5_120atom_tzvp"] = c5_sampled(E, make_config(5), stream)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
+        if not a.no_extra:
+            res["cpu_baseline_per_config"] = cpu_baselines_per_config()
     print(json.dumps(res), flush=True)
 
 

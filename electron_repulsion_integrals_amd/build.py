@@ -85,9 +85,13 @@ def build(lmax: int = 4, jobs: int | None = None, use_cache: bool = True, verbos
     os.makedirs(os.path.dirname(lib), exist_ok=True)
     os.makedirs(GEN_DIR, exist_ok=True)
     _write_if_changed(os.path.join(GEN_DIR, "eri_sph_table.h"), sph_table_header())
+    from electron_repulsion_integrals_amd.gen.graph import derivative_classes
     prev = V.set_variant(v)
     try:
-        files, entries = generate(gen_dir, lmax=lmax, classes=classes)
+        # the product library also holds the raised-shell classes of the derivative
+        # integrals (Cartesian kernels only); ablation variants leave them out
+        files, entries = generate(gen_dir, lmax=lmax, classes=classes,
+                                  cartesian_only=derivative_classes(lmax) if product else ())
     finally:
         V.set_variant(prev)
     keep = {os.path.basename(f) for f in files}
@@ -127,7 +131,8 @@ def resource_report(lmax: int = 4, jobs: int | None = None):
     {source file: {kernel symbol: {remark: value}}}."""
     import re
     from electron_repulsion_integrals_amd.gen.emit import generate
-    files, entries = generate(GEN_DIR, lmax=lmax)
+    from electron_repulsion_integrals_amd.gen.graph import derivative_classes
+    files, entries = generate(GEN_DIR, lmax=lmax, cartesian_only=derivative_classes(lmax))
     jobs = jobs or min(16, os.cpu_count() or 4)
 
     def one(src):

@@ -43,6 +43,10 @@ struct HipFail {
         }                                                                                             \
     } while (0)
 
+// class ids of quartets whose shells reach l = ERI_MAX_L + 1 (the raised-shell
+// classes of the derivative integrals): 21 pair classes, 231 class ids
+constexpr int ERI_NCLASS = 231;
+
 inline int ncart(int l) { return (l + 1) * (l + 2) / 2; }
 inline int nsph(int l) { return 2 * l + 1; }
 inline int nfun(int l, bool sph) { return sph ? nsph(l) : ncart(l); }
@@ -1413,14 +1417,14 @@ void host_explicit(const eri_shells *sh, int flags, const int32_t *quartets, int
     host_common(sh, (flags & ERI_SPHERICAL) != 0, H);
     H.nq = nq;
     H.np = 2 * nq;
-    bool present[120] = {};
+    bool present[ERI_NCLASS] = {};
     for (int64_t x = 0; x < nq; ++x) {
         const int *q = quartets + 4 * x;
         H.nppd += (int64_t)sh->nprim[q[0]] * sh->nprim[q[1]] + (int64_t)sh->nprim[q[2]] * sh->nprim[q[3]];
         present[class_of(sh->l[q[0]], sh->l[q[1]], sh->l[q[2]], sh->l[q[3]])] = true;
     }
     std::vector<int> cids;
-    for (int c = 0; c < 120; ++c)
+    for (int c = 0; c < ERI_NCLASS; ++c)
         if (present[c]) cids.push_back(c);
     H.scratch = scratch_need(cids, kernel_sph_flags((flags & ERI_SPHERICAL) != 0));
     H.cub = std::max(sort_pairs_u64<int64_t>(nullptr, nullptr, nullptr, nullptr, nq, nullptr, 0, nullptr),
@@ -1503,8 +1507,8 @@ void plan_layout(Arena &A, eri_plan *P, const BuildHost &H, BuildBufs &X)
         P->d_qmap = A.take<int>((size_t)5 * nq);
         P->d_qbra = A.take<int>(nq);
         P->d_qket = A.take<int>(nq);
-        X.st = A.take<int64_t>(121);
-        X.k1e = A.take<int64_t>(121);
+        X.st = A.take<int64_t>(ERI_NCLASS + 1);
+        X.k1e = A.take<int64_t>(ERI_NCLASS + 1);
     } else {
         const int64_t np = H.np;
         X.pck = A.take<uint64_t>(np);
@@ -1567,8 +1571,8 @@ void build_explicit(eri_plan *P, const BuildHost &H, BuildBufs &X, const int32_t
     hipLaunchKernelGGL(k_explicit_fill, dim3(nblk(nq, 256)), dim3(256), 0, s, nq, P->d_qsrc, X.q, P->d_l, P->d_nprim,
                        P->d_qmap, P->d_qbra, P->d_qket, P->d_pinfo);
     HIP_CHECK(hipGetLastError());
-    const int NC = 120;
-    hipLaunchKernelGGL(k_class_starts, dim3(1), dim3(128), 0, s, nq, X.k1, X.st, X.k1e, NC);
+    const int NC = ERI_NCLASS;
+    hipLaunchKernelGGL(k_class_starts, dim3(nblk(NC + 1, 128)), dim3(128), 0, s, nq, X.k1, X.st, X.k1e, NC);
     HIP_CHECK(hipGetLastError());
     std::vector<int64_t> st(NC + 1), k1e(NC + 1);
     HIP_CHECK(hipMemcpyAsync(st.data(), X.st, sizeof(int64_t) * (NC + 1), hipMemcpyDeviceToHost, s));
@@ -2180,9 +2184,20 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
     fetch_rows(P, first, count, H.rows, s);
     const int ns = P->nshell;
     const std::vector<int> &hl = P->hl, &hk = P->hk, &hoff = P->hoff;
-    for (int64_t t = 0; t < count; ++t)
-        for (int k = 0; k < 4; ++k)
-            if (hl[H.rows[5 * t + k]] + 1 > ERI_MAX_L) return ERI_E_UNSUPPORTED;
+    // every auxiliary class (one shell raised or lowered) must be in the library
+    bool checked[ERI_NCLASS] = {};
+    for (int64_t t = 0; t < count; ++t) {
+        const int *r = &H.rows[5 * t];
+        for (int p = 0; p < 4; ++p)
+            for (int dl = -1; dl <= 1; dl += 2) {
+                int l4[4] = {hl[r[0]], hl[r[1]], hl[r[2]], hl[r[3]]};
+                l4[p] = std::max(l4[p] + dl, 0);
+                const int cid = class_of(l4[0], l4[1], l4[2], l4[3]);
+                if (checked[cid]) continue;
+                if (!find_class(cid, false)) return ERI_E_UNSUPPORTED;
+                checked[cid] = true;
+            }
+    }
     const bool sph = P->sph;
     H.dst_off.resize(count);
     H.cart_off.resize(count);
@@ -2246,7 +2261,7 @@ void deriv_layout(Arena &A, const eri_plan *P, int64_t count, const DerivHost &H
     X.rows = A.take<int>(5 * (size_t)count);
     X.aux = A.take<double>(H.aux_nout);
     X.slot_of = A.take<int64_t>(8 * (size_t)count);
-    X.bt = A.take<int64_t>(3 * 120);
+    X.bt = A.take<int64_t>(3 * ERI_NCLASS);
     X.aux_off = A.take<int64_t>(8 * (size_t)count);
     X.off = A.take<int64_t>(2 * (size_t)count);
     if (P->sph) {

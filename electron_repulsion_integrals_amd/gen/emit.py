@@ -1013,15 +1013,18 @@ def tier_of(ci: ClassInfo, spherical: bool = True) -> str:
     return "V" if ci.G <= 64 else "M"
 
 
-def generate(out_dir: str, lmax: int = 4, classes=None):
-    """Write one .hip per (class, output kind) plus the dispatch table."""
+def generate(out_dir: str, lmax: int = 4, classes=None, cartesian_only=()):
+    """Write one .hip per (class, output kind) plus the dispatch table; the
+    classes in ``cartesian_only`` (the raised-shell classes of the derivative
+    integrals, which run on raw Cartesian monomials) get the Cartesian kind only."""
     from .graph import all_classes
     os.makedirs(out_dir, exist_ok=True)
-    cls = classes if classes is not None else all_classes(lmax)
+    cls = list(classes if classes is not None else all_classes(lmax))
+    cart_only = list(cartesian_only)
     entries = []
     files = []
-    for ci in cls:
-        for spherical in (False, True):
+    for ci in cls + cart_only:
+        for spherical in ((False,) if ci in cart_only else (False, True)):
             tier = tier_of(ci, spherical)
             if tier == "V":
                 src = emit_register_tier(ci, spherical)

@@ -234,6 +234,20 @@ def all_classes(lmax: int = 4):
     return out
 
 
+def derivative_classes(lmax: int = 4):
+    """Classes with one shell raised to l = lmax + 1 and the others at most lmax:
+    the neighbouring classes a first derivative with respect to a centre needs
+    (d/dA_i phi_a = 2 alpha phi_(a+1_i) - a_i phi_(a-1_i)) when the differentiated
+    shell has l = lmax.  Canonical form: bra (lmax+1, lb), lb <= lmax, any ket
+    pair of shells up to lmax."""
+    out = []
+    for lb in range(lmax + 1):
+        for pk in range((lmax + 1) * (lmax + 2) // 2):
+            lc, ld = pair_class_ls(pk)
+            out.append(ClassInfo(lmax + 1, lb, lc, ld))
+    return out
+
+
 def flop_count(ci: ClassInfo, spherical: bool, K4: int = 1):
     """Algorithmic FP64 operations (one FMA = 2) of the generated algorithm per quartet.
 

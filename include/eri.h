@@ -254,8 +254,10 @@ int eri_digest_J_noalloc(const eri_plan *plan, const double *D, int32_t ldd, dou
  *     after another, so slot s starts at 12 x (sum of the block sizes of the
  *     slots before it in the range).
  *   out_capacity: doubles available at out (ERI_E_CAPACITY if too few).
- *   count <= 2^24; every shell of the range must have l <= ERI_MAX_L - 1
- *     (ERI_E_UNSUPPORTED otherwise).
+ *   count <= 2^24.  Shells up to l = ERI_MAX_L: the library holds the
+ *     classes with one shell raised to l = ERI_MAX_L + 1 (Cartesian kernels);
+ *     a build without one of the auxiliary classes a range needs (the
+ *     ablation variants) returns ERI_E_UNSUPPORTED.
  *   workspace == NULL: *ws_bytes <- bytes needed (out may be NULL then).
  * Both the query and the call read the range's shells back to the host and
  * synchronise `stream`.

@@ -64,8 +64,11 @@ typedef double real;
 #ifndef ORACLE_MUTANT
 #define ORACLE_MUTANT 0 /* >0 only in test builds that plant a known mistake */
 #endif
-#define OR_LMAX 8 /* largest shell l the oracle accepts (4 + headroom for FD tests) */
-#define OR_MMAX 40
+#define OR_LMAX 10 /* largest shell l the oracle accepts (4, plus headroom for the finite-difference
+                      pins and the intermediates (e_A s_B| of the two-phase floor, |e| <= 9) */
+#define OR_MMAX (4 * (OR_LMAX + 1))
+#define OR_NCART ((OR_LMAX + 2) * (OR_LMAX + 3) / 2)                  /* components of l <= OR_LMAX + 1 */
+#define OR_NTRIP ((OR_LMAX + 2) * (OR_LMAX + 3) * (OR_LMAX + 4) / 6)  /* triples of total <= OR_LMAX + 1 */
 
 enum { OR_SPHERICAL = 1, OR_NO_NORMALIZE = 2 };
 
@@ -136,7 +139,7 @@ static void cart_list(int l, int (*c)[3])
 /* All exponent triples with total <= L, ordered by total then the order above. */
 typedef struct {
     int n;
-    int t[200][3];
+    int t[OR_NTRIP][3];
     int idx[OR_LMAX + 2][OR_LMAX + 2][OR_LMAX + 2];
 } tripset;
 
@@ -147,7 +150,7 @@ static void tripset_init(tripset *s, int L)
         for (int j = 0; j < OR_LMAX + 2; ++j)
             for (int k = 0; k < OR_LMAX + 2; ++k) s->idx[i][j][k] = -1;
     for (int tot = 0; tot <= L; ++tot) {
-        int c[64][3];
+        int c[OR_NCART][3];
         cart_list(tot, c);
         for (int q = 0; q < ncart(tot); ++q) {
             s->t[s->n][0] = c[q][0];
@@ -229,7 +232,7 @@ static real cart_overlap(const int *p, const int *q, int l)
 static void sph_coeffs_r(int l, real *T)
 {
     int nc = ncart(l);
-    int c[64][3];
+    int c[OR_NCART][3];
     cart_list(l, c);
     for (int mi = 0; mi < nsph(l); ++mi) {
         int m = mi - l, am = abs(m);
@@ -259,7 +262,7 @@ static void sph_coeffs_r(int l, real *T)
 
 void oracle_sph_coeffs(int l, double *T)
 {
-    real Tr[17 * 45];
+    real Tr[(2 * OR_LMAX + 1) * OR_NCART];
     if (l < 0 || l > OR_LMAX) return;
     sph_coeffs_r(l, Tr);
     for (int q = 0; q < nsph(l) * ncart(l); ++q) T[q] = (double)Tr[q];
@@ -322,7 +325,7 @@ static void os_quartet(os_work *w, const int l4[4], const double *cen[4], int K4
         w->cap = need;
     }
     real *V = w->V;
-    int ca[64][3], cb[64][3], ccc[64][3], cd[64][3];
+    int ca[OR_NCART][3], cb[OR_NCART][3], ccc[OR_NCART][3], cd[OR_NCART][3];
     cart_list(la, ca);
     cart_list(lb, cb);
     cart_list(lc, ccc);
@@ -501,7 +504,7 @@ int oracle_eri_quartets(int nshell, const double *centers, const int32_t *l, con
         else
             normalize_r(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
     }
-    real Tsph[OR_LMAX + 1][17 * 45];
+    real Tsph[OR_LMAX + 1][(2 * OR_LMAX + 1) * OR_NCART];
     for (int L = 0; L <= OR_LMAX; ++L) sph_coeffs_r(L, Tsph[L]);
     int bad = 0;
 #pragma omp parallel
@@ -580,7 +583,7 @@ int oracle_eri_deriv_quartets(int nshell, const double *centers, const int32_t *
         else
             normalize_r(l[s], nprim[s], exps + prim_off[s], coefs + prim_off[s], cn + prim_off[s]);
     }
-    real Tsph[OR_LMAX + 1][17 * 45];
+    real Tsph[OR_LMAX + 1][(2 * OR_LMAX + 1) * OR_NCART];
     for (int L = 0; L <= OR_LMAX; ++L) sph_coeffs_r(L, Tsph[L]);
     int bad = 0;
 #pragma omp parallel

@@ -166,6 +166,30 @@ def _mixed(seed, nshell, nq, lmax, kmax):
     return sh, q
 
 
+def _mixed_g(seed, nshell, nq, kmax, cap=8e6):
+    """Random shells up to l = 4 (a quarter of them g) and nq quartets that each
+    hold at least one g shell, limited to quartets whose oracle derivative table
+    (every index one higher) stays below ``cap`` doubles."""
+    def tri(l):
+        return (l + 1) * (l + 2) * (l + 3) // 6
+    rng = np.random.default_rng(seed)
+    cen = rng.uniform(0, 5, (nshell, 3))
+    ls = rng.integers(0, 5, nshell)
+    ls[: nshell // 4] = 4
+    ks = rng.integers(1, kmax + 1, nshell)
+    ex = [np.exp(rng.uniform(np.log(0.15), np.log(20.0), k)) for k in ks]
+    co = [rng.uniform(0.1, 1.0, k) for k in ks]
+    sh = _pack(cen, ls, ks, ex, co)
+    out = []
+    while len(out) < nq:
+        q = rng.integers(0, nshell, 4)
+        l4 = ls[q]
+        if 4 not in l4 or np.prod([tri(int(l) + 1) for l in l4]) * (int(l4.sum()) + 5) > cap:
+            continue
+        out.append(q)
+    return sh, np.array(out, dtype=np.int32)
+
+
 def test_deriv_tiny_molecule_cartesian(eri):
     """All 666 unique quartets of the s/p tiny molecule, every derivative block."""
     _log("case: derivatives, tiny molecule, Cartesian")
@@ -184,6 +208,19 @@ def test_deriv_mixed_classes_l3(eri, spherical):
     plan, got, rows = run_deriv(eri, sh, 1 if spherical else 0, q)
     ref, _ = oracle.eri_deriv(sh, rows, spherical)
     assert_deriv_parity(got, ref, deriv_bar(sh, rows, spherical), f"mixed l<=3 derivatives sph={spherical}")
+
+
+@pytest.mark.parametrize("spherical", [False, True])
+def test_deriv_g_shells(eri, spherical):
+    """Quartets with g shells (K <= 2): the raised shell reaches l = 5, which the
+    library's raised-shell classes (Cartesian kernels) compute; against the
+    oracle's derivatives (its four-index table one higher on every index)."""
+    _log(f"case: derivatives with g shells, spherical={spherical}")
+    sh, q = _mixed_g(43, 16, 60, 2)
+    plan, got, rows = run_deriv(eri, sh, 1 if spherical else 0, q)
+    assert max(int(sh.l[s]) for s in rows.ravel()) == 4
+    ref, _ = oracle.eri_deriv(sh, rows, spherical)
+    assert_deriv_parity(got, ref, deriv_bar(sh, rows, spherical), f"g-shell derivatives sph={spherical}")
 
 
 def test_deriv_slot_range_and_translational_invariance(eri):
@@ -225,8 +262,8 @@ def test_deriv_cluster_subset(eri):
 
 
 def test_deriv_errors(eri):
-    """l = 4 shells are rejected (the raised shell would exceed the library's
-    l <= 4), as are short output buffers; nothing is written then."""
+    """Short output buffers and more than 2^24 slots are rejected; nothing is
+    written then."""
     import torch
     from electron_repulsion_integrals_amd import EriError
     sh, q = _mixed(41, 6, 10, 1, 1)
@@ -235,12 +272,7 @@ def test_deriv_errors(eri):
     with pytest.raises(EriError) as e:
         eri.compute_deriv(plan, small)
     assert e.value.code == -3
-    cen = np.zeros((2, 3))
-    cen[1, 2] = 1.0
-    sh4 = _pack(cen, [4, 0], [1, 1], [np.array([1.0]), np.array([0.5])], [np.array([1.0]), np.array([1.0])])
-    plan4 = eri.build_quartets(sh4, 0, np.array([[0, 1, 1, 1]], dtype=np.int32), 0.0)
-    big = torch.zeros(12 * 15, dtype=torch.float64, device="cuda")
+    assert float(small.abs().sum()) == 0.0
     with pytest.raises(EriError) as e:
-        eri.compute_deriv(plan4, big)
-    assert e.value.code == -2
-    assert float(big.abs().sum()) == 0.0
+        eri.compute_deriv(plan, small, 0, (1 << 24) + 1)
+    assert e.value.code == -1

@@ -201,7 +201,7 @@ def _shifted(sh, pos, axis, h):
 
 @pytest.mark.parametrize("ls,spherical", [((0, 0, 0, 0), False), ((1, 0, 0, 0), False), ((1, 1, 1, 0), False),
                                           ((2, 1, 0, 1), True), ((2, 2, 1, 1), False), ((3, 1, 2, 0), True),
-                                          ((3, 3, 2, 2), False)])
+                                          ((3, 3, 2, 2), False), ((4, 1, 2, 0), True), ((4, 4, 1, 0), False)])
 def test_derivative_finite_differences(ls, spherical):
     """Each of the 12 derivative blocks against a fourth-order central
     difference of the integrals, moving one centre along one axis (contracted,

@@ -185,7 +185,12 @@ def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None, compact=
             lines.append(f"{ind}  const double gn = (double)(ax == 0 ? {s - 1} : ax == 1 ? {s - 1} - ex : "
                          f"ax == 2 ? {s - 1} - ex - ey : 0) * i2z;")
         for m in range(top + 1):
-            lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1} + gn * (p{m} - roz * p{m + 1});")
+            if s == 1:  # nothing to lower yet: the p terms are zero
+                lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1};")
+            else:
+                lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1} + gn * (p{m} - roz * p{m + 1});")
+        if s == 1:
+            lines.append(f"{ind}  (void)gn;")
         for m in range(top + 1):
             lines.append(f"{ind}  p{m} = c{m}; c{m} = n{m};")
         lines.append(f"{ind}}}")
@@ -708,13 +713,17 @@ def _emit_scheduled(ops, initial, names, lines, ind, ahead=None):
 
 
 
-def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, prefix, outputs=None):
+def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, prefix, outputs=None,
+                        preload=False):
     """HRR + transform of one column, emitted in liveness order.
 
     base_load(e) -> C expression reading base value (e, 0) (issued where first
     needed); store(k, expr) -> statement consuming output k.  ``outputs``, if
     given, restricts the column to those output indices and the values they
-    depend on.
+    depend on.  ``preload`` issues every base read first and waits for them
+    once (empty asm statements that take the values as operands), instead of
+    letting the compiler place each read just before its first use, which
+    exposes the LDS latency at every read.
     """
     from .graph import schedule_min_live
     ops, base, outs = _hrr_ops(l1, l2, R, spherical)
@@ -748,6 +757,16 @@ def _emit_hrr_scheduled(l1, l2, base_load, R, spherical, store, lines, ind, pref
         k = ("w", i)
         items.append((k, [ok], True))
         code[k] = (lambda i=i, ok=ok: store(i, nm(ok)))
+    if preload:
+        bn = [names_[("b", e)] for e in base]
+        for e, x in zip(base, bn):
+            lines.append(f"{ind}double {x} = {base_load(e)};")
+        lines.append(f"{ind}{{  // every base value in registers before the recurrence starts")
+        for i in range(0, len(bn), 8):
+            ops_ = ", ".join(f'"+v"({x})' for x in bn[i:i + 8])
+            lines.append(f'{ind}  asm volatile("" : {ops_});')
+        lines.append(f"{ind}}}")
+        items = [it for it in items if it[0][0] != "b"]
     for (k, ds, sink) in schedule_min_live(items, ()):
         lines.append(f"{ind}{code[k]()}")
 

@@ -27,6 +27,8 @@ finish with the bra HRR and transform.
 """
 from __future__ import annotations
 
+import functools
+
 from .cartesian import components, sub
 from .graph import ClassInfo, build_ket_vrr, class_id
 
@@ -69,12 +71,35 @@ def packed_k1_waves(ci: ClassInfo) -> int:
     return _wide_waves(ci) if ci.G > 64 else PACK_WAVES
 
 
-def packed_k1_min_waves(ci: ClassInfo) -> int:
+# K4 = 1 kernels built for three waves per SIMD instead of two.  Their
+# bra-path selectors are packed one int per step and a record batch covers
+# four groups, which keeps (dd|dd) at 164 VGPRs with no scratch and six
+# two-wave workgroups within a compute unit's LDS.  Measured on the (dd|dd)
+# batch: 5% faster than two waves per SIMD.
+K1_THREE_WAVES = {(2, 2, 2, 2, True)}  # (la, lb, lc, ld, spherical)
+K1_THREE_WAVES_RB = 4
+
+
+def _k1_three(ci: ClassInfo, spherical: bool) -> bool:
+    return (ci.la, ci.lb, ci.lc, ci.ld, spherical) in K1_THREE_WAVES and ci.G <= 64
+
+
+def _k1_waves_per_simd(ci: ClassInfo, spherical: bool) -> int:
+    return 3 if _k1_three(ci, spherical) else 2
+
+
+def _k1_rb(ci: ClassInfo, spherical: bool) -> int:
+    return K1_THREE_WAVES_RB if _k1_three(ci, spherical) else PACK_RB
+
+
+def packed_k1_min_waves(ci: ClassInfo, spherical: bool = True) -> int:
     """Occupancy bound of the K4 = 1 kernel (0: the compiler's choice).  84-lane
     bras with kets up to l = 4 otherwise take 56-62 AGPRs beyond 256 VGPRs and
     run at one wave per SIMD; capped at two they measured 1.15-1.39x faster for
     (ff|ps) .. (ff|fp) on K = 1 batches and even for (gd| apart from (gd|fp)
     (1.22x).  The cap made the 120-lane kernels slower."""
+    if _k1_three(ci, spherical):
+        return 3
     return 2 if wide_packed(ci) and ci.G == 84 and ci.Lk <= 4 else 0
 
 
@@ -94,14 +119,56 @@ def _levels(kv):
     return lv
 
 
-def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB) -> int:
+# The exchange rows of the bra HRR lie apart from the last ket level's buffer,
+# so the exchange can be written right after that level's reads without a
+# second barrier; the levels before alternate between the start of the buffer
+# and the offset past the exchange.  Kept only where the larger buffer leaves
+# as many workgroups per compute unit.
+XD_APART = True
+
+
+def _level_buffers(ci: ClassInfo, spherical: bool, waves: int, apart: bool):
+    """(offset of each ket level's buffer in doubles, doubles of the whole
+    buffer).  Level k's buffer may not overlap level k-1's (a lane can publish
+    level k while another still reads level k-1); with ``apart`` the exchange
+    rows (written after the last level's reads) do not overlap the last
+    level's buffer."""
     kv = build_ket_vrr(ci.lc, ci.Lk)
     W, Q, NT = packed_shape(ci, spherical, waves)
     lv = _levels(kv)
+    levels = sorted(lv)
     NC = max((len(v) for v in lv.values()), default=0)
     NX = Q * ci.n_ebra * ci.nket(spherical) + ci.nket(spherical)
+    if not apart:
+        # levels of even index at the start, odd ones after the widest even one
+        ne = max((len(lv[k]) for li, k in enumerate(levels) if li % 2 == 0), default=0)
+        no = max((len(lv[k]) for li, k in enumerate(levels) if li % 2 == 1), default=0)
+        return [(li % 2) * ne * NT for li in range(len(levels))], max((ne + no) * NT, NX)
+    far = max(NX, NC * NT)
+    nl = len(levels)
+    offs = [far if (nl - 1 - li) % 2 == 0 else 0 for li in range(nl)]
+    size = max([NX] + [offs[li] + len(lv[k]) * NT for li, k in enumerate(levels)])
+    return offs, size
+
+
+def _lds_bytes(ci, spherical, waves, rb, apart):
+    W, Q, NT = packed_shape(ci, spherical, waves)
     NR = 17 + ci.L + 1 + 6 + 2
-    return 8 * (max(2 * NC * NT, NX) + NR * ((rb * Q) | 1))
+    return 8 * (_level_buffers(ci, spherical, waves, apart)[1] + NR * ((rb * Q) | 1))
+
+
+def xd_apart(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = 0) -> bool:
+    if not XD_APART:
+        return False
+    rb = rb or _k1_rb(ci, spherical)
+    cap = 4 * _k1_waves_per_simd(ci, spherical) // waves
+    return min(cap, LDS_BYTES // _lds_bytes(ci, spherical, waves, rb, True)) >= \
+        min(cap, LDS_BYTES // _lds_bytes(ci, spherical, waves, rb, False))
+
+
+def packed_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = 0) -> int:
+    rb = rb or _k1_rb(ci, spherical)
+    return _lds_bytes(ci, spherical, waves, rb, xd_apart(ci, spherical, waves, rb))
 
 
 def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
@@ -118,10 +185,11 @@ def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
     return packed_wg_per_cu(ci, spherical) >= 2
 
 
-def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = PACK_RB) -> int:
-    """Workgroups per compute unit: LDS-bound, at most two waves per SIMD."""
+def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = 0) -> int:
+    """Workgroups per compute unit: LDS-bound, at most two waves per SIMD
+    (three for the kernels built for three)."""
     by_lds = LDS_BYTES // packed_lds_bytes(ci, spherical, waves, rb)
-    return int(min(by_lds, 8 // waves))
+    return int(min(by_lds, 4 * _k1_waves_per_simd(ci, spherical) // waves))
 
 
 def _lane_table(ci: ClassInfo, tag: str):
@@ -164,7 +232,101 @@ def _lane_table(ci: ClassInfo, tag: str):
     return decl, dec
 
 
+# Level-buffer slots of the K4 = 1 kernels.  Lane t publishes its values at
+# slot pi(t) and reads its coupling operands at pi(source lane).  A lane whose
+# component along the read's axis is zero needs no operand (its factor e_i is
+# zero); it reads a slot that another lane of its 16-lane group reads anyway,
+# so the read adds no address.  pi is searched (fixed seed) so that the
+# distinct addresses of every 16- and 32-lane group of a read and of the
+# publishing write fall in distinct 8-byte banks modulo 16 and 32 -- the
+# conflict-free pattern whether the LDS serves 16 lanes over 32 banks or 32
+# lanes over 64 banks per cycle.  Measured on the (dd|dd) batch: 4% faster
+# than identity slots with reads of the lane itself.
+K1_SLOTS = True
+
+
+def _source_lanes(lanes, NT: int):
+    """Per axis, per lane t: the lane of e - 1_axis in t's quartet, or None where
+    e_axis = 0 (spare lanes beyond the last quartet shadow e = 0)."""
+    G = len(lanes)
+    Q = NT // G
+    lpos = {e: i for i, e in enumerate(lanes)}
+    out = []
+    for ax in range(3):
+        col = []
+        for t in range(NT):
+            qi, sb = divmod(t, G)
+            if qi >= Q:
+                qi, sb = 0, 0
+            e = lanes[sb]
+            col.append(qi * G + lpos[sub(e, ax)] if e[ax] > 0 else None)
+        out.append(col)
+    return out
+
+
+def slot_layout(ci: ClassInfo, NT: int):
+    """(pi, reads): pi[t] is lane t's slot, reads[ax][t] the slot lane t reads
+    along axis ax (see K1_SLOTS)."""
+    return _slot_layout(tuple(ci.lanes), NT)
+
+
+@functools.lru_cache(maxsize=None)
+def _slot_layout(lanes, NT: int, iters: int = 20000, seed: int = 1):
+    import random
+    import numpy as np
+    srcs = _source_lanes(lanes, NT)
+    red = []
+    for col in srcs:
+        r = list(col)
+        for t in range(NT):
+            if r[t] is None:
+                g0 = t - t % 16
+                cand = [col[u] for u in range(g0, g0 + 16) if col[u] is not None]
+                r[t] = min(cand, key=lambda v: abs(v - t)) if cand else g0
+        red.append(r)
+    # every access group: the distinct source lanes it touches, per bank modulus
+    groups = []
+    for width, mod in ((16, 16), (32, 32)):
+        for col in red + [list(range(NT))]:
+            for g0 in range(0, NT, width):
+                groups.append((sorted(set(col[g0:g0 + width])), mod))
+    ng = len(groups)
+    L = max(len(g) for g, _ in groups)
+    idx = np.full((ng, L), NT, dtype=np.int64)
+    mods = np.array([m for _, m in groups], dtype=np.int64)
+    for i, (g, _) in enumerate(groups):
+        idx[i, :len(g)] = g
+
+    def cost(pi):
+        piv = np.append(pi, -1)[idx]  # padding maps to -1: a bank of its own
+        b = np.where(piv < 0, 64, piv % mods[:, None])
+        cnt = np.zeros((ng, 65), dtype=np.int64)
+        np.add.at(cnt, (np.repeat(np.arange(ng), L), b.ravel()), 1)
+        cnt[:, 64] = 0
+        return int(cnt.max(axis=1).sum())
+    rng = random.Random(seed)
+    pi = np.arange(NT)
+    cur = cost(pi)
+    best_possible = ng
+    for _ in range(iters):
+        if cur == best_possible:
+            break
+        i, j = rng.randrange(NT), rng.randrange(NT)
+        pi[i], pi[j] = pi[j], pi[i]
+        c = cost(pi)
+        if c <= cur:
+            cur = c
+        else:
+            pi[i], pi[j] = pi[j], pi[i]
+    pi = [int(v) for v in pi]
+    return pi, [[pi[r] for r in col] for col in red]
+
+
 SPLIT_BRA_HRR = True
+# the bra HRR of the K4 = 1 kernels reads its whole exchange column up front
+BRA_PRELOAD = True
+# each ket level computes the lane's own terms before the barrier
+K1_OWN_TERMS_FIRST = True
 
 
 def bra_hrr_parts(ci: ClassInfo, spherical: bool, waves: int, Q: int, contracted: bool = False) -> int:
@@ -211,11 +373,12 @@ def _emit_bra_hrr_split(ci, spherical, o, ind, P, slot_expr, setup, src_of):
     o.append(f"{ind}}}")
 
 
-def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PACK_RB, wg_per_cu: int = 0,
+def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = 0, wg_per_cu: int = 0,
                    min_waves: int = 0):
     """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
     waves = waves or packed_k1_waves(ci)
-    min_waves = min_waves or packed_k1_min_waves(ci)
+    min_waves = min_waves or packed_k1_min_waves(ci, spherical)
+    rb = rb or _k1_rb(ci, spherical)
     from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
     kv = build_ket_vrr(ci.lc, ci.Lk)
     names = Names("V", kv, ci.Lk)
@@ -231,6 +394,17 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
     cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
     tag = f"c{cid}_{'s' if spherical else 'c'}_k1"
     lane_decl, lane_dec = _lane_table(ci, tag)
+    if K1_SLOTS:
+        pi, rd = slot_layout(ci, NT)
+        assert NT <= 256
+        tab = [pi[t] | (rd[0][t] << 8) | (rd[1][t] << 16) | (rd[2][t] << 24) for t in range(NT)]
+        lane_decl += (f"\n__constant__ unsigned k_{tag}_slot[{NT}] = {{" +
+                      ", ".join(f"{v}u" for v in tab) + "};")
+        lane_dec = [ln for ln in lane_dec if not ln.lstrip().startswith("const int src")]
+        lane_dec.append(f"  const unsigned slt = k_{tag}_slot[tid];")
+        lane_dec.append("  const int myslot = (int)(slt & 255u), srcx = (int)((slt >> 8) & 255u),"
+                        " srcy = (int)((slt >> 16) & 255u), srcz = (int)(slt >> 24);")
+    me = "myslot" if K1_SLOTS else "tid"
     lv = _levels(kv)
     levels = sorted(lv)
     NC = max((len(v) for v in lv.values()), default=0)
@@ -242,7 +416,9 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
     NRL = RB * Q
     assert NRL <= NT
     NX = Q * NEB * NK + NK  # exchange rows, then a junk row
-    NU = max(2 * NC * NT, NX)
+    apart = xd_apart(ci, spherical, waves, rb)
+    bufs, NU = _level_buffers(ci, spherical, waves, apart)
+    assert NU >= NX
     o = []
     o.append("namespace {")
     o.append(lane_decl)
@@ -266,7 +442,8 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
     o.append("  (void)srcx; (void)srcy; (void)srcz; (void)es;")
     o.append("  const int ngroups = (a.nq + Q - 1) / Q;")
     o.append(f"  if (tid < NRL) {{ rec[{NR - 2} * RS + tid] = 1.0; rec[{NR - 1} * RS + tid] = 0.0; }}")
-    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1)
+    k1c = "all" if _k1_three(ci, spherical) else None
+    _stage1_selectors(ci, o, "RS", NR - 2, NR - 1, compact=k1c)
     o.append(f"  double* xd = xu + ((real && es >= {ci.la}) ? (qi * NEB + (sub - {EOFF})) * NK : Q * NEB * NK);")
     o.append("  int it = 0;")
     o.append("  for (int g = blockIdx.x; g < ngroups; g += (int)gridDim.x, ++it) {")
@@ -310,12 +487,22 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
     o.append("    const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
     o.append("    (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
     o.append("    (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-    _stage1(ci, kv.base_m, o, "    ", rsel="r")
+    _stage1(ci, kv.base_m, o, "    ", rsel="r", compact=k1c)
     for li, k in enumerate(levels):
-        buf = (li % 2) * NC * NT
+        buf = bufs[li]
         o.append(f"    // ket level {k}: publish level {k - 1} values read across lanes")
         for j, key in enumerate(lv[k]):
-            o.append(f"    xu[{buf + j * NT} + tid] = {names.ket(key)};")
+            o.append(f"    xu[{buf + j * NT} + {me}] = {names.ket(key)};")
+        # the lane's own terms of every node first: they fill the wait for the
+        # other waves at the barrier; only the coupling term follows the reads
+        for n in kv.nodes:
+            if sum(n.f) != k or not K1_OWN_TERMS_FIRST:
+                continue
+            a_ = AX[n.axis]
+            expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+            if n.b0 is not None:
+                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            o.append(f"    const double {names.ket((n.f, n.m))}p = {expr};")
         o.append("    __syncthreads();")
         reads = {}
         for n in kv.nodes:
@@ -325,17 +512,19 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
             if rk not in reads:
                 reads[rk] = f"xr{k}_{len(reads)}"
                 o.append(f"    const double {reads[rk]} = xu[{buf + rk[0] * NT} + src{AX[n.axis]}];")
-        if li == len(levels) - 1:
+        if li == len(levels) - 1 and not apart:
             o.append("    __syncthreads();  // every level buffer read: the exchange may overwrite them")
         for n in kv.nodes:
             if sum(n.f) != k:
                 continue
             a_ = AX[n.axis]
-            expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
-            if n.b0 is not None:
-                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
-            expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
-            o.append(f"    const double {names.ket((n.f, n.m))} = {expr};")
+            own = f"{names.ket((n.f, n.m))}p"
+            if not K1_OWN_TERMS_FIRST:
+                own = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+                if n.b0 is not None:
+                    own += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            o.append(f"    const double {names.ket((n.f, n.m))} = {own}"
+                     f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]};")
     # ket HRR and transform per lane, straight into the exchange row of this lane's e
     _emit_hrr_scheduled(ci.lc, ci.ld, lambda f: names.ket((f, 0)), "CD", spherical,
                         lambda kk, x: f"xd[{kk}] = {x};", o, "    ", "y")
@@ -363,7 +552,8 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = PAC
         o.append("      const double* src = xu + q2 * NEB * NK + kap;")
         o.append("      double* dst = a.out + (size_t)slot * BLK + kap;")
         _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "      ", "z")
+                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "      ", "z",
+                            preload=BRA_PRELOAD)
         o.append("    }")
     o.append("    __syncthreads();  // exchange and records are rewritten next")
     o.append("  }")

@@ -171,17 +171,24 @@ def test_packed_k1_routing_and_shapes():
                 continue
             used.append((c.la, c.lb, c.lc, c.ld))
             W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
-            assert c.G in (35, 84, 120, 165) and Q * c.G <= NT and P.PACK_RB * Q <= NT
+            assert c.G in (35, 84, 120, 165) and Q * c.G <= NT and P._k1_rb(c, sph) * Q <= NT
             assert W == {84: 4, 165: 3}.get(c.G, 2)
-            assert 1 <= P.packed_wg_per_cu(c, sph, W) and \
-                P.packed_lds_bytes(c, sph, W) * P.packed_wg_per_cu(c, sph, W) <= P.LDS_BYTES
+            wg = P.packed_wg_per_cu(c, sph, W)
+            assert 1 <= wg and P.packed_lds_bytes(c, sph, W) * wg <= P.LDS_BYTES
+            # two waves per SIMD at most, three for the kernels built for three
+            assert wg * W <= 4 * (3 if (c.la, c.lb, c.lc, c.ld, sph) in P.K1_THREE_WAVES else 2)
             src = emit_register_tier(c, sph)
             if "lane tier" not in src.splitlines()[0]:
-                lb = f"{NT}, {P.packed_k1_min_waves(c)}" if P.packed_k1_min_waves(c) else f"{NT}"
+                mw = P.packed_k1_min_waves(c, sph)
+                lb = f"{NT}, {mw}" if mw else f"{NT}"
                 assert f"__launch_bounds__({lb}) eri_kernel_" in src and "_k1(" in src and "xu[" in src
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
     assert (4, 3, 4, 1) in used and (4, 3, 3, 3) not in used
     assert P.packed_k1_min_waves(gg.ClassInfo(3, 3, 2, 2)) == 2 and P.packed_k1_min_waves(gg.ClassInfo(4, 3, 1, 0)) == 0
+    # spherical (dd|dd): three waves per SIMD, six workgroups per compute unit
+    dd = gg.ClassInfo(2, 2, 2, 2)
+    assert P.packed_k1_min_waves(dd, True) == 3 and P.packed_wg_per_cu(dd, True, 2) == 6
+    assert P.packed_k1_min_waves(dd, False) == 0
     assert all(sum(u[:2]) in (4, 6, 7, 8) and sum(u[2:]) <= {4: 4, 6: 6, 7: 5, 8: 4}[sum(u[:2])] for u in used)
     assert (4, 4, 2, 2) in used and (4, 4, 3, 2) not in used
 

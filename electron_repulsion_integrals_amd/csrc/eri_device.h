@@ -116,14 +116,15 @@ __device__ __forceinline__ void eri_geom(const EriPrimPair& B, const EriPrimPair
 //     degree-7 polynomial, then the downward recursion
 //     F_m = (2 T F_{m+1} + exp(-T)) / (2m + 1).
 //   T >= ERI_BT_TMAX: F_0 = sqrt(pi / T) / 2 (erfc(6) < 3e-17) and the upward
-//     recursion F_{m+1} = ((2m+1) F_m - exp(-T)) / (2T).  There exp(-T) comes
-//     from the same table: T = 2^j t with t in [TMAX/2, TMAX), exp(-T) =
-//     exp(-t)^(2^j).  The j squarings scale its relative error by 2^j (j <= 5
-//     until exp(-T) underflows, near T = 745), while the share of exp(-T) in
-//     F_m falls from at most 1e-4 (m = 16, T = 36) to below 1e-15 at T = 72,
-//     so F_m keeps full precision.  Unlike a call of exp(), this needs no
-//     constants of its own, which a kernel would otherwise hold in registers
-//     across its whole loop.
+//     recursion F_{m+1} = ((2m+1) F_m - exp(-T)) / (2T).
+//   TAB_EXP: exp(-T) of the upward branch comes from the same table instead of
+//     exp(): T = 2^j t with t in [TMAX/2, TMAX), exp(-T) = exp(-t)^(2^j).  The
+//     j squarings scale its relative error by 2^j (j <= 5 until exp(-T)
+//     underflows, near T = 745), while the share of exp(-T) in F_m falls from
+//     at most 1e-4 (m = 16, T = 36) to below 1e-15 at T = 72, so F_m keeps
+//     full precision.  It takes a few more instructions than exp() but no
+//     constants of its own, which a kernel whose loop holds exp() keeps in
+//     registers across the whole loop.
 
 // exp(-t) for t in [0, ERI_BT_TMAX]: the table point exp(-T_k) times the
 // degree-7 Taylor polynomial of exp(-d), |d| <= 1/64 (remainder below 4e-19).
@@ -139,7 +140,7 @@ __device__ __forceinline__ double eri_exp_tab(const double* __restrict__ row, do
     return row[0] * ed;
 }
 
-template <int L>
+template <int L, bool TAB_EXP = false>
 __device__ __forceinline__ void eri_boys(double T, double pref, const double* __restrict__ tab, double* F)
 {
     if (T < (double)ERI_BT_TMAX) {
@@ -158,15 +159,20 @@ __device__ __forceinline__ void eri_boys(double T, double pref, const double* __
 #pragma unroll
         for (int m = L - 1; m >= 0; --m) F[m] = (2.0 * T * F[m + 1] + e) * (1.0 / (2 * m + 1));
     } else {
-        double t = T;
-        int j = 0;
-        while (t >= (double)ERI_BT_TMAX) {
-            t *= 0.5;
-            ++j;
+        double e;
+        if (TAB_EXP) {
+            double t = T;
+            int j = 0;
+            while (t >= (double)ERI_BT_TMAX) {
+                t *= 0.5;
+                ++j;
+            }
+            const int k = (int)(t * (double)ERI_BT_PER_UNIT + 0.5);
+            e = eri_exp_tab(tab + (size_t)k * ERI_BT_COLS, t - (double)k * (1.0 / ERI_BT_PER_UNIT));
+            for (int i = 0; i < j; ++i) e *= e;
+        } else {
+            e = exp(-T);
         }
-        const int k = (int)(t * (double)ERI_BT_PER_UNIT + 0.5);
-        double e = eri_exp_tab(tab + (size_t)k * ERI_BT_COLS, t - (double)k * (1.0 / ERI_BT_PER_UNIT));
-        for (int i = 0; i < j; ++i) e *= e;
         const double it = 1.0 / T;
         F[0] = 0.88622692545275801365 * sqrt(it);  // sqrt(pi)/2 / sqrt(T)
 #pragma unroll

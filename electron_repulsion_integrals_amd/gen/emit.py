@@ -151,6 +151,9 @@ def _stage1_selectors(ci: ClassInfo, lines, stride, one_field, zero_field, ind="
         lines.append(f"{ind}const double gnf{s} = (double){gnf};")
 
 
+STEP1_SHORTCUT = True
+
+
 def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None, compact=None):
     """Bra phase for the lane's own e: [e0|00]^(m), m = 0..base_m, from F_m.
     rsel: name of this lane's record pointer (factors read through the
@@ -185,11 +188,11 @@ def _stage1(ci: ClassInfo, base_m: int, lines, ind="      ", rsel=None, compact=
             lines.append(f"{ind}  const double gn = (double)(ax == 0 ? {s - 1} : ax == 1 ? {s - 1} - ex : "
                          f"ax == 2 ? {s - 1} - ex - ey : 0) * i2z;")
         for m in range(top + 1):
-            if s == 1:  # nothing to lower yet: the p terms are zero
+            if s == 1 and STEP1_SHORTCUT:  # nothing to lower yet: the p terms are zero
                 lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1};")
             else:
                 lines.append(f"{ind}  const double n{m} = g1 * c{m} + g2 * c{m + 1} + gn * (p{m} - roz * p{m + 1});")
-        if s == 1:
+        if s == 1 and STEP1_SHORTCUT:
             lines.append(f"{ind}  (void)gn;")
         for m in range(top + 1):
             lines.append(f"{ind}  p{m} = c{m}; c{m} = n{m};")

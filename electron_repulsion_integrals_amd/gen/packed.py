@@ -67,17 +67,22 @@ def _wide_waves(ci: ClassInfo) -> int:
     return {84: 4, 165: 3}.get(ci.G, 2)
 
 
-def packed_k1_waves(ci: ClassInfo) -> int:
+def packed_k1_waves(ci: ClassInfo, spherical: bool = True) -> int:
+    if _k1_three(ci, spherical):
+        return K1_THREE_WAVES_W
     return _wide_waves(ci) if ci.G > 64 else PACK_WAVES
 
 
-# K4 = 1 kernels built for three waves per SIMD instead of two.  Their
-# bra-path selectors are packed one int per step and a record batch covers
-# four groups, which keeps (dd|dd) at 164 VGPRs with no scratch and six
-# two-wave workgroups within a compute unit's LDS.  Measured on the (dd|dd)
-# batch: 5% faster than two waves per SIMD.
+# K4 = 1 kernels built for three waves per SIMD instead of two, on workgroups
+# of three waves (five 35-lane quartets in 192 lanes).  Their bra-path
+# selectors are packed one int per step, which keeps (dd|dd) at 164 VGPRs
+# with no scratch, and a record batch of five groups fits four workgroups in
+# a compute unit's LDS.  Measured on the (dd|dd) batch against two waves per
+# SIMD: three waves per SIMD 5% faster, the five-group record batch (no reload
+# within a 20,000-quartet batch) 2% more, three-wave workgroups 1.5% more.
 K1_THREE_WAVES = {(2, 2, 2, 2, True)}  # (la, lb, lc, ld, spherical)
-K1_THREE_WAVES_RB = 4
+K1_THREE_WAVES_RB = 5
+K1_THREE_WAVES_W = 3
 
 
 def _k1_three(ci: ClassInfo, spherical: bool) -> bool:
@@ -175,14 +180,14 @@ def use_packed_k1(ci: ClassInfo, spherical: bool) -> bool:
     """Packing pays where a wave64 would leave many lanes idle, and a lane
     group wider than a wave needs it."""
     if wide_packed(ci, spherical):
-        return packed_wg_per_cu(ci, spherical, packed_k1_waves(ci)) >= 1
+        return packed_wg_per_cu(ci, spherical, packed_k1_waves(ci, spherical)) >= 1
     if ci.G > 64 or ci.G < 20:
         return False
     if (64 % ci.G) * 4 < 64:  # at most a quarter of the wave idles already
         return False
     if ci.Lk > 4:  # longer ket recurrences hold too many values for two waves per SIMD
         return False
-    return packed_wg_per_cu(ci, spherical) >= 2
+    return packed_wg_per_cu(ci, spherical, packed_k1_waves(ci, spherical)) >= 2
 
 
 def packed_wg_per_cu(ci: ClassInfo, spherical: bool, waves: int = PACK_WAVES, rb: int = 0) -> int:
@@ -376,7 +381,7 @@ def _emit_bra_hrr_split(ci, spherical, o, ind, P, slot_expr, setup, src_of):
 def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = 0, wg_per_cu: int = 0,
                    min_waves: int = 0):
     """K4 = 1 kernel, Q quartets per workgroup of `waves` waves."""
-    waves = waves or packed_k1_waves(ci)
+    waves = waves or packed_k1_waves(ci, spherical)
     min_waves = min_waves or packed_k1_min_waves(ci, spherical)
     rb = rb or _k1_rb(ci, spherical)
     from .emit import Names, _stage1, _stage1_selectors, _emit_hrr_scheduled, _fmt, AX
@@ -462,7 +467,9 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = 0, 
     o.append("        EriQuartetGeom gq;")
     o.append("        eri_geom(P, K, Ax - Cx, Ay - Cy, Az - Cz, gq);")
     o.append(f"        double F[{L + 1}];")
-    o.append(f"        eri_boys<{L}>(gq.T, gq.pref, a.boys, F);")
+    # the three-wave kernels take exp(-T) from the table: exp()'s constants
+    # would be held in registers across the loop and spill
+    o.append(f"        eri_boys<{L}{', true' if _k1_three(ci, spherical) else ''}>(gq.T, gq.pref, a.boys, F);")
     vals = ["P.PA[0]", "P.PA[1]", "P.PA[2]", "gq.WP[0]", "gq.WP[1]", "gq.WP[2]", "K.PA[0]", "K.PA[1]", "K.PA[2]",
             "gq.WQ[0]", "gq.WQ[1]", "gq.WQ[2]", "0.5 * P.izeta", "0.5 * K.izeta", "gq.roz", "gq.roe", "gq.i2ze"]
     vals += [f"F[{m}]" for m in range(L + 1)]

@@ -170,13 +170,14 @@ def test_packed_k1_routing_and_shapes():
             if not P.use_packed_k1(c, sph):
                 continue
             used.append((c.la, c.lb, c.lc, c.ld))
-            W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
+            W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c, sph))
+            three = (c.la, c.lb, c.lc, c.ld, sph) in P.K1_THREE_WAVES
             assert c.G in (35, 84, 120, 165) and Q * c.G <= NT and P._k1_rb(c, sph) * Q <= NT
-            assert W == {84: 4, 165: 3}.get(c.G, 2)
+            assert W == (3 if three else {84: 4, 165: 3}.get(c.G, 2))
             wg = P.packed_wg_per_cu(c, sph, W)
             assert 1 <= wg and P.packed_lds_bytes(c, sph, W) * wg <= P.LDS_BYTES
             # two waves per SIMD at most, three for the kernels built for three
-            assert wg * W <= 4 * (3 if (c.la, c.lb, c.lc, c.ld, sph) in P.K1_THREE_WAVES else 2)
+            assert wg * W <= 4 * (3 if three else 2)
             src = emit_register_tier(c, sph)
             if "lane tier" not in src.splitlines()[0]:
                 mw = P.packed_k1_min_waves(c, sph)
@@ -185,9 +186,10 @@ def test_packed_k1_routing_and_shapes():
     assert (2, 2, 2, 2) in used and (3, 1, 2, 2) in used and (3, 3, 2, 1) in used
     assert (4, 3, 4, 1) in used and (4, 3, 3, 3) not in used
     assert P.packed_k1_min_waves(gg.ClassInfo(3, 3, 2, 2)) == 2 and P.packed_k1_min_waves(gg.ClassInfo(4, 3, 1, 0)) == 0
-    # spherical (dd|dd): three waves per SIMD, six workgroups per compute unit
+    # spherical (dd|dd): three waves per SIMD, four three-wave workgroups per compute unit
     dd = gg.ClassInfo(2, 2, 2, 2)
-    assert P.packed_k1_min_waves(dd, True) == 3 and P.packed_wg_per_cu(dd, True, 2) == 6
+    assert P.packed_k1_waves(dd, True) == 3 and P.packed_k1_min_waves(dd, True) == 3
+    assert P.packed_wg_per_cu(dd, True, 3) == 4 and P.packed_shape(dd, True, 3) == (3, 5, 192)
     assert P.packed_k1_min_waves(dd, False) == 0
     assert all(sum(u[:2]) in (4, 6, 7, 8) and sum(u[2:]) <= {4: 4, 6: 6, 7: 5, 8: 4}[sum(u[:2])] for u in used)
     assert (4, 4, 2, 2) in used and (4, 4, 3, 2) not in used
@@ -264,7 +266,7 @@ def test_split_bra_hrr_covers_outputs_once():
     from electron_repulsion_integrals_amd.gen.emit import emit_register_tier
     for c, sph in ((gg.ClassInfo(3, 3, 1, 0), True), (gg.ClassInfo(4, 4, 1, 1), False), (gg.ClassInfo(4, 3, 2, 0), True)):
         src = emit_register_tier(c, sph)
-        W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c))
+        W, Q, NT = P.packed_shape(c, sph, P.packed_k1_waves(c, sph))
         assert P.bra_hrr_parts(c, sph, W, Q) == W > 1
         kernels = src.split("__global__")[1:]
         assert len(kernels) == 2

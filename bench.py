@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 # reported as null once either changes.
 TRAFFIC = {"kernel_sources": ["electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
                               "electron_repulsion_integrals_amd/csrc/eri_device.h"],
-           "sha1": "08a779daafca427b33fdeae2cf08013a7832398c",
-           "fetch_kib": 5006.13, "fetch_scale": 2.0, "write_kib": 97817.92, "write_scale": 1.0}
+           "sha1": "8be5a7b6b1aa9c0785780a5188002533f93c8d87",
+           "fetch_kib": 4698.29, "fetch_scale": 2.0, "write_kib": 97764.22, "write_scale": 1.0}
 
 
 def measured_traffic():
@@ -94,18 +94,23 @@ def time_launches(fn, steps, warmup, stream):
     return [a.elapsed_time(b) for a, b in ev], wall
 
 
-def back_to_back(fn, n, stream):
-    """Mean ms per call of n calls issued back to back between one pair of events."""
+def timed_steps(fn, steps, warmup, stream):
+    """ms per step of `steps` calls of fn() issued back to back between one pair
+    of HIP events on `stream`, with the device synchronized before and after;
+    and the host wall time of that region (s)."""
     import torch
-    fn()
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     a.record(stream)
-    for _ in range(n):
+    for _ in range(steps):
         fn()
     b.record(stream)
-    b.synchronize()
-    return a.elapsed_time(b) / n
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall
 
 
 def clock_under_load(fn, seconds=1.0):
@@ -460,11 +465,12 @@ def main():
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
     out = torch.empty(plan.n_out, dtype=torch.float64, device="cuda")
-    times, wall = time_launches(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
-    ms = sum(times) / len(times)
-    b2b = clocks = fma_tflops = None
+    # the timed region: K steps back to back, the device synchronized on both sides
+    ms, wall = timed_steps(lambda: E.compute_batch(plan, out), a.steps, a.warmup, stream)
+    # single launches between their own events, for the spread (each includes the launch gap)
+    times, _ = time_launches(lambda: E.compute_batch(plan, out), a.steps, 0, stream)
+    clocks = fma_tflops = None
     if not a.no_extra:  # extra launches would also enter a profiler's per-kernel average
-        b2b = back_to_back(lambda: E.compute_batch(plan, out), 100, stream)
         clocks = clock_under_load(lambda: E.compute_batch(plan, out))
         fma_tflops = E.fp64_fma_tflops()
     nq = plan.n_quartets
@@ -489,10 +495,9 @@ def main():
                    "quartets": nq, "output_doubles": plan.n_out},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP64_VECTOR_PEAK_TFLOPS, "traffic": measured_traffic()},
-        "ms_median": sorted(times)[len(times) // 2],
-        "ms_min": min(times),
-        "ms_max": max(times),
-        "ms_per_launch_100_back_to_back": b2b,
+        "ms_single_launch_median": sorted(times)[len(times) // 2],
+        "ms_single_launch_min": min(times),
+        "ms_single_launch_max": max(times),
         "gpu_clocks_under_load": clocks,
         "fp64_fma_measured_TFLOPs": fma_tflops,
         "achieved_over_measured_fma": achieved / fma_tflops if fma_tflops else None,

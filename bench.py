@@ -301,13 +301,16 @@ def deriv_sampled(E, plan, w, per_block=2000):
             "per_class": res}
 
 
-def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=200000):
+def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=1000000):
     """The 120-atom cluster: the full screened plan (implicit) is built and
     timed; every class block is then sampled in ``strata`` evenly spaced
     slot ranges (blocks are ordered by contraction length, so the strata span
     the block's K mix) and timed with HIP events.  The full integral time is
     extrapolated block by block -- an estimate, labelled as such: evaluating
-    all 2e10 quartets takes tens of minutes."""
+    all 2e10 quartets takes about an hour (c5_measured times it piece by
+    piece).  A stratum of a one-quartet-per-lane class holds up to 125,000
+    quartets: smaller launches leave most of the GPU idle and would make the
+    estimate pessimistic."""
     import numpy as np
     import torch
     from electron_repulsion_integrals_amd.gen import graph as G
@@ -420,6 +423,101 @@ def cpu_baselines_per_config(seconds=6.0):
     return res
 
 
+def c5_pieces(E, plan, w, n_target=400, setup_flops=150, samples=64):
+    """The 120-atom cluster's J build cut into about ``n_target`` slot ranges
+    (block, first, count) of similar estimated cost, in block order.  A block's
+    cost per slot is estimated from K4 at ``samples`` evenly spaced slots
+    (blocks are ordered by contraction length): per primitive quartet the
+    graph's FLOPs plus ``setup_flops`` for its set-up, plus the per-quartet
+    part.  Deterministic for a given plan."""
+    import numpy as np
+    from electron_repulsion_integrals_amd.gen import graph as G
+    K = np.asarray(w.shells.nprim, dtype=np.int64)
+    blocks = []
+    for b in range(plan.n_blocks):
+        cid, st, cnt = int(plan.block_class[b]), int(plan.block_start[b]), int(plan.block_count[b])
+        la, lb = G.pair_class_ls(_pcb(cid))
+        lc, ld = G.pair_class_ls(_pck(cid))
+        per_prim, once = G.dag_flops(G.ClassInfo(la, lb, lc, ld), True)
+        pos = np.unique(np.linspace(0, cnt - 1, min(cnt, samples)).astype(np.int64))
+        k4 = []
+        for p_ in pos:
+            r = plan.quartets(st + int(p_), 1).cpu().numpy()[0]
+            k4.append(float(K[r[0]] * K[r[1]] * K[r[2]] * K[r[3]]))
+        cost_at = (per_prim + setup_flops) * np.asarray(k4) + once
+        # cumulative cost at every sample position, trapezoid between them
+        cum = np.concatenate([[0.0], np.cumsum(0.5 * (cost_at[1:] + cost_at[:-1]) * np.diff(pos))])
+        total = cum[-1] + cost_at[-1]
+        blocks.append((b, cnt, pos, cum, total))
+    grand = sum(t for *_, t in blocks)
+    cap = grand / n_target
+    pieces = []
+    for b, cnt, pos, cum, total in blocks:
+        npc = max(1, int(np.ceil(total / cap)))
+        cuts = [0]
+        for k in range(1, npc):
+            cuts.append(int(np.interp(total * k / npc, cum, pos)))
+        cuts.append(cnt)
+        cuts = sorted(set(cuts))
+        for f, g in zip(cuts, cuts[1:]):
+            pieces.append((b, f, g - f))
+    return pieces, grand
+
+
+def c5_measured(E, first_piece, last_piece, budget_s, stream):
+    """Measured J build of the 120-atom cluster, slot range by slot range
+    (eri_digest_J_range into one J): pieces [first_piece, last_piece) of
+    c5_pieces, each timed with HIP events, one JSON line per piece; stops
+    before a piece once ``budget_s`` of wall time has passed.  The last line
+    carries the totals and sampled elements of this run's partial J (the
+    partial J of all runs add up to the full J)."""
+    import numpy as np
+    import torch
+    from workloads import make_config
+    from electron_repulsion_integrals_amd.gen import graph as G
+    t_start = time.perf_counter()
+    w = make_config(5)
+    t0 = time.perf_counter()
+    plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, None, w.tau)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    pieces, grand = c5_pieces(E, plan, w)
+    last_piece = min(last_piece, len(pieces))
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.zeros_like(D)
+    print(json.dumps({"c5_pieces": len(pieces), "plan_build_ms": plan_ms, "quartets": plan.n_quartets,
+                      "first_piece": first_piece}), flush=True)
+    done_ms, nq, i = 0.0, 0, first_piece
+    while i < last_piece:
+        if time.perf_counter() - t_start > budget_s:
+            break
+        b, f, n = pieces[i]
+        a_, z_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        E.digest_J_range(plan, b, f, n, D, J)
+        z_.record(stream)
+        z_.synchronize()
+        ms = a_.elapsed_time(z_)
+        done_ms += ms
+        nq += n
+        cid = int(plan.block_class[b])
+        la, lb = G.pair_class_ls(_pcb(cid))
+        lc, ld = G.pair_class_ls(_pck(cid))
+        name = "(" + "spdfg"[la] + "spdfg"[lb] + "|" + "spdfg"[lc] + "spdfg"[ld] + ")"
+        print(json.dumps({"piece": i, "block": b, "class": name, "first": f, "count": n, "ms": ms}), flush=True)
+        i += 1
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    nbf = D.shape[0]
+    idx = rng.integers(0, nbf, size=(256, 2))
+    Jh = J.cpu().numpy()
+    print(json.dumps({"c5_part_done": True, "pieces": [first_piece, i], "next_piece": i, "of": len(pieces),
+                      "quartets": nq, "digest_ms": done_ms, "J_sum": float(Jh.sum()),
+                      "J_abs_sum": float(np.abs(Jh).sum()), "J_trace": float(np.trace(Jh)),
+                      "J_asym_max": float(np.abs(Jh - Jh.T).max()),
+                      "J_samples": [[int(r), int(c), float(Jh[r, c])] for r, c in idx]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,6 +528,10 @@ def main():
                     help="skip the secondary workloads and the extra launches (back to back, clocks, FMA rate)")
     ap.add_argument("--only-j-build", action="store_true",
                     help="only the 30-atom cluster: J build and per-class times (for profiler runs)")
+    ap.add_argument("--c5-j-pieces", default="",
+                    help="A:B -- measured 120-atom J build, slot-range pieces A..B-1 (see c5_pieces)")
+    ap.add_argument("--budget-s", type=float, default=900.0,
+                    help="with --c5-j-pieces: start no piece after this many seconds")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
@@ -454,6 +556,10 @@ def main():
     E.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if a.c5_j_pieces:
+        lo, hi = (int(x) for x in a.c5_j_pieces.split(":"))
+        c5_measured(E, lo, hi, a.budget_s, stream)
+        return
     if a.only_j_build:
         w3 = make_config(3)
         plan3, jb = j_build(E, w3, 5, stream)

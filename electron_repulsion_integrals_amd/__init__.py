@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     compute_deriv,
     compute_range,
     digest_J,
+    digest_J_range,
     digest_JK,
     fp64_fma_tflops,
     load,

@@ -86,6 +86,9 @@ def load(path=None):
     L.eri_plan_quartets.restype = ctypes.c_int
     L.eri_digest_J.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, szp, vp]
     L.eri_digest_J.restype = ctypes.c_int
+    L.eri_digest_J_range.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int32, vp,
+                                     ctypes.c_int32, vp, szp, vp]
+    L.eri_digest_J_range.restype = ctypes.c_int
     L.eri_digest_JK.argtypes = [vp, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, ctypes.c_int32, vp, szp, vp]
     L.eri_digest_JK.restype = ctypes.c_int
     L.eri_compute_deriv.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64, vp, szp, vp]
@@ -290,6 +293,18 @@ def digest_J(plan: Plan, D, J, stream=None):
     nbytes = ctypes.c_size_t(ws.numel())
     _check(L.eri_digest_J(plan.handle, _ptr(D), int(D.stride(0)), _ptr(J), int(J.stride(0)), _ptr(ws),
                           ctypes.byref(nbytes), st))
+    return J
+
+
+def digest_J_range(plan: Plan, block: int, first: int, count: int, D, J, stream=None):
+    """J (device, nbf x nbf, float64) += the Coulomb contributions of quartets
+    [first, first + count) of class block ``block``; J is not cleared."""
+    L = load()
+    st = _stream_handle(stream)
+    ws = _digest_workspace(plan, (True, False), lambda nb: L.eri_digest_J(plan.handle, None, 0, None, 0, None, nb, st))
+    nbytes = ctypes.c_size_t(ws.numel())
+    _check(L.eri_digest_J_range(plan.handle, int(block), int(first), int(count), _ptr(D), int(D.stride(0)), _ptr(J),
+                                int(J.stride(0)), _ptr(ws), ctypes.byref(nbytes), st))
     return J
 
 

@@ -1260,9 +1260,20 @@ bool digest_shape_capped(const eri_plan *P, bool wantJ, bool wantK, size_t cap, 
     }
 }
 
+// Quartet ranges to digest: every block whole, or slots [first, first + count)
+// of one block.
+struct DigestRange {
+    int block = -1;  // -1: all blocks
+    int64_t first = 0, count = 0;
+};
+
+// accumulate: J gets the range's contributions added to what it holds instead
+// of being overwritten.
 void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int ldj, double *K, int ldk, Arena &ws,
-                   hipStream_t s, const DigestShape *shape = nullptr)
+                   hipStream_t s, const DigestShape *shape = nullptr, DigestRange rg = DigestRange(),
+                   bool accumulate = false)
 {
+    const int b0 = rg.block < 0 ? 0 : rg.block, b1 = rg.block < 0 ? (int)P->blocks.size() : rg.block + 1;
     const DigestShape d = shape ? *shape : digest_shape(P, J != nullptr, K != nullptr);
     std::vector<ChunkLane> L;
     double *kacc = nullptr;
@@ -1275,12 +1286,14 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
         ChunkLane &W = L[l];
         double *Jl = l == 0 ? J : W.J;
         const int ldl = l == 0 ? ldj : n;
-        if (J) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, Jl, ldl);
+        if (J && !(accumulate && l == 0))
+            hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, Jl, ldl);
         if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, W.A, n);
         HIP_CHECK(hipGetLastError());
     }
     int64_t chunk_index = 0;
-    for (const EriBlock &B : P->blocks) {
+    for (int bi = b0; bi < b1; ++bi) {
+        const EriBlock &B = P->blocks[bi];
         const int nab = B.na * B.nb, ncd = B.nc * B.nd;
         const int nkv = B.na * B.nc + B.nb * B.nc + B.na * B.nd + B.nb * B.nd;
         const int64_t blk = (int64_t)nab * ncd;
@@ -1289,13 +1302,14 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
         if (K) step = std::min<int64_t>(step, d.CB / nkv);
         step = std::max<int64_t>(1, step);
         const bool scratch_class = uses_scratch(P, B.cid);
-        for (int64_t c = 0; c < B.count; c += step, ++chunk_index) {
+        const int64_t c0 = rg.block < 0 ? 0 : rg.first, c1 = rg.block < 0 ? B.count : rg.first + rg.count;
+        for (int64_t c = c0; c < c1; c += step, ++chunk_index) {
             const int l = scratch_class ? 0 : (int)(chunk_index % NL);
             const hipStream_t ls = lane_stream(P, l, s);
             ChunkLane &W = L[l];
             double *Jl = l == 0 ? J : W.J;
             const int ldl = l == 0 ? ldj : n;
-            const int64_t m = std::min(step, B.count - c);
+            const int64_t m = std::min(step, c1 - c);
             const int *qb = nullptr, *qk = nullptr;
             slot_lists(P, B.start + c, m, &qb, &qk, ls, l);
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
@@ -2055,7 +2069,8 @@ extern "C" int eri_compute_range(const eri_plan *P, int32_t block, int64_t first
 namespace {
 
 int digest_entry(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj, double *K, int32_t ldk,
-                 bool wantJ, bool wantK, void *workspace, size_t *ws_bytes, void *stream)
+                 bool wantJ, bool wantK, void *workspace, size_t *ws_bytes, void *stream,
+                 DigestRange rg = DigestRange(), bool accumulate = false)
 {
     if (!P || !ws_bytes) return ERI_E_INVALID;
     if (!P->screened) return ERI_E_UNSUPPORTED;
@@ -2071,7 +2086,8 @@ int digest_entry(const eri_plan *P, const double *D, int32_t ldd, double *J, int
         if (!D || ldd < P->nbf || (wantJ && (!J || ldj < P->nbf)) || (wantK && (!K || ldk < P->nbf)))
             return ERI_E_INVALID;
         Arena A(workspace, *ws_bytes);
-        digest_JK_run(P, D, ldd, wantJ ? J : nullptr, ldj, wantK ? K : nullptr, ldk, A, (hipStream_t)stream);
+        digest_JK_run(P, D, ldd, wantJ ? J : nullptr, ldj, wantK ? K : nullptr, ldk, A, (hipStream_t)stream, nullptr,
+                      rg, accumulate);
     } catch (const HipFail &f) {
         return translate(f);
     } catch (const WsShort &) {
@@ -2086,6 +2102,18 @@ extern "C" int eri_digest_J(const eri_plan *P, const double *D, int32_t ldd, dou
                             size_t *ws_bytes, void *stream)
 {
     return digest_entry(P, D, ldd, J, ldj, nullptr, 0, true, false, workspace, ws_bytes, stream);
+}
+
+extern "C" int eri_digest_J_range(const eri_plan *P, int32_t block, int64_t first, int64_t count, const double *D,
+                                  int32_t ldd, double *J, int32_t ldj, void *workspace, size_t *ws_bytes, void *stream)
+{
+    if (!P || block < 0 || block >= (int32_t)P->blocks.size() || first < 0 || count < 0) return ERI_E_INVALID;
+    if (first > P->blocks[block].count || count > P->blocks[block].count - first) return ERI_E_INVALID;
+    DigestRange rg;
+    rg.block = block;
+    rg.first = first;
+    rg.count = count;
+    return digest_entry(P, D, ldd, J, ldj, nullptr, 0, true, false, workspace, ws_bytes, stream, rg, true);
 }
 
 extern "C" int eri_digest_JK(const eri_plan *P, const double *D, int32_t ldd, double *J, int32_t ldj, double *K,

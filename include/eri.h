@@ -207,6 +207,21 @@ int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, 
                  size_t *ws_bytes, void *stream);
 
 /*
+ * The Coulomb contributions of quartets [first, first + count) of class block
+ * `block` of a screened plan (counted from the block's first slot, as
+ * eri_compute_range) added to J: the sum of Algorithm 2 line 10 restricted to
+ * those quartets, with eri_digest_J's D~ weights and row-major layouts.  J is
+ * not cleared: over ranges that partition every block, with J zeroed first,
+ * the calls add up to eri_digest_J's result (equal to rounding: the chunks are
+ * spread over the stream lanes per call).  For J builds longer than one call
+ * may take (time-sliced or checkpointed jobs).  ERI_E_INVALID for a block or
+ * slot range outside the plan.  Workspace and query as eri_digest_J (a
+ * workspace sized for eri_digest_J serves every range); asynchronous.
+ */
+int eri_digest_J_range(const eri_plan *plan, int32_t block, int64_t first, int64_t count, const double *D,
+                       int32_t ldd, double *J, int32_t ldj, void *workspace, size_t *ws_bytes, void *stream);
+
+/*
  * Coulomb and exchange matrices of a screened plan in one pass over its
  * integrals (Algorithm 2 line 10 scatters into J and K; section III-C2): J as
  * eri_digest_J, and K_mu,nu = sum (mu la|nu si) D_la,si (no factor -1/2),

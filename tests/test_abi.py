@@ -42,6 +42,7 @@ def test_strerror_and_argument_validation_without_gpu():
     assert L.eri_compute_range(None, 0, 0, 1, None, 0, None) == -1
     assert L.eri_plan_quartets(None, 0, 1, None, None) == -1
     assert L.eri_digest_JK(None, None, 0, None, 0, None, 0, None, ctypes.byref(sz), None) == -1
+    assert L.eri_digest_J_range(None, 0, 0, 1, None, 0, None, 0, None, ctypes.byref(sz), None) == -1
     assert L.eri_compute_deriv(None, 0, 1, None, 0, None, ctypes.byref(sz), None) == -1
     assert L.eri_plan_set_streams(None, None, 0) == -1
     assert L.eri_fp64_fma_tflops(None, None) == -1

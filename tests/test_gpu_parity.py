@@ -266,6 +266,39 @@ def test_c3_reduced_plan_and_J(eri):
     assert_parity(Jg, Jref, "J")
 
 
+def test_J_by_slot_ranges(eri):
+    """eri_digest_J_range over ranges that partition every class block (the
+    first block in three slot ranges, one of them empty), added into one zeroed
+    J, gives the oracle's J of the 4-atom cluster; an empty range adds nothing;
+    ranges outside the plan are rejected."""
+    import torch
+    _log("case: C3 4-atom cluster, J from slot ranges")
+    w = make_config(3, scale={"natoms": 4})
+    sh = w.shells
+    plan = eri.build_quartets(sh, 1, None, w.tau)
+    nb = plan.n_blocks
+    cnt = [int(c) for c in plan.block_count]
+    assert nb >= 3 and cnt[0] >= 2
+    D = torch.tensor(w.density, device="cuda")
+    J = torch.zeros_like(D)
+    h = cnt[0] // 2
+    ranges = [(0, 0, h), (0, h, 0), (0, h, cnt[0] - h)] + [(b, 0, cnt[b]) for b in range(1, nb)]
+    for b, f, n in ranges:
+        before = J.clone()
+        eri.digest_J_range(plan, b, f, n, D, J)
+        if n == 0:
+            torch.cuda.synchronize()
+            assert torch.equal(J, before), "an empty range changed J"
+    for bad in ((nb, 0, 0), (0, 0, cnt[0] + 1), (0, cnt[0], 1), (-1, 0, 0)):
+        with pytest.raises(eri.EriError):
+            eri.digest_J_range(plan, *bad, D, J)
+    torch.cuda.synchronize()
+    imap = plan.index_map().cpu().numpy()
+    flat, off = oracle.eri(sh, imap[:, :4], True)
+    Jref = oracle.J_from_quartets(sh, True, imap[:, :4], flat, off, w.density)
+    assert_parity(J.cpu().numpy(), Jref, "J by slot ranges")
+
+
 def test_multi_block_call_matches_block_by_block(eri):
     """A call over all class blocks (blocks spread over the plan's side streams)
     gives bitwise the integrals of one call per block, on the caller's stream,

@@ -578,6 +578,11 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = 0, 
 
 
 PACK_CH = 21  # primitive quartets per quartet set up together (one lane each)
+# the contracted packed kernels share the K4 = 1 kernels' conflict-free level
+# slots, own-terms-first levels and bra-HRR preload
+CONTRACTED_SLOTS = True
+CONTRACTED_OWN_FIRST = True
+CONTRACTED_PRELOAD = True
 
 
 # Register form of the contracted kernels.  With loop-invariant selectors (two
@@ -669,6 +674,17 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     cid = class_id(ci.la, ci.lb, ci.lc, ci.ld)
     tag = f"c{cid}_{'s' if spherical else 'c'}"
     lane_decl, lane_dec = _lane_table(ci, tag)
+    if CONTRACTED_SLOTS:
+        pi, rd = slot_layout(ci, NT)
+        assert NT <= 256
+        tab = [pi[t] | (rd[0][t] << 8) | (rd[1][t] << 16) | (rd[2][t] << 24) for t in range(NT)]
+        lane_decl += (f"\n__constant__ unsigned k_{tag}_slot[{NT}] = {{" +
+                      ", ".join(f"{v}u" for v in tab) + "};")
+        lane_dec = [ln for ln in lane_dec if not ln.lstrip().startswith("const int src")]
+        lane_dec.append(f"  const unsigned slt = k_{tag}_slot[tid];")
+        lane_dec.append("  const int myslot = (int)(slt & 255u), srcx = (int)((slt >> 8) & 255u),"
+                        " srcy = (int)((slt >> 16) & 255u), srcz = (int)(slt >> 24);")
+    me = "myslot" if CONTRACTED_SLOTS else "tid"
     lv = _levels(kv)
     levels = sorted(lv)
     NC = max((len(v) for v in lv.values()), default=0)
@@ -775,10 +791,20 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
             o.append(f"      acc{t} += wgt * s1_{tg[1]};")
     for li, k in enumerate(levels):
         o.append(f"      // ket level {k}: publish level {k - 1} values read across lanes")
-        o.append(f"      {{ double* xb = xu + (lvl & 1) * (NC * NT) + tid;")
+        o.append(f"      {{ double* xb = xu + (lvl & 1) * (NC * NT) + {me};")
         for j, key in enumerate(lv[k]):
             o.append(f"        xb[{j * NT}] = {names.ket(key)};")
         o.append("      }")
+        if CONTRACTED_OWN_FIRST:
+            # the lane's own terms of every node before the barrier
+            for n in kv.nodes:
+                if sum(n.f) != k:
+                    continue
+                a_ = AX[n.axis]
+                expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+                if n.b0 is not None:
+                    expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+                o.append(f"      const double {names.ket((n.f, n.m))}p = {expr};")
         o.append("      __syncthreads();")
         o.append(f"      const double* xrb{k} = xu + (lvl & 1) * (NC * NT);")
         o.append("      ++lvl;")
@@ -794,9 +820,12 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
             if sum(n.f) != k:
                 continue
             a_ = AX[n.axis]
-            expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
-            if n.b0 is not None:
-                expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+            if CONTRACTED_OWN_FIRST:
+                expr = f"{names.ket((n.f, n.m))}p"
+            else:
+                expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+                if n.b0 is not None:
+                    expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
             expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
             o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
             if n.m == 0 and n.f in tpos:
@@ -835,7 +864,8 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
         o.append("    const double* src = xu + q2 * NEB * NK + kap;")
         o.append("    double* dst = a.out + (size_t)slot * BLK + kap;")
         _emit_hrr_scheduled(ci.la, ci.lb, lambda e: f"src[{epos[e]} * NK]", "AB", spherical,
-                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "    ", "z")
+                            lambda kk, x: f"eri_out_merged(&dst[{kk} * NK], {x});", o, "    ", "z",
+                            preload=CONTRACTED_PRELOAD)
         o.append("  }")
     o.append("}")
     o.append("")

@@ -241,24 +241,31 @@ def _deriv_flops(w, rows):
     lowered (Cartesian kernels), K4 primitive quartets each."""
     import numpy as np
     from electron_repulsion_integrals_amd.gen import graph as G
+    rows = np.asarray(rows)
+    if len(rows) == 0:
+        return 0
     K = np.asarray(w.shells.nprim, dtype=np.int64)
-    L = np.asarray(w.shells.l)
+    L = np.asarray(w.shells.l, dtype=np.int64)
+    k4 = K[rows[:, 0]] * K[rows[:, 1]] * K[rows[:, 2]] * K[rows[:, 3]]
+    l4 = L[rows[:, :4]]
     cache, total = {}, 0
-    for r in rows:
-        k4 = int(K[r[0]] * K[r[1]] * K[r[2]] * K[r[3]])
-        for p in range(4):
-            for dl in (1, -1):
-                l4 = [int(L[r[t]]) for t in range(4)]
-                if l4[p] + dl < 0:
-                    continue
-                l4[p] += dl
-                key = (max(l4[0], l4[1]), min(l4[0], l4[1]), max(l4[2], l4[3]), min(l4[2], l4[3]))
-                if key[0] * (key[0] + 1) // 2 + key[1] < key[2] * (key[2] + 1) // 2 + key[3]:
-                    key = (key[2], key[3], key[0], key[1])
-                if key not in cache:
-                    cache[key] = G.dag_flops(G.ClassInfo(*key), False)
-                per_prim, once = cache[key]
-                total += k4 * per_prim + once
+    for p in range(4):
+        for dl in (1, -1):
+            ll = l4.copy()
+            ll[:, p] += dl
+            ok = ll[:, p] >= 0
+            a, b = np.maximum(ll[:, 0], ll[:, 1]), np.minimum(ll[:, 0], ll[:, 1])
+            c, d = np.maximum(ll[:, 2], ll[:, 3]), np.minimum(ll[:, 2], ll[:, 3])
+            swap = a * (a + 1) // 2 + b < c * (c + 1) // 2 + d
+            key = np.where(swap[:, None], np.stack([c, d, a, b], 1), np.stack([a, b, c, d], 1))
+            uk, inv = np.unique(key[ok], axis=0, return_inverse=True)
+            for j, kk in enumerate(uk):
+                kk = tuple(int(x) for x in kk)
+                if kk not in cache:
+                    cache[kk] = G.dag_flops(G.ClassInfo(*kk), False)
+                per_prim, once = cache[kk]
+                sel = inv.ravel() == j
+                total += int(k4[ok][sel].sum()) * per_prim + int(sel.sum()) * once
     return total
 
 
@@ -532,6 +539,8 @@ def main():
                     help="A:B -- measured 120-atom J build, slot-range pieces A..B-1 (see c5_pieces)")
     ap.add_argument("--budget-s", type=float, default=900.0,
                     help="with --c5-j-pieces: start no piece after this many seconds")
+    ap.add_argument("--only-deriv", action="store_true",
+                    help="only the 30-atom cluster's first derivatives, 50,000 slots per class block (profiler runs)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run one plain device copy of this many MiB (scales rocprofv3 FETCH/WRITE_SIZE)")
     a = ap.parse_args()
@@ -559,6 +568,11 @@ def main():
     if a.c5_j_pieces:
         lo, hi = (int(x) for x in a.c5_j_pieces.split(":"))
         c5_measured(E, lo, hi, a.budget_s, stream)
+        return
+    if a.only_deriv:
+        w3 = make_config(3)
+        plan3 = E.build_quartets(w3.shells, E.ERI_SPHERICAL, None, w3.tau)
+        print(json.dumps({"derivatives_30atom_svp_50k": deriv_sampled(E, plan3, w3, per_block=50000)}), flush=True)
         return
     if a.only_j_build:
         w3 = make_config(3)
@@ -622,6 +636,7 @@ def main():
         res["j_build_30atom_svp_cartesian"] = jbc
         res["per_class"]["30-atom SVP-like cluster"] = per_class(E, plan3, w3, 3, stream)
         res["derivatives_30atom_svp"] = deriv_sampled(E, plan3, w3)
+        res["derivatives_30atom_svp_50k"] = deriv_sampled(E, plan3, w3, per_block=50000)
         del plan3
         w4 = make_config(4)
         plan4 = E.build_quartets(w4.shells, E.ERI_SPHERICAL, w4.quartets, 0.0)

@@ -48,6 +48,7 @@ struct EriClassArgs {
     double* scratch;        // memory-tier scratch (scratch_wgs workgroup slices)
     int scratch_wgs;
     int grid_cap;           // register tier: persistent grid size (workgroups)
+    long long pair_base;    // >= 0: qbra[q] = pair_base + 2q and qket[q] = qbra[q] + 1 (explicit lists)
 };
 
 typedef void (*EriLaunchFn)(const EriClassArgs&, hipStream_t);

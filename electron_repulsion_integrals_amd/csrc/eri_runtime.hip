@@ -985,6 +985,11 @@ void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, co
     a.scratch = P->d_scratch;
     a.scratch_wgs = P->scratch_wgs;
     a.grid_cap = P->grid_cap;
+    // an explicit plan's own lists pair slot s with pairs 2s and 2s + 1: kernels
+    // may then skip reading them
+    long long base = -1;
+    if (!P->screened && qbra >= P->d_qbra && qbra < P->d_qbra + P->nq && qket == P->d_qket + (qbra - P->d_qbra))
+        base = 2 * (long long)(qbra - P->d_qbra);
     const int blk = nfun(ce->la, sph) * nfun(ce->lb, sph) * nfun(ce->lc, sph) * nfun(ce->ld, sph);
     if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
         g_last_error = "memory-tier class without scratch";
@@ -999,6 +1004,7 @@ void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, co
             const int64_t m = std::min(CH, hi - b);
             a.qbra = qbra + b;
             a.qket = qket + b;
+            a.pair_base = base >= 0 ? base + 2 * b : -1;
             a.nq = (int)m;
             a.out = out + b * blk;
             (part == 0 ? ce->launch_k1 : ce->launch)(a, s);

@@ -511,7 +511,9 @@ def _register_kernel_k1_batched(ci: ClassInfo, spherical: bool):
     o.append("        const int k = lane / Q, gk = g + k * (int)gridDim.x;")
     o.append("        int q = gk * Q + (lane - k * Q);")
     o.append("        if (gk >= ngroups || q >= a.nq) q = a.nq - 1;  // past the end: a valid record, never used")
-    o.append("        const int bra = a.qbra[q], ket = a.qket[q];")
+    # explicit lists are the identity pairing: one dependent load less
+    o.append("        const int bra = a.pair_base >= 0 ? (int)(a.pair_base + 2 * (long long)q) : a.qbra[q];")
+    o.append("        const int ket = a.pair_base >= 0 ? bra + 1 : a.qket[q];")
     o.append("        const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
     o.append("        const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
     o.append("        const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")

@@ -458,7 +458,9 @@ def emit_packed_k1(ci: ClassInfo, spherical: bool, waves: int = 0, rb: int = 0, 
     o.append("        const int k = tid / Q, gk = g + k * (int)gridDim.x;")
     o.append("        int q = gk * Q + (tid - k * Q);")
     o.append("        if (gk >= ngroups || q >= a.nq) q = a.nq - 1;  // past the end: a valid record, never stored")
-    o.append("        const int bra = a.qbra[q], ket = a.qket[q];")
+    # explicit lists are the identity pairing: one dependent load less
+    o.append("        const int bra = a.pair_base >= 0 ? (int)(a.pair_base + 2 * (long long)q) : a.qbra[q];")
+    o.append("        const int ket = a.pair_base >= 0 ? bra + 1 : a.qket[q];")
     o.append("        const int4 pb = a.pair_info[bra], pk = a.pair_info[ket];")
     o.append("        const double Ax = a.cen[3 * pb.x], Ay = a.cen[3 * pb.x + 1], Az = a.cen[3 * pb.x + 2];")
     o.append("        const double Cx = a.cen[3 * pk.x], Cy = a.cen[3 * pk.x + 1], Cz = a.cen[3 * pk.x + 2];")
@@ -772,64 +774,80 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     o.append("    }")
     o.append("    __syncthreads();")
     o.append("    const int n = K4max - c0 < CH ? K4max - c0 : CH;")
-    o.append("    for (int j = 0; j < n; ++j) {")
-    o.append("      const double* r = rec + qi * CH + j;")
-    o.append("      const double wgt = c0 + j < K4 ? 1.0 : 0.0;  // quartets shorter than the longest")
-    for fi, nm in enumerate(fields):
-        if nm.startswith("F") or fi < 6:
-            continue
-        o.append(f"      const double {nm} = r[{fi} * RS];")
-    o.append(f"      double F[{L + 1}];")
-    for m in range(L + 1):
-        o.append(f"      F[{m}] = r[{fields.index('F0') + m} * RS];")
-    o.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
-    o.append("      (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
-    o.append("      (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
-    _stage1(ci, kv.base_m, o, "      ", rsel="r", compact="all" if _compact(ci) else None)
-    for t, tg in enumerate(targets):
-        if sum(tg[0]) == 0:
-            o.append(f"      acc{t} += wgt * s1_{tg[1]};")
-    for li, k in enumerate(levels):
-        o.append(f"      // ket level {k}: publish level {k - 1} values read across lanes")
-        o.append(f"      {{ double* xb = xu + (lvl & 1) * (NC * NT) + {me};")
-        for j, key in enumerate(lv[k]):
-            o.append(f"        xb[{j * NT}] = {names.ket(key)};")
-        o.append("      }")
-        if CONTRACTED_OWN_FIRST:
-            # the lane's own terms of every node before the barrier
+    def segments(jexpr, wexpr, off_of):
+        """One primitive quartet's code in phases: prologue, bra path, and per
+        ket level (publish, own terms, reads, final terms); off_of[k] is the
+        first level-buffer array of its level-k values."""
+        pro = [f"      const double* r = rec + qi * CH + {jexpr};",
+               f"      const double wgt = {wexpr};  // quartets shorter than the longest"]
+        for fi, nm in enumerate(fields):
+            if nm.startswith("F") or fi < 6:
+                continue
+            pro.append(f"      const double {nm} = r[{fi} * RS];")
+        pro.append(f"      double F[{L + 1}];")
+        for m in range(L + 1):
+            pro.append(f"      F[{m}] = r[{fields.index('F0') + m} * RS];")
+        pro.append("      const double ehx = ex * i2ze, ehy = ey * i2ze, ehz = ez * i2ze;")
+        pro.append("      (void)QCx; (void)QCy; (void)QCz; (void)WQx; (void)WQy; (void)WQz; (void)i2z; (void)i2e;")
+        pro.append("      (void)roz; (void)roe; (void)ehx; (void)ehy; (void)ehz;")
+        bra = []
+        _stage1(ci, kv.base_m, bra, "      ", rsel="r", compact="all" if _compact(ci) else None)
+        for t, tg in enumerate(targets):
+            if sum(tg[0]) == 0:
+                bra.append(f"      acc{t} += wgt * s1_{tg[1]};")
+        lvs = []
+        for k in levels:
+            pub = [f"        xb[{(off_of[k] + j) * NT}] = {names.ket(key)};" for j, key in enumerate(lv[k])]
+            own = []
+            if CONTRACTED_OWN_FIRST:
+                for n in kv.nodes:
+                    if sum(n.f) != k:
+                        continue
+                    a_ = AX[n.axis]
+                    expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+                    if n.b0 is not None:
+                        expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+                    own.append(f"      const double {names.ket((n.f, n.m))}p = {expr};")
+            rds, reads = [], {}
+            for n in kv.nodes:
+                if sum(n.f) != k:
+                    continue
+                rk = (lv[k].index(n.a1), n.axis)
+                if rk not in reads:
+                    reads[rk] = f"xr{k}_{len(reads)}"
+                    rds.append(f"      const double {reads[rk]} = xrb{k}[{(off_of[k] + rk[0]) * NT} + src{AX[n.axis]}];")
+            fin = []
             for n in kv.nodes:
                 if sum(n.f) != k:
                     continue
                 a_ = AX[n.axis]
-                expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
-                if n.b0 is not None:
-                    expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
-                o.append(f"      const double {names.ket((n.f, n.m))}p = {expr};")
+                if CONTRACTED_OWN_FIRST:
+                    expr = f"{names.ket((n.f, n.m))}p"
+                else:
+                    expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
+                    if n.b0 is not None:
+                        expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
+                expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
+                fin.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
+                if n.m == 0 and n.f in tpos:
+                    fin.append(f"      acc{tpos[n.f]} += wgt * {names.ket((n.f, n.m))};")
+            lvs.append((pub, own, rds, fin))
+        return pro, bra, lvs
+
+    o.append("    for (int j = 0; j < n; ++j) {")
+    pro, bra, lvs = segments("j", "c0 + j < K4 ? 1.0 : 0.0", {k: 0 for k in levels})
+    o += pro + bra
+    for li, k in enumerate(levels):
+        pub, own, rds, fin = lvs[li]
+        o.append(f"      // ket level {k}: publish level {k - 1} values read across lanes")
+        o.append(f"      {{ double* xb = xu + (lvl & 1) * (NC * NT) + {me};")
+        o += pub
+        o.append("      }")
+        o += own
         o.append("      __syncthreads();")
         o.append(f"      const double* xrb{k} = xu + (lvl & 1) * (NC * NT);")
         o.append("      ++lvl;")
-        reads = {}
-        for n in kv.nodes:
-            if sum(n.f) != k:
-                continue
-            rk = (lv[k].index(n.a1), n.axis)
-            if rk not in reads:
-                reads[rk] = f"xr{k}_{len(reads)}"
-                o.append(f"      const double {reads[rk]} = xrb{k}[{rk[0] * NT} + src{AX[n.axis]}];")
-        for n in kv.nodes:
-            if sum(n.f) != k:
-                continue
-            a_ = AX[n.axis]
-            if CONTRACTED_OWN_FIRST:
-                expr = f"{names.ket((n.f, n.m))}p"
-            else:
-                expr = f"QC{a_} * {names.ket(n.a0)} + WQ{a_} * {names.ket(n.a1)}"
-                if n.b0 is not None:
-                    expr += f" + {_fmt(n.fi_minus_1)} * i2e * ({names.ket(n.b0)} - roe * {names.ket(n.b1)})"
-            expr += f" + eh{a_} * {reads[(lv[k].index(n.a1), n.axis)]}"
-            o.append(f"      const double {names.ket((n.f, n.m))} = {expr};")
-            if n.m == 0 and n.f in tpos:
-                o.append(f"      acc{tpos[n.f]} += wgt * {names.ket((n.f, n.m))};")
+        o += rds + fin
     o.append("    }")
     o.append("  }")
     o.append("  __syncthreads();  // level buffers and records read: the exchange may overwrite them")

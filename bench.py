@@ -168,12 +168,45 @@ def gpu_clocks():
     return cards or None
 
 
+PRIM_QMAX = 230.0  # the library's primitive-pair screen of screened plans
+
+
+def _k4(w, rows):
+    """Primitive quartets each quartet (rows of shell indices) evaluates: the
+    product of the shells' contraction degrees for an explicit list; for a
+    screened list the product of the two shell pairs' kept primitive pairs
+    (pairs with alpha beta / (alpha + beta) |AB|^2 <= 230, at least one)."""
+    import numpy as np
+    rows = np.asarray(rows)[:, :4].astype(np.int64)
+    sh = w.shells
+    K = np.asarray(sh.nprim, dtype=np.int64)
+    if w.quartets is not None:
+        return K[rows[:, 0]] * K[rows[:, 1]] * K[rows[:, 2]] * K[rows[:, 3]]
+    cen = np.asarray(sh.centers, dtype=np.float64).reshape(-1, 3)
+    exps = np.asarray(sh.exps, dtype=np.float64)
+    j = np.arange(int(K.max()))
+    idx = np.minimum(np.asarray(sh.prim_off, dtype=np.int64)[:len(K), None] + j, len(exps) - 1)
+    E = np.where(j < K[:, None], exps[idx], np.nan)
+
+    def kept(a, b):
+        d = cen[a] - cen[b]
+        ab2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+        al, be = E[a][:, :, None], E[b][:, None, :]
+        with np.errstate(invalid="ignore"):
+            n = ((al * be) / (al + be) * ab2[:, None, None] <= PRIM_QMAX).sum(axis=(1, 2))
+        return np.maximum(n, 1)
+    out = np.empty(len(rows), dtype=np.int64)
+    for c in range(0, len(rows), 65536):
+        r = rows[c:c + 65536]
+        out[c:c + 65536] = kept(r[:, 0], r[:, 1]) * kept(r[:, 2], r[:, 3])
+    return out
+
+
 def _block_flops(plan, w, imap):
     """Algorithmic FLOPs per class block: sum over quartets of K4 x per-primitive + once."""
     import numpy as np
     from electron_repulsion_integrals_amd.gen import graph as G
-    K = np.asarray(w.shells.nprim, dtype=np.int64)
-    k4 = K[imap[:, 0]] * K[imap[:, 1]] * K[imap[:, 2]] * K[imap[:, 3]]
+    k4 = _k4(w, imap)
     out = []
     for cid, st, cnt in zip(plan.block_class, plan.block_start, plan.block_count):
         cid, st, cnt = int(cid), int(st), int(cnt)
@@ -325,7 +358,6 @@ def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=1000000):
     plan = E.build_quartets(w.shells, E.ERI_SPHERICAL, None, w.tau)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
-    K = np.asarray(w.shells.nprim, dtype=np.int64)
     classes, est_total_s, flops_total, sample_s = {}, 0.0, 0.0, 0.0
     for b in range(plan.n_blocks):
         cid, cnt = int(plan.block_class[b]), int(plan.block_count[b])
@@ -343,7 +375,7 @@ def c5_sampled(E, w, stream, strata=8, max_doubles=1.5e8, max_quartets=1000000):
             times, _ = time_launches(lambda: E.compute_range(plan, b, f, per, out), 3, 1, stream)
             ms += sorted(times)[1]
             rows = plan.quartets(int(plan.block_start[b]) + f, per).cpu().numpy()
-            k4 = K[rows[:, 0]] * K[rows[:, 1]] * K[rows[:, 2]] * K[rows[:, 3]]
+            k4 = _k4(w, rows)
             flops += float(k4.sum()) * per_prim + per * once
         n = per * len(firsts)
         est_s = ms * 1e-3 * cnt / n
@@ -439,7 +471,6 @@ def c5_pieces(E, plan, w, n_target=400, setup_flops=150, samples=64):
     part.  Deterministic for a given plan."""
     import numpy as np
     from electron_repulsion_integrals_amd.gen import graph as G
-    K = np.asarray(w.shells.nprim, dtype=np.int64)
     blocks = []
     for b in range(plan.n_blocks):
         cid, st, cnt = int(plan.block_class[b]), int(plan.block_start[b]), int(plan.block_count[b])
@@ -447,11 +478,8 @@ def c5_pieces(E, plan, w, n_target=400, setup_flops=150, samples=64):
         lc, ld = G.pair_class_ls(_pck(cid))
         per_prim, once = G.dag_flops(G.ClassInfo(la, lb, lc, ld), True)
         pos = np.unique(np.linspace(0, cnt - 1, min(cnt, samples)).astype(np.int64))
-        k4 = []
-        for p_ in pos:
-            r = plan.quartets(st + int(p_), 1).cpu().numpy()[0]
-            k4.append(float(K[r[0]] * K[r[1]] * K[r[2]] * K[r[3]]))
-        cost_at = (per_prim + setup_flops) * np.asarray(k4) + once
+        rows = np.concatenate([plan.quartets(st + int(p_), 1).cpu().numpy() for p_ in pos])
+        cost_at = (per_prim + setup_flops) * _k4(w, rows).astype(np.float64) + once
         # cumulative cost at every sample position, trapezoid between them
         cum = np.concatenate([[0.0], np.cumsum(0.5 * (cost_at[1:] + cost_at[:-1]) * np.diff(pos))])
         total = cum[-1] + cost_at[-1]

@@ -152,9 +152,41 @@ __global__ void k_normalize(int nshell, const int *l, const int *nprim, const in
     for (int k = 0; k < K; ++k) out[o + k] *= f;
 }
 
-// Primitive-pair records for every shell pair (the page's GAUSSIANPAIRS).
+// Primitive-pair screening of screened plans.  A primitive pair (alpha of
+// shell A, beta of shell B) enters the plan when its Gaussian-product exponent
+// q = alpha beta / (alpha + beta) |AB|^2 is at most PRIM_QMAX, i.e. its factor
+// exp(-q) is at least 1.3e-100; a shell pair with no such primitive pair keeps
+// its first one.  A dropped pair's share of any integral is below 1e-100 times
+// its normalisation and polynomial factors, far under the rounding of the
+// result.  q is formed as ((alpha beta) / (alpha + beta)) AB2 with AB2 =
+// (dx dx + dy dy) + dz dz in correctly rounded steps and no fused operations,
+// on the host (bucket sizes) and on the device (records) alike, so both take
+// the same decisions.
+constexpr double PRIM_QMAX = 230.0;
+
+__host__ __device__ inline double prim_q(double al, double be, double dx, double dy, double dz)
+{
+#pragma clang fp contract(off)
+    const double AB2 = (dx * dx + dy * dy) + dz * dz;
+    return (al * be) / (al + be) * AB2;
+}
+
+// number of primitive pairs of shells a, b a screened plan keeps
+__host__ __device__ inline int prim_pairs_kept(const double *cen, const int *off, const double *exps, int a, int b)
+{
+    const double dx = cen[3 * a] - cen[3 * b], dy = cen[3 * a + 1] - cen[3 * b + 1], dz = cen[3 * a + 2] - cen[3 * b + 2];
+    int n = 0;
+    for (int ia = off[a]; ia < off[a + 1]; ++ia)
+        for (int ib = off[b]; ib < off[b + 1]; ++ib)
+            n += prim_q(exps[ia], exps[ib], dx, dy, dz) <= PRIM_QMAX ? 1 : 0;
+    return n > 0 ? n : 1;
+}
+
+// Primitive-pair records for every shell pair (the page's GAUSSIANPAIRS);
+// screened plans keep the primitive pairs prim_pairs_kept counts, in
+// (alpha, beta) order.
 __global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, const int *off,
-                            const double *exps, const double *cn, double *ppd)
+                            const double *exps, const double *cn, int screened, double *ppd)
 {
     const int p = blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= npairs) return;
@@ -164,12 +196,24 @@ __global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, co
     const double Bx = cen[3 * b], By = cen[3 * b + 1], Bz = cen[3 * b + 2];
     const double AB2 = (Ax - Bx) * (Ax - Bx) + (Ay - By) * (Ay - By) + (Az - Bz) * (Az - Bz);
     const int Ka = off[a + 1] - off[a], Kb = off[b + 1] - off[b];
+    // primitive pairs within the screen; a shell pair with none keeps its first
+    int within = 0;
+    if (screened)
+        for (int ia = 0; ia < Ka; ++ia)
+            for (int ib = 0; ib < Kb; ++ib)
+                within += prim_q(exps[off[a] + ia], exps[off[b] + ib], Ax - Bx, Ay - By, Az - Bz) <= PRIM_QMAX ? 1 : 0;
+    int n = 0;
     for (int ia = 0; ia < Ka; ++ia)
         for (int ib = 0; ib < Kb; ++ib) {
             const double al = exps[off[a] + ia], be = exps[off[b] + ib];
+            if (screened) {
+                const bool keep = within == 0 ? (ia == 0 && ib == 0)
+                                              : prim_q(al, be, Ax - Bx, Ay - By, Az - Bz) <= PRIM_QMAX;
+                if (!keep) continue;
+            }
             const double z = al + be, iz = 1.0 / z;
             const double Px = (al * Ax + be * Bx) * iz, Py = (al * Ay + be * By) * iz, Pz = (al * Az + be * Bz) * iz;
-            double *r = ppd + (size_t)(pi.z + ia * Kb + ib) * ERI_PP_STRIDE;
+            double *r = ppd + (size_t)(pi.z + n++) * ERI_PP_STRIDE;
             r[0] = z;
             r[1] = iz;
             r[2] = Px;
@@ -267,8 +311,10 @@ __global__ void k_set_z(int n, int4 *pinfo, const int *z)
     if (p < n) pinfo[p].z = z[p];
 }
 
-// All pairs i >= j, oriented so that l_a >= l_b (equal l: a = i).
-__global__ void k_all_pairs(int nshell, const int *l, const int *nprim, int4 *pinfo, uint64_t *pc_key, int *pidx)
+// All pairs i >= j, oriented so that l_a >= l_b (equal l: a = i), with the
+// primitive pairs a screened plan keeps.
+__global__ void k_all_pairs(int nshell, const int *l, const double *cen, const int *off, const double *exps,
+                            int4 *pinfo, uint64_t *pc_key, int *pidx)
 {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t np = (int64_t)nshell * (nshell + 1) / 2;
@@ -282,7 +328,7 @@ __global__ void k_all_pairs(int nshell, const int *l, const int *nprim, int4 *pi
         a = j;
         b = i;
     }
-    pinfo[p] = make_int4(a, b, 0, nprim[a] * nprim[b]);
+    pinfo[p] = make_int4(a, b, 0, prim_pairs_kept(cen, off, exps, a, b));
     pc_key[p] = (uint64_t)d_pair_class(l[a], l[b]);
     pidx[p] = (int)p;
 }
@@ -418,7 +464,8 @@ __global__ void k_zero_mat(int n, double *A, int lda)
 
 // chunk entries: (pair, offset of its contribution vector) for both sides of
 // every quartet; a quartet of two equal pairs has one side only
-__global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int *ekey, int64_t *eoff)
+__global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int none, int *ekey,
+                                int64_t *eoff)
 {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= m) return;
@@ -426,7 +473,7 @@ __global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab
     ekey[2 * s] = qbra[s];
     eoff[2 * s] = off;
     const bool two = qbra[s] != qket[s];
-    ekey[2 * s + 1] = two ? qket[s] : 0x7fffffff;  // sorts last, never read
+    ekey[2 * s + 1] = two ? qket[s] : none;  // sorts last, never read
     eoff[2 * s + 1] = two ? off + nab : -1;
 }
 
@@ -459,13 +506,13 @@ constexpr int RUN_THREADS = 256;
 __global__ void __launch_bounds__(RUN_THREADS) k_add_runs(const int *nruns, const int *key, const int *rstart,
                                                           const int *rlen, const int64_t *eoff, const double *cb,
                                                           const int4 *pinfo, const int *bf, const int *nfun_sh,
-                                                          double *J, int ldj)
+                                                          int none, double *J, int ldj)
 {
     __shared__ double part[RUN_THREADS];
     const int u = blockIdx.x;
     if (u >= *nruns) return;
     const int p = key[u];
-    if (p == 0x7fffffff) return;
+    if (p == none) return;
     const int4 pi = pinfo[p];
     const int na = nfun_sh[pi.x], nb = nfun_sh[pi.y], n = na * nb;
     const int64_t e0 = rstart[u], e1 = e0 + rlen[u];
@@ -544,7 +591,7 @@ __global__ void k_kchunk_entries(int m, const int *qbra, const int *qket, const 
     const int4 ib = pinfo[qbra[q]], ik = pinfo[qket[q]];
     const bool dij = ib.x != ib.y, dkl = ik.x != ik.y;
     const int64_t base = (int64_t)q * (na * nc + nb * nc + na * nd + nb * nd);
-    const int none = 0x7fffffff;
+    const int none = nshell * nshell;  // above every block key
     ekey[4 * q] = ib.x * nshell + ik.x;
     eoff[4 * q] = base;
     ekey[4 * q + 1] = dij ? ib.y * nshell + ik.x : none;
@@ -565,7 +612,7 @@ __global__ void __launch_bounds__(RUN_THREADS) k_add_runs_K(const int *nruns, co
     const int u = blockIdx.x;
     if (u >= *nruns) return;
     const int k = key[u];
-    if (k == 0x7fffffff) return;
+    if (k == nshell * nshell) return;
     const int s1 = k / nshell, s2 = k - s1 * nshell;
     const int n1 = nfun_sh[s1], n2 = nfun_sh[s2];
     const int64_t e0 = rstart[u], e1 = e0 + rlen[u];
@@ -1186,6 +1233,14 @@ struct ChunkLane {
     size_t tmp_bytes = 0;
 };
 
+// bits of the smallest radix that holds keys 0..maxkey
+inline int key_bits(int64_t maxkey)
+{
+    int b = 1;
+    while (b < 31 && (int64_t(1) << b) <= maxkey) ++b;
+    return b;
+}
+
 struct DigestShape {
     int lanes;
     int64_t CQ, CO, CB, NE;
@@ -1320,10 +1375,10 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
             slot_lists(P, B.start + c, m, &qb, &qk, ls, l);
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
             launch_class(P, B.cid, qb, qk, m, W.ints, ls, nk1);
-            // sort the n2 entries in W.ek/W.eo and encode their runs
-            auto sort_runs = [&](int n2) {
+            // sort the n2 entries in W.ek/W.eo (keys below 2^bits) and encode their runs
+            auto sort_runs = [&](int n2, int bits) {
                 size_t tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, 32, ls));
+                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, bits, ls));
                 tb = W.tmp_bytes;
                 HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
                 tb = W.tmp_bytes;
@@ -1334,14 +1389,14 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
                 hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, ls, nv, B.na, B.nb,
                                    B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb);
                 hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, nab, ncd,
-                                   W.ek, W.eo);
+                                   (int)P->npairs, W.ek, W.eo);
                 HIP_CHECK(hipGetLastError());
-                sort_runs((int)(2 * m));
+                sort_runs((int)(2 * m), key_bits(P->npairs));
                 // at most one run per pair key (and one for the sentinel key); workgroups
                 // past the device-side run count exit at once
                 const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
                 hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
-                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, Jl, ldl);
+                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, (int)P->npairs, Jl, ldl);
                 HIP_CHECK(hipGetLastError());
             }
             if (K) {
@@ -1351,7 +1406,7 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
                 hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, P->d_pinfo,
                                    P->nshell, B.na, B.nb, B.nc, B.nd, W.ek, W.eo);
                 HIP_CHECK(hipGetLastError());
-                sort_runs((int)(4 * m));
+                sort_runs((int)(4 * m), key_bits((int64_t)P->nshell * P->nshell));
                 // at most one run per target block key (and one for the sentinel key)
                 const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
                 hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk,
@@ -1464,7 +1519,7 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
         for (int j = 0; j <= i; ++j) {
             const int a = sh->l[i] >= sh->l[j] ? i : j, b = a == i ? j : i;
             const int pc = pair_class(sh->l[a], sh->l[b]);
-            const int64_t K = (int64_t)sh->nprim[a] * sh->nprim[b];
+            const int64_t K = prim_pairs_kept(sh->centers, sh->prim_off, sh->exps, a, b);
             H.nppd += K;
             keys.push_back(((uint64_t)pc << 16) | (uint64_t)K);
             pc_present[pc] = true;
@@ -1574,7 +1629,7 @@ void make_pair_data(eri_plan *P, const BuildHost &H, BuildBufs &X, hipStream_t s
     scan_i32(X.w, X.z, np, X.cub, H.cub, s);
     hipLaunchKernelGGL(k_set_z, dim3(nblk(np, 256)), dim3(256), 0, s, np, P->d_pinfo, X.z);
     hipLaunchKernelGGL(k_pair_data, dim3(nblk(np, 128)), dim3(128), 0, s, np, P->d_pinfo, P->d_cen, P->d_off,
-                       P->d_exps, P->d_cn, P->d_ppd);
+                       P->d_exps, P->d_cn, P->screened ? 1 : 0, P->d_ppd);
     HIP_CHECK(hipGetLastError());
 }
 
@@ -1626,7 +1681,8 @@ void build_screened(eri_plan *P, const BuildHost &H, BuildBufs &X, double tau, h
         throw HipFail{hipErrorInvalidValue};
     }
     P->npairs = np;
-    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_nprim, P->d_pinfo, X.pck,
+    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_cen, P->d_off, P->d_exps,
+                       P->d_pinfo, X.pck,
                        X.pidx);
     HIP_CHECK(hipGetLastError());
     make_pair_data(P, H, X, s);

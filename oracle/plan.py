@@ -23,6 +23,12 @@ rules independently):
   fl(S_p * S_q) >= fl(tau * tau).  Order: (class id, K_bra, K_ket, bra rank,
   ket rank).  The Schwarz factor itself is S_ij = max |(mu nu|mu nu)| over
   the (ij|ij) block (the caller supplies S).
+* primitive pairs of screened lists (a reading beyond the pages, which print
+  no such rule): a primitive pair (alpha, beta) of shells a, b is kept when
+  its Gaussian-product exponent q = alpha beta / (alpha + beta) |AB|^2 is at
+  most 230 (exp(-q) >= 1.3e-100); a shell pair with none keeps its first.
+  K_pair of a screened list counts the kept primitive pairs (``prim_pairs_kept``);
+  the oracle's integrals themselves always sum over every primitive pair.
 """
 from __future__ import annotations
 
@@ -103,8 +109,44 @@ def explicit_plan(l, nprim, quartets):
             "class": cls[order]}
 
 
-def pair_table(l, nprim, S):
-    """Pairs i >= j with orientation, bucket and in-bucket rank."""
+PRIM_QMAX = 230.0
+
+
+def prim_pairs_kept(centers, prim_off, exps, A, B):
+    """Kept primitive-pair counts of shell pairs (A[n], B[n]) (see the module
+    docstring): q is formed as ((alpha beta) / (alpha + beta)) AB2 with
+    AB2 = (dx dx + dy dy) + dz dz, every step a correctly rounded fp64
+    operation, so the decision at the threshold is reproducible."""
+    centers = np.asarray(centers, dtype=np.float64).reshape(-1, 3)
+    prim_off = np.asarray(prim_off, dtype=np.int64)
+    exps = np.asarray(exps, dtype=np.float64)
+    A = np.asarray(A, dtype=np.int64)
+    B = np.asarray(B, dtype=np.int64)
+    out = np.zeros(len(A), dtype=np.int64)
+    K = prim_off[1:] - prim_off[:-1]
+    kmax = int(K.max()) if len(K) else 1
+    # exponents padded per shell; padding never counts
+    E = np.full((len(K), kmax), np.nan)
+    for s_ in range(len(K)):
+        E[s_, :K[s_]] = exps[prim_off[s_]:prim_off[s_ + 1]]
+    step = 65536
+    for c in range(0, len(A), step):
+        a, b = A[c:c + step], B[c:c + step]
+        d = centers[a] - centers[b]
+        ab2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+        al = E[a][:, :, None]
+        be = E[b][:, None, :]
+        with np.errstate(invalid="ignore"):
+            q = (al * be) / (al + be) * ab2[:, None, None]
+            n = (q <= PRIM_QMAX).sum(axis=(1, 2))
+        out[c:c + step] = np.maximum(n, 1)
+    return out
+
+
+def pair_table(l, nprim, S, shells=None):
+    """Pairs i >= j with orientation, bucket and in-bucket rank.  K_pair is the
+    primitive-pair count nprim[a] nprim[b], or with ``shells`` (centers,
+    prim_off, exps) the kept count of a screened list."""
     l = np.asarray(l)
     nprim = np.asarray(nprim)
     ns = len(l)
@@ -114,6 +156,8 @@ def pair_table(l, nprim, S):
             a, b = (i, j) if l[i] >= l[j] else (j, i)
             pairs.append((i, j, a, b, pair_class(l[a], l[b]), int(nprim[a] * nprim[b])))
     P = np.array(pairs, dtype=np.int64).reshape(-1, 6)
+    if shells is not None and len(P):
+        P[:, 5] = prim_pairs_kept(shells.centers, shells.prim_off, shells.exps, P[:, 2], P[:, 3])
     S = np.asarray(S, dtype=np.float64)
     npair = len(P)
     pidx = np.arange(npair)
@@ -137,14 +181,14 @@ def pair_table(l, nprim, S):
     return {"pairs": P, "bucket": bucket, "rank": rank, "order": order}
 
 
-def screened_plan(l, nprim, S, tau):
+def screened_plan(l, nprim, S, tau, shells=None):
     """All unique quartets that pass fl(S_p S_q) >= fl(tau^2), in plan order.
 
     S is indexed by pair index i(i+1)/2 + j.  Returns dict(index_map[n,5],
     pair_bra[n], pair_ket[n], blocks, bucket, rank).  The perm bits are taken
     relative to the natural unique form (i >= j, k >= l, pair(ij) >= pair(kl)).
     """
-    pt = pair_table(l, nprim, S)
+    pt = pair_table(l, nprim, S, shells)
     P, bucket, rank = pt["pairs"], pt["bucket"], pt["rank"]
     S = np.asarray(S, dtype=np.float64)
     npair = len(P)
@@ -185,7 +229,7 @@ def screened_plan(l, nprim, S, tau):
             "bucket": bucket, "rank": rank}
 
 
-def screened_counts(l, nprim, S, tau):
+def screened_counts(l, nprim, S, tau, shells=None):
     """Counts of the screened plan without listing its quartets (for plans too
     large to enumerate).  Same rules as ``screened_plan``.
 
@@ -198,7 +242,7 @@ def screened_counts(l, nprim, S, tau):
     groups = [(class, K_bra, K_ket, B, Bk, start, counts[bra rank])] in plan
     order, pairs, bucket_members[b] = pair indices of bucket b in rank order).
     """
-    pt = pair_table(l, nprim, S)
+    pt = pair_table(l, nprim, S, shells)
     P, bucket, order = pt["pairs"], pt["bucket"], pt["order"]
     S = np.asarray(S, dtype=np.float64)
     t2 = np.float64(tau) * np.float64(tau)

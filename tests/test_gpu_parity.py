@@ -170,7 +170,7 @@ def test_c1_all_unique_cartesian(eri):
     assert plan.n_quartets == 666
     S_gpu = plan.schwarz().cpu().numpy()
     assert_schwarz(S_gpu, sh, False)
-    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, 0.0)
+    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, 0.0, shells=sh)
     np.testing.assert_array_equal(imap, twin["index_map"])
     assert [b[0] for b in twin["blocks"]] == list(plan.block_class)
     assert_parity(got, oracle_flat(sh, imap, False), "C1 integrals", sh, imap[:, :4], False)
@@ -249,7 +249,7 @@ def test_c3_reduced_plan_and_J(eri):
     plan, got, imap = run_plan(eri, sh, 1, None, w.tau)
     S_gpu = plan.schwarz().cpu().numpy()
     assert_schwarz(S_gpu, sh, True)
-    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau)
+    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau, shells=sh)
     np.testing.assert_array_equal(imap, twin["index_map"])
     flat = oracle_flat(sh, imap, True)
     assert_parity(got, flat, "C3 integrals", sh, imap[:, :4], True)
@@ -433,7 +433,7 @@ def test_c5_full_plan_counts_and_sampled_integrals(eri):
     plan = eri.build_quartets(sh, eri.ERI_SPHERICAL, None, w.tau)
     S = plan.schwarz().cpu().numpy()
     _log(f"  plan: {plan.n_quartets} quartets, {plan.n_blocks} blocks")
-    sc = oplan.screened_counts(sh.l, sh.nprim, S, w.tau)
+    sc = oplan.screened_counts(sh.l, sh.nprim, S, w.tau, shells=sh)
     assert plan.n_quartets == sc["n_quartets"]
     assert [(int(c), int(s), int(n)) for c, s, n in zip(plan.block_class, plan.block_start, plan.block_count)] == \
         [tuple(int(v) for v in b) for b in sc["blocks"]]
@@ -541,7 +541,7 @@ def test_c3_full_size_plan_and_sampled_J(eri):
     psel = rng.choice(len(pairs_all), 60, replace=False)
     assert_schwarz(S_gpu, sh, True)
     imap = plan.index_map().cpu().numpy()
-    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau)
+    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, w.tau, shells=sh)
     np.testing.assert_array_equal(imap, twin["index_map"])
     _log(f"  plan: {plan.n_quartets} quartets in {plan.n_blocks} class blocks")
     # unique quartets whose Schwarz product lies within 1e-9 (relative) of tau^2, where

@@ -52,3 +52,56 @@ def test_tau_zero_keeps_every_unique_quartet():
     npair = ns * (ns + 1) // 2
     sc = op.screened_counts(l, K, rng.uniform(0, 1, npair), 0.0)
     assert sc["n_quartets"] == npair * (npair + 1) // 2
+
+
+class _Sh:
+    def __init__(self, centers, exps_per_shell):
+        self.centers = np.asarray(centers, dtype=np.float64)
+        self.exps = np.concatenate([np.asarray(e, dtype=np.float64) for e in exps_per_shell])
+        self.prim_off = np.concatenate([[0], np.cumsum([len(e) for e in exps_per_shell])])
+
+
+def test_prim_pairs_kept_hand_cases():
+    """Kept counts worked out by hand: q = alpha beta / (alpha + beta) |AB|^2."""
+    sh = _Sh([[0, 0, 0], [10, 0, 0], [100, 0, 0], [15, 2, 1], [15, 2, 1]],
+             [[1.0, 10.0], [1.0, 100.0], [1.0], [2.0], [2.0000001]])
+    # |AB|^2 = 100: q(1,1) = 50, q(1,100) = 99.0, q(10,1) = 90.9 kept; q(10,100) = 909 dropped
+    # |AB|^2 = 1e4 with (1, 1): q = 5,000 for every pair -> none within, the first pair is kept
+    # the same shell twice: |AB|^2 = 0, all K^2 pairs kept
+    # |AB|^2 = 225 + 4 + 1 = 230 exactly and alpha = beta = 2: q = 230 exactly, kept;
+    # a hair larger exponent puts q above 230
+    got = op.prim_pairs_kept(sh.centers, sh.prim_off, sh.exps, [0, 2, 1, 3, 4], [1, 0, 1, 0, 0])
+    np.testing.assert_array_equal(got, [3, 1, 4, 1, 1])
+    s2 = _Sh([[0, 0, 0], [15, 2, 1]], [[2.0], [2.0]])
+    assert op.prim_pairs_kept(s2.centers, s2.prim_off, s2.exps, [1], [0])[0] == 1
+    s3 = _Sh([[0, 0, 0], [15, 2, 1]], [[2.0, 2.0000001], [2.0, 2.0000001]])
+    # pairs (2, 2) -> q = 230 kept; any pair with 2.0000001 lies above
+    assert op.prim_pairs_kept(s3.centers, s3.prim_off, s3.exps, [1], [0])[0] == 1
+    s4 = _Sh([[0, 0, 0], [15, 2, 1]], [[2.0, 1.0], [2.0, 1.0]])
+    # (2,2): 230 kept; (2,1) and (1,2): 2/3 * 230 kept; (1,1): 115 kept
+    assert op.prim_pairs_kept(s4.centers, s4.prim_off, s4.exps, [1], [0])[0] == 4
+
+
+def test_kept_counts_order_the_buckets():
+    """With shells given, a pair's K is its kept count: two pairs of the same
+    class and shell contraction degrees land in different buckets when one of
+    them is far apart."""
+    cen = [[0, 0, 0], [0, 0, 1], [0, 0, 50]]
+    sh = _Sh(cen, [[1.0, 4.0], [1.0, 4.0], [1.0, 4.0]])
+    l = np.zeros(3, dtype=int)
+    K = np.full(3, 2)
+    S = np.ones(6)
+    pt_all = op.pair_table(l, K, S)
+    pt = op.pair_table(l, K, S, shells=sh)
+    assert set(pt_all["pairs"][:, 5]) == {4}
+    kept = {(int(a), int(b)): int(k) for a, b, k in pt["pairs"][:, [2, 3, 5]]}
+    # |AB|^2 = 1: every q <= 2; |AB|^2 = 2,500 or 2,401: q >= 1,200, none kept -> 1
+    assert kept[(1, 0)] == 4 and kept[(0, 0)] == 4 and kept[(2, 2)] == 4
+    assert kept[(2, 0)] == 1 and kept[(2, 1)] == 1
+    full = op.screened_plan(l, K, S, 0.0, shells=sh)
+    sc = op.screened_counts(l, K, S, 0.0, shells=sh)
+    # one class block, ordered by (K_bra, K_ket): the far pairs (K = 1) lead
+    kk = [(kept[tuple(sorted(r[:2], reverse=True))], kept[tuple(sorted(r[2:4], reverse=True))])
+          for r in full["index_map"]]
+    assert kk == sorted(kk) and kk[0] == (1, 1) and kk[-1] == (4, 4)
+    np.testing.assert_array_equal(op.screened_decode(sc, np.arange(sc["n_quartets"])), full["index_map"])

@@ -397,7 +397,49 @@ def K_blocks(sh, spherical: bool, pairs, D, S, tau):
     return out
 
 
-def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, normalize_: bool = True):
+def _intermediate_magnitudes(sh, a, b, c, d, normalize_: bool, per_primitive: bool):
+    """{(e, f): magnitude} of the contracted intermediates [e0|f0] of quartet
+    (a b|c d), |e| in [l_a, l_a+l_b], |f| in [l_c, l_c+l_d]: |[e0|f0]|, or with
+    per_primitive the sum over the primitive quartets of |their term|."""
+    import itertools
+    from workloads.configs import _pack
+    la, lb, lc, ld = (int(sh.l[s]) for s in (a, b, c, d))
+    prim = []
+    for s, l in ((a, la), (b, lb), (c, lc), (d, ld)):
+        e = sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]
+        raw = sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]]
+        prim.append((np.asarray(e, dtype=float), normalize(l, e, raw) if normalize_ else np.asarray(raw, dtype=float)))
+    cen = [sh.centers[s] for s in (a, b, c, d)]
+    V = {}
+    for le in range(la, la + lb + 1):
+        for lf in range(lc, lc + ld + 1):
+            if not per_primitive:
+                s2 = _pack(cen, [le, 0, lf, 0], [len(p[0]) for p in prim], [p[0] for p in prim], [p[1] for p in prim])
+                mag = np.abs(eri_block(s2, [0, 1, 2, 3], False, normalize_=False)[:, 0, :, 0])
+            else:
+                # one shell per primitive; every primitive quartet as its own quartet
+                C, L, E, CF, first = [], [], [], [], []
+                for t, ((e, co), l) in enumerate(zip(prim, (le, 0, lf, 0))):
+                    first.append(len(L))
+                    for x in range(len(e)):
+                        C.append(cen[t])
+                        L.append(l)
+                        E.append(e[x:x + 1])
+                        CF.append(co[x:x + 1])
+                s2 = _pack(np.array(C), L, [1] * len(L), E, CF)
+                qs = [[first[0] + i, first[1] + j, first[2] + k, first[3] + m]
+                      for i, j, k, m in itertools.product(*[range(len(p[0])) for p in prim])]
+                flat, _ = eri(s2, qs, False, normalize_=False)
+                n1, n2 = len(cart_components(le)), len(cart_components(lf))
+                mag = np.abs(flat.reshape(len(qs), n1, n2)).sum(axis=0)
+            for i, e_ in enumerate(cart_components(le)):
+                for j, f_ in enumerate(cart_components(lf)):
+                    V[(e_, f_)] = mag[i, j]
+    return V
+
+
+def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, normalize_: bool = True,
+                       per_primitive: bool = False):
     """First-order fp64 error floor of the two-phase (VRR + HRR) evaluation.
 
     The two-phase method holds the contracted intermediates
@@ -414,28 +456,16 @@ def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, n
     exceed 1e-10 of the result.  The intermediates are computed here by the
     oracle's own four-index recurrence on raw primitives, weighted by the
     normalised contraction coefficients, or by the raw ones with
-    normalize_=False (for quartets evaluated with raw coefficients).
+    normalize_=False (for quartets evaluated with raw coefficients).  With
+    per_primitive, |[a+k 0|c+k' 0]| is replaced by the sum over the primitive
+    quartets of the magnitudes of their terms (see contraction_rounding_bound).
     """
     from math import comb
     q = np.asarray(quartets).reshape(-1, 4)
     out = []
     for a, b, c, d in q:
         la, lb, lc, ld = (int(sh.l[s]) for s in (a, b, c, d))
-        prim = []
-        for s, l in ((a, la), (b, lb), (c, lc), (d, ld)):
-            e = sh.exps[sh.prim_off[s]:sh.prim_off[s + 1]]
-            raw = sh.coefs[sh.prim_off[s]:sh.prim_off[s + 1]]
-            prim.append((e, normalize(l, e, raw) if normalize_ else np.asarray(raw, dtype=float)))
-        cen = [sh.centers[s] for s in (a, b, c, d)]
-        V = {}
-        for le in range(la, la + lb + 1):
-            for lf in range(lc, lc + ld + 1):
-                from workloads.configs import _pack
-                s2 = _pack(cen, [le, 0, lf, 0], [len(p[0]) for p in prim], [p[0] for p in prim], [p[1] for p in prim])
-                blk = eri_block(s2, [0, 1, 2, 3], False, normalize_=False)[:, 0, :, 0]
-                for i, e_ in enumerate(cart_components(le)):
-                    for j, f_ in enumerate(cart_components(lf)):
-                        V[(e_, f_)] = abs(blk[i, j])
+        V = _intermediate_magnitudes(sh, a, b, c, d, normalize_, per_primitive)
         AB = np.abs(sh.centers[a] - sh.centers[b])
         CD = np.abs(sh.centers[c] - sh.centers[d])
 
@@ -466,6 +496,30 @@ def hgp_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53, n
             for pos, l in enumerate((la, lb, lc, ld)):
                 bound = np.moveaxis(np.tensordot(np.abs(sph_coeffs(l)), np.moveaxis(bound, pos, 0), axes=(1, 0)), 0, pos)
         out.append(bound.ravel())
+    return np.concatenate(out) if out else np.zeros(0)
+
+
+def contraction_rounding_bound(sh, quartets, spherical: bool, eps: float = 2.0 ** -53):
+    """Floor for the rounding of the contraction sums of the two-phase method.
+
+    Each contracted intermediate [e0|f0] is a sum of K4 = K_a K_b K_c K_d
+    primitive terms accumulated in fp64.  The worst-case bound on the rounding
+    of such a sum grows as (K4 - 1) eps sum |term|; the probabilistic analysis
+    of Higham and Mary ("A new approach to probabilistic rounding error
+    analysis", SIAM J. Sci. Comput. 41, 2019) shows that with independent
+    rounding errors it grows as lambda sqrt(K4 - 1) eps sum |term|, lambda a
+    small constant that sets the confidence.  This returns, per element,
+    sqrt(K4 - 1) times hgp_rounding_bound with the per-primitive magnitudes
+    (that bound at lambda = 1, propagated through the unrolled horizontal
+    recurrence); the caller chooses lambda.  Zero for K4 = 1."""
+    q = np.asarray(quartets).reshape(-1, 4)
+    out = []
+    for row in q:
+        k4 = int(np.prod([int(sh.prim_off[s + 1] - sh.prim_off[s]) for s in row]))
+        if k4 <= 1:
+            out.append(np.zeros(int(block_sizes(sh, row[None, :], spherical)[0])))
+            continue
+        out.append(np.sqrt(k4 - 1.0) * hgp_rounding_bound(sh, row[None, :], spherical, eps, per_primitive=True))
     return np.concatenate(out) if out else np.zeros(0)
 
 

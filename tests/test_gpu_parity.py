@@ -2,13 +2,15 @@
 
 Bar (fp64), element by element:
     |gpu - oracle| <= max(1e-10 |oracle|, 1e-13, 4 * B)
-where B is the oracle's first-order fp64 error floor of the two-phase method
-(oracle.hgp_rounding_bound: rounding the contracted [e0|f0] intermediates to
-fp64, propagated through the unrolled horizontal recurrence).  B only matters
-for diffuse high-l quartets far apart, where that floor exceeds 1e-10 of the
-result; it is computed only for quartets that miss the first two terms.  The
-factor 4 is what the binary128 adjudication of tests/test_oracle_quad.py
-supports.  Every check records how many elements needed the floor, and the
+where B is the oracle's first-order fp64 error floor of the two-phase method:
+rounding the contracted [e0|f0] intermediates to fp64, propagated through the
+unrolled horizontal recurrence (oracle.hgp_rounding_bound), plus the rounding
+of their contraction sums over K4 primitive quartets, sqrt(K4 - 1) eps
+sum |term| propagated the same way (oracle.contraction_rounding_bound; zero
+at K4 = 1).  B only matters for diffuse high-l quartets far apart, where that
+floor exceeds 1e-10 of the result; it is computed only for quartets that miss
+the first two terms.  The factor 4 is what the binary128 adjudication of
+tests/test_oracle_quad.py supports.  Every check records how many elements needed the floor, and the
 largest |gpu - oracle| / B among them, in gpurun_out/parity_floor_usage.jsonl.
 Plans (index maps) are bit-exact against the oracle's plan twin fed the GPU's
 Schwarz factors.
@@ -64,7 +66,8 @@ def assert_parity(got, ref, what="", sh=None, quartets=None, spherical=None):
         offs = np.concatenate([[0], np.cumsum(sizes)])
         qbad = np.unique(np.searchsorted(offs, np.nonzero(bad)[0], side="right") - 1)
         for x in qbad:
-            B = oracle.hgp_rounding_bound(sh, q[x:x + 1], spherical)
+            B = oracle.hgp_rounding_bound(sh, q[x:x + 1], spherical) + \
+                oracle.contraction_rounding_bound(sh, q[x:x + 1], spherical)
             sl = slice(offs[x], offs[x + 1])
             newtol = np.maximum(tol[sl], HGP_FLOOR_FACTOR * B)
             m = err[sl] > tol[sl]
@@ -230,6 +233,69 @@ def test_single_quartet_and_long_contractions(eri):
         plan, got, imap = run_plan(eri, sh, 1 if spherical else 0, [[0, 1, 2, 3]])
         assert plan.n_quartets == 1
         assert_parity(got, oracle_flat(sh, imap, spherical), "single quartet", sh, imap[:, :4], spherical)
+
+
+def test_long_contractions_f_and_g_classes(eri):
+    """f and g classes at contraction degree 5-8 (K4 of 300-2,700 primitive
+    quartets), so the contracted kernels run their primitive-chunk loops many
+    times: (ff|ff), (gf|dd), (gg|ps), (fd|dp), (dd|dd) and (gg|dd), two
+    orientations each, both output kinds, against the oracle in full."""
+    _log("case: f/g classes with K = 5-8, explicit list, both output kinds")
+    rng = np.random.default_rng(31)
+    ls = [3, 3, 4, 4, 2, 2, 1, 0, 4]
+    ks = [6, 7, 6, 8, 8, 6, 7, 8, 5]
+    sh = _pack(rng.uniform(0, 2.5, (len(ls), 3)), ls, ks,
+               [np.exp(rng.uniform(np.log(0.1), np.log(50), k)) for k in ks], [rng.uniform(0.1, 1, k) for k in ks])
+    q = [[0, 1, 0, 1], [1, 0, 0, 1], [2, 0, 4, 5], [3, 1, 5, 4], [3, 2, 6, 7], [2, 3, 7, 6],
+         [0, 4, 5, 6], [1, 5, 4, 6], [4, 5, 4, 5], [5, 4, 5, 4], [8, 2, 4, 5], [2, 8, 5, 4]]
+    for spherical in (True, False):
+        plan, got, imap = run_plan(eri, sh, 1 if spherical else 0, q)
+        assert plan.n_quartets == len(q)
+        assert_parity(got, oracle_flat(sh, imap, spherical), "long contractions f/g", sh, imap[:, :4], spherical)
+
+
+def test_screened_plan_with_dropped_primitive_pairs(eri):
+    """Three atoms 3-4 bohr apart with s, p, d shells of contraction degree 4-6
+    and exponents from 0.05 to 1e4: many primitive pairs of the shell pairs
+    across atoms lie beyond the primitive-pair screen. Every unique quartet
+    (tau = 0) is compared with the oracle, which sums every primitive pair, and
+    so is J; the plan equals the twin built from the kept counts."""
+    import torch
+    _log("case: screened plan with dropped primitive pairs, tau=0, spherical, plan + J")
+    rng = np.random.default_rng(32)
+    atoms = np.array([[0, 0, 0], [3.0, 0.5, 0], [0.5, 4.0, 1.0]])
+    ls, ks, cen = [], [], []
+    for a in range(3):
+        for l, k in ((0, 6), (1, 5), (2, 4)):
+            ls.append(l)
+            ks.append(k)
+            cen.append(atoms[a])
+    sh = _pack(np.array(cen), ls, ks, [np.exp(rng.uniform(np.log(0.05), np.log(1e4), k)) for k in ks],
+               [rng.uniform(0.1, 1, k) for k in ks])
+    ns = len(ls)
+    i, j = np.tril_indices(ns)
+    kept = oplan.prim_pairs_kept(sh.centers, sh.prim_off, sh.exps, i, j)
+    full = np.asarray(ks)[i] * np.asarray(ks)[j]
+    assert (kept < full).sum() >= 10 and (kept == full).sum() >= 10
+    plan, got, imap = run_plan(eri, sh, 1, None, 0.0)
+    S_gpu = plan.schwarz().cpu().numpy()
+    assert_schwarz(S_gpu, sh, True)
+    twin = oplan.screened_plan(sh.l, sh.nprim, S_gpu, 0.0, shells=sh)
+    np.testing.assert_array_equal(imap, twin["index_map"])
+    npair = ns * (ns + 1) // 2
+    assert plan.n_quartets == npair * (npair + 1) // 2
+    flat = oracle_flat(sh, imap, True)
+    assert_parity(got, flat, "screened plan, dropped primitive pairs", sh, imap[:, :4], True)
+    nb = int(oracle.basis_offsets(sh, True)[-1])
+    C = rng.standard_normal((nb, nb // 2))
+    Dn = C @ C.T
+    D = torch.tensor(Dn, device="cuda")
+    J = torch.empty_like(D)
+    eri.digest_J(plan, D, J)
+    torch.cuda.synchronize()
+    _, off = oracle.eri(sh, imap[:, :4], True)
+    Jref = oracle.J_from_quartets(sh, True, imap[:, :4], flat, off, Dn)
+    assert_J_parity(J.cpu().numpy(), Jref, sh, True, Dn, S_gpu, 0.0, "J, dropped primitive pairs")
 
 
 def test_unnormalised_flag(eri):

@@ -145,3 +145,36 @@ def test_two_phase_fp64_needs_the_floor_and_stays_within_it():
             worst = max(worst, f)
             assert f <= FLOOR_FACTOR, (q, f)
     print(f"largest err/B over missed elements: {worst:.2f}")
+
+
+def _long_contraction():
+    import os
+    from types import SimpleNamespace
+    fx = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "long_contraction_quad.npz"))
+    sh = SimpleNamespace(**{k: fx[k] for k in ("centers", "l", "nprim", "prim_off", "exps", "coefs")})
+    return sh, [int(s) for s in fx["quartet"]], fx["quad"]
+
+
+def test_long_contraction_needs_the_contraction_floor():
+    """A (gf|dd) quartet contracted over 2,688 primitive quartets (binary128
+    values from tests/golden/make_long_contraction_quad.py): the fp64 oracle
+    matches them to 1e-2 of the bar; the emulated fp64 two-phase method misses
+    the bar on dozens of elements and by more than FLOOR_FACTOR x B on some, the
+    rounding of its contraction sums that B does not count; adding the
+    contraction floor C (sqrt(K4 - 1) eps sum |term|, propagated) brings every
+    miss within (B + C), a quarter of the GPU bar FLOOR_FACTOR x (B + C)."""
+    sh, q, x = _long_contraction()
+    a = oracle.eri_block(sh, q, True).ravel()
+    assert np.max(np.abs(a - x) / _bar(x)) <= 1e-2
+    em = _emulated(sh, q)
+    err = np.abs(em - x)
+    miss = err > _bar(x)
+    assert miss.sum() >= 10
+    B = oracle.hgp_rounding_bound(sh, [q], True)
+    C = oracle.contraction_rounding_bound(sh, [q], True)
+    assert np.max(err[miss] / B[miss]) > FLOOR_FACTOR
+    assert np.max(err[miss] / (B + C)[miss]) <= 1.0
+    # C is the per-primitive floor times sqrt(K4 - 1); K4 = 8 * 7 * 6 * 8
+    P = oracle.hgp_rounding_bound(sh, [q], True, per_primitive=True)
+    np.testing.assert_allclose(C, np.sqrt(2688 - 1) * P, rtol=1e-14)
+    assert np.all(P >= B * (1 - 1e-12))

@@ -735,12 +735,15 @@ __global__ void k_slot_offsets(int64_t n, int nb, const int64_t *bstart, const i
     off[x] = bout[lo] + (x - bstart[lo]) * bsize[lo];
 }
 
-// one workgroup per quartet: its 12 Cartesian derivative blocks into dst + dst_off[t]
-__global__ void k_deriv_combine(int64_t n, const int *rows, const int *lsh, const int64_t *aux_slot_of,
-                                const int *aux_qmap, const int *aux_l, const int64_t *aux_off, const double *aux,
-                                const int64_t *dst_off, double *dst)
+// tpi threads per quartet (a power of two dividing the 256 of a workgroup): its
+// 12 Cartesian derivative blocks into dst + dst_off[t]
+__global__ void __launch_bounds__(256) k_deriv_combine(int64_t n, int tpi, const int *rows, const int *lsh,
+                                                       const int64_t *aux_slot_of, const int *aux_qmap,
+                                                       const int *aux_l, const int64_t *aux_off, const double *aux,
+                                                       const int64_t *dst_off, double *dst)
 {
-    const int64_t t = blockIdx.x;
+    const int64_t t = (int64_t)blockIdx.x * (256 / tpi) + threadIdx.x / tpi;
+    const int lane = threadIdx.x % tpi;
     if (t >= n) return;
     int l4[4], n4[4];
     for (int k = 0; k < 4; ++k) {
@@ -748,7 +751,7 @@ __global__ void k_deriv_combine(int64_t n, const int *rows, const int *lsh, cons
         n4[k] = dv_ncart(l4[k]);
     }
     const int ncar = n4[0] * n4[1] * n4[2] * n4[3];
-    for (int idx = threadIdx.x; idx < 12 * ncar; idx += blockDim.x) {
+    for (int idx = lane; idx < 12 * ncar; idx += tpi) {
         const int comp = idx / ncar, e = idx - comp * ncar;
         const int p = comp / 3, ax = comp - 3 * p;
         int ci[4], r = e;
@@ -788,17 +791,23 @@ __global__ void k_deriv_combine(int64_t n, const int *rows, const int *lsh, cons
     }
 }
 
-// one workgroup per (quartet, derivative component): t^(l) on the four indices,
-// ping-pong between the Cartesian block and a scratch block, last pass into dst
-__global__ void k_deriv_sph(int64_t n, const int *rows, const int *lsh, double *cart, double *tmp,
-                            const int64_t *cart_off, const int64_t *dst_off, double *dst)
+// tpi threads per (quartet, derivative component) item (a power of two
+// dividing the 256 of a workgroup): t^(l) on the four indices, ping-pong
+// between the Cartesian block and a scratch block, last pass into dst.  Every
+// thread of the workgroup takes part in its barriers; threads past the last
+// item only wait.
+__global__ void __launch_bounds__(256) k_deriv_sph(int64_t n, int tpi, const int *rows, const int *lsh, double *cart,
+                                                   double *tmp, const int64_t *cart_off, const int64_t *dst_off,
+                                                   double *dst)
 {
-    const int64_t t = blockIdx.x / 12;
-    const int comp = blockIdx.x - (int)(t * 12);
-    if (t >= n) return;
+    const int64_t u = (int64_t)blockIdx.x * (256 / tpi) + threadIdx.x / tpi;
+    const int lane = threadIdx.x % tpi;
+    const bool live = u < 12 * n;
+    const int64_t t = live ? u / 12 : 0;
+    const int comp = live ? (int)(u - t * 12) : 0;
     int l4[4], dims[4], ns[4];
     for (int k = 0; k < 4; ++k) {
-        l4[k] = lsh[rows[5 * t + k]];
+        l4[k] = live ? lsh[rows[5 * t + k]] : 0;
         dims[k] = dv_ncart(l4[k]);
         ns[k] = dv_nsph(l4[k]);
     }
@@ -814,8 +823,8 @@ __global__ void k_deriv_sph(int64_t n, const int *rows, const int *lsh, double *
         const int nc = dims[pos], nsv = ns[pos];
         const double *in = (pos % 2 == 0) ? a : b;
         double *o = pos == 3 ? dst + dst_off[t] + (int64_t)comp * nsp : ((pos % 2 == 0) ? b : a);
-        const int total = before * nsv * after;
-        for (int x = threadIdx.x; x < total; x += blockDim.x) {
+        const int total = live ? before * nsv * after : 0;
+        for (int x = lane; x < total; x += tpi) {
             const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
             double acc = 0.0;
             for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
@@ -1088,8 +1097,8 @@ __global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const d
         const double *T = eri_sph_T[l4[pos]];
         const int nc = dims[pos], nsv = ns[pos];
         double *o = pos == 3 ? dst + t * nsp : ((pos % 2 == 0) ? w0 : w1) + t * ncar;
-        const int total = before * nsv * after;
-        for (int x = threadIdx.x; x < total; x += blockDim.x) {
+        const int total = live ? before * nsv * after : 0;
+        for (int x = lane; x < total; x += tpi) {
             const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
             double acc = 0.0;
             for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];
@@ -2408,14 +2417,29 @@ extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count
         HIP_CHECK(hipGetLastError());
         upload(X.off, H.dst_off.data(), count, s);
         upload(X.off + count, H.cart_off.data(), count, s);
+        // threads per item: the smallest power of two (at most 256) covering the
+        // largest Cartesian block of the call, so that small classes share a workgroup
+        int64_t max_ncar = 1;
+        for (int64_t t = 0; t < count; ++t) {
+            int64_t nc = 1;
+            for (int k = 0; k < 4; ++k) nc *= ncart(P->hl[H.rows[5 * t + k]]);
+            max_ncar = std::max(max_ncar, nc);
+        }
+        auto tpi_for = [](int64_t work) {
+            int v = 1;
+            while (v < 256 && v < work) v *= 2;
+            return v;
+        };
+        const int tpc = tpi_for(12 * max_ncar), tps = tpi_for(max_ncar);
+        const int64_t nwc = (count + 256 / tpc - 1) / (256 / tpc), nws = (12 * count + 256 / tps - 1) / (256 / tps);
         if (!P->sph) {
-            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, X.rows, P->d_l,
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)nwc), dim3(256), 0, s, count, tpc, X.rows, P->d_l,
                                X.slot_of, Ap->d_qmap, Ap->d_l, X.aux_off, X.aux, X.off, out);
         } else {
-            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)count), dim3(256), 0, s, count, X.rows, P->d_l,
+            hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)nwc), dim3(256), 0, s, count, tpc, X.rows, P->d_l,
                                X.slot_of, Ap->d_qmap, Ap->d_l, X.aux_off, X.aux, X.off + count, X.cart);
             HIP_CHECK(hipGetLastError());
-            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)(12 * count)), dim3(256), 0, s, count, X.rows, P->d_l,
+            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)nws), dim3(256), 0, s, count, tps, X.rows, P->d_l,
                                X.cart, X.tmp, X.off + count, X.off, out);
         }
         HIP_CHECK(hipGetLastError());

@@ -172,7 +172,7 @@ __host__ __device__ inline double prim_q(double al, double be, double dx, double
 }
 
 // number of primitive pairs of shells a, b a screened plan keeps
-__host__ __device__ inline int prim_pairs_kept(const double *cen, const int *off, const double *exps, int a, int b)
+inline int prim_pairs_kept(const double *cen, const int *off, const double *exps, int a, int b)
 {
     const double dx = cen[3 * a] - cen[3 * b], dy = cen[3 * a + 1] - cen[3 * b + 1], dz = cen[3 * a + 2] - cen[3 * b + 2];
     int n = 0;
@@ -211,6 +211,7 @@ __global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, co
                                               : prim_q(al, be, Ax - Bx, Ay - By, Az - Bz) <= PRIM_QMAX;
                 if (!keep) continue;
             }
+            if (n >= pi.w) continue;  // never past the records the plan reserved for this pair
             const double z = al + be, iz = 1.0 / z;
             const double Px = (al * Ax + be * Bx) * iz, Py = (al * Ay + be * By) * iz, Pz = (al * Az + be * Bz) * iz;
             double *r = ppd + (size_t)(pi.z + n++) * ERI_PP_STRIDE;
@@ -226,6 +227,14 @@ __global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, co
             r[8] = cn[off[a] + ia] * cn[off[b] + ib] * exp(-al * be * iz * AB2) * iz;
             r[9] = 0.0;
         }
+    // The host counted the same kept pairs with the same arithmetic, so n equals
+    // pi.w; should it fall short, the missing records repeat the first with
+    // zero weight instead of being left unwritten.
+    const double *r0 = ppd + (size_t)pi.z * ERI_PP_STRIDE;
+    for (; n > 0 && n < pi.w; ++n) {
+        double *r = ppd + (size_t)(pi.z + n) * ERI_PP_STRIDE;
+        for (int f = 0; f < ERI_PP_STRIDE; ++f) r[f] = f == 8 ? 0.0 : r0[f];
+    }
 }
 
 __device__ inline void canonical4(const int *l, int &i, int &j, int &k, int &m, int &perm)
@@ -312,9 +321,8 @@ __global__ void k_set_z(int n, int4 *pinfo, const int *z)
 }
 
 // All pairs i >= j, oriented so that l_a >= l_b (equal l: a = i), with the
-// primitive pairs a screened plan keeps.
-__global__ void k_all_pairs(int nshell, const int *l, const double *cen, const int *off, const double *exps,
-                            int4 *pinfo, uint64_t *pc_key, int *pidx)
+// primitive pairs a screened plan keeps (counted on the host, kept[p]).
+__global__ void k_all_pairs(int nshell, const int *l, const int *kept, int4 *pinfo, uint64_t *pc_key, int *pidx)
 {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t np = (int64_t)nshell * (nshell + 1) / 2;
@@ -328,7 +336,7 @@ __global__ void k_all_pairs(int nshell, const int *l, const double *cen, const i
         a = j;
         b = i;
     }
-    pinfo[p] = make_int4(a, b, 0, prim_pairs_kept(cen, off, exps, a, b));
+    pinfo[p] = make_int4(a, b, 0, kept[p]);
     pc_key[p] = (uint64_t)d_pair_class(l[a], l[b]);
     pidx[p] = (int)p;
 }
@@ -1455,6 +1463,7 @@ struct BuildHost {
     int64_t chunk_q = 0;
     size_t cub = 0;
     std::vector<int> hbf, hnf;
+    std::vector<int> kept;  // screened: kept primitive pairs of pair p = i(i+1)/2 + j
 };
 
 struct BuildBufs {
@@ -1529,6 +1538,7 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
             const int a = sh->l[i] >= sh->l[j] ? i : j, b = a == i ? j : i;
             const int pc = pair_class(sh->l[a], sh->l[b]);
             const int64_t K = prim_pairs_kept(sh->centers, sh->prim_off, sh->exps, a, b);
+            H.kept.push_back((int)K);
             H.nppd += K;
             keys.push_back(((uint64_t)pc << 16) | (uint64_t)K);
             pc_present[pc] = true;
@@ -1690,8 +1700,9 @@ void build_screened(eri_plan *P, const BuildHost &H, BuildBufs &X, double tau, h
         throw HipFail{hipErrorInvalidValue};
     }
     P->npairs = np;
-    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, P->d_cen, P->d_off, P->d_exps,
-                       P->d_pinfo, X.pck,
+    // the host's kept counts, so that buckets and record offsets follow the sizes it reserved
+    upload(X.w, H.kept.data(), (size_t)np, s);
+    hipLaunchKernelGGL(k_all_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, ns, P->d_l, X.w, P->d_pinfo, X.pck,
                        X.pidx);
     HIP_CHECK(hipGetLastError());
     make_pair_data(P, H, X, s);

@@ -1027,8 +1027,9 @@ long long scratch_need(const std::vector<int> &cids, bool ksph)
 }
 
 #ifdef ERI_UNFUSED_SPHERICAL
-// work buffer of the unfused path (three Cartesian chunks), doubles
-constexpr int64_t UNFUSED_DOUBLES = int64_t(3) << 22;
+// work buffer of the unfused path (three Cartesian chunks, 800 MB: a few hundred
+// (gg|gg) quartets per chunk, so that its class launches are not tiny), doubles
+constexpr int64_t UNFUSED_DOUBLES = int64_t(3) << 25;
 #endif
 
 void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, const int *qket, int64_t n, double *out,
@@ -1105,8 +1106,8 @@ __global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const d
         const double *T = eri_sph_T[l4[pos]];
         const int nc = dims[pos], nsv = ns[pos];
         double *o = pos == 3 ? dst + t * nsp : ((pos % 2 == 0) ? w0 : w1) + t * ncar;
-        const int total = live ? before * nsv * after : 0;
-        for (int x = lane; x < total; x += tpi) {
+        const int total = before * nsv * after;
+        for (int x = threadIdx.x; x < total; x += blockDim.x) {
             const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
             double acc = 0.0;
             for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[((int64_t)bb * nc + c) * after + y];

@@ -3,8 +3,9 @@
 The parity bar of the GPU tests is, per element,
     max(1e-10 |oracle|, 1e-13, FLOOR_FACTOR * B)
 with B the oracle's first-order floor of the two-phase method
-(oracle.hgp_rounding_bound, plus oracle.contraction_rounding_bound for the
-contraction sums).  FLOOR_FACTOR = 4 is the factor the binary128
+(oracle.hgp_rounding_bound; for integrals plus a quarter of
+oracle.contraction_rounding_bound, the contraction sums' floor, so that the
+bar is 4 B + C).  FLOOR_FACTOR = 4 is the factor the binary128
 adjudication supports (tests/test_oracle_quad.py: the emulated fp64 method
 needs at most 3.2 x B on the hardest quartets).  Every parity check appends one
 JSON line to gpurun_out/parity_floor_usage.jsonl: the test, the check, the

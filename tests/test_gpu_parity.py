@@ -1,16 +1,16 @@
 """GPU parity: the HIP library through its C ABI against the CPU oracle.
 
 Bar (fp64), element by element:
-    |gpu - oracle| <= max(1e-10 |oracle|, 1e-13, 4 * B)
+    |gpu - oracle| <= max(1e-10 |oracle|, 1e-13, 4 * B + C)
 where B is the oracle's first-order fp64 error floor of the two-phase method:
 rounding the contracted [e0|f0] intermediates to fp64, propagated through the
-unrolled horizontal recurrence (oracle.hgp_rounding_bound), plus the rounding
+unrolled horizontal recurrence (oracle.hgp_rounding_bound), and C the rounding
 of their contraction sums over K4 primitive quartets, sqrt(K4 - 1) eps
 sum |term| propagated the same way (oracle.contraction_rounding_bound; zero
-at K4 = 1).  B only matters for diffuse high-l quartets far apart, where that
-floor exceeds 1e-10 of the result; it is computed only for quartets that miss
-the first two terms.  The factor 4 is what the binary128 adjudication of
-tests/test_oracle_quad.py supports.  Every check records how many elements needed the floor, and the
+at K4 = 1).  The floor only matters for diffuse high-l quartets far apart,
+where it exceeds 1e-10 of the result; it is computed only for quartets that
+miss the first two terms.  The factor 4 and C are what the binary128
+adjudication of tests/test_oracle_quad.py supports.  Every check records how many elements needed the floor, and the
 largest |gpu - oracle| / B among them, in gpurun_out/parity_floor_usage.jsonl.
 Plans (index maps) are bit-exact against the oracle's plan twin fed the GPU's
 Schwarz factors.
@@ -66,8 +66,9 @@ def assert_parity(got, ref, what="", sh=None, quartets=None, spherical=None):
         offs = np.concatenate([[0], np.cumsum(sizes)])
         qbad = np.unique(np.searchsorted(offs, np.nonzero(bad)[0], side="right") - 1)
         for x in qbad:
+            # bar 4 B + C, written as 4 (B + C / 4)
             B = oracle.hgp_rounding_bound(sh, q[x:x + 1], spherical) + \
-                oracle.contraction_rounding_bound(sh, q[x:x + 1], spherical)
+                oracle.contraction_rounding_bound(sh, q[x:x + 1], spherical) / HGP_FLOOR_FACTOR
             sl = slice(offs[x], offs[x + 1])
             newtol = np.maximum(tol[sl], HGP_FLOOR_FACTOR * B)
             m = err[sl] > tol[sl]

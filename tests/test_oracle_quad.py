@@ -162,7 +162,7 @@ def test_long_contraction_needs_the_contraction_floor():
     the bar on dozens of elements and by more than FLOOR_FACTOR x B on some, the
     rounding of its contraction sums that B does not count; adding the
     contraction floor C (sqrt(K4 - 1) eps sum |term|, propagated) brings every
-    miss within (B + C), a quarter of the GPU bar FLOOR_FACTOR x (B + C)."""
+    miss within B + C, inside the GPU bar FLOOR_FACTOR x B + C."""
     sh, q, x = _long_contraction()
     a = oracle.eri_block(sh, q, True).ravel()
     assert np.max(np.abs(a - x) / _bar(x)) <= 1e-2

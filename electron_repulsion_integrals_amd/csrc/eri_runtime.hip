@@ -472,12 +472,13 @@ __global__ void k_zero_mat(int n, double *A, int lda)
 
 // chunk entries: (pair, offset of its contribution vector) for both sides of
 // every quartet; a quartet of two equal pairs has one side only
-__global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int none, int *ekey,
-                                int64_t *eoff)
+// (contribution vectors at cb offset base + s (nab + ncd), entries from ekey/eoff on)
+__global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int none, int64_t base,
+                                int *ekey, int64_t *eoff)
 {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= m) return;
-    const int64_t off = (int64_t)s * (nab + ncd);
+    const int64_t off = base + (int64_t)s * (nab + ncd);
     ekey[2 * s] = qbra[s];
     eoff[2 * s] = off;
     const bool two = qbra[s] != qket[s];
@@ -1370,6 +1371,36 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
         if (K) hipLaunchKernelGGL(k_zero_mat, dim3(nblk((int64_t)n * n, 256)), dim3(256), 0, ls, n, W.A, n);
         HIP_CHECK(hipGetLastError());
     }
+    // J entries of consecutive chunks of a lane collect in its buffers and are
+    // sorted and added together when the next chunk would not fit (and at the
+    // end): fewer, larger sorts.  The flush points follow from the plan and the
+    // shape alone, and the sort is stable, so every sum keeps a fixed order.
+    struct Pending {
+        int64_t e = 0, cb = 0;
+    };
+    std::vector<Pending> pend(NL);
+    auto sort_runs = [&](ChunkLane &W, hipStream_t ls, int n2, int bits) {
+        size_t tb = W.tmp_bytes;
+        HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, bits, ls));
+        tb = W.tmp_bytes;
+        HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
+        tb = W.tmp_bytes;
+        HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(W.tmp, tb, W.rlen, W.rst, n2, ls));
+    };
+    auto flush_J = [&](int l) {
+        if (pend[l].e == 0) return;
+        const hipStream_t ls = lane_stream(P, l, s);
+        ChunkLane &W = L[l];
+        sort_runs(W, ls, (int)pend[l].e, key_bits(P->npairs));
+        // at most one run per pair key (and one for the sentinel key); workgroups
+        // past the device-side run count exit at once
+        const int64_t nrun = std::min<int64_t>(pend[l].e, P->npairs + 1);
+        hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
+                           W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, (int)P->npairs,
+                           l == 0 ? J : W.J, l == 0 ? ldj : n);
+        HIP_CHECK(hipGetLastError());
+        pend[l] = Pending();
+    };
     int64_t chunk_index = 0;
     for (int bi = b0; bi < b1; ++bi) {
         const EriBlock &B = P->blocks[bi];
@@ -1386,36 +1417,22 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
             const int l = scratch_class ? 0 : (int)(chunk_index % NL);
             const hipStream_t ls = lane_stream(P, l, s);
             ChunkLane &W = L[l];
-            double *Jl = l == 0 ? J : W.J;
-            const int ldl = l == 0 ? ldj : n;
             const int64_t m = std::min(step, c1 - c);
             const int *qb = nullptr, *qk = nullptr;
             slot_lists(P, B.start + c, m, &qb, &qk, ls, l);
             const int64_t nk1 = std::max<int64_t>(0, std::min<int64_t>(B.n_k1 - c, m));
             launch_class(P, B.cid, qb, qk, m, W.ints, ls, nk1);
-            // sort the n2 entries in W.ek/W.eo (keys below 2^bits) and encode their runs
-            auto sort_runs = [&](int n2, int bits) {
-                size_t tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(W.tmp, tb, W.ek, W.ek2, W.eo, W.eo2, n2, 0, bits, ls));
-                tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(W.tmp, tb, W.ek2, W.ruk, W.rlen, W.nruns, n2, ls));
-                tb = W.tmp_bytes;
-                HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(W.tmp, tb, W.rlen, W.rst, n2, ls));
-            };
             if (J) {
                 const int64_t nv = m * (nab + ncd);
+                if (pend[l].e + 2 * m > d.NE || pend[l].cb + nv > d.CB) flush_J(l);
                 hipLaunchKernelGGL(k_digest_rows, dim3((unsigned)nblk(nv, 256)), dim3(256), 0, ls, nv, B.na, B.nb,
-                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb);
+                                   B.nc, B.nd, qb, qk, P->d_pinfo, P->d_bf, W.ints, D, ldd, W.cb + pend[l].cb);
                 hipLaunchKernelGGL(k_chunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, nab, ncd,
-                                   (int)P->npairs, W.ek, W.eo);
+                                   (int)P->npairs, pend[l].cb, W.ek + pend[l].e, W.eo + pend[l].e);
                 HIP_CHECK(hipGetLastError());
-                sort_runs((int)(2 * m), key_bits(P->npairs));
-                // at most one run per pair key (and one for the sentinel key); workgroups
-                // past the device-side run count exit at once
-                const int64_t nrun = std::min<int64_t>(2 * m, P->npairs + 1);
-                hipLaunchKernelGGL(k_add_runs, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk, W.rst,
-                                   W.rlen, W.eo2, W.cb, P->d_pinfo, P->d_bf, P->d_nfun, (int)P->npairs, Jl, ldl);
-                HIP_CHECK(hipGetLastError());
+                pend[l].e += 2 * m;
+                pend[l].cb += nv;
+                if (K) flush_J(l);  // the K entries below reuse the entry buffers
             }
             if (K) {
                 const int64_t nkt = m * nkv;
@@ -1424,7 +1441,7 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
                 hipLaunchKernelGGL(k_kchunk_entries, dim3(nblk(m, 256)), dim3(256), 0, ls, (int)m, qb, qk, P->d_pinfo,
                                    P->nshell, B.na, B.nb, B.nc, B.nd, W.ek, W.eo);
                 HIP_CHECK(hipGetLastError());
-                sort_runs((int)(4 * m), key_bits((int64_t)P->nshell * P->nshell));
+                sort_runs(W, ls, (int)(4 * m), key_bits((int64_t)P->nshell * P->nshell));
                 // at most one run per target block key (and one for the sentinel key)
                 const int64_t nrun = std::min<int64_t>(4 * m, (int64_t)P->nshell * P->nshell + 1);
                 hipLaunchKernelGGL(k_add_runs_K, dim3((unsigned)nrun), dim3(RUN_THREADS), 0, ls, W.nruns, W.ruk,
@@ -1433,6 +1450,8 @@ void digest_JK_run(const eri_plan *P, const double *D, int ldd, double *J, int l
             }
         }
     }
+    if (J)
+        for (int l = 0; l < NL; ++l) flush_J(l);
     if (NL > 1) side_join(P, s, NL);
     for (int l = 1; l < NL; ++l) {
         if (J)

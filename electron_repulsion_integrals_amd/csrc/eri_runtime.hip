@@ -474,11 +474,11 @@ __global__ void k_zero_mat(int n, double *A, int lda)
 // every quartet; a quartet of two equal pairs has one side only
 // (contribution vectors at cb offset base + s (nab + ncd), entries from ekey/eoff on)
 __global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab, int ncd, int none, int64_t base,
-                                int *ekey, int64_t *eoff)
+                                int *ekey, int *eoff)
 {
     const int s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s >= m) return;
-    const int64_t off = base + (int64_t)s * (nab + ncd);
+    const int off = (int)(base + (int64_t)s * (nab + ncd));  // below the lane's CB <= 2^26 doubles
     ekey[2 * s] = qbra[s];
     eoff[2 * s] = off;
     const bool two = qbra[s] != qket[s];
@@ -491,7 +491,7 @@ __global__ void k_chunk_entries(int m, const int *qbra, const int *qket, int nab
 // S = blockDim.x / n slices, slice k adds the entries e0 + k, e0 + k + S, ...
 // in entry order, and thread v < n then adds the S partial sums in slice
 // order.  Deterministic for a given blockDim; the result is left in part[v].
-__device__ __forceinline__ void run_sum(int n, int64_t e0, int64_t e1, const int64_t *eoff, const double *cb,
+__device__ __forceinline__ void run_sum(int n, int64_t e0, int64_t e1, const int *eoff, const double *cb,
                                         double *part)
 {
     const int S = blockDim.x / n;
@@ -513,7 +513,7 @@ constexpr int RUN_THREADS = 256;
 // one workgroup per run of equal pairs in the sorted chunk entries: add the
 // run's contribution vectors into the J block (and its transpose)
 __global__ void __launch_bounds__(RUN_THREADS) k_add_runs(const int *nruns, const int *key, const int *rstart,
-                                                          const int *rlen, const int64_t *eoff, const double *cb,
+                                                          const int *rlen, const int *eoff, const double *cb,
                                                           const int4 *pinfo, const int *bf, const int *nfun_sh,
                                                           int none, double *J, int ldj)
 {
@@ -593,13 +593,13 @@ __global__ void k_kdigest_rows(int64_t n_out, int na, int nb, int nc, int nd, co
 // vector) for the four blocks of every quartet; blocks a quartet does not have
 // get a key that sorts last
 __global__ void k_kchunk_entries(int m, const int *qbra, const int *qket, const int4 *pinfo, int nshell, int na,
-                                 int nb, int nc, int nd, int *ekey, int64_t *eoff)
+                                 int nb, int nc, int nd, int *ekey, int *eoff)
 {
     const int q = blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= m) return;
     const int4 ib = pinfo[qbra[q]], ik = pinfo[qket[q]];
     const bool dij = ib.x != ib.y, dkl = ik.x != ik.y;
-    const int64_t base = (int64_t)q * (na * nc + nb * nc + na * nd + nb * nd);
+    const int base = q * (na * nc + nb * nc + na * nd + nb * nd);  // below the lane's CB <= 2^26 doubles
     const int none = nshell * nshell;  // above every block key
     ekey[4 * q] = ib.x * nshell + ik.x;
     eoff[4 * q] = base;
@@ -613,7 +613,7 @@ __global__ void k_kchunk_entries(int m, const int *qbra, const int *qket, const 
 
 // one workgroup per run of equal target blocks: add the run's vectors into A
 __global__ void __launch_bounds__(RUN_THREADS) k_add_runs_K(const int *nruns, const int *key, const int *rstart,
-                                                            const int *rlen, const int64_t *eoff, const double *kv,
+                                                            const int *rlen, const int *eoff, const double *kv,
                                                             int nshell, const int *bf, const int *nfun_sh, double *A,
                                                             int lda)
 {
@@ -1247,7 +1247,7 @@ struct ChunkLane {
     double *ints = nullptr, *cb = nullptr, *kv = nullptr;  // integrals, J and K contribution vectors of a chunk
     double *J = nullptr, *A = nullptr;                     // lane accumulators (lane 0's J is the caller's)
     int *ek = nullptr, *ek2 = nullptr, *ruk = nullptr, *rlen = nullptr, *rst = nullptr, *nruns = nullptr;
-    int64_t *eo = nullptr, *eo2 = nullptr;
+    int *eo = nullptr, *eo2 = nullptr;  // entry offsets into the lane's contribution vectors
     void *tmp = nullptr;
     size_t tmp_bytes = 0;
 };
@@ -1290,8 +1290,8 @@ void digest_layout(Arena &A, const eri_plan *P, bool wantJ, bool wantK, const Di
     L.assign(d.lanes, ChunkLane());
     size_t t1 = 0, t2 = 0, t3 = 0;
     const int n2 = (int)d.NE;
-    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, (int *)nullptr, (int *)nullptr, (int64_t *)nullptr,
-                                                 (int64_t *)nullptr, n2, 0, 32));
+    HIP_CHECK(hipcub::DeviceRadixSort::SortPairs(nullptr, t1, (int *)nullptr, (int *)nullptr, (int *)nullptr,
+                                                 (int *)nullptr, n2, 0, 32));
     HIP_CHECK(hipcub::DeviceRunLengthEncode::Encode(nullptr, t2, (int *)nullptr, (int *)nullptr, (int *)nullptr,
                                                     (int *)nullptr, n2));
     HIP_CHECK(hipcub::DeviceScan::ExclusiveSum(nullptr, t3, (int *)nullptr, (int *)nullptr, n2));
@@ -1303,8 +1303,8 @@ void digest_layout(Arena &A, const eri_plan *P, bool wantJ, bool wantK, const Di
         if (wantK) W.kv = A.take<double>(d.CB);
         W.ek = A.take<int>(d.NE);
         W.ek2 = A.take<int>(d.NE);
-        W.eo = A.take<int64_t>(d.NE);
-        W.eo2 = A.take<int64_t>(d.NE);
+        W.eo = A.take<int>(d.NE);
+        W.eo2 = A.take<int>(d.NE);
         W.ruk = A.take<int>(d.NE);
         W.rlen = A.take<int>(d.NE);
         W.rst = A.take<int>(d.NE);

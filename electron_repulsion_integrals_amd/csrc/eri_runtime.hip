@@ -341,14 +341,41 @@ __global__ void k_all_pairs(int nshell, const int *l, const int *kept, int4 *pin
     pidx[p] = (int)p;
 }
 
-// Schwarz factor of each pair from its diagonal block (pair-major block of n*n x n*n).
-__global__ void k_schwarz_max(int n, const int *pairs, const double *blk, int nab, double *S)
+// Sub-pairs for the Schwarz diagonals: pair p's kept primitive-pair records
+// split into ceil(K / SCHWARZ_SUBK) consecutive runs, sub-pair kpo[p] + i
+// holding records i SCHWARZ_SUBK ... (as many as remain).  The diagonal block
+// (p|p) is the sum of the blocks (p_i|p_j) over all sub-pair pairs (the
+// integral is linear in the primitive pairs of each side), and a quartet of
+// sub-pairs has at most SCHWARZ_SUBK^2 primitive quartets, so a pair with a
+// long contraction no longer runs as one long loop on one lane.
+constexpr int SCHWARZ_SUBK = 6;
+
+__global__ void k_sub_pairs(int np, const int4 *pinfo, const int64_t *kpo, int4 *sub)
+{
+    const int p = blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= np) return;
+    const int4 pi = pinfo[p];
+    const int64_t o = kpo[p];
+    const int k = (pi.w + SCHWARZ_SUBK - 1) / SCHWARZ_SUBK;
+    for (int i = 0; i < k; ++i)
+        sub[o + i] = make_int4(pi.x, pi.y, pi.z + i * SCHWARZ_SUBK, min(SCHWARZ_SUBK, pi.w - i * SCHWARZ_SUBK));
+}
+
+// S of each pair of a batch: the diagonal of the sum of its k^2 sub-pair blocks
+// (block offset boff[t], in units of blocks of nab^2), summed in (i, j) order
+__global__ void k_schwarz_sum_max(int n, const int *pairs, const int *ksub, const int64_t *boff, const double *blk,
+                                  int nab, double *S)
 {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= n) return;
-    const double *B = blk + (size_t)t * nab * nab;
+    const int k2 = ksub[t] * ksub[t];
+    const double *B = blk + (size_t)boff[t] * nab * nab;
     double mx = 0.0;
-    for (int u = 0; u < nab; ++u) mx = fmax(mx, fabs(B[(size_t)u * nab + u]));
+    for (int u = 0; u < nab; ++u) {
+        double v = 0.0;
+        for (int x = 0; x < k2; ++x) v += B[(size_t)x * nab * nab + (size_t)u * nab + u];
+        mx = fmax(mx, fabs(v));
+    }
     S[pairs[t]] = mx;
 }
 
@@ -1034,7 +1061,7 @@ constexpr int64_t UNFUSED_DOUBLES = int64_t(3) << 25;
 #endif
 
 void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, const int *qket, int64_t n, double *out,
-                       hipStream_t s, int64_t n_k1)
+                       hipStream_t s, int64_t n_k1, const int4 *pinfo = nullptr)
 {
     const EriClassEntry *ce = find_class(cid, sph);
     if (!ce) {
@@ -1044,7 +1071,7 @@ void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, co
     EriClassArgs a;
     a.qbra = qbra;
     a.qket = qket;
-    a.pair_info = P->d_pinfo;
+    a.pair_info = pinfo ? pinfo : P->d_pinfo;
     a.ppd = P->d_ppd;
     a.cen = P->d_cen;
     a.boys = P->d_boys;
@@ -1054,7 +1081,8 @@ void launch_class_kind(const eri_plan *P, int cid, bool sph, const int *qbra, co
     // an explicit plan's own lists pair slot s with pairs 2s and 2s + 1: kernels
     // may then skip reading them
     long long base = -1;
-    if (!P->screened && qbra >= P->d_qbra && qbra < P->d_qbra + P->nq && qket == P->d_qket + (qbra - P->d_qbra))
+    if (!pinfo && !P->screened && qbra >= P->d_qbra && qbra < P->d_qbra + P->nq &&
+        qket == P->d_qket + (qbra - P->d_qbra))
         base = 2 * (long long)(qbra - P->d_qbra);
     const int blk = nfun(ce->la, sph) * nfun(ce->lb, sph) * nfun(ce->lc, sph) * nfun(ce->ld, sph);
     if (ce->tier == 'M' && ce->scratch_doubles > 0 && (!P->d_scratch || P->scratch_doubles < ce->scratch_doubles)) {
@@ -1121,10 +1149,10 @@ __global__ void k_sph_unfused(int64_t n, int la, int lb, int lc, int ld, const d
 }
 
 void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
-                  int64_t n_k1 = 0)
+                  int64_t n_k1 = 0, const int4 *pinfo = nullptr)
 {
     if (!P->sph) {
-        launch_class_kind(P, cid, false, qbra, qket, n, out, s, n_k1);
+        launch_class_kind(P, cid, false, qbra, qket, n, out, s, n_k1, pinfo);
         return;
     }
     const EriClassEntry *ce = find_class(cid, false);
@@ -1139,7 +1167,7 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
     for (int64_t b = 0; b < n; b += chunk) {
         const int64_t m = std::min(chunk, n - b);
         const int64_t k1 = std::min(m, std::max<int64_t>(0, n_k1 - b));
-        launch_class_kind(P, cid, false, qbra + b, qket + b, m, cart, s, k1);
+        launch_class_kind(P, cid, false, qbra + b, qket + b, m, cart, s, k1, pinfo);
         hipLaunchKernelGGL(k_sph_unfused, dim3((unsigned)m), dim3(256), 0, s, m, ce->la, ce->lb, ce->lc, ce->ld, cart,
                            w0, w1, out + b * ns);
         HIP_CHECK(hipGetLastError());
@@ -1147,9 +1175,9 @@ void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, 
 }
 #else
 void launch_class(const eri_plan *P, int cid, const int *qbra, const int *qket, int64_t n, double *out, hipStream_t s,
-                  int64_t n_k1 = 0)
+                  int64_t n_k1 = 0, const int4 *pinfo = nullptr)
 {
-    launch_class_kind(P, cid, P->sph, qbra, qket, n, out, s, n_k1);
+    launch_class_kind(P, cid, P->sph, qbra, qket, n, out, s, n_k1, pinfo);
 }
 #endif
 
@@ -1479,6 +1507,8 @@ struct BuildHost {
     int64_t nent = 0;      // screened: (block, bra rank) entries
     int nbuck = 0, nbd = 0;
     size_t diag_doubles = 0;
+    int64_t diag_q = 0;     // screened: sub-pair quartets per Schwarz batch
+    int64_t nsub = 0;       // screened: sub-pairs of all pairs
     long long scratch = 0;
     int64_t chunk_q = 0;
     size_t cub = 0;
@@ -1501,6 +1531,9 @@ struct BuildBufs {
         *bstart = nullptr;
     double *diag = nullptr;
     int64_t *cnt = nullptr, *idx = nullptr, *bs = nullptr;
+    int4 *sub = nullptr;                 // sub-pairs of the Schwarz diagonals
+    int64_t *kpo = nullptr, *boff = nullptr;
+    int *dq = nullptr, *ksub = nullptr;  // sub-pair quartet lists of a batch; sub-pairs per pair
 };
 
 constexpr size_t DIAG_DOUBLES = size_t(1) << 24;  // Schwarz diagonal blocks per launch
@@ -1552,7 +1585,7 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
     std::vector<uint64_t> keys;
     keys.reserve(H.np);
     bool pc_present[15] = {};
-    int64_t pc_count[15] = {};
+    int64_t pc_count[15] = {}, pc_k2[15] = {}, pc_kmax2[15] = {};
     for (int i = 0; i < ns; ++i)
         for (int j = 0; j <= i; ++j) {
             const int a = sh->l[i] >= sh->l[j] ? i : j, b = a == i ? j : i;
@@ -1560,6 +1593,10 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
             const int64_t K = prim_pairs_kept(sh->centers, sh->prim_off, sh->exps, a, b);
             H.kept.push_back((int)K);
             H.nppd += K;
+            const int64_t ks = (K + SCHWARZ_SUBK - 1) / SCHWARZ_SUBK;  // sub-pairs of the Schwarz diagonal
+            H.nsub += ks;
+            pc_k2[pc] += ks * ks;
+            pc_kmax2[pc] = std::max(pc_kmax2[pc], ks * ks);
             keys.push_back(((uint64_t)pc << 16) | (uint64_t)K);
             pc_present[pc] = true;
             ++pc_count[pc];
@@ -1583,7 +1620,10 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
         int la = 0;
         while ((la + 1) * (la + 2) / 2 <= pc) ++la;
         const size_t nab = (size_t)nfun(la, sph) * nfun(pc - la * (la + 1) / 2, sph);
-        H.diag_doubles = std::max(H.diag_doubles, std::min<size_t>(DIAG_DOUBLES, (size_t)pc_count[pc] * nab * nab));
+        // a batch of the class's sub-pair quartets; at least every sub-pair quartet of its largest pair
+        const size_t fit = std::max<size_t>(DIAG_DOUBLES / (nab * nab), (size_t)pc_kmax2[pc]);
+        H.diag_doubles = std::max(H.diag_doubles, std::min<size_t>(fit, (size_t)pc_k2[pc]) * nab * nab);
+        H.diag_q = std::max<int64_t>(H.diag_q, (int64_t)std::min<size_t>(fit, (size_t)pc_k2[pc]));
     }
     const int64_t nuq = H.np * (H.np + 1) / 2;
     H.chunk_q = std::min<int64_t>(chunk_q, std::max<int64_t>(nuq, 1));
@@ -1631,6 +1671,11 @@ void plan_layout(Arena &A, eri_plan *P, const BuildHost &H, BuildBufs &X)
         X.pidx2 = A.take<int>(np);
         P->d_S = A.take<double>(np);
         X.diag = A.take<double>(H.diag_doubles);
+        X.sub = A.take<int4>(H.nsub);
+        X.kpo = A.take<int64_t>(np);
+        X.boff = A.take<int64_t>(np);
+        X.ksub = A.take<int>(np);
+        X.dq = A.take<int>((size_t)2 * H.diag_q);
         X.seq = A.take<int>(np);
         X.ka = A.take<uint64_t>(np);
         X.kb = A.take<uint64_t>(np);
@@ -1727,12 +1772,28 @@ void build_screened(eri_plan *P, const BuildHost &H, BuildBufs &X, double tau, h
     HIP_CHECK(hipGetLastError());
     make_pair_data(P, H, X, s);
 
-    // --- Schwarz factors from the diagonal quartets (p|p), grouped by pair class
+    // --- Schwarz factors from the diagonal quartets (p|p), grouped by pair class,
+    // each computed as the sum over its sub-pair quartets (k_sub_pairs)
+    std::vector<int64_t> kpo(np);
+    {
+        int64_t o = 0;
+        for (int64_t p = 0; p < np; ++p) {
+            kpo[p] = o;
+            o += (H.kept[p] + SCHWARZ_SUBK - 1) / SCHWARZ_SUBK;
+        }
+    }
+    upload(X.kpo, kpo.data(), (size_t)np, s);
+    hipLaunchKernelGGL(k_sub_pairs, dim3(nblk(np, 256)), dim3(256), 0, s, (int)np, P->d_pinfo, X.kpo, X.sub);
+    HIP_CHECK(hipGetLastError());
     sort_pairs_u64(X.pck, X.pck2, X.pidx, X.pidx2, np, X.cub, H.cub, s);  // pidx2: pairs ordered by pair class
     std::vector<uint64_t> hpc(np);
+    std::vector<int> hpidx(np);
     HIP_CHECK(hipMemcpyAsync(hpc.data(), X.pck2, sizeof(uint64_t) * np, hipMemcpyDeviceToHost, s));
+    HIP_CHECK(hipMemcpyAsync(hpidx.data(), X.pidx2, sizeof(int) * np, hipMemcpyDeviceToHost, s));
     HIP_CHECK(hipStreamSynchronize(s));
     {
+        std::vector<int> qb, qk, hk;
+        std::vector<int64_t> hoff;
         int64_t i = 0;
         while (i < np) {
             int64_t j = i;
@@ -1742,13 +1803,40 @@ void build_screened(eri_plan *P, const BuildHost &H, BuildBufs &X, double tau, h
             while ((la + 1) * (la + 2) / 2 <= pc) ++la;
             const int lb = pc - la * (la + 1) / 2;
             const int64_t nab = nfun(la, P->sph) * nfun(lb, P->sph);
-            const int64_t per = std::max<int64_t>(1, (int64_t)H.diag_doubles / (nab * nab));
-            for (int64_t b = i; b < j; b += per) {
-                const int64_t m = std::min(per, j - b);
-                launch_class(P, class_id_of(pc, pc), X.pidx2 + b, X.pidx2 + b, m, X.diag, s);
-                hipLaunchKernelGGL(k_schwarz_max, dim3(nblk(m, 256)), dim3(256), 0, s, (int)m, X.pidx2 + b, X.diag,
-                                   (int)nab, P->d_S);
+            const int64_t capb = std::min<int64_t>((int64_t)H.diag_doubles / (nab * nab), H.diag_q);
+            for (int64_t t = i; t < j;) {
+                qb.clear();
+                qk.clear();
+                hk.clear();
+                hoff.clear();
+                int64_t u = t, nb = 0;
+                while (u < j) {
+                    const int p = hpidx[u];
+                    const int64_t k = (H.kept[p] + SCHWARZ_SUBK - 1) / SCHWARZ_SUBK;
+                    if (nb + k * k > capb) break;
+                    hoff.push_back(nb);
+                    hk.push_back((int)k);
+                    for (int64_t x = 0; x < k; ++x)
+                        for (int64_t y = 0; y < k; ++y) {
+                            qb.push_back((int)(kpo[p] + x));
+                            qk.push_back((int)(kpo[p] + y));
+                        }
+                    nb += k * k;
+                    ++u;
+                }
+                if (u == t) {  // cannot happen: capb holds the largest pair's sub-pair quartets
+                    g_last_error = "Schwarz batch too small";
+                    throw HipFail{hipErrorInvalidValue};
+                }
+                upload(X.dq, qb.data(), qb.size(), s);
+                upload(X.dq + H.diag_q, qk.data(), qk.size(), s);
+                upload(X.ksub, hk.data(), hk.size(), s);
+                upload(X.boff, hoff.data(), hoff.size(), s);
+                launch_class(P, class_id_of(pc, pc), X.dq, X.dq + H.diag_q, nb, X.diag, s, 0, X.sub);
+                hipLaunchKernelGGL(k_schwarz_sum_max, dim3(nblk(u - t, 256)), dim3(256), 0, s, (int)(u - t),
+                                   X.pidx2 + t, X.ksub, X.boff, X.diag, (int)nab, P->d_S);
                 HIP_CHECK(hipGetLastError());
+                t = u;
             }
             i = j;
         }

@@ -585,6 +585,7 @@ PACK_CH = 21  # primitive quartets per quartet set up together (one lane each)
 CONTRACTED_SLOTS = True
 CONTRACTED_OWN_FIRST = True
 CONTRACTED_PRELOAD = True
+CONTRACTED_MIN_WAVES = 2  # waves per SIMD the contracted kernels are bounded to
 
 
 # Register form of the contracted kernels.  With loop-invariant selectors (two
@@ -602,8 +603,8 @@ def _compact(ci: ClassInfo) -> bool:
     return (ci.la, ci.lb, ci.lc, ci.ld) in COMPACT_CONTRACTED
 
 
-def _chunk(Q, NT, ch=PACK_CH):
-    return max(1, min(ch, NT // Q))
+def _chunk(Q, NT, ch=0):
+    return max(1, min(ch or PACK_CH, NT // Q))
 
 
 def packed_contracted_waves(ci: ClassInfo) -> int:
@@ -620,7 +621,7 @@ def packed_contracted_waves(ci: ClassInfo) -> int:
     return PACK_WAVES
 
 
-def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = PACK_CH) -> int:
+def packed_contracted_lds_bytes(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = 0) -> int:
     kv = build_ket_vrr(ci.lc, ci.Lk)
     W, Q, NT = packed_shape(ci, spherical, waves or packed_contracted_waves(ci))
     ch = _chunk(Q, NT, ch)
@@ -651,7 +652,7 @@ def use_packed_contracted(ci: ClassInfo, spherical: bool) -> bool:
     return packed_contracted_wg_per_cu(ci, spherical) >= 2
 
 
-def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = PACK_CH):
+def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: int = 0):
     """General (contracted) kernel, Q quartets per workgroup of `waves` waves.
 
     Algorithm 2 of "FusionRCG": the primitive quartets of each quartet are set
@@ -708,7 +709,7 @@ def emit_packed_contracted(ci: ClassInfo, spherical: bool, waves: int = 0, ch: i
     # at least two waves per SIMD: (dd|dd), (fp|dd) and (fp|fp) otherwise take a
     # few registers over 256 and run at one; capped, they spill a few values and
     # measured 20-30% faster
-    o.append(f"__global__ void __launch_bounds__({NT}, 2) eri_kernel_{tag}(EriClassArgs a)")
+    o.append(f"__global__ void __launch_bounds__({NT}, {CONTRACTED_MIN_WAVES}) eri_kernel_{tag}(EriClassArgs a)")
     o.append("{")
     o.append(f"  constexpr int G = {G}, Q = {Q}, NT = {NT}, NK = {NK}, NEB = {NEB}, BLK = {BLK};")
     o.append(f"  constexpr int CH = {CH}, NRL = {NRL}, NC = {max(NC, 1)};")

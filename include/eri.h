@@ -112,8 +112,13 @@ typedef struct eri_plan eri_plan;
  *   quartets == NULL: all unique quartets (pair(ij) >= pair(kl), i >= j,
  *     k >= l) that pass the Schwarz test fl(S_ij * S_kl) >= fl(tau * tau),
  *     with S_ij = max |(mu nu|mu nu)| over the (ij|ij) block, computed on the
- *     device by the same class kernels (tau = 0 keeps every quartet; the
- *     page states no screen, this is the reading taken).  Pairs are bucketed
+ *     device by the same class kernels as sums over sub-pair quartets of at
+ *     most 6 primitive pairs per side (tau = 0 keeps every quartet; the page
+ *     states no screen, this is the reading taken).  Such plans keep only the
+ *     primitive pairs (alpha, beta) of a shell pair with
+ *     alpha beta / (alpha + beta) |AB|^2 <= 230 (their Gaussian-product factor
+ *     is at least 1.3e-100; a shell pair with none keeps its first), and
+ *     K_pair counts those.  Pairs are bucketed
  *     by (pair class, K_pair) and ranked by S descending (ties by pair index);
  *     order (class id, K_bra, K_ket, bra rank, ket rank).  Because the kets of
  *     one bra are ranked by S descending, the survivors of each (block, bra)

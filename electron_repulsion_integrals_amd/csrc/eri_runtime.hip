@@ -1601,6 +1601,10 @@ void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &
             pc_present[pc] = true;
             ++pc_count[pc];
         }
+    if (H.nsub > (int64_t)INT32_MAX) {  // sub-pair indices of the Schwarz diagonals are 32-bit
+        g_last_error = "too many Schwarz sub-pairs";
+        throw HipFail{hipErrorInvalidValue};
+    }
     std::sort(keys.begin(), keys.end());
     std::vector<int64_t> nB;
     for (size_t x = 0; x < keys.size(); ++x)

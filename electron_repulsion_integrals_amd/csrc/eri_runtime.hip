@@ -872,6 +872,55 @@ __global__ void __launch_bounds__(256) k_deriv_sph(int64_t n, int tpi, const int
 }
 
 
+// The same transform with the item's block in LDS: the Cartesian block is read
+// once, coalesced, and the four passes ping-pong between two LDS buffers of
+// `stride` doubles per item (stride >= the call's largest Cartesian block;
+// the caller sizes the dynamic LDS to (256 / tpi) x 2 x stride doubles).  The
+// passes sum in the same order as k_deriv_sph.
+__global__ void __launch_bounds__(256) k_deriv_sph_lds(int64_t n, int tpi, int stride, const int *rows, const int *lsh,
+                                                       const double *cart, const int64_t *cart_off,
+                                                       const int64_t *dst_off, double *dst)
+{
+    extern __shared__ double sm[];
+    const int64_t u = (int64_t)blockIdx.x * (256 / tpi) + threadIdx.x / tpi;
+    const int lane = threadIdx.x % tpi;
+    const bool live = u < 12 * n;
+    const int64_t t = live ? u / 12 : 0;
+    const int comp = live ? (int)(u - t * 12) : 0;
+    double *bufA = sm + (size_t)(threadIdx.x / tpi) * 2 * stride, *bufB = bufA + stride;
+    int l4[4], dims[4], ns[4];
+    for (int k = 0; k < 4; ++k) {
+        l4[k] = live ? lsh[rows[5 * t + k]] : 0;
+        dims[k] = dv_ncart(l4[k]);
+        ns[k] = dv_nsph(l4[k]);
+    }
+    const int ncar = dims[0] * dims[1] * dims[2] * dims[3];
+    const int nsp = ns[0] * ns[1] * ns[2] * ns[3];
+    if (live) {
+        const double *src = cart + cart_off[t] + (int64_t)comp * ncar;
+        for (int x = lane; x < ncar; x += tpi) bufA[x] = src[x];
+    }
+    __syncthreads();
+    for (int pos = 0; pos < 4; ++pos) {
+        int before = 1, after = 1;
+        for (int k = 0; k < pos; ++k) before *= dims[k];
+        for (int k = pos + 1; k < 4; ++k) after *= dims[k];
+        const double *T = eri_sph_T[l4[pos]];
+        const int nc = dims[pos], nsv = ns[pos];
+        const double *in = (pos % 2 == 0) ? bufA : bufB;
+        double *o = pos == 3 ? dst + (live ? dst_off[t] : 0) + (int64_t)comp * nsp : ((pos % 2 == 0) ? bufB : bufA);
+        const int total = live ? before * nsv * after : 0;
+        for (int x = lane; x < total; x += tpi) {
+            const int y = x % after, rr = x / after, sv = rr % nsv, bb = rr / nsv;
+            double acc = 0.0;
+            for (int c = 0; c < nc; ++c) acc += T[sv * nc + c] * in[(bb * nc + c) * after + y];
+            o[x] = acc;
+        }
+        dims[pos] = nsv;
+        __syncthreads();
+    }
+}
+
 // FP64 FMA issue rate: every lane runs eight independent chains of fused
 // multiply-adds, eight waves per SIMD.
 constexpr int FMA_CHAINS = 8, FMA_ITERS = 4096;
@@ -2562,8 +2611,14 @@ extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count
             hipLaunchKernelGGL(k_deriv_combine, dim3((unsigned)nwc), dim3(256), 0, s, count, tpc, X.rows, P->d_l,
                                X.slot_of, Ap->d_qmap, Ap->d_l, X.aux_off, X.aux, X.off + count, X.cart);
             HIP_CHECK(hipGetLastError());
-            hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)nws), dim3(256), 0, s, count, tps, X.rows, P->d_l,
-                               X.cart, X.tmp, X.off + count, X.off, out);
+            // blocks staged in LDS where two buffers per item fit 64 KB per workgroup
+            const size_t lds = (size_t)(256 / tps) * 2 * max_ncar * sizeof(double);
+            if (lds <= 65536)
+                hipLaunchKernelGGL(k_deriv_sph_lds, dim3((unsigned)nws), dim3(256), lds, s, count, tps, (int)max_ncar,
+                                   X.rows, P->d_l, X.cart, X.off + count, X.off, out);
+            else
+                hipLaunchKernelGGL(k_deriv_sph, dim3((unsigned)nws), dim3(256), 0, s, count, tps, X.rows, P->d_l,
+                                   X.cart, X.tmp, X.off + count, X.off, out);
         }
         HIP_CHECK(hipGetLastError());
         // the host vectors uploaded above are read by the copies before they return

@@ -583,7 +583,7 @@ def main():
         print(json.dumps({"copy_MiB": a.calibrate_copy_mib}), flush=True)
         return
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (one process, one MI355X).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (one process, one MI355X).",
               file=sys.stderr)
         sys.exit(2)
     import torch

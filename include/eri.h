@@ -72,7 +72,7 @@ extern "C" {
 
 #define ERI_OK 0
 #define ERI_E_INVALID (-1)     /* malformed argument (index out of range, l > 4, K < 1, ...) */
-#define ERI_E_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define ERI_E_UNSUPPORTED (-2) /* valid request the library does not implement */
 #define ERI_E_CAPACITY (-3)    /* output buffer smaller than the call's output */
 #define ERI_E_HIP (-4)         /* a HIP runtime call failed; see eri_strerror */
 #define ERI_E_NOMEM (-5)       /* host memory exhausted */

@@ -8,7 +8,7 @@ oracle.contraction_rounding_bound, the contraction sums' floor, so that the
 bar is 4 B + C).  FLOOR_FACTOR = 4 is the factor the binary128
 adjudication supports (tests/test_oracle_quad.py: the emulated fp64 method
 needs at most 3.2 x B on the hardest quartets).  Every parity check appends one
-JSON line to gpurun_out/parity_floor_usage.jsonl: the test, the check, the
+JSON line to parity_floor_usage.jsonl in the results folder: the test, the check, the
 number of elements, how many missed the plain 1e-10/1e-13 bar (and were
 accepted only through the floor), and the largest |gpu - oracle| / B among
 those.

@@ -11,7 +11,7 @@ at K4 = 1).  The floor only matters for diffuse high-l quartets far apart,
 where it exceeds 1e-10 of the result; it is computed only for quartets that
 miss the first two terms.  The factor 4 and C are what the binary128
 adjudication of tests/test_oracle_quad.py supports.  Every check records how many elements needed the floor, and the
-largest |gpu - oracle| / B among them, in gpurun_out/parity_floor_usage.jsonl.
+largest |gpu - oracle| / B among them, in parity_floor_usage.jsonl (tests/floor_log.py).
 Plans (index maps) are bit-exact against the oracle's plan twin fed the GPU's
 Schwarz factors.
 """

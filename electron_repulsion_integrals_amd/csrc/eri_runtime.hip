@@ -750,10 +750,12 @@ __device__ inline void dv_ctrip(int l, int i, int *t)
     t[2] = l - t[0] - t[1];
 }
 
-__global__ void k_invert_src(int64_t n, const int64_t *src, int64_t *slot_of)
+// slot of every listed auxiliary quartet, by its derivative index u (umap: the
+// list's u in input order)
+__global__ void k_invert_src(int64_t n, const int64_t *src, const int *umap, int64_t *slot_of)
 {
     const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (x < n) slot_of[src[x]] = x;
+    if (x < n) slot_of[umap[src[x]]] = x;
 }
 
 // output offset of every slot from the block table (blocks ordered by first slot)
@@ -2444,7 +2446,7 @@ struct DerivHost {
     std::vector<int64_t> dst_off, cart_off;
     int64_t dtot = 0, ctot = 0;
     // auxiliary shells: [0, ns) the shells, [ns, 2ns) raised, [2ns, 3ns) lowered (raw coefficients)
-    std::vector<int32_t> al, ak, aoff, aq;
+    std::vector<int32_t> al, ak, aoff, aq, umap;
     std::vector<double> acen, aexp, acf;
     eri_shells ash{};
     int64_t aux_nout = 0;
@@ -2506,23 +2508,29 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
             }
         }
     H.ash = eri_shells{3 * ns, H.acen.data(), H.al.data(), H.ak.data(), H.aoff.data(), H.aexp.data(), H.acf.data()};
-    // slot t, centre p, raised (0) or lowered (1): auxiliary quartet u = (t 4 + p) 2 + sg
-    H.aq.resize(32 * (size_t)count);
+    // slot t, centre p, raised (0) or lowered (1): derivative index u = (t 4 + p) 2 + sg.
+    // An s shell has no lowered term (every exponent of the centre is zero), so
+    // its lowered quartet is not listed; umap holds the u of every listed quartet.
+    H.aq.reserve(32 * (size_t)count);
+    H.umap.reserve(8 * (size_t)count);
     for (int64_t t = 0; t < count; ++t)
         for (int p = 0; p < 4; ++p)
             for (int sg = 0; sg < 2; ++sg) {
-                int32_t *q = &H.aq[4 * ((t * 4 + p) * 2 + sg)];
+                if (sg == 1 && hl[H.rows[5 * t + p]] == 0) continue;
+                int32_t q[4];
                 int64_t blk = 1;
                 for (int k = 0; k < 4; ++k) q[k] = H.rows[5 * t + k];
                 q[p] += (sg == 0 ? 1 : 2) * ns;
                 for (int k = 0; k < 4; ++k) blk *= ncart(H.al[q[k]]);
                 H.aux_nout += blk;
+                H.aq.insert(H.aq.end(), q, q + 4);
+                H.umap.push_back((int32_t)((t * 4 + p) * 2 + sg));
             }
     return ERI_OK;
 }
 
 struct DerivBufs {
-    int *rows = nullptr;
+    int *rows = nullptr, *umap = nullptr;
     double *aux = nullptr, *cart = nullptr, *tmp = nullptr;
     int64_t *slot_of = nullptr, *bt = nullptr, *aux_off = nullptr, *off = nullptr;
 };
@@ -2530,10 +2538,11 @@ struct DerivBufs {
 void deriv_layout(Arena &A, const eri_plan *P, int64_t count, const DerivHost &H, DerivBufs &X)
 {
     X.rows = A.take<int>(5 * (size_t)count);
+    X.umap = A.take<int>(H.umap.size());
     X.aux = A.take<double>(H.aux_nout);
     X.slot_of = A.take<int64_t>(8 * (size_t)count);
     X.bt = A.take<int64_t>(3 * ERI_NCLASS);
-    X.aux_off = A.take<int64_t>(8 * (size_t)count);
+    X.aux_off = A.take<int64_t>(H.umap.size());
     X.off = A.take<int64_t>(2 * (size_t)count);
     if (P->sph) {
         X.cart = A.take<double>(H.ctot);
@@ -2560,20 +2569,21 @@ extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count
         if (rc != ERI_OK) return rc;
         DerivBufs X;
         Arena cnt;
-        build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), 8 * count, 0.0, cnt, s);
+        const int64_t na = (int64_t)H.umap.size();
+        build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), na, 0.0, cnt, s);
         deriv_layout(cnt, P, count, H, X);
         const int w = workspace_check(workspace, ws_bytes, cnt.used);
         if (w) return w > 0 ? ERI_OK : w;
         if (!out) return ERI_E_INVALID;
         if (cap < H.dtot) return ERI_E_CAPACITY;
         Arena A(workspace, *ws_bytes);
-        Aux.reset(build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), 8 * count, 0.0, A, s));
+        Aux.reset(build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), na, 0.0, A, s));
         deriv_layout(A, P, count, H, X);
         const eri_plan *Ap = Aux.get();
         for (const EriBlock &B : Ap->blocks) compute_range(Ap, B, 0, B.count, X.aux + B.out_off, s, 0);
         upload(X.rows, H.rows.data(), 5 * (size_t)count, s);
-        const int64_t na = 8 * count;
-        hipLaunchKernelGGL(k_invert_src, dim3(nblk(na, 256)), dim3(256), 0, s, na, Ap->d_qsrc, X.slot_of);
+        upload(X.umap, H.umap.data(), (size_t)na, s);
+        hipLaunchKernelGGL(k_invert_src, dim3(nblk(na, 256)), dim3(256), 0, s, na, Ap->d_qsrc, X.umap, X.slot_of);
         HIP_CHECK(hipGetLastError());
         const int nb = (int)Ap->blocks.size();
         std::vector<int64_t> bt(3 * (size_t)nb);

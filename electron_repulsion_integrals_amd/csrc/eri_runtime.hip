@@ -2459,8 +2459,12 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
     const std::vector<int> &hl = P->hl, &hk = P->hk, &hoff = P->hoff;
     // every auxiliary class (one shell raised or lowered) must be in the library
     bool checked[ERI_NCLASS] = {};
+    int prev[4] = {-1, -1, -1, -1};
     for (int64_t t = 0; t < count; ++t) {
         const int *r = &H.rows[5 * t];
+        const int lt[4] = {hl[r[0]], hl[r[1]], hl[r[2]], hl[r[3]]};
+        if (lt[0] == prev[0] && lt[1] == prev[1] && lt[2] == prev[2] && lt[3] == prev[3]) continue;
+        for (int k = 0; k < 4; ++k) prev[k] = lt[k];
         for (int p = 0; p < 4; ++p)
             for (int dl = -1; dl <= 1; dl += 2) {
                 int l4[4] = {hl[r[0]], hl[r[1]], hl[r[2]], hl[r[3]]};
@@ -2511,21 +2515,26 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
     // slot t, centre p, raised (0) or lowered (1): derivative index u = (t 4 + p) 2 + sg.
     // An s shell has no lowered term (every exponent of the centre is zero), so
     // its lowered quartet is not listed; umap holds the u of every listed quartet.
-    H.aq.reserve(32 * (size_t)count);
-    H.umap.reserve(8 * (size_t)count);
+    std::vector<int64_t> anc(3 * (size_t)ns);
+    for (int y = 0; y < 3 * ns; ++y) anc[y] = ncart(H.al[y]);
+    int64_t na = 0;
     for (int64_t t = 0; t < count; ++t)
+        for (int p = 0; p < 4; ++p) na += hl[H.rows[5 * t + p]] > 0 ? 2 : 1;
+    H.aq.resize(4 * (size_t)na);
+    H.umap.resize((size_t)na);
+    int64_t x = 0;
+    for (int64_t t = 0; t < count; ++t) {
+        const int *r = &H.rows[5 * t];
         for (int p = 0; p < 4; ++p)
             for (int sg = 0; sg < 2; ++sg) {
-                if (sg == 1 && hl[H.rows[5 * t + p]] == 0) continue;
-                int32_t q[4];
-                int64_t blk = 1;
-                for (int k = 0; k < 4; ++k) q[k] = H.rows[5 * t + k];
+                if (sg == 1 && hl[r[p]] == 0) continue;
+                int32_t *q = &H.aq[4 * (size_t)x];
+                for (int k = 0; k < 4; ++k) q[k] = r[k];
                 q[p] += (sg == 0 ? 1 : 2) * ns;
-                for (int k = 0; k < 4; ++k) blk *= ncart(H.al[q[k]]);
-                H.aux_nout += blk;
-                H.aq.insert(H.aq.end(), q, q + 4);
-                H.umap.push_back((int32_t)((t * 4 + p) * 2 + sg));
+                H.aux_nout += anc[q[0]] * anc[q[1]] * anc[q[2]] * anc[q[3]];
+                H.umap[x++] = (int32_t)((t * 4 + p) * 2 + sg);
             }
+    }
     return ERI_OK;
 }
 

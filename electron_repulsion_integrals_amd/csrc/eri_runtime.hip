@@ -1609,23 +1609,33 @@ int class_of(int li, int lj, int lk, int ll)
     return class_id_of(std::max(pb, pk), std::min(pb, pk));
 }
 
-void host_explicit(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, BuildHost &H)
+// sizes of an explicit plan from its quartet count, the sum of its pairs'
+// primitive pair counts and the classes present
+void host_explicit_counts(const eri_shells *sh, int flags, int64_t nq, int64_t nppd, const bool *present,
+                          BuildHost &H)
 {
     host_common(sh, (flags & ERI_SPHERICAL) != 0, H);
     H.nq = nq;
     H.np = 2 * nq;
-    bool present[ERI_NCLASS] = {};
-    for (int64_t x = 0; x < nq; ++x) {
-        const int *q = quartets + 4 * x;
-        H.nppd += (int64_t)sh->nprim[q[0]] * sh->nprim[q[1]] + (int64_t)sh->nprim[q[2]] * sh->nprim[q[3]];
-        present[class_of(sh->l[q[0]], sh->l[q[1]], sh->l[q[2]], sh->l[q[3]])] = true;
-    }
+    H.nppd = nppd;
     std::vector<int> cids;
     for (int c = 0; c < ERI_NCLASS; ++c)
         if (present[c]) cids.push_back(c);
     H.scratch = scratch_need(cids, kernel_sph_flags((flags & ERI_SPHERICAL) != 0));
     H.cub = std::max(sort_pairs_u64<int64_t>(nullptr, nullptr, nullptr, nullptr, nq, nullptr, 0, nullptr),
                      scan_i32(nullptr, nullptr, H.np, nullptr, 0, nullptr));
+}
+
+void host_explicit(const eri_shells *sh, int flags, const int32_t *quartets, int64_t nq, BuildHost &H)
+{
+    int64_t nppd = 0;
+    bool present[ERI_NCLASS] = {};
+    for (int64_t x = 0; x < nq; ++x) {
+        const int *q = quartets + 4 * x;
+        nppd += (int64_t)sh->nprim[q[0]] * sh->nprim[q[1]] + (int64_t)sh->nprim[q[2]] * sh->nprim[q[3]];
+        present[class_of(sh->l[q[0]], sh->l[q[1]], sh->l[q[2]], sh->l[q[3]])] = true;
+    }
+    host_explicit_counts(sh, flags, nq, nppd, present, H);
 }
 
 void host_screened(const eri_shells *sh, int flags, int64_t chunk_q, BuildHost &H)
@@ -2450,15 +2460,19 @@ struct DerivHost {
     std::vector<double> acen, aexp, acf;
     eri_shells ash{};
     int64_t aux_nout = 0;
+    // the auxiliary plan's quartet count, primitive pair total and classes
+    int64_t na = 0, nppd = 0;
+    bool present[ERI_NCLASS] = {};
 };
 
-int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, DerivHost &H)
+// list: fill the auxiliary quartet list (aq, umap); a size query needs only its counts
+int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, DerivHost &H, bool list)
 {
     fetch_rows(P, first, count, H.rows, s);
     const int ns = P->nshell;
     const std::vector<int> &hl = P->hl, &hk = P->hk, &hoff = P->hoff;
     // every auxiliary class (one shell raised or lowered) must be in the library
-    bool checked[ERI_NCLASS] = {};
+    bool *checked = H.present;
     int prev[4] = {-1, -1, -1, -1};
     for (int64_t t = 0; t < count; ++t) {
         const int *r = &H.rows[5 * t];
@@ -2467,8 +2481,9 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
         for (int k = 0; k < 4; ++k) prev[k] = lt[k];
         for (int p = 0; p < 4; ++p)
             for (int dl = -1; dl <= 1; dl += 2) {
-                int l4[4] = {hl[r[0]], hl[r[1]], hl[r[2]], hl[r[3]]};
-                l4[p] = std::max(l4[p] + dl, 0);
+                if (dl < 0 && lt[p] == 0) continue;  // no lowered quartet for an s shell
+                int l4[4] = {lt[0], lt[1], lt[2], lt[3]};
+                l4[p] += dl;
                 const int cid = class_of(l4[0], l4[1], l4[2], l4[3]);
                 if (checked[cid]) continue;
                 if (!find_class(cid, false)) return ERI_E_UNSUPPORTED;
@@ -2518,8 +2533,28 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
     std::vector<int64_t> anc(3 * (size_t)ns);
     for (int y = 0; y < 3 * ns; ++y) anc[y] = ncart(H.al[y]);
     int64_t na = 0;
-    for (int64_t t = 0; t < count; ++t)
-        for (int p = 0; p < 4; ++p) na += hl[H.rows[5 * t + p]] > 0 ? 2 : 1;
+    for (int64_t t = 0; t < count; ++t) {
+        const int *r = &H.rows[5 * t];
+        int n = 0;
+        for (int p = 0; p < 4; ++p) n += hl[r[p]] > 0 ? 2 : 1;
+        na += n;
+        // raised and lowered shells keep their primitive counts
+        H.nppd += n * ((int64_t)hk[r[0]] * hk[r[1]] + (int64_t)hk[r[2]] * hk[r[3]]);
+    }
+    H.na = na;
+    if (!list) {
+        for (int64_t t = 0; t < count; ++t) {
+            const int *r = &H.rows[5 * t];
+            for (int p = 0; p < 4; ++p)
+                for (int sg = 0; sg < 2; ++sg) {
+                    if (sg == 1 && hl[r[p]] == 0) continue;
+                    int64_t blk = 1;
+                    for (int k = 0; k < 4; ++k) blk *= anc[r[k] + (k == p ? (sg == 0 ? 1 : 2) * ns : 0)];
+                    H.aux_nout += blk;
+                }
+        }
+        return ERI_OK;
+    }
     H.aq.resize(4 * (size_t)na);
     H.umap.resize((size_t)na);
     int64_t x = 0;
@@ -2547,11 +2582,11 @@ struct DerivBufs {
 void deriv_layout(Arena &A, const eri_plan *P, int64_t count, const DerivHost &H, DerivBufs &X)
 {
     X.rows = A.take<int>(5 * (size_t)count);
-    X.umap = A.take<int>(H.umap.size());
+    X.umap = A.take<int>(H.na);
     X.aux = A.take<double>(H.aux_nout);
     X.slot_of = A.take<int64_t>(8 * (size_t)count);
     X.bt = A.take<int64_t>(3 * ERI_NCLASS);
-    X.aux_off = A.take<int64_t>(H.umap.size());
+    X.aux_off = A.take<int64_t>(H.na);
     X.off = A.take<int64_t>(2 * (size_t)count);
     if (P->sph) {
         X.cart = A.take<double>(H.ctot);
@@ -2574,12 +2609,20 @@ extern "C" int eri_compute_deriv(const eri_plan *P, int64_t first, int64_t count
     std::unique_ptr<eri_plan> Aux;
     try {
         DerivHost H;
-        int rc = deriv_host(P, first, count, s, H);
+        int rc = deriv_host(P, first, count, s, H, workspace != nullptr);
         if (rc != ERI_OK) return rc;
         DerivBufs X;
         Arena cnt;
-        const int64_t na = (int64_t)H.umap.size();
-        build_plan(&H.ash, ERI_NO_NORMALIZE, H.aq.data(), na, 0.0, cnt, s);
+        const int64_t na = H.na;
+        {
+            BuildHost BH;
+            host_explicit_counts(&H.ash, ERI_NO_NORMALIZE, na, H.nppd, H.present, BH);
+            eri_plan L;
+            L.flags = ERI_NO_NORMALIZE;
+            L.nshell = H.ash.nshell;
+            BuildBufs LX;
+            plan_layout(cnt, &L, BH, LX);
+        }
         deriv_layout(cnt, P, count, H, X);
         const int w = workspace_check(workspace, ws_bytes, cnt.used);
         if (w) return w > 0 ? ERI_OK : w;

@@ -2471,7 +2471,8 @@ int deriv_host(const eri_plan *P, int64_t first, int64_t count, hipStream_t s, D
     fetch_rows(P, first, count, H.rows, s);
     const int ns = P->nshell;
     const std::vector<int> &hl = P->hl, &hk = P->hk, &hoff = P->hoff;
-    // every auxiliary class (one shell raised or lowered) must be in the library
+    // every auxiliary class (one shell raised or lowered) must be in the library;
+    // the flags set here are the auxiliary plan's classes
     bool *checked = H.present;
     int prev[4] = {-1, -1, -1, -1};
     for (int64_t t = 0; t < count; ++t) {

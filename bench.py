@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # reported as null once either changes.
 TRAFFIC = {"kernel_sources": ["electron_repulsion_integrals_amd/csrc/generated/eri_c20_s.hip",
                               "electron_repulsion_integrals_amd/csrc/eri_device.h"],
-           "sha1": "a2dc962e60ad7a9846f38a71b5e4159f45282a54",
+           "sha1": "cdd96791f0cf2aeedced5eab34dbd0b23872fb17",
            "fetch_kib": 4132.99, "fetch_scale": 2.0, "write_kib": 97758.13, "write_scale": 1.0}
 
 

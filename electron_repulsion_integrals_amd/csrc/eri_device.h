@@ -4,7 +4,7 @@
 // Memory Hierarchies".  Section II-A: the recurrence starts from Boys values
 // F_m(T) and the Gaussian-product quantities zeta, eta, rho, P, Q, W of Eq. (2);
 // Algorithm 2 (section III-C) forms them per primitive quartet
-// ("GAUSSIANPAIRS", "BOYS") inside the primitive loops.
+// (its Gaussian-pair and Boys steps) inside the primitive loops.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -3,7 +3,7 @@
 // Source: "FusionRCG: Orchestrating Recursive Computation Graphs across GPU
 // Memory Hierarchies".  The page's runtime (section III-C, Algorithm 2) takes
 // shell quartets with their primitives {(alpha_i, c_i)}, forms Gaussian-pair
-// data ("GAUSSIANPAIRS"), evaluates one angular-momentum class per kernel and
+// data, evaluates one angular-momentum class per kernel and
 // scatters into J.  Everything here runs on the device except argument
 // validation and the small class-block bookkeeping the host needs to launch.
 // The library allocates no device memory: plans and calls work in workspaces
@@ -182,7 +182,7 @@ inline int prim_pairs_kept(const double *cen, const int *off, const double *exps
     return n > 0 ? n : 1;
 }
 
-// Primitive-pair records for every shell pair (the page's GAUSSIANPAIRS);
+// Primitive-pair records for every shell pair (the page's Gaussian-pair step);
 // screened plans keep the primitive pairs prim_pairs_kept counts, in
 // (alpha, beta) order.
 __global__ void k_pair_data(int npairs, const int4 *pinfo, const double *cen, const int *off,

@@ -433,8 +433,8 @@ def schedule_min_live(items, initial=(), remote=None, min_dist=0):
 def topo_order(items):
     """A plain topological order of the same items: Kahn's algorithm taking the
     ready item that comes first in the given order (no liveness objective; the
-    "safe but non-optimized topological order" that section V-B of "FusionRCG"
-    compares DSA against)."""
+    plain valid ordering without liveness optimisation that section V-B of
+    "FusionRCG" compares DSA against)."""
     import heapq
     n = len(items)
     idx_of = {k: i for i, (k, ds, s) in enumerate(items)}

@@ -2,9 +2,9 @@
 
 For classes with few contracted targets, a lane owns a quartet: it loops over
 the quartet's primitive quartets, sets each up itself (geometry and Boys
-values, "GAUSSIANPAIRS" and "BOYS" in Algorithm 2 of "FusionRCG"), evaluates
+values: the Gaussian-pair and Boys steps of Algorithm 2 of "FusionRCG"), evaluates
 the vertical recurrence of Eq. (2) and its ket twin over every bra component
-e at once, adds the targets [e0|f0] into accumulators (Algorithm 2, line 7),
+e at once, adds the targets [e0|f0] into accumulators (as in Algorithm 2),
 and after the loop applies the horizontal recurrence of Eq. (3) and the
 stepwise spherical transform of Eq. (14) to both pairs.  No value crosses
 lanes, so there are no LDS records, no coupling reads and no barriers: the

@@ -12,7 +12,7 @@
  *     the transform applied index by index inside the horizontal phase
  *     (stepwise fusion, Eqs. (11)-(16), identical to Eq. (17));
  *   - the Coulomb matrix J_mu,nu = sum_(la,si) (mu nu|la si) D_la,si that
- *     Algorithm 2 scatters (line 10), using the 8-fold permutation symmetry of
+ *     Algorithm 2 accumulates from each quartet, using the 8-fold permutation symmetry of
  *     section III-C2 (Kernel 2) over Schwarz-screened unique quartets, and the
  *     exchange matrix K it scatters beside J.
  *
@@ -87,7 +87,7 @@ extern "C" {
 
 /* Shells as structure-of-arrays, all host memory, read (and copied) during
  * eri_build_quartets only.  The page's statement of the problem (section
- * III-C, Algorithm 2 line 1): each shell has a centre, an angular momentum and
+ * III-C, the input of Algorithm 2): each shell has a centre, an angular momentum and
  * primitives {(alpha_i, c_i)}. */
 typedef struct eri_shells {
     int32_t nshell;
@@ -102,8 +102,8 @@ typedef struct eri_shells {
 typedef struct eri_plan eri_plan;
 
 /*
- * Build a quartet plan: the shells' primitive-pair data (Algorithm 2 line 2,
- * "GAUSSIANPAIRS"), and the quartets batched by angular-momentum class and
+ * Build a quartet plan: the shells' primitive-pair data (the Gaussian-pair step
+ * of Algorithm 2), and the quartets batched by angular-momentum class and
  * contraction length (section III-C: kernels per shell-quartet class; the 120
  * classes of section IV for l <= 4).
  *   quartets != NULL (host): explicit list of nq shell quartets [4*nq]; each
@@ -175,7 +175,7 @@ int eri_plan_schwarz(const eri_plan *plan, double *dst, void *stream);
 
 /*
  * Integrals (Eq. (1) by Eqs. (2)-(3), spherical by Eq. (8) fused stepwise,
- * Algorithm 2 lines 3-9) of class blocks [block_begin, block_end) into `out`
+ * the primitive loop of Algorithm 2) of class blocks [block_begin, block_end) into `out`
  * (device): block b's quartets start at out + out_offset[b] -
  * out_offset[block_begin]; out_capacity is the number of doubles at `out`
  * (ERI_E_CAPACITY if too few).  Work memory is the plan's.  Asynchronous: the
@@ -196,7 +196,7 @@ int eri_compute_range(const eri_plan *plan, int32_t block, int64_t first, int64_
                       int64_t out_capacity, void *stream);
 
 /*
- * Coulomb matrix of a screened plan (Algorithm 2 line 10, "J += SCATTER";
+ * Coulomb matrix of a screened plan (the J update of Algorithm 2;
  * section III-C2 Kernel 2, 8-fold symmetry through scale factors):
  * J = sum over the plan's unique quartets with D~_kl = D_kl (2 for k != l),
  * D and J dense row-major device matrices of order nbf with leading dimensions
@@ -214,7 +214,7 @@ int eri_digest_J(const eri_plan *plan, const double *D, int32_t ldd, double *J, 
 /*
  * The Coulomb contributions of quartets [first, first + count) of class block
  * `block` of a screened plan (counted from the block's first slot, as
- * eri_compute_range) added to J: the sum of Algorithm 2 line 10 restricted to
+ * eri_compute_range) added to J: the J update of Algorithm 2 restricted to
  * those quartets, with eri_digest_J's D~ weights and row-major layouts.  J is
  * not cleared: over ranges that partition every block, with J zeroed first,
  * the calls add up to eri_digest_J's result (equal to rounding: the chunks are
@@ -228,7 +228,7 @@ int eri_digest_J_range(const eri_plan *plan, int32_t block, int64_t first, int64
 
 /*
  * Coulomb and exchange matrices of a screened plan in one pass over its
- * integrals (Algorithm 2 line 10 scatters into J and K; section III-C2): J as
+ * integrals (Algorithm 2 updates J and K from each quartet; section III-C2): J as
  * eri_digest_J, and K_mu,nu = sum (mu la|nu si) D_la,si (no factor -1/2),
  * both over the plan's unique quartets with their index permutations, D
  * symmetric.  J or K may be NULL (not both; the query must pass the same

@@ -700,8 +700,8 @@ int oracle_schwarz(int nshell, const double *centers, const int32_t *l, const in
 /* ------------------------------------------------------------------------ */
 /* J from a list of unique quartets                                          */
 /* ------------------------------------------------------------------------ */
-/* J_mu,nu = sum_(la,si) (mu nu|la si) D_la,si (the J update of Algorithm 2,
- * line 10).  Reading of the page's "8-fold symmetry via scale factors": for a
+/* J_mu,nu = sum_(la,si) (mu nu|la si) D_la,si (the J update of Algorithm 2).
+ * Reading of the page's 8-fold symmetry taken through weighting factors: for a
  * unique quartet (ij|kl) with integrals I, and D~_kl = D_kl * (2 if k != l
  * else 1) taken per shell pair,
  *   J_ij += I . D~_kl ;  and, if the pairs (ij) and (kl) differ,

@@ -8,7 +8,7 @@ every surviving quartet (oracle.eri, four-index Obara-Saika) and the
 unique-quartet digestion with the 8-fold symmetry factors
 (oracle.J_from_quartets), in chunks whose J are added (the digestion is linear
 in the quartets).  J_mu,nu = sum (mu nu|la si) D_la,si is the J update of
-Algorithm 2 (line 10) of "FusionRCG: Orchestrating Recursive Computation Graphs
+Algorithm 2 of "FusionRCG: Orchestrating Recursive Computation Graphs
 across GPU Memory Hierarchies".  About 20 minutes on 8 cores.
 
 Usage: python tests/golden/make_c3_J.py
